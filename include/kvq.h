@@ -1,0 +1,184 @@
+/*
+ * kvq.h -- C ABI of the MI355X (gfx950) KIVI-style quantized KV-cache library.
+ *
+ * The method (cited by page title and section):
+ *  - "KV cache compression: quantization, eviction and sparse attention",
+ *    section 3.2 (KIVI): keys are quantized per channel over groups of G
+ *    tokens, values per token, with a min/max scale and zero point; the most
+ *    recent R tokens stay in full precision and a group is quantized once it
+ *    is full; attention is computed over the quantized part and the
+ *    full-precision part and the two are merged.  Section 3.4: paged blocks of
+ *    16 tokens carry their own scale/zero tables, the key group is aligned to
+ *    the block, and the attention kernel dequantizes while it reads.
+ *  - "KV Cache compression lab", experiment 01: 2^b equally spaced levels
+ *    between min and max, spacing (max - min)/(2^b - 1), zero = the grid's
+ *    start, every value goes to its nearest level.
+ *  - "KV cache compression" (jaedaily), formula paragraph: the per-channel
+ *    key and per-token value dequantization q*s + z, and attention
+ *    softmax(q k^T / sqrt(d_h)).
+ *
+ * Numeric contract (identical on every entry point):
+ *   n_q  = G * floor(max(0, n - R) / G) quantized tokens; [n_q, n) stay fp16.
+ *   For each key (group, channel) and each value token: mn, mx = min, max of
+ *   the fp16 inputs (as fp32, -0 canonicalised to +0); s = fp16_rn((mx - mn)
+ *   / (2^b - 1)); z = fp16(mn); inv = s > 0 ? 1/s : 0 (IEEE division);
+ *   code = clamp(rint((x - z) * inv), 0, 2^b - 1) in fp32, ties to even.
+ *   Dequantized value: fmaf(code, s, z).
+ *   Attention: out[b][h] = sum_t softmax_t(scale * q[b][h] . k_t) v_t over all
+ *   n tokens (dequantized part and fp16 residual), query head h reading kv
+ *   head h / (Hq / H).  n = 0 gives out = 0.
+ *
+ * Conventions for every call below:
+ *   - Pointers named *_host are host memory; every other data pointer is a
+ *     device pointer owned by the caller.  The library allocates and frees
+ *     nothing and keeps no pointer after a call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).  All
+ *     device work is enqueued asynchronously on it; the call returns once the
+ *     work is enqueued.
+ *   - Arguments are validated on the host before anything is enqueued; a bad
+ *     argument returns KVQ_EINVAL (or KVQ_EUNSUPPORTED for a valid but
+ *     unimplemented shape) and enqueues nothing.  A failed launch returns
+ *     KVQ_EHIP; kvq_last_error() then holds the HIP error text.
+ *   - Inputs must be finite fp16; this is not checked on the hot path.
+ *   - Calls on one cache must be ordered (same stream, or caller-synchronised).
+ */
+#ifndef KVQ_H_
+#define KVQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_HEAD_DIM 128
+
+typedef enum kvq_status {
+    KVQ_OK = 0,
+    KVQ_EINVAL = 1,        /* malformed argument (null pointer, bad size)      */
+    KVQ_EUNSUPPORTED = 2,  /* well-formed but not implemented (e.g. d != 128)  */
+    KVQ_ECAPACITY = 3,     /* buffer or workspace too small                    */
+    KVQ_EHIP = 4           /* HIP runtime error while enqueueing               */
+} kvq_status;
+
+/* Shape of one quantized cache (one attention layer, or several layers folded
+ * into the sequence axis). */
+typedef struct kvq_config {
+    int32_t num_seqs;           /* B >= 1                                        */
+    int32_t num_kv_heads;       /* H >= 1                                        */
+    int32_t head_dim;           /* d, must be 128                                */
+    int32_t k_bits;             /* key code width: 2 or 4                        */
+    int32_t v_bits;             /* value code width: 2 or 4                      */
+    int32_t group_size;         /* G: 16, 32, 64 or 128 tokens per key group     */
+    int32_t residual;           /* R >= 0, a multiple of G                       */
+    int32_t max_tokens;         /* contiguous mode: per-sequence capacity        */
+    int32_t block_size;         /* 0 = contiguous; otherwise paged, == G         */
+    int32_t num_blocks;         /* paged: blocks in the pool                     */
+    int32_t max_blocks_per_seq; /* paged: length of one block-table row          */
+} kvq_config;
+
+/* Device buffers of one cache.  Sizes come from kvq_buffer_sizes(). */
+typedef struct kvq_cache {
+    void *packed;               /* group records (codes + fp16 scale/zero)       */
+    void *k_res;                /* fp16 key residual ring   [B][H][R+G][d]       */
+    void *v_res;                /* fp16 value residual ring [B][H][R+G][d]       */
+    int32_t *n_tokens;          /* [B] tokens held per sequence (n)              */
+    int32_t *n_quant;           /* [B] quantized tokens per sequence (n_q)       */
+    const int32_t *block_table; /* paged: [B][max_blocks_per_seq] block ids; a
+                                   sequence's key group g lives in block
+                                   block_table[b][g].  NULL in contiguous mode. */
+} kvq_cache;
+
+/* Byte sizes of the buffers of kvq_cache and of one group record.
+ * Record = one (key group, kv head): G*d*k_bits/8 key-code bytes,
+ * G*d*v_bits/8 value-code bytes, d fp16 (s, z) key pairs and G fp16 (s, z)
+ * value pairs.  Contiguous mode holds B*H*floor(max(0,max_tokens-R)/G)
+ * records; paged mode holds num_blocks*H records. */
+typedef struct kvq_sizes {
+    size_t packed_bytes;
+    size_t record_bytes;
+    size_t residual_bytes;     /* each of k_res and v_res                        */
+    size_t counter_bytes;      /* each of n_tokens and n_quant                   */
+    size_t block_table_bytes;  /* paged mode only, else 0                        */
+    int32_t groups_per_seq;    /* key groups one sequence can hold               */
+    int32_t residual_slots;    /* R + G                                          */
+} kvq_sizes;
+
+/* Host only, no device work.  Validates cfg and fills *out. */
+kvq_status kvq_buffer_sizes(const kvq_config *cfg, kvq_sizes *out);
+
+/* Bulk quantization of whole sequences ("KV cache compression" (jaedaily),
+ * deployment step (c); "KV cache compression: ...", section 3.2).
+ * k, v: fp16 [B][H][max_len][d]; seq_lens: device int32 [B], the number of
+ * valid tokens of each sequence.  Overwrites the cache state: for every
+ * sequence, groups [0, n_q) are quantized into records and tokens [n_q, n)
+ * are copied into the residual ring; n_tokens = n and n_quant = n_q.
+ * Preconditions (caller): 0 <= seq_lens[b] <= max_len, seq_lens[b] within the
+ * capacity (max_tokens, or max_blocks_per_seq*G with block_table rows filled
+ * for every quantized group).  The kernels clamp a violating length to the
+ * capacity and skip a record whose block id is outside [0, num_blocks), so no
+ * access leaves the buffers; the cache content is then unspecified. */
+kvq_status kv_quantize_prefill(const kvq_config *cfg, const kvq_cache *cache,
+                               const void *k, const void *v, int32_t max_len,
+                               const int32_t *seq_lens, void *stream);
+
+/* Append one fp16 token to every sequence ("KV cache compression: ...",
+ * section 3.2: the newest tokens stay full precision; once the full-precision
+ * tail holds R + G tokens its oldest G tokens form a full group outside the
+ * most recent R, which is quantized into a record and leaves the ring).
+ * k_new, v_new: fp16 [B][H][d].  n_tokens and n_quant are updated on the
+ * device, so a sequence of appends needs no host synchronisation.
+ * Preconditions (caller): n + 1 within capacity; in paged mode
+ * block_table[b][n_q/G] holds a free block before the append that flushes.
+ * A flush that would leave the buffers is skipped (no write) and the token is
+ * still appended to the ring only if the ring has room. */
+kvq_status kv_append_token(const kvq_config *cfg, const kvq_cache *cache,
+                           const void *k_new, const void *v_new, void *stream);
+
+/* Dequantize the whole cache ("KV cache compression" (jaedaily), formula
+ * paragraph: q*s + z, one fp32 rounding).  k_out, v_out: fp32
+ * [B][H][out_tokens][d]; token t < n_tokens[b] receives its dequantized
+ * (t < n_q) or exact fp16 (t >= n_q) value, later positions receive 0.
+ * Tokens beyond out_tokens are not written. */
+kvq_status kv_dequantize(const kvq_config *cfg, const kvq_cache *cache,
+                         float *k_out, float *v_out, int32_t out_tokens, void *stream);
+
+/* Workspace bytes kv_decode_attention needs for num_q_heads query heads.
+ * Host only.  Returns 0 for an invalid cfg. */
+size_t kv_decode_attention_workspace_bytes(const kvq_config *cfg, int32_t num_q_heads);
+
+/* Decode attention of one query token per sequence over the whole cache
+ * ("KV cache compression: ...", sections 3.1, 3.2 and 8.2: the kernel
+ * dequantizes while it reads, the quantized part and the full-precision
+ * residual are computed separately and merged).  q: fp16 [B][Hq][d];
+ * out: fp32 [B][Hq][d]; Hq a multiple of H with Hq/H <= 16; softmax_scale is
+ * normally 1/sqrt(d).  workspace: device memory of at least
+ * kv_decode_attention_workspace_bytes(cfg, Hq) bytes, used for per-split
+ * partial results; its content need not be preserved between calls. */
+kvq_status kv_decode_attention(const kvq_config *cfg, const kvq_cache *cache,
+                               const void *q, int32_t num_q_heads, float softmax_scale,
+                               float *out, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* Logical view of the quantized part (test hook).  k_codes, v_codes: uint8
+ * [B][H][out_tokens][d], one code per element for t < n_q[b], 0 elsewhere;
+ * k_s, k_z: fp16 bits [B][H][out_tokens/G][d] for groups < n_q[b]/G, 0
+ * elsewhere; v_s, v_z: fp16 bits [B][H][out_tokens] for t < n_q[b], 0
+ * elsewhere.  out_tokens must be a multiple of G. */
+kvq_status kv_export_codes(const kvq_config *cfg, const kvq_cache *cache,
+                           uint8_t *k_codes, uint8_t *v_codes,
+                           uint16_t *k_s, uint16_t *k_z, uint16_t *v_s, uint16_t *v_z,
+                           int32_t out_tokens, void *stream);
+
+/* Static description of a status code. */
+const char *kvq_status_string(kvq_status status);
+
+/* Text of the last KVQ_EHIP error raised on the calling thread ("" if none). */
+const char *kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H_ */

@@ -1,0 +1,297 @@
+/*
+ * kvq_oracle.c -- plain, slow CPU oracle for KIVI-style asymmetric low-bit
+ * KV-cache quantization and for decode attention over the dequantized cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU library shares
+ * no code, header, table or helper with it; the two meet only through the
+ * seeded input generators and the comparison in the tests.
+ *
+ * Build: gcc -std=c99 -O2 -ffp-contract=off -fno-fast-math -shared -fPIC
+ * (contraction off so every fp32 step below is one IEEE operation, as written).
+ *
+ * Sources (cited by page title and section):
+ *  [P1] "KV cache compression: quantization, eviction and sparse attention",
+ *       section 3.2 (KIVI: keys per-channel over G-token groups, values
+ *       per-token, full-precision residual of the most recent R tokens, a
+ *       group is quantized once it is full), section 3.4 (paged blocks),
+ *       section 8.1 (byte accounting), section 2.2 (sum of weights is 1).
+ *  [P3] "KV Cache compression lab", experiment 01 (grid of 2^bits lines between
+ *       min and max, spacing (max-min)/(2^bits-1), each value snaps to the
+ *       nearest line, zero = starting point of the grid).
+ *  [P4] "KV cache compression" (jaedaily), formula paragraph: per-channel key
+ *       dequant k = round((k - z_c)/s_c) s_c + z_c, per-token value dequant,
+ *       M_KV = 2 L H_kv n d_h b, attention softmax(q k^T / sqrt(d_h)).
+ *
+ * Readings where the pages leave a step open (each also listed in the design
+ * notes): scale and zero are computed in fp32 and stored as fp16 (round to
+ * nearest even); codes are computed from the STORED scale and zero as
+ * clamp(rint((x - z) * (1/s)), 0, 2^b - 1) with ties to even; a group whose
+ * stored scale is 0 gets all-zero codes; min and max are canonicalised so a
+ * -0 extreme becomes +0; the residual keeps at least R tokens, and a group
+ * is quantized only once it lies wholly outside them, so
+ * n_q = G * floor(max(0, n - R) / G).
+ *
+ * Parity pins (tests that tie this file to something other than itself) live
+ * in tests/test_oracle_pins.py.  Every function below is pinned there.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* IEEE 754 binary16 codec, written from the format's definition:           */
+/* 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits; exponent 0 holds */
+/* subnormals (fraction * 2^-24), exponent 31 holds inf / NaN.              */
+/* ------------------------------------------------------------------------ */
+
+float orc_h2f(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1f;
+    int frac = h & 0x3ff;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -24);
+    else if (expo == 31)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(frac + 1024), expo - 25);
+    return (float)(sign ? -v : v);
+}
+
+/* Round a float to the nearest binary16 value, ties to even. */
+uint16_t orc_f2h(float xf)
+{
+    double x = (double)xf; /* exact */
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isnan(x))
+        return (uint16_t)(sign | 0x7e00);
+    if (isinf(x))
+        return (uint16_t)(sign | 0x7c00);
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal range: value = m * 2^-24, m an integer 0..1024 */
+        double m = rint(ldexp(a, 24)); /* exact scaling; rint is ties-to-even */
+        return (uint16_t)(sign | (uint16_t)m); /* m == 1024 is the smallest normal */
+    }
+    int e2;
+    frexp(a, &e2);             /* a = f * 2^e2, f in [0.5, 1) */
+    int e = e2 - 1;            /* a in [2^e, 2^(e+1)) */
+    double m = rint(ldexp(a, 10 - e)); /* in [1024, 2048] */
+    if (m == 2048.0) {
+        m = 1024.0;
+        e += 1;
+    }
+    if (e > 15)
+        return (uint16_t)(sign | 0x7c00); /* overflow rounds to infinity */
+    return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)((int)m - 1024));
+}
+
+/* ------------------------------------------------------------------------ */
+/* Asymmetric uniform min/max quantizer of one set of fp16 values.          */
+/* [P3] exp. 01: 2^b grid lines between min and max, spacing                 */
+/* s = (max - min)/(2^b - 1), zero = min, each value snaps to the nearest   */
+/* line.  [P4]: dequant q*s + z.                                             */
+/* ------------------------------------------------------------------------ */
+
+static void quantize_set(const uint16_t *x, int count, long stride, int bits,
+                         uint8_t *codes, long code_stride, uint16_t *s_out, uint16_t *z_out)
+{
+    const int qmax = (1 << bits) - 1;
+    float mn = orc_h2f(x[0]);
+    float mx = mn;
+    for (int i = 1; i < count; ++i) {
+        float v = orc_h2f(x[(long)i * stride]);
+        if (v < mn) mn = v;
+        if (v > mx) mx = v;
+    }
+    mn = mn + 0.0f; /* -0 + +0 = +0 under round-to-nearest */
+    mx = mx + 0.0f;
+    float s32 = (mx - mn) / (float)qmax;
+    uint16_t s16 = orc_f2h(s32);
+    uint16_t z16 = orc_f2h(mn); /* exact: mn is an fp16 value */
+    float s = orc_h2f(s16);
+    float z = orc_h2f(z16);
+    float inv = (s > 0.0f) ? 1.0f / s : 0.0f;
+    for (int i = 0; i < count; ++i) {
+        float v = orc_h2f(x[(long)i * stride]);
+        float t = (v - z) * inv;
+        float r = rintf(t);
+        if (r < 0.0f) r = 0.0f;
+        if (r > (float)qmax) r = (float)qmax;
+        codes[(long)i * code_stride] = (uint8_t)r;
+    }
+    *s_out = s16;
+    *z_out = z16;
+}
+
+/* Number of quantized tokens of a sequence holding n tokens ([P1] 3.2:
+ * a group of G tokens is quantized only once it is full and outside the
+ * most recent R tokens). */
+int orc_num_quantized(int n, int G, int R)
+{
+    int over = n - R;
+    if (over <= 0) return 0;
+    return G * (over / G);
+}
+
+/* Keys of one group, per channel over the group's G tokens ([P1] 3.2, [P4]).
+ * x, codes: [G][d] row-major; s, z: [d]. */
+void orc_quantize_key_group(const uint16_t *x, int G, int d, int bits,
+                            uint8_t *codes, uint16_t *s, uint16_t *z)
+{
+    for (int c = 0; c < d; ++c)
+        quantize_set(x + c, G, d, bits, codes + c, d, &s[c], &z[c]);
+}
+
+/* Values of one token, over its d channels ([P1] 3.2, [P4]). */
+void orc_quantize_value_token(const uint16_t *x, int d, int bits,
+                              uint8_t *codes, uint16_t *s, uint16_t *z)
+{
+    quantize_set(x, d, 1, bits, codes, 1, s, z);
+}
+
+/* Whole-sequence quantization of one (sequence, kv-head) stream holding n
+ * tokens: groups [0, n_q) are quantized, [n_q, n) stay fp16 (the caller keeps
+ * them).  k, v: [n][d]; kcodes, vcodes: [n_q][d]; ks, kz: [n_q/G][d];
+ * vs, vz: [n_q].  Returns n_q. */
+int orc_prefill_stream(const uint16_t *k, const uint16_t *v, int n, int d,
+                       int kbits, int vbits, int G, int R,
+                       uint8_t *kcodes, uint16_t *ks, uint16_t *kz,
+                       uint8_t *vcodes, uint16_t *vs, uint16_t *vz)
+{
+    int nq = orc_num_quantized(n, G, R);
+    for (int g = 0; g < nq / G; ++g)
+        orc_quantize_key_group(k + (long)g * G * d, G, d, kbits,
+                               kcodes + (long)g * G * d, ks + (long)g * d, kz + (long)g * d);
+    for (int t = 0; t < nq; ++t)
+        orc_quantize_value_token(v + (long)t * d, d, vbits, vcodes + (long)t * d, vs + t, vz + t);
+    return nq;
+}
+
+/* Incremental form ([P1] 3.2, [P4] deployment step (c)): append one fp16
+ * token to a stream's state; when the full-precision tail reaches R + G
+ * tokens, its oldest G tokens form a full group outside the most recent R
+ * and are quantized.  State: *n, *nq; hist_k/hist_v [cap][d] hold every
+ * appended fp16 token at its position (the oracle keeps the whole history;
+ * only [nq, n) is treated as residual); the quantized arrays are indexed as
+ * in orc_prefill_stream.  Returns 1 if a group was flushed, 0 otherwise,
+ * -1 if cap would be exceeded. */
+int orc_append_stream(uint16_t *hist_k, uint16_t *hist_v, int cap, int *n, int *nq,
+                      const uint16_t *k_new, const uint16_t *v_new, int d,
+                      int kbits, int vbits, int G, int R,
+                      uint8_t *kcodes, uint16_t *ks, uint16_t *kz,
+                      uint8_t *vcodes, uint16_t *vs, uint16_t *vz)
+{
+    if (*n >= cap) return -1;
+    memcpy(hist_k + (long)(*n) * d, k_new, sizeof(uint16_t) * d);
+    memcpy(hist_v + (long)(*n) * d, v_new, sizeof(uint16_t) * d);
+    *n += 1;
+    if (*n - *nq == R + G) {
+        int g = *nq / G;
+        orc_quantize_key_group(hist_k + (long)(*nq) * d, G, d, kbits,
+                               kcodes + (long)(*nq) * d, ks + (long)g * d, kz + (long)g * d);
+        for (int t = *nq; t < *nq + G; ++t)
+            orc_quantize_value_token(hist_v + (long)t * d, d, vbits,
+                                     vcodes + (long)t * d, vs + t, vz + t);
+        *nq += G;
+        return 1;
+    }
+    return 0;
+}
+
+/* Dequantized stream ([P4]: x = q*s + z, one fp32 rounding via fma; the
+ * residual tokens are the fp16 values themselves).  out_k, out_v: [n][d]. */
+void orc_dequantize_stream(const uint16_t *k, const uint16_t *v, int n, int nq, int d, int G,
+                           const uint8_t *kcodes, const uint16_t *ks, const uint16_t *kz,
+                           const uint8_t *vcodes, const uint16_t *vs, const uint16_t *vz,
+                           float *out_k, float *out_v)
+{
+    for (int t = 0; t < n; ++t) {
+        for (int c = 0; c < d; ++c) {
+            long i = (long)t * d + c;
+            if (t < nq) {
+                long gi = (long)(t / G) * d + c;
+                out_k[i] = fmaf((float)kcodes[i], orc_h2f(ks[gi]), orc_h2f(kz[gi]));
+                out_v[i] = fmaf((float)vcodes[i], orc_h2f(vs[t]), orc_h2f(vz[t]));
+            } else {
+                out_k[i] = orc_h2f(k[i]);
+                out_v[i] = orc_h2f(v[i]);
+            }
+        }
+    }
+}
+
+/* Scaled dot-product attention of gq query rows against n key/value rows,
+ * accumulated in fp64 ([P4]: softmax(q k^T / sqrt(d_h)) weighting v; the
+ * softmax subtracts the row maximum before exponentiating, which leaves its
+ * value unchanged).  q: [gq][d]; kh, vh: [n][d]; out: [gq][d];
+ * weights (optional, may be NULL): [gq][n].  n == 0 gives out = 0. */
+void orc_attention(const float *q, int gq, const float *kh, const float *vh, int n, int d,
+                   float scale, double *out, double *weights)
+{
+    double *logit = (double *)malloc(sizeof(double) * (n > 0 ? n : 1));
+    for (int h = 0; h < gq; ++h) {
+        double *o = out + (long)h * d;
+        for (int c = 0; c < d; ++c) o[c] = 0.0;
+        if (n == 0) continue;
+        double m = -INFINITY;
+        for (int t = 0; t < n; ++t) {
+            double acc = 0.0;
+            for (int c = 0; c < d; ++c)
+                acc += (double)q[(long)h * d + c] * (double)kh[(long)t * d + c];
+            logit[t] = (double)scale * acc;
+            if (logit[t] > m) m = logit[t];
+        }
+        double l = 0.0;
+        for (int t = 0; t < n; ++t) {
+            logit[t] = exp(logit[t] - m);
+            l += logit[t];
+        }
+        for (int t = 0; t < n; ++t) {
+            double p = logit[t] / l;
+            if (weights) weights[(long)h * n + t] = p;
+            for (int c = 0; c < d; ++c) o[c] += p * (double)vh[(long)t * d + c];
+        }
+    }
+    free(logit);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Byte accounting ([P4] M_KV = 2 L H_kv n d_h b; [P1] 8.1 per-token table).  */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of one (sequence, kv-head) stream holding n tokens in the KIVI
+ * format: packed key and value codes for the n_q quantized tokens, one fp16
+ * (scale, zero) pair per (key group, channel) and per quantized value token,
+ * and fp16 keys and values for the n - n_q residual tokens.  Bit widths of 16
+ * mean "not quantized" (plain fp16 cache, no metadata). */
+double orc_stream_bytes(long n, int d, int kbits, int vbits, int G, int R)
+{
+    if (kbits == 16 && vbits == 16) return 2.0 * (double)n * d * 2.0;
+    long nq = orc_num_quantized((int)n, G, R);
+    double codes = (double)nq * d * (kbits + vbits) / 8.0;
+    double kmeta = (double)(nq / G) * d * 4.0;
+    double vmeta = (double)nq * 4.0;
+    double resid = (double)(n - nq) * d * 2.0 * 2.0;
+    return codes + kmeta + vmeta + resid;
+}
+
+/* [P4] closed form for an unquantized cache: 2 * L * H_kv * n * d_h * b. */
+double orc_kv_bytes_closed_form(long L, long Hkv, long n, long d, double bytes_per_elem)
+{
+    return 2.0 * (double)L * (double)Hkv * (double)n * (double)d * bytes_per_elem;
+}
+
+/* Array helpers so the tests can run the codec over every bit pattern. */
+void orc_h2f_array(const uint16_t *h, float *f, long count)
+{
+    for (long i = 0; i < count; ++i) f[i] = orc_h2f(h[i]);
+}
+
+void orc_f2h_array(const float *f, uint16_t *h, long count)
+{
+    for (long i = 0; i < count; ++i) h[i] = orc_f2h(f[i]);
+}

@@ -1,0 +1,156 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module holds no arithmetic of the quantization method: it only draws
+random numbers with the structure the pages describe for real K/V caches and
+names the workloads.
+
+Structure ("KV cache compression: quantization, eviction and sparse
+attention", section 2.1; "KV Cache compression lab", experiment 03):
+  * keys carry a few fixed outlier channels, tens of times larger than the
+    rest, at the same channels for every token -> 4 seed-chosen channels per
+    (layer, kv head) scaled x20 (section 3.1 of the first page uses 20x);
+  * values have no channel outliers; their large entries come by token row ->
+    for the long-context workloads 1% of the token rows per (sequence, kv head)
+    are scaled x5;
+  * everything else, and the query, is N(0, 1), cast to fp16.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+BASE_SEED = 0x4B495649
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    k_bits: int
+    v_bits: int
+    group_size: int
+    residual: int
+    context: int                 # tokens per sequence (max for the paged mix)
+    head_dim: int = 128
+    paged: bool = False
+    min_context: int = 0         # paged mix: lengths uniform in [min_context, context]
+    v_outlier_frac: float = 0.01
+    layers: int = 1              # layers folded into the sequence axis
+    tag: int = 0                 # distinguishes seeds between workloads
+
+    @property
+    def gq(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+
+# The five workloads the method is measured on (sizes from the task's
+# statement of the problem; readings of unstated parameters are explained in
+# the design notes: paged G = block size = 16 with R = 128; the full-cache
+# workload uses R = 128).
+WORKLOADS = {
+    "single_head_1k_int2": Workload(
+        "single_head_1k_int2", num_seqs=1, num_q_heads=1, num_kv_heads=1, k_bits=2, v_bits=2,
+        group_size=32, residual=32, context=1024, v_outlier_frac=0.0, tag=1),
+    "llama3_8b_layer_b8_32k_int4": Workload(
+        "llama3_8b_layer_b8_32k_int4", num_seqs=8, num_q_heads=32, num_kv_heads=8, k_bits=4,
+        v_bits=4, group_size=32, residual=128, context=32768, tag=2),
+    "llama3_70b_layer_b1_128k_int2": Workload(
+        "llama3_70b_layer_b1_128k_int2", num_seqs=1, num_q_heads=64, num_kv_heads=8, k_bits=2,
+        v_bits=2, group_size=32, residual=128, context=131072, tag=3),
+    "paged_64seq_1k_16k_k4v2": Workload(
+        "paged_64seq_1k_16k_k4v2", num_seqs=64, num_q_heads=32, num_kv_heads=8, k_bits=4,
+        v_bits=2, group_size=16, residual=128, context=16384, min_context=1024, paged=True, tag=4),
+    "llama3_70b_cache_80l_128k_int2": Workload(
+        "llama3_70b_cache_80l_128k_int2", num_seqs=80, num_q_heads=64, num_kv_heads=8, k_bits=2,
+        v_bits=2, group_size=32, residual=128, context=131072, layers=80, tag=5),
+}
+
+
+def seed_for(tag: int, *parts: int) -> int:
+    """Deterministic 63-bit seed for (workload tag, layer, tensor, ...)."""
+    ss = np.random.SeedSequence([BASE_SEED, tag, *parts])
+    return int(ss.generate_state(2, dtype=np.uint64)[0] & np.uint64(0x7FFFFFFFFFFFFFFF))
+
+
+def seq_lengths(w: Workload) -> np.ndarray:
+    """Per-sequence token counts (uniform mix for the paged workload)."""
+    if not w.paged and w.min_context == 0:
+        return np.full(w.num_seqs, w.context, np.int32)
+    rng = np.random.Generator(np.random.PCG64(seed_for(w.tag, 99)))
+    return rng.integers(w.min_context, w.context + 1, size=w.num_seqs).astype(np.int32)
+
+
+def outlier_channels(w: Workload, layer: int, head: int, count: int = 4) -> np.ndarray:
+    rng = np.random.Generator(np.random.PCG64(seed_for(w.tag, layer, 7, head)))
+    return np.sort(rng.permutation(w.head_dim)[:count])
+
+
+def _gen(device, seed):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def make_kv(w: Workload, seqs=None, max_len=None, device="cpu", layer_of_seq=None,
+            k_outlier=20.0, v_outlier=5.0):
+    """fp16 K and V tensors [S][H][max_len][d] for the sequences `seqs`
+    (default: all).  Sequence b belongs to layer layer_of_seq(b) (default:
+    b // (num_seqs / layers)); its outlier channels come from that layer."""
+    lens = seq_lengths(w)
+    seqs = list(range(w.num_seqs)) if seqs is None else list(seqs)
+    L = int(max_len if max_len is not None else max(int(lens[b]) for b in seqs))
+    H, d = w.num_kv_heads, w.head_dim
+    per_layer = max(1, w.num_seqs // w.layers)
+    lay = layer_of_seq or (lambda b: b // per_layer)
+    K = torch.empty((len(seqs), H, L, d), dtype=torch.float16, device=device)
+    V = torch.empty((len(seqs), H, L, d), dtype=torch.float16, device=device)
+    for i, b in enumerate(seqs):
+        n = min(int(lens[b]), L)
+        for h in range(H):
+            g = _gen(device, seed_for(w.tag, lay(b), 1, b, h))
+            kk = torch.randn((L, d), generator=g, device=device, dtype=torch.float32)
+            ch = torch.as_tensor(outlier_channels(w, lay(b), h), device=device)
+            kk[:, ch] *= k_outlier
+            K[i, h] = kk.to(torch.float16)
+            g = _gen(device, seed_for(w.tag, lay(b), 2, b, h))
+            vv = torch.randn((L, d), generator=g, device=device, dtype=torch.float32)
+            nrows = int(w.v_outlier_frac * n)
+            if nrows > 0:
+                rng = np.random.Generator(np.random.PCG64(seed_for(w.tag, lay(b), 3, b, h)))
+                rows = torch.as_tensor(rng.choice(n, size=nrows, replace=False), device=device)
+                vv[rows] *= v_outlier
+            V[i, h] = vv.to(torch.float16)
+    return K, V
+
+
+def make_query(w: Workload, device="cpu", step: int = 0, seqs=None):
+    """fp16 query [S][Hq][d]."""
+    S = w.num_seqs if seqs is None else len(list(seqs))
+    g = _gen(device, seed_for(w.tag, 0, 4, step))
+    return torch.randn((S, w.num_q_heads, w.head_dim), generator=g, device=device,
+                       dtype=torch.float32).to(torch.float16)
+
+
+def make_tokens(w: Workload, step: int, device="cpu", k_outlier=20.0):
+    """One new fp16 (k, v) token per (sequence, kv head): [B][H][d] each, with
+    the same outlier channels as the cache it is appended to."""
+    B, H, d = w.num_seqs, w.num_kv_heads, w.head_dim
+    g = _gen(device, seed_for(w.tag, 0, 5, step))
+    k = torch.randn((B, H, d), generator=g, device=device, dtype=torch.float32)
+    per_layer = max(1, w.num_seqs // w.layers)
+    for b in range(B):
+        for h in range(H):
+            ch = torch.as_tensor(outlier_channels(w, b // per_layer, h), device=device)
+            k[b, h, ch] *= k_outlier
+    v = torch.randn((B, H, d), generator=g, device=device, dtype=torch.float32)
+    return k.to(torch.float16), v.to(torch.float16)
+
+
+def random_fp16(shape, seed: int, scale: float = 1.0) -> np.ndarray:
+    """Plain N(0, scale^2) fp16 bit patterns (numpy, for small host tests)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return (rng.standard_normal(shape) * scale).astype(np.float16).view(np.uint16)
