@@ -70,7 +70,7 @@ typedef struct kvq_config {
     int32_t head_dim;           /* d, must be 128                                */
     int32_t k_bits;             /* key code width: 2 or 4                        */
     int32_t v_bits;             /* value code width: 2 or 4                      */
-    int32_t group_size;         /* G: 16, 32, 64 or 128 tokens per key group     */
+    int32_t group_size;         /* G: 16, 32 or 64 tokens per key group          */
     int32_t residual;           /* R >= 0, a multiple of G                       */
     int32_t max_tokens;         /* contiguous mode: per-sequence capacity        */
     int32_t block_size;         /* 0 = contiguous; otherwise paged, == G         */

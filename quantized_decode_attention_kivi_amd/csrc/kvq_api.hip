@@ -1,0 +1,176 @@
+// kvq_api.hip -- C ABI of libkvq: host-side validation, sizes and dispatch.
+// Every entry point validates its arguments before anything is enqueued and
+// never allocates device memory.
+#include <stdio.h>
+#include <string.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+
+static thread_local char g_last_error[256] = "";
+
+static kvq_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return KVQ_OK;
+    snprintf(g_last_error, sizeof(g_last_error), "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+    return KVQ_EHIP;
+}
+
+kvq_status make_layout(const kvq_config* cfg, Layout* L) {
+    if (!cfg || !L) return KVQ_EINVAL;
+    if (cfg->num_seqs < 1 || cfg->num_kv_heads < 1) return KVQ_EINVAL;
+    if (cfg->head_dim != kD) return KVQ_EUNSUPPORTED;
+    if ((cfg->k_bits != 2 && cfg->k_bits != 4) || (cfg->v_bits != 2 && cfg->v_bits != 4)) return KVQ_EUNSUPPORTED;
+    const int G = cfg->group_size;
+    if (G != 16 && G != 32 && G != 64) return KVQ_EUNSUPPORTED;
+    if (cfg->residual < 0 || cfg->residual % G != 0) return KVQ_EINVAL;
+    if (cfg->residual > (1 << 20)) return KVQ_EINVAL;
+    L->B = cfg->num_seqs;
+    L->H = cfg->num_kv_heads;
+    L->kbits = cfg->k_bits;
+    L->vbits = cfg->v_bits;
+    L->G = G;
+    L->R = cfg->residual;
+    L->ring = cfg->residual + G;
+    L->paged = cfg->block_size != 0;
+    if (L->paged) {
+        if (cfg->block_size != G) return KVQ_EINVAL;
+        if (cfg->num_blocks < 1 || cfg->max_blocks_per_seq < 1) return KVQ_EINVAL;
+        L->num_blocks = cfg->num_blocks;
+        L->max_blocks = cfg->max_blocks_per_seq;
+        L->groups = cfg->max_blocks_per_seq;
+        const long cap = (long)L->R + (long)(L->max_blocks + 1) * G - 1;
+        L->capacity = cap > 0x7fffffffL ? 0x7fffffff : (int)cap;
+    } else {
+        if (cfg->max_tokens < 0) return KVQ_EINVAL;
+        L->num_blocks = 0;
+        L->max_blocks = 0;
+        L->groups = num_quantized(cfg->max_tokens, G, L->R) / G;
+        L->capacity = cfg->max_tokens;
+    }
+    L->kcode = G * kD * L->kbits / 8;
+    L->vcode = G * kD * L->vbits / 8;
+    L->vcode_off = L->kcode;
+    L->kmeta_off = L->vcode_off + L->vcode;
+    L->vmeta_off = L->kmeta_off + kD * 4;
+    L->record = L->vmeta_off + G * 4;
+    return KVQ_OK;
+}
+
+static kvq_status check_cache(const Layout& L, const kvq_cache* c) {
+    if (!c || !c->packed || !c->k_res || !c->v_res || !c->n_tokens || !c->n_quant) return KVQ_EINVAL;
+    if (L.paged && !c->block_table) return KVQ_EINVAL;
+    if (((uintptr_t)c->packed & 15) || ((uintptr_t)c->k_res & 15) || ((uintptr_t)c->v_res & 15))
+        return KVQ_EINVAL;
+    return KVQ_OK;
+}
+
+}  // namespace kvq
+
+using namespace kvq;
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+kvq_status kvq_buffer_sizes(const kvq_config* cfg, kvq_sizes* out) {
+    Layout L;
+    if (!out) return KVQ_EINVAL;
+    kvq_status st = make_layout(cfg, &L);
+    if (st != KVQ_OK) return st;
+    const size_t nrec = L.paged ? (size_t)L.num_blocks * L.H : (size_t)L.B * L.H * L.groups;
+    out->record_bytes = (size_t)L.record;
+    out->packed_bytes = nrec * L.record;
+    out->residual_bytes = (size_t)L.B * L.H * L.ring * kD * 2;
+    out->counter_bytes = (size_t)L.B * sizeof(int32_t);
+    out->block_table_bytes = L.paged ? (size_t)L.B * L.max_blocks * sizeof(int32_t) : 0;
+    out->groups_per_seq = L.groups;
+    out->residual_slots = L.ring;
+    return KVQ_OK;
+}
+
+kvq_status kv_quantize_prefill(const kvq_config* cfg, const kvq_cache* cache, const void* k, const void* v,
+                               int32_t max_len, const int32_t* seq_lens, void* stream) {
+    Layout L;
+    kvq_status st = make_layout(cfg, &L);
+    if (st != KVQ_OK) return st;
+    if ((st = check_cache(L, cache)) != KVQ_OK) return st;
+    if (!k || !v || !seq_lens || max_len < 0) return KVQ_EINVAL;
+    if (((uintptr_t)k & 3) || ((uintptr_t)v & 3)) return KVQ_EINVAL;
+    return hip_status(launch_prefill(L, *cache, (const _Float16*)k, (const _Float16*)v, max_len, seq_lens,
+                                     (hipStream_t)stream));
+}
+
+kvq_status kv_append_token(const kvq_config* cfg, const kvq_cache* cache, const void* k_new, const void* v_new,
+                           void* stream) {
+    Layout L;
+    kvq_status st = make_layout(cfg, &L);
+    if (st != KVQ_OK) return st;
+    if ((st = check_cache(L, cache)) != KVQ_OK) return st;
+    if (!k_new || !v_new || ((uintptr_t)k_new & 3) || ((uintptr_t)v_new & 3)) return KVQ_EINVAL;
+    return hip_status(launch_append(L, *cache, (const _Float16*)k_new, (const _Float16*)v_new,
+                                    (hipStream_t)stream));
+}
+
+kvq_status kv_dequantize(const kvq_config* cfg, const kvq_cache* cache, float* k_out, float* v_out,
+                         int32_t out_tokens, void* stream) {
+    Layout L;
+    kvq_status st = make_layout(cfg, &L);
+    if (st != KVQ_OK) return st;
+    if ((st = check_cache(L, cache)) != KVQ_OK) return st;
+    if (!k_out || !v_out || out_tokens < 0) return KVQ_EINVAL;
+    return hip_status(launch_dequantize(L, *cache, k_out, v_out, out_tokens, (hipStream_t)stream));
+}
+
+size_t kv_decode_attention_workspace_bytes(const kvq_config* cfg, int32_t num_q_heads) {
+    Layout L;
+    if (make_layout(cfg, &L) != KVQ_OK) return 0;
+    if (num_q_heads < L.H || num_q_heads % L.H) return 0;
+    return plan_attention(L, num_q_heads).workspace;
+}
+
+kvq_status kv_decode_attention(const kvq_config* cfg, const kvq_cache* cache, const void* q, int32_t num_q_heads,
+                               float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    Layout L;
+    kvq_status st = make_layout(cfg, &L);
+    if (st != KVQ_OK) return st;
+    if ((st = check_cache(L, cache)) != KVQ_OK) return st;
+    if (!q || !out || !workspace || ((uintptr_t)q & 3) || ((uintptr_t)workspace & 15)) return KVQ_EINVAL;
+    if (num_q_heads < L.H || num_q_heads % L.H) return KVQ_EINVAL;
+    const int gq = num_q_heads / L.H;
+    if (gq != 1 && gq != 2 && gq != 4 && gq != 8 && gq != 16) return KVQ_EUNSUPPORTED;
+    if (!(softmax_scale > 0.0f) || softmax_scale > 1e30f) return KVQ_EINVAL;
+    const AttnPlan P = plan_attention(L, num_q_heads);
+    if (workspace_bytes < P.workspace) return KVQ_ECAPACITY;
+    return hip_status(launch_attention(L, P, *cache, (const _Float16*)q, num_q_heads, softmax_scale, out,
+                                       workspace, (hipStream_t)stream));
+}
+
+kvq_status kv_export_codes(const kvq_config* cfg, const kvq_cache* cache, uint8_t* k_codes, uint8_t* v_codes,
+                           uint16_t* k_s, uint16_t* k_z, uint16_t* v_s, uint16_t* v_z, int32_t out_tokens,
+                           void* stream) {
+    Layout L;
+    kvq_status st = make_layout(cfg, &L);
+    if (st != KVQ_OK) return st;
+    if ((st = check_cache(L, cache)) != KVQ_OK) return st;
+    if (!k_codes || !v_codes || !k_s || !k_z || !v_s || !v_z) return KVQ_EINVAL;
+    if (out_tokens < 0 || out_tokens % L.G) return KVQ_EINVAL;
+    return hip_status(launch_export(L, *cache, k_codes, v_codes, k_s, k_z, v_s, v_z, out_tokens,
+                                    (hipStream_t)stream));
+}
+
+const char* kvq_status_string(kvq_status s) {
+    switch (s) {
+        case KVQ_OK: return "ok";
+        case KVQ_EINVAL: return "invalid argument";
+        case KVQ_EUNSUPPORTED: return "unsupported configuration";
+        case KVQ_ECAPACITY: return "buffer or workspace too small";
+        case KVQ_EHIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* kvq_last_error(void) { return g_last_error; }
+
+}  // extern "C"
+#pragma GCC visibility pop

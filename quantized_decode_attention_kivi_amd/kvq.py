@@ -1,0 +1,316 @@
+"""ctypes binding of libkvq (the C ABI in include/kvq.h).
+
+Argument marshalling only: the functions below carry the C names, turn torch
+tensors into device pointers and the current HIP stream into a void*, and
+raise on a non-OK status.  Every step of the computation runs in the HIP
+kernels of libkvq.so; if the library is not built, loading fails loudly --
+there is no fallback.
+
+`QuantizedKVCache` allocates the caller-owned buffers with torch (device
+memory and streams are all torch provides here) and keeps the host-side copy
+of the per-sequence token counts that argument validation needs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+_lib = None
+
+KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ECAPACITY, KVQ_EHIP = range(5)
+HEAD_DIM = 128
+
+
+class kvq_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_seqs", "num_kv_heads", "head_dim", "k_bits", "v_bits", "group_size", "residual",
+        "max_tokens", "block_size", "num_blocks", "max_blocks_per_seq")]
+
+
+class kvq_cache(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
+                ("n_tokens", ctypes.c_void_p), ("n_quant", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p)]
+
+
+class kvq_sizes(ctypes.Structure):
+    _fields_ = [("packed_bytes", ctypes.c_size_t), ("record_bytes", ctypes.c_size_t),
+                ("residual_bytes", ctypes.c_size_t), ("counter_bytes", ctypes.c_size_t),
+                ("block_table_bytes", ctypes.c_size_t), ("groups_per_seq", ctypes.c_int32),
+                ("residual_slots", ctypes.c_int32)]
+
+
+EXPORTED = ["kvq_buffer_sizes", "kv_quantize_prefill", "kv_append_token", "kv_dequantize",
+            "kv_decode_attention_workspace_bytes", "kv_decode_attention", "kv_export_codes",
+            "kvq_status_string", "kvq_last_error"]
+
+
+class KVQError(RuntimeError):
+    def __init__(self, status, where):
+        msg = "%s: %s" % (where, lib().kvq_status_string(status).decode())
+        if status == KVQ_EHIP:
+            msg += " (" + lib().kvq_last_error().decode() + ")"
+        super().__init__(msg)
+        self.status = status
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libkvq.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        vp = ctypes.c_void_p
+        L.kvq_buffer_sizes.argtypes = [P(kvq_config), P(kvq_sizes)]
+        L.kvq_buffer_sizes.restype = ctypes.c_int
+        L.kv_quantize_prefill.argtypes = [P(kvq_config), P(kvq_cache), vp, vp, ctypes.c_int32, vp, vp]
+        L.kv_quantize_prefill.restype = ctypes.c_int
+        L.kv_append_token.argtypes = [P(kvq_config), P(kvq_cache), vp, vp, vp]
+        L.kv_append_token.restype = ctypes.c_int
+        L.kv_dequantize.argtypes = [P(kvq_config), P(kvq_cache), vp, vp, ctypes.c_int32, vp]
+        L.kv_dequantize.restype = ctypes.c_int
+        L.kv_decode_attention_workspace_bytes.argtypes = [P(kvq_config), ctypes.c_int32]
+        L.kv_decode_attention_workspace_bytes.restype = ctypes.c_size_t
+        L.kv_decode_attention.argtypes = [P(kvq_config), P(kvq_cache), vp, ctypes.c_int32, ctypes.c_float,
+                                          vp, vp, ctypes.c_size_t, vp]
+        L.kv_decode_attention.restype = ctypes.c_int
+        L.kv_export_codes.argtypes = [P(kvq_config), P(kvq_cache)] + [vp] * 6 + [ctypes.c_int32, vp]
+        L.kv_export_codes.restype = ctypes.c_int
+        L.kvq_status_string.argtypes = [ctypes.c_int]
+        L.kvq_status_string.restype = ctypes.c_char_p
+        L.kvq_last_error.argtypes = []
+        L.kvq_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status, where):
+    if status != KVQ_OK:
+        raise KVQError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# C-ABI functions, same names
+# ---------------------------------------------------------------------------
+
+def kvq_buffer_sizes(cfg: kvq_config) -> kvq_sizes:
+    out = kvq_sizes()
+    _check(lib().kvq_buffer_sizes(ctypes.byref(cfg), ctypes.byref(out)), "kvq_buffer_sizes")
+    return out
+
+
+def kv_quantize_prefill(cfg, cache, k, v, max_len, seq_lens, stream=None):
+    _check(lib().kv_quantize_prefill(ctypes.byref(cfg), ctypes.byref(cache), _ptr(k), _ptr(v), int(max_len),
+                                     _ptr(seq_lens), _stream(stream)), "kv_quantize_prefill")
+
+
+def kv_append_token(cfg, cache, k_new, v_new, stream=None):
+    _check(lib().kv_append_token(ctypes.byref(cfg), ctypes.byref(cache), _ptr(k_new), _ptr(v_new),
+                                 _stream(stream)), "kv_append_token")
+
+
+def kv_dequantize(cfg, cache, k_out, v_out, out_tokens, stream=None):
+    _check(lib().kv_dequantize(ctypes.byref(cfg), ctypes.byref(cache), _ptr(k_out), _ptr(v_out),
+                               int(out_tokens), _stream(stream)), "kv_dequantize")
+
+
+def kv_decode_attention_workspace_bytes(cfg, num_q_heads) -> int:
+    return int(lib().kv_decode_attention_workspace_bytes(ctypes.byref(cfg), int(num_q_heads)))
+
+
+def kv_decode_attention(cfg, cache, q, num_q_heads, softmax_scale, out, workspace, stream=None):
+    _check(lib().kv_decode_attention(ctypes.byref(cfg), ctypes.byref(cache), _ptr(q), int(num_q_heads),
+                                     ctypes.c_float(softmax_scale), _ptr(out), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)),
+           "kv_decode_attention")
+
+
+def kv_export_codes(cfg, cache, k_codes, v_codes, k_s, k_z, v_s, v_z, out_tokens, stream=None):
+    _check(lib().kv_export_codes(ctypes.byref(cfg), ctypes.byref(cache), _ptr(k_codes), _ptr(v_codes),
+                                 _ptr(k_s), _ptr(k_z), _ptr(v_s), _ptr(v_z), int(out_tokens),
+                                 _stream(stream)), "kv_export_codes")
+
+
+# ---------------------------------------------------------------------------
+# Buffer owner
+# ---------------------------------------------------------------------------
+
+def num_quantized(n, G, R):
+    return 0 if n <= R else G * ((n - R) // G)
+
+
+@dataclass
+class CacheShape:
+    num_seqs: int
+    num_kv_heads: int
+    k_bits: int
+    v_bits: int
+    group_size: int
+    residual: int
+    max_tokens: int = 0
+    paged: bool = False
+    num_blocks: int = 0
+    max_blocks_per_seq: int = 0
+
+    def config(self) -> kvq_config:
+        return kvq_config(self.num_seqs, self.num_kv_heads, HEAD_DIM, self.k_bits, self.v_bits,
+                          self.group_size, self.residual, self.max_tokens if not self.paged else 0,
+                          self.group_size if self.paged else 0, self.num_blocks, self.max_blocks_per_seq)
+
+
+class QuantizedKVCache:
+    """Device buffers of one quantized cache plus host-side bookkeeping of the
+    token counts (used only to validate calls and size exports).  In paged
+    mode a simple host free-list hands out blocks ahead of the device flushes."""
+
+    def __init__(self, shape: CacheShape, device="cuda"):
+        self.shape = shape
+        self.cfg = shape.config()
+        self.sizes = kvq_buffer_sizes(self.cfg)
+        self.device = torch.device(device)
+        sz = self.sizes
+        self.packed = torch.empty(max(sz.packed_bytes, 16), dtype=torch.uint8, device=self.device)
+        self.k_res = torch.zeros(sz.residual_bytes // 2, dtype=torch.float16, device=self.device)
+        self.v_res = torch.zeros(sz.residual_bytes // 2, dtype=torch.float16, device=self.device)
+        self.n_tokens = torch.zeros(shape.num_seqs, dtype=torch.int32, device=self.device)
+        self.n_quant = torch.zeros(shape.num_seqs, dtype=torch.int32, device=self.device)
+        self.block_table = None
+        if shape.paged:
+            self.block_table = torch.full((shape.num_seqs, shape.max_blocks_per_seq), -1, dtype=torch.int32,
+                                          device=self.device)
+            self._bt_host = np.full((shape.num_seqs, shape.max_blocks_per_seq), -1, np.int32)
+            self._block_order = list(range(shape.num_blocks - 1, -1, -1))  # pop() hands out 0, 1, 2, ...
+            self._free = list(self._block_order)
+        self.lens = np.zeros(shape.num_seqs, np.int64)
+        self.cache = kvq_cache(self.packed.data_ptr(), self.k_res.data_ptr(), self.v_res.data_ptr(),
+                               self.n_tokens.data_ptr(), self.n_quant.data_ptr(),
+                               self.block_table.data_ptr() if self.block_table is not None else None)
+        self._ws = None
+
+    @property
+    def G(self):
+        return self.shape.group_size
+
+    @property
+    def R(self):
+        return self.shape.residual
+
+    def capacity(self):
+        s = self.shape
+        if s.paged:
+            return s.residual + (s.max_blocks_per_seq + 1) * s.group_size - 1
+        return s.max_tokens
+
+    # -- paged block bookkeeping (host) ------------------------------------
+    def _ensure_blocks(self, lens_after):
+        """Give every sequence a block for each key group it will hold."""
+        if not self.shape.paged:
+            return
+        changed = False
+        for b, n in enumerate(lens_after):
+            need = num_quantized(int(n), self.G, self.R) // self.G
+            have = int(np.count_nonzero(self._bt_host[b] >= 0))
+            while have < need:
+                if not self._free:
+                    raise KVQError(KVQ_ECAPACITY, "paged cache out of blocks")
+                self._bt_host[b, have] = self._free.pop()
+                have += 1
+                changed = True
+        if changed:
+            self.block_table.copy_(torch.from_numpy(self._bt_host))
+
+    def shuffle_free_blocks(self, seed):
+        """Hand blocks out in a seeded random order (so paged parity tests do
+        not see an accidentally contiguous pool)."""
+        rng = np.random.Generator(np.random.PCG64(seed))
+        self._block_order = [int(i) for i in rng.permutation(self.shape.num_blocks)]
+        self._free = list(self._block_order)
+
+    # -- calls --------------------------------------------------------------
+    def prefill(self, k, v, seq_lens, stream=None):
+        """k, v: fp16 [B][H][max_len][d] on the device; seq_lens: ints [B]."""
+        lens = np.asarray(seq_lens, np.int64)
+        B, H, max_len, d = k.shape
+        if (B, H, d) != (self.shape.num_seqs, self.shape.num_kv_heads, HEAD_DIM) or k.shape != v.shape:
+            raise ValueError("k/v shape %s does not match the cache" % (tuple(k.shape),))
+        if k.dtype != torch.float16 or v.dtype != torch.float16 or not k.is_contiguous() or not v.is_contiguous():
+            raise ValueError("k and v must be contiguous fp16")
+        if np.any(lens < 0) or np.any(lens > max_len) or np.any(lens > self.capacity()):
+            raise ValueError("sequence length outside [0, min(max_len, capacity)]")
+        if self.shape.paged:
+            self._bt_host[:] = -1
+            self._free = list(self._block_order)
+            self._ensure_blocks(lens)
+        sl = torch.as_tensor(lens.astype(np.int32), device=self.device)
+        kv_quantize_prefill(self.cfg, self.cache, k, v, max_len, sl, stream)
+        self.lens = lens.copy()
+        self._keep = sl  # keep alive until the stream has consumed it
+
+    def append(self, k_new, v_new, stream=None):
+        """k_new, v_new: fp16 [B][H][d] on the device."""
+        if np.any(self.lens + 1 > self.capacity()):
+            raise KVQError(KVQ_ECAPACITY, "kv_append_token: a sequence is full")
+        self._ensure_blocks(self.lens + 1)
+        kv_append_token(self.cfg, self.cache, k_new, v_new, stream)
+        self.lens = self.lens + 1
+
+    def dequantize(self, out_tokens=None, stream=None):
+        T = int(out_tokens if out_tokens is not None else max(int(self.lens.max()), 1))
+        B, H = self.shape.num_seqs, self.shape.num_kv_heads
+        ko = torch.empty((B, H, T, HEAD_DIM), dtype=torch.float32, device=self.device)
+        vo = torch.empty_like(ko)
+        kv_dequantize(self.cfg, self.cache, ko, vo, T, stream)
+        return ko, vo
+
+    def export_codes(self, out_tokens=None, stream=None):
+        G = self.G
+        T = int(out_tokens if out_tokens is not None else max(int(self.lens.max()), 1))
+        T = (T + G - 1) // G * G
+        B, H = self.shape.num_seqs, self.shape.num_kv_heads
+        dev = self.device
+        kc = torch.empty((B, H, T, HEAD_DIM), dtype=torch.uint8, device=dev)
+        vc = torch.empty_like(kc)
+        ks = torch.empty((B, H, T // G, HEAD_DIM), dtype=torch.int16, device=dev)
+        kz = torch.empty_like(ks)
+        vs = torch.empty((B, H, T), dtype=torch.int16, device=dev)
+        vz = torch.empty_like(vs)
+        kv_export_codes(self.cfg, self.cache, kc, vc, ks, kz, vs, vz, T, stream)
+        return kc, vc, ks, kz, vs, vz
+
+    def workspace(self, num_q_heads):
+        nb = kv_decode_attention_workspace_bytes(self.cfg, num_q_heads)
+        if nb == 0:
+            raise KVQError(KVQ_EINVAL, "kv_decode_attention_workspace_bytes")
+        if self._ws is None or self._ws.numel() < nb:
+            self._ws = torch.empty(nb, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def decode_attention(self, q, softmax_scale=None, out=None, stream=None):
+        """q: fp16 [B][Hq][d] -> fp32 [B][Hq][d]."""
+        B, Hq, d = q.shape
+        if B != self.shape.num_seqs or d != HEAD_DIM or q.dtype != torch.float16 or not q.is_contiguous():
+            raise ValueError("q must be contiguous fp16 [B][Hq][128]")
+        if softmax_scale is None:
+            softmax_scale = HEAD_DIM ** -0.5
+        if out is None:
+            out = torch.empty((B, Hq, d), dtype=torch.float32, device=self.device)
+        ws = self.workspace(Hq)
+        kv_decode_attention(self.cfg, self.cache, q, Hq, softmax_scale, out, ws, stream)
+        return out

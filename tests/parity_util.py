@@ -1,0 +1,121 @@
+"""Helpers of the GPU parity tests: run the HIP path through the C ABI, run
+the oracle on the same seeded inputs, compare.
+
+The bar: codes, scales, zeros and dequantized values bit-exact; attention
+within max-abs 2e-3 of the oracle (fp64) with per-row cosine >= 0.9999.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import torch
+
+import oracle
+from quantized_decode_attention_kivi_amd import kvq, synth
+
+ATOL = 2e-3
+MIN_COS = 0.9999
+THREADS = min(16, os.cpu_count() or 1)
+
+
+def make_cache(w: synth.Workload, lens, max_tokens=None, num_blocks=None, shuffle_seed=None):
+    G, R = w.group_size, w.residual
+    if w.paged:
+        mb = max(1, (int(np.max(lens)) + 64 - R) // G + 1)
+        nb = num_blocks if num_blocks is not None else int(sum(kvq.num_quantized(int(n) + 64, G, R) // G
+                                                               for n in lens)) + 4
+        shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, G, R, paged=True,
+                               num_blocks=nb, max_blocks_per_seq=mb)
+    else:
+        shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, G, R,
+                               max_tokens=max_tokens if max_tokens is not None else int(np.max(lens)) + 64)
+    c = kvq.QuantizedKVCache(shape)
+    if w.paged and shuffle_seed is not None:
+        c.shuffle_free_blocks(shuffle_seed)
+    return c
+
+
+def oracle_states(kb: np.ndarray, vb: np.ndarray, lens, w: synth.Workload, cap=None):
+    """kb, vb: uint16 [B][H][L][d] -> StreamState per (b, h)."""
+    return oracle.prefill_batch(kb, vb, lens, w.k_bits, w.v_bits, w.group_size, w.residual,
+                                cap=cap, threads=THREADS)
+
+
+def compare_codes(cache: kvq.QuantizedKVCache, states, streams=None):
+    """Bit-exact comparison of codes, scales, zeros and dequantized values."""
+    torch.cuda.synchronize()
+    T = max(int(cache.lens.max()), 1)
+    kc, vc, ks, kz, vs, vz = [t.cpu().numpy() for t in cache.export_codes(T)]
+    ks, kz, vs, vz = (a.view(np.uint16) for a in (ks, kz, vs, vz))
+    kd, vd = [t.cpu().numpy() for t in cache.dequantize(T)]
+    nt = cache.n_tokens.cpu().numpy()
+    nqs = cache.n_quant.cpu().numpy()
+    G = cache.G
+    B, H = kc.shape[:2]
+    streams = streams if streams is not None else [(b, h) for b in range(B) for h in range(H)]
+    for b, h in streams:
+        st = states[b][h]
+        assert nt[b] == st.n and nqs[b] == st.nq, (b, nt[b], st.n, nqs[b], st.nq)
+        nq, n = st.nq, st.n
+        assert np.array_equal(kc[b, h, :nq], st.key_codes()), ("key codes", b, h)
+        assert np.array_equal(vc[b, h, :nq], st.value_codes()), ("value codes", b, h)
+        oks, okz = st.key_meta()
+        assert np.array_equal(ks[b, h, :nq // G], oks), ("key scales", b, h)
+        assert np.array_equal(kz[b, h, :nq // G], okz), ("key zeros", b, h)
+        ovs, ovz = st.value_meta()
+        assert np.array_equal(vs[b, h, :nq], ovs), ("value scales", b, h)
+        assert np.array_equal(vz[b, h, :nq], ovz), ("value zeros", b, h)
+        okd, ovd = st.dequantize()
+        assert np.array_equal(kd[b, h, :n], okd), ("dequantized keys", b, h)
+        assert np.array_equal(vd[b, h, :n], ovd), ("dequantized values", b, h)
+        assert np.all(kd[b, h, n:] == 0) and np.all(vd[b, h, n:] == 0)
+
+
+def oracle_attention(q16: np.ndarray, states, scale, rows=None):
+    """q16: uint16 fp16 bits [B][Hq][d] -> fp64 [B][Hq][d] (rows: list of
+    (b, hq) to compute, others NaN)."""
+    qf = oracle.h2f(q16)
+    B, Hq, d = qf.shape
+    H = len(states[0])
+    gq = Hq // H
+    out = np.full((B, Hq, d), np.nan)
+    if rows is None:
+        return oracle.decode_attention_batch(qf, states, scale, threads=THREADS)
+    from concurrent.futures import ThreadPoolExecutor
+    by_stream = {}
+    for b, hq in rows:
+        by_stream.setdefault((b, hq // gq), []).append(hq)
+
+    def one(item):
+        (b, h), hqs = item
+        kh, vh = states[b][h].dequantize()
+        o = oracle.attention(qf[b, hqs], kh, vh, scale)
+        for i, hq in enumerate(hqs):
+            out[b, hq] = o[i]
+
+    with ThreadPoolExecutor(THREADS) as ex:
+        list(ex.map(one, by_stream.items()))
+    return out
+
+
+def compare_attention(got: np.ndarray, ref: np.ndarray, rows=None):
+    got = got.astype(np.float64)
+    if rows is not None:
+        idx = tuple(np.array(rows).T)
+        got, ref = got[idx], ref[idx]
+    else:
+        got = got.reshape(-1, got.shape[-1])
+        ref = ref.reshape(-1, ref.shape[-1])
+    err = np.abs(got - ref).max()
+    ng = np.linalg.norm(got, axis=-1)
+    nr = np.linalg.norm(ref, axis=-1)
+    both_zero = (ng == 0) & (nr == 0)
+    cos = np.where(both_zero, 1.0, (got * ref).sum(-1) / np.maximum(ng * nr, 1e-300))
+    assert err <= ATOL, "max abs error %.3g > %.1g" % (err, ATOL)
+    assert cos.min() >= MIN_COS, "min row cosine %.8f < %.4f" % (cos.min(), MIN_COS)
+    return err, float(cos.min())
+
+
+def to_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy().view(np.uint16)
