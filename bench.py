@@ -1,0 +1,326 @@
+"""Benchmark of the quantized decode path on one MI355X.
+
+One step is one decode step of the serving loop on one batch: append the new
+token of every (sequence, kv head) to the fp16 residual (kv_append_token; on
+every G-th step the oldest G residual tokens are quantized and leave the
+ring) followed by decode attention of one query token per sequence over the
+whole cache (kv_decode_attention: quantized part dequantized in-kernel,
+fp16 residual, split merge).  Bulk quantization of the prompt
+(kv_quantize_prefill) runs once per request, so it is timed as its own leg
+over the same batch and reported as the quantize rate.
+
+Timing is taken with HIP events recorded on the stream the kernels run on.
+Every step reads a different copy of the packed cache (enough copies to
+exceed the 256 MB last-level cache), so the reads measured come from HBM as
+they would inside a multi-layer decode step.
+
+Prints ONE JSON line.  `value` is the decode attention's effective bandwidth:
+algorithmic bytes of one launch (packed codes, scale/zero pairs, fp16
+residual, query and output) divided by its average event-timed duration.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
+MALL_BYTES = 256 << 20         # last-level (Infinity) cache
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+ATTN_KERNEL_SOURCES = ["quantized_decode_attention_kivi_amd/csrc/kvq_attn.hip",
+                       "quantized_decode_attention_kivi_amd/csrc/kvq_device.h",
+                       "quantized_decode_attention_kivi_amd/csrc/kvq_internal.h"]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="llama3_8b_layer_b8_32k_int4")
+    ap.add_argument("--prefill-reps", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=0, help="cache copies rotated per step (0: auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-baseline sample")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic byte counts (what the method must move at minimum)
+# ---------------------------------------------------------------------------
+
+def n_quant(n, G, R):
+    return 0 if n <= R else G * ((n - R) // G)
+
+
+def attention_bytes(lens, w, d=128):
+    """Bytes one decode-attention launch must read/write: per (sequence, kv
+    head) the packed key/value codes of the n_q quantized tokens, one fp16
+    (scale, zero) pair per (key group, channel) and per value token, the fp16
+    residual keys and values; per sequence the fp16 query and fp32 output."""
+    tot = 0
+    for n in lens:
+        nq = n_quant(int(n), w.group_size, w.residual)
+        per_head = (nq * d * (w.k_bits + w.v_bits) // 8 + (nq // w.group_size) * d * 4 + nq * 4
+                    + (int(n) - nq) * d * 2 * 2)
+        tot += w.num_kv_heads * per_head + w.num_q_heads * d * (2 + 4)
+    return tot
+
+
+def prefill_bytes(lens, w, d=128):
+    """fp16 K and V read, packed records and fp16 residual written."""
+    tot = 0
+    for n in lens:
+        nq = n_quant(int(n), w.group_size, w.residual)
+        tot += w.num_kv_heads * (int(n) * d * 2 * 2 + nq * d * (w.k_bits + w.v_bits) // 8
+                                 + (nq // w.group_size) * d * 4 + nq * 4 + (int(n) - nq) * d * 2 * 2)
+    return tot
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload, digest):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILE_DIR, "attn_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get(workload)
+    if not ent or ent.get("kernel_source_sha256_16") != digest:
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(w, K, V, q, lens, budget_s):
+    """Time the oracle (quantize the streams, then dequantize + fp64 attention)
+    on whole (sequence, kv-head) streams of the workload until about
+    budget_s seconds of CPU work are spent; report the oracle's decode
+    attention rate in the bench's unit (effective GB/s over the same
+    algorithmic bytes) and its quantize rate."""
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    B, H = w.num_seqs, w.num_kv_heads
+    gq = w.gq
+    jobs = [(b, h) for b in range(B) for h in range(H)]
+    done = []
+    qf = oracle.h2f(q.cpu().numpy().view(np.uint16))
+    scale = 128 ** -0.5
+
+    def one(bh):
+        b, h = bh
+        n = int(lens[b])
+        kx = K[b, h, :n].cpu().numpy().view(np.uint16)
+        vx = V[b, h, :n].cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        st = oracle.StreamState.prefill(kx, vx, w.k_bits, w.v_bits, w.group_size, w.residual)
+        t1 = time.perf_counter()
+        kh, vh = st.dequantize()
+        oracle.attention(qf[b, h * gq:(h + 1) * gq], kh, vh, scale)
+        t2 = time.perf_counter()
+        return t1 - t0, t2 - t1
+
+    wall0 = time.perf_counter()
+    attn_wall = 0.0
+    quant_wall = 0.0
+    with ThreadPoolExecutor(threads) as ex:
+        i = 0
+        while i < len(jobs) and time.perf_counter() - wall0 < budget_s:
+            batch = jobs[i:i + threads]
+            tb = time.perf_counter()
+            res = list(ex.map(one, batch))
+            te = time.perf_counter()
+            # wall time of the batch split between the two legs in proportion
+            # to the summed per-thread times
+            sq = sum(r[0] for r in res)
+            sa = sum(r[1] for r in res)
+            quant_wall += (te - tb) * sq / max(sq + sa, 1e-12)
+            attn_wall += (te - tb) * sa / max(sq + sa, 1e-12)
+            done.extend(batch)
+            i += len(batch)
+    # algorithmic bytes of the sampled streams (query/output shares included)
+    sb = 0
+    stok = 0
+    for b, h in done:
+        n = int(lens[b])
+        nq = n_quant(n, w.group_size, w.residual)
+        sb += (nq * 128 * (w.k_bits + w.v_bits) // 8 + (nq // w.group_size) * 128 * 4 + nq * 4
+               + (n - nq) * 128 * 4 + gq * 128 * 6)
+        stok += n
+    return {
+        "value": round(sb / attn_wall / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d of %d (sequence, kv head) streams of %s, each quantized then dequantized and "
+                  "attended by its %d query heads in fp64 (%.1f s wall)" % (
+                      len(done), len(jobs), w.name, gq, time.perf_counter() - wall0),
+        "quantize_tokens_per_s": round(stok / w.num_kv_heads / quant_wall, 1),
+        "host_cpus": os.cpu_count(),
+    }
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the quantized decode path runs on a single "
+              "MI355X here (multi-GPU sharding is a design note, not built); got --gpus %d" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from quantized_decode_attention_kivi_amd import kvq, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    kvq.lib()  # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    w = synth.WORKLOADS[args.workload]
+    if w.paged or w.layers != 1:
+        print("bench.py times the contiguous single-layer workloads", file=sys.stderr)
+        sys.exit(2)
+    lens = synth.seq_lengths(w).astype(np.int64)
+    L = int(lens.max())
+    print("# generating %s: B=%d Hkv=%d Hq=%d n=%d k%d/v%d G=%d R=%d" % (
+        w.name, w.num_seqs, w.num_kv_heads, w.num_q_heads, L, w.k_bits, w.v_bits, w.group_size, w.residual),
+        file=sys.stderr, flush=True)
+    K, V = synth.make_kv(w, max_len=L, device=dev)
+    q = synth.make_query(w, device=dev)
+    total_steps = args.warmup + args.steps
+    toks = [synth.make_tokens(w, s, device=dev) for s in range(total_steps)]
+
+    abytes = attention_bytes(lens, w)
+    copies = args.copies or min(64, max(2, math.ceil(2 * MALL_BYTES / abytes)))
+    shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, w.group_size, w.residual,
+                           max_tokens=L + total_steps + 8)
+    caches = [kvq.QuantizedKVCache(shape, device=dev) for _ in range(copies)]
+    stream = torch.cuda.current_stream()
+
+    # ---- prefill (bulk quantize) leg ------------------------------------
+    pre_ms = []
+    lens_dev = torch.as_tensor(lens.astype(np.int32), device=dev)
+    for r in range(args.prefill_reps + 1):
+        for c in caches:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            c.prefill(K, V, lens, seq_lens_device=lens_dev)
+            e1.record(stream)
+            if r > 0:
+                pre_ms.append((e0, e1))
+    torch.cuda.synchronize()
+    pre_t = float(np.mean([a.elapsed_time(b) for a, b in pre_ms]))
+    pbytes = prefill_bytes(lens, w)
+
+    # ---- decode steps ---------------------------------------------------
+    outs = [torch.empty((w.num_seqs, w.num_q_heads, 128), dtype=torch.float32, device=dev) for _ in caches]
+    for c in caches:
+        c.workspace(w.num_q_heads)
+
+    def step(s, ev=None):
+        c = caches[s % copies]
+        kn, vn = toks[s]
+        c.append(kn, vn)
+        if ev is not None:
+            ev[0].record(stream)
+        c.decode_attention(q, out=outs[s % copies])
+        if ev is not None:
+            ev[1].record(stream)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    # attention bytes at each timed step (lengths grow by one per step)
+    step_bytes = []
+    for i in range(args.steps):
+        s = args.warmup + i
+        cnt = s // copies + 1  # appends this copy has seen once step s is done
+        step_bytes.append(attention_bytes(lens + cnt, w))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    attn_avg_s = float(attn_ms.mean()) / 1e3
+    bytes_avg = float(np.mean(step_bytes))
+    achieved = bytes_avg / attn_avg_s / 1e9
+    ms_per_step = wall / args.steps * 1e3
+
+    digest = source_digest(ATTN_KERNEL_SOURCES)
+    traffic = recorded_traffic(w.name, digest)
+    res = {
+        "metric": "quantized decode-attention effective HBM GB/s (% of peak); quantize tokens/s",
+        "value": round(achieved, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 (int%d keys / int%d values, fp16 scale/zero and residual)" % (w.k_bits, w.v_bits),
+        "data": "synthetic (seeded N(0,1) K/V, 4 key outlier channels x20 per head, 1% value rows x5)",
+        "config": {
+            "workload": w.name,
+            "num_seqs": w.num_seqs, "context": L, "num_q_heads": w.num_q_heads,
+            "num_kv_heads": w.num_kv_heads, "head_dim": 128, "k_bits": w.k_bits, "v_bits": w.v_bits,
+            "group_size": w.group_size, "residual": w.residual, "cache_copies_rotated": copies,
+        },
+        "pct_of_hbm_peak": round(100.0 * achieved / HBM_PEAK_GBS, 2),
+        "attention_us": round(attn_avg_s * 1e6, 3),
+        "attention_us_median": round(float(np.median(attn_ms)) * 1e3, 3),
+        "attention_bytes_per_launch": int(bytes_avg),
+        "quantize_tokens_per_s": round(float(lens.sum()) / (pre_t / 1e3), 1),
+        "quantize_gbs": round(pbytes / (pre_t / 1e3) / 1e9, 2),
+        "quantize_us": round(pre_t * 1e3, 3),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "kv_decode_attention",
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, K, V, q, lens, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -244,8 +244,10 @@ class QuantizedKVCache:
         self._free = list(self._block_order)
 
     # -- calls --------------------------------------------------------------
-    def prefill(self, k, v, seq_lens, stream=None):
-        """k, v: fp16 [B][H][max_len][d] on the device; seq_lens: ints [B]."""
+    def prefill(self, k, v, seq_lens, stream=None, seq_lens_device=None):
+        """k, v: fp16 [B][H][max_len][d] on the device; seq_lens: ints [B]
+        (host).  seq_lens_device: optional int32 device copy of seq_lens,
+        reused instead of a fresh host-to-device copy."""
         lens = np.asarray(seq_lens, np.int64)
         B, H, max_len, d = k.shape
         if (B, H, d) != (self.shape.num_seqs, self.shape.num_kv_heads, HEAD_DIM) or k.shape != v.shape:
@@ -258,7 +260,9 @@ class QuantizedKVCache:
             self._bt_host[:] = -1
             self._free = list(self._block_order)
             self._ensure_blocks(lens)
-        sl = torch.as_tensor(lens.astype(np.int32), device=self.device)
+        sl = seq_lens_device
+        if sl is None:
+            sl = torch.as_tensor(lens.astype(np.int32), device=self.device)
         kv_quantize_prefill(self.cfg, self.cache, k, v, max_len, sl, stream)
         self.lens = lens.copy()
         self._keep = sl  # keep alive until the stream has consumed it
