@@ -70,7 +70,7 @@ typedef struct kvq_config {
     int32_t head_dim;           /* d, must be 128                                */
     int32_t k_bits;             /* key code width: 2 or 4                        */
     int32_t v_bits;             /* value code width: 2 or 4                      */
-    int32_t group_size;         /* G: 16, 32 or 64 tokens per key group          */
+    int32_t group_size;         /* G: 16 or 32 tokens per key group              */
     int32_t residual;           /* R >= 0, a multiple of G                       */
     int32_t max_tokens;         /* contiguous mode: per-sequence capacity        */
     int32_t block_size;         /* 0 = contiguous; otherwise paged, == G         */
@@ -92,8 +92,10 @@ typedef struct kvq_cache {
 
 /* Byte sizes of the buffers of kvq_cache and of one group record.
  * Record = one (key group, kv head): G*d*k_bits/8 key-code bytes,
- * G*d*v_bits/8 value-code bytes, d fp16 (s, z) key pairs and G fp16 (s, z)
- * value pairs.  Contiguous mode holds B*H*floor(max(0,max_tokens-R)/G)
+ * G*d*v_bits/8 value-code bytes, d fp16 key scales and d fp16 key zeros,
+ * G fp16 value scales and G fp16 value zeros, arranged inside the record in
+ * the order the decode kernel consumes them (an internal format: use
+ * kv_export_codes / kv_dequantize for a logical view).  Contiguous mode holds B*H*floor(max(0,max_tokens-R)/G)
  * records; paged mode holds num_blocks*H records. */
 typedef struct kvq_sizes {
     size_t packed_bytes;
@@ -153,9 +155,16 @@ size_t kv_decode_attention_workspace_bytes(const kvq_config *cfg, int32_t num_q_
  * dequantizes while it reads, the quantized part and the full-precision
  * residual are computed separately and merged).  q: fp16 [B][Hq][d];
  * out: fp32 [B][Hq][d]; Hq a multiple of H with Hq/H <= 16; softmax_scale is
- * normally 1/sqrt(d).  workspace: device memory of at least
- * kv_decode_attention_workspace_bytes(cfg, Hq) bytes, used for per-split
- * partial results; its content need not be preserved between calls. */
+ * normally 1/sqrt(d).  q must be 16-byte aligned.  The products
+ * |q[c]| * s[c] of a query element and its key group's channel scale must
+ * stay below 65504 (they are formed in fp16; true for any query of O(1..100)
+ * against keys whose per-group range is below ~1000).
+ * workspace: 256-byte aligned device memory of at least
+ * kv_decode_attention_workspace_bytes(cfg, Hq) bytes holding per-split
+ * partial results and merge counters.  It must be zero-filled before its
+ * first use; every call returns the counters to zero, so one zeroed
+ * workspace serves any sequence of calls (of any configuration that fits)
+ * as long as calls sharing it are ordered on one stream. */
 kvq_status kv_decode_attention(const kvq_config *cfg, const kvq_cache *cache,
                                const void *q, int32_t num_q_heads, float softmax_scale,
                                float *out, void *workspace, size_t workspace_bytes,

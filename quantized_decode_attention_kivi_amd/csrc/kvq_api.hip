@@ -22,7 +22,7 @@ kvq_status make_layout(const kvq_config* cfg, Layout* L) {
     if (cfg->head_dim != kD) return KVQ_EUNSUPPORTED;
     if ((cfg->k_bits != 2 && cfg->k_bits != 4) || (cfg->v_bits != 2 && cfg->v_bits != 4)) return KVQ_EUNSUPPORTED;
     const int G = cfg->group_size;
-    if (G != 16 && G != 32 && G != 64) return KVQ_EUNSUPPORTED;
+    if (G != 16 && G != 32) return KVQ_EUNSUPPORTED;
     if (cfg->residual < 0 || cfg->residual % G != 0) return KVQ_EINVAL;
     if (cfg->residual > (1 << 20)) return KVQ_EINVAL;
     L->B = cfg->num_seqs;
@@ -48,6 +48,7 @@ kvq_status make_layout(const kvq_config* cfg, Layout* L) {
         L->groups = num_quantized(cfg->max_tokens, G, L->R) / G;
         L->capacity = cfg->max_tokens;
     }
+    L->spt = G == 16 ? 4 : 8;
     L->kcode = G * kD * L->kbits / 8;
     L->vcode = G * kD * L->vbits / 8;
     L->vcode_off = L->kcode;
@@ -95,7 +96,7 @@ kvq_status kv_quantize_prefill(const kvq_config* cfg, const kvq_cache* cache, co
     if (st != KVQ_OK) return st;
     if ((st = check_cache(L, cache)) != KVQ_OK) return st;
     if (!k || !v || !seq_lens || max_len < 0) return KVQ_EINVAL;
-    if (((uintptr_t)k & 3) || ((uintptr_t)v & 3)) return KVQ_EINVAL;
+    if (((uintptr_t)k & 15) || ((uintptr_t)v & 15)) return KVQ_EINVAL;
     return hip_status(launch_prefill(L, *cache, (const _Float16*)k, (const _Float16*)v, max_len, seq_lens,
                                      (hipStream_t)stream));
 }
@@ -135,10 +136,10 @@ kvq_status kv_decode_attention(const kvq_config* cfg, const kvq_cache* cache, co
     kvq_status st = make_layout(cfg, &L);
     if (st != KVQ_OK) return st;
     if ((st = check_cache(L, cache)) != KVQ_OK) return st;
-    if (!q || !out || !workspace || ((uintptr_t)q & 3) || ((uintptr_t)workspace & 15)) return KVQ_EINVAL;
+    if (!q || !out || !workspace || ((uintptr_t)q & 15) || ((uintptr_t)workspace & 255)) return KVQ_EINVAL;
     if (num_q_heads < L.H || num_q_heads % L.H) return KVQ_EINVAL;
     const int gq = num_q_heads / L.H;
-    if (gq != 1 && gq != 2 && gq != 4 && gq != 8 && gq != 16) return KVQ_EUNSUPPORTED;
+    if (gq < 1 || gq > kMaxGq) return KVQ_EUNSUPPORTED;
     if (!(softmax_scale > 0.0f) || softmax_scale > 1e30f) return KVQ_EINVAL;
     const AttnPlan P = plan_attention(L, num_q_heads);
     if (workspace_bytes < P.workspace) return KVQ_ECAPACITY;

@@ -8,23 +8,40 @@
 // residual tokens.  The kernel dequantizes while it reads; the quantized part
 // and the residual are processed by different workgroups and merged.
 //
-// Dequantization is folded into the arithmetic instead of materialised:
-//   q . k_t  = sum_c (q_c s_c) code_tc + sum_c q_c z_c        (key group scales)
-//   sum_t p_t v_t = sum_t (p_t s_t) code_t + (sum_t p_t z_t)    (value token scales)
-// so each packed code costs one multiply-add per query head.  All query heads
-// of one kv head (the GQA group) are served by the same workgroup, so every
-// packed byte is read from HBM once per step.
+// Dequantization is folded into the contractions instead of materialised:
+//   q . k_t      = sum_c (q_c s_c) code_tc + sum_c q_c z_c        (key group)
+//   sum_t p_t v_t = sum_t (p_t s_t) code_t + sum_t p_t z_t        (value tokens)
+// For one kv head and 32 tokens both are small dense products between the
+// query heads of the GQA group (up to 16, padded to 16) and the codes, so they
+// run on the matrix cores (v_mfma_f32_16x16x32_f16, fp32 accumulation):
+//   keys:   C[token][head]  = codes[token][c] . (q s)[c][head]
+//   values: acc[head][c]   += (p s)[head][token] . codes[token][c]
+// Codes are exact small integers in fp16.  q s is the exact product of two
+// fp16 numbers (22 significant bits), so it is split exactly into an fp16
+// high and low part and contracted twice; p s is split the same way (to 22
+// bits).  The key zero points enter as one more product, z[c] . q[c][head],
+// whose result seeds the key accumulator.  The vector ALU only unpacks codes
+// and runs the online softmax.
 //
-// Split-K: each stream (b, kv head) is cut into `splits` ranges of key groups
-// plus one workgroup for the residual ring; each writes (m, l, acc) partials,
-// which attn_merge_kernel combines by log-sum-exp.
+// Work split: each stream (b, kv head) is cut into `splits` ranges of 32-token
+// units plus one workgroup for the fp16 residual ring.  Waves walk their units
+// independently (two units in flight per wave), combine in LDS, and every
+// workgroup writes a partial (max, sum, output) to the workspace.  A second,
+// small kernel merges the partials of each (stream, head) by log-sum-exp.
+// The kernel boundary makes the partials visible to it; a per-workgroup
+// device-scope release would write back the XCD's L2 once per workgroup.
 #include "kvq_device.h"
 
 namespace kvq {
 
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
 constexpr int kWaves = 4;
-constexpr int kPartStride = kD + 2;   // partial: acc[128], m, l
+constexpr int kPart = kD + 4;          // floats per head in a partial: out[128], m, l, pad
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -32,362 +49,506 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    return x;
+__device__ __forceinline__ h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
+__device__ __forceinline__ uint32_t as_u32(h2 x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ h8 make_h8(h2 a, h2 b, h2 c, h2 d) {
+    return h8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
-__device__ __forceinline__ float wave_sum(float x) {
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-    return x;
+__device__ __forceinline__ h8 words_h8(uint4 w) {
+    return make_h8(as_h2(w.x), as_h2(w.y), as_h2(w.z), as_h2(w.w));
 }
 
-template <int GQ>
-struct AttnSmem {
-    float qt[kWaves][GQ][4][36];   // per wave: folded query (or raw query for the residual)
-    float w[kWaves][GQ][16];       // per wave: p_t * s_t of the current 16 tokens
-    float m[kWaves][GQ], l[kWaves][GQ], pz[kWaves][GQ];
+// Max over the four lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float group_max(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    x = fmaxf(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
+    const uint32_t v = __builtin_bit_cast(uint32_t, x);
+    auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
+}
+__device__ __forceinline__ float group_sum(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    x = __builtin_bit_cast(float, (uint32_t)a[0]) + __builtin_bit_cast(float, (uint32_t)a[1]);
+    const uint32_t v = __builtin_bit_cast(uint32_t, x);
+    auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return __builtin_bit_cast(float, (uint32_t)b[0]) + __builtin_bit_cast(float, (uint32_t)b[1]);
+}
+
+// Code unpacking (word layout: code_bit()).  INT4: byte-spread nibbles read as
+// fp8 e4m3 are c * 2^-9 (exact, subnormals included), scaled by 512.  INT2:
+// codes 0..3 in the low bits of a nibble read as fp4 e2m1 are c / 2, scaled by 2.
+__device__ __forceinline__ h8 unpack4(uint32_t w) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    return make_h8(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false),
+                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true),
+                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, false),
+                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, true));
+}
+__device__ __forceinline__ h8 unpack2_half(uint32_t w, bool upper) {
+    const uint32_t x = (upper ? (w >> 2) : w) & 0x33333333u;
+    return make_h8(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 0),
+                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 1),
+                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 2),
+                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 3));
+}
+// Codes 8j..8j+7 of a lane's code sequence held in words w[].
+template <int BITS>
+__device__ __forceinline__ h8 codes8(const uint32_t* w, int j) {
+    if (BITS == 4) return unpack4(w[j]);
+    return unpack2_half(w[j >> 1], j & 1);
+}
+
+__device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Raw loads of one 32-token unit: NR records (1 for G = 32, 2 for G = 16).
+template <int G, int KB, int VB>
+struct UnitRaw {
+    static constexpr int NR = 32 / G;
+    static constexpr int SPT = G == 16 ? 4 : 8;
+    static constexpr int VW = SPT * VB / 4;    // value words per lane and record
+    uint32_t kc[2][KB];                        // per row tile: this lane's 32 key codes
+    uint32_t vc[NR][VW];                       // per record: this lane's value codes
+    uint2 km[NR];                              // per record: 8 bytes of key meta
+    uint4 vm[NR];                              // per record: 16 bytes of value meta (some lanes)
+    bool has[NR];
 };
 
-// Per-wave online-softmax state.  Values in log2 units (query pre-scaled by
-// scale * log2(e)), so exp2 is the exponential.
-template <int GQ>
-struct WaveState {
-    float m[GQ], l[GQ], pz[GQ];
-    float2 acc[GQ];   // channels 2*lane, 2*lane+1
-};
-
-// Update with the logits lg[hh] of 16 tokens held by lanes (token tl = lane/4,
-// part = lane%4; all 4 parts hold the same value).  valid: token exists.
-// vs, vz: value scale/zero of the lane's token.  Writes w = p*s to LDS.
-template <int GQ>
-__device__ __forceinline__ void softmax_16(WaveState<GQ>& st, float (&lg)[GQ], bool valid, float vs, float vz,
-                                           float (*wbuf)[16], int tl, int part) {
+template <int G, int KB, int VB>
+__device__ __forceinline__ void load_unit(UnitRaw<G, KB, VB>& r, const Layout& L, const kvq_cache& c, int b, int h,
+                                          int unit, int ngroups, int lane) {
+    // Branch-free: a missing record (odd group count, bad block id) is read
+    // from the pool's first record and its slots are masked later (weights and
+    // value zeros of invalid slots are forced to 0), so every call issues the
+    // same loads and the wait counts stay exact.  Codes are small integers
+    // whatever the bytes, so masked operands stay finite.
+    using R = UnitRaw<G, KB, VB>;
+    const int g = lane >> 4, n = lane & 15;
 #pragma unroll
-    for (int hh = 0; hh < GQ; ++hh) {
-        const float x = valid ? lg[hh] : -INFINITY;
-        const float mp = wave_max(x);
-        const float mnew = fmaxf(st.m[hh], mp);
-        float alpha, p;
-        if (mnew == -INFINITY) {
-            alpha = 1.0f;
-            p = 0.0f;
-        } else {
-            alpha = exp2f(st.m[hh] - mnew);
-            p = valid ? exp2f(x - mnew) : 0.0f;
+    for (int i = 0; i < R::NR; ++i) {
+        const int grp = unit * R::NR + i;
+        const uint8_t* rec = grp < ngroups ? record_at(L, c.packed, c.block_table, b, h, grp) : nullptr;
+        const bool ok = rec != nullptr;
+        r.has[i] = ok;
+        if (!ok) rec = (const uint8_t*)c.packed;
+        r.km[i] = *(const uint2*)(rec + L.kmeta_off + 8 * lane);
+        r.vm[i] = *(const uint4*)(rec + L.vmeta_off + 16 * (lane < G / 4 ? lane : 0));
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            if (R::NR == 2 && rt != i) continue;
+            const int t = R::NR == 2 ? n : 16 * rt + n;
+            const uint8_t* p = rec + t * 16 * KB + 4 * KB * g;
+            if (KB == 4) {
+                const uint4 x = *(const uint4*)p;
+                r.kc[rt][0] = x.x; r.kc[rt][1] = x.y; r.kc[rt][2] = x.z; r.kc[rt][3] = x.w;
+            } else {
+                const uint2 x = *(const uint2*)p;
+                r.kc[rt][0] = x.x; r.kc[rt][1] = x.y;
+            }
         }
-        st.m[hh] = mnew;
-        st.l[hh] = st.l[hh] * alpha + (part == 0 ? p : 0.0f);
-        st.pz[hh] = st.pz[hh] * alpha + (part == 0 ? p * vz : 0.0f);
-        st.acc[hh].x *= alpha;
-        st.acc[hh].y *= alpha;
-        if (part == 0) wbuf[hh][tl] = p * vs;
-    }
-}
-
-template <int KB>
-__device__ __forceinline__ float kcode(const uint4& u, int i) {
-    if (KB == 2) {
-        const uint32_t w = i < 16 ? u.x : u.y;
-        return (float)((w >> ((i & 15) * 2)) & 3u);
-    } else {
-        const uint32_t w = i < 8 ? u.x : (i < 16 ? u.y : (i < 24 ? u.z : u.w));
-        return (float)((w >> ((i & 7) * 4)) & 15u);
-    }
-}
-
-template <int GQ, int KB, int VB>
-__device__ void attend_group(AttnSmem<GQ>& sm, WaveState<GQ>& st, const Layout& L, const uint8_t* __restrict__ rec,
-                             const float2 (&qs)[GQ], int wave, int lane) {
-    const int tl = lane >> 2, part = lane & 3;
-    // Fold the group's key scales into the query; key zeros give a per-head bias.
-    const uint2 km = *(const uint2*)(rec + L.kmeta_off + 8 * lane);
-    const float s0 = h2f(km.x & 0xffffu), z0 = h2f(km.x >> 16);
-    const float s1 = h2f(km.y & 0xffffu), z1 = h2f(km.y >> 16);
-    float bias[GQ];
+        const uint8_t* pv = rec + L.vcode_off + lane * R::VW * 4;
 #pragma unroll
-    for (int hh = 0; hh < GQ; ++hh) {
-        *(float2*)&sm.qt[wave][hh][lane >> 4][(2 * lane) & 31] = make_float2(qs[hh].x * s0, qs[hh].y * s1);
-        bias[hh] = wave_sum(qs[hh].x * z0 + qs[hh].y * z1);
+        for (int w = 0; w < R::VW; w += 4) {
+            if (w + 4 <= R::VW) {
+                const uint4 x = *(const uint4*)(pv + 4 * w);
+                r.vc[i][w] = x.x; r.vc[i][w + 1] = x.y; r.vc[i][w + 2] = x.z; r.vc[i][w + 3] = x.w;
+            } else {
+                const uint2 x = *(const uint2*)(pv + 4 * w);
+                r.vc[i][w] = x.x; r.vc[i][w + 1] = x.y;
+            }
+        }
+    }
+}
+
+// Per-wave online-softmax state and value accumulators.
+struct WaveAcc {
+    f4 acc[8];        // acc[ct][i]: head 4g+i, channel 16ct+n
+    float m;          // running max of head n (log2 units), same in all lane groups
+    float l, pz;      // this lane's share of sum p and sum p*z for head n
+};
+
+__device__ __forceinline__ void acc_init(WaveAcc& A) {
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) A.acc[ct] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    A.m = kNegInf;
+    A.l = 0.0f;
+    A.pz = 0.0f;
+}
+
+// Online-softmax step over the 8 logits x[] (raw q.k, slot order) of this
+// lane's head, then the value contraction with operands vop(ct).  vs/vz: value
+// scale/zero of each slot; valid: slot holds a token.
+template <typename VOp>
+__device__ __forceinline__ void softmax_and_values(WaveAcc& A, const float (&x)[8], const float (&vs)[8],
+                                                   const float (&vz)[8], const bool (&valid)[8], float sl2,
+                                                   int lane, VOp vop) {
+    float cm = kNegInf;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) cm = valid[k] ? fmaxf(cm, x[k]) : cm;
+    cm = group_max(cm);
+    const float mnew = fmaxf(A.m, cm * sl2);
+    const float alpha = mnew == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(A.m - mnew);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+        // rows of acc are heads 4g+i; head j's alpha lives in lanes with n == j
+        const int base = (lane & 48) | ((lane >> 4) << 2);
+        float ai[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, base + i);
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) A.acc[ct][i] *= ai[i];
+        A.l *= alpha;
+        A.pz *= alpha;
+    }
+    A.m = mnew;
+    float w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        // invalid slots (masked tokens, missing records) contribute nothing,
+        // whatever their (possibly non-finite) scale and zero bits
+        const float p = valid[k] ? __builtin_amdgcn_exp2f(fmaf(x[k], sl2, -mnew)) : 0.0f;
+        A.l += p;
+        A.pz = valid[k] ? fmaf(p, vz[k], A.pz) : A.pz;
+        w[k] = valid[k] ? p * vs[k] : 0.0f;
+    }
+    // exact-to-22-bit split of the weights into two fp16 operands
+    h8 whi, wlo;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const _Float16 hi = (_Float16)w[k];
+        whi[k] = hi;
+        wlo[k] = (_Float16)(w[k] - (float)hi);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+        const h8 bop = vop(ct);
+        A.acc[ct] = mfma(whi, bop, A.acc[ct]);
+        A.acc[ct] = mfma(wlo, bop, A.acc[ct]);
+    }
+}
+
+template <int G>
+struct AttnSmem {
+    // per wave: key meta (2 records x 512 B) and value meta (2 records x 128 B)
+    uint32_t kmeta[kWaves][2][kD];
+    uint32_t vmeta[kWaves][2][32];
+    float wm[kWaves][16], wl[kWaves][16], wpz[kWaves][16];
+    float wacc[kWaves][16][kD];
+};
+
+// Query operand of lane (g, n): q[head n][32g + 8j + e], zero for heads >= gq.
+struct QOps {
+    h8 q[4];
+};
+
+template <int G, int KB, int VB>
+__device__ __forceinline__ void process_unit(AttnSmem<G>& sm, WaveAcc& A, const UnitRaw<G, KB, VB>& r,
+                                             const QOps& Q, float sl2, int wave, int lane) {
+    using R = UnitRaw<G, KB, VB>;
+    constexpr int SPT = R::SPT;
+    const int g = lane >> 4;
+    // stage the records' scale/zero tables
+#pragma unroll
+    for (int i = 0; i < R::NR; ++i) {
+        *(uint2*)&sm.kmeta[wave][i][2 * lane] = r.km[i];
+        if (lane < G / 4) *(uint4*)&sm.vmeta[wave][i][4 * lane] = r.vm[i];
     }
     wave_sync();
 
-    for (int pass = 0; pass < L.G / 16; ++pass) {
-        const int t = pass * 16 + tl;
-        uint4 kc;
-        if (KB == 2) {
-            const uint2 x = *(const uint2*)(rec + t * 32 + part * 8);
-            kc = make_uint4(x.x, x.y, 0, 0);
-        } else {
-            kc = *(const uint4*)(rec + t * 64 + part * 16);
-        }
-        const uint32_t vm = *(const uint32_t*)(rec + L.vmeta_off + 4 * t);
-        float dot[GQ];
+    f4 C[2];
 #pragma unroll
-        for (int hh = 0; hh < GQ; ++hh) dot[hh] = 0.0f;
+    for (int i = 0; i < R::NR; ++i) {
+        const uint4* km = (const uint4*)&sm.kmeta[wave][i][0];
+        // key scale/zero pairs of channels 32g + 8j .. +7
+        f4 cz = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        h8 qhi[4], qlo[4];
 #pragma unroll
-        for (int i = 0; i < 32; i += 4) {
-            const float c0 = kcode<KB>(kc, i), c1 = kcode<KB>(kc, i + 1);
-            const float c2 = kcode<KB>(kc, i + 2), c3 = kcode<KB>(kc, i + 3);
-#pragma unroll
-            for (int hh = 0; hh < GQ; ++hh) {
-                const float4 qv = *(const float4*)&sm.qt[wave][hh][part][i];
-                dot[hh] += qv.x * c0 + qv.y * c1 + qv.z * c2 + qv.w * c3;
+        for (int j = 0; j < 4; ++j) {
+            const h8 s = words_h8(km[4 * g + j]);
+            const h8 z = words_h8(km[16 + 4 * g + j]);
+            cz = mfma(z, Q.q[j], cz);      // every row: sum_c z[c] q[c][head]
+            {
+#pragma clang fp contract(off)
+                const h8 hi = Q.q[j] * s;
+                qhi[j] = hi;
+                qlo[j] = __builtin_elementwise_fma(Q.q[j], s, -hi);
             }
         }
-        float lg[GQ];
 #pragma unroll
-        for (int hh = 0; hh < GQ; ++hh) {
-            float x = dot[hh];
-            x += __shfl_xor(x, 1);
-            x += __shfl_xor(x, 2);
-            lg[hh] = x + bias[hh];
-        }
-        softmax_16<GQ>(st, lg, true, h2f(vm & 0xffffu), h2f(vm >> 16), sm.w[wave], tl, part);
-        wave_sync();
-        // values: lane owns channels 2*lane, 2*lane+1; units (pass, c) are adjacent
-        uint32_t u0[2], u1[2];
-        if (VB == 2) {
-            const uint2 x = *(const uint2*)(rec + L.vcode_off + (pass * kD + 2 * lane) * 4);
-            u0[0] = x.x; u1[0] = x.y;
-        } else {
-            const uint4 x = *(const uint4*)(rec + L.vcode_off + (pass * kD + 2 * lane) * 8);
-            u0[0] = x.x; u0[1] = x.y; u1[0] = x.z; u1[1] = x.w;
-        }
-#pragma unroll
-        for (int tt = 0; tt < 16; tt += 4) {
-            float a[4], bb[4];
+        for (int rt = 0; rt < 2; ++rt) {
+            if (R::NR == 2 && rt != i) continue;
+            f4 acc = cz;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int k = tt + j;
-                if (VB == 2) {
-                    a[j] = (float)((u0[0] >> (2 * k)) & 3u);
-                    bb[j] = (float)((u1[0] >> (2 * k)) & 3u);
-                } else {
-                    a[j] = (float)((u0[k >> 3] >> (4 * (k & 7))) & 15u);
-                    bb[j] = (float)((u1[k >> 3] >> (4 * (k & 7))) & 15u);
-                }
+                const h8 a = codes8<KB>(r.kc[rt], j);
+                acc = mfma(a, qhi[j], acc);
+                acc = mfma(a, qlo[j], acc);
             }
-#pragma unroll
-            for (int hh = 0; hh < GQ; ++hh) {
-                const float4 wv = *(const float4*)&sm.w[wave][hh][tt];
-                st.acc[hh].x += wv.x * a[0] + wv.y * a[1] + wv.z * a[2] + wv.w * a[3];
-                st.acc[hh].y += wv.x * bb[0] + wv.y * bb[1] + wv.z * bb[2] + wv.w * bb[3];
-            }
+            C[rt] = acc;
         }
-        wave_sync();
     }
+
+    // value scale/zero of the lane's 8 slots: slot k = 4*rt + i <-> token 16rt + 4g + i
+    float x[8], vs[8], vz[8];
+    bool valid[8];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const int rec = R::NR == 2 ? rt : 0;
+        const uint16_t* vm = (const uint16_t*)&sm.vmeta[wave][rec][0] + g * 2 * SPT;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = 4 * rt + i;
+            const int slot = R::NR == 2 ? i : k;
+            x[k] = C[rt][i];
+            vs[k] = h2f(vm[slot]);
+            vz[k] = h2f(vm[SPT + slot]);
+            valid[k] = r.has[rec];
+        }
+    }
+    softmax_and_values(A, x, vs, vz, valid, sl2, lane, [&](int ct) -> h8 {
+        if (R::NR == 1) return codes8<VB>(r.vc[0], ct);
+        // G = 16: 4 slots of each record; code q = 4ct + slot
+        const h8 a = codes8<VB>(r.vc[0], ct >> 1);
+        const h8 b = codes8<VB>(r.vc[1], ct >> 1);
+        const int o = 4 * (ct & 1);
+        return h8{a[o], a[o + 1], a[o + 2], a[o + 3], b[o], b[o + 1], b[o + 2], b[o + 3]};
+    });
+    wave_sync();   // LDS meta slots are rewritten by the next unit
 }
 
-// Residual ring: tokens [nq, n) of stream sh, 16 per pass, spread over waves.
-template <int GQ>
-__device__ void attend_residual(AttnSmem<GQ>& sm, WaveState<GQ>& st, const Layout& L, const kvq_cache& c,
-                                long sh, int nq, int n, const float2 (&qs)[GQ], int wave, int lane) {
-    const int tl = lane >> 2, part = lane & 3;
-#pragma unroll
-    for (int hh = 0; hh < GQ; ++hh)
-        *(float2*)&sm.qt[wave][hh][lane >> 4][(2 * lane) & 31] = qs[hh];
-    wave_sync();
+// One 32-token unit of the fp16 residual ring: tokens t0 .. t0+31 (< n).
+__device__ __forceinline__ void process_residual(WaveAcc& A, const Layout& L, const kvq_cache& c, long sh, int t0,
+                                                 int n, const QOps& Q, float sl2, int lane) {
+    const int g = lane >> 4, n16 = lane & 15;
     const half_t* kr = (const half_t*)c.k_res + sh * L.ring * kD;
     const half_t* vr = (const half_t*)c.v_res + sh * L.ring * kD;
-    for (int base = nq + wave * 16; base < n; base += kWaves * 16) {
-        const int t = base + tl;
-        const bool valid = t < n;
-        const int slot = (valid ? t : base) % L.ring;
-        float dot[GQ];
+    f4 C[2];
 #pragma unroll
-        for (int hh = 0; hh < GQ; ++hh) dot[hh] = 0.0f;
-        const uint4* krow = (const uint4*)(kr + (long)slot * kD + part * 32);
+    for (int rt = 0; rt < 2; ++rt) {
+        const int t = t0 + 16 * rt + n16;
+        f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        const uint32_t keep = t < n ? 0xffffffffu : 0u;
+        const uint4* row = (const uint4*)(kr + (long)((t < n ? t : t0) % L.ring) * kD + 32 * g);
 #pragma unroll
-        for (int i = 0; i < 32; i += 8) {
-            const uint4 x = krow[i / 8];
-            const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
-            float kv[8];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                kv[2 * j] = h2f(xs[j] & 0xffffu);
-                kv[2 * j + 1] = h2f(xs[j] >> 16);
-            }
-#pragma unroll
-            for (int hh = 0; hh < GQ; ++hh) {
-                const float4 qa = *(const float4*)&sm.qt[wave][hh][part][i];
-                const float4 qb = *(const float4*)&sm.qt[wave][hh][part][i + 4];
-                dot[hh] += qa.x * kv[0] + qa.y * kv[1] + qa.z * kv[2] + qa.w * kv[3] +
-                           qb.x * kv[4] + qb.y * kv[5] + qb.z * kv[6] + qb.w * kv[7];
-            }
+        for (int j = 0; j < 4; ++j) {
+            uint4 w = row[j];
+            w.x &= keep; w.y &= keep; w.z &= keep; w.w &= keep;
+            acc = mfma(words_h8(w), Q.q[j], acc);
         }
-        float lg[GQ];
-#pragma unroll
-        for (int hh = 0; hh < GQ; ++hh) {
-            float x = dot[hh];
-            x += __shfl_xor(x, 1);
-            x += __shfl_xor(x, 2);
-            lg[hh] = x;
-        }
-        softmax_16<GQ>(st, lg, valid, 1.0f, 0.0f, sm.w[wave], tl, part);
-        wave_sync();
-        for (int tt = 0; tt < 16; ++tt) {
-            const int tok = base + tt;
-            if (tok >= n) break;
-            const uint32_t x = ((const uint32_t*)(vr + (long)(tok % L.ring) * kD))[lane];
-            const float va = h2f(x & 0xffffu), vb = h2f(x >> 16);
-#pragma unroll
-            for (int hh = 0; hh < GQ; ++hh) {
-                const float wv = sm.w[wave][hh][tt];
-                st.acc[hh].x += wv * va;
-                st.acc[hh].y += wv * vb;
-            }
-        }
-        wave_sync();
+        C[rt] = acc;
     }
+    float x[8], vs[8], vz[8];
+    bool valid[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        x[k] = C[k >> 2][k & 3];
+        vs[k] = 1.0f;
+        vz[k] = 0.0f;
+        valid[k] = t0 + (k >> 2) * 16 + 4 * g + (k & 3) < n;
+    }
+    softmax_and_values(A, x, vs, vz, valid, sl2, lane, [&](int ct) -> h8 {
+        h8 b;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int t = t0 + (k >> 2) * 16 + 4 * g + (k & 3);
+            const _Float16 x = vr[(long)((t < n ? t : t0) % L.ring) * kD + 16 * ct + n16];
+            b[k] = t < n ? x : (_Float16)0.0f;
+        }
+        return b;
+    });
 }
 
-template <int GQ, int KB, int VB>
-__global__ __launch_bounds__(256) void attn_split_kernel(Layout L, kvq_cache c, const half_t* __restrict__ q,
-                                                         float qscale, float* __restrict__ ws, int splits,
-                                                         int gps) {
-    __shared__ AttnSmem<GQ> sm;
+template <int G, int KB, int VB>
+__global__ __launch_bounds__(256) void attn_kernel(Layout L, kvq_cache c, const half_t* __restrict__ q,
+                                                   float sl2, float* __restrict__ out, float* __restrict__ ws,
+                                                   int gq, int splits, int ups) {
+    __shared__ AttnSmem<G> sm;
     const int sp = blockIdx.x;
     const int sh = blockIdx.y;
     const int b = sh / L.H, h = sh % L.H;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
+    const int g = lane >> 4, n16 = lane & 15;
     // counters written by this library satisfy 0 <= nq <= n <= nq + ring; clamp
     // so that no other value can index outside the records or the ring
     const int nq = max(c.n_quant[b], 0);
     const int n = min(max(c.n_tokens[b], nq), nq + L.ring);
-    const int Hq = L.H * GQ;
+    const int Hq = L.H * gq;
+    const int parts = splits + 1;
 
-    float2 qs[GQ];
+    QOps Q;
+    {
+        const bool hv = n16 < gq;
+        const uint4* qp = (const uint4*)(q + ((long)b * Hq + h * gq + (hv ? n16 : 0)) * kD + 32 * g);
 #pragma unroll
-    for (int hh = 0; hh < GQ; ++hh) {
-        const uint32_t x = ((const uint32_t*)(q + ((long)b * Hq + h * GQ + hh) * kD))[lane];
-        qs[hh] = make_float2(h2f(x & 0xffffu) * qscale, h2f(x >> 16) * qscale);
+        for (int j = 0; j < 4; ++j) Q.q[j] = words_h8(hv ? qp[j] : make_uint4(0, 0, 0, 0));
     }
-    WaveState<GQ> st;
-#pragma unroll
-    for (int hh = 0; hh < GQ; ++hh) {
-        st.m[hh] = -INFINITY;
-        st.l[hh] = 0.0f;
-        st.pz[hh] = 0.0f;
-        st.acc[hh] = make_float2(0.0f, 0.0f);
-    }
+    WaveAcc A;
+    acc_init(A);
 
     if (sp < splits) {
-        const int ng = nq / L.G;
-        const int g0 = sp * gps;
-        const int g1 = min(g0 + gps, ng);
-        for (int g = g0 + wave; g < g1; g += kWaves) {
-            const uint8_t* rec = record_at(L, c.packed, c.block_table, b, h, g);
-            if (rec) attend_group<GQ, KB, VB>(sm, st, L, rec, qs, wave, lane);
+        const int ngroups = nq / L.G;
+        const int units = (ngroups * L.G + 31) / 32;
+        const int u0 = sp * ups, u1 = min(u0 + ups, units);
+        int u = u0 + wave;
+        if (u < u1) {
+            // two buffers in turn, no copies; the load past the end re-reads
+            // the current unit (an L2 hit) so that every step issues the same loads
+            UnitRaw<G, KB, VB> ra, rb;
+            load_unit(ra, L, c, b, h, u, ngroups, lane);
+            for (;;) {
+                load_unit(rb, L, c, b, h, u + kWaves < u1 ? u + kWaves : u, ngroups, lane);
+                process_unit(sm, A, ra, Q, sl2, wave, lane);
+                u += kWaves;
+                if (u >= u1) break;
+                load_unit(ra, L, c, b, h, u + kWaves < u1 ? u + kWaves : u, ngroups, lane);
+                process_unit(sm, A, rb, Q, sl2, wave, lane);
+                u += kWaves;
+                if (u >= u1) break;
+            }
         }
     } else {
-        attend_residual<GQ>(sm, st, L, c, sh, nq, n, qs, wave, lane);
+        for (int t0 = nq + 32 * wave; t0 < n; t0 += 32 * kWaves)
+            process_residual(A, L, c, sh, t0, n, Q, sl2, lane);
     }
 
-    // Combine the four waves.
-#pragma unroll
-    for (int hh = 0; hh < GQ; ++hh) {
-        const float lt = wave_sum(st.l[hh]);
-        const float pzt = wave_sum(st.pz[hh]);
-        if (lane == 0) {
-            sm.m[wave][hh] = st.m[hh];
-            sm.l[wave][hh] = lt;
-            sm.pz[wave][hh] = pzt;
-        }
+    // Wave results -> LDS: totals over the lane groups, accumulators by head.
+    const float lt = group_sum(A.l);
+    const float pzt = group_sum(A.pz);
+    if (lane < 16) {
+        sm.wm[wave][lane] = A.m;
+        sm.wl[wave][lane] = lt;
+        sm.wpz[wave][lane] = pzt;
     }
-    __syncthreads();
-    float* accbuf = &sm.qt[0][0][0][0];   // reuse: [wave][GQ][128] fits in qt
 #pragma unroll
-    for (int hh = 0; hh < GQ; ++hh) {
-        float M = -INFINITY;
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][hh]);
-        const float f = (M == -INFINITY || st.m[hh] == -INFINITY) ? 0.0f : exp2f(st.m[hh] - M);
-        *(float2*)&accbuf[((wave * GQ) + hh) * kD + 2 * lane] = make_float2(st.acc[hh].x * f, st.acc[hh].y * f);
-    }
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.wacc[wave][4 * g + i][16 * ct + n16] = A.acc[ct][i];
     __syncthreads();
-    for (int i = threadIdx.x; i < GQ * kD; i += 256) {
-        const int hh = i / kD, ch = i % kD;
-        float M = -INFINITY;
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][hh]);
-        float lsum = 0.0f, pzs = 0.0f, a = 0.0f;
+
+    // Workgroup partial (heads < gq) -> workspace.
+    float* part = ws + ((long)sh * parts + sp) * gq * kPart;
+    for (int idx = threadIdx.x; idx < gq * kD; idx += 256) {
+        const int hh = idx >> 7, ch = idx & (kD - 1);
+        float M = kNegInf;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.wm[w][hh]);
+        float o = 0.0f, Ls = 0.0f;
+#pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float f = (M == -INFINITY || sm.m[w][hh] == -INFINITY) ? 0.0f : exp2f(sm.m[w][hh] - M);
-            lsum += sm.l[w][hh] * f;
-            pzs += sm.pz[w][hh] * f;
-            a += accbuf[((w * GQ) + hh) * kD + ch];
+            const float mw = sm.wm[w][hh];
+            const float f = mw == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+            o += (sm.wacc[w][hh][ch] + sm.wpz[w][hh]) * f;
+            Ls += sm.wl[w][hh] * f;
         }
-        float* part = ws + (((long)b * Hq + h * GQ + hh) * (splits + 1) + sp) * kPartStride;
-        part[ch] = a + pzs;
+        part[hh * kPart + ch] = o;
         if (ch == 0) {
-            part[kD] = M;
-            part[kD + 1] = lsum;
+            part[hh * kPart + kD] = M;
+            part[hh * kPart + kD + 1] = Ls;
         }
     }
 }
 
-// out[b][hq][c] = sum_s acc_s e^(m_s - M) / sum_s l_s e^(m_s - M); 0 if empty.
-__global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict__ ws, float* __restrict__ out,
-                                                         int nparts) {
-    const long row = blockIdx.x;
-    const float* p = ws + row * nparts * kPartStride;
-    float M = -INFINITY;
-    for (int s = 0; s < nparts; ++s) M = fmaxf(M, p[s * kPartStride + kD]);
-    float L = 0.0f, o = 0.0f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < nparts; ++s) {
-            const float m = p[s * kPartStride + kD];
-            const float f = m == -INFINITY ? 0.0f : exp2f(m - M);
-            L += p[s * kPartStride + kD + 1] * f;
-            o += p[s * kPartStride + threadIdx.x] * f;
+// Split merge: grid (B*H, gq), 256 threads.  Log-sum-exp over the parts of
+// one (stream, head): out = sum_p o_p e^(m_p-M) / sum_p l_p e^(m_p-M), 0 for
+// an empty sequence.  The part factors are computed once into LDS; the output
+// sums then need only independent loads, split over two halves of the block.
+constexpr int kMaxParts = 256;
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ ws, float* __restrict__ out,
+                                                        int parts, int gq) {
+    __shared__ float fac[kMaxParts];
+    __shared__ float red[2][kD];
+    __shared__ float tot[2];
+    const int sh = blockIdx.x, hh = blockIdx.y, tid = threadIdx.x;
+    const long stride = (long)gq * kPart;
+    const float* p = ws + ((long)sh * parts * gq + hh) * kPart;
+    if (tid < 64) {
+        float M = kNegInf;
+        for (int i = tid; i < parts; i += 64) M = fmaxf(M, p[i * stride + kD]);
+        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+        float Ls = 0.0f;
+        for (int i = tid; i < parts; i += 64) {
+            const float m = p[i * stride + kD];
+            const float f = m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+            fac[i] = f;
+            Ls = fmaf(p[i * stride + kD + 1], f, Ls);
         }
+        for (int off = 32; off >= 1; off >>= 1) Ls += __shfl_xor(Ls, off);
+        if (tid == 0) tot[0] = Ls;
     }
-    out[row * kD + threadIdx.x] = L > 0.0f ? o / L : 0.0f;
+    __syncthreads();
+    const int half = tid >> 7, ch = tid & (kD - 1);
+    float o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
+    int i = half;
+    for (; i + 6 < parts; i += 8) {
+        o0 = fmaf(p[i * stride + ch], fac[i], o0);
+        o1 = fmaf(p[(i + 2) * stride + ch], fac[i + 2], o1);
+        o2 = fmaf(p[(i + 4) * stride + ch], fac[i + 4], o2);
+        o3 = fmaf(p[(i + 6) * stride + ch], fac[i + 6], o3);
+    }
+    for (; i < parts; i += 2) o0 = fmaf(p[i * stride + ch], fac[i], o0);
+    red[half][ch] = (o0 + o1) + (o2 + o3);
+    __syncthreads();
+    if (half == 0) {
+        const float Ls = tot[0];
+        out[((long)sh * gq + hh) * kD + ch] = Ls > 0.0f ? (red[0][ch] + red[1][ch]) / Ls : 0.0f;
+    }
 }
 
 AttnPlan plan_attention(const Layout& L, int num_q_heads) {
     AttnPlan P;
+    const int gq = num_q_heads / L.H;
     const int streams = L.B * L.H;
     const int maxg = L.paged ? L.max_blocks : L.groups;
-    // Aim for ~2048 workgroups over the chip, at least 8 groups per wave.
-    int splits = (2048 + streams - 1) / streams;
-    const int cap = maxg / (kWaves * 8);
+    const int maxu = (maxg * L.G + 31) / 32;
+    // About one round of resident workgroups (two per CU on 256 CUs), and at
+    // least 8 units (two per wave) in each split.
+    int target = 512;
+    if (const char* e = getenv("KVQ_TARGET_WGS")) {
+        const int v = atoi(e);
+        if (v >= 1) target = v;
+    }
+    int splits = (target + streams / 2) / streams;
+    const int cap = (maxu + 7) / 8;
     if (splits > cap) splits = cap;
     if (splits < 1) splits = 1;
-    if (const char* e = getenv("KVQ_SPLITS")) {
-        const int v = atoi(e);
-        if (v >= 1) splits = v;
-    }
+    if (splits > kMaxParts - 1) splits = kMaxParts - 1;
     P.splits = splits;
-    P.groups_per_split = maxg > 0 ? (maxg + splits - 1) / splits : 0;
-    P.workspace = (size_t)L.B * num_q_heads * (splits + 1) * kPartStride * sizeof(float);
+    P.units_per_split = maxu > 0 ? (maxu + splits - 1) / splits : 0;
+    P.parts = splits + 1;
+    P.part_floats = (size_t)gq * kPart;
+    P.workspace = (size_t)streams * P.parts * P.part_floats * sizeof(float);
     return P;
 }
 
 hipError_t launch_attention(const Layout& L, const AttnPlan& P, const kvq_cache& c, const half_t* q,
                             int num_q_heads, float scale, float* out, void* ws, hipStream_t s) {
     const int gq = num_q_heads / L.H;
-    const float qscale = scale * kLog2e;
-    dim3 grid(P.splits + 1, L.B * L.H);
-#define KVQ_ATT(GQ, KB, VB) hipLaunchKernelGGL((attn_split_kernel<GQ, KB, VB>), grid, dim3(256), 0, s, L, c, q, \
-                                               qscale, (float*)ws, P.splits, P.groups_per_split)
-#define KVQ_ATT_B(GQ)                                              \
-    if (L.kbits == 2 && L.vbits == 2) KVQ_ATT(GQ, 2, 2);            \
-    else if (L.kbits == 2 && L.vbits == 4) KVQ_ATT(GQ, 2, 4);       \
-    else if (L.kbits == 4 && L.vbits == 2) KVQ_ATT(GQ, 4, 2);       \
-    else KVQ_ATT(GQ, 4, 4);
-    switch (gq) {
-        case 1: KVQ_ATT_B(1); break;
-        case 2: KVQ_ATT_B(2); break;
-        case 4: KVQ_ATT_B(4); break;
-        case 8: KVQ_ATT_B(8); break;
-        case 16: KVQ_ATT_B(16); break;
+    const float sl2 = scale * kLog2e;
+    dim3 grid(P.parts, L.B * L.H);
+#define KVQ_ATT(GG, KB, VB)                                                                               \
+    hipLaunchKernelGGL((attn_kernel<GG, KB, VB>), grid, dim3(256), 0, s, L, c, q, sl2, out, (float*)ws, gq, \
+                       P.splits, P.units_per_split)
+    const int key = L.G * 100 + L.kbits * 10 + L.vbits;
+    switch (key) {
+        case 1622: KVQ_ATT(16, 2, 2); break;
+        case 1624: KVQ_ATT(16, 2, 4); break;
+        case 1642: KVQ_ATT(16, 4, 2); break;
+        case 1644: KVQ_ATT(16, 4, 4); break;
+        case 3222: KVQ_ATT(32, 2, 2); break;
+        case 3224: KVQ_ATT(32, 2, 4); break;
+        case 3242: KVQ_ATT(32, 4, 2); break;
+        case 3244: KVQ_ATT(32, 4, 4); break;
         default: return hipErrorInvalidValue;
     }
-#undef KVQ_ATT_B
 #undef KVQ_ATT
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(L.B * num_q_heads), dim3(kD), 0, s, (const float*)ws, out,
-                       P.splits + 1);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(L.B * L.H, gq), dim3(256), 0, s, (const float*)ws, out, P.parts, gq);
     return hipGetLastError();
 }
 

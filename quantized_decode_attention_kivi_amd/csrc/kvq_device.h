@@ -1,5 +1,5 @@
 // kvq_device.h -- device helpers of libkvq: record addressing, the fp32
-// quantizer step, code extraction.  gfx950 only.
+// quantizer step, code positions inside a record.  gfx950 only.
 #pragma once
 
 #include "kvq_internal.h"
@@ -38,7 +38,7 @@ __device__ __forceinline__ uint8_t* record_at(const Layout& L, void* packed, con
 // Computed in fp32, stored in fp16; the codes use the stored values.
 struct QParams {
     float z, inv;
-    uint32_t sz_bits;  // fp16 s in the low half, fp16 z in the high half
+    uint16_t s_bits, z_bits;
 };
 
 __device__ __forceinline__ QParams make_qparams(float mn, float mx, int bits) {
@@ -52,7 +52,8 @@ __device__ __forceinline__ QParams make_qparams(float mn, float mx, int bits) {
     QParams p;
     p.z = h2f(zb);
     p.inv = s > 0.0f ? 1.0f / s : 0.0f;
-    p.sz_bits = (uint32_t)sb | ((uint32_t)zb << 16);
+    p.s_bits = sb;
+    p.z_bits = zb;
     return p;
 }
 
@@ -62,6 +63,59 @@ __device__ __forceinline__ uint32_t quant_code(float x, float z, float inv, floa
     const float t = (x - z) * inv;
     const float r = __builtin_rintf(t);
     return (uint32_t)fminf(fmaxf(r, 0.0f), qmax);
+}
+
+// ---------------------------------------------------------------------------
+// Positions inside a record (see kvq_internal.h for the layout).
+// ---------------------------------------------------------------------------
+
+// Byte offset and bit of key code (token t, channel c).
+__device__ __forceinline__ void kcode_pos(const Layout& L, int t, int c, int* byte, int* bit) {
+    const int cpw = 32 / L.kbits;           // codes per word
+    const int q = c & 31;
+    *byte = t * 16 * L.kbits + 4 * L.kbits * (c >> 5) + 4 * (q / cpw);
+    *bit = code_bit(L.kbits, q % cpw);
+}
+
+// Byte offset (from the record start) and bit of value code (token t, channel c).
+__device__ __forceinline__ void vcode_pos(const Layout& L, int t, int c, int* byte, int* bit) {
+    int g, slot;
+    vslot(t, &g, &slot);
+    const int cpw = 32 / L.vbits;
+    const int lane = 16 * g + (c & 15);
+    const int q = (c >> 4) * L.spt + slot;
+    *byte = L.vcode_off + lane * L.spt * L.vbits + 4 * (q / cpw);
+    *bit = code_bit(L.vbits, q % cpw);
+}
+
+// Byte offsets of the fp16 scale and zero of value token t.
+__device__ __forceinline__ int vmeta_pos(const Layout& L, int t) {
+    int g, slot;
+    vslot(t, &g, &slot);
+    return L.vmeta_off + g * 4 * L.spt + 2 * slot;   // zero at + 2*spt
+}
+
+__device__ __forceinline__ uint32_t kcode_at(const Layout& L, const uint8_t* rec, int t, int c) {
+    int by, bi;
+    kcode_pos(L, t, c, &by, &bi);
+    return (*(const uint32_t*)(rec + by) >> bi) & ((1u << L.kbits) - 1);
+}
+__device__ __forceinline__ uint32_t vcode_at(const Layout& L, const uint8_t* rec, int t, int c) {
+    int by, bi;
+    vcode_pos(L, t, c, &by, &bi);
+    return (*(const uint32_t*)(rec + by) >> bi) & ((1u << L.vbits) - 1);
+}
+__device__ __forceinline__ uint16_t kscale_bits(const Layout& L, const uint8_t* rec, int c) {
+    return *(const uint16_t*)(rec + L.kmeta_off + 2 * c);
+}
+__device__ __forceinline__ uint16_t kzero_bits(const Layout& L, const uint8_t* rec, int c) {
+    return *(const uint16_t*)(rec + L.kmeta_off + 2 * kD + 2 * c);
+}
+__device__ __forceinline__ uint16_t vscale_bits(const Layout& L, const uint8_t* rec, int t) {
+    return *(const uint16_t*)(rec + vmeta_pos(L, t));
+}
+__device__ __forceinline__ uint16_t vzero_bits(const Layout& L, const uint8_t* rec, int t) {
+    return *(const uint16_t*)(rec + vmeta_pos(L, t) + 2 * L.spt);
 }
 
 }  // namespace kvq

@@ -1,22 +1,36 @@
 // kvq_internal.h -- layout of the packed cache and launcher declarations shared
 // by the HIP translation units of libkvq (gfx950).  Not part of the public ABI.
 //
-// Packed cache: one RECORD per (key group of G tokens, kv head).  A record holds
-// everything the decode kernel needs for those G tokens ("KV cache compression:
-// quantization, eviction and sparse attention", section 3.4: a block carries its
-// codes and its scale/zero tables, the key group is aligned to the block):
+// Packed cache: one RECORD per (key group of G tokens, kv head), G = 16 or 32.
+// A record holds everything the decode kernel needs for those G tokens ("KV
+// cache compression: quantization, eviction and sparse attention", section
+// 3.4: a block carries its codes and its scale/zero tables, the key group is
+// aligned to the block).  Its sections are laid out for the decode kernel's
+// matrix-core operands (16x16 f16 MFMA tiles, wave64: lane l = 16*g + n with
+// lane group g = l/16 and row/column n = l%16):
 //
-//   [0, kcode)            key codes, token-major, LSB-first:
-//                         element (t, c) at bit (t*128 + c) * k_bits
-//   [vcode_off, +vcode)   value codes in 16-token units: unit (j = t/16, c) is
-//                         16*v_bits bits at unit index j*128 + c; token t%16
-//                         at bit (t%16) * v_bits of the unit
-//   [kmeta_off, +512)     128 key (s, z) fp16 pairs, channel c at 4*c
-//   [vmeta_off, +4G)      G value (s, z) fp16 pairs, token t at 4*t
+//   [0, kcode)            key codes, token-major, 16*kb bytes per token.  Inside
+//                         a token the 32 channels 32g..32g+31 of lane group g
+//                         occupy 4*kb bytes at offset 4*kb*g, in code order
+//                         q = channel - 32g packed by code_bit().
+//   [vcode_off, +vcode)   value codes, lane-major: lane l = 16g + n owns SPT*vb
+//                         bytes at offset l*SPT*vb holding, in code order
+//                         q = ct*SPT + slot (ct = 0..7, slot = 0..SPT-1), the
+//                         code of channel 16*ct + n for the token of that slot
+//                         (vslot()).  SPT = 8 for G = 32, 4 for G = 16.
+//   [kmeta_off, +512)     key scales s[128] then key zeros z[128], fp16,
+//                         channel order.
+//   [vmeta_off, +4G)      per lane group g: SPT value scales then SPT value
+//                         zeros, fp16, slot order (4*SPT bytes per group).
+//
+// Code order inside a 32-bit word (code_bit): INT4 code q (0..7) sits at nibble
+// {0,2,4,6,1,3,5,7}[q]; INT2 code q (0..15) at bit 4*(q%8) + 2*(q/8).  These
+// are the orders in which the gfx950 fp8 / fp4 conversion instructions return
+// nibbles, so the decode kernel unpacks a word straight into operand order.
 //
 // Contiguous caches address record (b, h, g) at ((b*H + h)*groups + g); paged
 // caches at (block_table[b][g]*H + h).  The fp16 residual ring of (b, h) holds
-// token i at slot i % (R + G).
+// token i at slot i % (R + G), token-major, 128 channels per slot.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -33,6 +47,7 @@ struct Layout {
     int B, H, kbits, vbits, G, R, ring;
     int paged, num_blocks, max_blocks, groups;   // groups: record slots per sequence
     int capacity;                                 // max tokens a sequence may hold
+    int spt;                                      // value-code slots per lane and column tile
     int kcode, vcode, vcode_off, kmeta_off, vmeta_off, record;
 };
 
@@ -43,6 +58,22 @@ kvq_status make_layout(const kvq_config* cfg, Layout* L);
 __host__ __device__ inline int num_quantized(int n, int G, int R) {
     int over = n - R;
     return over <= 0 ? 0 : G * (over / G);
+}
+
+// Bit offset of code q inside its 32-bit word.
+__host__ __device__ inline int code_bit(int bits, int q) {
+    if (bits == 4) {
+        const int nib = (q & 3) * 2 + ((q >> 2) & 1);   // {0,2,4,6,1,3,5,7}[q]
+        return 4 * nib;
+    }
+    return 4 * (q & 7) + 2 * ((q >> 3) & 1);
+}
+
+// Lane group and slot of record token t in the value-code and value-meta
+// sections; inverse: t = (slot/4)*16 + 4*g + slot%4.
+__host__ __device__ inline void vslot(int t, int* g, int* slot) {
+    *g = (t & 15) >> 2;
+    *slot = ((t >> 4) << 2) | (t & 3);
 }
 
 // Launchers (return hipSuccess or the launch error).
@@ -56,9 +87,11 @@ hipError_t launch_export(const Layout& L, const kvq_cache& c, uint8_t* kc, uint8
                          uint16_t* kz, uint16_t* vs, uint16_t* vz, int out_tokens, hipStream_t s);
 
 struct AttnPlan {
-    int splits;        // quantized-part splits per stream (plus one residual split)
-    int groups_per_split;
-    size_t workspace;  // bytes
+    int splits;          // quantized-part splits per stream (plus one residual split)
+    int units_per_split; // 32-token units per quantized split
+    int parts;           // splits + 1
+    size_t part_floats;  // floats of one partial result (Hq/H heads x (128 + 4))
+    size_t workspace;    // bytes
 };
 AttnPlan plan_attention(const Layout& L, int num_q_heads);
 hipError_t launch_attention(const Layout& L, const AttnPlan& P, const kvq_cache& c, const _Float16* q,

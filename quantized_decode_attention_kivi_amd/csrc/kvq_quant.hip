@@ -11,115 +11,143 @@
 
 namespace kvq {
 
-// Shared memory of one group quantization (G tokens x 128 channels).
 template <int G>
 struct QuantSmem {
-    uint32_t ktile[G][kD / 2];     // fp16 pairs, token-major
-    uint32_t vtile[G][kD / 2];
-    float4 red[4][kD / 2];         // per token slice: (min0, min1, max0, max1)
+    float kmn[16][kD], kmx[16][kD];   // per token slice, per channel
     float kz[kD], kinv[kD];
-    uint8_t vcode[kD][G];          // value codes, channel-major
+    uint8_t vcode[G][kD];             // value codes before packing
 };
 
 // Quantize G consecutive fp16 rows of keys (ksrc) and values (vsrc) into one
-// record.  Called by all 256 threads of a workgroup.
-template <int G>
+// record.  Called by all 256 threads of a workgroup.  Thread (ts = tid/16,
+// cg = tid%16) holds channels 8cg..8cg+7 of tokens ts, ts+16, ...
+template <int G, int KB, int VB>
 __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* __restrict__ ksrc,
                                const half_t* __restrict__ vsrc, uint8_t* __restrict__ rec) {
+    constexpr int NT = G / 16;
+    constexpr float kq = (float)((1 << KB) - 1);
+    constexpr float vq = (float)((1 << VB) - 1);
     const int tid = threadIdx.x;
-    const int cp = tid & 63;   // channel pair
-    const int ts = tid >> 6;   // token slice
-    const float kq = (float)((1 << L.kbits) - 1);
-    const float vq = (float)((1 << L.vbits) - 1);
+    const int cg = tid & 15;
+    const int ts = tid >> 4;
 
-    // Phase A: stage both tiles in LDS; per-channel key min/max over the group.
-    float mn0 = INFINITY, mn1 = INFINITY, mx0 = -INFINITY, mx1 = -INFINITY;
-    const uint32_t* k32 = (const uint32_t*)ksrc;
-    const uint32_t* v32 = (const uint32_t*)vsrc;
-    for (int t = ts; t < G; t += 4) {
-        const uint32_t kx = k32[t * (kD / 2) + cp];
-        const uint32_t vx = v32[t * (kD / 2) + cp];
-        sm.ktile[t][cp] = kx;
-        sm.vtile[t][cp] = vx;
-        const float a = h2f(kx & 0xffffu), b = h2f(kx >> 16);
-        mn0 = fminf(mn0, a); mx0 = fmaxf(mx0, a);
-        mn1 = fminf(mn1, b); mx1 = fmaxf(mx1, b);
+    float kx[NT][8], vx[NT][8];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int t = ts + 16 * j;
+        const uint4 a = *(const uint4*)(ksrc + t * kD + 8 * cg);
+        const uint4 b = *(const uint4*)(vsrc + t * kD + 8 * cg);
+        const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+        const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kx[j][2 * e] = h2f(aw[e] & 0xffffu);
+            kx[j][2 * e + 1] = h2f(aw[e] >> 16);
+            vx[j][2 * e] = h2f(bw[e] & 0xffffu);
+            vx[j][2 * e + 1] = h2f(bw[e] >> 16);
+        }
     }
-    sm.red[ts][cp] = make_float4(mn0, mn1, mx0, mx1);
-    __syncthreads();
-    if (ts == 0) {
-        for (int j = 1; j < 4; ++j) {
-            const float4 r = sm.red[j][cp];
-            mn0 = fminf(mn0, r.x); mn1 = fminf(mn1, r.y);
-            mx0 = fmaxf(mx0, r.z); mx1 = fmaxf(mx1, r.w);
+
+    // Key statistics: per channel over the G tokens.
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float mn = kx[0][e], mx = kx[0][e];
+#pragma unroll
+        for (int j = 1; j < NT; ++j) {
+            mn = fminf(mn, kx[j][e]);
+            mx = fmaxf(mx, kx[j][e]);
         }
-        const QParams p0 = make_qparams(mn0, mx0, L.kbits);
-        const QParams p1 = make_qparams(mn1, mx1, L.kbits);
-        sm.kz[2 * cp] = p0.z; sm.kinv[2 * cp] = p0.inv;
-        sm.kz[2 * cp + 1] = p1.z; sm.kinv[2 * cp + 1] = p1.inv;
-        *(uint2*)(rec + L.kmeta_off + 8 * cp) = make_uint2(p0.sz_bits, p1.sz_bits);
+        sm.kmn[ts][8 * cg + e] = mn;
+        sm.kmx[ts][8 * cg + e] = mx;
+    }
+
+    // Value statistics: per token over its 128 channels (16 lanes of a row).
+    QParams pv[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        float mn = vx[j][0], mx = vx[j][0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) {
+            mn = fminf(mn, vx[j][e]);
+            mx = fmaxf(mx, vx[j][e]);
+        }
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            mn = fminf(mn, __shfl_xor(mn, off));
+            mx = fmaxf(mx, __shfl_xor(mx, off));
+        }
+        pv[j] = make_qparams(mn, mx, VB);
+        if (cg == 0) {
+            const int t = ts + 16 * j;
+            const int pos = vmeta_pos(L, t);
+            *(uint16_t*)(rec + pos) = pv[j].s_bits;
+            *(uint16_t*)(rec + pos + 2 * L.spt) = pv[j].z_bits;
+        }
     }
     __syncthreads();
-
-    // Phase B: key codes, one unit = (token t, 16 channels), token-major rows.
-    // Phase C: value min/max per token (8 lanes per token), value codes.
-    for (int u = tid; u < G * 8; u += 256) {
-        const int t = u >> 3, ch = u & 7;
-        // keys
-        uint32_t lo = 0, hi = 0;
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t x = sm.ktile[t][ch * 8 + i];
-            const int c = ch * 16 + 2 * i;
-            const uint32_t q0 = quant_code(h2f(x & 0xffffu), sm.kz[c], sm.kinv[c], kq);
-            const uint32_t q1 = quant_code(h2f(x >> 16), sm.kz[c + 1], sm.kinv[c + 1], kq);
-            if (L.kbits == 2) {
-                lo |= (q0 | (q1 << 2)) << (4 * i);
-            } else {
-                const uint32_t pair = q0 | (q1 << 4);
-                if (i < 4) lo |= pair << (8 * i); else hi |= pair << (8 * (i - 4));
-            }
+    if (tid < kD) {
+        float mn = sm.kmn[0][tid], mx = sm.kmx[0][tid];
+        for (int j = 1; j < 16; ++j) {
+            mn = fminf(mn, sm.kmn[j][tid]);
+            mx = fmaxf(mx, sm.kmx[j][tid]);
         }
-        if (L.kbits == 2)
-            *(uint32_t*)(rec + t * 32 + ch * 4) = lo;
-        else
-            *(uint2*)(rec + t * 64 + ch * 8) = make_uint2(lo, hi);
-
-        // values: this token's min/max over its 128 channels
-        float vals[16];
-        float vmn = INFINITY, vmx = -INFINITY;
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t x = sm.vtile[t][ch * 8 + i];
-            vals[2 * i] = h2f(x & 0xffffu);
-            vals[2 * i + 1] = h2f(x >> 16);
-            vmn = fminf(vmn, fminf(vals[2 * i], vals[2 * i + 1]));
-            vmx = fmaxf(vmx, fmaxf(vals[2 * i], vals[2 * i + 1]));
-        }
-        for (int off = 1; off < 8; off <<= 1) {
-            vmn = fminf(vmn, __shfl_xor(vmn, off));
-            vmx = fmaxf(vmx, __shfl_xor(vmx, off));
-        }
-        const QParams pv = make_qparams(vmn, vmx, L.vbits);
-        for (int i = 0; i < 16; ++i)
-            sm.vcode[ch * 16 + i][t] = (uint8_t)quant_code(vals[i], pv.z, pv.inv, vq);
-        if (ch == 0) *(uint32_t*)(rec + L.vmeta_off + 4 * t) = pv.sz_bits;
+        const QParams p = make_qparams(mn, mx, KB);
+        sm.kz[tid] = p.z;
+        sm.kinv[tid] = p.inv;
+        *(uint16_t*)(rec + L.kmeta_off + 2 * tid) = p.s_bits;
+        *(uint16_t*)(rec + L.kmeta_off + 2 * kD + 2 * tid) = p.z_bits;
     }
     __syncthreads();
 
-    // Phase D: value code units (16 tokens of one channel).
-    for (int u = tid; u < (G / 16) * kD; u += 256) {
-        const int j = u >> 7, c = u & 127;
-        const uint4 w = *(const uint4*)&sm.vcode[c][16 * j];
-        const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-        if (L.vbits == 2) {
-            uint32_t packed = 0;
-            for (int i = 0; i < 16; ++i) packed |= ((wv[i >> 2] >> (8 * (i & 3))) & 3u) << (2 * i);
-            *(uint32_t*)(rec + L.vcode_off + u * 4) = packed;
+    // Key codes: the 8 channels of a thread are one INT4 word, half an INT2 word.
+    float kzr[8], kir[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        kzr[e] = sm.kz[8 * cg + e];
+        kir[e] = sm.kinv[8 * cg + e];
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int t = ts + 16 * j;
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t q = quant_code(kx[j][e], kzr[e], kir[e], kq);
+            w |= q << (KB == 4 ? code_bit(4, e) : code_bit(2, e + 8 * (cg & 1)));
+        }
+        if (KB == 4) {
+            *(uint32_t*)(rec + t * 64 + 4 * cg) = w;
         } else {
-            uint32_t lo = 0, hi = 0;
-            for (int i = 0; i < 8; ++i) lo |= ((wv[i >> 2] >> (8 * (i & 3))) & 15u) << (4 * i);
-            for (int i = 8; i < 16; ++i) hi |= ((wv[i >> 2] >> (8 * (i & 3))) & 15u) << (4 * (i - 8));
-            *(uint2*)(rec + L.vcode_off + u * 8) = make_uint2(lo, hi);
+            w |= __shfl_xor(w, 1);
+            if ((cg & 1) == 0) *(uint32_t*)(rec + t * 32 + 2 * cg) = w;
         }
+        // value codes of the same token into LDS, channel order
+        uint32_t v0 = 0, v1 = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v0 |= quant_code(vx[j][e], pv[j].z, pv[j].inv, vq) << (8 * e);
+            v1 |= quant_code(vx[j][e + 4], pv[j].z, pv[j].inv, vq) << (8 * e);
+        }
+        *(uint2*)&sm.vcode[t][8 * cg] = make_uint2(v0, v1);
+    }
+    __syncthreads();
+
+    // Value code words, lane-major in decode-operand order.
+    constexpr int SPT = G == 16 ? 4 : 8;
+    constexpr int WPL = SPT * VB / 4;        // words per lane
+    constexpr int CPW = 32 / VB;             // codes per word
+    for (int D = tid; D < 64 * WPL; D += 256) {
+        const int lane = D / WPL, wi = D % WPL;
+        const int g = lane >> 4, n = lane & 15;
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < CPW; ++e) {
+            const int q = wi * CPW + e;
+            const int ct = q / SPT, slot = q % SPT;
+            const int t = (slot >> 2) * 16 + 4 * g + (slot & 3);
+            w |= (uint32_t)sm.vcode[t][16 * ct + n] << code_bit(VB, e);
+        }
+        *(uint32_t*)(rec + L.vcode_off + lane * SPT * VB + 4 * wi) = w;
     }
     __syncthreads();  // LDS may be reused by the caller
 }
@@ -136,7 +164,7 @@ __device__ __forceinline__ int clamped_len(const Layout& L, const int32_t* seq_l
     return n;
 }
 
-template <int G>
+template <int G, int KB, int VB>
 __global__ __launch_bounds__(256) void prefill_groups_kernel(Layout L, kvq_cache c, const half_t* k,
                                                              const half_t* v, int max_len,
                                                              const int32_t* seq_lens) {
@@ -150,7 +178,7 @@ __global__ __launch_bounds__(256) void prefill_groups_kernel(Layout L, kvq_cache
     uint8_t* rec = record_at(L, c.packed, c.block_table, b, h, g);
     if (!rec) return;
     const long base = ((long)sh * max_len + (long)g * G) * kD;
-    quantize_group<G>(sm, L, k + base, v + base, rec);
+    quantize_group<G, KB, VB>(sm, L, k + base, v + base, rec);
 }
 
 // Residual copy and counters: grid (B*H), 256 threads.
@@ -161,15 +189,15 @@ __global__ __launch_bounds__(256) void prefill_tail_kernel(Layout L, kvq_cache c
     const int b = sh / L.H, h = sh % L.H;
     const int n = clamped_len(L, seq_lens, b, max_len);
     const int nq = num_quantized(n, L.G, L.R);
-    const uint32_t* k32 = (const uint32_t*)(k + (long)sh * max_len * kD);
-    const uint32_t* v32 = (const uint32_t*)(v + (long)sh * max_len * kD);
-    uint32_t* kr = (uint32_t*)c.k_res + (long)sh * L.ring * (kD / 2);
-    uint32_t* vr = (uint32_t*)c.v_res + (long)sh * L.ring * (kD / 2);
-    for (int i = nq + (threadIdx.x >> 6); i < n; i += 4) {
+    const uint4* k16 = (const uint4*)(k + (long)sh * max_len * kD);
+    const uint4* v16 = (const uint4*)(v + (long)sh * max_len * kD);
+    uint4* kr = (uint4*)c.k_res + (long)sh * L.ring * (kD / 8);
+    uint4* vr = (uint4*)c.v_res + (long)sh * L.ring * (kD / 8);
+    const int cp = threadIdx.x & 15;
+    for (int i = nq + (threadIdx.x >> 4); i < n; i += 16) {
         const int slot = i % L.ring;
-        const int cp = threadIdx.x & 63;
-        kr[slot * (kD / 2) + cp] = k32[(long)i * (kD / 2) + cp];
-        vr[slot * (kD / 2) + cp] = v32[(long)i * (kD / 2) + cp];
+        kr[slot * (kD / 8) + cp] = k16[(long)i * (kD / 8) + cp];
+        vr[slot * (kD / 8) + cp] = v16[(long)i * (kD / 8) + cp];
     }
     if (h == 0 && threadIdx.x == 0) {
         c.n_tokens[b] = n;
@@ -181,7 +209,7 @@ __global__ __launch_bounds__(256) void prefill_tail_kernel(Layout L, kvq_cache c
 // Append one token per (sequence, head) and flush a full group: grid (B).
 // ---------------------------------------------------------------------------
 
-template <int G>
+template <int G, int KB, int VB>
 __global__ __launch_bounds__(256) void append_kernel(Layout L, kvq_cache c, const half_t* knew,
                                                      const half_t* vnew) {
     __shared__ QuantSmem<G> sm;
@@ -208,7 +236,8 @@ __global__ __launch_bounds__(256) void append_kernel(Layout L, kvq_cache c, cons
             uint8_t* rec = record_at(L, c.packed, c.block_table, b, h, nq / G);
             if (rec) {
                 const long row = (sh * L.ring + (nq % L.ring)) * kD;
-                quantize_group<G>(sm, L, (const half_t*)c.k_res + row, (const half_t*)c.v_res + row, rec);
+                quantize_group<G, KB, VB>(sm, L, (const half_t*)c.k_res + row, (const half_t*)c.v_res + row,
+                                          rec);
             } else {
                 flushed = false;
             }
@@ -226,16 +255,6 @@ __global__ __launch_bounds__(256) void append_kernel(Layout L, kvq_cache c, cons
 // per block; thread -> token t = tid/16, channels (tid%16)*8 .. +8.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ uint32_t kcode_at(const uint8_t* rec, int kbits, int t, int c) {
-    const int bit = (t * kD + c) * kbits;
-    return (rec[bit >> 3] >> (bit & 7)) & ((1u << kbits) - 1);
-}
-__device__ __forceinline__ uint32_t vcode_at(const uint8_t* rec, const Layout& L, int t, int c) {
-    const int unit = (t >> 4) * kD + c;
-    const int bit = unit * 16 * L.vbits + (t & 15) * L.vbits;
-    return (rec[L.vcode_off + (bit >> 3)] >> (bit & 7)) & ((1u << L.vbits) - 1);
-}
-
 __global__ __launch_bounds__(256) void dequantize_kernel(Layout L, kvq_cache c, float* ko, float* vo,
                                                          int out_tokens) {
     const int sh = blockIdx.y;
@@ -248,16 +267,14 @@ __global__ __launch_bounds__(256) void dequantize_kernel(Layout L, kvq_cache c, 
     float* kd = ko + ((long)sh * out_tokens + t) * kD + c0;
     float* vd = vo + ((long)sh * out_tokens + t) * kD + c0;
     const uint8_t* rec = t < nq ? record_at(L, c.packed, c.block_table, b, h, t / L.G) : nullptr;
+    const int tg = t % L.G;
     for (int i = 0; i < 8; ++i) {
         const int ch = c0 + i;
         float kv = 0.0f, vv = 0.0f;
         if (t < nq) {
             if (rec) {
-                const int tg = t % L.G;
-                const uint32_t km = *(const uint32_t*)(rec + L.kmeta_off + 4 * ch);
-                const uint32_t vm = *(const uint32_t*)(rec + L.vmeta_off + 4 * tg);
-                kv = fmaf((float)kcode_at(rec, L.kbits, tg, ch), h2f(km & 0xffffu), h2f(km >> 16));
-                vv = fmaf((float)vcode_at(rec, L, tg, ch), h2f(vm & 0xffffu), h2f(vm >> 16));
+                kv = fmaf((float)kcode_at(L, rec, tg, ch), h2f(kscale_bits(L, rec, ch)), h2f(kzero_bits(L, rec, ch)));
+                vv = fmaf((float)vcode_at(L, rec, tg, ch), h2f(vscale_bits(L, rec, tg)), h2f(vzero_bits(L, rec, tg)));
             }
         } else if (t < n) {
             const long row = ((long)sh * L.ring + (t % L.ring)) * kD + ch;
@@ -282,21 +299,19 @@ __global__ __launch_bounds__(256) void export_kernel(Layout L, kvq_cache c, uint
     const int tg = t % L.G;
     const long e = ((long)sh * out_tokens + t) * kD + c0;
     for (int i = 0; i < 8; ++i) {
-        kc[e + i] = rec ? (uint8_t)kcode_at(rec, L.kbits, tg, c0 + i) : 0;
-        vc[e + i] = rec ? (uint8_t)vcode_at(rec, L, tg, c0 + i) : 0;
+        kc[e + i] = rec ? (uint8_t)kcode_at(L, rec, tg, c0 + i) : 0;
+        vc[e + i] = rec ? (uint8_t)vcode_at(L, rec, tg, c0 + i) : 0;
     }
     if (tg == 0) {  // key metadata row of this group
         const long gi = ((long)sh * (out_tokens / L.G) + t / L.G) * kD + c0;
         for (int i = 0; i < 8; ++i) {
-            const uint32_t km = rec ? *(const uint32_t*)(rec + L.kmeta_off + 4 * (c0 + i)) : 0u;
-            ks[gi + i] = (uint16_t)(km & 0xffffu);
-            kz[gi + i] = (uint16_t)(km >> 16);
+            ks[gi + i] = rec ? kscale_bits(L, rec, c0 + i) : 0;
+            kz[gi + i] = rec ? kzero_bits(L, rec, c0 + i) : 0;
         }
     }
     if (c0 == 0) {
-        const uint32_t vm = rec ? *(const uint32_t*)(rec + L.vmeta_off + 4 * tg) : 0u;
-        vs[(long)sh * out_tokens + t] = (uint16_t)(vm & 0xffffu);
-        vz[(long)sh * out_tokens + t] = (uint16_t)(vm >> 16);
+        vs[(long)sh * out_tokens + t] = rec ? vscale_bits(L, rec, tg) : 0;
+        vz[(long)sh * out_tokens + t] = rec ? vzero_bits(L, rec, tg) : 0;
     }
 }
 
@@ -304,21 +319,30 @@ __global__ __launch_bounds__(256) void export_kernel(Layout L, kvq_cache c, uint
 // Launchers
 // ---------------------------------------------------------------------------
 
-#define KVQ_DISPATCH_G(G_, F)          \
-    switch (G_) {                      \
-        case 16: F(16); break;         \
-        case 32: F(32); break;         \
-        case 64: F(64); break;         \
-        default: return hipErrorInvalidValue; \
-    }
+#define KVQ_DISPATCH(L_, F)                                                    \
+    do {                                                                       \
+        const int key_ = (L_).G * 100 + (L_).kbits * 10 + (L_).vbits;           \
+        switch (key_) {                                                        \
+            case 1622: F(16, 2, 2); break;                                     \
+            case 1624: F(16, 2, 4); break;                                     \
+            case 1642: F(16, 4, 2); break;                                     \
+            case 1644: F(16, 4, 4); break;                                     \
+            case 3222: F(32, 2, 2); break;                                     \
+            case 3224: F(32, 2, 4); break;                                     \
+            case 3242: F(32, 4, 2); break;                                     \
+            case 3244: F(32, 4, 4); break;                                     \
+            default: return hipErrorInvalidValue;                              \
+        }                                                                      \
+    } while (0)
 
 hipError_t launch_prefill(const Layout& L, const kvq_cache& c, const half_t* k, const half_t* v,
                           int max_len, const int32_t* seq_lens, hipStream_t s) {
     const int ngroups = (max_len + L.G - 1) / L.G;
     if (ngroups > 0) {
         dim3 grid(ngroups, L.B * L.H);
-#define KVQ_PF(GG) hipLaunchKernelGGL(prefill_groups_kernel<GG>, grid, dim3(256), 0, s, L, c, k, v, max_len, seq_lens)
-        KVQ_DISPATCH_G(L.G, KVQ_PF);
+#define KVQ_PF(GG, KB, VB) \
+    hipLaunchKernelGGL((prefill_groups_kernel<GG, KB, VB>), grid, dim3(256), 0, s, L, c, k, v, max_len, seq_lens)
+        KVQ_DISPATCH(L, KVQ_PF);
 #undef KVQ_PF
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -329,8 +353,8 @@ hipError_t launch_prefill(const Layout& L, const kvq_cache& c, const half_t* k, 
 
 hipError_t launch_append(const Layout& L, const kvq_cache& c, const half_t* k, const half_t* v,
                          hipStream_t s) {
-#define KVQ_AP(GG) hipLaunchKernelGGL(append_kernel<GG>, dim3(L.B), dim3(256), 0, s, L, c, k, v)
-    KVQ_DISPATCH_G(L.G, KVQ_AP);
+#define KVQ_AP(GG, KB, VB) hipLaunchKernelGGL((append_kernel<GG, KB, VB>), dim3(L.B), dim3(256), 0, s, L, c, k, v)
+    KVQ_DISPATCH(L, KVQ_AP);
 #undef KVQ_AP
     return hipGetLastError();
 }

@@ -303,7 +303,9 @@ class QuantizedKVCache:
         if nb == 0:
             raise KVQError(KVQ_EINVAL, "kv_decode_attention_workspace_bytes")
         if self._ws is None or self._ws.numel() < nb:
-            self._ws = torch.empty(nb, dtype=torch.uint8, device=self.device)
+            # zero-filled once: the kernel's merge tickets start from zero and
+            # every call leaves them at zero again
+            self._ws = torch.zeros(nb, dtype=torch.uint8, device=self.device)
         return self._ws
 
     def decode_attention(self, q, softmax_scale=None, out=None, stream=None):

@@ -28,8 +28,11 @@ SMALL = {
     "single_head_1k_int2": _w("single_head_1k_int2"),
     "gqa4_int4_ragged": _w("llama3_8b_layer_b8_32k_int4", num_seqs=3, context=2048 + 37),
     "gqa8_int2_ragged": _w("llama3_70b_layer_b1_128k_int2", num_seqs=2, context=4096 + 5),
-    "gqa2_k2v4_g64": _w("llama3_8b_layer_b8_32k_int4", name="g64", num_seqs=2, num_q_heads=4, num_kv_heads=2,
-                        k_bits=2, v_bits=4, group_size=64, residual=64, context=1500, tag=21),
+    "gqa2_k2v4_r64": _w("llama3_8b_layer_b8_32k_int4", name="k2v4", num_seqs=2, num_q_heads=4, num_kv_heads=2,
+                        k_bits=2, v_bits=4, group_size=32, residual=64, context=1500, tag=21),
+    "gqa1_k4v4_g16_odd": _w("llama3_8b_layer_b8_32k_int4", name="g16odd", num_seqs=3, num_q_heads=3,
+                            num_kv_heads=3, k_bits=4, v_bits=4, group_size=16, residual=16, context=16 * 37 + 9,
+                            tag=24),
     "gqa16_k4v2_g16": _w("llama3_8b_layer_b8_32k_int4", name="gq16", num_seqs=2, num_q_heads=32,
                          num_kv_heads=2, k_bits=4, v_bits=2, group_size=16, residual=32, context=777, tag=22),
     "mha_g32_r0": _w("llama3_8b_layer_b8_32k_int4", name="mha", num_seqs=2, num_q_heads=4, num_kv_heads=4,
