@@ -24,6 +24,9 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # matrix-core accumulators in ordinary VGPRs: no copies between register
+    # files around the softmax, and a smaller footprint (higher occupancy)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-fno-gpu-rdc", "-Wall", "-Wno-unused-function",
     "-I", INCLUDE, "-I", CSRC,
 ]

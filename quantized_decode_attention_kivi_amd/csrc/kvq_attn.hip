@@ -117,47 +117,55 @@ struct UnitRaw {
     bool has[NR];
 };
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Buffer resource over one record (hardware range check: an absent record
+// gets num_records = 0 and every load from it returns zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t record_rsrc(const uint8_t* rec, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, rec ? bytes : 0, 0x00020000);
+}
+
 template <int G, int KB, int VB>
 __device__ __forceinline__ void load_unit(UnitRaw<G, KB, VB>& r, const Layout& L, const kvq_cache& c, int b, int h,
                                           int unit, int ngroups, int lane) {
-    // Branch-free: a missing record (odd group count, bad block id) is read
-    // from the pool's first record and its slots are masked later (weights and
-    // value zeros of invalid slots are forced to 0), so every call issues the
-    // same loads and the wait counts stay exact.  Codes are small integers
-    // whatever the bytes, so masked operands stay finite.
+    // Buffer loads: every call issues the same loads (so the wait counts stay
+    // exact and the next unit's loads overlap this unit's arithmetic), and the
+    // compiler does not re-issue them at their point of use.
     using R = UnitRaw<G, KB, VB>;
     const int g = lane >> 4, n = lane & 15;
 #pragma unroll
     for (int i = 0; i < R::NR; ++i) {
         const int grp = unit * R::NR + i;
         const uint8_t* rec = grp < ngroups ? record_at(L, c.packed, c.block_table, b, h, grp) : nullptr;
-        const bool ok = rec != nullptr;
-        r.has[i] = ok;
-        if (!ok) rec = (const uint8_t*)c.packed;
-        r.km[i] = *(const uint2*)(rec + L.kmeta_off + 8 * lane);
-        r.vm[i] = *(const uint4*)(rec + L.vmeta_off + 16 * (lane < G / 4 ? lane : 0));
+        r.has[i] = rec != nullptr;
+        const __amdgpu_buffer_rsrc_t rs = record_rsrc(rec, L.record);
+        const u32x2 km = __builtin_amdgcn_raw_buffer_load_b64(rs, L.kmeta_off + 8 * lane, 0, 0);
+        r.km[i] = make_uint2(km[0], km[1]);
+        const u32x4 vm = __builtin_amdgcn_raw_buffer_load_b128(rs, L.vmeta_off + 16 * (lane < G / 4 ? lane : 0), 0, 0);
+        r.vm[i] = make_uint4(vm[0], vm[1], vm[2], vm[3]);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             if (R::NR == 2 && rt != i) continue;
             const int t = R::NR == 2 ? n : 16 * rt + n;
-            const uint8_t* p = rec + t * 16 * KB + 4 * KB * g;
+            const int off = t * 16 * KB + 4 * KB * g;
             if (KB == 4) {
-                const uint4 x = *(const uint4*)p;
-                r.kc[rt][0] = x.x; r.kc[rt][1] = x.y; r.kc[rt][2] = x.z; r.kc[rt][3] = x.w;
+                const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+                r.kc[rt][0] = x[0]; r.kc[rt][1] = x[1]; r.kc[rt][2] = x[2]; r.kc[rt][3] = x[3];
             } else {
-                const uint2 x = *(const uint2*)p;
-                r.kc[rt][0] = x.x; r.kc[rt][1] = x.y;
+                const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+                r.kc[rt][0] = x[0]; r.kc[rt][1] = x[1];
             }
         }
-        const uint8_t* pv = rec + L.vcode_off + lane * R::VW * 4;
+        const int pv = L.vcode_off + lane * R::VW * 4;
 #pragma unroll
         for (int w = 0; w < R::VW; w += 4) {
             if (w + 4 <= R::VW) {
-                const uint4 x = *(const uint4*)(pv + 4 * w);
-                r.vc[i][w] = x.x; r.vc[i][w + 1] = x.y; r.vc[i][w + 2] = x.z; r.vc[i][w + 3] = x.w;
+                const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, pv + 4 * w, 0, 0);
+                r.vc[i][w] = x[0]; r.vc[i][w + 1] = x[1]; r.vc[i][w + 2] = x[2]; r.vc[i][w + 3] = x[3];
             } else {
-                const uint2 x = *(const uint2*)(pv + 4 * w);
-                r.vc[i][w] = x.x; r.vc[i][w + 1] = x.y;
+                const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, pv + 4 * w, 0, 0);
+                r.vc[i][w] = x[0]; r.vc[i][w + 1] = x[1];
             }
         }
     }
@@ -306,7 +314,7 @@ __device__ __forceinline__ void process_unit(AttnSmem<G>& sm, WaveAcc& A, const 
             x[k] = C[rt][i];
             vs[k] = h2f(vm[slot]);
             vz[k] = h2f(vm[SPT + slot]);
-            valid[k] = r.has[rec];
+            valid[k] = R::NR == 1 || r.has[rec];
         }
     }
     softmax_and_values(A, x, vs, vz, valid, sl2, lane, [&](int ct) -> h8 {
@@ -505,16 +513,18 @@ AttnPlan plan_attention(const Layout& L, int num_q_heads) {
     const int streams = L.B * L.H;
     const int maxg = L.paged ? L.max_blocks : L.groups;
     const int maxu = (maxg * L.G + 31) / 32;
-    // About one round of resident workgroups (two per CU on 256 CUs), and at
-    // least 8 units (two per wave) in each split.
-    int target = 512;
-    if (const char* e = getenv("KVQ_TARGET_WGS")) {
+    // 32 units (8 per wave) per split amortise the per-split set-up and keep
+    // the partials few; smaller problems get shorter splits (down to 8 units)
+    // so that they still spread over ~512 workgroups.
+    const long total = (long)streams * maxu;
+    long ups = (total + 511) / 512;
+    if (ups > 32) ups = 32;
+    if (ups < 8) ups = 8;
+    if (const char* e = getenv("KVQ_UNITS_PER_SPLIT")) {
         const int v = atoi(e);
-        if (v >= 1) target = v;
+        if (v >= 1) ups = v;
     }
-    int splits = (target + streams / 2) / streams;
-    const int cap = (maxu + 7) / 8;
-    if (splits > cap) splits = cap;
+    int splits = maxu > 0 ? (int)((maxu + ups - 1) / ups) : 1;
     if (splits < 1) splits = 1;
     if (splits > kMaxParts - 1) splits = kMaxParts - 1;
     P.splits = splits;
