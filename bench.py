@@ -15,8 +15,10 @@ exceed the 256 MB last-level cache), so the reads measured come from HBM as
 they would inside a multi-layer decode step.
 
 Prints ONE JSON line.  `value` is the decode attention's effective bandwidth:
-algorithmic bytes of one launch (packed codes, scale/zero pairs, fp16
-residual, query and output) divided by its average event-timed duration.
+algorithmic bytes of one call (packed codes, scale/zero pairs, fp16 residual,
+query and output) divided by the average event-timed duration of the call
+(split-K kernel and merge kernel).  `roofline.achieved` divides the same bytes
+by the split-K kernel's own event-timed duration.
 """
 from __future__ import annotations
 
@@ -39,7 +41,8 @@ MALL_BYTES = 256 << 20         # last-level (Infinity) cache
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 ATTN_KERNEL_SOURCES = ["quantized_decode_attention_kivi_amd/csrc/kvq_attn.hip",
                        "quantized_decode_attention_kivi_amd/csrc/kvq_device.h",
-                       "quantized_decode_attention_kivi_amd/csrc/kvq_internal.h"]
+                       "quantized_decode_attention_kivi_amd/csrc/kvq_internal.h",
+                       "quantized_decode_attention_kivi_amd/build.py"]
 
 
 def parse_args():
@@ -52,6 +55,12 @@ def parse_args():
     ap.add_argument("--copies", type=int, default=0, help="cache copies rotated per step (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-baseline sample")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="before the steps, run a read+write elementwise kernel over this many MiB (the "
+                         "known-size reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE) of a --copy-calibration-mb run into profiles/attn_traffic.json")
     return ap.parse_args()
 
 
@@ -107,6 +116,56 @@ def recorded_traffic(workload, digest):
     if not ent or ent.get("kernel_source_sha256_16") != digest:
         return None
     return ent.get("hbm_bytes_per_launch")
+
+
+def write_traffic(args):
+    """HBM bytes per attention launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what the same counter reads for the
+    calibration kernel of known size (reads N bytes, writes N bytes)."""
+    import csv
+    from quantized_decode_attention_kivi_amd import synth
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch = per_kernel(args.write_traffic[0], "FETCH_SIZE")
+    write = per_kernel(args.write_traffic[1], "WRITE_SIZE")
+    nbytes = args.copy_calibration_mb << 20
+    cal = [k for k in fetch if "neg_kernel" in k]
+    att = [k for k in fetch if "attn_kernel" in k]
+    if not cal or not att or not nbytes:
+        raise SystemExit("calibration or attention kernel missing in %s (or --copy-calibration-mb not given)"
+                         % args.write_traffic[0])
+    med = lambda v: float(np.median(v))
+    f_scale = nbytes / (med(fetch[cal[0]]) * 1024.0)
+    w_scale = nbytes / (med(write[cal[0]]) * 1024.0)
+    w = synth.WORKLOADS[args.workload]
+    lens = synth.seq_lengths(w).astype(np.int64)
+    fetched = med(fetch[att[0]]) * 1024.0 * f_scale
+    written = med(write[att[0]]) * 1024.0 * w_scale
+    path = os.path.join(PROFILE_DIR, "attn_traffic.json")
+    rec = json.load(open(path)) if os.path.exists(path) else {}
+    rec[w.name] = {
+        "kernel": att[0],
+        "kernel_source_sha256_16": source_digest(ATTN_KERNEL_SOURCES),
+        "fetch_kib_per_dispatch": med(fetch[att[0]]),
+        "write_kib_per_dispatch": med(write[att[0]]),
+        "calibration_mib": args.copy_calibration_mb,
+        "calibration_fetch_scale": f_scale,
+        "calibration_write_scale": w_scale,
+        "hbm_bytes_per_launch": int(fetched + written),
+        "algorithmic_bytes_per_launch": attention_bytes(lens, w),
+    }
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(rec[w.name]))
 
 
 # ---------------------------------------------------------------------------
@@ -186,6 +245,9 @@ def cpu_baseline(w, K, V, q, lens, budget_s):
 
 def main():
     args = parse_args()
+    if args.write_traffic:
+        write_traffic(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the quantized decode path runs on a single "
@@ -202,6 +264,13 @@ def main():
     kvq.lib()  # fail loudly if the HIP library is missing
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    if args.copy_calibration_mb:
+        src = torch.ones(args.copy_calibration_mb << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     w = synth.WORKLOADS[args.workload]
     if w.paged or w.layers != 1:
         print("bench.py times the contiguous single-layer workloads", file=sys.stderr)
@@ -248,17 +317,12 @@ def main():
         c = caches[s % copies]
         kn, vn = toks[s]
         c.append(kn, vn)
-        if ev is not None:
-            ev[0].record(stream)
-        c.decode_attention(q, out=outs[s % copies])
-        if ev is not None:
-            ev[1].record(stream)
+        c.decode_attention(q, out=outs[s % copies], split_events=ev)
 
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     # attention bytes at each timed step (lengths grow by one per step)
     step_bytes = []
     for i in range(args.steps):
@@ -271,10 +335,14 @@ def main():
         step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    # whole attention call (split-K kernel + merge) and the split-K kernel alone
+    attn_ms = np.array([a.elapsed_time(c) for a, _, c in evs])
+    kern_ms = np.array([a.elapsed_time(b) for a, b, _ in evs])
     attn_avg_s = float(attn_ms.mean()) / 1e3
+    kern_avg_s = float(kern_ms.mean()) / 1e3
     bytes_avg = float(np.mean(step_bytes))
     achieved = bytes_avg / attn_avg_s / 1e9
+    kern_achieved = bytes_avg / kern_avg_s / 1e9
     ms_per_step = wall / args.steps * 1e3
 
     digest = source_digest(ATTN_KERNEL_SOURCES)
@@ -301,18 +369,20 @@ def main():
         "pct_of_hbm_peak": round(100.0 * achieved / HBM_PEAK_GBS, 2),
         "attention_us": round(attn_avg_s * 1e6, 3),
         "attention_us_median": round(float(np.median(attn_ms)) * 1e3, 3),
+        "attention_kernel_us": round(kern_avg_s * 1e6, 3),
+        "merge_kernel_us": round((attn_avg_s - kern_avg_s) * 1e6, 3),
         "attention_bytes_per_launch": int(bytes_avg),
         "quantize_tokens_per_s": round(float(lens.sum()) / (pre_t / 1e3), 1),
         "quantize_gbs": round(pbytes / (pre_t / 1e3) / 1e9, 2),
         "quantize_us": round(pre_t * 1e3, 3),
         "roofline": {
             "bound": "hbm",
-            "achieved": round(achieved, 2),
+            "achieved": round(kern_achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "frac": round(kern_achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "kv_decode_attention",
+            "kernel": "attn_kernel (split-K decode attention; the merge kernel is timed in value only)",
         },
         "cpu_baseline": None,
     }

@@ -160,15 +160,34 @@ size_t kv_decode_attention_workspace_bytes(const kvq_config *cfg, int32_t num_q_
  * stay below 65504 (they are formed in fp16; true for any query of O(1..100)
  * against keys whose per-group range is below ~1000).
  * workspace: 256-byte aligned device memory of at least
- * kv_decode_attention_workspace_bytes(cfg, Hq) bytes holding per-split
- * partial results and merge counters.  It must be zero-filled before its
- * first use; every call returns the counters to zero, so one zeroed
- * workspace serves any sequence of calls (of any configuration that fits)
- * as long as calls sharing it are ordered on one stream. */
+ * kv_decode_attention_workspace_bytes(cfg, Hq) bytes that receives the
+ * per-split partial results (no initialisation needed, content not preserved
+ * between calls).  Two kernels are enqueued: the split-K attention and the
+ * log-sum-exp merge that writes out; calls sharing a workspace must be
+ * ordered on one stream. */
 kvq_status kv_decode_attention(const kvq_config *cfg, const kvq_cache *cache,
                                const void *q, int32_t num_q_heads, float softmax_scale,
                                float *out, void *workspace, size_t workspace_bytes,
                                void *stream);
+
+/* The two steps of kv_decode_attention, for callers that place the merge
+ * themselves (for example after gathering partials of a sequence split over
+ * several devices: every partial is a (max, sum, output) triple that merges
+ * by log-sum-exp).
+ *
+ * kv_decode_attention_partials: same arguments and checks as
+ * kv_decode_attention without `out`; writes, for every (sequence, kv head),
+ * `parts` partial results of Hq/H heads x 132 floats into the workspace:
+ * output[128] (unnormalised), running max (log2 units), sum of weights, pad.
+ *
+ * kv_decode_attention_merge: reads those partials for the same cfg and
+ * num_q_heads and writes out fp32 [B][Hq][d]. */
+kvq_status kv_decode_attention_partials(const kvq_config *cfg, const kvq_cache *cache,
+                                        const void *q, int32_t num_q_heads, float softmax_scale,
+                                        void *workspace, size_t workspace_bytes, void *stream);
+kvq_status kv_decode_attention_merge(const kvq_config *cfg, int32_t num_q_heads,
+                                     const void *workspace, size_t workspace_bytes, float *out,
+                                     void *stream);
 
 /* Logical view of the quantized part (test hook).  k_codes, v_codes: uint8
  * [B][H][out_tokens][d], one code per element for t < n_q[b], 0 elsewhere;

@@ -187,9 +187,13 @@ __device__ __forceinline__ void acc_init(WaveAcc& A) {
 }
 
 // Online-softmax step over the 8 logits x[] (raw q.k, slot order) of this
-// lane's head, then the value contraction with operands vop(ct).  vs/vz: value
-// scale/zero of each slot; valid: slot holds a token.
-template <typename VOp>
+// lane's column, then the value contraction with operands vop(ct).  vs/vz:
+// value scale/zero of each slot; valid: slot holds a token.  The weights p*s
+// are split into fp16 high and low parts (22 bits).  LP (limb-packed): rows
+// 0-7 of the value product take the high parts and rows 8-15 the low parts of
+// heads 0-7, one product per column tile; otherwise each part is a product of
+// its own over rows = heads.
+template <bool LP, typename VOp>
 __device__ __forceinline__ void softmax_and_values(WaveAcc& A, const float (&x)[8], const float (&vs)[8],
                                                    const float (&vz)[8], const bool (&valid)[8], float sl2,
                                                    int lane, VOp vop) {
@@ -200,7 +204,7 @@ __device__ __forceinline__ void softmax_and_values(WaveAcc& A, const float (&x)[
     const float mnew = fmaxf(A.m, cm * sl2);
     const float alpha = mnew == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(A.m - mnew);
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-        // rows of acc are heads 4g+i; head j's alpha lives in lanes with n == j
+        // rows of acc are columns 4g+i; column j's alpha lives in lanes with n == j
         const int base = (lane & 48) | ((lane >> 4) << 2);
         float ai[4];
 #pragma unroll
@@ -223,7 +227,6 @@ __device__ __forceinline__ void softmax_and_values(WaveAcc& A, const float (&x)[
         A.pz = valid[k] ? fmaf(p, vz[k], A.pz) : A.pz;
         w[k] = valid[k] ? p * vs[k] : 0.0f;
     }
-    // exact-to-22-bit split of the weights into two fp16 operands
     h8 whi, wlo;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -231,12 +234,25 @@ __device__ __forceinline__ void softmax_and_values(WaveAcc& A, const float (&x)[
         whi[k] = hi;
         wlo[k] = (_Float16)(w[k] - (float)hi);
     }
+    if (LP) {
+        const h8 wop = (lane & 8) ? wlo : whi;
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-        const h8 bop = vop(ct);
-        A.acc[ct] = mfma(whi, bop, A.acc[ct]);
-        A.acc[ct] = mfma(wlo, bop, A.acc[ct]);
+        for (int ct = 0; ct < 8; ++ct) A.acc[ct] = mfma(wop, vop(ct), A.acc[ct]);
+    } else {
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const h8 bop = vop(ct);
+            A.acc[ct] = mfma(whi, bop, A.acc[ct]);
+            A.acc[ct] = mfma(wlo, bop, A.acc[ct]);
+        }
     }
+}
+
+// LP: the two limb partials of a logit sit in columns n and n^8 of the same
+// 16-lane row; one DPP rotation by 8 brings them together.
+__device__ __forceinline__ float add_limb_partner(float x) {
+    const int y = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128 /* row_ror:8 */, 0xf, 0xf, false);
+    return x + __builtin_bit_cast(float, y);
 }
 
 template <int G>
@@ -253,12 +269,13 @@ struct QOps {
     h8 q[4];
 };
 
-template <int G, int KB, int VB>
+template <int G, int KB, int VB, bool LP>
 __device__ __forceinline__ void process_unit(AttnSmem<G>& sm, WaveAcc& A, const UnitRaw<G, KB, VB>& r,
                                              const QOps& Q, float sl2, int wave, int lane) {
     using R = UnitRaw<G, KB, VB>;
     constexpr int SPT = R::SPT;
     const int g = lane >> 4;
+    const bool lo_limb = LP && (lane & 8);
     // stage the records' scale/zero tables
 #pragma unroll
     for (int i = 0; i < R::NR; ++i) {
@@ -267,25 +284,29 @@ __device__ __forceinline__ void process_unit(AttnSmem<G>& sm, WaveAcc& A, const 
     }
     wave_sync();
 
+    // Key side: accumulators start from sum_c z[c] q[c][head] (every row; LP:
+    // high-limb columns only), then add codes . (q s) with q s split exactly
+    // into fp16 high and low parts (LP: the part of the lane's column).
     f4 C[2];
 #pragma unroll
     for (int i = 0; i < R::NR; ++i) {
         const uint4* km = (const uint4*)&sm.kmeta[wave][i][0];
-        // key scale/zero pairs of channels 32g + 8j .. +7
         f4 cz = f4{0.0f, 0.0f, 0.0f, 0.0f};
         h8 qhi[4], qlo[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const h8 s = words_h8(km[4 * g + j]);
             const h8 z = words_h8(km[16 + 4 * g + j]);
-            cz = mfma(z, Q.q[j], cz);      // every row: sum_c z[c] q[c][head]
+            cz = mfma(z, Q.q[j], cz);
             {
 #pragma clang fp contract(off)
                 const h8 hi = Q.q[j] * s;
-                qhi[j] = hi;
-                qlo[j] = __builtin_elementwise_fma(Q.q[j], s, -hi);
+                const h8 lo = __builtin_elementwise_fma(Q.q[j], s, -hi);
+                qhi[j] = LP ? (lo_limb ? lo : hi) : hi;
+                qlo[j] = lo;
             }
         }
+        if (LP && lo_limb) cz = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             if (R::NR == 2 && rt != i) continue;
@@ -294,7 +315,7 @@ __device__ __forceinline__ void process_unit(AttnSmem<G>& sm, WaveAcc& A, const 
             for (int j = 0; j < 4; ++j) {
                 const h8 a = codes8<KB>(r.kc[rt], j);
                 acc = mfma(a, qhi[j], acc);
-                acc = mfma(a, qlo[j], acc);
+                if (!LP) acc = mfma(a, qlo[j], acc);
             }
             C[rt] = acc;
         }
@@ -311,13 +332,13 @@ __device__ __forceinline__ void process_unit(AttnSmem<G>& sm, WaveAcc& A, const 
         for (int i = 0; i < 4; ++i) {
             const int k = 4 * rt + i;
             const int slot = R::NR == 2 ? i : k;
-            x[k] = C[rt][i];
+            x[k] = LP ? add_limb_partner(C[rt][i]) : C[rt][i];
             vs[k] = h2f(vm[slot]);
             vz[k] = h2f(vm[SPT + slot]);
             valid[k] = R::NR == 1 || r.has[rec];
         }
     }
-    softmax_and_values(A, x, vs, vz, valid, sl2, lane, [&](int ct) -> h8 {
+    softmax_and_values<LP>(A, x, vs, vz, valid, sl2, lane, [&](int ct) -> h8 {
         if (R::NR == 1) return codes8<VB>(r.vc[0], ct);
         // G = 16: 4 slots of each record; code q = 4ct + slot
         const h8 a = codes8<VB>(r.vc[0], ct >> 1);
@@ -329,6 +350,9 @@ __device__ __forceinline__ void process_unit(AttnSmem<G>& sm, WaveAcc& A, const 
 }
 
 // One 32-token unit of the fp16 residual ring: tokens t0 .. t0+31 (< n).
+// Keys and query are exact fp16, so the key product needs one part (LP: the
+// high-limb columns carry it, the low-limb columns add zero).
+template <bool LP>
 __device__ __forceinline__ void process_residual(WaveAcc& A, const Layout& L, const kvq_cache& c, long sh, int t0,
                                                  int n, const QOps& Q, float sl2, int lane) {
     const int g = lane >> 4, n16 = lane & 15;
@@ -347,18 +371,18 @@ __device__ __forceinline__ void process_residual(WaveAcc& A, const Layout& L, co
             w.x &= keep; w.y &= keep; w.z &= keep; w.w &= keep;
             acc = mfma(words_h8(w), Q.q[j], acc);
         }
-        C[rt] = acc;
+        C[rt] = LP && (lane & 8) ? f4{0.0f, 0.0f, 0.0f, 0.0f} : acc;
     }
     float x[8], vs[8], vz[8];
     bool valid[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        x[k] = C[k >> 2][k & 3];
+        x[k] = LP ? add_limb_partner(C[k >> 2][k & 3]) : C[k >> 2][k & 3];
         vs[k] = 1.0f;
         vz[k] = 0.0f;
         valid[k] = t0 + (k >> 2) * 16 + 4 * g + (k & 3) < n;
     }
-    softmax_and_values(A, x, vs, vz, valid, sl2, lane, [&](int ct) -> h8 {
+    softmax_and_values<LP>(A, x, vs, vz, valid, sl2, lane, [&](int ct) -> h8 {
         h8 b;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -370,9 +394,9 @@ __device__ __forceinline__ void process_residual(WaveAcc& A, const Layout& L, co
     });
 }
 
-template <int G, int KB, int VB>
+template <int G, int KB, int VB, bool LP>
 __global__ __launch_bounds__(256) void attn_kernel(Layout L, kvq_cache c, const half_t* __restrict__ q,
-                                                   float sl2, float* __restrict__ out, float* __restrict__ ws,
+                                                   float sl2, float* __restrict__ ws,
                                                    int gq, int splits, int ups) {
     __shared__ AttnSmem<G> sm;
     const int sp = blockIdx.x;
@@ -386,43 +410,46 @@ __global__ __launch_bounds__(256) void attn_kernel(Layout L, kvq_cache c, const 
     const int nq = max(c.n_quant[b], 0);
     const int n = min(max(c.n_tokens[b], nq), nq + L.ring);
     const int Hq = L.H * gq;
-    const int parts = splits + 1;
+    const int parts = splits;
 
     QOps Q;
     {
-        const bool hv = n16 < gq;
-        const uint4* qp = (const uint4*)(q + ((long)b * Hq + h * gq + (hv ? n16 : 0)) * kD + 32 * g);
+        // column n: head n (LP: head n%8, high limb for n < 8, low limb above)
+        const int hd = LP ? (n16 & 7) : n16;
+        const bool hv = hd < gq;
+        const uint4* qp = (const uint4*)(q + ((long)b * Hq + h * gq + (hv ? hd : 0)) * kD + 32 * g);
 #pragma unroll
         for (int j = 0; j < 4; ++j) Q.q[j] = words_h8(hv ? qp[j] : make_uint4(0, 0, 0, 0));
     }
     WaveAcc A;
     acc_init(A);
 
-    if (sp < splits) {
-        const int ngroups = nq / L.G;
-        const int units = (ngroups * L.G + 31) / 32;
-        const int u0 = sp * ups, u1 = min(u0 + ups, units);
+    // Units of this stream: the quantized ones first, then the 32-token units
+    // of the fp16 residual ring; split sp takes units [sp*ups, sp*ups + ups).
+    const int ngroups = nq / L.G;
+    const int uq = (ngroups * L.G + 31) / 32;
+    const int units = uq + (n - nq + 31) / 32;
+    const int u0 = sp * ups, u1 = min(u0 + ups, units);
+    {
+        const int q1 = min(u1, uq);
         int u = u0 + wave;
-        if (u < u1) {
-            // two buffers in turn, no copies; the load past the end re-reads
-            // the current unit (an L2 hit) so that every step issues the same loads
+        if (u < q1) {
             UnitRaw<G, KB, VB> ra, rb;
             load_unit(ra, L, c, b, h, u, ngroups, lane);
             for (;;) {
-                load_unit(rb, L, c, b, h, u + kWaves < u1 ? u + kWaves : u, ngroups, lane);
-                process_unit(sm, A, ra, Q, sl2, wave, lane);
+                load_unit(rb, L, c, b, h, u + kWaves < q1 ? u + kWaves : u, ngroups, lane);
+                process_unit<G, KB, VB, LP>(sm, A, ra, Q, sl2, wave, lane);
                 u += kWaves;
-                if (u >= u1) break;
-                load_unit(ra, L, c, b, h, u + kWaves < u1 ? u + kWaves : u, ngroups, lane);
-                process_unit(sm, A, rb, Q, sl2, wave, lane);
+                if (u >= q1) break;
+                load_unit(ra, L, c, b, h, u + kWaves < q1 ? u + kWaves : u, ngroups, lane);
+                process_unit<G, KB, VB, LP>(sm, A, rb, Q, sl2, wave, lane);
                 u += kWaves;
-                if (u >= u1) break;
+                if (u >= q1) break;
             }
         }
-    } else {
-        for (int t0 = nq + 32 * wave; t0 < n; t0 += 32 * kWaves)
-            process_residual(A, L, c, sh, t0, n, Q, sl2, lane);
     }
+    for (int u = u0 + wave; u < u1; u += kWaves)
+        if (u >= uq) process_residual<LP>(A, L, c, sh, nq + 32 * (u - uq), n, Q, sl2, lane);
 
     // Wave results -> LDS: totals over the lane groups, accumulators by head.
     const float lt = group_sum(A.l);
@@ -450,7 +477,9 @@ __global__ __launch_bounds__(256) void attn_kernel(Layout L, kvq_cache c, const 
         for (int w = 0; w < kWaves; ++w) {
             const float mw = sm.wm[w][hh];
             const float f = mw == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-            o += (sm.wacc[w][hh][ch] + sm.wpz[w][hh]) * f;
+            // LP: rows hh and hh+8 hold the high- and low-limb sums of head hh
+            const float a = LP ? sm.wacc[w][hh][ch] + sm.wacc[w][hh + 8][ch] : sm.wacc[w][hh][ch];
+            o += (a + sm.wpz[w][hh]) * f;
             Ls += sm.wl[w][hh] * f;
         }
         part[hh * kPart + ch] = o;
@@ -461,50 +490,103 @@ __global__ __launch_bounds__(256) void attn_kernel(Layout L, kvq_cache c, const 
     }
 }
 
-// Split merge: grid (B*H, gq), 256 threads.  Log-sum-exp over the parts of
+// Split merge: grid (B*H, gq), 1024 threads.  Log-sum-exp over the parts of
 // one (stream, head): out = sum_p o_p e^(m_p-M) / sum_p l_p e^(m_p-M), 0 for
-// an empty sequence.  The part factors are computed once into LDS; the output
-// sums then need only independent loads, split over two halves of the block.
+// an empty sequence.  Every load (outputs of up to 32 parts per thread, and
+// the parts' max and sum) is issued before any is used: one memory round trip.
 constexpr int kMaxParts = 256;
-__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ ws, float* __restrict__ out,
-                                                        int parts, int gq) {
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeSlices = kMergeThreads / kD;
+constexpr int kMergePer = kMaxParts / kMergeSlices;
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float* __restrict__ ws,
+                                                                  float* __restrict__ out, int parts, int gq) {
     __shared__ float fac[kMaxParts];
-    __shared__ float red[2][kD];
-    __shared__ float tot[2];
+    __shared__ float red[kMergeThreads / 64][2];
+    __shared__ float acc[kMergeSlices][kD];
     const int sh = blockIdx.x, hh = blockIdx.y, tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int slice = tid >> 7, ch = tid & (kD - 1);
     const long stride = (long)gq * kPart;
     const float* p = ws + ((long)sh * parts * gq + hh) * kPart;
-    if (tid < 64) {
-        float M = kNegInf;
-        for (int i = tid; i < parts; i += 64) M = fmaxf(M, p[i * stride + kD]);
-        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-        float Ls = 0.0f;
-        for (int i = tid; i < parts; i += 64) {
-            const float m = p[i * stride + kD];
-            const float f = m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-            fac[i] = f;
-            Ls = fmaf(p[i * stride + kD + 1], f, Ls);
-        }
-        for (int off = 32; off >= 1; off >>= 1) Ls += __shfl_xor(Ls, off);
-        if (tid == 0) tot[0] = Ls;
+    float o[kMergePer];
+#pragma unroll
+    for (int j = 0; j < kMergePer; ++j) {
+        const int i = slice + j * kMergeSlices;
+        o[j] = i < parts ? p[i * stride + ch] : 0.0f;
     }
+    float m = kNegInf, l = 0.0f;
+    if (tid < parts) {
+        m = p[tid * stride + kD];
+        l = p[tid * stride + kD + 1];
+    }
+    float M = m;
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    if (lane == 0) red[wv][0] = M;
     __syncthreads();
-    const int half = tid >> 7, ch = tid & (kD - 1);
-    float o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
-    int i = half;
-    for (; i + 6 < parts; i += 8) {
-        o0 = fmaf(p[i * stride + ch], fac[i], o0);
-        o1 = fmaf(p[(i + 2) * stride + ch], fac[i + 2], o1);
-        o2 = fmaf(p[(i + 4) * stride + ch], fac[i + 4], o2);
-        o3 = fmaf(p[(i + 6) * stride + ch], fac[i + 6], o3);
-    }
-    for (; i < parts; i += 2) o0 = fmaf(p[i * stride + ch], fac[i], o0);
-    red[half][ch] = (o0 + o1) + (o2 + o3);
+    M = red[0][0];
+    for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, red[w][0]);
+    const float f = m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+    if (tid < parts) fac[tid] = f;
+    float Ls = l * f;
+    for (int off = 32; off >= 1; off >>= 1) Ls += __shfl_xor(Ls, off);
+    if (lane == 0) red[wv][1] = Ls;
     __syncthreads();
-    if (half == 0) {
-        const float Ls = tot[0];
-        out[((long)sh * gq + hh) * kD + ch] = Ls > 0.0f ? (red[0][ch] + red[1][ch]) / Ls : 0.0f;
+    Ls = 0.0f;
+    for (int w = 0; w < kMergeThreads / 64; ++w) Ls += red[w][1];
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMergePer; ++j) {
+        const int i = slice + j * kMergeSlices;
+        if (i < parts) sum = fmaf(o[j], fac[i], sum);
     }
+    acc[slice][ch] = sum;
+    __syncthreads();
+    if (slice == 0) {
+        float s = acc[0][ch];
+        for (int k = 1; k < kMergeSlices; ++k) s += acc[k][ch];
+        out[((long)sh * gq + hh) * kD + ch] = Ls > 0.0f ? s / Ls : 0.0f;
+    }
+}
+
+// Resident attention workgroups on the current device: CUs x workgroups per
+// CU for this instantiation (from its register and LDS footprint).  Falls
+// back to 256 CUs x 3 when no device is visible (host-only size queries).
+template <int G, int KB, int VB, bool LP>
+static int attn_slots_for() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256 * 3;
+    if (cached[dev]) return cached[dev];
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)attn_kernel<G, KB, VB, LP>, 256, 0) !=
+            hipSuccess || per_cu <= 0)
+        per_cu = 3;
+    (void)hipGetLastError();
+    cached[dev] = cus * per_cu;
+    return cached[dev];
+}
+
+// Limb packing: with at most 8 query heads per kv head, the high and low
+// fp16 parts of q*s and p*s share one 16-column product.
+static inline bool limb_packed(int gq) { return gq <= 8; }
+
+template <bool LP>
+static int attn_slots_lp(const Layout& L) {
+    switch (L.G * 100 + L.kbits * 10 + L.vbits) {
+        case 1622: return attn_slots_for<16, 2, 2, LP>();
+        case 1624: return attn_slots_for<16, 2, 4, LP>();
+        case 1642: return attn_slots_for<16, 4, 2, LP>();
+        case 1644: return attn_slots_for<16, 4, 4, LP>();
+        case 3222: return attn_slots_for<32, 2, 2, LP>();
+        case 3224: return attn_slots_for<32, 2, 4, LP>();
+        case 3242: return attn_slots_for<32, 4, 2, LP>();
+        default: return attn_slots_for<32, 4, 4, LP>();
+    }
+}
+static int attn_slots(const Layout& L, int gq) {
+    return limb_packed(gq) ? attn_slots_lp<true>(L) : attn_slots_lp<false>(L);
 }
 
 AttnPlan plan_attention(const Layout& L, int num_q_heads) {
@@ -512,37 +594,45 @@ AttnPlan plan_attention(const Layout& L, int num_q_heads) {
     const int gq = num_q_heads / L.H;
     const int streams = L.B * L.H;
     const int maxg = L.paged ? L.max_blocks : L.groups;
-    const int maxu = (maxg * L.G + 31) / 32;
-    // 32 units (8 per wave) per split amortise the per-split set-up and keep
-    // the partials few; smaller problems get shorter splits (down to 8 units)
-    // so that they still spread over ~512 workgroups.
-    const long total = (long)streams * maxu;
-    long ups = (total + 511) / 512;
-    if (ups > 32) ups = 32;
-    if (ups < 8) ups = 8;
+    // 32-token units at capacity: quantized groups, then the residual ring
+    const int maxu = (maxg * L.G + 31) / 32 + (L.R + L.G - 1 + 31) / 32;
+    // One round of resident workgroups when the work allows it: all splits
+    // are the same length, so a round with a partly filled tail is avoided.
+    // At least one unit per wave, at most 128 units (32 per wave) per split.
+    const int slots = attn_slots(L, gq);
+    int splits = slots / streams;
+    if (splits < 1) splits = 1;
+    const int minsplit = (maxu + 3) / 4;
+    if (splits > minsplit) splits = minsplit;
+    int ups = (maxu + splits - 1) / splits;
+    if (ups > 128) splits = (maxu + 127) / 128;
     if (const char* e = getenv("KVQ_UNITS_PER_SPLIT")) {
         const int v = atoi(e);
-        if (v >= 1) ups = v;
+        if (v >= 1) splits = (maxu + v - 1) / v;
     }
-    int splits = maxu > 0 ? (int)((maxu + ups - 1) / ups) : 1;
+    if (splits > kMaxParts) splits = kMaxParts;
     if (splits < 1) splits = 1;
-    if (splits > kMaxParts - 1) splits = kMaxParts - 1;
     P.splits = splits;
-    P.units_per_split = maxu > 0 ? (maxu + splits - 1) / splits : 0;
-    P.parts = splits + 1;
+    P.units_per_split = (maxu + splits - 1) / splits;
+    P.parts = splits;
     P.part_floats = (size_t)gq * kPart;
     P.workspace = (size_t)streams * P.parts * P.part_floats * sizeof(float);
     return P;
 }
 
-hipError_t launch_attention(const Layout& L, const AttnPlan& P, const kvq_cache& c, const half_t* q,
-                            int num_q_heads, float scale, float* out, void* ws, hipStream_t s) {
+hipError_t launch_attention_partials(const Layout& L, const AttnPlan& P, const kvq_cache& c, const half_t* q,
+                                     int num_q_heads, float scale, void* ws, hipStream_t s) {
     const int gq = num_q_heads / L.H;
     const float sl2 = scale * kLog2e;
     dim3 grid(P.parts, L.B * L.H);
-#define KVQ_ATT(GG, KB, VB)                                                                               \
-    hipLaunchKernelGGL((attn_kernel<GG, KB, VB>), grid, dim3(256), 0, s, L, c, q, sl2, out, (float*)ws, gq, \
+#define KVQ_ATT2(GG, KB, VB, LP)                                                                           \
+    hipLaunchKernelGGL((attn_kernel<GG, KB, VB, LP>), grid, dim3(256), 0, s, L, c, q, sl2, (float*)ws, gq, \
                        P.splits, P.units_per_split)
+#define KVQ_ATT(GG, KB, VB)              \
+    if (limb_packed(gq))                  \
+        KVQ_ATT2(GG, KB, VB, true);       \
+    else                                  \
+        KVQ_ATT2(GG, KB, VB, false)
     const int key = L.G * 100 + L.kbits * 10 + L.vbits;
     switch (key) {
         case 1622: KVQ_ATT(16, 2, 2); break;
@@ -556,9 +646,15 @@ hipError_t launch_attention(const Layout& L, const AttnPlan& P, const kvq_cache&
         default: return hipErrorInvalidValue;
     }
 #undef KVQ_ATT
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(L.B * L.H, gq), dim3(256), 0, s, (const float*)ws, out, P.parts, gq);
+#undef KVQ_ATT2
+    return hipGetLastError();
+}
+
+hipError_t launch_attention_merge(const Layout& L, const AttnPlan& P, int num_q_heads, const void* ws, float* out,
+                                  hipStream_t s) {
+    const int gq = num_q_heads / L.H;
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(L.B * L.H, gq), dim3(kMergeThreads), 0, s, (const float*)ws, out,
+                       P.parts, gq);
     return hipGetLastError();
 }
 

@@ -87,14 +87,16 @@ hipError_t launch_export(const Layout& L, const kvq_cache& c, uint8_t* kc, uint8
                          uint16_t* kz, uint16_t* vs, uint16_t* vz, int out_tokens, hipStream_t s);
 
 struct AttnPlan {
-    int splits;          // quantized-part splits per stream (plus one residual split)
-    int units_per_split; // 32-token units per quantized split
-    int parts;           // splits + 1
+    int splits;          // splits per stream (quantized units, then residual units)
+    int units_per_split; // 32-token units per split
+    int parts;           // partial results per stream (= splits)
     size_t part_floats;  // floats of one partial result (Hq/H heads x (128 + 4))
     size_t workspace;    // bytes
 };
 AttnPlan plan_attention(const Layout& L, int num_q_heads);
-hipError_t launch_attention(const Layout& L, const AttnPlan& P, const kvq_cache& c, const _Float16* q,
-                            int num_q_heads, float scale, float* out, void* ws, hipStream_t s);
+hipError_t launch_attention_partials(const Layout& L, const AttnPlan& P, const kvq_cache& c, const _Float16* q,
+                                     int num_q_heads, float scale, void* ws, hipStream_t s);
+hipError_t launch_attention_merge(const Layout& L, const AttnPlan& P, int num_q_heads, const void* ws, float* out,
+                                  hipStream_t s);
 
 }  // namespace kvq

@@ -47,8 +47,8 @@ class kvq_sizes(ctypes.Structure):
 
 
 EXPORTED = ["kvq_buffer_sizes", "kv_quantize_prefill", "kv_append_token", "kv_dequantize",
-            "kv_decode_attention_workspace_bytes", "kv_decode_attention", "kv_export_codes",
-            "kvq_status_string", "kvq_last_error"]
+            "kv_decode_attention_workspace_bytes", "kv_decode_attention", "kv_decode_attention_partials",
+            "kv_decode_attention_merge", "kv_export_codes", "kvq_status_string", "kvq_last_error"]
 
 
 class KVQError(RuntimeError):
@@ -81,6 +81,11 @@ def lib():
         L.kv_decode_attention.argtypes = [P(kvq_config), P(kvq_cache), vp, ctypes.c_int32, ctypes.c_float,
                                           vp, vp, ctypes.c_size_t, vp]
         L.kv_decode_attention.restype = ctypes.c_int
+        L.kv_decode_attention_partials.argtypes = [P(kvq_config), P(kvq_cache), vp, ctypes.c_int32, ctypes.c_float,
+                                                   vp, ctypes.c_size_t, vp]
+        L.kv_decode_attention_partials.restype = ctypes.c_int
+        L.kv_decode_attention_merge.argtypes = [P(kvq_config), ctypes.c_int32, vp, ctypes.c_size_t, vp, vp]
+        L.kv_decode_attention_merge.restype = ctypes.c_int
         L.kv_export_codes.argtypes = [P(kvq_config), P(kvq_cache)] + [vp] * 6 + [ctypes.c_int32, vp]
         L.kv_export_codes.restype = ctypes.c_int
         L.kvq_status_string.argtypes = [ctypes.c_int]
@@ -140,6 +145,19 @@ def kv_decode_attention(cfg, cache, q, num_q_heads, softmax_scale, out, workspac
                                      ctypes.c_float(softmax_scale), _ptr(out), _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(stream)),
            "kv_decode_attention")
+
+
+def kv_decode_attention_partials(cfg, cache, q, num_q_heads, softmax_scale, workspace, stream=None):
+    _check(lib().kv_decode_attention_partials(ctypes.byref(cfg), ctypes.byref(cache), _ptr(q), int(num_q_heads),
+                                              ctypes.c_float(softmax_scale), _ptr(workspace),
+                                              workspace.numel() * workspace.element_size(), _stream(stream)),
+           "kv_decode_attention_partials")
+
+
+def kv_decode_attention_merge(cfg, num_q_heads, workspace, out, stream=None):
+    _check(lib().kv_decode_attention_merge(ctypes.byref(cfg), int(num_q_heads), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _ptr(out),
+                                           _stream(stream)), "kv_decode_attention_merge")
 
 
 def kv_export_codes(cfg, cache, k_codes, v_codes, k_s, k_z, v_s, v_z, out_tokens, stream=None):
@@ -303,13 +321,13 @@ class QuantizedKVCache:
         if nb == 0:
             raise KVQError(KVQ_EINVAL, "kv_decode_attention_workspace_bytes")
         if self._ws is None or self._ws.numel() < nb:
-            # zero-filled once: the kernel's merge tickets start from zero and
-            # every call leaves them at zero again
-            self._ws = torch.zeros(nb, dtype=torch.uint8, device=self.device)
+            self._ws = torch.empty(nb, dtype=torch.uint8, device=self.device)
         return self._ws
 
-    def decode_attention(self, q, softmax_scale=None, out=None, stream=None):
-        """q: fp16 [B][Hq][d] -> fp32 [B][Hq][d]."""
+    def decode_attention(self, q, softmax_scale=None, out=None, stream=None, split_events=None):
+        """q: fp16 [B][Hq][d] -> fp32 [B][Hq][d].  split_events: optional
+        (start, mid, end) torch.cuda.Event triple recorded around the two
+        kernels (partials, merge) on the stream."""
         B, Hq, d = q.shape
         if B != self.shape.num_seqs or d != HEAD_DIM or q.dtype != torch.float16 or not q.is_contiguous():
             raise ValueError("q must be contiguous fp16 [B][Hq][128]")
@@ -318,5 +336,13 @@ class QuantizedKVCache:
         if out is None:
             out = torch.empty((B, Hq, d), dtype=torch.float32, device=self.device)
         ws = self.workspace(Hq)
-        kv_decode_attention(self.cfg, self.cache, q, Hq, softmax_scale, out, ws, stream)
+        if split_events is None:
+            kv_decode_attention(self.cfg, self.cache, q, Hq, softmax_scale, out, ws, stream)
+            return out
+        st = stream if stream is not None else torch.cuda.current_stream()
+        split_events[0].record(st)
+        kv_decode_attention_partials(self.cfg, self.cache, q, Hq, softmax_scale, ws, stream)
+        split_events[1].record(st)
+        kv_decode_attention_merge(self.cfg, Hq, ws, out, stream)
+        split_events[2].record(st)
         return out

@@ -1,0 +1,148 @@
+"""Host-side tests of the C ABI (no GPU): the library loads and exports every
+entry point include/kvq.h declares, the size queries agree with the oracle's
+byte accounting of the packed format ("KV cache compression: quantization,
+eviction and sparse attention", section 8.1; per-token value metadata as in
+its section 3.2), and malformed arguments are rejected before anything is
+enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+def _kvq():
+    from quantized_decode_attention_kivi_amd import kvq
+    if not os.path.exists(kvq.LIB_PATH):
+        pytest.skip("libkvq.so not built")
+    return kvq
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) -
+                  {"defined", "sizeof", "if", "ifdef", "extern"})
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["kv_quantize_prefill", "kv_append_token", "kv_dequantize", "kv_decode_attention",
+              "kvq_buffer_sizes", "kv_decode_attention_workspace_bytes", "kv_export_codes"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    kvq = _kvq()
+    lib = ctypes.CDLL(kvq.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(kvq.EXPORTED) <= set(declared_functions())
+
+
+def _cfg(kvq, **kw):
+    d = dict(num_seqs=2, num_kv_heads=3, head_dim=128, k_bits=4, v_bits=2, group_size=32, residual=64,
+             max_tokens=1000, block_size=0, num_blocks=0, max_blocks_per_seq=0)
+    d.update(kw)
+    return kvq.kvq_config(**d)
+
+
+@pytest.mark.parametrize("kb,vb,G,R,T", [(4, 4, 32, 128, 32768), (2, 2, 32, 128, 131072), (4, 2, 16, 128, 4000),
+                                         (2, 4, 32, 0, 33), (4, 4, 16, 16, 15)])
+def test_buffer_sizes_match_oracle_bytes(orc, kb, vb, G, R, T):
+    kvq = _kvq()
+    cfg = _cfg(kvq, num_seqs=3, num_kv_heads=2, k_bits=kb, v_bits=vb, group_size=G, residual=R, max_tokens=T)
+    sz = kvq.kvq_buffer_sizes(cfg)
+    groups = max(0, (T - R) // G)
+    assert sz.groups_per_seq == groups
+    assert sz.residual_slots == R + G
+    # one record = the oracle's bytes of one more quantized group of G tokens
+    # (codes + per-channel key pairs + per-token value pairs)
+    one_group = orc.stream_bytes(R + 2 * G, 128, kb, vb, G, R) - orc.stream_bytes(R + G, 128, kb, vb, G, R)
+    assert sz.record_bytes == one_group
+    assert sz.packed_bytes == 3 * 2 * groups * sz.record_bytes
+    assert sz.residual_bytes == 3 * 2 * (R + G) * 128 * 2
+    assert sz.counter_bytes == 3 * 4
+    assert sz.block_table_bytes == 0
+
+
+def test_paged_sizes():
+    kvq = _kvq()
+    cfg = _cfg(kvq, group_size=16, residual=128, max_tokens=0, block_size=16, num_blocks=100,
+               max_blocks_per_seq=20)
+    sz = kvq.kvq_buffer_sizes(cfg)
+    assert sz.packed_bytes == 100 * 3 * sz.record_bytes
+    assert sz.block_table_bytes == 2 * 20 * 4
+    assert sz.groups_per_seq == 20
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, "KVQ_EUNSUPPORTED"),
+    ("k_bits", 3, "KVQ_EUNSUPPORTED"),
+    ("v_bits", 8, "KVQ_EUNSUPPORTED"),
+    ("group_size", 64, "KVQ_EUNSUPPORTED"),
+    ("residual", 40, "KVQ_EINVAL"),    # not a multiple of G = 16
+    ("residual", -32, "KVQ_EINVAL"),
+    ("num_seqs", 0, "KVQ_EINVAL"),
+    ("num_kv_heads", 0, "KVQ_EINVAL"),
+    ("block_size", 32, "KVQ_EINVAL"),   # paged block must equal G (16 here)
+])
+def test_config_validation(field, value, status):
+    kvq = _kvq()
+    base = dict(group_size=16, residual=32)
+    base[field] = value
+    cfg = _cfg(kvq, **base)
+    out = kvq.kvq_sizes()
+    got = kvq.lib().kvq_buffer_sizes(ctypes.byref(cfg), ctypes.byref(out))
+    assert got == getattr(kvq, status)
+    assert kvq.kv_decode_attention_workspace_bytes(cfg, 12) == 0
+
+
+def _no_gpu():
+    import torch
+    return not torch.cuda.is_available()
+
+
+@pytest.mark.skipif("not _no_gpu()", reason="argument rejection is exercised only where no kernel can launch")
+def test_calls_reject_bad_arguments_before_launch():
+    """Every call below is malformed in exactly one way and must return the
+    validation status (the fake pointers are never dereferenced)."""
+    kvq = _kvq()
+    L = kvq.lib()
+    cfg = _cfg(kvq)
+    good = 0x10000
+    cache = kvq.kvq_cache(good, good, good, good, good, None)
+    vp = ctypes.c_void_p
+    by = ctypes.byref
+    # null cache pointer
+    bad = kvq.kvq_cache(good, None, good, good, good, None)
+    assert L.kv_quantize_prefill(by(cfg), by(bad), vp(good), vp(good), 10, vp(good), None) == kvq.KVQ_EINVAL
+    # misaligned k (kernels use 128-bit loads)
+    assert L.kv_quantize_prefill(by(cfg), by(cache), vp(good + 4), vp(good), 10, vp(good), None) == kvq.KVQ_EINVAL
+    # negative max_len
+    assert L.kv_quantize_prefill(by(cfg), by(cache), vp(good), vp(good), -1, vp(good), None) == kvq.KVQ_EINVAL
+    # append: null token
+    assert L.kv_append_token(by(cfg), by(cache), None, vp(good), None) == kvq.KVQ_EINVAL
+    # dequantize: negative token count
+    assert L.kv_dequantize(by(cfg), by(cache), vp(good), vp(good), -5, None) == kvq.KVQ_EINVAL
+    # attention: Hq not a multiple of H, too many query heads per kv head, tiny workspace
+    ws = kvq.kv_decode_attention_workspace_bytes(cfg, 6)
+    assert ws > 0
+    assert L.kv_decode_attention(by(cfg), by(cache), vp(good), 7, ctypes.c_float(0.088), vp(good), vp(good),
+                                 ws, None) == kvq.KVQ_EINVAL
+    assert L.kv_decode_attention(by(cfg), by(cache), vp(good), 3 * 17, ctypes.c_float(0.088), vp(good),
+                                 vp(good), 10 ** 9, None) == kvq.KVQ_EUNSUPPORTED
+    assert L.kv_decode_attention(by(cfg), by(cache), vp(good), 6, ctypes.c_float(0.088), vp(good), vp(good),
+                                 ws - 1, None) == kvq.KVQ_ECAPACITY
+    assert L.kv_decode_attention(by(cfg), by(cache), vp(good), 6, ctypes.c_float(-1.0), vp(good), vp(good),
+                                 ws, None) == kvq.KVQ_EINVAL
+    # export: token count not a multiple of G
+    assert L.kv_export_codes(by(cfg), by(cache), *[vp(good)] * 6, 33, None) == kvq.KVQ_EINVAL
+    # paged cache without block table
+    pcfg = _cfg(kvq, group_size=16, residual=32, max_tokens=0, block_size=16, num_blocks=8, max_blocks_per_seq=4)
+    assert L.kv_append_token(by(pcfg), by(cache), vp(good), vp(good), None) == kvq.KVQ_EINVAL
+    assert L.kvq_status_string(kvq.KVQ_ECAPACITY).decode() == "buffer or workspace too small"

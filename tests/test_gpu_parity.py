@@ -164,3 +164,17 @@ def test_full_size_workload(name):
     out = cache.decode_attention(q, SCALE)
     torch.cuda.synchronize()
     compare_attention(out.cpu().numpy(), oracle_attention(to_bits(q), states, SCALE))
+
+
+def test_split_entry_points_equal_combined_call():
+    """kv_decode_attention_partials followed by kv_decode_attention_merge is
+    the same computation as kv_decode_attention (bit for bit)."""
+    w = SMALL["gqa8_int2_ragged"]
+    cache, states, _, _ = _run_prefill(w)
+    q = synth.make_query(w, device="cuda", step=2)
+    a = cache.decode_attention(q, SCALE).clone()
+    ev = tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+    b = cache.decode_attention(q, SCALE, split_events=ev)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    compare_attention(b.cpu().numpy(), oracle_attention(to_bits(q), states, SCALE))
