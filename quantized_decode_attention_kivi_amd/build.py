@@ -32,6 +32,12 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source additions.  The attention kernels never produce or test for NaN
+# (masked slots are removed by selects, not arithmetic), so their max/min need
+# no NaN-quieting operand canonicalization.
+SOURCE_FLAGS = {"kvq_attn.hip": ["-fno-honor-nans"]}
+
+
 def hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     return os.path.join(rocm, "bin", "hipcc")
@@ -42,7 +48,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-        cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc(), *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -104,71 +104,111 @@ __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Raw loads of one 32-token unit: NR records (1 for G = 32, 2 for G = 16).
-template <int G, int KB, int VB>
-struct UnitRaw {
-    static constexpr int NR = 32 / G;
-    static constexpr int SPT = G == 16 ? 4 : 8;
-    static constexpr int VW = SPT * VB / 4;    // value words per lane and record
-    uint32_t kc[2][KB];                        // per row tile: this lane's 32 key codes
-    uint32_t vc[NR][VW];                       // per record: this lane's value codes
-    uint2 km[NR];                              // per record: 8 bytes of key meta
-    uint4 vm[NR];                              // per record: 16 bytes of value meta (some lanes)
-    bool has[NR];
-};
-
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-// Buffer resource over one record (hardware range check: an absent record
-// gets num_records = 0 and every load from it returns zeros).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t record_rsrc(const uint8_t* rec, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, rec ? bytes : 0, 0x00020000);
+// One 32-token unit (NR = 32/G records) staged in LDS by the buffer unit's
+// direct-to-LDS loads: each load instruction moves 16 bytes per lane from any
+// record offset to LDS slot (base + 16*lane), so the next unit's codes are in
+// flight without occupying registers.  Byte offsets inside one stage buffer:
+//   KC   key codes.  16-bit keys (INT4): the 16 bytes lane (g, n) feeds the
+//        key product of row tile rt sit at KC + rt*1024 + 16*lane.  INT2: the 8
+//        bytes of (g, n, rt) sit at KC + rt*512 + 16*((g/2)*16 + n) + 8*(g%2).
+//   VC   value codes.  G = 32: lane l's words 0-3 at VC + 16l, words 4-7 (INT4)
+//        at VC + 1024 + 16l.  G = 16: record i's words of lane l at
+//        VC + i*64*VW*4 + VW*4*l (VW words per lane and record).
+//   META record i's key scale/zero table (512 B) then its value scale/zero
+//        table (4G B) at META + i*MREC.
+template <int G, int KB, int VB>
+struct Stage {
+    static constexpr int NR = 32 / G;
+    static constexpr int SPT = G == 16 ? 4 : 8;
+    static constexpr int VW = SPT * VB / 4;          // value words per lane and record
+    static constexpr int KC = 0;
+    static constexpr int VC = 512 * KB;
+    static constexpr int META = VC + 512 * VB;
+    static constexpr int MREC = 512 + 4 * G;
+    static constexpr int BYTES = META + NR * MREC;
+    // 16-byte aligned and large enough to hold a wave's [16][128] fp32
+    // accumulators at the end (two waves per stage array)
+    static constexpr int PITCH = BYTES < 4096 ? 4096 : (BYTES + 15) / 16 * 16;
+    // direct-to-LDS load instructions per unit (the wait counts below)
+    static constexpr int LOADS = G == 32 ? KB / 2 + VB / 2 + 1 : 6;
+};
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
+// memory operations of this wave are outstanding; other counters untouched.
+__device__ __forceinline__ constexpr int vmcnt_imm(int n) {
+    return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
+// Buffer descriptor of one record, wave uniform (hardware range check: an
+// absent record gets num_records = 0 and every load from it returns zeros).
+__device__ __forceinline__ u32x4 record_desc(const uint8_t* rec, int bytes) {
+    const uint64_t a = (uint64_t)rec;
+    u32x4 d;
+    d[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    d[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+    d[2] = __builtin_amdgcn_readfirstlane(rec ? (uint32_t)bytes : 0u);
+    d[3] = 0x00020000u;
+    return d;
+}
+
+// 16 bytes per lane from record offset `off` to LDS address lds + 16*lane.
+// Issued from inline assembly so that the compiler inserts no waits of its
+// own for the LDS write (it cannot tell the two stage buffers apart and would
+// drain the prefetch); the kernel waits explicitly before reading a buffer.
+__device__ __forceinline__ void lds_load16(u32x4 desc, lds_u8* dst, int off) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(desc), "{m0}"(m0) : "memory");
+}
+
+// Issues the direct-to-LDS loads of one unit into stage buffer `buf` (wave
+// uniform address) and returns which of its records exist.  Every call issues
+// exactly Stage::LOADS load instructions, so the wait counts stay exact.
 template <int G, int KB, int VB>
-__device__ __forceinline__ void load_unit(UnitRaw<G, KB, VB>& r, const Layout& L, const kvq_cache& c, int b, int h,
-                                          int unit, int ngroups, int lane) {
-    // Buffer loads: every call issues the same loads (so the wait counts stay
-    // exact and the next unit's loads overlap this unit's arithmetic), and the
-    // compiler does not re-issue them at their point of use.
-    using R = UnitRaw<G, KB, VB>;
+__device__ __forceinline__ uint32_t issue_unit(lds_u8* buf, const Layout& L, const kvq_cache& c, int b, int h,
+                                               int unit, int ngroups, int lane) {
+    using S = Stage<G, KB, VB>;
     const int g = lane >> 4, n = lane & 15;
+    uint32_t has = 0;
 #pragma unroll
-    for (int i = 0; i < R::NR; ++i) {
-        const int grp = unit * R::NR + i;
+    for (int i = 0; i < S::NR; ++i) {
+        const int grp = unit * S::NR + i;
         const uint8_t* rec = grp < ngroups ? record_at(L, c.packed, c.block_table, b, h, grp) : nullptr;
-        r.has[i] = rec != nullptr;
-        const __amdgpu_buffer_rsrc_t rs = record_rsrc(rec, L.record);
-        const u32x2 km = __builtin_amdgcn_raw_buffer_load_b64(rs, L.kmeta_off + 8 * lane, 0, 0);
-        r.km[i] = make_uint2(km[0], km[1]);
-        const u32x4 vm = __builtin_amdgcn_raw_buffer_load_b128(rs, L.vmeta_off + 16 * (lane < G / 4 ? lane : 0), 0, 0);
-        r.vm[i] = make_uint4(vm[0], vm[1], vm[2], vm[3]);
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            if (R::NR == 2 && rt != i) continue;
-            const int t = R::NR == 2 ? n : 16 * rt + n;
-            const int off = t * 16 * KB + 4 * KB * g;
+        has |= (rec != nullptr) << i;
+        const u32x4 rs = record_desc(rec, L.record);
+        if (G == 32) {
             if (KB == 4) {
-                const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-                r.kc[rt][0] = x[0]; r.kc[rt][1] = x[1]; r.kc[rt][2] = x[2]; r.kc[rt][3] = x[3];
+                lds_load16(rs, buf + S::KC, n * 64 + 16 * g);
+                lds_load16(rs, buf + S::KC + 1024, (16 + n) * 64 + 16 * g);
             } else {
-                const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
-                r.kc[rt][0] = x[0]; r.kc[rt][1] = x[1];
+                // slot l = rt*32 + gh*16 + n  <-  token 16rt + n, lane groups 2gh, 2gh+1
+                const int rt = lane >> 5, gh = (lane >> 4) & 1;
+                lds_load16(rs, buf + S::KC, (16 * rt + n) * 32 + 16 * gh);
+            }
+            lds_load16(rs, buf + S::VC, L.vcode_off + S::VW * 4 * lane);
+            if (VB == 4) lds_load16(rs, buf + S::VC + 1024, L.vcode_off + S::VW * 4 * lane + 16);
+        } else {
+            if (KB == 4) {
+                lds_load16(rs, buf + S::KC + i * 1024, n * 64 + 16 * g);
+            } else if (lane < 32) {
+                const int gh = lane >> 4;
+                lds_load16(rs, buf + S::KC + i * 512, n * 32 + 16 * gh);
+            }
+            if (VB == 4) {
+                lds_load16(rs, buf + S::VC + i * 1024, L.vcode_off + 16 * lane);
+            } else if (lane < 32) {
+                lds_load16(rs, buf + S::VC + i * 512, L.vcode_off + 16 * lane);
             }
         }
-        const int pv = L.vcode_off + lane * R::VW * 4;
-#pragma unroll
-        for (int w = 0; w < R::VW; w += 4) {
-            if (w + 4 <= R::VW) {
-                const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, pv + 4 * w, 0, 0);
-                r.vc[i][w] = x[0]; r.vc[i][w + 1] = x[1]; r.vc[i][w + 2] = x[2]; r.vc[i][w + 3] = x[3];
-            } else {
-                const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, pv + 4 * w, 0, 0);
-                r.vc[i][w] = x[0]; r.vc[i][w + 1] = x[1];
-            }
-        }
+        if (lane < 32 + G / 4)
+            lds_load16(rs, buf + S::META + i * S::MREC,
+                       lane < 32 ? L.kmeta_off + 16 * lane : L.vmeta_off + 16 * (lane - 32));
     }
+    return has;
 }
 
 // Per-wave online-softmax state and value accumulators.
@@ -202,7 +242,8 @@ __device__ __forceinline__ void softmax_and_values(WaveAcc& A, const float (&x)[
     for (int k = 0; k < 8; ++k) cm = valid[k] ? fmaxf(cm, x[k]) : cm;
     cm = group_max(cm);
     const float mnew = fmaxf(A.m, cm * sl2);
-    const float alpha = mnew == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(A.m - mnew);
+    // nothing accumulated yet (running max still -inf): no rescale needed
+    const float alpha = A.m == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(A.m - mnew);
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
         // rows of acc are columns 4g+i; column j's alpha lives in lanes with n == j
         const int base = (lane & 48) | ((lane >> 4) << 2);
@@ -251,73 +292,103 @@ __device__ __forceinline__ void softmax_and_values(WaveAcc& A, const float (&x)[
 // LP: the two limb partials of a logit sit in columns n and n^8 of the same
 // 16-lane row; one DPP rotation by 8 brings them together.
 __device__ __forceinline__ float add_limb_partner(float x) {
-    const int y = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128 /* row_ror:8 */, 0xf, 0xf, false);
+    // bound_ctrl with a zero "old" lets the compiler fold the move into the add
+    const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128 /* row_ror:8 */, 0xf, 0xf, true);
     return x + __builtin_bit_cast(float, y);
 }
-
-template <int G>
-struct AttnSmem {
-    // per wave: key meta (2 records x 512 B) and value meta (2 records x 128 B)
-    uint32_t kmeta[kWaves][2][kD];
-    uint32_t vmeta[kWaves][2][32];
-    float wm[kWaves][16], wl[kWaves][16], wpz[kWaves][16];
-    float wacc[kWaves][16][kD];
-};
 
 // Query operand of lane (g, n): q[head n][32g + 8j + e], zero for heads >= gq.
 struct QOps {
     h8 q[4];
 };
 
+template <typename T>
+__device__ __forceinline__ T lds_read(const lds_u8* p) {
+    return *(const __attribute__((address_space(3))) T*)p;
+}
+
+// One staged unit (see Stage): key logits on the matrix cores, then the
+// online-softmax step and the value product.
 template <int G, int KB, int VB, bool LP>
-__device__ __forceinline__ void process_unit(AttnSmem<G>& sm, WaveAcc& A, const UnitRaw<G, KB, VB>& r,
-                                             const QOps& Q, float sl2, int wave, int lane) {
-    using R = UnitRaw<G, KB, VB>;
-    constexpr int SPT = R::SPT;
-    const int g = lane >> 4;
+__device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, WaveAcc& A, const QOps& Q, float sl2,
+                                             int lane) {
+    using S = Stage<G, KB, VB>;
+    constexpr int SPT = S::SPT;
+    const int g = lane >> 4, n = lane & 15;
     const bool lo_limb = LP && (lane & 8);
-    // stage the records' scale/zero tables
-#pragma unroll
-    for (int i = 0; i < R::NR; ++i) {
-        *(uint2*)&sm.kmeta[wave][i][2 * lane] = r.km[i];
-        if (lane < G / 4) *(uint4*)&sm.vmeta[wave][i][4 * lane] = r.vm[i];
-    }
-    wave_sync();
 
     // Key side: accumulators start from sum_c z[c] q[c][head] (every row; LP:
     // high-limb columns only), then add codes . (q s) with q s split exactly
     // into fp16 high and low parts (LP: the part of the lane's column).
     f4 C[2];
 #pragma unroll
-    for (int i = 0; i < R::NR; ++i) {
-        const uint4* km = (const uint4*)&sm.kmeta[wave][i][0];
+    for (int i = 0; i < S::NR; ++i) {
+        const lds_u8* km = buf + S::META + i * S::MREC;
         f4 cz = f4{0.0f, 0.0f, 0.0f, 0.0f};
         h8 qhi[4], qlo[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const h8 s = words_h8(km[4 * g + j]);
-            const h8 z = words_h8(km[16 + 4 * g + j]);
+            const h8 s = __builtin_bit_cast(h8, lds_read<u32x4>(km + 16 * (4 * g + j)));
+            const h8 z = __builtin_bit_cast(h8, lds_read<u32x4>(km + 256 + 16 * (4 * g + j)));
             cz = mfma(z, Q.q[j], cz);
             {
 #pragma clang fp contract(off)
                 const h8 hi = Q.q[j] * s;
-                const h8 lo = __builtin_elementwise_fma(Q.q[j], s, -hi);
-                qhi[j] = LP ? (lo_limb ? lo : hi) : hi;
-                qlo[j] = lo;
+                qhi[j] = hi;
+                if (!LP) qlo[j] = __builtin_elementwise_fma(Q.q[j], s, -hi);
             }
         }
-        if (LP && lo_limb) cz = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (LP && lo_limb) {
+            // low-limb columns (a divergent branch: only these lanes pay for
+            // it): the exact low parts q s - hi(q s), and no bias
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const h8 s = __builtin_bit_cast(h8, lds_read<u32x4>(km + 16 * (4 * g + j)));
+                qhi[j] = __builtin_elementwise_fma(Q.q[j], s, -qhi[j]);
+            }
+            cz = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            if (R::NR == 2 && rt != i) continue;
+            if (S::NR == 2 && rt != i) continue;
+            uint32_t kc[KB];
+            if (KB == 4) {
+                const u32x4 x = lds_read<u32x4>(buf + S::KC + rt * 1024 + 16 * lane);
+                kc[0] = x[0]; kc[1] = x[1]; kc[2] = x[2]; kc[3] = x[3];
+            } else {
+                const u32x2 x = lds_read<u32x2>(buf + S::KC + rt * 512 + 16 * ((g >> 1) * 16 + n) + 8 * (g & 1));
+                kc[0] = x[0]; kc[1] = x[1];
+            }
             f4 acc = cz;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const h8 a = codes8<KB>(r.kc[rt], j);
+                const h8 a = codes8<KB>(kc, j);
                 acc = mfma(a, qhi[j], acc);
                 if (!LP) acc = mfma(a, qlo[j], acc);
             }
             C[rt] = acc;
+        }
+    }
+
+    // value codes of this lane (per record)
+    uint32_t vc[S::NR][S::VW];
+    if (G == 32) {
+        const u32x4 x = lds_read<u32x4>(buf + S::VC + 16 * lane);
+        vc[0][0] = x[0]; vc[0][1] = x[1]; vc[0][2] = x[2]; vc[0][3] = x[3];
+        if (VB == 4) {
+            const u32x4 y = lds_read<u32x4>(buf + S::VC + 1024 + 16 * lane);
+            vc[0][4] = y[0]; vc[0][5] = y[1]; vc[0][6] = y[2]; vc[0][7] = y[3];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < S::NR; ++i) {
+            if (VB == 4) {
+                const u32x4 x = lds_read<u32x4>(buf + S::VC + i * 1024 + 16 * lane);
+                vc[i][0] = x[0]; vc[i][1] = x[1]; vc[i][2] = x[2]; vc[i][3] = x[3];
+            } else {
+                const u32x2 x = lds_read<u32x2>(buf + S::VC + i * 512 + 8 * lane);
+                vc[i][0] = x[0]; vc[i][1] = x[1];
+            }
         }
     }
 
@@ -326,27 +397,26 @@ __device__ __forceinline__ void process_unit(AttnSmem<G>& sm, WaveAcc& A, const 
     bool valid[8];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-        const int rec = R::NR == 2 ? rt : 0;
-        const uint16_t* vm = (const uint16_t*)&sm.vmeta[wave][rec][0] + g * 2 * SPT;
+        const int rec = S::NR == 2 ? rt : 0;
+        const lds_u8* vm = buf + S::META + rec * S::MREC + 512 + g * 4 * SPT;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int k = 4 * rt + i;
-            const int slot = R::NR == 2 ? i : k;
+            const int slot = S::NR == 2 ? i : k;
             x[k] = LP ? add_limb_partner(C[rt][i]) : C[rt][i];
-            vs[k] = h2f(vm[slot]);
-            vz[k] = h2f(vm[SPT + slot]);
-            valid[k] = R::NR == 1 || r.has[rec];
+            vs[k] = h2f(lds_read<uint16_t>(vm + 2 * slot));
+            vz[k] = h2f(lds_read<uint16_t>(vm + 2 * (SPT + slot)));
+            valid[k] = S::NR == 1 || ((has >> rec) & 1);
         }
     }
     softmax_and_values<LP>(A, x, vs, vz, valid, sl2, lane, [&](int ct) -> h8 {
-        if (R::NR == 1) return codes8<VB>(r.vc[0], ct);
+        if (S::NR == 1) return codes8<VB>(vc[0], ct);
         // G = 16: 4 slots of each record; code q = 4ct + slot
-        const h8 a = codes8<VB>(r.vc[0], ct >> 1);
-        const h8 b = codes8<VB>(r.vc[1], ct >> 1);
+        const h8 a = codes8<VB>(vc[0], ct >> 1);
+        const h8 b = codes8<VB>(vc[1], ct >> 1);
         const int o = 4 * (ct & 1);
         return h8{a[o], a[o + 1], a[o + 2], a[o + 3], b[o], b[o + 1], b[o + 2], b[o + 3]};
     });
-    wave_sync();   // LDS meta slots are rewritten by the next unit
 }
 
 // One 32-token unit of the fp16 residual ring: tokens t0 .. t0+31 (< n).
@@ -394,11 +464,27 @@ __device__ __forceinline__ void process_residual(WaveAcc& A, const Layout& L, co
     });
 }
 
+// s_waitcnt immediate that waits for all LDS operations of the wave.
+constexpr int kLgkmZero = 15 | (3 << 14) | (7 << 4);
+
+// A wave's [16][128] fp32 accumulator image after the unit loop.
+__device__ __forceinline__ float* wave_acc(uint8_t* stage_a, uint8_t* stage_b, int w, int pitch) {
+    return (float*)((w < 2 ? stage_a : stage_b) + (w & 1) * 16 * kD * 4);
+}
+
+// At most 128 registers: four waves per SIMD (four workgroups per CU when the
+// stage buffers allow it).
 template <int G, int KB, int VB, bool LP>
-__global__ __launch_bounds__(256) void attn_kernel(Layout L, kvq_cache c, const half_t* __restrict__ q,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void attn_kernel(Layout L, kvq_cache c, const half_t* __restrict__ q,
                                                    float sl2, float* __restrict__ ws,
                                                    int gq, int splits, int ups) {
-    __shared__ AttnSmem<G> sm;
+    using S = Stage<G, KB, VB>;
+    // Two stage buffers per wave (ping-pong), in two arrays: the compiler
+    // treats them as separate objects.  After the unit loop the same memory
+    // holds the waves' accumulators (waves 0-1 in stage_a, 2-3 in stage_b).
+    __shared__ __attribute__((aligned(16))) uint8_t stage_a[kWaves * S::PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_b[kWaves * S::PITCH];
+    __shared__ float wm[kWaves][16], wl[kWaves][16], wpz[kWaves][16];
     const int sp = blockIdx.x;
     const int sh = blockIdx.y;
     const int b = sh / L.H, h = sh % L.H;
@@ -420,6 +506,9 @@ __global__ __launch_bounds__(256) void attn_kernel(Layout L, kvq_cache c, const 
         const uint4* qp = (const uint4*)(q + ((long)b * Hq + h * gq + (hv ? hd : 0)) * kD + 32 * g);
 #pragma unroll
         for (int j = 0; j < 4; ++j) Q.q[j] = words_h8(hv ? qp[j] : make_uint4(0, 0, 0, 0));
+        // The unit loop's loads are invisible to the compiler's wait counting:
+        // retire these here so that it places no wait on them inside the loop.
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
     WaveAcc A;
     acc_init(A);
@@ -434,15 +523,33 @@ __global__ __launch_bounds__(256) void attn_kernel(Layout L, kvq_cache c, const 
         const int q1 = min(u1, uq);
         int u = u0 + wave;
         if (u < q1) {
-            UnitRaw<G, KB, VB> ra, rb;
-            load_unit(ra, L, c, b, h, u, ngroups, lane);
+            // Direct-to-LDS loads: unit u is staged in one buffer while the
+            // previous one is processed from the other.  The waits are explicit
+            // (vmcnt counts this wave's outstanding loads, in issue order).
+            lds_u8* const sa = (lds_u8*)(stage_a + wave * S::PITCH);
+            lds_u8* const sb = (lds_u8*)(stage_b + wave * S::PITCH);
+            uint32_t ha = issue_unit<G, KB, VB>(sa, L, c, b, h, u, ngroups, lane), hb = 0;
             for (;;) {
-                load_unit(rb, L, c, b, h, u + kWaves < q1 ? u + kWaves : u, ngroups, lane);
-                process_unit<G, KB, VB, LP>(sm, A, ra, Q, sl2, wave, lane);
+                if (u + kWaves < q1) {
+                    __builtin_amdgcn_s_waitcnt(kLgkmZero);   // last reads of sb returned
+                    hb = issue_unit<G, KB, VB>(sb, L, c, b, h, u + kWaves, ngroups, lane);
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::LOADS));
+                } else {
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                }
+                wave_sync();
+                process_unit<G, KB, VB, LP>(sa, ha, A, Q, sl2, lane);
                 u += kWaves;
                 if (u >= q1) break;
-                load_unit(ra, L, c, b, h, u + kWaves < q1 ? u + kWaves : u, ngroups, lane);
-                process_unit<G, KB, VB, LP>(sm, A, rb, Q, sl2, wave, lane);
+                if (u + kWaves < q1) {
+                    __builtin_amdgcn_s_waitcnt(kLgkmZero);
+                    ha = issue_unit<G, KB, VB>(sa, L, c, b, h, u + kWaves, ngroups, lane);
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::LOADS));
+                } else {
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                }
+                wave_sync();
+                process_unit<G, KB, VB, LP>(sb, hb, A, Q, sl2, lane);
                 u += kWaves;
                 if (u >= q1) break;
             }
@@ -452,17 +559,23 @@ __global__ __launch_bounds__(256) void attn_kernel(Layout L, kvq_cache c, const 
         if (u >= uq) process_residual<LP>(A, L, c, sh, nq + 32 * (u - uq), n, Q, sl2, lane);
 
     // Wave results -> LDS: totals over the lane groups, accumulators by head.
+    // The accumulators reuse the stage buffers: every wave has consumed its
+    // staged units and has no load in flight once all have passed the barrier.
     const float lt = group_sum(A.l);
     const float pzt = group_sum(A.pz);
+    __syncthreads();
     if (lane < 16) {
-        sm.wm[wave][lane] = A.m;
-        sm.wl[wave][lane] = lt;
-        sm.wpz[wave][lane] = pzt;
+        wm[wave][lane] = A.m;
+        wl[wave][lane] = lt;
+        wpz[wave][lane] = pzt;
     }
+    {
+        float* wacc = wave_acc(stage_a, stage_b, wave, S::PITCH);
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
+        for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sm.wacc[wave][4 * g + i][16 * ct + n16] = A.acc[ct][i];
+            for (int i = 0; i < 4; ++i) wacc[(4 * g + i) * kD + 16 * ct + n16] = A.acc[ct][i];
+    }
     __syncthreads();
 
     // Workgroup partial (heads < gq) -> workspace.
@@ -471,16 +584,17 @@ __global__ __launch_bounds__(256) void attn_kernel(Layout L, kvq_cache c, const 
         const int hh = idx >> 7, ch = idx & (kD - 1);
         float M = kNegInf;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.wm[w][hh]);
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w][hh]);
         float o = 0.0f, Ls = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float mw = sm.wm[w][hh];
+            const float mw = wm[w][hh];
             const float f = mw == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
             // LP: rows hh and hh+8 hold the high- and low-limb sums of head hh
-            const float a = LP ? sm.wacc[w][hh][ch] + sm.wacc[w][hh + 8][ch] : sm.wacc[w][hh][ch];
-            o += (a + sm.wpz[w][hh]) * f;
-            Ls += sm.wl[w][hh] * f;
+            const float* wacc = wave_acc(stage_a, stage_b, w, S::PITCH);
+            const float a = LP ? wacc[hh * kD + ch] + wacc[(hh + 8) * kD + ch] : wacc[hh * kD + ch];
+            o += (a + wpz[w][hh]) * f;
+            Ls += wl[w][hh] * f;
         }
         part[hh * kPart + ch] = o;
         if (ch == 0) {

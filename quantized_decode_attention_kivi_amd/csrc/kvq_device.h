@@ -23,7 +23,9 @@ __device__ __forceinline__ uint8_t* record_at(const Layout& L, void* packed, con
     long idx;
     if (L.paged) {
         if (g < 0 || g >= L.max_blocks) return nullptr;
-        int id = bt[(long)b * L.max_blocks + g];
+        // read through the constant address space: a scalar load when the
+        // index is wave uniform (the table does not change during a kernel)
+        const int id = *(const __attribute__((address_space(4))) int32_t*)(bt + (long)b * L.max_blocks + g);
         if (id < 0 || id >= L.num_blocks) return nullptr;
         idx = (long)id * L.H + h;
     } else {
