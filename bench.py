@@ -49,7 +49,8 @@ def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
-    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed decode steps first (enough to bring the GPU clocks up)")
     ap.add_argument("--workload", default="llama3_8b_layer_b8_32k_int4")
     ap.add_argument("--prefill-reps", type=int, default=5)
     ap.add_argument("--copies", type=int, default=0, help="cache copies rotated per step (0: auto)")
@@ -272,24 +273,35 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     w = synth.WORKLOADS[args.workload]
-    if w.paged or w.layers != 1:
-        print("bench.py times the contiguous single-layer workloads", file=sys.stderr)
-        sys.exit(2)
     lens = synth.seq_lengths(w).astype(np.int64)
     L = int(lens.max())
-    print("# generating %s: B=%d Hkv=%d Hq=%d n=%d k%d/v%d G=%d R=%d" % (
-        w.name, w.num_seqs, w.num_kv_heads, w.num_q_heads, L, w.k_bits, w.v_bits, w.group_size, w.residual),
-        file=sys.stderr, flush=True)
+    print("# generating %s: B=%d Hkv=%d Hq=%d n=%d..%d k%d/v%d G=%d R=%d%s%s" % (
+        w.name, w.num_seqs, w.num_kv_heads, w.num_q_heads, int(lens.min()), L, w.k_bits, w.v_bits,
+        w.group_size, w.residual, " paged" if w.paged else "",
+        " (%d layers folded into the batch)" % w.layers if w.layers > 1 else ""), file=sys.stderr, flush=True)
     K, V = synth.make_kv(w, max_len=L, device=dev)
     q = synth.make_query(w, device=dev)
-    total_steps = args.warmup + args.steps
+    total_steps = args.warmup + 2 * args.steps
     toks = [synth.make_tokens(w, s, device=dev) for s in range(total_steps)]
 
     abytes = attention_bytes(lens, w)
     copies = args.copies or min(64, max(2, math.ceil(2 * MALL_BYTES / abytes)))
-    shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, w.group_size, w.residual,
-                           max_tokens=L + total_steps + 8)
+    if w.paged:
+        G, R = w.group_size, w.residual
+        grow = total_steps + 8
+        mb = (L + grow - R) // G + 1
+        nb = int(sum(n_quant(int(n) + grow, G, R) // G for n in lens)) + 8
+        shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, G, R, paged=True,
+                               num_blocks=nb, max_blocks_per_seq=mb)
+    else:
+        shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, w.group_size, w.residual,
+                               max_tokens=L + total_steps + 8)
     caches = [kvq.QuantizedKVCache(shape, device=dev) for _ in range(copies)]
+    if w.paged:
+        # blocks handed out in a shuffled order: a fragmented pool, as after
+        # many requests have come and gone
+        for i, c in enumerate(caches):
+            c.shuffle_free_blocks(1000 + i)
     stream = torch.cuda.current_stream()
 
     # ---- prefill (bulk quantize) leg ------------------------------------
@@ -307,42 +319,63 @@ def main():
     torch.cuda.synchronize()
     pre_t = float(np.mean([a.elapsed_time(b) for a, b in pre_ms]))
     pbytes = prefill_bytes(lens, w)
+    if args.no_cpu_baseline:
+        del K, V
+        K = V = None
 
     # ---- decode steps ---------------------------------------------------
     outs = [torch.empty((w.num_seqs, w.num_q_heads, 128), dtype=torch.float32, device=dev) for _ in caches]
     for c in caches:
         c.workspace(w.num_q_heads)
 
-    def step(s, ev=None):
+    def step(s, ev=None, split=False):
         c = caches[s % copies]
         kn, vn = toks[s]
         c.append(kn, vn)
-        c.decode_attention(q, out=outs[s % copies], split_events=ev)
+        if split:
+            c.decode_attention(q, out=outs[s % copies], split_events=ev)
+        else:
+            ev[0].record(stream)
+            c.decode_attention(q, out=outs[s % copies])
+            ev[1].record(stream)
+
+    def bytes_at(s):
+        # attention bytes at step s (every copy grows by one token per append)
+        return attention_bytes(lens + (s // copies + 1), w)
 
     for s in range(args.warmup):
-        step(s)
+        c = caches[s % copies]
+        c.append(*toks[s])
+        c.decode_attention(q, out=outs[s % copies])
     torch.cuda.synchronize()
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
-    # attention bytes at each timed step (lengths grow by one per step)
-    step_bytes = []
-    for i in range(args.steps):
-        s = args.warmup + i
-        cnt = s // copies + 1  # appends this copy has seen once step s is done
-        step_bytes.append(attention_bytes(lens + cnt, w))
+    # timed region 1: whole decode steps; the attention call bracketed by two
+    # events (start, end) on the stream
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(args.steps)]
+    step_bytes = [bytes_at(args.warmup + i) for i in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # whole attention call (split-K kernel + merge) and the split-K kernel alone
-    attn_ms = np.array([a.elapsed_time(c) for a, _, c in evs])
-    kern_ms = np.array([a.elapsed_time(b) for a, b, _ in evs])
+    attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    # timed region 2: the same steps with a third event between the split-K
+    # kernel and the merge kernel (the extra event itself costs ~2 us, so
+    # the whole-call figure comes from region 1)
+    s0 = args.warmup + args.steps
+    evs2 = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    step_bytes2 = [bytes_at(s0 + i) for i in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(s0 + i, evs2[i], split=True)
+    torch.cuda.synchronize()
+    kern_ms = np.array([a.elapsed_time(b) for a, b, _ in evs2])
+    merge_ms = np.array([b.elapsed_time(c) for _, b, c in evs2])
     attn_avg_s = float(attn_ms.mean()) / 1e3
     kern_avg_s = float(kern_ms.mean()) / 1e3
     bytes_avg = float(np.mean(step_bytes))
     achieved = bytes_avg / attn_avg_s / 1e9
-    kern_achieved = bytes_avg / kern_avg_s / 1e9
+    kern_achieved = float(np.mean(step_bytes2)) / kern_avg_s / 1e9
     ms_per_step = wall / args.steps * 1e3
 
     digest = source_digest(ATTN_KERNEL_SOURCES)
@@ -365,12 +398,14 @@ def main():
             "num_seqs": w.num_seqs, "context": L, "num_q_heads": w.num_q_heads,
             "num_kv_heads": w.num_kv_heads, "head_dim": 128, "k_bits": w.k_bits, "v_bits": w.v_bits,
             "group_size": w.group_size, "residual": w.residual, "cache_copies_rotated": copies,
+            "paged": w.paged, "layers": w.layers, "min_context": int(lens.min()),
+            "tokens": int(lens.sum()),
         },
         "pct_of_hbm_peak": round(100.0 * achieved / HBM_PEAK_GBS, 2),
         "attention_us": round(attn_avg_s * 1e6, 3),
         "attention_us_median": round(float(np.median(attn_ms)) * 1e3, 3),
         "attention_kernel_us": round(kern_avg_s * 1e6, 3),
-        "merge_kernel_us": round((attn_avg_s - kern_avg_s) * 1e6, 3),
+        "merge_kernel_us": round(float(merge_ms.mean()) * 1e3, 3),
         "attention_bytes_per_launch": int(bytes_avg),
         "quantize_tokens_per_s": round(float(lens.sum()) / (pre_t / 1e3), 1),
         "quantize_gbs": round(pbytes / (pre_t / 1e3) / 1e9, 2),
@@ -389,6 +424,10 @@ def main():
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, K, V, q, lens, args.cpu_seconds)
+    res["quantize_token_layers_per_s"] = res["quantize_tokens_per_s"]
+    if w.layers > 1:
+        # n tokens of context across all layers: token count per layer
+        res["quantize_tokens_per_s"] = round(float(lens.sum()) / w.layers / (pre_t / 1e3), 1)
     print(json.dumps(res), flush=True)
 
 

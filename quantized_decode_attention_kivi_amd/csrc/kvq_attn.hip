@@ -472,6 +472,19 @@ __device__ __forceinline__ float* wave_acc(uint8_t* stage_a, uint8_t* stage_b, i
     return (float*)((w < 2 ? stage_a : stage_b) + (w & 1) * 16 * kD * 4);
 }
 
+// Wave priority from the share of this wave's units still to do (3: more
+// than 3/4 left ... 0: under 1/4).  Waves issue oldest-first, so without
+// this the first workgroup placed on a CU runs ahead and the CU spends the
+// end of the kernel with few waves; lagging waves now win arbitration and
+// the workgroups of a CU finish close together.
+__device__ __forceinline__ void set_progress_prio(int left, int total) {
+    const int lvl = (4 * left - 1) / total;   // 0..3 for 1 <= left <= total
+    if (lvl >= 3) __builtin_amdgcn_s_setprio(3);
+    else if (lvl == 2) __builtin_amdgcn_s_setprio(2);
+    else if (lvl == 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
 // At most 128 registers: four waves per SIMD (four workgroups per CU when the
 // stage buffers allow it).
 template <int G, int KB, int VB, bool LP>
@@ -521,6 +534,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
     const int u0 = sp * ups, u1 = min(u0 + ups, units);
     {
         const int q1 = min(u1, uq);
+        const int ntot = max(1, (q1 - (u0 + wave) + kWaves - 1) / kWaves);   // this wave's units
         int u = u0 + wave;
         if (u < q1) {
             // Direct-to-LDS loads: unit u is staged in one buffer while the
@@ -538,6 +552,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
                 }
                 wave_sync();
+                set_progress_prio((q1 - u + kWaves - 1) / kWaves, ntot);
                 process_unit<G, KB, VB, LP>(sa, ha, A, Q, sl2, lane);
                 u += kWaves;
                 if (u >= q1) break;
@@ -549,6 +564,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
                 }
                 wave_sync();
+                set_progress_prio((q1 - u + kWaves - 1) / kWaves, ntot);
                 process_unit<G, KB, VB, LP>(sb, hb, A, Q, sl2, lane);
                 u += kWaves;
                 if (u >= q1) break;

@@ -14,7 +14,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from dataclasses import dataclass
+from dataclasses import dataclass, replace
 
 import numpy as np
 import torch
@@ -222,6 +222,45 @@ class QuantizedKVCache:
                                self.block_table.data_ptr() if self.block_table is not None else None)
         self._ws = None
 
+    def sequence_view(self, b: int) -> "QuantizedKVCache":
+        """Read-only cache of sequence b alone, sharing this cache's memory.
+
+        A sequence of a cache is itself a valid one-sequence cache: its
+        records (contiguous mode; paged mode keeps the shared block pool and
+        uses the sequence's block-table row), its residual ring and its two
+        counters sit at fixed offsets.  Used to export or dequantize single
+        sequences of caches too large to export whole."""
+        if not 0 <= b < self.shape.num_seqs:
+            raise IndexError(b)
+        v = object.__new__(QuantizedKVCache)
+        v.shape = replace(self.shape, num_seqs=1)
+        v.cfg = v.shape.config()
+        v.sizes = kvq_buffer_sizes(v.cfg)
+        v.device = self.device
+        v._parent = self
+        v._view = True
+        per_ring = v.sizes.residual_bytes // 2
+        if self.shape.paged:
+            v.packed = self.packed
+        else:
+            per = v.sizes.packed_bytes
+            v.packed = self.packed[b * per:(b + 1) * per]
+        v.k_res = self.k_res[b * per_ring:(b + 1) * per_ring]
+        v.v_res = self.v_res[b * per_ring:(b + 1) * per_ring]
+        v.n_tokens = self.n_tokens[b:b + 1]
+        v.n_quant = self.n_quant[b:b + 1]
+        v.block_table = self.block_table[b:b + 1] if self.block_table is not None else None
+        v.lens = self.lens[b:b + 1].copy()
+        v.cache = kvq_cache(v.packed.data_ptr(), v.k_res.data_ptr(), v.v_res.data_ptr(),
+                            v.n_tokens.data_ptr(), v.n_quant.data_ptr(),
+                            v.block_table.data_ptr() if v.block_table is not None else None)
+        v._ws = None
+        return v
+
+    def _writable(self, what):
+        if getattr(self, "_view", False):
+            raise KVQError(KVQ_EINVAL, "%s on a read-only sequence view" % what)
+
     @property
     def G(self):
         return self.shape.group_size
@@ -266,6 +305,7 @@ class QuantizedKVCache:
         """k, v: fp16 [B][H][max_len][d] on the device; seq_lens: ints [B]
         (host).  seq_lens_device: optional int32 device copy of seq_lens,
         reused instead of a fresh host-to-device copy."""
+        self._writable("prefill")
         lens = np.asarray(seq_lens, np.int64)
         B, H, max_len, d = k.shape
         if (B, H, d) != (self.shape.num_seqs, self.shape.num_kv_heads, HEAD_DIM) or k.shape != v.shape:
@@ -287,6 +327,7 @@ class QuantizedKVCache:
 
     def append(self, k_new, v_new, stream=None):
         """k_new, v_new: fp16 [B][H][d] on the device."""
+        self._writable("append")
         if np.any(self.lens + 1 > self.capacity()):
             raise KVQError(KVQ_ECAPACITY, "kv_append_token: a sequence is full")
         self._ensure_blocks(self.lens + 1)

@@ -141,13 +141,26 @@ def make_tokens(w: Workload, step: int, device="cpu", k_outlier=20.0):
     B, H, d = w.num_seqs, w.num_kv_heads, w.head_dim
     g = _gen(device, seed_for(w.tag, 0, 5, step))
     k = torch.randn((B, H, d), generator=g, device=device, dtype=torch.float32)
-    per_layer = max(1, w.num_seqs // w.layers)
-    for b in range(B):
-        for h in range(H):
-            ch = torch.as_tensor(outlier_channels(w, b // per_layer, h), device=device)
-            k[b, h, ch] *= k_outlier
+    k *= torch.as_tensor(_outlier_gain(w, k_outlier), device=device)
     v = torch.randn((B, H, d), generator=g, device=device, dtype=torch.float32)
     return k.to(torch.float16), v.to(torch.float16)
+
+
+_GAIN_CACHE = {}
+
+
+def _outlier_gain(w: Workload, k_outlier: float) -> np.ndarray:
+    """[B][H][d] multipliers: k_outlier on each (sequence, head)'s outlier
+    channels (those of the sequence's layer), 1 elsewhere."""
+    key = (w, k_outlier)
+    if key not in _GAIN_CACHE:
+        per_layer = max(1, w.num_seqs // w.layers)
+        gain = np.ones((w.num_seqs, w.num_kv_heads, w.head_dim), np.float32)
+        for b in range(w.num_seqs):
+            for h in range(w.num_kv_heads):
+                gain[b, h, outlier_channels(w, b // per_layer, h)] = k_outlier
+        _GAIN_CACHE[key] = gain
+    return _GAIN_CACHE[key]
 
 
 def random_fp16(shape, seed: int, scale: float = 1.0) -> np.ndarray:

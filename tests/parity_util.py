@@ -43,33 +43,40 @@ def oracle_states(kb: np.ndarray, vb: np.ndarray, lens, w: synth.Workload, cap=N
 
 
 def compare_codes(cache: kvq.QuantizedKVCache, states, streams=None):
-    """Bit-exact comparison of codes, scales, zeros and dequantized values."""
+    """Bit-exact comparison of codes, scales, zeros and dequantized values of
+    the (b, h) streams (default: all), exported one sequence at a time through
+    read-only sequence views of the cache."""
     torch.cuda.synchronize()
-    T = max(int(cache.lens.max()), 1)
-    kc, vc, ks, kz, vs, vz = [t.cpu().numpy() for t in cache.export_codes(T)]
-    ks, kz, vs, vz = (a.view(np.uint16) for a in (ks, kz, vs, vz))
-    kd, vd = [t.cpu().numpy() for t in cache.dequantize(T)]
-    nt = cache.n_tokens.cpu().numpy()
-    nqs = cache.n_quant.cpu().numpy()
-    G = cache.G
-    B, H = kc.shape[:2]
+    B, H = cache.shape.num_seqs, cache.shape.num_kv_heads
     streams = streams if streams is not None else [(b, h) for b in range(B) for h in range(H)]
+    by_seq = {}
     for b, h in streams:
-        st = states[b][h]
-        assert nt[b] == st.n and nqs[b] == st.nq, (b, nt[b], st.n, nqs[b], st.nq)
-        nq, n = st.nq, st.n
-        assert np.array_equal(kc[b, h, :nq], st.key_codes()), ("key codes", b, h)
-        assert np.array_equal(vc[b, h, :nq], st.value_codes()), ("value codes", b, h)
-        oks, okz = st.key_meta()
-        assert np.array_equal(ks[b, h, :nq // G], oks), ("key scales", b, h)
-        assert np.array_equal(kz[b, h, :nq // G], okz), ("key zeros", b, h)
-        ovs, ovz = st.value_meta()
-        assert np.array_equal(vs[b, h, :nq], ovs), ("value scales", b, h)
-        assert np.array_equal(vz[b, h, :nq], ovz), ("value zeros", b, h)
-        okd, ovd = st.dequantize()
-        assert np.array_equal(kd[b, h, :n], okd), ("dequantized keys", b, h)
-        assert np.array_equal(vd[b, h, :n], ovd), ("dequantized values", b, h)
-        assert np.all(kd[b, h, n:] == 0) and np.all(vd[b, h, n:] == 0)
+        by_seq.setdefault(b, []).append(h)
+    G = cache.G
+    for b, heads in sorted(by_seq.items()):
+        view = cache.sequence_view(b)
+        T = int(view.lens.max()) + G     # a group past the end: must read back as zeros
+        kc, vc, ks, kz, vs, vz = [t[0].cpu().numpy() for t in view.export_codes(T)]
+        ks, kz, vs, vz = (a.view(np.uint16) for a in (ks, kz, vs, vz))
+        kd, vd = [t[0].cpu().numpy() for t in view.dequantize(T)]
+        nt = int(view.n_tokens.cpu()[0])
+        nqs = int(view.n_quant.cpu()[0])
+        for h in heads:
+            st = states[b][h]
+            assert nt == st.n and nqs == st.nq, (b, nt, st.n, nqs, st.nq)
+            nq, n = st.nq, st.n
+            assert np.array_equal(kc[h, :nq], st.key_codes()), ("key codes", b, h)
+            assert np.array_equal(vc[h, :nq], st.value_codes()), ("value codes", b, h)
+            oks, okz = st.key_meta()
+            assert np.array_equal(ks[h, :nq // G], oks), ("key scales", b, h)
+            assert np.array_equal(kz[h, :nq // G], okz), ("key zeros", b, h)
+            ovs, ovz = st.value_meta()
+            assert np.array_equal(vs[h, :nq], ovs), ("value scales", b, h)
+            assert np.array_equal(vz[h, :nq], ovz), ("value zeros", b, h)
+            okd, ovd = st.dequantize()
+            assert np.array_equal(kd[h, :n], okd), ("dequantized keys", b, h)
+            assert np.array_equal(vd[h, :n], ovd), ("dequantized values", b, h)
+            assert np.all(kd[h, n:] == 0) and np.all(vd[h, n:] == 0)
 
 
 def oracle_attention(q16: np.ndarray, states, scale, rows=None):

@@ -146,3 +146,32 @@ def test_calls_reject_bad_arguments_before_launch():
     pcfg = _cfg(kvq, group_size=16, residual=32, max_tokens=0, block_size=16, num_blocks=8, max_blocks_per_seq=4)
     assert L.kv_append_token(by(pcfg), by(cache), vp(good), vp(good), None) == kvq.KVQ_EINVAL
     assert L.kvq_status_string(kvq.KVQ_ECAPACITY).decode() == "buffer or workspace too small"
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_sequence_view_offsets(paged):
+    """A sequence view is the one-sequence cache at fixed offsets of the
+    parent's buffers (host tensors here; no kernel is called)."""
+    kvq = _kvq()
+    if paged:
+        shape = kvq.CacheShape(5, 3, 4, 2, 16, 32, paged=True, num_blocks=40, max_blocks_per_seq=9)
+    else:
+        shape = kvq.CacheShape(5, 3, 4, 2, 32, 64, max_tokens=700)
+    c = kvq.QuantizedKVCache(shape, device="cpu")
+    one = kvq.kvq_buffer_sizes(kvq.CacheShape(**{**shape.__dict__, "num_seqs": 1}).config())
+    for b in (0, 2, 4):
+        v = c.sequence_view(b)
+        assert v.cfg.num_seqs == 1
+        if paged:
+            assert v.cache.packed == c.cache.packed
+            assert v.cache.block_table == c.cache.block_table + b * shape.max_blocks_per_seq * 4
+        else:
+            assert v.cache.packed == c.cache.packed + b * one.packed_bytes
+        assert v.cache.k_res == c.cache.k_res + b * one.residual_bytes
+        assert v.cache.v_res == c.cache.v_res + b * one.residual_bytes
+        assert v.cache.n_tokens == c.cache.n_tokens + 4 * b
+        assert v.cache.n_quant == c.cache.n_quant + 4 * b
+    with pytest.raises(kvq.KVQError):
+        c.sequence_view(1).append(None, None)
+    with pytest.raises(IndexError):
+        c.sequence_view(5)

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from quantized_decode_attention_kivi_amd import synth
 from parity_util import (compare_attention, compare_codes, make_cache, oracle_attention, oracle_states,
                          to_bits)
@@ -164,6 +165,56 @@ def test_full_size_workload(name):
     out = cache.decode_attention(q, SCALE)
     torch.cuda.synchronize()
     compare_attention(out.cpu().numpy(), oracle_attention(to_bits(q), states, SCALE))
+
+
+def test_full_size_paged_workload():
+    """The paged workload at full size (64 sequences of 1K-16K tokens, G = 16
+    blocks handed out from a shuffled pool): sampled sequences bit-exact,
+    every attention row."""
+    w = synth.WORKLOADS["paged_64seq_1k_16k_k4v2"]
+    cache, states, _, _ = _run_prefill(w)
+    compare_codes(cache, states, streams=[(0, 0), (17, 3), (w.num_seqs - 1, w.num_kv_heads - 1)])
+    q = synth.make_query(w, device="cuda")
+    out = cache.decode_attention(q, SCALE)
+    torch.cuda.synchronize()
+    compare_attention(out.cpu().numpy(), oracle_attention(to_bits(q), states, SCALE))
+
+
+def test_full_size_80_layer_cache():
+    """The 80-layer, 128K-token INT2 cache with the layers folded into the
+    batch (43 GB of fp16 input, 7 GB packed): sampled (layer, kv head) streams
+    are quantized by the oracle from the same input bits and must match bit
+    for bit; their query rows of one decode call must match the oracle."""
+    w = synth.WORKLOADS["llama3_70b_cache_80l_128k_int2"]
+    lens = synth.seq_lengths(w)
+    L = int(lens.max())
+    print("generating %s (%d x %d x %d x 128 fp16, K and V)" % (w.name, w.num_seqs, w.num_kv_heads, L), flush=True)
+    K, V = synth.make_kv(w, max_len=L, device="cuda")
+    cache = make_cache(w, lens)
+    cache.prefill(K, V, lens)
+    torch.cuda.synchronize()
+    samples = [(0, 0), (37, 5), (w.num_seqs - 1, w.num_kv_heads - 1)]
+    states = {}
+    for b, h in samples:
+        print("oracle prefill of stream", (b, h), flush=True)
+        states.setdefault(b, {})[h] = oracle.StreamState.prefill(to_bits(K[b, h]), to_bits(V[b, h]), w.k_bits,
+                                                                 w.v_bits, w.group_size, w.residual)
+    del K, V
+    torch.cuda.empty_cache()
+    compare_codes(cache, states, streams=samples)
+    q = synth.make_query(w, device="cuda")
+    out = cache.decode_attention(q, SCALE)
+    torch.cuda.synchronize()
+    got, ref = [], []
+    qf = oracle.h2f(to_bits(q))
+    for b, h in samples:
+        kh, vh = states[b][h].dequantize()
+        hqs = list(range(h * w.gq, (h + 1) * w.gq))
+        ref.append(oracle.attention(qf[b, hqs], kh, vh, SCALE))
+        got.append(out[b, hqs].cpu().numpy())
+    compare_attention(np.concatenate(got), np.concatenate(ref))
+    del cache
+    torch.cuda.empty_cache()
 
 
 def test_split_entry_points_equal_combined_call():
