@@ -161,10 +161,11 @@ size_t kv_decode_attention_workspace_bytes(const kvq_config *cfg, int32_t num_q_
  * against keys whose per-group range is below ~1000).
  * workspace: 256-byte aligned device memory of at least
  * kv_decode_attention_workspace_bytes(cfg, Hq) bytes that receives the
- * per-split partial results (no initialisation needed, content not preserved
- * between calls).  Two kernels are enqueued: the split-K attention and the
- * log-sum-exp merge that writes out; calls sharing a workspace must be
- * ordered on one stream. */
+ * partial results (no initialisation needed, content not preserved between
+ * calls).  Two kernels are enqueued: the attention, in which every workgroup
+ * takes an equal share of all (sequence, kv head, 32-token unit) work of the
+ * batch whatever the sequence lengths, and the log-sum-exp merge that writes
+ * out; calls sharing a workspace must be ordered on one stream. */
 kvq_status kv_decode_attention(const kvq_config *cfg, const kvq_cache *cache,
                                const void *q, int32_t num_q_heads, float softmax_scale,
                                float *out, void *workspace, size_t workspace_bytes,
@@ -176,18 +177,21 @@ kvq_status kv_decode_attention(const kvq_config *cfg, const kvq_cache *cache,
  * by log-sum-exp).
  *
  * kv_decode_attention_partials: same arguments and checks as
- * kv_decode_attention without `out`; writes, for every (sequence, kv head),
- * `parts` partial results of Hq/H heads x 132 floats into the workspace:
- * output[128] (unnormalised), running max (log2 units), sum of weights, pad.
+ * kv_decode_attention without `out`; writes partial results of Hq/H heads x
+ * 132 floats each (output[128] unnormalised, running max in log2 units, sum
+ * of weights, pad) into the workspace, every (sequence, kv head) with
+ * tokens getting one or more, and records per (sequence, kv head) where its
+ * partials are.
  *
- * kv_decode_attention_merge: reads those partials for the same cfg and
- * num_q_heads and writes out fp32 [B][Hq][d]. */
+ * kv_decode_attention_merge: reads those partials for the same cfg, cache
+ * counters and num_q_heads (the cache must not change in between) and writes
+ * out fp32 [B][Hq][d] (0 for an empty sequence). */
 kvq_status kv_decode_attention_partials(const kvq_config *cfg, const kvq_cache *cache,
                                         const void *q, int32_t num_q_heads, float softmax_scale,
                                         void *workspace, size_t workspace_bytes, void *stream);
-kvq_status kv_decode_attention_merge(const kvq_config *cfg, int32_t num_q_heads,
-                                     const void *workspace, size_t workspace_bytes, float *out,
-                                     void *stream);
+kvq_status kv_decode_attention_merge(const kvq_config *cfg, const kvq_cache *cache,
+                                     int32_t num_q_heads, const void *workspace,
+                                     size_t workspace_bytes, float *out, void *stream);
 
 /* Logical view of the quantized part (test hook).  k_codes, v_codes: uint8
  * [B][H][out_tokens][d], one code per element for t < n_q[b], 0 elsewhere;

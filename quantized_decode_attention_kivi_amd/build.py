@@ -34,8 +34,24 @@ HIPCC_FLAGS = [
 
 # Per-source additions.  The attention kernels never produce or test for NaN
 # (masked slots are removed by selects, not arithmetic), so their max/min need
-# no NaN-quieting operand canonicalization.
-SOURCE_FLAGS = {"kvq_attn.hip": ["-fno-honor-nans"]}
+# no NaN-quieting operand canonicalization; their resource usage is reported
+# so that the build can reject any that spills to scratch.
+SOURCE_FLAGS = {"kvq_attn.hip": ["-fno-honor-nans", "-Rpass-analysis=kernel-resource-usage"]}
+NO_SCRATCH = {"kvq_attn.hip": "attn_kernel"}
+
+
+def scratch_users(remarks: str, name_part: str):
+    """Kernels whose name contains name_part and whose resource-usage remark
+    reports a nonzero ScratchSize."""
+    bad, current = [], None
+    for line in remarks.splitlines():
+        if "remark: Function Name:" in line:
+            current = line.split("Function Name:")[1].split("[")[0].strip()
+        elif "ScratchSize [bytes/lane]:" in line and current and name_part in current:
+            n = int(line.split("ScratchSize [bytes/lane]:")[1].split("[")[0])
+            if n:
+                bad.append((current, n))
+    return bad
 
 
 def hipcc() -> str:
@@ -54,6 +70,11 @@ def build(verbose: bool = False) -> str:
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError("hipcc failed for %s:\n%s%s" % (src, r.stdout, r.stderr))
+        if src in NO_SCRATCH:
+            bad = scratch_users(r.stderr, NO_SCRATCH[src])
+            if bad:
+                raise RuntimeError("%s: kernels spill to scratch (lower their waves-per-SIMD target): %s"
+                                   % (src, ", ".join("%s (%d B/lane)" % x for x in bad)))
         return obj
 
     with ThreadPoolExecutor(len(SOURCES)) as ex:

@@ -126,7 +126,8 @@ size_t kv_decode_attention_workspace_bytes(const kvq_config* cfg, int32_t num_q_
     Layout L;
     if (make_layout(cfg, &L) != KVQ_OK) return 0;
     if (num_q_heads < L.H || num_q_heads % L.H) return 0;
-    return plan_attention(L, num_q_heads).workspace;
+    const AttnPlan P = plan_attention(L, num_q_heads);
+    return P.fits ? P.workspace : 0;
 }
 
 static kvq_status check_attention(const kvq_config* cfg, const kvq_cache* cache, const void* q, int32_t num_q_heads,
@@ -141,6 +142,7 @@ static kvq_status check_attention(const kvq_config* cfg, const kvq_cache* cache,
     if (gq < 1 || gq > kMaxGq) return KVQ_EUNSUPPORTED;
     if (!(softmax_scale > 0.0f) || softmax_scale > 1e30f) return KVQ_EINVAL;
     *P = plan_attention(*L, num_q_heads);
+    if (!P->fits) return KVQ_EUNSUPPORTED;
     if (workspace_bytes < P->workspace) return KVQ_ECAPACITY;
     return KVQ_OK;
 }
@@ -156,18 +158,20 @@ kvq_status kv_decode_attention_partials(const kvq_config* cfg, const kvq_cache* 
                                                 workspace, (hipStream_t)stream));
 }
 
-kvq_status kv_decode_attention_merge(const kvq_config* cfg, int32_t num_q_heads, const void* workspace,
-                                     size_t workspace_bytes, float* out, void* stream) {
+kvq_status kv_decode_attention_merge(const kvq_config* cfg, const kvq_cache* cache, int32_t num_q_heads,
+                                     const void* workspace, size_t workspace_bytes, float* out, void* stream) {
     Layout L;
     kvq_status st = make_layout(cfg, &L);
     if (st != KVQ_OK) return st;
+    if ((st = check_cache(L, cache)) != KVQ_OK) return st;
     if (!workspace || !out || ((uintptr_t)workspace & 255)) return KVQ_EINVAL;
     if (num_q_heads < L.H || num_q_heads % L.H) return KVQ_EINVAL;
     const int gq = num_q_heads / L.H;
     if (gq < 1 || gq > kMaxGq) return KVQ_EUNSUPPORTED;
     const AttnPlan P = plan_attention(L, num_q_heads);
+    if (!P.fits) return KVQ_EUNSUPPORTED;
     if (workspace_bytes < P.workspace) return KVQ_ECAPACITY;
-    return hip_status(launch_attention_merge(L, P, num_q_heads, workspace, out, (hipStream_t)stream));
+    return hip_status(launch_attention_merge(L, P, *cache, num_q_heads, workspace, out, (hipStream_t)stream));
 }
 
 kvq_status kv_decode_attention(const kvq_config* cfg, const kvq_cache* cache, const void* q, int32_t num_q_heads,
@@ -181,7 +185,7 @@ kvq_status kv_decode_attention(const kvq_config* cfg, const kvq_cache* cache, co
     st = hip_status(launch_attention_partials(L, P, *cache, (const _Float16*)q, num_q_heads, softmax_scale,
                                               workspace, (hipStream_t)stream));
     if (st != KVQ_OK) return st;
-    return hip_status(launch_attention_merge(L, P, num_q_heads, workspace, out, (hipStream_t)stream));
+    return hip_status(launch_attention_merge(L, P, *cache, num_q_heads, workspace, out, (hipStream_t)stream));
 }
 
 kvq_status kv_export_codes(const kvq_config* cfg, const kvq_cache* cache, uint8_t* k_codes, uint8_t* v_codes,

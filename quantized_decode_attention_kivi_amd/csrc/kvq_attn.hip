@@ -30,6 +30,8 @@
 // small kernel merges the partials of each (stream, head) by log-sum-exp.
 // The kernel boundary makes the partials visible to it; a per-workgroup
 // device-scope release would write back the XCD's L2 once per workgroup.
+#include <algorithm>
+
 #include "kvq_device.h"
 
 namespace kvq {
@@ -138,6 +140,9 @@ struct Stage {
     static constexpr int LOADS = G == 32 ? KB / 2 + VB / 2 + 1 : 6;
 };
 
+// s_waitcnt immediate that waits for all LDS operations of the wave.
+constexpr int kLgkmZero = 15 | (3 << 14) | (7 << 4);
+
 // s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
 // memory operations of this wave are outstanding; other counters untouched.
 __device__ __forceinline__ constexpr int vmcnt_imm(int n) {
@@ -168,16 +173,22 @@ __device__ __forceinline__ void lds_load16(u32x4 desc, lds_u8* dst, int off) {
 // Issues the direct-to-LDS loads of one unit into stage buffer `buf` (wave
 // uniform address) and returns which of its records exist.  Every call issues
 // exactly Stage::LOADS load instructions, so the wait counts stay exact.
-template <int G, int KB, int VB>
+template <int G, int KB, int VB, bool PG>
 __device__ __forceinline__ uint32_t issue_unit(lds_u8* buf, const Layout& L, const kvq_cache& c, int b, int h,
                                                int unit, int ngroups, int lane) {
     using S = Stage<G, KB, VB>;
     const int g = lane >> 4, n = lane & 15;
+    // The buffer's LDS address, made opaque here so that the per-load M0
+    // values are formed next to each load rather than hoisted out of the unit
+    // loop into scalar registers of their own.
+    uint32_t base = (uint32_t)(uintptr_t)buf;
+    asm volatile("" : "+s"(base));
+    buf = (lds_u8*)(uintptr_t)base;
     uint32_t has = 0;
 #pragma unroll
     for (int i = 0; i < S::NR; ++i) {
         const int grp = unit * S::NR + i;
-        const uint8_t* rec = grp < ngroups ? record_at(L, c.packed, c.block_table, b, h, grp) : nullptr;
+        const uint8_t* rec = grp < ngroups ? record_at_t<PG>(L, c.packed, c.block_table, b, h, grp) : nullptr;
         has |= (rec != nullptr) << i;
         const u32x4 rs = record_desc(rec, L.record);
         if (G == 32) {
@@ -419,22 +430,44 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
     });
 }
 
+// Ring slot of token t0 + r (0 <= r < 32) given slot0 = t0 % ring; ring >= 16.
+__device__ __forceinline__ int ring_slot(int slot0, int r, int ring) {
+    int s = slot0 + r;
+    s -= s >= ring ? ring : 0;
+    s -= s >= ring ? ring : 0;
+    return s;
+}
+
 // One 32-token unit of the fp16 residual ring: tokens t0 .. t0+31 (< n).
 // Keys and query are exact fp16, so the key product needs one part (LP: the
-// high-limb columns carry it, the low-limb columns add zero).
+// high-limb columns carry it, the low-limb columns add zero).  The value rows
+// go straight to LDS (rows 0-15 to sva, 16-31 to svb, 256 bytes each; rows at
+// or past n read as zeros), from where each lane gathers its operand columns.
 template <bool LP>
 __device__ __forceinline__ void process_residual(WaveAcc& A, const Layout& L, const kvq_cache& c, long sh, int t0,
-                                                 int n, const QOps& Q, float sl2, int lane) {
+                                                 int n, const QOps& Q, float sl2, int lane, lds_u8* sva,
+                                                 lds_u8* svb) {
     const int g = lane >> 4, n16 = lane & 15;
+    const int slot0 = t0 % L.ring;
+    {
+        const uint8_t* vbase = (const uint8_t*)c.v_res + sh * L.ring * kD * 2;
+        const u32x4 vd = record_desc(vbase, L.ring * kD * 2);
+        __builtin_amdgcn_s_waitcnt(kLgkmZero);   // earlier reads of these buffers returned
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 4 * i + (lane >> 4);
+            const int off = t0 + r < n ? ring_slot(slot0, r, L.ring) * (kD * 2) + 16 * n16 : 0x40000000;
+            lds_load16(vd, i < 4 ? sva + 1024 * i : svb + 1024 * (i - 4), off);
+        }
+    }
     const half_t* kr = (const half_t*)c.k_res + sh * L.ring * kD;
-    const half_t* vr = (const half_t*)c.v_res + sh * L.ring * kD;
     f4 C[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-        const int t = t0 + 16 * rt + n16;
+        const int r = 16 * rt + n16;
         f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
-        const uint32_t keep = t < n ? 0xffffffffu : 0u;
-        const uint4* row = (const uint4*)(kr + (long)((t < n ? t : t0) % L.ring) * kD + 32 * g);
+        const uint32_t keep = t0 + r < n ? 0xffffffffu : 0u;
+        const uint4* row = (const uint4*)(kr + (long)(t0 + r < n ? ring_slot(slot0, r, L.ring) : slot0) * kD + 32 * g);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             uint4 w = row[j];
@@ -452,20 +485,19 @@ __device__ __forceinline__ void process_residual(WaveAcc& A, const Layout& L, co
         vz[k] = 0.0f;
         valid[k] = t0 + (k >> 2) * 16 + 4 * g + (k & 3) < n;
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the value rows are in LDS
+    wave_sync();
     softmax_and_values<LP>(A, x, vs, vz, valid, sl2, lane, [&](int ct) -> h8 {
         h8 b;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const int t = t0 + (k >> 2) * 16 + 4 * g + (k & 3);
-            const _Float16 x = vr[(long)((t < n ? t : t0) % L.ring) * kD + 16 * ct + n16];
-            b[k] = t < n ? x : (_Float16)0.0f;
+            const lds_u8* rows = (k >> 2) ? svb : sva;
+            b[k] = __builtin_bit_cast(_Float16, lds_read<uint16_t>(rows + (4 * g + (k & 3)) * (kD * 2) +
+                                                                   (16 * ct + n16) * 2));
         }
         return b;
     });
 }
-
-// s_waitcnt immediate that waits for all LDS operations of the wave.
-constexpr int kLgkmZero = 15 | (3 << 14) | (7 << 4);
 
 // A wave's [16][128] fp32 accumulator image after the unit loop.
 __device__ __forceinline__ float* wave_acc(uint8_t* stage_a, uint8_t* stage_b, int w, int pitch) {
@@ -485,31 +517,52 @@ __device__ __forceinline__ void set_progress_prio(int left, int total) {
     else __builtin_amdgcn_s_setprio(0);
 }
 
-// At most 128 registers: four waves per SIMD (four workgroups per CU when the
-// stage buffers allow it).
-template <int G, int KB, int VB, bool LP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void attn_kernel(Layout L, kvq_cache c, const half_t* __restrict__ q,
-                                                   float sl2, float* __restrict__ ws,
-                                                   int gq, int splits, int ups) {
+// 32-token units of sequence b: its quantized groups first (G = 16: two
+// records per unit), then its fp16 residual tokens.  Counters written by this
+// library satisfy 0 <= nq <= n <= nq + ring; the clamps keep any other value
+// inside the records and the ring.
+// In the flattened work split a residual unit counts kResCost times a
+// quantized one (its fp16 rows are gathered with plain loads, without the
+// staged prefetch): `cost` is the stream's length in those terms.
+constexpr int kResCost = 3;
+struct SeqUnits {
+    int nq, n, ngroups, uq, units, cost;
+};
+__device__ __forceinline__ SeqUnits seq_units(const Layout& L, const kvq_cache& c, int b) {
+    SeqUnits u;
+    u.nq = max(c.n_quant[b], 0);
+    u.n = min(max(c.n_tokens[b], u.nq), u.nq + L.ring);
+    u.ngroups = u.nq / L.G;
+    u.uq = (u.ngroups * L.G + 31) / 32;
+    u.units = u.uq + (u.n - u.nq + 31) / 32;
+    u.cost = u.uq + kResCost * (u.units - u.uq);
+    return u;
+}
+// First unit whose cost position is >= x (a unit belongs to the workgroup
+// that holds its first cost position).
+__device__ __forceinline__ int unit_at(const SeqUnits& u, int x) {
+    return x <= u.uq ? x : u.uq + (x - u.uq + kResCost - 1) / kResCost;
+}
+
+// Units [lo, hi) of stream (b, h) by the four waves of the workgroup (wave w
+// takes lo + w, lo + w + 4, ...), combined into one partial result (heads
+// < gq: output[128] unnormalised, running max in log2 units, weight sum) at
+// `part`.  Called by every thread of the workgroup.
+template <int G, int KB, int VB, bool LP, bool PG>
+__device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_b, float (*wm)[16], float (*wl)[16],
+                                               float (*wpz)[16], const Layout& L, const kvq_cache& c,
+                                               const half_t* __restrict__ q, float sl2, int gq, int b, int h,
+                                               const SeqUnits& su, int lo, int hi, float* __restrict__ part,
+                                               int lane, int wave) {
     using S = Stage<G, KB, VB>;
-    // Two stage buffers per wave (ping-pong), in two arrays: the compiler
-    // treats them as separate objects.  After the unit loop the same memory
-    // holds the waves' accumulators (waves 0-1 in stage_a, 2-3 in stage_b).
-    __shared__ __attribute__((aligned(16))) uint8_t stage_a[kWaves * S::PITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t stage_b[kWaves * S::PITCH];
-    __shared__ float wm[kWaves][16], wl[kWaves][16], wpz[kWaves][16];
-    const int sp = blockIdx.x;
-    const int sh = blockIdx.y;
-    const int b = sh / L.H, h = sh % L.H;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
+    // The lane index, produced afresh: per-lane addresses derived from it are
+    // formed here, once per segment, instead of being hoisted out of the
+    // segment loop and held (or spilled) across every unit loop.
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
     const int g = lane >> 4, n16 = lane & 15;
-    // counters written by this library satisfy 0 <= nq <= n <= nq + ring; clamp
-    // so that no other value can index outside the records or the ring
-    const int nq = max(c.n_quant[b], 0);
-    const int n = min(max(c.n_tokens[b], nq), nq + L.ring);
+    const int tid = wave * 64 + lane;
     const int Hq = L.H * gq;
-    const int parts = splits;
+    const long sh = (long)b * L.H + h;
 
     QOps Q;
     {
@@ -526,27 +579,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
     WaveAcc A;
     acc_init(A);
 
-    // Units of this stream: the quantized ones first, then the 32-token units
-    // of the fp16 residual ring; split sp takes units [sp*ups, sp*ups + ups).
-    const int ngroups = nq / L.G;
-    const int uq = (ngroups * L.G + 31) / 32;
-    const int units = uq + (n - nq + 31) / 32;
-    const int u0 = sp * ups, u1 = min(u0 + ups, units);
     {
-        const int q1 = min(u1, uq);
-        const int ntot = max(1, (q1 - (u0 + wave) + kWaves - 1) / kWaves);   // this wave's units
-        int u = u0 + wave;
+        const int q1 = min(hi, su.uq);
+        const int ntot = max(1, (q1 - (lo + wave) + kWaves - 1) / kWaves);   // this wave's units
+        int u = lo + wave;
         if (u < q1) {
             // Direct-to-LDS loads: unit u is staged in one buffer while the
             // previous one is processed from the other.  The waits are explicit
             // (vmcnt counts this wave's outstanding loads, in issue order).
             lds_u8* const sa = (lds_u8*)(stage_a + wave * S::PITCH);
             lds_u8* const sb = (lds_u8*)(stage_b + wave * S::PITCH);
-            uint32_t ha = issue_unit<G, KB, VB>(sa, L, c, b, h, u, ngroups, lane), hb = 0;
+            uint32_t ha = issue_unit<G, KB, VB, PG>(sa, L, c, b, h, u, su.ngroups, lane), hb = 0;
             for (;;) {
                 if (u + kWaves < q1) {
                     __builtin_amdgcn_s_waitcnt(kLgkmZero);   // last reads of sb returned
-                    hb = issue_unit<G, KB, VB>(sb, L, c, b, h, u + kWaves, ngroups, lane);
+                    hb = issue_unit<G, KB, VB, PG>(sb, L, c, b, h, u + kWaves, su.ngroups, lane);
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::LOADS));
                 } else {
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -558,7 +605,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
                 if (u >= q1) break;
                 if (u + kWaves < q1) {
                     __builtin_amdgcn_s_waitcnt(kLgkmZero);
-                    ha = issue_unit<G, KB, VB>(sa, L, c, b, h, u + kWaves, ngroups, lane);
+                    ha = issue_unit<G, KB, VB, PG>(sa, L, c, b, h, u + kWaves, su.ngroups, lane);
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::LOADS));
                 } else {
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -571,8 +618,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
             }
         }
     }
-    for (int u = u0 + wave; u < u1; u += kWaves)
-        if (u >= uq) process_residual<LP>(A, L, c, sh, nq + 32 * (u - uq), n, Q, sl2, lane);
+    for (int u = lo + wave; u < hi; u += kWaves)
+        if (u >= su.uq)
+            process_residual<LP>(A, L, c, sh, su.nq + 32 * (u - su.uq), su.n, Q, sl2, lane,
+                                 (lds_u8*)(stage_a + wave * S::PITCH), (lds_u8*)(stage_b + wave * S::PITCH));
+    __builtin_amdgcn_s_setprio(0);
 
     // Wave results -> LDS: totals over the lane groups, accumulators by head.
     // The accumulators reuse the stage buffers: every wave has consumed its
@@ -595,8 +645,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
     __syncthreads();
 
     // Workgroup partial (heads < gq) -> workspace.
-    float* part = ws + ((long)sh * parts + sp) * gq * kPart;
-    for (int idx = threadIdx.x; idx < gq * kD; idx += 256) {
+    for (int idx = tid; idx < gq * kD; idx += 256) {
         const int hh = idx >> 7, ch = idx & (kD - 1);
         float M = kNegInf;
 #pragma unroll
@@ -618,34 +667,167 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
             part[hh * kPart + kD + 1] = Ls;
         }
     }
+    __syncthreads();   // the stage buffers are staged into again by the next segment
 }
 
-// Split merge: grid (B*H, gq), 1024 threads.  Log-sum-exp over the parts of
-// one (stream, head): out = sum_p o_p e^(m_p-M) / sum_p l_p e^(m_p-M), 0 for
-// an empty sequence.  Every load (outputs of up to 32 parts per thread, and
-// the parts' max and sum) is issued before any is used: one memory round trip.
-constexpr int kMaxParts = 256;
+// Decode attention over the whole batch as one flattened sequence of work:
+// sequence b contributes H streams (b, h) of cost_b each (its units, residual
+// ones weighted kResCost), in (b, h) order, T in all, and workgroup w takes
+// positions [w T / nwg, (w+1) T / nwg), a unit going to the workgroup holding
+// its first position, whatever the sequence lengths (ragged batches and long
+// single streams are balanced alike).  It writes one partial per stream segment it covers, at
+// slot w + s for stream s (unique: along the workgroup order the covered
+// streams never decrease).  The first workgroup of each stream records the
+// stream's flattened start, and workgroup 0 records T; from these the merge
+// finds the stream's workgroups.
+// Waves per SIMD each instantiation is compiled for: four (at most 128
+// registers) where that fits without spilling, else three.  A kernel that
+// spills runs with scratch memory and far slower; the build rejects any
+// attention kernel that uses scratch, so this table is checked.  Four waves
+// fit the limb-packed kernels with INT2 values; without limb packing the
+// separate high/low query operands take 16 more registers, INT4 values more
+// than INT2 ones.  (Three waves lose little where the kernel waits on HBM.)
+constexpr int attn_waves(int G, int KB, int VB, bool LP, bool PG) {
+    return LP && VB == 2 && !(G == 16 && KB == 2) ? 4 : 3;
+}
+
+template <int G, int KB, int VB, bool LP, bool PG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves(G, KB, VB, LP, PG)))) void attn_kernel(
+    Layout L, kvq_cache c, const half_t* __restrict__ q, float sl2, float* __restrict__ ws, int gq, int nwg,
+    long meta_off) {
+    using S = Stage<G, KB, VB>;
+    // Two stage buffers per wave (ping-pong), in two arrays: the compiler
+    // treats them as separate objects.  After the unit loop the same memory
+    // holds the waves' accumulators (waves 0-1 in stage_a, 2-3 in stage_b).
+    __shared__ __attribute__((aligned(16))) uint8_t stage_a[kWaves * S::PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_b[kWaves * S::PITCH];
+    __shared__ float wm[kWaves][16], wl[kWaves][16], wpz[kWaves][16];
+    __shared__ int wsum[kWaves];
+    __shared__ int first[2];   // sequence holding unit w T / nwg, flattened start of that sequence
+    const int w = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
+
+    // Units per sequence, prefix over the batch (each thread a run of
+    // consecutive sequences, then a scan over the threads).  Flattened
+    // positions fit in 32 bits (the host rejects larger batches).
+    const int per = (L.B + 255) / 256;
+    const int b0 = min(tid * per, L.B), b1 = min(b0 + per, L.B);
+    int mine = 0;
+    for (int b = b0; b < b1; ++b) mine += L.H * seq_units(L, c, b).cost;
+    int incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int T = 0, below = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        const int v = wsum[i];
+        below += i < wave ? v : 0;
+        T += v;
+    }
+    T = __builtin_amdgcn_readfirstlane(T);
+    const int excl = below + incl - mine;
+    const int start = __builtin_amdgcn_readfirstlane((int)((long)w * T / nwg));
+    const int end = __builtin_amdgcn_readfirstlane((int)((long)(w + 1) * T / nwg));
+    if (start < end && excl <= start && start < excl + mine) {
+        int p = excl;
+        for (int b = b0; b < b1; ++b) {
+            const int f = L.H * seq_units(L, c, b).cost;
+            if (start < p + f) {
+                first[0] = b;
+                first[1] = p;
+                break;
+            }
+            p += f;
+        }
+    }
+    __syncthreads();
+    int* meta = (int*)((uint8_t*)ws + meta_off);
+    if (w == 0 && tid == 0) meta[0] = T;
+    if (start >= end) return;   // fewer units than workgroups
+
+    int b = __builtin_amdgcn_readfirstlane(first[0]);
+    const int pb = __builtin_amdgcn_readfirstlane(first[1]);
+    SeqUnits su = seq_units(L, c, b);
+    // (the division runs on the vector ALU: bring the result back to a scalar
+    // register, or everything derived from it becomes per-lane)
+    int h = __builtin_amdgcn_readfirstlane((start - pb) / su.cost);
+    int ps = pb + h * su.cost;   // flattened start of stream (b, h)
+    for (;;) {
+        const int lo = __builtin_amdgcn_readfirstlane(max(start - ps, 0));
+        const int hi = __builtin_amdgcn_readfirstlane(min(end - ps, su.cost));
+        const int s = b * L.H + h;
+        if (lo == 0 && wave == 0) {
+            // the merge finds the stream's workgroups from its flattened start
+            int l0;
+            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l0));
+            if (l0 == 0) meta[1 + s] = ps;
+        }
+        attend_segment<G, KB, VB, LP, PG>(stage_a, stage_b, wm, wl, wpz, L, c, q, sl2, gq, b, h, su,
+                                          unit_at(su, lo), unit_at(su, hi), ws + ((long)w + s) * gq * kPart,
+                                          lane, wave);
+        if (ps + hi >= end) break;
+        // next stream that has work (x < end <= T guarantees one)
+        ps += su.cost;
+        if (++h == L.H) {
+            h = 0;
+            do su = seq_units(L, c, ++b);
+            while (su.units == 0);
+        }
+    }
+}
+
+// Workgroup w of nwg covers units [w T / nwg, (w + 1) T / nwg): empty when
+// there are fewer units than workgroups; an empty one writes no partial.
+__device__ __forceinline__ bool covers_units(long w, long T, long nwg) {
+    return w * T / nwg != (w + 1) * T / nwg;
+}
+
+// Split merge: grid (B*H, gq), 1024 threads.  Log-sum-exp over the partials
+// of one (stream, head): out = sum_p o_p e^(m_p-M) / sum_p l_p e^(m_p-M); 0 for
+// an empty sequence (no partials).  The stream's partials are in the slots
+// w + s of the workgroups w0 <= w <= w1 that cover its units (those with an
+// empty share wrote none and are skipped); w1 - w0 < nwg <= kMaxParts.
+constexpr int kMaxParts = 1024;
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeSlices = kMergeThreads / kD;
-constexpr int kMergePer = kMaxParts / kMergeSlices;
-__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float* __restrict__ ws,
-                                                                  float* __restrict__ out, int parts, int gq) {
+constexpr int kMergeBatch = 16;   // partial outputs in flight per thread
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(Layout L, kvq_cache c, const float* __restrict__ ws,
+                                                                  float* __restrict__ out, int gq, int nwg,
+                                                                  long meta_off) {
     __shared__ float fac[kMaxParts];
     __shared__ float red[kMergeThreads / 64][2];
     __shared__ float acc[kMergeSlices][kD];
-    const int sh = blockIdx.x, hh = blockIdx.y, tid = threadIdx.x;
+    const int s = blockIdx.x, hh = blockIdx.y, tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     const int slice = tid >> 7, ch = tid & (kD - 1);
-    const long stride = (long)gq * kPart;
-    const float* p = ws + ((long)sh * parts * gq + hh) * kPart;
-    float o[kMergePer];
-#pragma unroll
-    for (int j = 0; j < kMergePer; ++j) {
-        const int i = slice + j * kMergeSlices;
-        o[j] = i < parts ? p[i * stride + ch] : 0.0f;
+    float* orow = out + ((long)s * gq + hh) * kD;   // query head (s % H) * gq + hh of sequence s / H
+    if (seq_units(L, c, s / L.H).units == 0) {
+        if (tid < kD) orow[tid] = 0.0f;
+        return;
     }
+    // Workgroups covering the stream's units [P, P + units) of the T in all:
+    // w covers [w T / nwg, (w + 1) T / nwg), so unit x lies in
+    // ceil((x + 1) nwg / T) - 1 (clamped: a slot outside the workspace is
+    // never read).
+    const int* meta = (const int*)((const uint8_t*)ws + meta_off);
+    const long T = max(meta[0], 1);
+    const long P = meta[1 + s];
+    const long units = seq_units(L, c, s / L.H).cost;   // (cost positions)
+    const int w0 = (int)min(max(((P + 1) * nwg - 1) / T, 0L), (long)nwg - 1);
+    const int w1 = (int)min(max(((P + units) * nwg - 1) / T, (long)w0), (long)nwg - 1);
+    const int parts = w1 - w0 + 1;
+    const long stride = (long)gq * kPart;
+    const float* p = ws + ((long)(w0 + s) * gq + hh) * kPart;
+
     float m = kNegInf, l = 0.0f;
-    if (tid < parts) {
+    if (tid < parts && covers_units(w0 + tid, T, nwg)) {
         m = p[tid * stride + kD];
         l = p[tid * stride + kD + 1];
     }
@@ -664,24 +846,94 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float* 
     Ls = 0.0f;
     for (int w = 0; w < kMergeThreads / 64; ++w) Ls += red[w][1];
     float sum = 0.0f;
+    for (int i0 = slice; i0 < parts; i0 += kMergeSlices * kMergeBatch) {
+        float o[kMergeBatch];
 #pragma unroll
-    for (int j = 0; j < kMergePer; ++j) {
-        const int i = slice + j * kMergeSlices;
-        if (i < parts) sum = fmaf(o[j], fac[i], sum);
+        for (int j = 0; j < kMergeBatch; ++j) {
+            const int i = i0 + j * kMergeSlices;
+            o[j] = i < parts && fac[i] != 0.0f ? p[i * stride + ch] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {
+            const int i = i0 + j * kMergeSlices;
+            if (i < parts) sum = fmaf(o[j], fac[i], sum);
+        }
     }
     acc[slice][ch] = sum;
     __syncthreads();
     if (slice == 0) {
-        float s = acc[0][ch];
-        for (int k = 1; k < kMergeSlices; ++k) s += acc[k][ch];
-        out[((long)sh * gq + hh) * kD + ch] = Ls > 0.0f ? s / Ls : 0.0f;
+        float t = acc[0][ch];
+        for (int k = 1; k < kMergeSlices; ++k) t += acc[k][ch];
+        orow[ch] = Ls > 0.0f ? t / Ls : 0.0f;
     }
+}
+
+// Split merge for batches of many streams with few partials each: one wave
+// per (stream, head) row, four rows per workgroup; lane l produces channels
+// 2l and 2l+1.  Same arithmetic as attn_merge_kernel.
+constexpr int kRowsPerMerge = 4;
+__global__ __launch_bounds__(256) void attn_merge_rows_kernel(Layout L, kvq_cache c, const float* __restrict__ ws,
+                                                              float* __restrict__ out, int gq, int nwg,
+                                                              long meta_off) {
+    __shared__ float fac[kRowsPerMerge][kMaxParts];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long row = (long)blockIdx.x * kRowsPerMerge + wave;
+    if (row >= (long)L.B * L.H * gq) return;   // (no workgroup barrier below)
+    const int s = (int)(row / gq), hh = (int)(row % gq);
+    float2* orow = (float2*)(out + row * kD);
+    const long units = seq_units(L, c, s / L.H).cost;   // (cost positions)
+    if (units == 0) {
+        orow[lane] = make_float2(0.0f, 0.0f);
+        return;
+    }
+    const int* meta = (const int*)((const uint8_t*)ws + meta_off);
+    const long T = max(meta[0], 1);
+    const long P = meta[1 + s];
+    const int w0 = (int)min(max(((P + 1) * nwg - 1) / T, 0L), (long)nwg - 1);
+    const int w1 = (int)min(max(((P + units) * nwg - 1) / T, (long)w0), (long)nwg - 1);
+    const int parts = w1 - w0 + 1;
+    const long stride = (long)gq * kPart;
+    const float* p = ws + ((long)(w0 + s) * gq + hh) * kPart;
+
+    float M = kNegInf;
+    for (int i = lane; i < parts; i += 64)
+        if (covers_units(w0 + i, T, nwg)) M = fmaxf(M, p[i * stride + kD]);
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float Ls = 0.0f;
+    for (int i = lane; i < parts; i += 64) {
+        float f = 0.0f;
+        if (covers_units(w0 + i, T, nwg)) {
+            const float m = p[i * stride + kD];
+            f = m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+            Ls += p[i * stride + kD + 1] * f;
+        }
+        fac[wave][i] = f;
+    }
+    for (int off = 32; off >= 1; off >>= 1) Ls += __shfl_xor(Ls, off);
+    wave_sync();   // fac written by other lanes of this wave
+    float2 acc = make_float2(0.0f, 0.0f);
+    for (int i0 = 0; i0 < parts; i0 += 8) {
+        float2 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            v[j] = i0 + j < parts && fac[wave][i0 + j] != 0.0f ? *(const float2*)(p + (i0 + j) * stride + 2 * lane)
+                                                              : make_float2(0.0f, 0.0f);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (i0 + j < parts) {
+                const float f = fac[wave][i0 + j];
+                acc.x = fmaf(v[j].x, f, acc.x);
+                acc.y = fmaf(v[j].y, f, acc.y);
+            }
+        }
+    }
+    orow[lane] = Ls > 0.0f ? make_float2(acc.x / Ls, acc.y / Ls) : make_float2(0.0f, 0.0f);
 }
 
 // Resident attention workgroups on the current device: CUs x workgroups per
 // CU for this instantiation (from its register and LDS footprint).  Falls
 // back to 256 CUs x 3 when no device is visible (host-only size queries).
-template <int G, int KB, int VB, bool LP>
+template <int G, int KB, int VB, bool LP, bool PG>
 static int attn_slots_for() {
     static int cached[64];
     int dev = 0;
@@ -690,7 +942,7 @@ static int attn_slots_for() {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)attn_kernel<G, KB, VB, LP>, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)attn_kernel<G, KB, VB, LP, PG>, 256, 0) !=
             hipSuccess || per_cu <= 0)
         per_cu = 3;
     (void)hipGetLastError();
@@ -702,51 +954,47 @@ static int attn_slots_for() {
 // fp16 parts of q*s and p*s share one 16-column product.
 static inline bool limb_packed(int gq) { return gq <= 8; }
 
-template <bool LP>
+template <bool LP, bool PG>
 static int attn_slots_lp(const Layout& L) {
     switch (L.G * 100 + L.kbits * 10 + L.vbits) {
-        case 1622: return attn_slots_for<16, 2, 2, LP>();
-        case 1624: return attn_slots_for<16, 2, 4, LP>();
-        case 1642: return attn_slots_for<16, 4, 2, LP>();
-        case 1644: return attn_slots_for<16, 4, 4, LP>();
-        case 3222: return attn_slots_for<32, 2, 2, LP>();
-        case 3224: return attn_slots_for<32, 2, 4, LP>();
-        case 3242: return attn_slots_for<32, 4, 2, LP>();
-        default: return attn_slots_for<32, 4, 4, LP>();
+        case 1622: return attn_slots_for<16, 2, 2, LP, PG>();
+        case 1624: return attn_slots_for<16, 2, 4, LP, PG>();
+        case 1642: return attn_slots_for<16, 4, 2, LP, PG>();
+        case 1644: return attn_slots_for<16, 4, 4, LP, PG>();
+        case 3222: return attn_slots_for<32, 2, 2, LP, PG>();
+        case 3224: return attn_slots_for<32, 2, 4, LP, PG>();
+        case 3242: return attn_slots_for<32, 4, 2, LP, PG>();
+        default: return attn_slots_for<32, 4, 4, LP, PG>();
     }
 }
 static int attn_slots(const Layout& L, int gq) {
-    return limb_packed(gq) ? attn_slots_lp<true>(L) : attn_slots_lp<false>(L);
+    if (L.paged) return limb_packed(gq) ? attn_slots_lp<true, true>(L) : attn_slots_lp<false, true>(L);
+    return limb_packed(gq) ? attn_slots_lp<true, false>(L) : attn_slots_lp<false, false>(L);
 }
 
 AttnPlan plan_attention(const Layout& L, int num_q_heads) {
     AttnPlan P;
     const int gq = num_q_heads / L.H;
-    const int streams = L.B * L.H;
+    const long streams = (long)L.B * L.H;
     const int maxg = L.paged ? L.max_blocks : L.groups;
-    // 32-token units at capacity: quantized groups, then the residual ring
-    const int maxu = (maxg * L.G + 31) / 32 + (L.R + L.G - 1 + 31) / 32;
-    // One round of resident workgroups when the work allows it: all splits
-    // are the same length, so a round with a partly filled tail is avoided.
-    // At least one unit per wave, at most 128 units (32 per wave) per split.
-    const int slots = attn_slots(L, gq);
-    int splits = slots / streams;
-    if (splits < 1) splits = 1;
-    const int minsplit = (maxu + 3) / 4;
-    if (splits > minsplit) splits = minsplit;
-    int ups = (maxu + splits - 1) / splits;
-    if (ups > 128) splits = (maxu + 127) / 128;
-    if (const char* e = getenv("KVQ_UNITS_PER_SPLIT")) {
+    // 32-token units per stream at capacity: quantized groups, then the residual
+    const long maxu = ((long)maxg * L.G + 31) / 32 + (L.R + L.G - 1 + 31) / 32;
+    // One round of resident workgroups (the flattened split balances any
+    // mix of lengths), no more than 1 per 8 units of the batch at capacity,
+    // and never more partials per stream than the merge holds.
+    long nwg = attn_slots(L, gq);
+    nwg = std::min(nwg, std::max(1L, (streams * maxu + 7) / 8));
+    if (const char* e = getenv("KVQ_WORKGROUPS")) {
         const int v = atoi(e);
-        if (v >= 1) splits = (maxu + v - 1) / v;
+        if (v >= 1) nwg = v;
     }
-    if (splits > kMaxParts) splits = kMaxParts;
-    if (splits < 1) splits = 1;
-    P.splits = splits;
-    P.units_per_split = (maxu + splits - 1) / splits;
-    P.parts = splits;
+    nwg = std::min(nwg, (long)kMaxParts);
+    P.nwg = (int)nwg;
+    P.fits = streams * maxu < (1L << 31);   // flattened unit positions are 32-bit
+    P.slots = nwg + streams - 1;
     P.part_floats = (size_t)gq * kPart;
-    P.workspace = (size_t)streams * P.parts * P.part_floats * sizeof(float);
+    P.meta_off = (P.slots * P.part_floats * sizeof(float) + 255) / 256 * 256;
+    P.workspace = P.meta_off + (size_t)(1 + streams) * sizeof(int32_t);
     return P;
 }
 
@@ -754,15 +1002,20 @@ hipError_t launch_attention_partials(const Layout& L, const AttnPlan& P, const k
                                      int num_q_heads, float scale, void* ws, hipStream_t s) {
     const int gq = num_q_heads / L.H;
     const float sl2 = scale * kLog2e;
-    dim3 grid(P.parts, L.B * L.H);
-#define KVQ_ATT2(GG, KB, VB, LP)                                                                           \
-    hipLaunchKernelGGL((attn_kernel<GG, KB, VB, LP>), grid, dim3(256), 0, s, L, c, q, sl2, (float*)ws, gq, \
-                       P.splits, P.units_per_split)
-#define KVQ_ATT(GG, KB, VB)              \
-    if (limb_packed(gq))                  \
-        KVQ_ATT2(GG, KB, VB, true);       \
+#define KVQ_ATT3(GG, KB, VB, LP, PG)                                                                       \
+    hipLaunchKernelGGL((attn_kernel<GG, KB, VB, LP, PG>), dim3(P.nwg), dim3(256), 0, s, L, c, q, sl2,        \
+                       (float*)ws, gq, P.nwg, (long)P.meta_off)
+#define KVQ_ATT2(GG, KB, VB, LP)         \
+    if (L.paged)                          \
+        KVQ_ATT3(GG, KB, VB, LP, true);   \
     else                                  \
-        KVQ_ATT2(GG, KB, VB, false)
+        KVQ_ATT3(GG, KB, VB, LP, false)
+#define KVQ_ATT(GG, KB, VB)              \
+    if (limb_packed(gq)) {                \
+        KVQ_ATT2(GG, KB, VB, true);       \
+    } else {                              \
+        KVQ_ATT2(GG, KB, VB, false);      \
+    }
     const int key = L.G * 100 + L.kbits * 10 + L.vbits;
     switch (key) {
         case 1622: KVQ_ATT(16, 2, 2); break;
@@ -777,14 +1030,25 @@ hipError_t launch_attention_partials(const Layout& L, const AttnPlan& P, const k
     }
 #undef KVQ_ATT
 #undef KVQ_ATT2
+#undef KVQ_ATT3
     return hipGetLastError();
 }
 
-hipError_t launch_attention_merge(const Layout& L, const AttnPlan& P, int num_q_heads, const void* ws, float* out,
-                                  hipStream_t s) {
+hipError_t launch_attention_merge(const Layout& L, const AttnPlan& P, const kvq_cache& c, int num_q_heads,
+                                  const void* ws, float* out, hipStream_t s) {
     const int gq = num_q_heads / L.H;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(L.B * L.H, gq), dim3(kMergeThreads), 0, s, (const float*)ws, out,
-                       P.parts, gq);
+    const long streams = (long)L.B * L.H;
+    // partials per stream when the lengths are equal: a few -> one wave per
+    // row; many -> a workgroup per row to keep all their loads in flight
+    const long expect = (P.nwg + streams - 1) / streams + 2;
+    if (expect <= 16) {
+        const long rows = streams * gq;
+        hipLaunchKernelGGL(attn_merge_rows_kernel, dim3((unsigned)((rows + kRowsPerMerge - 1) / kRowsPerMerge)),
+                           dim3(64 * kRowsPerMerge), 0, s, L, c, (const float*)ws, out, gq, P.nwg, (long)P.meta_off);
+    } else {
+        hipLaunchKernelGGL(attn_merge_kernel, dim3(L.B * L.H, gq), dim3(kMergeThreads), 0, s, L, c,
+                           (const float*)ws, out, gq, P.nwg, (long)P.meta_off);
+    }
     return hipGetLastError();
 }
 

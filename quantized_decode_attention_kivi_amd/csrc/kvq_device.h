@@ -17,11 +17,12 @@ __device__ __forceinline__ uint16_t f2h_bits(float x) {  // round to nearest eve
 
 // Record of key group g of stream (b, h); nullptr if it lies outside the
 // cache (contiguous: g >= groups; paged: g >= max_blocks or a block id
-// outside [0, num_blocks)).
-__device__ __forceinline__ uint8_t* record_at(const Layout& L, void* packed, const int32_t* bt,
-                                              int b, int h, int g) {
+// outside [0, num_blocks)).  PG: the cache is paged (L.paged).
+template <bool PG>
+__device__ __forceinline__ uint8_t* record_at_t(const Layout& L, void* packed, const int32_t* bt, int b, int h,
+                                                int g) {
     long idx;
-    if (L.paged) {
+    if (PG) {
         if (g < 0 || g >= L.max_blocks) return nullptr;
         // read through the constant address space: a scalar load when the
         // index is wave uniform (the table does not change during a kernel)
@@ -33,6 +34,10 @@ __device__ __forceinline__ uint8_t* record_at(const Layout& L, void* packed, con
         idx = ((long)b * L.H + h) * L.groups + g;
     }
     return (uint8_t*)packed + idx * (long)L.record;
+}
+__device__ __forceinline__ uint8_t* record_at(const Layout& L, void* packed, const int32_t* bt, int b, int h,
+                                              int g) {
+    return L.paged ? record_at_t<true>(L, packed, bt, b, h, g) : record_at_t<false>(L, packed, bt, b, h, g);
 }
 
 // Grid parameters of one quantized set ("KV Cache compression lab",

@@ -87,16 +87,17 @@ hipError_t launch_export(const Layout& L, const kvq_cache& c, uint8_t* kc, uint8
                          uint16_t* kz, uint16_t* vs, uint16_t* vz, int out_tokens, hipStream_t s);
 
 struct AttnPlan {
-    int splits;          // splits per stream (quantized units, then residual units)
-    int units_per_split; // 32-token units per split
-    int parts;           // partial results per stream (= splits)
+    int nwg;             // attention workgroups (each an equal share of the batch's units)
+    long slots;          // partial-result slots: nwg + streams - 1
     size_t part_floats;  // floats of one partial result (Hq/H heads x (128 + 4))
+    size_t meta_off;     // bytes: T (units of the batch), then each stream's first unit, after the slots
     size_t workspace;    // bytes
+    bool fits;           // the batch's units at capacity fit the kernel's 32-bit positions
 };
 AttnPlan plan_attention(const Layout& L, int num_q_heads);
 hipError_t launch_attention_partials(const Layout& L, const AttnPlan& P, const kvq_cache& c, const _Float16* q,
                                      int num_q_heads, float scale, void* ws, hipStream_t s);
-hipError_t launch_attention_merge(const Layout& L, const AttnPlan& P, int num_q_heads, const void* ws, float* out,
-                                  hipStream_t s);
+hipError_t launch_attention_merge(const Layout& L, const AttnPlan& P, const kvq_cache& c, int num_q_heads,
+                                  const void* ws, float* out, hipStream_t s);
 
 }  // namespace kvq

@@ -84,7 +84,8 @@ def lib():
         L.kv_decode_attention_partials.argtypes = [P(kvq_config), P(kvq_cache), vp, ctypes.c_int32, ctypes.c_float,
                                                    vp, ctypes.c_size_t, vp]
         L.kv_decode_attention_partials.restype = ctypes.c_int
-        L.kv_decode_attention_merge.argtypes = [P(kvq_config), ctypes.c_int32, vp, ctypes.c_size_t, vp, vp]
+        L.kv_decode_attention_merge.argtypes = [P(kvq_config), P(kvq_cache), ctypes.c_int32, vp, ctypes.c_size_t,
+                                                vp, vp]
         L.kv_decode_attention_merge.restype = ctypes.c_int
         L.kv_export_codes.argtypes = [P(kvq_config), P(kvq_cache)] + [vp] * 6 + [ctypes.c_int32, vp]
         L.kv_export_codes.restype = ctypes.c_int
@@ -154,8 +155,8 @@ def kv_decode_attention_partials(cfg, cache, q, num_q_heads, softmax_scale, work
            "kv_decode_attention_partials")
 
 
-def kv_decode_attention_merge(cfg, num_q_heads, workspace, out, stream=None):
-    _check(lib().kv_decode_attention_merge(ctypes.byref(cfg), int(num_q_heads), _ptr(workspace),
+def kv_decode_attention_merge(cfg, cache, num_q_heads, workspace, out, stream=None):
+    _check(lib().kv_decode_attention_merge(ctypes.byref(cfg), ctypes.byref(cache), int(num_q_heads), _ptr(workspace),
                                            workspace.numel() * workspace.element_size(), _ptr(out),
                                            _stream(stream)), "kv_decode_attention_merge")
 
@@ -384,6 +385,6 @@ class QuantizedKVCache:
         split_events[0].record(st)
         kv_decode_attention_partials(self.cfg, self.cache, q, Hq, softmax_scale, ws, stream)
         split_events[1].record(st)
-        kv_decode_attention_merge(self.cfg, Hq, ws, out, stream)
+        kv_decode_attention_merge(self.cfg, self.cache, Hq, ws, out, stream)
         split_events[2].record(st)
         return out

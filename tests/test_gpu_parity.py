@@ -6,6 +6,7 @@ Sizes: small cases span several key groups, several splits and a ragged tail;
 the full-size cases are the five measured workloads themselves.
 """
 import dataclasses
+import os
 
 import numpy as np
 import pytest
@@ -215,6 +216,29 @@ def test_full_size_80_layer_cache():
     compare_attention(np.concatenate(got), np.concatenate(ref))
     del cache
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("nwg", [1, 2, 5, 13, 64, 300, 1024])
+def test_any_workgroup_count(nwg):
+    """The flattened split gives the oracle's result for any number of
+    attention workgroups: workgroups spanning several streams, streams spread
+    over many workgroups, more workgroups than units, and empty sequences at
+    the start, in the middle and at the end of the batch (both merge kernels
+    are used across these counts)."""
+    base = _w("llama3_8b_layer_b8_32k_int4", name="flat", num_kv_heads=2, num_q_heads=8, k_bits=4, v_bits=2,
+              group_size=32, residual=64, tag=32)
+    lens = [0, 700, 33, 0, 2100, 64, 0]
+    w = dataclasses.replace(base, num_seqs=len(lens), context=max(lens))
+    cache, states, _, _ = _run_prefill(w, lens)
+    q = synth.make_query(w, device="cuda")
+    os.environ["KVQ_WORKGROUPS"] = str(nwg)
+    try:
+        out = cache.decode_attention(q, SCALE).cpu().numpy()
+    finally:
+        del os.environ["KVQ_WORKGROUPS"]
+    for b in (0, 3, 6):
+        assert np.all(out[b] == 0)
+    compare_attention(out, oracle_attention(to_bits(q), states, SCALE))
 
 
 def test_split_entry_points_equal_combined_call():
