@@ -78,6 +78,24 @@ def lib():
                 [_u8p, _u16p, _u16p, _u8p, _u16p, _u16p, _f32p, _f32p]
             L.orc_attention.argtypes = [_f32p, ctypes.c_int, _f32p, _f32p, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_float, _f64p, _f64p]
+            L.orc_fp8_e4m3_decode.restype = ctypes.c_float
+            L.orc_fp8_e4m3_decode.argtypes = [ctypes.c_uint8]
+            L.orc_fp8_e4m3_encode.restype = ctypes.c_uint8
+            L.orc_fp8_e4m3_encode.argtypes = [ctypes.c_float]
+            L.orc_fp8_decode_array.argtypes = [_u8p, _f32p, ctypes.c_long]
+            L.orc_fp8_encode_array.argtypes = [_f32p, _u8p, ctypes.c_long]
+            L.orc_quantize_token_fp8.argtypes = [_u16p, ctypes.c_int, ctypes.c_float, _u8p]
+            L.orc_prefill_stream8.restype = ctypes.c_int
+            L.orc_prefill_stream8.argtypes = [ctypes.c_int, _u16p, _u16p] + [ctypes.c_int] * 4 + \
+                [ctypes.c_float] * 2 + [_u8p, _u16p, _u16p, _u8p, _u16p, _u16p]
+            L.orc_append_stream8.restype = ctypes.c_int
+            L.orc_append_stream8.argtypes = [ctypes.c_int, _u16p, _u16p, ctypes.c_int, _i32p, _i32p,
+                                             _u16p, _u16p] + [ctypes.c_int] * 3 + \
+                [ctypes.c_float] * 2 + [_u8p, _u16p, _u16p, _u8p, _u16p, _u16p]
+            L.orc_dequantize_stream8.argtypes = [ctypes.c_int, _u16p, _u16p] + [ctypes.c_int] * 3 + \
+                [ctypes.c_float] * 2 + [_u8p, _u16p, _u16p, _u8p, _u16p, _u16p, _f32p, _f32p]
+            L.orc_stream_bytes8.restype = ctypes.c_double
+            L.orc_stream_bytes8.argtypes = [ctypes.c_int, ctypes.c_long] + [ctypes.c_int] * 3
             L.orc_stream_bytes.restype = ctypes.c_double
             L.orc_stream_bytes.argtypes = [ctypes.c_long] + [ctypes.c_int] * 5
             L.orc_kv_bytes_closed_form.restype = ctypes.c_double
@@ -108,9 +126,26 @@ def f2h(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def fp8_decode(codes: np.ndarray) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float32)
+    lib().orc_fp8_decode_array(_p(c, _u8p), _p(out, _f32p), c.size)
+    return out
+
+
+def fp8_encode(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    lib().orc_fp8_encode_array(_p(x, _f32p), _p(out, _u8p), x.size)
+    return out
+
+
 # --------------------------------------------------------------------------
 # quantizer
 # --------------------------------------------------------------------------
+
+# cache formats: the low-bit KIVI format, and the two 8-bit formats
+FMT_KIVI, FMT_INT8, FMT_FP8 = 0, 1, 2
 
 def num_quantized(n: int, G: int, R: int) -> int:
     return int(lib().orc_num_quantized(int(n), int(G), int(R)))
@@ -127,6 +162,14 @@ def quantize_key_group(x_bits: np.ndarray, bits: int):
     return codes, s, z
 
 
+def quantize_token_fp8(x_bits: np.ndarray, scale: float):
+    """x_bits: uint16 [d] -> E4M3 codes [d] under a static scale."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    codes = np.empty(x.shape[0], np.uint8)
+    lib().orc_quantize_token_fp8(_p(x, _u16p), x.shape[0], ctypes.c_float(scale), _p(codes, _u8p))
+    return codes
+
+
 def quantize_value_token(x_bits: np.ndarray, bits: int):
     """x_bits: uint16 [d] -> (codes [d], s, z)."""
     x = np.ascontiguousarray(x_bits, dtype=np.uint16)
@@ -141,34 +184,51 @@ def quantize_value_token(x_bits: np.ndarray, bits: int):
 class StreamState:
     """Quantized state of one (sequence, kv-head) stream, as the oracle
     defines it: codes and fp16 metadata for tokens [0, nq), fp16 history for
-    every token (only [nq, n) is the residual)."""
+    every token (only [nq, n) is the residual).
 
-    def __init__(self, d, kbits, vbits, G, R, cap):
+    fmt FMT_KIVI: kbits/vbits in {2, 4}, key scale/zero per (group, channel),
+    value scale/zero per token.  FMT_INT8: 8-bit codes, key and value
+    scale/zero per token.  FMT_FP8: E4M3 codes under the static scales
+    kscale / vscale of the stream's kv head, no per-token metadata."""
+
+    def __init__(self, d, kbits, vbits, G, R, cap, fmt=FMT_KIVI, kscale=0.0, vscale=0.0):
         self.d, self.kbits, self.vbits, self.G, self.R, self.cap = d, kbits, vbits, G, R, cap
+        self.fmt, self.kscale, self.vscale = fmt, float(kscale), float(vscale)
         self.n = 0
         self.nq = 0
         self.hist_k = np.zeros((cap, d), np.uint16)
         self.hist_v = np.zeros((cap, d), np.uint16)
         self.kcodes = np.zeros((cap, d), np.uint8)
         self.vcodes = np.zeros((cap, d), np.uint8)
-        ng = cap // G + 1
-        self.ks = np.zeros((ng, d), np.uint16)
-        self.kz = np.zeros((ng, d), np.uint16)
+        if fmt == FMT_KIVI:
+            ng = cap // G + 1
+            self.ks = np.zeros((ng, d), np.uint16)
+            self.kz = np.zeros((ng, d), np.uint16)
+        else:
+            self.ks = np.zeros(cap, np.uint16)
+            self.kz = np.zeros(cap, np.uint16)
         self.vs = np.zeros(cap, np.uint16)
         self.vz = np.zeros(cap, np.uint16)
 
+    def _arrays(self):
+        return (_p(self.kcodes, _u8p), _p(self.ks, _u16p), _p(self.kz, _u16p),
+                _p(self.vcodes, _u8p), _p(self.vs, _u16p), _p(self.vz, _u16p))
+
     @classmethod
-    def prefill(cls, k_bits, v_bits, kbits, vbits, G, R, cap=None):
+    def prefill(cls, k_bits, v_bits, kbits, vbits, G, R, cap=None, fmt=FMT_KIVI, kscale=0.0, vscale=0.0):
         k = np.ascontiguousarray(k_bits, np.uint16)
         v = np.ascontiguousarray(v_bits, np.uint16)
         n, d = k.shape
-        st = cls(d, kbits, vbits, G, R, cap if cap is not None else max(n, 1))
+        st = cls(d, kbits, vbits, G, R, cap if cap is not None else max(n, 1), fmt, kscale, vscale)
         st.hist_k[:n] = k
         st.hist_v[:n] = v
-        st.nq = int(lib().orc_prefill_stream(
-            _p(k, _u16p), _p(v, _u16p), n, d, kbits, vbits, G, R,
-            _p(st.kcodes, _u8p), _p(st.ks, _u16p), _p(st.kz, _u16p),
-            _p(st.vcodes, _u8p), _p(st.vs, _u16p), _p(st.vz, _u16p)))
+        if fmt == FMT_KIVI:
+            st.nq = int(lib().orc_prefill_stream(
+                _p(k, _u16p), _p(v, _u16p), n, d, kbits, vbits, G, R, *st._arrays()))
+        else:
+            st.nq = int(lib().orc_prefill_stream8(
+                fmt, _p(k, _u16p), _p(v, _u16p), n, d, G, R,
+                ctypes.c_float(st.kscale), ctypes.c_float(st.vscale), *st._arrays()))
         st.n = n
         return st
 
@@ -177,12 +237,17 @@ class StreamState:
         vn = np.ascontiguousarray(v_new_bits, np.uint16)
         n = ctypes.c_int(self.n)
         nq = ctypes.c_int(self.nq)
-        r = lib().orc_append_stream(
-            _p(self.hist_k, _u16p), _p(self.hist_v, _u16p), self.cap,
-            ctypes.byref(n), ctypes.byref(nq), _p(kn, _u16p), _p(vn, _u16p),
-            self.d, self.kbits, self.vbits, self.G, self.R,
-            _p(self.kcodes, _u8p), _p(self.ks, _u16p), _p(self.kz, _u16p),
-            _p(self.vcodes, _u8p), _p(self.vs, _u16p), _p(self.vz, _u16p))
+        if self.fmt == FMT_KIVI:
+            r = lib().orc_append_stream(
+                _p(self.hist_k, _u16p), _p(self.hist_v, _u16p), self.cap,
+                ctypes.byref(n), ctypes.byref(nq), _p(kn, _u16p), _p(vn, _u16p),
+                self.d, self.kbits, self.vbits, self.G, self.R, *self._arrays())
+        else:
+            r = lib().orc_append_stream8(
+                self.fmt, _p(self.hist_k, _u16p), _p(self.hist_v, _u16p), self.cap,
+                ctypes.byref(n), ctypes.byref(nq), _p(kn, _u16p), _p(vn, _u16p),
+                self.d, self.G, self.R, ctypes.c_float(self.kscale), ctypes.c_float(self.vscale),
+                *self._arrays())
         if r < 0:
             raise ValueError("oracle stream capacity exceeded")
         self.n, self.nq = n.value, nq.value
@@ -193,11 +258,15 @@ class StreamState:
         n, d = self.n, self.d
         ok = np.empty((max(n, 1), d), np.float32)
         ov = np.empty((max(n, 1), d), np.float32)
-        lib().orc_dequantize_stream(
-            _p(self.hist_k, _u16p), _p(self.hist_v, _u16p), n, self.nq, d, self.G,
-            _p(self.kcodes, _u8p), _p(self.ks, _u16p), _p(self.kz, _u16p),
-            _p(self.vcodes, _u8p), _p(self.vs, _u16p), _p(self.vz, _u16p),
-            _p(ok, _f32p), _p(ov, _f32p))
+        if self.fmt == FMT_KIVI:
+            lib().orc_dequantize_stream(
+                _p(self.hist_k, _u16p), _p(self.hist_v, _u16p), n, self.nq, d, self.G,
+                *self._arrays(), _p(ok, _f32p), _p(ov, _f32p))
+        else:
+            lib().orc_dequantize_stream8(
+                self.fmt, _p(self.hist_k, _u16p), _p(self.hist_v, _u16p), n, self.nq, d,
+                ctypes.c_float(self.kscale), ctypes.c_float(self.vscale),
+                *self._arrays(), _p(ok, _f32p), _p(ov, _f32p))
         return ok[:n], ov[:n]
 
     # logical views used by the parity tests
@@ -208,8 +277,11 @@ class StreamState:
         return self.vcodes[: self.nq]
 
     def key_meta(self):
-        g = self.nq // self.G
-        return self.ks[:g], self.kz[:g]
+        """KIVI: per (group, channel) [nq/G][d]; INT8 / FP8: per token [nq]."""
+        if self.fmt == FMT_KIVI:
+            g = self.nq // self.G
+            return self.ks[:g], self.kz[:g]
+        return self.ks[: self.nq], self.kz[: self.nq]
 
     def value_meta(self):
         return self.vs[: self.nq], self.vz[: self.nq]
@@ -240,7 +312,9 @@ def attention(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, scale: float,
     return out
 
 
-def stream_bytes(n, d, kbits, vbits, G, R) -> float:
+def stream_bytes(n, d, kbits, vbits, G, R, fmt=FMT_KIVI) -> float:
+    if fmt != FMT_KIVI:
+        return float(lib().orc_stream_bytes8(fmt, int(n), d, G, R))
     return float(lib().orc_stream_bytes(int(n), d, kbits, vbits, G, R))
 
 
@@ -252,16 +326,21 @@ def kv_bytes_closed_form(L, Hkv, n, d, bytes_per_elem) -> float:
 # batch helpers: loop over (sequence, kv-head) streams
 # --------------------------------------------------------------------------
 
-def prefill_batch(k_bits, v_bits, seq_lens, kbits, vbits, G, R, cap=None, threads=1):
-    """k_bits, v_bits: uint16 [B][H][L][d]; seq_lens: [B].
+def prefill_batch(k_bits, v_bits, seq_lens, kbits, vbits, G, R, cap=None, threads=1,
+                  fmt=FMT_KIVI, kscales=None, vscales=None):
+    """k_bits, v_bits: uint16 [B][H][L][d]; seq_lens: [B]; kscales, vscales:
+    FP8 static scales per kv head [H].
     -> list (per sequence) of lists (per kv-head) of StreamState."""
     B, H = k_bits.shape[:2]
 
     def one(bh):
         b, h = bh
         n = int(seq_lens[b])
+        ks = float(kscales[h]) if kscales is not None else 0.0
+        vs = float(vscales[h]) if vscales is not None else 0.0
         return StreamState.prefill(k_bits[b, h, :n], v_bits[b, h, :n], kbits, vbits, G, R,
-                                   cap=cap if cap is not None else max(n, 1))
+                                   cap=cap if cap is not None else max(n, 1), fmt=fmt,
+                                   kscale=ks, vscale=vs)
 
     jobs = [(b, h) for b in range(B) for h in range(H)]
     if threads > 1:

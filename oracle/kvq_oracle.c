@@ -19,6 +19,10 @@
  *  [P3] "KV Cache compression lab", experiment 01 (grid of 2^bits lines between
  *       min and max, spacing (max-min)/(2^bits-1), each value snaps to the
  *       nearest line, zero = starting point of the grid).
+ *  [P1] section 3.1: 8-bit KV (FP8 E4M3 with a static per-tensor or per-head
+ *       scale, or INT8 with a dynamic per-token scale) as the first 2x.
+ *  [P2] "KV compression and quantization", part B.1 (FP8 E4M3/E5M2 and INT8
+ *       at 0.5x the fp16 bytes).
  *  [P4] "KV cache compression" (jaedaily), formula paragraph: per-channel key
  *       dequant k = round((k - z_c)/s_c) s_c + z_c, per-token value dequant,
  *       M_KV = 2 L H_kv n d_h b, attention softmax(q k^T / sqrt(d_h)).
@@ -31,6 +35,12 @@
  * -0 extreme becomes +0; the residual keeps at least R tokens, and a group
  * is quantized only once it lies wholly outside them, so
  * n_q = G * floor(max(0, n - R) / G).
+ * 8-bit formats: INT8 is the same min/max quantizer with 8 bits applied to
+ * every key and value token over its d channels (asymmetric, like the rest
+ * of the method); FP8 takes the nearest E4M3 value (ties to even) of
+ * x * (1/scale) clamped to +-448, with one static fp32 scale per kv head for
+ * keys and one for values supplied by the caller; both keep the residual
+ * window and the group flush of the low-bit format.
  *
  * Parity pins (tests that tie this file to something other than itself) live
  * in tests/test_oracle_pins.py.  Every function below is pinned there.
@@ -257,6 +267,182 @@ void orc_attention(const float *q, int gq, const float *kh, const float *vh, int
         }
     }
     free(logit);
+}
+
+/* ------------------------------------------------------------------------ */
+/* 8-bit KV formats ([P1] section 3.1: FP8 E4M3 with a static per-tensor or  */
+/* per-head scale, or INT8 with a dynamic per-token scale, dequantized by    */
+/* the attention kernel as it reads; [P2] part B.1: FP8 and INT8 hold the    */
+/* cache at half the fp16 bytes).  Both keep the residual window and group   */
+/* bookkeeping of the low-bit format: tokens [0, n_q) are quantized, every   */
+/* token on its own (no per-channel key groups).                             */
+/* ------------------------------------------------------------------------ */
+
+#define ORC_FMT_INT8 1
+#define ORC_FMT_FP8_E4M3 2
+
+/* FP8 E4M3 (the OCP "FN" variant): 1 sign bit, 4 exponent bits (bias 7), 3
+ * fraction bits; exponent 0 holds subnormals (fraction * 2^-9); there is no
+ * infinity, and only exponent 15 with fraction 7 is NaN, so the largest
+ * finite value is 1.75 * 2^8 = 448. */
+float orc_fp8_e4m3_decode(uint8_t c)
+{
+    int sign = (c >> 7) & 1;
+    int expo = (c >> 3) & 0xf;
+    int frac = c & 7;
+    double v;
+    if (expo == 15 && frac == 7)
+        v = NAN;
+    else if (expo == 0)
+        v = ldexp((double)frac, -9);
+    else
+        v = ldexp((double)(frac + 8), expo - 10);
+    return (float)(sign ? -v : v);
+}
+
+/* Nearest E4M3 value of a float, ties to even, saturating at +-448; the sign
+ * of a value that rounds to zero is kept (code 0x80 for -0). */
+uint8_t orc_fp8_e4m3_encode(float xf)
+{
+    double x = (double)xf;
+    uint8_t sign = signbit(x) ? 0x80 : 0;
+    double a = fabs(x);
+    if (isnan(x))
+        return (uint8_t)(sign | 0x7f);
+    if (a >= 448.0)
+        return (uint8_t)(sign | 0x7e);
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal range: value = m * 2^-9 with m an integer 0..8 */
+        double m = rint(ldexp(a, 9)); /* exact scaling; ties to even */
+        return (uint8_t)(sign | (uint8_t)m); /* m == 8 is the smallest normal */
+    }
+    int e2;
+    frexp(a, &e2);
+    int e = e2 - 1;                    /* a in [2^e, 2^(e+1)), -6 <= e <= 8 */
+    double m = rint(ldexp(a, 3 - e));  /* in [8, 16] */
+    if (m == 16.0) {
+        m = 8.0;
+        e += 1;
+    }
+    /* a < 448 rounds to at most 448 = 1.75 * 2^8 (e = 8, m = 14) */
+    return (uint8_t)(sign | (uint8_t)((e + 7) << 3) | (uint8_t)((int)m - 8));
+}
+
+/* One token under a static scale: code = E4M3(x * (1/scale)), the quotient
+ * clamped to +-448 first.  A scale that is not positive gives 1/scale := 0
+ * (all codes +0). */
+void orc_quantize_token_fp8(const uint16_t *x, int d, float scale, uint8_t *codes)
+{
+    float inv = (scale > 0.0f) ? 1.0f / scale : 0.0f;
+    for (int c = 0; c < d; ++c) {
+        float t = orc_h2f(x[c]) * inv;
+        if (t > 448.0f) t = 448.0f;
+        if (t < -448.0f) t = -448.0f;
+        codes[c] = orc_fp8_e4m3_encode(t);
+    }
+}
+
+/* One key or value token of an 8-bit format.  INT8: the min/max quantizer
+ * above with 8 bits over the token's d channels (dynamic, per token), scale
+ * and zero in *s, *z.  FP8: the static scale; *s = *z = 0. */
+static void quantize_token8(int fmt, const uint16_t *x, int d, float scale,
+                            uint8_t *codes, uint16_t *s, uint16_t *z)
+{
+    if (fmt == ORC_FMT_FP8_E4M3) {
+        orc_quantize_token_fp8(x, d, scale, codes);
+        *s = 0;
+        *z = 0;
+    } else {
+        quantize_set(x, d, 1, 8, codes, 1, s, z);
+    }
+}
+
+/* Whole-stream quantization in an 8-bit format (fmt 1 = INT8 per token,
+ * 2 = FP8 E4M3 with static scales kscale / vscale of this kv head).
+ * k, v: [n][d]; kcodes, vcodes: [n_q][d]; ks, kz, vs, vz: [n_q] (INT8 only,
+ * zeros for FP8).  Returns n_q. */
+int orc_prefill_stream8(int fmt, const uint16_t *k, const uint16_t *v, int n, int d, int G, int R,
+                        float kscale, float vscale,
+                        uint8_t *kcodes, uint16_t *ks, uint16_t *kz,
+                        uint8_t *vcodes, uint16_t *vs, uint16_t *vz)
+{
+    int nq = orc_num_quantized(n, G, R);
+    for (int t = 0; t < nq; ++t) {
+        quantize_token8(fmt, k + (long)t * d, d, kscale, kcodes + (long)t * d, ks + t, kz + t);
+        quantize_token8(fmt, v + (long)t * d, d, vscale, vcodes + (long)t * d, vs + t, vz + t);
+    }
+    return nq;
+}
+
+/* Incremental form of orc_prefill_stream8, with the same flush rule as
+ * orc_append_stream (the oldest G tail tokens once the tail holds R + G). */
+int orc_append_stream8(int fmt, uint16_t *hist_k, uint16_t *hist_v, int cap, int *n, int *nq,
+                       const uint16_t *k_new, const uint16_t *v_new, int d, int G, int R,
+                       float kscale, float vscale,
+                       uint8_t *kcodes, uint16_t *ks, uint16_t *kz,
+                       uint8_t *vcodes, uint16_t *vs, uint16_t *vz)
+{
+    if (*n >= cap) return -1;
+    memcpy(hist_k + (long)(*n) * d, k_new, sizeof(uint16_t) * d);
+    memcpy(hist_v + (long)(*n) * d, v_new, sizeof(uint16_t) * d);
+    *n += 1;
+    if (*n - *nq == R + G) {
+        for (int t = *nq; t < *nq + G; ++t) {
+            quantize_token8(fmt, hist_k + (long)t * d, d, kscale, kcodes + (long)t * d, ks + t, kz + t);
+            quantize_token8(fmt, hist_v + (long)t * d, d, vscale, vcodes + (long)t * d, vs + t, vz + t);
+        }
+        *nq += G;
+        return 1;
+    }
+    return 0;
+}
+
+/* Dequantized stream of an 8-bit format.  INT8: fmaf(code, s_t, z_t); FP8:
+ * E4M3(code) * scale, one fp32 rounding; residual tokens as stored. */
+void orc_dequantize_stream8(int fmt, const uint16_t *k, const uint16_t *v, int n, int nq, int d,
+                            float kscale, float vscale,
+                            const uint8_t *kcodes, const uint16_t *ks, const uint16_t *kz,
+                            const uint8_t *vcodes, const uint16_t *vs, const uint16_t *vz,
+                            float *out_k, float *out_v)
+{
+    for (int t = 0; t < n; ++t) {
+        for (int c = 0; c < d; ++c) {
+            long i = (long)t * d + c;
+            if (t < nq && fmt == ORC_FMT_FP8_E4M3) {
+                out_k[i] = orc_fp8_e4m3_decode(kcodes[i]) * kscale;
+                out_v[i] = orc_fp8_e4m3_decode(vcodes[i]) * vscale;
+            } else if (t < nq) {
+                out_k[i] = fmaf((float)kcodes[i], orc_h2f(ks[t]), orc_h2f(kz[t]));
+                out_v[i] = fmaf((float)vcodes[i], orc_h2f(vs[t]), orc_h2f(vz[t]));
+            } else {
+                out_k[i] = orc_h2f(k[i]);
+                out_v[i] = orc_h2f(v[i]);
+            }
+        }
+    }
+}
+
+/* Bytes of one stream in an 8-bit format: one byte per code, plus (INT8) an
+ * fp16 (scale, zero) pair per quantized key token and per value token, plus
+ * the fp16 residual.  FP8's static scales belong to the layer, not to a
+ * stream, and are not counted. */
+double orc_stream_bytes8(int fmt, long n, int d, int G, int R)
+{
+    long nq = orc_num_quantized((int)n, G, R);
+    double codes = (double)nq * d * 2.0;
+    double meta = fmt == ORC_FMT_INT8 ? (double)nq * 8.0 : 0.0;
+    double resid = (double)(n - nq) * d * 2.0 * 2.0;
+    return codes + meta + resid;
+}
+
+void orc_fp8_decode_array(const uint8_t *c, float *f, long count)
+{
+    for (long i = 0; i < count; ++i) f[i] = orc_fp8_e4m3_decode(c[i]);
+}
+
+void orc_fp8_encode_array(const float *f, uint8_t *c, long count)
+{
+    for (long i = 0; i < count; ++i) c[i] = orc_fp8_e4m3_encode(f[i]);
 }
 
 /* ------------------------------------------------------------------------ */

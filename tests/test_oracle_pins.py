@@ -431,6 +431,202 @@ def test_bytes_closed_forms_golden(orc):
 
 
 # --------------------------------------------------------------------------
+# 8-bit formats ("KV cache compression: ...", section 3.1: FP8 E4M3 with a
+# static per-head scale, or INT8 with a dynamic per-token scale; "KV
+# compression and quantization", part B.1: both at half the fp16 bytes).
+# The E4M3 codec is checked against torch's float8_e4m3fn conversion, an
+# independent implementation of the same format.
+# --------------------------------------------------------------------------
+
+def _torch_e4m3(x):
+    import torch
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_fp8_decode_every_code(orc):
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ours = orc.fp8_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    # facts of the format: largest finite 448, smallest subnormal 2^-9, 1.0 = 0x38
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9 and ours[0x38] == 1.0
+
+
+def test_fp8_encode_matches_torch(orc):
+    rng = np.random.default_rng(8)
+    mant = rng.random(200000) + 1.0
+    expo = rng.integers(-12, 9, size=mant.size)
+    x = mant * np.exp2(expo) * rng.choice([-1.0, 1.0], size=mant.size)
+    x = np.clip(x, -448.0, 448.0).astype(np.float32)
+    # exact halfway points between neighbouring codes (ties, both parities)
+    # and the floats just beside them
+    vals = np.sort(orc.fp8_decode(np.arange(0, 0x7F, dtype=np.uint8)).astype(np.float64))
+    mid = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    near = np.concatenate([np.nextafter(mid, np.float32(0)), np.nextafter(mid, np.float32(1000))])
+    edges = np.array([0.0, -0.0, 448.0, -448.0, 2.0 ** -9, 2.0 ** -10, 2.0 ** -11, 3 * 2.0 ** -11,
+                      2.0 ** -6, 1e-30], np.float32)
+    for arr in (x, mid, -mid, near, -near, edges):
+        assert np.array_equal(orc.fp8_encode(arr), _torch_e4m3(arr))
+    # beyond the largest finite value the encoder saturates (the quantizer
+    # clamps before encoding, so only +-448 itself reaches it from there)
+    big = np.array([448.5, 464.0, 1e6, np.inf], np.float32)
+    assert np.all(orc.fp8_encode(big) == 0x7E) and np.all(orc.fp8_encode(-big) == 0xFE)
+
+
+def _fp8_bound(x, scale):
+    """|x - x_hat| for one element under a static scale: half a step of a
+    3-bit fraction (2^-4 relative) in the normal range, half the subnormal
+    spacing (2^-10 scale) below it, plus the fp32 roundings of x/s and e*s."""
+    return np.maximum(np.abs(x) * 2.0 ** -4, scale * 2.0 ** -10) * (1 + 2.0 ** -20) + 1e-30
+
+
+@pytest.mark.parametrize("G,R", [(32, 0), (16, 128)])
+def test_fp8_roundtrip_bound_and_saturation(orc, G, R):
+    rng = np.random.default_rng(81 + G)
+    n = 300
+    k = (rng.standard_normal((n, 128)) * np.exp2(rng.integers(-8, 6, size=(n, 1)))).astype(np.float16)
+    v = (rng.standard_normal((n, 128)) * 3).astype(np.float16)
+    ks, vs = 0.0125, 0.75    # about 5.6 and 336 at the top of the grid: k saturates in places
+    st = orc.StreamState.prefill(k.view(np.uint16), v.view(np.uint16), 8, 8, G, R,
+                                 fmt=orc.FMT_FP8, kscale=ks, vscale=vs)
+    nq = st.nq
+    assert nq == orc.num_quantized(n, G, R)
+    kh, vh = st.dequantize()
+    for x16, xh, sc in ((k, kh, ks), (v, vh, vs)):
+        x = x16[:nq].astype(np.float64)
+        sat = np.abs(x) > 448 * sc
+        assert np.all(np.abs(x - xh[:nq])[~sat] <= _fp8_bound(x, sc)[~sat])
+        assert np.array_equal(xh[:nq][sat], (np.sign(x[sat]) * np.float32(448 * sc)).astype(np.float32))
+        assert np.array_equal(xh[nq:], x16[nq:].astype(np.float32))
+    assert (np.abs(k[:nq].astype(np.float64)) > 448 * ks).any()
+    # no per-token metadata in this format
+    assert not st.key_meta()[0].any() and not st.value_meta()[0].any()
+
+
+def test_fp8_grid_aligned_exact(orc):
+    """Inputs that are E4M3 values times a power-of-two scale come back
+    exactly, with the codes they were built from; the key and value scales
+    are kept apart."""
+    rng = np.random.default_rng(82)
+    G, R, n = 16, 16, 16 * 6 + 5
+    ks, vs = 2.0 ** -3, 2.0 ** 2
+    ok = np.concatenate([np.arange(0, 0x7F), np.arange(0x80, 0xFF)]).astype(np.uint8)
+    kc = rng.choice(ok, size=(n, 128)).astype(np.uint8)
+    vc = rng.choice(ok, size=(n, 128)).astype(np.uint8)
+    kx = (orc.fp8_decode(kc).astype(np.float64) * ks).astype(np.float16)
+    vx = (orc.fp8_decode(vc).astype(np.float64) * vs).astype(np.float16)
+    st = orc.StreamState.prefill(kx.view(np.uint16), vx.view(np.uint16), 8, 8, G, R,
+                                 fmt=orc.FMT_FP8, kscale=ks, vscale=vs)
+    nq = st.nq
+    assert np.array_equal(st.key_codes(), kc[:nq]) and np.array_equal(st.value_codes(), vc[:nq])
+    kh, vh = st.dequantize()
+    assert np.array_equal(kh, kx.astype(np.float32)) and np.array_equal(vh, vx.astype(np.float32))
+
+
+def test_int8_per_token_grid_aligned(orc):
+    """INT8 is per token for keys as well as values: every key token gets its
+    own (s, z), so tokens built on different grids come back with exactly
+    the codes they were built from (a per-channel key grid would not)."""
+    rng = np.random.default_rng(83)
+    G, R, n = 32, 0, 32 * 3
+    kx = np.zeros((n, 128))
+    vx = np.zeros((n, 128))
+    codes = {}
+    meta = {}
+    for name, x in (("k", kx), ("v", vx)):
+        cs, S, Z = [], [], []
+        for t in range(n):
+            c, s, z = _grid_aligned(rng, 128, 8)
+            x[t] = z + c * s
+            cs.append(c)
+            S.append(s)
+            Z.append(z)
+        codes[name] = np.array(cs)
+        meta[name] = (f16bits(S), f16bits(Z))
+    st = orc.StreamState.prefill(f16bits(kx), f16bits(vx), 8, 8, G, R, fmt=orc.FMT_INT8)
+    assert st.nq == n
+    assert np.array_equal(st.key_codes(), codes["k"]) and np.array_equal(st.value_codes(), codes["v"])
+    for got, want in zip(st.key_meta() + st.value_meta(), meta["k"] + meta["v"]):
+        assert np.array_equal(got, want)
+    kh, vh = st.dequantize()
+    assert np.array_equal(kh, kx.astype(np.float32)) and np.array_equal(vh, vx.astype(np.float32))
+
+
+def test_int8_ties_to_even(orc):
+    # s = 1, z = 0: the token spans 0..255; x.5 goes to the even neighbour
+    tok = np.full(128, 7.0)
+    tok[:8] = [0.0, 255.0, 0.5, 1.5, 2.5, 254.5, 127.5, 128.5]
+    st = orc.StreamState.prefill(np.tile(f16bits(tok), (32, 1)), np.tile(f16bits(tok), (32, 1)),
+                                 8, 8, 32, 0, fmt=orc.FMT_INT8)
+    want = [0, 255, 0, 2, 2, 254, 128, 128]
+    assert st.key_codes()[5, :8].tolist() == want and st.value_codes()[9, :8].tolist() == want
+    assert orc.h2f(st.key_meta()[0][:1])[0] == 1.0 and orc.h2f(st.key_meta()[1][:1])[0] == 0.0
+
+
+def test_int8_roundtrip_bound_and_extreme_codes(orc):
+    from quantized_decode_attention_kivi_amd import synth
+    w = synth.Workload("t", 1, 4, 2, 8, 8, 32, 128, context=1024 + 45, tag=84)
+    K, V = synth.make_kv(w)
+    kb = K.numpy().view(np.uint16)
+    vb = V.numpy().view(np.uint16)
+    for h in range(2):
+        st = orc.StreamState.prefill(kb[0, h], vb[0, h], 8, 8, 32, 128, fmt=orc.FMT_INT8)
+        nq = st.nq
+        kh, vh = st.dequantize()
+        for xb, xh, (s16, z16), c in ((kb[0, h], kh, st.key_meta(), st.key_codes()),
+                                      (vb[0, h], vh, st.value_meta(), st.value_codes())):
+            x = orc.h2f(xb[:nq]).astype(np.float64)
+            s = orc.h2f(s16)[:, None]
+            z = orc.h2f(z16)[:, None]
+            assert np.all(np.abs(x - xh[:nq]) <= _roundtrip_bound(x, s, z, 8))
+            assert np.all(c.min(axis=1) == 0) and np.all(c.max(axis=1) == 255)
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("G,R", [(32, 0), (16, 128), (32, 128)])
+def test_8bit_prefill_equals_prefill_plus_appends(orc, fmt, G, R):
+    n_total, m = 420, 101
+    rng = np.random.default_rng(85 + G + R + fmt)
+    kb = (rng.standard_normal((n_total, 128)) * 4).astype(np.float16).view(np.uint16)
+    vb = rng.standard_normal((n_total, 128)).astype(np.float16).view(np.uint16)
+    kw = dict(fmt=fmt, kscale=0.02, vscale=0.01)
+    full = orc.StreamState.prefill(kb, vb, 8, 8, G, R, cap=n_total, **kw)
+    inc = orc.StreamState.prefill(kb[:m], vb[:m], 8, 8, G, R, cap=n_total, **kw)
+    for t in range(m, n_total):
+        inc.append(kb[t], vb[t])
+        assert inc.nq == orc.num_quantized(inc.n, G, R)
+    assert inc.n == full.n and inc.nq == full.nq
+    assert np.array_equal(inc.key_codes(), full.key_codes())
+    assert np.array_equal(inc.value_codes(), full.value_codes())
+    for a, b in zip(inc.key_meta() + inc.value_meta(), full.key_meta() + full.value_meta()):
+        assert np.array_equal(a, b)
+    ka, va = inc.dequantize()
+    kf, vf = full.dequantize()
+    assert np.array_equal(ka, kf) and np.array_equal(va, vf)
+
+
+def test_8bit_bytes_golden(orc):
+    """FP8 holds 160 KiB per token for the 80-layer, 8-kv-head, d = 128 shape
+    (section 8.1), half the fp16 cache (part B.1); INT8 adds two fp16 pairs
+    per token and head."""
+    g = _golden("bytes_70b_shape.json")
+    L, H, d = g["shape"]["layers"], g["shape"]["kv_heads"], g["shape"]["head_dim"]
+    n = 4096
+    fp8 = orc.stream_bytes(n, d, 8, 8, 32, 0, fmt=orc.FMT_FP8)
+    int8 = orc.stream_bytes(n, d, 8, 8, 32, 0, fmt=orc.FMT_INT8)
+    assert fp8 * L * H / n == g["fp8_kib_per_token"] * 1024
+    assert fp8 == orc.kv_bytes_closed_form(1, 1, n, d, 1)
+    assert fp8 / orc.stream_bytes(n, d, 16, 16, 32, 0) == 0.5
+    assert int8 == fp8 + n * 8
+    # with a residual window the newest tokens are counted at fp16
+    assert orc.stream_bytes(n, d, 8, 8, 32, 128, fmt=orc.FMT_FP8) == (n - 128) * 256 + 128 * 512
+
+
+# --------------------------------------------------------------------------
 # Mutation check: planted mistakes in a copy of the oracle must be caught
 # --------------------------------------------------------------------------
 
@@ -445,6 +641,13 @@ MUTATIONS = [
     ("logit[t] = exp(logit[t] - m);", "logit[t] = exp(logit[t]);", None),  # still exact (no overflow here)
     ("p = logit[t] / l;", "p = logit[t];", "attn"),                     # dropped normalisation
     ("mn = mn + 0.0f;", "mn = mn;", "negzero"),                        # -0 not canonicalised
+    ("double m = rint(ldexp(a, 3 - e));", "double m = floor(ldexp(a, 3 - e) + 0.5);", "fp8enc"),  # ties away
+    ("v = ldexp((double)(frac + 8), expo - 10);", "v = ldexp((double)(frac + 8), expo - 9);", "fp8dec"),
+    ("quantize_token8(fmt, k + (long)t * d, d, kscale,", "quantize_token8(fmt, k + (long)t * d, d, vscale,",
+     "fp8grid"),                                                        # key/value scales swapped
+    ("out_k[i] = orc_fp8_e4m3_decode(kcodes[i]) * kscale;",
+     "out_k[i] = orc_fp8_e4m3_decode(kcodes[i]);", "fp8grid"),          # scale not applied
+    ("quantize_set(x, d, 1, 8, codes, 1, s, z);", "quantize_set(x, d, 1, 7, codes, 1, s, z);", "int8grid"),
 ]
 
 
@@ -459,6 +662,10 @@ def test_pin_catches_planted_mistakes(tmp_path):
         "append": "test_prefill_equals_prefill_plus_appends",
         "attn": "test_attention_weights_sum_to_one",
         "negzero": "test_negative_zero_extremes_canonicalised",
+        "fp8enc": "test_fp8_encode_matches_torch",
+        "fp8dec": "test_fp8_decode_every_code",
+        "fp8grid": "test_fp8_grid_aligned_exact",
+        "int8grid": "test_int8_per_token_grid_aligned",
     }
     for i, (old, new, which) in enumerate(MUTATIONS):
         assert old in src, old
