@@ -73,16 +73,26 @@ def n_quant(n, G, R):
     return 0 if n <= R else G * ((n - R) // G)
 
 
+def meta_bytes(nq, w, d=128):
+    """fp16 (scale, zero) pairs of n_q quantized tokens of one stream: per
+    (key group, channel) and per value token (low-bit format), per key and per
+    value token (INT8), none (FP8: static per-head scales, read once)."""
+    if w.kv_format == 2:
+        return 0
+    if w.kv_format == 1:
+        return nq * 8
+    return (nq // w.group_size) * d * 4 + nq * 4
+
+
 def attention_bytes(lens, w, d=128):
     """Bytes one decode-attention launch must read/write: per (sequence, kv
-    head) the packed key/value codes of the n_q quantized tokens, one fp16
-    (scale, zero) pair per (key group, channel) and per value token, the fp16
-    residual keys and values; per sequence the fp16 query and fp32 output."""
+    head) the packed key/value codes of the n_q quantized tokens, their
+    scale/zero pairs (meta_bytes), the fp16 residual keys and values; per
+    sequence the fp16 query and fp32 output."""
     tot = 0
     for n in lens:
         nq = n_quant(int(n), w.group_size, w.residual)
-        per_head = (nq * d * (w.k_bits + w.v_bits) // 8 + (nq // w.group_size) * d * 4 + nq * 4
-                    + (int(n) - nq) * d * 2 * 2)
+        per_head = nq * d * (w.k_bits + w.v_bits) // 8 + meta_bytes(nq, w, d) + (int(n) - nq) * d * 2 * 2
         tot += w.num_kv_heads * per_head + w.num_q_heads * d * (2 + 4)
     return tot
 
@@ -93,7 +103,7 @@ def prefill_bytes(lens, w, d=128):
     for n in lens:
         nq = n_quant(int(n), w.group_size, w.residual)
         tot += w.num_kv_heads * (int(n) * d * 2 * 2 + nq * d * (w.k_bits + w.v_bits) // 8
-                                 + (nq // w.group_size) * d * 4 + nq * 4 + (int(n) - nq) * d * 2 * 2)
+                                 + meta_bytes(nq, w, d) + (int(n) - nq) * d * 2 * 2)
     return tot
 
 
@@ -145,7 +155,7 @@ def write_traffic(args):
     med = lambda v: float(np.median(v))
     f_scale = nbytes / (med(fetch[cal[0]]) * 1024.0)
     w_scale = nbytes / (med(write[cal[0]]) * 1024.0)
-    w = synth.WORKLOADS[args.workload]
+    w = synth.workload(args.workload)
     lens = synth.seq_lengths(w).astype(np.int64)
     fetched = med(fetch[att[0]]) * 1024.0 * f_scale
     written = med(write[att[0]]) * 1024.0 * w_scale
@@ -173,7 +183,7 @@ def write_traffic(args):
 # CPU baseline: the oracle on a bounded sample of the same workload
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(w, K, V, q, lens, budget_s):
+def cpu_baseline(w, K, V, q, lens, budget_s, scales=None):
     """Time the oracle (quantize the streams, then dequantize + fp64 attention)
     on whole (sequence, kv-head) streams of the workload until about
     budget_s seconds of CPU work are spent; report the oracle's decode
@@ -188,6 +198,9 @@ def cpu_baseline(w, K, V, q, lens, budget_s):
     done = []
     qf = oracle.h2f(q.cpu().numpy().view(np.uint16))
     scale = 128 ** -0.5
+    ksc = vsc = None
+    if scales is not None:
+        ksc, vsc = (t.cpu().numpy() for t in scales)
 
     def one(bh):
         b, h = bh
@@ -195,7 +208,9 @@ def cpu_baseline(w, K, V, q, lens, budget_s):
         kx = K[b, h, :n].cpu().numpy().view(np.uint16)
         vx = V[b, h, :n].cpu().numpy().view(np.uint16)
         t0 = time.perf_counter()
-        st = oracle.StreamState.prefill(kx, vx, w.k_bits, w.v_bits, w.group_size, w.residual)
+        st = oracle.StreamState.prefill(kx, vx, w.k_bits, w.v_bits, w.group_size, w.residual, fmt=w.kv_format,
+                                        kscale=float(ksc[h]) if ksc is not None else 0.0,
+                                        vscale=float(vsc[h]) if vsc is not None else 0.0)
         t1 = time.perf_counter()
         kh, vh = st.dequantize()
         oracle.attention(qf[b, h * gq:(h + 1) * gq], kh, vh, scale)
@@ -226,8 +241,7 @@ def cpu_baseline(w, K, V, q, lens, budget_s):
     for b, h in done:
         n = int(lens[b])
         nq = n_quant(n, w.group_size, w.residual)
-        sb += (nq * 128 * (w.k_bits + w.v_bits) // 8 + (nq // w.group_size) * 128 * 4 + nq * 4
-               + (n - nq) * 128 * 4 + gq * 128 * 6)
+        sb += (nq * 128 * (w.k_bits + w.v_bits) // 8 + meta_bytes(nq, w) + (n - nq) * 128 * 4 + gq * 128 * 6)
         stok += n
     return {
         "value": round(sb / attn_wall / 1e9, 4),
@@ -272,7 +286,7 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    w = synth.WORKLOADS[args.workload]
+    w = synth.workload(args.workload)
     lens = synth.seq_lengths(w).astype(np.int64)
     L = int(lens.max())
     print("# generating %s: B=%d Hkv=%d Hq=%d n=%d..%d k%d/v%d G=%d R=%d%s%s" % (
@@ -280,6 +294,8 @@ def main():
         w.group_size, w.residual, " paged" if w.paged else "",
         " (%d layers folded into the batch)" % w.layers if w.layers > 1 else ""), file=sys.stderr, flush=True)
     K, V = synth.make_kv(w, max_len=L, device=dev)
+    # FP8: static per-head scales, calibrated on the prompt (outside any timing)
+    scales = synth.calibrate_fp8_scales(K, V) if w.kv_format == 2 else None
     q = synth.make_query(w, device=dev)
     total_steps = args.warmup + 2 * args.steps
     toks = [synth.make_tokens(w, s, device=dev) for s in range(total_steps)]
@@ -292,11 +308,12 @@ def main():
         mb = (L + grow - R) // G + 1
         nb = int(sum(n_quant(int(n) + grow, G, R) // G for n in lens)) + 8
         shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, G, R, paged=True,
-                               num_blocks=nb, max_blocks_per_seq=mb)
+                               num_blocks=nb, max_blocks_per_seq=mb, kv_format=w.kv_format)
     else:
         shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, w.group_size, w.residual,
-                               max_tokens=L + total_steps + 8)
-    caches = [kvq.QuantizedKVCache(shape, device=dev) for _ in range(copies)]
+                               max_tokens=L + total_steps + 8, kv_format=w.kv_format)
+    ks, vs = scales if scales is not None else (None, None)
+    caches = [kvq.QuantizedKVCache(shape, device=dev, k_scale=ks, v_scale=vs) for _ in range(copies)]
     if w.paged:
         # blocks handed out in a shuffled order: a fragmented pool, as after
         # many requests have come and gone
@@ -391,13 +408,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 (int%d keys / int%d values, fp16 scale/zero and residual)" % (w.k_bits, w.v_bits),
+        "dtype": ["f32 (int%d keys / int%d values, fp16 scale/zero and residual)" % (w.k_bits, w.v_bits),
+                  "f32 (int8 keys and values, per-token fp16 scale/zero, fp16 residual)",
+                  "f32 (fp8 e4m3 keys and values, static fp32 per-head scales, fp16 residual)"][w.kv_format],
         "data": "synthetic (seeded N(0,1) K/V, 4 key outlier channels x20 per head, 1% value rows x5)",
         "config": {
             "workload": w.name,
             "num_seqs": w.num_seqs, "context": L, "num_q_heads": w.num_q_heads,
             "num_kv_heads": w.num_kv_heads, "head_dim": 128, "k_bits": w.k_bits, "v_bits": w.v_bits,
             "group_size": w.group_size, "residual": w.residual, "cache_copies_rotated": copies,
+            "kv_format": ["kivi", "int8", "fp8_e4m3"][w.kv_format],
             "paged": w.paged, "layers": w.layers, "min_context": int(lens.min()),
             "tokens": int(lens.sum()),
         },
@@ -423,7 +443,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, K, V, q, lens, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(w, K, V, q, lens, args.cpu_seconds, scales)
     res["quantize_token_layers_per_s"] = res["quantize_tokens_per_s"]
     if w.layers > 1:
         # n tokens of context across all layers: token count per layer

@@ -16,6 +16,10 @@
  *  - "KV cache compression" (jaedaily), formula paragraph: the per-channel
  *    key and per-token value dequantization q*s + z, and attention
  *    softmax(q k^T / sqrt(d_h)).
+ *  - "KV cache compression: ...", section 3.1, and "KV compression and
+ *    quantization", part B.1: 8-bit caches at half the fp16 bytes, either
+ *    FP8 E4M3 under a static per-head scale or INT8 under a dynamic
+ *    per-token scale, dequantized by the attention kernel while it reads.
  *
  * Numeric contract (identical on every entry point):
  *   n_q  = G * floor(max(0, n - R) / G) quantized tokens; [n_q, n) stay fp16.
@@ -24,6 +28,12 @@
  *   / (2^b - 1)); z = fp16(mn); inv = s > 0 ? 1/s : 0 (IEEE division);
  *   code = clamp(rint((x - z) * inv), 0, 2^b - 1) in fp32, ties to even.
  *   Dequantized value: fmaf(code, s, z).
+ *   8-bit formats (kv_format): INT8 applies the same quantizer with b = 8 to
+ *   every key and every value token over its 128 channels; FP8 E4M3 stores
+ *   code = E4M3_rn(clamp(x * (1/scale), -448, 448)) (ties to even, the sign
+ *   of a zero kept) with one static fp32 scale per kv head for keys and one
+ *   for values, dequantized as E4M3(code) * scale.  Both keep n_q, the
+ *   residual ring and the group flush above; only the codes differ.
  *   Attention: out[b][h] = sum_t softmax_t(scale * q[b][h] . k_t) v_t over all
  *   n tokens (dequantized part and fp16 residual), query head h reading kv
  *   head h / (Hq / H).  n = 0 gives out = 0.
@@ -54,6 +64,15 @@ extern "C" {
 
 #define KVQ_HEAD_DIM 128
 
+/* Cache formats (kvq_config.kv_format). */
+#define KVQ_FORMAT_KIVI 0     /* keys per channel over G-token groups, values per
+                                 token; k_bits, v_bits in {2, 4}                 */
+#define KVQ_FORMAT_INT8 1     /* keys and values per token, 8-bit min/max grid
+                                 computed at write time; k_bits = v_bits = 8     */
+#define KVQ_FORMAT_FP8_E4M3 2 /* keys and values FP8 E4M3 under static per-kv-head
+                                 scales (kvq_cache.k_scale / v_scale);
+                                 k_bits = v_bits = 8                             */
+
 typedef enum kvq_status {
     KVQ_OK = 0,
     KVQ_EINVAL = 1,        /* malformed argument (null pointer, bad size)      */
@@ -68,14 +87,15 @@ typedef struct kvq_config {
     int32_t num_seqs;           /* B >= 1                                        */
     int32_t num_kv_heads;       /* H >= 1                                        */
     int32_t head_dim;           /* d, must be 128                                */
-    int32_t k_bits;             /* key code width: 2 or 4                        */
-    int32_t v_bits;             /* value code width: 2 or 4                      */
+    int32_t k_bits;             /* key code width: 2 or 4 (8 in 8-bit formats)   */
+    int32_t v_bits;             /* value code width: 2 or 4 (8 in 8-bit formats) */
     int32_t group_size;         /* G: 16 or 32 tokens per key group              */
     int32_t residual;           /* R >= 0, a multiple of G                       */
     int32_t max_tokens;         /* contiguous mode: per-sequence capacity        */
     int32_t block_size;         /* 0 = contiguous; otherwise paged, == G         */
     int32_t num_blocks;         /* paged: blocks in the pool                     */
     int32_t max_blocks_per_seq; /* paged: length of one block-table row          */
+    int32_t kv_format;          /* KVQ_FORMAT_*                                  */
 } kvq_config;
 
 /* Device buffers of one cache.  Sizes come from kvq_buffer_sizes(). */
@@ -88,12 +108,17 @@ typedef struct kvq_cache {
     const int32_t *block_table; /* paged: [B][max_blocks_per_seq] block ids; a
                                    sequence's key group g lives in block
                                    block_table[b][g].  NULL in contiguous mode. */
+    const float *k_scale;       /* FP8 format: [H] static key scale per kv head,
+                                   positive and finite (caller-calibrated, e.g.
+                                   max |k| / 448); ignored by other formats      */
+    const float *v_scale;       /* FP8 format: [H] static value scale, likewise  */
 } kvq_cache;
 
 /* Byte sizes of the buffers of kvq_cache and of one group record.
  * Record = one (key group, kv head): G*d*k_bits/8 key-code bytes,
  * G*d*v_bits/8 value-code bytes, d fp16 key scales and d fp16 key zeros,
- * G fp16 value scales and G fp16 value zeros, arranged inside the record in
+ * G fp16 value scales and G fp16 value zeros (INT8: G fp16 key scales and
+ * zeros instead of d; FP8: no scales or zeros), arranged inside the record in
  * the order the decode kernel consumes them (an internal format: use
  * kv_export_codes / kv_dequantize for a logical view).  Contiguous mode holds B*H*floor(max(0,max_tokens-R)/G)
  * records; paged mode holds num_blocks*H records. */
@@ -155,7 +180,7 @@ size_t kv_decode_attention_workspace_bytes(const kvq_config *cfg, int32_t num_q_
  * dequantizes while it reads, the quantized part and the full-precision
  * residual are computed separately and merged).  q: fp16 [B][Hq][d];
  * out: fp32 [B][Hq][d]; Hq a multiple of H with Hq/H <= 16; softmax_scale is
- * normally 1/sqrt(d).  q must be 16-byte aligned.  The products
+ * normally 1/sqrt(d).  q must be 16-byte aligned.  KIVI format: the products
  * |q[c]| * s[c] of a query element and its key group's channel scale must
  * stay below 65504 (they are formed in fp16; true for any query of O(1..100)
  * against keys whose per-group range is below ~1000).
@@ -197,7 +222,9 @@ kvq_status kv_decode_attention_merge(const kvq_config *cfg, const kvq_cache *cac
  * [B][H][out_tokens][d], one code per element for t < n_q[b], 0 elsewhere;
  * k_s, k_z: fp16 bits [B][H][out_tokens/G][d] for groups < n_q[b]/G, 0
  * elsewhere; v_s, v_z: fp16 bits [B][H][out_tokens] for t < n_q[b], 0
- * elsewhere.  out_tokens must be a multiple of G. */
+ * elsewhere.  INT8 format: k_s, k_z are per token, [B][H][out_tokens] like
+ * v_s, v_z.  FP8 format: the four scale/zero arrays are not written and may
+ * be NULL.  out_tokens must be a multiple of G. */
 kvq_status kv_export_codes(const kvq_config *cfg, const kvq_cache *cache,
                            uint8_t *k_codes, uint8_t *v_codes,
                            uint16_t *k_s, uint16_t *k_z, uint16_t *v_s, uint16_t *v_z,

@@ -20,11 +20,19 @@ kvq_status make_layout(const kvq_config* cfg, Layout* L) {
     if (!cfg || !L) return KVQ_EINVAL;
     if (cfg->num_seqs < 1 || cfg->num_kv_heads < 1) return KVQ_EINVAL;
     if (cfg->head_dim != kD) return KVQ_EUNSUPPORTED;
-    if ((cfg->k_bits != 2 && cfg->k_bits != 4) || (cfg->v_bits != 2 && cfg->v_bits != 4)) return KVQ_EUNSUPPORTED;
+    if (cfg->kv_format == kFmtKivi) {
+        if ((cfg->k_bits != 2 && cfg->k_bits != 4) || (cfg->v_bits != 2 && cfg->v_bits != 4))
+            return KVQ_EUNSUPPORTED;
+    } else if (cfg->kv_format == kFmtInt8 || cfg->kv_format == kFmtFp8) {
+        if (cfg->k_bits != 8 || cfg->v_bits != 8) return KVQ_EINVAL;
+    } else {
+        return KVQ_EINVAL;
+    }
     const int G = cfg->group_size;
     if (G != 16 && G != 32) return KVQ_EUNSUPPORTED;
     if (cfg->residual < 0 || cfg->residual % G != 0) return KVQ_EINVAL;
     if (cfg->residual > (1 << 20)) return KVQ_EINVAL;
+    L->fmt = cfg->kv_format;
     L->B = cfg->num_seqs;
     L->H = cfg->num_kv_heads;
     L->kbits = cfg->k_bits;
@@ -53,8 +61,10 @@ kvq_status make_layout(const kvq_config* cfg, Layout* L) {
     L->vcode = G * kD * L->vbits / 8;
     L->vcode_off = L->kcode;
     L->kmeta_off = L->vcode_off + L->vcode;
-    L->vmeta_off = L->kmeta_off + kD * 4;
-    L->record = L->vmeta_off + G * 4;
+    // key table: per (group, channel) for KIVI, per token for INT8, none for FP8
+    const int kmeta = L->fmt == kFmtKivi ? kD * 4 : L->fmt == kFmtInt8 ? G * 4 : 0;
+    L->vmeta_off = L->kmeta_off + kmeta;
+    L->record = L->vmeta_off + (L->fmt == kFmtFp8 ? 0 : G * 4);
     return KVQ_OK;
 }
 
@@ -62,6 +72,9 @@ static kvq_status check_cache(const Layout& L, const kvq_cache* c) {
     if (!c || !c->packed || !c->k_res || !c->v_res || !c->n_tokens || !c->n_quant) return KVQ_EINVAL;
     if (L.paged && !c->block_table) return KVQ_EINVAL;
     if (((uintptr_t)c->packed & 15) || ((uintptr_t)c->k_res & 15) || ((uintptr_t)c->v_res & 15))
+        return KVQ_EINVAL;
+    if (L.fmt == kFmtFp8 && (!c->k_scale || !c->v_scale || ((uintptr_t)c->k_scale & 3) ||
+                             ((uintptr_t)c->v_scale & 3)))
         return KVQ_EINVAL;
     return KVQ_OK;
 }
@@ -195,7 +208,8 @@ kvq_status kv_export_codes(const kvq_config* cfg, const kvq_cache* cache, uint8_
     kvq_status st = make_layout(cfg, &L);
     if (st != KVQ_OK) return st;
     if ((st = check_cache(L, cache)) != KVQ_OK) return st;
-    if (!k_codes || !v_codes || !k_s || !k_z || !v_s || !v_z) return KVQ_EINVAL;
+    if (!k_codes || !v_codes) return KVQ_EINVAL;
+    if (L.fmt != kFmtFp8 && (!k_s || !k_z || !v_s || !v_z)) return KVQ_EINVAL;
     if (out_tokens < 0 || out_tokens % L.G) return KVQ_EINVAL;
     return hip_status(launch_export(L, *cache, k_codes, v_codes, k_s, k_z, v_s, v_z, out_tokens,
                                     (hipStream_t)stream));

@@ -31,6 +31,7 @@
 // The kernel boundary makes the partials visible to it; a per-workgroup
 // device-scope release would write back the XCD's L2 once per workgroup.
 #include <algorithm>
+#include <type_traits>
 
 #include "kvq_device.h"
 
@@ -218,6 +219,62 @@ __device__ __forceinline__ uint32_t issue_unit(lds_u8* buf, const Layout& L, con
         if (lane < 32 + G / 4)
             lds_load16(rs, buf + S::META + i * S::MREC,
                        lane < 32 ? L.kmeta_off + 16 * lane : L.vmeta_off + 16 * (lane - 32));
+    }
+    return has;
+}
+
+// 8-bit formats (INT8, FP8 E4M3): one 32-token unit (NR = 32/G records)
+// staged the same way, byte offsets inside one stage buffer:
+//   KC   key bytes: load i = 2rt + half puts the 16 bytes lane (g, n) feeds
+//        the key product of row tile rt (token 16rt + n, channels
+//        32g + 16half .. +15) at KC + 1024 i + 16 lane.
+//   VC   value bytes.  G = 32: bytes 16i .. 16i+15 of lane l's 64 at
+//        VC + 1024 i + 16 l.  G = 16: record r's lane-l bytes 16half .. at
+//        VC + 1024 (2r + half) + 16 l.
+//   META INT8 only: record r's per-token key table (4G bytes) then its value
+//        table (4G bytes) at META + 8G r.
+template <int G, int F>
+struct Stage8 {
+    static constexpr int NR = 32 / G;
+    static constexpr int SPT = G == 16 ? 4 : 8;
+    static constexpr int KC = 0;
+    static constexpr int VC = 4096;
+    static constexpr int META = 8192;
+    static constexpr int MREC = F == kFmtInt8 ? 8 * G : 0;
+    static constexpr int BYTES = META + NR * MREC;
+    static constexpr int PITCH = (BYTES + 15) / 16 * 16;
+    static constexpr int LOADS = 8 + (F == kFmtInt8 ? NR : 0);
+};
+
+template <int G, int F, bool PG>
+__device__ __forceinline__ uint32_t issue_unit8(lds_u8* buf, const Layout& L, const kvq_cache& c, int b, int h,
+                                                int unit, int ngroups, int lane) {
+    using S = Stage8<G, F>;
+    const int g = lane >> 4, n = lane & 15;
+    uint32_t base = (uint32_t)(uintptr_t)buf;
+    asm volatile("" : "+s"(base));
+    buf = (lds_u8*)(uintptr_t)base;
+    uint32_t has = 0;
+#pragma unroll
+    for (int i = 0; i < S::NR; ++i) {
+        const int grp = unit * S::NR + i;
+        const uint8_t* rec = grp < ngroups ? record_at_t<PG>(L, c.packed, c.block_table, b, h, grp) : nullptr;
+        has |= (rec != nullptr) << i;
+        const u32x4 rs = record_desc(rec, L.record);
+        if (G == 32) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)   // k = 2rt + half
+                lds_load16(rs, buf + S::KC + 1024 * k, kD * (16 * (k >> 1) + n) + 32 * g + 16 * (k & 1));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) lds_load16(rs, buf + S::VC + 1024 * k, L.vcode_off + 64 * lane + 16 * k);
+        } else {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                lds_load16(rs, buf + S::KC + 1024 * (2 * i + hf), kD * n + 32 * g + 16 * hf);
+                lds_load16(rs, buf + S::VC + 1024 * (2 * i + hf), L.vcode_off + 32 * lane + 16 * hf);
+            }
+        }
+        if (F == kFmtInt8 && lane < G / 2) lds_load16(rs, buf + S::META + i * S::MREC, L.kmeta_off + 16 * lane);
     }
     return has;
 }
@@ -430,6 +487,123 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
     });
 }
 
+// Eight 8-bit codes (words w0, w1, byte order) as an fp16 operand.  INT8:
+// code - 128, exact: v_perm_b32 pairs each byte with 0x64 into the fp16
+// number 1024 + code, and one packed subtraction recentres it.  FP8: the
+// E4M3 values themselves (exact in fp16).
+template <int F>
+__device__ __forceinline__ h8 conv8(uint32_t w0, uint32_t w1) {
+    if (F == kFmtInt8) {
+        const h2 off = h2{(_Float16)-1152.0f, (_Float16)-1152.0f};
+        const h2 a = as_h2(__builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u)) + off;
+        const h2 b = as_h2(__builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u)) + off;
+        const h2 c = as_h2(__builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u)) + off;
+        const h2 d = as_h2(__builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u)) + off;
+        return make_h8(a, b, c, d);
+    }
+    return make_h8(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false),
+                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true),
+                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false),
+                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true));
+}
+
+// One staged unit of an 8-bit format.  The query is an exact fp16 operand
+// and so are the codes, so each key product is one MFMA per 32 channels with
+// no high/low split; the per-token dequantization acts on the finished dot
+// products:
+//   INT8  q . k_t = s_t (q . (code_t - 128)) + (z_t + 128 s_t) sum_c q_c
+//   FP8   q . k_t = s_k (q . e_t)       (s_k folded into sl2 by the caller)
+// and on the value side p s_t multiplies the code operand as in the low-bit
+// format, with z_t + 128 s_t (INT8) or 0 (FP8) as the zero term.  LP: the
+// columns n and n + 8 hold the same head, so both lane halves compute the
+// same logits and need no limb partner.  qsum: sum_c q_c of the lane's head;
+// vscl: the static value scale (FP8).
+template <int G, int F, bool LP>
+__device__ __forceinline__ void process_unit8(const lds_u8* buf, uint32_t has, WaveAcc& A, const QOps& Q,
+                                              float sl2, float qsum, float vscl, int lane) {
+    using S = Stage8<G, F>;
+    constexpr int SPT = S::SPT;
+    const int g = lane >> 4;
+
+    f4 C[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const u32x4 x0 = lds_read<u32x4>(buf + S::KC + 1024 * (2 * rt) + 16 * lane);
+        const u32x4 x1 = lds_read<u32x4>(buf + S::KC + 1024 * (2 * rt + 1) + 16 * lane);
+        f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        acc = mfma(conv8<F>(x0[0], x0[1]), Q.q[0], acc);
+        acc = mfma(conv8<F>(x0[2], x0[3]), Q.q[1], acc);
+        acc = mfma(conv8<F>(x1[0], x1[1]), Q.q[2], acc);
+        acc = mfma(conv8<F>(x1[2], x1[3]), Q.q[3], acc);
+        C[rt] = acc;
+    }
+
+    // value words of this lane: w[2][8]; column tile ct uses w[0][ct] and
+    // w[1][ct] (G = 32: the slot halves 0-3 and 4-7 of the same record;
+    // G = 16: slots 0-3 of records 0 and 1)
+    uint32_t w[2][8];
+    if (G == 32) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const u32x4 v = lds_read<u32x4>(buf + S::VC + 1024 * k + 16 * lane);
+            w[0][2 * k] = v[0];
+            w[1][2 * k] = v[1];
+            w[0][2 * k + 1] = v[2];
+            w[1][2 * k + 1] = v[3];
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const u32x4 v = lds_read<u32x4>(buf + S::VC + 1024 * (2 * r + hf) + 16 * lane);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[r][4 * hf + e] = v[e];
+            }
+    }
+
+    // slot k = 4rt + i <-> token 16rt + 4g + i
+    float x[8], vs[8], vz[8];
+    bool valid[8];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const int rec = S::NR == 2 ? rt : 0;
+        float ks4[4], kz4[4], vs4[4], vz4[4];
+        if (F == kFmtInt8) {
+            // the record's tables: per lane group g, SPT scales then SPT zeros
+            const lds_u8* km = buf + S::META + rec * S::MREC + g * 4 * SPT;
+            const lds_u8* vm = km + 4 * G;
+            const int s0 = S::NR == 2 ? 0 : 4 * rt;   // first slot of this row tile
+            const u32x2 a = lds_read<u32x2>(km + 2 * s0);
+            const u32x2 bz = lds_read<u32x2>(km + 2 * SPT + 2 * s0);
+            const u32x2 cv = lds_read<u32x2>(vm + 2 * s0);
+            const u32x2 dz = lds_read<u32x2>(vm + 2 * SPT + 2 * s0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ks4[i] = h2f((a[i >> 1] >> (16 * (i & 1))) & 0xffffu);
+                kz4[i] = h2f((bz[i >> 1] >> (16 * (i & 1))) & 0xffffu);
+                vs4[i] = h2f((cv[i >> 1] >> (16 * (i & 1))) & 0xffffu);
+                vz4[i] = h2f((dz[i >> 1] >> (16 * (i & 1))) & 0xffffu);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = 4 * rt + i;
+            if (F == kFmtInt8) {
+                x[k] = fmaf(ks4[i], C[rt][i], fmaf(128.0f, ks4[i], kz4[i]) * qsum);
+                vs[k] = vs4[i];
+                vz[k] = fmaf(128.0f, vs4[i], vz4[i]);
+            } else {
+                x[k] = C[rt][i];
+                vs[k] = vscl;
+                vz[k] = 0.0f;
+            }
+            valid[k] = S::NR == 1 || ((has >> rec) & 1);
+        }
+    }
+    softmax_and_values<LP>(A, x, vs, vz, valid, sl2, lane, [&](int ct) -> h8 { return conv8<F>(w[0][ct], w[1][ct]); });
+}
+
 // Ring slot of token t0 + r (0 <= r < 32) given slot0 = t0 % ring; ring >= 16.
 __device__ __forceinline__ int ring_slot(int slot0, int r, int ring) {
     int s = slot0 + r;
@@ -544,17 +718,35 @@ __device__ __forceinline__ int unit_at(const SeqUnits& u, int x) {
     return x <= u.uq ? x : u.uq + (x - u.uq + kResCost - 1) / kResCost;
 }
 
+// Stage layout, unit issue and unit processing of a format.
+template <int G, int KB, int VB, int F>
+using StageT = typename std::conditional<F == kFmtKivi, Stage<G, KB, VB>, Stage8<G, F>>::type;
+
+template <int G, int KB, int VB, int F, bool PG>
+__device__ __forceinline__ uint32_t issue_any(lds_u8* buf, const Layout& L, const kvq_cache& c, int b, int h,
+                                              int unit, int ngroups, int lane) {
+    if constexpr (F == kFmtKivi) return issue_unit<G, KB, VB, PG>(buf, L, c, b, h, unit, ngroups, lane);
+    else return issue_unit8<G, F, PG>(buf, L, c, b, h, unit, ngroups, lane);
+}
+
+template <int G, int KB, int VB, int F, bool LP>
+__device__ __forceinline__ void process_any(const lds_u8* buf, uint32_t has, WaveAcc& A, const QOps& Q, float sl2,
+                                            float qsum, float vscl, int lane) {
+    if constexpr (F == kFmtKivi) process_unit<G, KB, VB, LP>(buf, has, A, Q, sl2, lane);
+    else process_unit8<G, F, LP>(buf, has, A, Q, sl2, qsum, vscl, lane);
+}
+
 // Units [lo, hi) of stream (b, h) by the four waves of the workgroup (wave w
 // takes lo + w, lo + w + 4, ...), combined into one partial result (heads
 // < gq: output[128] unnormalised, running max in log2 units, weight sum) at
 // `part`.  Called by every thread of the workgroup.
-template <int G, int KB, int VB, bool LP, bool PG>
+template <int G, int KB, int VB, int F, bool LP, bool PG>
 __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_b, float (*wm)[16], float (*wl)[16],
                                                float (*wpz)[16], const Layout& L, const kvq_cache& c,
                                                const half_t* __restrict__ q, float sl2, int gq, int b, int h,
                                                const SeqUnits& su, int lo, int hi, float* __restrict__ part,
                                                int lane, int wave) {
-    using S = Stage<G, KB, VB>;
+    using S = StageT<G, KB, VB, F>;
     // The lane index, produced afresh: per-lane addresses derived from it are
     // formed here, once per segment, instead of being hoisted out of the
     // segment loop and held (or spilled) across every unit loop.
@@ -576,6 +768,20 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
         // retire these here so that it places no wait on them inside the loop.
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
+    // 8-bit formats: sum_c q_c of the lane's head (INT8), the kv head's
+    // static scales (FP8; the key scale joins the logit scale)
+    float qsum = 0.0f, vscl = 0.0f, sl2q = sl2;
+    if (F == kFmtInt8) {
+        float t = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t += (float)Q.q[j][e];
+        qsum = group_sum(t);
+    } else if (F == kFmtFp8) {
+        sl2q = sl2 * c.k_scale[h];
+        vscl = c.v_scale[h];
+    }
     WaveAcc A;
     acc_init(A);
 
@@ -589,30 +795,30 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
             // (vmcnt counts this wave's outstanding loads, in issue order).
             lds_u8* const sa = (lds_u8*)(stage_a + wave * S::PITCH);
             lds_u8* const sb = (lds_u8*)(stage_b + wave * S::PITCH);
-            uint32_t ha = issue_unit<G, KB, VB, PG>(sa, L, c, b, h, u, su.ngroups, lane), hb = 0;
+            uint32_t ha = issue_any<G, KB, VB, F, PG>(sa, L, c, b, h, u, su.ngroups, lane), hb = 0;
             for (;;) {
                 if (u + kWaves < q1) {
                     __builtin_amdgcn_s_waitcnt(kLgkmZero);   // last reads of sb returned
-                    hb = issue_unit<G, KB, VB, PG>(sb, L, c, b, h, u + kWaves, su.ngroups, lane);
+                    hb = issue_any<G, KB, VB, F, PG>(sb, L, c, b, h, u + kWaves, su.ngroups, lane);
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::LOADS));
                 } else {
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
                 }
                 wave_sync();
                 set_progress_prio((q1 - u + kWaves - 1) / kWaves, ntot);
-                process_unit<G, KB, VB, LP>(sa, ha, A, Q, sl2, lane);
+                process_any<G, KB, VB, F, LP>(sa, ha, A, Q, sl2q, qsum, vscl, lane);
                 u += kWaves;
                 if (u >= q1) break;
                 if (u + kWaves < q1) {
                     __builtin_amdgcn_s_waitcnt(kLgkmZero);
-                    ha = issue_unit<G, KB, VB, PG>(sa, L, c, b, h, u + kWaves, su.ngroups, lane);
+                    ha = issue_any<G, KB, VB, F, PG>(sa, L, c, b, h, u + kWaves, su.ngroups, lane);
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::LOADS));
                 } else {
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
                 }
                 wave_sync();
                 set_progress_prio((q1 - u + kWaves - 1) / kWaves, ntot);
-                process_unit<G, KB, VB, LP>(sb, hb, A, Q, sl2, lane);
+                process_any<G, KB, VB, F, LP>(sb, hb, A, Q, sl2q, qsum, vscl, lane);
                 u += kWaves;
                 if (u >= q1) break;
             }
@@ -687,15 +893,17 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
 // fit the limb-packed kernels with INT2 values; without limb packing the
 // separate high/low query operands take 16 more registers, INT4 values more
 // than INT2 ones.  (Three waves lose little where the kernel waits on HBM.)
-constexpr int attn_waves(int G, int KB, int VB, bool LP, bool PG) {
-    return LP && VB == 2 && !(G == 16 && KB == 2) ? 4 : 3;
+// The 8-bit formats stage twice the bytes per unit: their LDS allows two
+// workgroups per CU, two waves per SIMD.
+constexpr int attn_waves(int G, int KB, int VB, int F, bool LP, bool PG) {
+    return F != kFmtKivi ? 2 : LP && VB == 2 && !(G == 16 && KB == 2) ? 4 : 3;
 }
 
-template <int G, int KB, int VB, bool LP, bool PG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves(G, KB, VB, LP, PG)))) void attn_kernel(
+template <int G, int KB, int VB, int F, bool LP, bool PG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves(G, KB, VB, F, LP, PG)))) void attn_kernel(
     Layout L, kvq_cache c, const half_t* __restrict__ q, float sl2, float* __restrict__ ws, int gq, int nwg,
     long meta_off) {
-    using S = Stage<G, KB, VB>;
+    using S = StageT<G, KB, VB, F>;
     // Two stage buffers per wave (ping-pong), in two arrays: the compiler
     // treats them as separate objects.  After the unit loop the same memory
     // holds the waves' accumulators (waves 0-1 in stage_a, 2-3 in stage_b).
@@ -769,7 +977,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves(
             asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l0));
             if (l0 == 0) meta[1 + s] = ps;
         }
-        attend_segment<G, KB, VB, LP, PG>(stage_a, stage_b, wm, wl, wpz, L, c, q, sl2, gq, b, h, su,
+        attend_segment<G, KB, VB, F, LP, PG>(stage_a, stage_b, wm, wl, wpz, L, c, q, sl2, gq, b, h, su,
                                           unit_at(su, lo), unit_at(su, hi), ws + ((long)w + s) * gq * kPart,
                                           lane, wave);
         if (ps + hi >= end) break;
@@ -933,7 +1141,7 @@ __global__ __launch_bounds__(256) void attn_merge_rows_kernel(Layout L, kvq_cach
 // Resident attention workgroups on the current device: CUs x workgroups per
 // CU for this instantiation (from its register and LDS footprint).  Falls
 // back to 256 CUs x 3 when no device is visible (host-only size queries).
-template <int G, int KB, int VB, bool LP, bool PG>
+template <int G, int KB, int VB, int F, bool LP, bool PG>
 static int attn_slots_for() {
     static int cached[64];
     int dev = 0;
@@ -942,7 +1150,7 @@ static int attn_slots_for() {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)attn_kernel<G, KB, VB, LP, PG>, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)attn_kernel<G, KB, VB, F, LP, PG>, 256, 0) !=
             hipSuccess || per_cu <= 0)
         per_cu = 3;
     (void)hipGetLastError();
@@ -956,15 +1164,19 @@ static inline bool limb_packed(int gq) { return gq <= 8; }
 
 template <bool LP, bool PG>
 static int attn_slots_lp(const Layout& L) {
-    switch (L.G * 100 + L.kbits * 10 + L.vbits) {
-        case 1622: return attn_slots_for<16, 2, 2, LP, PG>();
-        case 1624: return attn_slots_for<16, 2, 4, LP, PG>();
-        case 1642: return attn_slots_for<16, 4, 2, LP, PG>();
-        case 1644: return attn_slots_for<16, 4, 4, LP, PG>();
-        case 3222: return attn_slots_for<32, 2, 2, LP, PG>();
-        case 3224: return attn_slots_for<32, 2, 4, LP, PG>();
-        case 3242: return attn_slots_for<32, 4, 2, LP, PG>();
-        default: return attn_slots_for<32, 4, 4, LP, PG>();
+    switch (layout_key(L)) {
+        case 1622: return attn_slots_for<16, 2, 2, kFmtKivi, LP, PG>();
+        case 1624: return attn_slots_for<16, 2, 4, kFmtKivi, LP, PG>();
+        case 1642: return attn_slots_for<16, 4, 2, kFmtKivi, LP, PG>();
+        case 1644: return attn_slots_for<16, 4, 4, kFmtKivi, LP, PG>();
+        case 3222: return attn_slots_for<32, 2, 2, kFmtKivi, LP, PG>();
+        case 3224: return attn_slots_for<32, 2, 4, kFmtKivi, LP, PG>();
+        case 3242: return attn_slots_for<32, 4, 2, kFmtKivi, LP, PG>();
+        case 11688: return attn_slots_for<16, 8, 8, kFmtInt8, LP, PG>();
+        case 13288: return attn_slots_for<32, 8, 8, kFmtInt8, LP, PG>();
+        case 21688: return attn_slots_for<16, 8, 8, kFmtFp8, LP, PG>();
+        case 23288: return attn_slots_for<32, 8, 8, kFmtFp8, LP, PG>();
+        default: return attn_slots_for<32, 4, 4, kFmtKivi, LP, PG>();
     }
 }
 static int attn_slots(const Layout& L, int gq) {
@@ -1002,30 +1214,33 @@ hipError_t launch_attention_partials(const Layout& L, const AttnPlan& P, const k
                                      int num_q_heads, float scale, void* ws, hipStream_t s) {
     const int gq = num_q_heads / L.H;
     const float sl2 = scale * kLog2e;
-#define KVQ_ATT3(GG, KB, VB, LP, PG)                                                                       \
-    hipLaunchKernelGGL((attn_kernel<GG, KB, VB, LP, PG>), dim3(P.nwg), dim3(256), 0, s, L, c, q, sl2,        \
+#define KVQ_ATT3(GG, KB, VB, FF, LP, PG)                                                                   \
+    hipLaunchKernelGGL((attn_kernel<GG, KB, VB, FF, LP, PG>), dim3(P.nwg), dim3(256), 0, s, L, c, q, sl2,    \
                        (float*)ws, gq, P.nwg, (long)P.meta_off)
-#define KVQ_ATT2(GG, KB, VB, LP)         \
-    if (L.paged)                          \
-        KVQ_ATT3(GG, KB, VB, LP, true);   \
-    else                                  \
-        KVQ_ATT3(GG, KB, VB, LP, false)
-#define KVQ_ATT(GG, KB, VB)              \
-    if (limb_packed(gq)) {                \
-        KVQ_ATT2(GG, KB, VB, true);       \
-    } else {                              \
-        KVQ_ATT2(GG, KB, VB, false);      \
+#define KVQ_ATT2(GG, KB, VB, FF, LP)         \
+    if (L.paged)                              \
+        KVQ_ATT3(GG, KB, VB, FF, LP, true);   \
+    else                                      \
+        KVQ_ATT3(GG, KB, VB, FF, LP, false)
+#define KVQ_ATT(GG, KB, VB, FF)              \
+    if (limb_packed(gq)) {                    \
+        KVQ_ATT2(GG, KB, VB, FF, true);       \
+    } else {                                  \
+        KVQ_ATT2(GG, KB, VB, FF, false);      \
     }
-    const int key = L.G * 100 + L.kbits * 10 + L.vbits;
-    switch (key) {
-        case 1622: KVQ_ATT(16, 2, 2); break;
-        case 1624: KVQ_ATT(16, 2, 4); break;
-        case 1642: KVQ_ATT(16, 4, 2); break;
-        case 1644: KVQ_ATT(16, 4, 4); break;
-        case 3222: KVQ_ATT(32, 2, 2); break;
-        case 3224: KVQ_ATT(32, 2, 4); break;
-        case 3242: KVQ_ATT(32, 4, 2); break;
-        case 3244: KVQ_ATT(32, 4, 4); break;
+    switch (layout_key(L)) {
+        case 1622: KVQ_ATT(16, 2, 2, kFmtKivi); break;
+        case 1624: KVQ_ATT(16, 2, 4, kFmtKivi); break;
+        case 1642: KVQ_ATT(16, 4, 2, kFmtKivi); break;
+        case 1644: KVQ_ATT(16, 4, 4, kFmtKivi); break;
+        case 3222: KVQ_ATT(32, 2, 2, kFmtKivi); break;
+        case 3224: KVQ_ATT(32, 2, 4, kFmtKivi); break;
+        case 3242: KVQ_ATT(32, 4, 2, kFmtKivi); break;
+        case 3244: KVQ_ATT(32, 4, 4, kFmtKivi); break;
+        case 11688: KVQ_ATT(16, 8, 8, kFmtInt8); break;
+        case 13288: KVQ_ATT(32, 8, 8, kFmtInt8); break;
+        case 21688: KVQ_ATT(16, 8, 8, kFmtFp8); break;
+        case 23288: KVQ_ATT(32, 8, 8, kFmtFp8); break;
         default: return hipErrorInvalidValue;
     }
 #undef KVQ_ATT

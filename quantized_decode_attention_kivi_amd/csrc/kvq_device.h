@@ -72,6 +72,22 @@ __device__ __forceinline__ uint32_t quant_code(float x, float z, float inv, floa
     return (uint32_t)fminf(fmaxf(r, 0.0f), qmax);
 }
 
+// FP8 E4M3 (OCP): value of a code, exact (every E4M3 value is an fp16 value).
+__device__ __forceinline__ float fp8_value(uint32_t code) {
+    return (float)__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code, 1.0f, false)[0];
+}
+
+// FP8 E4M3 code of x * inv: the product clamped to +-448 (the largest finite
+// value), then rounded to the nearest code, ties to even, by the hardware
+// conversion.  inv = 1/scale, or 0 for a scale that is not positive.
+__device__ __forceinline__ float fp8_inv_scale(float scale) { return scale > 0.0f ? 1.0f / scale : 0.0f; }
+__device__ __forceinline__ uint32_t fp8_code2(float x0, float x1, float inv) {
+#pragma clang fp contract(off)
+    const float a = __builtin_amdgcn_fmed3f(x0 * inv, -448.0f, 448.0f);
+    const float b = __builtin_amdgcn_fmed3f(x1 * inv, -448.0f, 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;   // bytes: a, b
+}
+
 // ---------------------------------------------------------------------------
 // Positions inside a record (see kvq_internal.h for the layout).
 // ---------------------------------------------------------------------------
@@ -95,12 +111,14 @@ __device__ __forceinline__ void vcode_pos(const Layout& L, int t, int c, int* by
     *bit = code_bit(L.vbits, q % cpw);
 }
 
-// Byte offsets of the fp16 scale and zero of value token t.
-__device__ __forceinline__ int vmeta_pos(const Layout& L, int t) {
+// Byte offset of the fp16 scale of token t in a per-token table starting at
+// `off` (the value table; the INT8 key table); its zero follows 2*spt bytes on.
+__device__ __forceinline__ int tmeta_pos(const Layout& L, int off, int t) {
     int g, slot;
     vslot(t, &g, &slot);
-    return L.vmeta_off + g * 4 * L.spt + 2 * slot;   // zero at + 2*spt
+    return off + g * 4 * L.spt + 2 * slot;
 }
+__device__ __forceinline__ int vmeta_pos(const Layout& L, int t) { return tmeta_pos(L, L.vmeta_off, t); }
 
 __device__ __forceinline__ uint32_t kcode_at(const Layout& L, const uint8_t* rec, int t, int c) {
     int by, bi;
@@ -117,6 +135,13 @@ __device__ __forceinline__ uint16_t kscale_bits(const Layout& L, const uint8_t* 
 }
 __device__ __forceinline__ uint16_t kzero_bits(const Layout& L, const uint8_t* rec, int c) {
     return *(const uint16_t*)(rec + L.kmeta_off + 2 * kD + 2 * c);
+}
+// INT8 format: per-token key scale and zero.
+__device__ __forceinline__ uint16_t ktok_scale_bits(const Layout& L, const uint8_t* rec, int t) {
+    return *(const uint16_t*)(rec + tmeta_pos(L, L.kmeta_off, t));
+}
+__device__ __forceinline__ uint16_t ktok_zero_bits(const Layout& L, const uint8_t* rec, int t) {
+    return *(const uint16_t*)(rec + tmeta_pos(L, L.kmeta_off, t) + 2 * L.spt);
 }
 __device__ __forceinline__ uint16_t vscale_bits(const Layout& L, const uint8_t* rec, int t) {
     return *(const uint16_t*)(rec + vmeta_pos(L, t));

@@ -23,10 +23,17 @@
 //   [vmeta_off, +4G)      per lane group g: SPT value scales then SPT value
 //                         zeros, fp16, slot order (4*SPT bytes per group).
 //
-// Code order inside a 32-bit word (code_bit): INT4 code q (0..7) sits at nibble
+// Code order inside a 32-bit word (code_bit): 8-bit code q (0..3) in byte q;
+// INT4 code q (0..7) sits at nibble
 // {0,2,4,6,1,3,5,7}[q]; INT2 code q (0..15) at bit 4*(q%8) + 2*(q/8).  These
 // are the orders in which the gfx950 fp8 / fp4 conversion instructions return
 // nibbles, so the decode kernel unpacks a word straight into operand order.
+//
+// 8-bit formats (INT8, FP8 E4M3) keep the same sections with one byte per
+// code (code_bit(8, q) = 8q, so key bytes are in channel order and a lane's
+// value bytes in code order); their key scale/zero table is per token, laid
+// out like the value table (kmeta_off, 4G bytes, INT8 only), and FP8 records
+// carry no tables at all (its scales are per kv head, outside the records).
 //
 // Contiguous caches address record (b, h, g) at ((b*H + h)*groups + g); paged
 // caches at (block_table[b][g]*H + h).  The fp16 residual ring of (b, h) holds
@@ -43,7 +50,13 @@ namespace kvq {
 constexpr int kD = 128;          // head dim (only size implemented)
 constexpr int kMaxGq = 16;       // query heads per kv head
 
+// Cache formats (KVQ_FORMAT_*).
+constexpr int kFmtKivi = KVQ_FORMAT_KIVI;
+constexpr int kFmtInt8 = KVQ_FORMAT_INT8;
+constexpr int kFmtFp8 = KVQ_FORMAT_FP8_E4M3;
+
 struct Layout {
+    int fmt;
     int B, H, kbits, vbits, G, R, ring;
     int paged, num_blocks, max_blocks, groups;   // groups: record slots per sequence
     int capacity;                                 // max tokens a sequence may hold
@@ -60,8 +73,12 @@ __host__ __device__ inline int num_quantized(int n, int G, int R) {
     return over <= 0 ? 0 : G * (over / G);
 }
 
+// Instantiation key of a layout: format * 10000 + G * 100 + kbits * 10 + vbits.
+inline int layout_key(const Layout& L) { return L.fmt * 10000 + L.G * 100 + L.kbits * 10 + L.vbits; }
+
 // Bit offset of code q inside its 32-bit word.
 __host__ __device__ inline int code_bit(int bits, int q) {
+    if (bits == 8) return 8 * q;
     if (bits == 4) {
         const int nib = (q & 3) * 2 + ((q >> 2) & 1);   // {0,2,4,6,1,3,5,7}[q]
         return 4 * nib;

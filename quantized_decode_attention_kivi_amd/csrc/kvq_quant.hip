@@ -152,6 +152,115 @@ __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* 
     __syncthreads();  // LDS may be reused by the caller
 }
 
+// The same for the 8-bit formats ("KV cache compression: ...", section 3.1):
+// every key and value token on its own.  F = kFmtInt8: the min/max grid with
+// 8 bits over the token's 128 channels (the 16 threads of a row reduce it);
+// F = kFmtFp8: E4M3 codes under the kv head's static scales (inverses kinv,
+// vinv).  Key bytes go straight to the record in channel order; value bytes
+// through LDS into the lane-major operand order.
+template <int G, int F>
+__device__ void quantize_group8(QuantSmem<G>& sm, const Layout& L, const half_t* __restrict__ ksrc,
+                                const half_t* __restrict__ vsrc, uint8_t* __restrict__ rec, float kinv,
+                                float vinv) {
+    constexpr int NT = G / 16;
+    constexpr int SPT = G == 16 ? 4 : 8;
+    const int tid = threadIdx.x;
+    const int cg = tid & 15;
+    const int ts = tid >> 4;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int t = ts + 16 * j;
+        const uint4 a = *(const uint4*)(ksrc + t * kD + 8 * cg);
+        const uint4 b = *(const uint4*)(vsrc + t * kD + 8 * cg);
+        const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+        const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+        float kx[8], vx[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kx[2 * e] = h2f(aw[e] & 0xffffu);
+            kx[2 * e + 1] = h2f(aw[e] >> 16);
+            vx[2 * e] = h2f(bw[e] & 0xffffu);
+            vx[2 * e + 1] = h2f(bw[e] >> 16);
+        }
+        uint32_t kw[2], vw[2];
+        if (F == kFmtInt8) {
+            float kmn = kx[0], kmx = kx[0], vmn = vx[0], vmx = vx[0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) {
+                kmn = fminf(kmn, kx[e]);
+                kmx = fmaxf(kmx, kx[e]);
+                vmn = fminf(vmn, vx[e]);
+                vmx = fmaxf(vmx, vx[e]);
+            }
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) {
+                kmn = fminf(kmn, __shfl_xor(kmn, off));
+                kmx = fmaxf(kmx, __shfl_xor(kmx, off));
+                vmn = fminf(vmn, __shfl_xor(vmn, off));
+                vmx = fmaxf(vmx, __shfl_xor(vmx, off));
+            }
+            const QParams pk = make_qparams(kmn, kmx, 8);
+            const QParams pv = make_qparams(vmn, vmx, 8);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                kw[h] = vw[h] = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    kw[h] |= quant_code(kx[4 * h + e], pk.z, pk.inv, 255.0f) << (8 * e);
+                    vw[h] |= quant_code(vx[4 * h + e], pv.z, pv.inv, 255.0f) << (8 * e);
+                }
+            }
+            if (cg == 0) {
+                const int kp = tmeta_pos(L, L.kmeta_off, t), vp = tmeta_pos(L, L.vmeta_off, t);
+                *(uint16_t*)(rec + kp) = pk.s_bits;
+                *(uint16_t*)(rec + kp + 2 * SPT) = pk.z_bits;
+                *(uint16_t*)(rec + vp) = pv.s_bits;
+                *(uint16_t*)(rec + vp + 2 * SPT) = pv.z_bits;
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                kw[h] = fp8_code2(kx[4 * h], kx[4 * h + 1], kinv) | fp8_code2(kx[4 * h + 2], kx[4 * h + 3], kinv) << 16;
+                vw[h] = fp8_code2(vx[4 * h], vx[4 * h + 1], vinv) | fp8_code2(vx[4 * h + 2], vx[4 * h + 3], vinv) << 16;
+            }
+        }
+        *(uint2*)(rec + t * kD + 8 * cg) = make_uint2(kw[0], kw[1]);
+        *(uint2*)&sm.vcode[t][8 * cg] = make_uint2(vw[0], vw[1]);
+    }
+    __syncthreads();
+
+    // Value bytes, lane-major: lane l = 16g + n holds, at byte ct*SPT + slot
+    // of its SPT*8 bytes, the code of channel 16ct + n for the slot's token.
+    constexpr int WPL = SPT * 2;   // words per lane
+    for (int D = tid; D < 64 * WPL; D += 256) {
+        const int lane = D / WPL, wi = D % WPL;
+        const int g = lane >> 4, n = lane & 15;
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int q = wi * 4 + e;
+            const int ct = q / SPT, slot = q % SPT;
+            const int t = (slot >> 2) * 16 + 4 * g + (slot & 3);
+            w |= (uint32_t)sm.vcode[t][16 * ct + n] << (8 * e);
+        }
+        *(uint32_t*)(rec + L.vcode_off + lane * SPT * 8 + 4 * wi) = w;
+    }
+    __syncthreads();  // LDS may be reused by the caller
+}
+
+// Quantizes one group of the format F (kFmtKivi: key bits KB, value bits VB).
+template <int G, int KB, int VB, int F>
+__device__ __forceinline__ void quantize_any(QuantSmem<G>& sm, const Layout& L, const kvq_cache& c, int h,
+                                             const half_t* ksrc, const half_t* vsrc, uint8_t* rec) {
+    if (F == kFmtKivi) {
+        quantize_group<G, KB, VB>(sm, L, ksrc, vsrc, rec);
+    } else {
+        const float kinv = F == kFmtFp8 ? fp8_inv_scale(c.k_scale[h]) : 0.0f;
+        const float vinv = F == kFmtFp8 ? fp8_inv_scale(c.v_scale[h]) : 0.0f;
+        quantize_group8<G, F>(sm, L, ksrc, vsrc, rec, kinv, vinv);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Prefill: grid (ceil(max_len / G), B*H); one workgroup per (group, stream).
 // ---------------------------------------------------------------------------
@@ -164,7 +273,7 @@ __device__ __forceinline__ int clamped_len(const Layout& L, const int32_t* seq_l
     return n;
 }
 
-template <int G, int KB, int VB>
+template <int G, int KB, int VB, int F>
 __global__ __launch_bounds__(256) void prefill_groups_kernel(Layout L, kvq_cache c, const half_t* k,
                                                              const half_t* v, int max_len,
                                                              const int32_t* seq_lens) {
@@ -178,7 +287,7 @@ __global__ __launch_bounds__(256) void prefill_groups_kernel(Layout L, kvq_cache
     uint8_t* rec = record_at(L, c.packed, c.block_table, b, h, g);
     if (!rec) return;
     const long base = ((long)sh * max_len + (long)g * G) * kD;
-    quantize_group<G, KB, VB>(sm, L, k + base, v + base, rec);
+    quantize_any<G, KB, VB, F>(sm, L, c, h, k + base, v + base, rec);
 }
 
 // Residual copy and counters: grid (B*H), 256 threads.
@@ -209,7 +318,7 @@ __global__ __launch_bounds__(256) void prefill_tail_kernel(Layout L, kvq_cache c
 // Append one token per (sequence, head) and flush a full group: grid (B).
 // ---------------------------------------------------------------------------
 
-template <int G, int KB, int VB>
+template <int G, int KB, int VB, int F>
 __global__ __launch_bounds__(256) void append_kernel(Layout L, kvq_cache c, const half_t* knew,
                                                      const half_t* vnew) {
     __shared__ QuantSmem<G> sm;
@@ -236,8 +345,8 @@ __global__ __launch_bounds__(256) void append_kernel(Layout L, kvq_cache c, cons
             uint8_t* rec = record_at(L, c.packed, c.block_table, b, h, nq / G);
             if (rec) {
                 const long row = (sh * L.ring + (nq % L.ring)) * kD;
-                quantize_group<G, KB, VB>(sm, L, (const half_t*)c.k_res + row, (const half_t*)c.v_res + row,
-                                          rec);
+                quantize_any<G, KB, VB, F>(sm, L, c, h, (const half_t*)c.k_res + row,
+                                           (const half_t*)c.v_res + row, rec);
             } else {
                 flushed = false;
             }
@@ -272,8 +381,15 @@ __global__ __launch_bounds__(256) void dequantize_kernel(Layout L, kvq_cache c, 
         const int ch = c0 + i;
         float kv = 0.0f, vv = 0.0f;
         if (t < nq) {
-            if (rec) {
-                kv = fmaf((float)kcode_at(L, rec, tg, ch), h2f(kscale_bits(L, rec, ch)), h2f(kzero_bits(L, rec, ch)));
+            if (rec && L.fmt == kFmtFp8) {
+#pragma clang fp contract(off)
+                kv = fp8_value(kcode_at(L, rec, tg, ch)) * c.k_scale[h];
+                vv = fp8_value(vcode_at(L, rec, tg, ch)) * c.v_scale[h];
+            } else if (rec) {
+                const bool tok = L.fmt == kFmtInt8;   // per-token key scale and zero
+                kv = fmaf((float)kcode_at(L, rec, tg, ch),
+                          h2f(tok ? ktok_scale_bits(L, rec, tg) : kscale_bits(L, rec, ch)),
+                          h2f(tok ? ktok_zero_bits(L, rec, tg) : kzero_bits(L, rec, ch)));
                 vv = fmaf((float)vcode_at(L, rec, tg, ch), h2f(vscale_bits(L, rec, tg)), h2f(vzero_bits(L, rec, tg)));
             }
         } else if (t < n) {
@@ -302,7 +418,13 @@ __global__ __launch_bounds__(256) void export_kernel(Layout L, kvq_cache c, uint
         kc[e + i] = rec ? (uint8_t)kcode_at(L, rec, tg, c0 + i) : 0;
         vc[e + i] = rec ? (uint8_t)vcode_at(L, rec, tg, c0 + i) : 0;
     }
-    if (tg == 0) {  // key metadata row of this group
+    if (L.fmt == kFmtFp8) return;   // no scale/zero tables
+    if (L.fmt == kFmtInt8) {
+        if (c0 == 0) {
+            ks[(long)sh * out_tokens + t] = rec ? ktok_scale_bits(L, rec, tg) : 0;
+            kz[(long)sh * out_tokens + t] = rec ? ktok_zero_bits(L, rec, tg) : 0;
+        }
+    } else if (tg == 0) {  // key metadata row of this group
         const long gi = ((long)sh * (out_tokens / L.G) + t / L.G) * kD + c0;
         for (int i = 0; i < 8; ++i) {
             ks[gi + i] = rec ? kscale_bits(L, rec, c0 + i) : 0;
@@ -321,16 +443,19 @@ __global__ __launch_bounds__(256) void export_kernel(Layout L, kvq_cache c, uint
 
 #define KVQ_DISPATCH(L_, F)                                                    \
     do {                                                                       \
-        const int key_ = (L_).G * 100 + (L_).kbits * 10 + (L_).vbits;           \
-        switch (key_) {                                                        \
-            case 1622: F(16, 2, 2); break;                                     \
-            case 1624: F(16, 2, 4); break;                                     \
-            case 1642: F(16, 4, 2); break;                                     \
-            case 1644: F(16, 4, 4); break;                                     \
-            case 3222: F(32, 2, 2); break;                                     \
-            case 3224: F(32, 2, 4); break;                                     \
-            case 3242: F(32, 4, 2); break;                                     \
-            case 3244: F(32, 4, 4); break;                                     \
+        switch (layout_key(L_)) {                                              \
+            case 1622: F(16, 2, 2, kFmtKivi); break;                           \
+            case 1624: F(16, 2, 4, kFmtKivi); break;                           \
+            case 1642: F(16, 4, 2, kFmtKivi); break;                           \
+            case 1644: F(16, 4, 4, kFmtKivi); break;                           \
+            case 3222: F(32, 2, 2, kFmtKivi); break;                           \
+            case 3224: F(32, 2, 4, kFmtKivi); break;                           \
+            case 3242: F(32, 4, 2, kFmtKivi); break;                           \
+            case 3244: F(32, 4, 4, kFmtKivi); break;                           \
+            case 11688: F(16, 8, 8, kFmtInt8); break;                          \
+            case 13288: F(32, 8, 8, kFmtInt8); break;                          \
+            case 21688: F(16, 8, 8, kFmtFp8); break;                           \
+            case 23288: F(32, 8, 8, kFmtFp8); break;                           \
             default: return hipErrorInvalidValue;                              \
         }                                                                      \
     } while (0)
@@ -340,8 +465,9 @@ hipError_t launch_prefill(const Layout& L, const kvq_cache& c, const half_t* k, 
     const int ngroups = (max_len + L.G - 1) / L.G;
     if (ngroups > 0) {
         dim3 grid(ngroups, L.B * L.H);
-#define KVQ_PF(GG, KB, VB) \
-    hipLaunchKernelGGL((prefill_groups_kernel<GG, KB, VB>), grid, dim3(256), 0, s, L, c, k, v, max_len, seq_lens)
+#define KVQ_PF(GG, KB, VB, FF)                                                                               \
+    hipLaunchKernelGGL((prefill_groups_kernel<GG, KB, VB, FF>), grid, dim3(256), 0, s, L, c, k, v, max_len, \
+                       seq_lens)
         KVQ_DISPATCH(L, KVQ_PF);
 #undef KVQ_PF
         hipError_t e = hipGetLastError();
@@ -353,7 +479,8 @@ hipError_t launch_prefill(const Layout& L, const kvq_cache& c, const half_t* k, 
 
 hipError_t launch_append(const Layout& L, const kvq_cache& c, const half_t* k, const half_t* v,
                          hipStream_t s) {
-#define KVQ_AP(GG, KB, VB) hipLaunchKernelGGL((append_kernel<GG, KB, VB>), dim3(L.B), dim3(256), 0, s, L, c, k, v)
+#define KVQ_AP(GG, KB, VB, FF) \
+    hipLaunchKernelGGL((append_kernel<GG, KB, VB, FF>), dim3(L.B), dim3(256), 0, s, L, c, k, v)
     KVQ_DISPATCH(L, KVQ_AP);
 #undef KVQ_AP
     return hipGetLastError();

@@ -25,18 +25,20 @@ _lib = None
 
 KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ECAPACITY, KVQ_EHIP = range(5)
 HEAD_DIM = 128
+# cache formats (KVQ_FORMAT_*)
+FORMAT_KIVI, FORMAT_INT8, FORMAT_FP8_E4M3 = 0, 1, 2
 
 
 class kvq_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_seqs", "num_kv_heads", "head_dim", "k_bits", "v_bits", "group_size", "residual",
-        "max_tokens", "block_size", "num_blocks", "max_blocks_per_seq")]
+        "max_tokens", "block_size", "num_blocks", "max_blocks_per_seq", "kv_format")]
 
 
 class kvq_cache(ctypes.Structure):
     _fields_ = [("packed", ctypes.c_void_p), ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
                 ("n_tokens", ctypes.c_void_p), ("n_quant", ctypes.c_void_p),
-                ("block_table", ctypes.c_void_p)]
+                ("block_table", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
 class kvq_sizes(ctypes.Structure):
@@ -187,11 +189,13 @@ class CacheShape:
     paged: bool = False
     num_blocks: int = 0
     max_blocks_per_seq: int = 0
+    kv_format: int = FORMAT_KIVI
 
     def config(self) -> kvq_config:
         return kvq_config(self.num_seqs, self.num_kv_heads, HEAD_DIM, self.k_bits, self.v_bits,
                           self.group_size, self.residual, self.max_tokens if not self.paged else 0,
-                          self.group_size if self.paged else 0, self.num_blocks, self.max_blocks_per_seq)
+                          self.group_size if self.paged else 0, self.num_blocks, self.max_blocks_per_seq,
+                          self.kv_format)
 
 
 class QuantizedKVCache:
@@ -199,7 +203,9 @@ class QuantizedKVCache:
     token counts (used only to validate calls and size exports).  In paged
     mode a simple host free-list hands out blocks ahead of the device flushes."""
 
-    def __init__(self, shape: CacheShape, device="cuda"):
+    def __init__(self, shape: CacheShape, device="cuda", k_scale=None, v_scale=None):
+        """k_scale, v_scale: FP8 format only, the static per-kv-head scales
+        (float sequences or tensors of H positive values)."""
         self.shape = shape
         self.cfg = shape.config()
         self.sizes = kvq_buffer_sizes(self.cfg)
@@ -218,10 +224,22 @@ class QuantizedKVCache:
             self._block_order = list(range(shape.num_blocks - 1, -1, -1))  # pop() hands out 0, 1, 2, ...
             self._free = list(self._block_order)
         self.lens = np.zeros(shape.num_seqs, np.int64)
-        self.cache = kvq_cache(self.packed.data_ptr(), self.k_res.data_ptr(), self.v_res.data_ptr(),
-                               self.n_tokens.data_ptr(), self.n_quant.data_ptr(),
-                               self.block_table.data_ptr() if self.block_table is not None else None)
+        self.k_scale = self.v_scale = None
+        if shape.kv_format == FORMAT_FP8_E4M3:
+            if k_scale is None or v_scale is None:
+                raise ValueError("the FP8 format needs static k_scale and v_scale per kv head")
+            H = shape.num_kv_heads
+            self.k_scale = torch.as_tensor(k_scale, dtype=torch.float32).reshape(H).to(self.device).contiguous()
+            self.v_scale = torch.as_tensor(v_scale, dtype=torch.float32).reshape(H).to(self.device).contiguous()
+        self.cache = self._make_cache()
         self._ws = None
+
+    def _make_cache(self):
+        return kvq_cache(self.packed.data_ptr(), self.k_res.data_ptr(), self.v_res.data_ptr(),
+                         self.n_tokens.data_ptr(), self.n_quant.data_ptr(),
+                         self.block_table.data_ptr() if self.block_table is not None else None,
+                         self.k_scale.data_ptr() if self.k_scale is not None else None,
+                         self.v_scale.data_ptr() if self.v_scale is not None else None)
 
     def sequence_view(self, b: int) -> "QuantizedKVCache":
         """Read-only cache of sequence b alone, sharing this cache's memory.
@@ -252,9 +270,8 @@ class QuantizedKVCache:
         v.n_quant = self.n_quant[b:b + 1]
         v.block_table = self.block_table[b:b + 1] if self.block_table is not None else None
         v.lens = self.lens[b:b + 1].copy()
-        v.cache = kvq_cache(v.packed.data_ptr(), v.k_res.data_ptr(), v.v_res.data_ptr(),
-                            v.n_tokens.data_ptr(), v.n_quant.data_ptr(),
-                            v.block_table.data_ptr() if v.block_table is not None else None)
+        v.k_scale, v.v_scale = self.k_scale, self.v_scale
+        v.cache = v._make_cache()
         v._ws = None
         return v
 
@@ -351,10 +368,15 @@ class QuantizedKVCache:
         dev = self.device
         kc = torch.empty((B, H, T, HEAD_DIM), dtype=torch.uint8, device=dev)
         vc = torch.empty_like(kc)
-        ks = torch.empty((B, H, T // G, HEAD_DIM), dtype=torch.int16, device=dev)
-        kz = torch.empty_like(ks)
-        vs = torch.empty((B, H, T), dtype=torch.int16, device=dev)
-        vz = torch.empty_like(vs)
+        fmt = self.shape.kv_format
+        if fmt == FORMAT_FP8_E4M3:   # no scale/zero tables
+            ks = kz = vs = vz = None
+        else:
+            kshape = (B, H, T // G, HEAD_DIM) if fmt == FORMAT_KIVI else (B, H, T)
+            ks = torch.empty(kshape, dtype=torch.int16, device=dev)
+            kz = torch.empty_like(ks)
+            vs = torch.empty((B, H, T), dtype=torch.int16, device=dev)
+            vz = torch.empty_like(vs)
         kv_export_codes(self.cfg, self.cache, kc, vc, ks, kz, vs, vz, T, stream)
         return kc, vc, ks, kz, vs, vz
 

@@ -41,6 +41,7 @@ class Workload:
     v_outlier_frac: float = 0.01
     layers: int = 1              # layers folded into the sequence axis
     tag: int = 0                 # distinguishes seeds between workloads
+    kv_format: int = 0           # 0 low-bit KIVI, 1 INT8 per token, 2 FP8 E4M3 static
 
     @property
     def gq(self) -> int:
@@ -68,6 +69,26 @@ WORKLOADS = {
         "llama3_70b_cache_80l_128k_int2", num_seqs=80, num_q_heads=64, num_kv_heads=8, k_bits=2,
         v_bits=2, group_size=32, residual=128, context=131072, layers=80, tag=5),
 }
+
+# The 8-bit formats on the shape and data of the 8B-layer workload (same
+# seeds): "KV cache compression: ...", section 3.1.
+WORKLOADS_8BIT = {
+    "llama3_8b_layer_b8_32k_fp8": Workload(
+        "llama3_8b_layer_b8_32k_fp8", num_seqs=8, num_q_heads=32, num_kv_heads=8, k_bits=8,
+        v_bits=8, group_size=32, residual=128, context=32768, tag=2, kv_format=2),
+    "llama3_8b_layer_b8_32k_int8": Workload(
+        "llama3_8b_layer_b8_32k_int8", num_seqs=8, num_q_heads=32, num_kv_heads=8, k_bits=8,
+        v_bits=8, group_size=32, residual=128, context=32768, tag=2, kv_format=1),
+}
+
+
+def workload(name: str) -> Workload:
+    """A named workload of either table."""
+    if name in WORKLOADS:
+        return WORKLOADS[name]
+    if name in WORKLOADS_8BIT:
+        return WORKLOADS_8BIT[name]
+    raise KeyError("unknown workload %r (known: %s)" % (name, ", ".join(list(WORKLOADS) + list(WORKLOADS_8BIT))))
 
 
 def seed_for(tag: int, *parts: int) -> int:
@@ -161,6 +182,18 @@ def _outlier_gain(w: Workload, k_outlier: float) -> np.ndarray:
                 gain[b, h, outlier_channels(w, b // per_layer, h)] = k_outlier
         _GAIN_CACHE[key] = gain
     return _GAIN_CACHE[key]
+
+
+def calibrate_fp8_scales(K: torch.Tensor, V: torch.Tensor):
+    """Static FP8 scales for the inputs: per kv head, the largest |value| of
+    the given keys (values) over every sequence, token and channel, divided
+    by 448 so that it lands on the largest E4M3 value.  This stands in for an
+    offline calibration set ("KV compression and quantization", part B.3:
+    static scales are fixed beforehand from calibration data); K, V:
+    [S][H][L][d].  -> two float32 tensors [H] on K's device."""
+    ks = K.abs().amax(dim=(0, 2, 3)).float() / 448.0
+    vs = V.abs().amax(dim=(0, 2, 3)).float() / 448.0
+    return ks, vs
 
 
 def random_fp16(shape, seed: int, scale: float = 1.0) -> np.ndarray:

@@ -19,27 +19,34 @@ MIN_COS = 0.9999
 THREADS = min(16, os.cpu_count() or 1)
 
 
-def make_cache(w: synth.Workload, lens, max_tokens=None, num_blocks=None, shuffle_seed=None):
+def make_cache(w: synth.Workload, lens, max_tokens=None, num_blocks=None, shuffle_seed=None, scales=None):
+    """scales: FP8 format, the (k_scale, v_scale) pair of per-head tensors."""
     G, R = w.group_size, w.residual
     if w.paged:
         mb = max(1, (int(np.max(lens)) + 64 - R) // G + 1)
         nb = num_blocks if num_blocks is not None else int(sum(kvq.num_quantized(int(n) + 64, G, R) // G
                                                                for n in lens)) + 4
         shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, G, R, paged=True,
-                               num_blocks=nb, max_blocks_per_seq=mb)
+                               num_blocks=nb, max_blocks_per_seq=mb, kv_format=w.kv_format)
     else:
         shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, G, R,
-                               max_tokens=max_tokens if max_tokens is not None else int(np.max(lens)) + 64)
-    c = kvq.QuantizedKVCache(shape)
+                               max_tokens=max_tokens if max_tokens is not None else int(np.max(lens)) + 64,
+                               kv_format=w.kv_format)
+    ks, vs = scales if scales is not None else (None, None)
+    c = kvq.QuantizedKVCache(shape, k_scale=ks, v_scale=vs)
     if w.paged and shuffle_seed is not None:
         c.shuffle_free_blocks(shuffle_seed)
     return c
 
 
-def oracle_states(kb: np.ndarray, vb: np.ndarray, lens, w: synth.Workload, cap=None):
-    """kb, vb: uint16 [B][H][L][d] -> StreamState per (b, h)."""
+def oracle_states(kb: np.ndarray, vb: np.ndarray, lens, w: synth.Workload, cap=None, scales=None):
+    """kb, vb: uint16 [B][H][L][d] -> StreamState per (b, h).  scales: FP8
+    format, the per-head (k_scale, v_scale) tensors the cache was given."""
+    ks = vs = None
+    if scales is not None:
+        ks, vs = (t.detach().cpu().numpy().astype(np.float32) for t in scales)
     return oracle.prefill_batch(kb, vb, lens, w.k_bits, w.v_bits, w.group_size, w.residual,
-                                cap=cap, threads=THREADS)
+                                cap=cap, threads=THREADS, fmt=w.kv_format, kscales=ks, vscales=vs)
 
 
 def compare_codes(cache: kvq.QuantizedKVCache, states, streams=None):
@@ -56,8 +63,10 @@ def compare_codes(cache: kvq.QuantizedKVCache, states, streams=None):
     for b, heads in sorted(by_seq.items()):
         view = cache.sequence_view(b)
         T = int(view.lens.max()) + G     # a group past the end: must read back as zeros
-        kc, vc, ks, kz, vs, vz = [t[0].cpu().numpy() for t in view.export_codes(T)]
-        ks, kz, vs, vz = (a.view(np.uint16) for a in (ks, kz, vs, vz))
+        fmt = cache.shape.kv_format
+        kc, vc, ks, kz, vs, vz = [None if t is None else t[0].cpu().numpy() for t in view.export_codes(T)]
+        if fmt != kvq.FORMAT_FP8_E4M3:
+            ks, kz, vs, vz = (a.view(np.uint16) for a in (ks, kz, vs, vz))
         kd, vd = [t[0].cpu().numpy() for t in view.dequantize(T)]
         nt = int(view.n_tokens.cpu()[0])
         nqs = int(view.n_quant.cpu()[0])
@@ -67,12 +76,14 @@ def compare_codes(cache: kvq.QuantizedKVCache, states, streams=None):
             nq, n = st.nq, st.n
             assert np.array_equal(kc[h, :nq], st.key_codes()), ("key codes", b, h)
             assert np.array_equal(vc[h, :nq], st.value_codes()), ("value codes", b, h)
-            oks, okz = st.key_meta()
-            assert np.array_equal(ks[h, :nq // G], oks), ("key scales", b, h)
-            assert np.array_equal(kz[h, :nq // G], okz), ("key zeros", b, h)
-            ovs, ovz = st.value_meta()
-            assert np.array_equal(vs[h, :nq], ovs), ("value scales", b, h)
-            assert np.array_equal(vz[h, :nq], ovz), ("value zeros", b, h)
+            if fmt != kvq.FORMAT_FP8_E4M3:
+                nk = nq // G if fmt == kvq.FORMAT_KIVI else nq   # per group or per token
+                oks, okz = st.key_meta()
+                assert np.array_equal(ks[h, :nk], oks), ("key scales", b, h)
+                assert np.array_equal(kz[h, :nk], okz), ("key zeros", b, h)
+                ovs, ovz = st.value_meta()
+                assert np.array_equal(vs[h, :nq], ovs), ("value scales", b, h)
+                assert np.array_equal(vz[h, :nq], ovz), ("value zeros", b, h)
             okd, ovd = st.dequantize()
             assert np.array_equal(kd[h, :n], okd), ("dequantized keys", b, h)
             assert np.array_equal(vd[h, :n], ovd), ("dequantized values", b, h)

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 def _cfg(kvq, **kw):
     d = dict(num_seqs=2, num_kv_heads=3, head_dim=128, k_bits=4, v_bits=2, group_size=32, residual=64,
-             max_tokens=1000, block_size=0, num_blocks=0, max_blocks_per_seq=0)
+             max_tokens=1000, block_size=0, num_blocks=0, max_blocks_per_seq=0, kv_format=0)
     d.update(kw)
     return kvq.kvq_config(**d)
 
@@ -68,6 +68,71 @@ def test_buffer_sizes_match_oracle_bytes(orc, kb, vb, G, R, T):
     assert sz.residual_bytes == 3 * 2 * (R + G) * 128 * 2
     assert sz.counter_bytes == 3 * 4
     assert sz.block_table_bytes == 0
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("G,R,T", [(32, 128, 32768), (16, 0, 4000), (16, 16, 15)])
+def test_buffer_sizes_8bit_match_oracle_bytes(orc, fmt, G, R, T):
+    """8-bit formats: one record = one more quantized group in the oracle's
+    accounting (a byte per code; INT8 adds a per-token fp16 pair for keys
+    and for values; FP8 none)."""
+    kvq = _kvq()
+    cfg = _cfg(kvq, num_seqs=2, num_kv_heads=3, k_bits=8, v_bits=8, group_size=G, residual=R, max_tokens=T,
+               kv_format=fmt)
+    sz = kvq.kvq_buffer_sizes(cfg)
+    one_group = orc.stream_bytes(R + 2 * G, 128, 8, 8, G, R, fmt=fmt) - orc.stream_bytes(R + G, 128, 8, 8, G, R,
+                                                                                         fmt=fmt)
+    assert sz.record_bytes == one_group == G * 256 + (8 * G if fmt == 1 else 0)
+    groups = max(0, (T - R) // G)
+    assert sz.packed_bytes == 2 * 3 * groups * sz.record_bytes
+    assert sz.residual_slots == R + G
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kv_format=1, k_bits=4, v_bits=4), "KVQ_EINVAL"),     # 8-bit formats take 8-bit codes only
+    (dict(kv_format=2, k_bits=8, v_bits=4), "KVQ_EINVAL"),
+    (dict(kv_format=3, k_bits=8, v_bits=8), "KVQ_EINVAL"),     # unknown format
+    (dict(kv_format=-1), "KVQ_EINVAL"),
+    (dict(kv_format=0, k_bits=8, v_bits=8), "KVQ_EUNSUPPORTED"),
+    (dict(kv_format=1, k_bits=8, v_bits=8, group_size=64), "KVQ_EUNSUPPORTED"),
+])
+def test_format_validation(kw, status):
+    kvq = _kvq()
+    cfg = _cfg(kvq, **kw)
+    out = kvq.kvq_sizes()
+    assert kvq.lib().kvq_buffer_sizes(ctypes.byref(cfg), ctypes.byref(out)) == getattr(kvq, status)
+
+
+@pytest.mark.skipif("not _no_gpu()", reason="argument rejection is exercised only where no kernel can launch")
+def test_fp8_calls_need_static_scales():
+    kvq = _kvq()
+    L = kvq.lib()
+    cfg = _cfg(kvq, k_bits=8, v_bits=8, kv_format=2)
+    good = 0x10000
+    vp = ctypes.c_void_p
+    by = ctypes.byref
+    no_scales = kvq.kvq_cache(good, good, good, good, good, None, None, None)
+    one_scale = kvq.kvq_cache(good, good, good, good, good, None, good, None)
+    odd = kvq.kvq_cache(good, good, good, good, good, None, good, good + 2)
+    for c in (no_scales, one_scale, odd):
+        assert L.kv_quantize_prefill(by(cfg), by(c), vp(good), vp(good), 10, vp(good), None) == kvq.KVQ_EINVAL
+        assert L.kv_append_token(by(cfg), by(c), vp(good), vp(good), None) == kvq.KVQ_EINVAL
+        assert L.kv_dequantize(by(cfg), by(c), vp(good), vp(good), 4, None) == kvq.KVQ_EINVAL
+    # export: FP8 writes no scale/zero tables, so they may be null; INT8 needs them
+    c8 = kvq.kvq_cache(good, good, good, good, good, None, None, None)
+    icfg = _cfg(kvq, k_bits=8, v_bits=8, kv_format=1)
+    assert L.kv_export_codes(by(icfg), by(c8), vp(good), vp(good), None, None, None, None, 32, None) == \
+        kvq.KVQ_EINVAL
+
+
+def test_fp8_cache_needs_scales_on_host():
+    kvq = _kvq()
+    shape = kvq.CacheShape(2, 3, 8, 8, 32, 64, max_tokens=300, kv_format=kvq.FORMAT_FP8_E4M3)
+    with pytest.raises(ValueError):
+        kvq.QuantizedKVCache(shape, device="cpu")
+    c = kvq.QuantizedKVCache(shape, device="cpu", k_scale=[0.1, 0.2, 0.3], v_scale=[1.0, 2.0, 3.0])
+    assert c.cache.k_scale == c.k_scale.data_ptr() and c.cache.v_scale == c.v_scale.data_ptr()
+    assert c.sequence_view(1).cache.k_scale == c.cache.k_scale
 
 
 def test_paged_sizes():
