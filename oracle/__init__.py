@@ -96,6 +96,10 @@ def lib():
                 [ctypes.c_float] * 2 + [_u8p, _u16p, _u16p, _u8p, _u16p, _u16p, _f32p, _f32p]
             L.orc_stream_bytes8.restype = ctypes.c_double
             L.orc_stream_bytes8.argtypes = [ctypes.c_int, ctypes.c_long] + [ctypes.c_int] * 3
+            L.orc_rope_rotate.argtypes = [_f32p, ctypes.c_int, ctypes.c_int, ctypes.c_long, ctypes.c_double,
+                                          _f64p]
+            L.orc_attention_d.argtypes = [_f32p, ctypes.c_int, _f64p, _f32p, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_float, _f64p]
             L.orc_stream_bytes.restype = ctypes.c_double
             L.orc_stream_bytes.argtypes = [ctypes.c_long] + [ctypes.c_int] * 5
             L.orc_kv_bytes_closed_form.restype = ctypes.c_double
@@ -312,6 +316,33 @@ def attention(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, scale: float,
     return out
 
 
+def rope_rotate(k: np.ndarray, base: float, pos0: int = 0) -> np.ndarray:
+    """k: float32 [n][d] keys at positions pos0.. -> fp64 rotated keys."""
+    k = np.ascontiguousarray(k, np.float32)
+    n, d = k.shape
+    out = np.empty((max(n, 1), d), np.float64)
+    if n:
+        lib().orc_rope_rotate(_p(k, _f32p), n, d, int(pos0), float(base), _p(out, _f64p))
+    return out[:n]
+
+
+def attention_rope(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, scale: float, base: float):
+    """Attention over pre-RoPE keys k_hat (float32 [n][d], token t at
+    position t) rotated on read: softmax(q . RoPE_t(k_t) * scale) v."""
+    q = np.ascontiguousarray(q, np.float32)
+    vh = np.ascontiguousarray(v_hat, np.float32)
+    gq, d = q.shape
+    n = k_hat.shape[0]
+    kr = rope_rotate(k_hat, base) if n else np.zeros((1, d))
+    if n == 0:
+        vh = np.zeros((1, d), np.float32)
+    kr = np.ascontiguousarray(kr, np.float64)
+    out = np.empty((gq, d), np.float64)
+    lib().orc_attention_d(_p(q, _f32p), gq, _p(kr, _f64p), _p(vh, _f32p), n, d, ctypes.c_float(scale),
+                          _p(out, _f64p))
+    return out
+
+
 def stream_bytes(n, d, kbits, vbits, G, R, fmt=FMT_KIVI) -> float:
     if fmt != FMT_KIVI:
         return float(lib().orc_stream_bytes8(fmt, int(n), d, G, R))
@@ -351,9 +382,10 @@ def prefill_batch(k_bits, v_bits, seq_lens, kbits, vbits, G, R, cap=None, thread
     return [[res[b * H + h] for h in range(H)] for b in range(B)]
 
 
-def decode_attention_batch(q_f32, states, scale, threads=1):
+def decode_attention_batch(q_f32, states, scale, threads=1, rope_base=0.0):
     """q_f32: float32 [B][Hq][d]; states from prefill_batch -> float64 [B][Hq][d].
-    Query head h reads kv head h // (Hq / H)."""
+    Query head h reads kv head h // (Hq / H).  rope_base > 0: the cached keys
+    are pre-RoPE and are rotated on read (attention_rope)."""
     B, Hq, d = q_f32.shape
     H = len(states[0])
     gq = Hq // H
@@ -362,7 +394,9 @@ def decode_attention_batch(q_f32, states, scale, threads=1):
     def one(bh):
         b, h = bh
         kh, vh = states[b][h].dequantize()
-        out[b, h * gq:(h + 1) * gq] = attention(q_f32[b, h * gq:(h + 1) * gq], kh, vh, scale)
+        qs = q_f32[b, h * gq:(h + 1) * gq]
+        out[b, h * gq:(h + 1) * gq] = attention_rope(qs, kh, vh, scale, rope_base) if rope_base > 0 \
+            else attention(qs, kh, vh, scale)
 
     jobs = [(b, h) for b in range(B) for h in range(H)]
     if threads > 1:

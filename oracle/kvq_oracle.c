@@ -21,6 +21,10 @@
  *       nearest line, zero = starting point of the grid).
  *  [P1] section 3.1: 8-bit KV (FP8 E4M3 with a static per-tensor or per-head
  *       scale, or INT8 with a dynamic per-token scale) as the first 2x.
+ *  [P1] section 3.3 (KVQuant: quantize keys before RoPE, apply RoPE when
+ *       reading) and section 2 (RoPE rotates pairs of dimensions, keeping
+ *       each pair's norm).
+ *  [P3] experiment 03: RoPE treats two adjacent dimensions as one plane.
  *  [P2] "KV compression and quantization", part B.1 (FP8 E4M3/E5M2 and INT8
  *       at 0.5x the fp16 bytes).
  *  [P4] "KV cache compression" (jaedaily), formula paragraph: per-channel key
@@ -443,6 +447,66 @@ void orc_fp8_decode_array(const uint8_t *c, float *f, long count)
 void orc_fp8_encode_array(const float *f, uint8_t *c, long count)
 {
     for (long i = 0; i < count; ++i) c[i] = orc_fp8_e4m3_encode(f[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Pre-RoPE keys ([P1] section 3.3: quantize the keys before the rotary      */
+/* position embedding, whose rotation makes an outlier channel's values vary */
+/* from token to token and widens the per-channel ranges, and apply RoPE to  */
+/* the keys when they are read; [P1] section 2: RoPE rotates each pair of     */
+/* dimensions and keeps the pair's norm; [P3] exp. 03: the two dimensions of */
+/* a pair are adjacent).  Token t's pair i = (2i, 2i+1) is rotated by the    */
+/* angle t * theta_i, theta_i = base^(-2i/d), counter-clockwise:             */
+/*   k'[2i]   = k[2i] cos(a) - k[2i+1] sin(a)                                 */
+/*   k'[2i+1] = k[2i] sin(a) + k[2i+1] cos(a)                                 */
+/* (the rotary embedding's own definition), all in fp64.                     */
+/* ------------------------------------------------------------------------ */
+
+/* Rotates rows [0, n) of k (fp32, [n][d]) as tokens at positions
+ * pos0 .. pos0 + n - 1 into out (fp64 [n][d]). */
+void orc_rope_rotate(const float *k, int n, int d, long pos0, double base, double *out)
+{
+    for (int t = 0; t < n; ++t) {
+        for (int i = 0; i < d / 2; ++i) {
+            double theta = pow(base, -2.0 * (double)i / (double)d);
+            double a = (double)(pos0 + t) * theta;
+            double c = cos(a), s = sin(a);
+            double x0 = (double)k[(long)t * d + 2 * i];
+            double x1 = (double)k[(long)t * d + 2 * i + 1];
+            out[(long)t * d + 2 * i] = x0 * c - x1 * s;
+            out[(long)t * d + 2 * i + 1] = x0 * s + x1 * c;
+        }
+    }
+}
+
+/* orc_attention with fp64 keys (e.g. keys rotated by orc_rope_rotate). */
+void orc_attention_d(const float *q, int gq, const double *kh, const float *vh, int n, int d,
+                     float scale, double *out)
+{
+    double *logit = (double *)malloc(sizeof(double) * (n > 0 ? n : 1));
+    for (int h = 0; h < gq; ++h) {
+        double *o = out + (long)h * d;
+        for (int c = 0; c < d; ++c) o[c] = 0.0;
+        if (n == 0) continue;
+        double m = -INFINITY;
+        for (int t = 0; t < n; ++t) {
+            double acc = 0.0;
+            for (int c = 0; c < d; ++c)
+                acc += (double)q[(long)h * d + c] * kh[(long)t * d + c];
+            logit[t] = (double)scale * acc;
+            if (logit[t] > m) m = logit[t];
+        }
+        double l = 0.0;
+        for (int t = 0; t < n; ++t) {
+            logit[t] = exp(logit[t] - m);
+            l += logit[t];
+        }
+        for (int t = 0; t < n; ++t) {
+            double p = logit[t] / l;
+            for (int c = 0; c < d; ++c) o[c] += p * (double)vh[(long)t * d + c];
+        }
+    }
+    free(logit);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -627,6 +627,110 @@ def test_8bit_bytes_golden(orc):
 
 
 # --------------------------------------------------------------------------
+# Pre-RoPE keys rotated on read ("KV cache compression: ...", section 3.3:
+# quantize keys before RoPE, apply RoPE when reading; section 2: RoPE rotates
+# pairs of dimensions and keeps each pair's norm; "KV Cache compression lab",
+# experiment 03: the pair is two adjacent dimensions).  The rotation is
+# checked against complex multiplication by exp(i t theta_i), a formulation
+# of its own, and against the properties that define RoPE.
+# --------------------------------------------------------------------------
+
+def _rope_complex(k, base, pos0=0):
+    """Independent formulation: pair (2i, 2i+1) as the complex number
+    k[2i] + i k[2i+1], multiplied by exp(i t base^(-i/64)) (d = 128)."""
+    n, d = k.shape
+    z = k[:, 0::2].astype(np.float64) + 1j * k[:, 1::2].astype(np.float64)
+    freq = np.power(float(base), -np.arange(d // 2) / (d / 2))
+    t = (pos0 + np.arange(n))[:, None].astype(np.float64)
+    r = z * np.exp(1j * t * freq[None, :])
+    out = np.empty((n, d))
+    out[:, 0::2], out[:, 1::2] = r.real, r.imag
+    return out
+
+
+@pytest.mark.parametrize("base", [10000.0, 500000.0])
+def test_rope_unit_pairs_closed_form(orc, base):
+    for i in (0, 1, 17, 32, 63):
+        for pos in (0, 1, 5, 1000, 131071):
+            th = base ** (-i / 64.0)
+            for which, want in ((0, (np.cos(pos * th), np.sin(pos * th))), (1, (-np.sin(pos * th), np.cos(pos * th)))):
+                k = np.zeros((1, 128), np.float32)
+                k[0, 2 * i + which] = 1.0
+                r = orc.rope_rotate(k, base, pos0=pos)[0]
+                assert abs(r[2 * i] - want[0]) < 1e-12 and abs(r[2 * i + 1] - want[1]) < 1e-12
+                r[2 * i: 2 * i + 2] = 0
+                assert not r.any()
+
+
+def test_rope_matches_complex_rotation_norms_and_identity(orc):
+    rng = np.random.default_rng(90)
+    k = (rng.standard_normal((300, 128)) * 3).astype(np.float32)
+    for base, pos0 in ((10000.0, 0), (500000.0, 77777)):
+        r = orc.rope_rotate(k, base, pos0=pos0)
+        assert np.allclose(r, _rope_complex(k, base, pos0), rtol=0, atol=1e-9)
+        kk = k.astype(np.float64)
+        assert np.allclose(r[:, 0::2] ** 2 + r[:, 1::2] ** 2, kk[:, 0::2] ** 2 + kk[:, 1::2] ** 2, atol=1e-9)
+    assert np.array_equal(orc.rope_rotate(k[:1], 10000.0, pos0=0)[0], k[0].astype(np.float64))
+
+
+def test_rope_relative_position(orc):
+    """RoPE(q, m) . RoPE(k, n) depends on m - n only."""
+    rng = np.random.default_rng(91)
+    q = rng.standard_normal((1, 128)).astype(np.float32)
+    k = rng.standard_normal((1, 128)).astype(np.float32)
+    for m, n in ((10, 3), (5000, 4993), (131000, 130993)):
+        a = orc.rope_rotate(q, 500000.0, m)[0] @ orc.rope_rotate(k, 500000.0, n)[0]
+        b = orc.rope_rotate(q, 500000.0, m - n)[0] @ k[0].astype(np.float64)
+        assert abs(a - b) < 1e-8 * (1 + abs(b))
+
+
+def test_attention_rope_matches_rotated_keys(orc):
+    """Attention over pre-RoPE keys rotated on read equals plain fp64
+    attention over keys rotated beforehand (complex formulation), with
+    positions 0 .. n-1."""
+    rng = np.random.default_rng(92)
+    n, gq = 70, 3
+    q = rng.standard_normal((gq, 128)).astype(np.float32)
+    k = (rng.standard_normal((n, 128)) * 2).astype(np.float32)
+    v = rng.standard_normal((n, 128)).astype(np.float32)
+    got = orc.attention_rope(q, k, v, 128 ** -0.5, 500000.0)
+    kr = _rope_complex(k, 500000.0)
+    lg = (q.astype(np.float64) @ kr.T) * np.float64(np.float32(128 ** -0.5))
+    p = np.exp(lg - lg.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    assert np.allclose(got, p @ v.astype(np.float64), rtol=0, atol=1e-12)
+
+
+def test_pre_rope_quantization_narrows_key_ranges(orc):
+    """Section 3.3's reason for quantizing before RoPE: on keys whose outlier
+    channels are consistently large (the "bright vertical lines" of
+    experiment 03), per-channel 2-bit quantization of the pre-RoPE keys,
+    rotated afterwards, errs less than quantizing the rotated keys."""
+    rng = np.random.default_rng(93)
+    n, G, base = 32 * 32, 32, 10000.0
+    k = rng.standard_normal((n, 128))
+    for c in (4, 9, 70, 101):                         # fixed outlier channels, same sign every token
+        k[:, c] = 20.0 + rng.standard_normal(n)
+    k16 = k.astype(np.float16)
+    kf = k16.astype(np.float32)
+    exact = orc.rope_rotate(kf, base)
+
+    def quant_groups(x16):
+        out = np.zeros(x16.shape, np.float64)
+        xb = x16.view(np.uint16)
+        for g in range(n // G):
+            c, s, z = orc.quantize_key_group(xb[g * G:(g + 1) * G], 2)
+            out[g * G:(g + 1) * G] = c * orc.h2f(s)[None, :].astype(np.float64) + orc.h2f(z)[None, :]
+        return out
+
+    pre = orc.rope_rotate(quant_groups(k16).astype(np.float32), base)
+    post = quant_groups(exact.astype(np.float16))
+    err_pre = np.mean((pre - exact) ** 2)
+    err_post = np.mean((post - exact) ** 2)
+    assert err_pre < 0.5 * err_post, (err_pre, err_post)
+
+
+# --------------------------------------------------------------------------
 # Mutation check: planted mistakes in a copy of the oracle must be caught
 # --------------------------------------------------------------------------
 
@@ -648,6 +752,11 @@ MUTATIONS = [
     ("out_k[i] = orc_fp8_e4m3_decode(kcodes[i]) * kscale;",
      "out_k[i] = orc_fp8_e4m3_decode(kcodes[i]);", "fp8grid"),          # scale not applied
     ("quantize_set(x, d, 1, 8, codes, 1, s, z);", "quantize_set(x, d, 1, 7, codes, 1, s, z);", "int8grid"),
+    ("out[(long)t * d + 2 * i] = x0 * c - x1 * s;", "out[(long)t * d + 2 * i] = x0 * c + x1 * s;",
+     "rope"),                                                           # rotation sign
+    ("double theta = pow(base, -2.0 * (double)i / (double)d);",
+     "double theta = pow(base, -1.0 * (double)i / (double)d);", "rope"),  # wrong frequencies
+    ("double a = (double)(pos0 + t) * theta;", "double a = (double)(pos0 + t + 1) * theta;", "rope"),  # positions from 1
 ]
 
 
@@ -666,6 +775,7 @@ def test_pin_catches_planted_mistakes(tmp_path):
         "fp8dec": "test_fp8_decode_every_code",
         "fp8grid": "test_fp8_grid_aligned_exact",
         "int8grid": "test_int8_per_token_grid_aligned",
+        "rope": "test_rope_unit_pairs_closed_form",
     }
     for i, (old, new, which) in enumerate(MUTATIONS):
         assert old in src, old
