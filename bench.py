@@ -213,7 +213,10 @@ def cpu_baseline(w, K, V, q, lens, budget_s, scales=None):
                                         vscale=float(vsc[h]) if vsc is not None else 0.0)
         t1 = time.perf_counter()
         kh, vh = st.dequantize()
-        oracle.attention(qf[b, h * gq:(h + 1) * gq], kh, vh, scale)
+        if w.rope_theta > 0:
+            oracle.attention_rope(qf[b, h * gq:(h + 1) * gq], kh, vh, scale, w.rope_theta)
+        else:
+            oracle.attention(qf[b, h * gq:(h + 1) * gq], kh, vh, scale)
         t2 = time.perf_counter()
         return t1 - t0, t2 - t1
 
@@ -308,10 +311,11 @@ def main():
         mb = (L + grow - R) // G + 1
         nb = int(sum(n_quant(int(n) + grow, G, R) // G for n in lens)) + 8
         shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, G, R, paged=True,
-                               num_blocks=nb, max_blocks_per_seq=mb, kv_format=w.kv_format)
+                               num_blocks=nb, max_blocks_per_seq=mb, kv_format=w.kv_format,
+                               rope_theta=w.rope_theta)
     else:
         shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, w.group_size, w.residual,
-                               max_tokens=L + total_steps + 8, kv_format=w.kv_format)
+                               max_tokens=L + total_steps + 8, kv_format=w.kv_format, rope_theta=w.rope_theta)
     ks, vs = scales if scales is not None else (None, None)
     caches = [kvq.QuantizedKVCache(shape, device=dev, k_scale=ks, v_scale=vs) for _ in range(copies)]
     if w.paged:
@@ -418,6 +422,7 @@ def main():
             "num_kv_heads": w.num_kv_heads, "head_dim": 128, "k_bits": w.k_bits, "v_bits": w.v_bits,
             "group_size": w.group_size, "residual": w.residual, "cache_copies_rotated": copies,
             "kv_format": ["kivi", "int8", "fp8_e4m3"][w.kv_format],
+            "rope_on_read_theta": w.rope_theta,
             "paged": w.paged, "layers": w.layers, "min_context": int(lens.min()),
             "tokens": int(lens.sum()),
         },

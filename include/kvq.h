@@ -16,6 +16,9 @@
  *  - "KV cache compression" (jaedaily), formula paragraph: the per-channel
  *    key and per-token value dequantization q*s + z, and attention
  *    softmax(q k^T / sqrt(d_h)).
+ *  - "KV cache compression: ...", section 3.3 (KVQuant): keys quantized
+ *    before the rotary position embedding, which is applied by the attention
+ *    kernel when it reads them; section 2: RoPE rotates pairs of dimensions.
  *  - "KV cache compression: ...", section 3.1, and "KV compression and
  *    quantization", part B.1: 8-bit caches at half the fp16 bytes, either
  *    FP8 E4M3 under a static per-head scale or INT8 under a dynamic
@@ -37,6 +40,11 @@
  *   Attention: out[b][h] = sum_t softmax_t(scale * q[b][h] . k_t) v_t over all
  *   n tokens (dequantized part and fp16 residual), query head h reading kv
  *   head h / (Hq / H).  n = 0 gives out = 0.
+ *   Pre-RoPE keys (rope_theta > 0): the cache holds keys before the rotary
+ *   embedding and attention uses RoPE_t(k_t) in place of k_t, pair
+ *   (2i, 2i+1) of token t (0-based position in its sequence) rotated by the
+ *   angle t * rope_theta^(-2i/128): (k0 cos - k1 sin, k0 sin + k1 cos).  The
+ *   query is passed already rotated to its own position, as usual.
  *
  * Conventions for every call below:
  *   - Pointers named *_host are host memory; every other data pointer is a
@@ -96,6 +104,9 @@ typedef struct kvq_config {
     int32_t num_blocks;         /* paged: blocks in the pool                     */
     int32_t max_blocks_per_seq; /* paged: length of one block-table row          */
     int32_t kv_format;          /* KVQ_FORMAT_*                                  */
+    float rope_theta;           /* 0: keys used as given.  > 0: keys are stored
+                                   before RoPE and rotated on read with this base
+                                   (10000, 500000, ...); low-bit format only     */
 } kvq_config;
 
 /* Device buffers of one cache.  Sizes come from kvq_buffer_sizes(). */

@@ -32,6 +32,9 @@ kvq_status make_layout(const kvq_config* cfg, Layout* L) {
     if (G != 16 && G != 32) return KVQ_EUNSUPPORTED;
     if (cfg->residual < 0 || cfg->residual % G != 0) return KVQ_EINVAL;
     if (cfg->residual > (1 << 20)) return KVQ_EINVAL;
+    if (!(cfg->rope_theta >= 0.0f) || cfg->rope_theta > 1e30f) return KVQ_EINVAL;   // also rejects NaN
+    if (cfg->rope_theta > 0.0f && (cfg->kv_format != kFmtKivi || cfg->rope_theta <= 1.0f)) return KVQ_EUNSUPPORTED;
+    L->rope_theta = cfg->rope_theta;
     L->fmt = cfg->kv_format;
     L->B = cfg->num_seqs;
     L->H = cfg->num_kv_heads;

@@ -375,11 +375,107 @@ __device__ __forceinline__ T lds_read(const lds_u8* p) {
     return *(const __attribute__((address_space(3))) T*)p;
 }
 
+// ---------------------------------------------------------------------------
+// Pre-RoPE keys rotated on read ("KV cache compression: ...", section 3.3:
+// KVQuant quantizes keys before the rotary embedding and applies it when
+// reading; section 2: RoPE rotates pairs of dimensions).  Pair i = (2i, 2i+1)
+// of token t turns by t * theta_i, theta_i = base^(-i/64).  The rotation
+// depends on the token, so it cannot be folded into the query operand: each
+// dequantized key element is rotated in fp32, split exactly into fp16 high
+// and low parts, and both parts go through the key product with the plain
+// fp16 query (its dequantization included: k = code * s + z per channel).
+//
+// Angles: phi_i = theta_i / 2pi turns per token as a 0.64 fixed-point
+// fraction, so t * phi_i mod 1 is an exact integer product at any position;
+// the (cos, sin) of a unit's first token comes from sincospi of that, those
+// of its tokens t0 + r from a per-workgroup table of (cos, sin)(r theta_i),
+// r <= 16, by the angle-addition formula.
+// ---------------------------------------------------------------------------
+constexpr int kFmtRope = 3;       // low-bit format with pre-RoPE keys (attention instantiations only)
+constexpr int kTabPitch = 66;     // float2 per table row: rows of lanes n = 0..15 hit distinct banks
+typedef float f2 __attribute__((ext_vector_type(2)));
+
+struct RopeLds {
+    uint64_t phi[64];                 // turns per token of pair i, 0.64 fixed point
+    f2 tab[17][kTabPitch];            // (cos, sin)(r theta_i), r = 0..16
+    f2 base[kWaves][2][64];           // per wave: (cos, sin) at the unit's tokens t0 and t0 + 16
+};
+
+// (sin, cos) of the angle a / 2^64 turns (the top 32 bits, signed: |turns| <= 1/2).
+__device__ __forceinline__ void turns_sincos(uint64_t a, float* s, float* c) {
+    const int hi = (int)(uint32_t)(a >> 32);
+    sincospif((float)hi * 0x1p-31f, s, c);
+}
+
+// Workgroup prologue: phi and the table.  All threads.
+__device__ void rope_setup(RopeLds& R, float theta, int tid) {
+    if (tid < 64) {
+        const double th = pow((double)theta, -(double)tid / 64.0);
+        R.phi[tid] = (uint64_t)(th * (18446744073709551616.0 / 6.283185307179586476925));
+    }
+    __syncthreads();
+    for (int e = tid; e < 17 * 64; e += 256) {
+        const int r = e >> 6, i = e & 63;
+        float sn, cs;
+        turns_sincos((uint64_t)r * R.phi[i], &sn, &cs);
+        R.tab[r][i] = f2{cs, sn};
+    }
+    __syncthreads();
+}
+
+// The wave's (cos, sin) at tokens t0 and t0 + 16 for every pair (lane = pair).
+__device__ __forceinline__ void rope_unit_base(RopeLds* R, int wave, int lane, int t0) {
+    float sn, cs;
+    turns_sincos((uint64_t)(uint32_t)t0 * R->phi[lane], &sn, &cs);
+    const f2 t16 = R->tab[16][lane];
+    R->base[wave][0][lane] = f2{cs, sn};
+    R->base[wave][1][lane] = f2{cs * t16[0] - sn * t16[1], sn * t16[0] + cs * t16[1]};
+    wave_sync();
+}
+
+// Key logits of row tile rt (token t0 + 16rt + n of lane (g, n)) against the
+// lane's column head: getx(j, x) gives the pre-RoPE key values x[0..7] of
+// channels 32g + 8j .. + 7 (pairs i = 16g + 4j + p).
+template <typename GetX>
+__device__ __forceinline__ f4 rope_key_tile(const RopeLds* R, int wave, int rt, int lane, const QOps& Q, GetX getx) {
+    const int g = lane >> 4, n = lane & 15;
+    f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float x[8];
+        getx(j, x);
+        const int i0 = 16 * g + 4 * j;
+        const f4 bs[2] = {*(const __attribute__((address_space(3))) f4*)&R->base[wave][rt][i0],
+                          *(const __attribute__((address_space(3))) f4*)&R->base[wave][rt][i0 + 2]};
+        const f4 ts[2] = {*(const __attribute__((address_space(3))) f4*)&R->tab[n][i0],
+                          *(const __attribute__((address_space(3))) f4*)&R->tab[n][i0 + 2]};
+        h8 hi, lo;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const f4 b = bs[p >> 1], t = ts[p >> 1];
+            const int o = 2 * (p & 1);
+            const float C = b[o] * t[o] - b[o + 1] * t[o + 1];
+            const float S = b[o + 1] * t[o] + b[o] * t[o + 1];
+            const float k0 = C * x[2 * p] - S * x[2 * p + 1];
+            const float k1 = S * x[2 * p] + C * x[2 * p + 1];
+            const _Float16 h0 = (_Float16)k0, h1 = (_Float16)k1;
+            hi[2 * p] = h0;
+            hi[2 * p + 1] = h1;
+            lo[2 * p] = (_Float16)(k0 - (float)h0);
+            lo[2 * p + 1] = (_Float16)(k1 - (float)h1);
+        }
+        acc = mfma(hi, Q.q[j], acc);
+        acc = mfma(lo, Q.q[j], acc);
+    }
+    return acc;
+}
+
 // One staged unit (see Stage): key logits on the matrix cores, then the
-// online-softmax step and the value product.
-template <int G, int KB, int VB, bool LP>
+// online-softmax step and the value product.  RP: pre-RoPE keys (R, wave:
+// the rotation tables; t0: the unit's first token).
+template <int G, int KB, int VB, bool LP, bool RP>
 __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, WaveAcc& A, const QOps& Q, float sl2,
-                                             int lane) {
+                                             int lane, RopeLds* R, int wave, int t0) {
     using S = Stage<G, KB, VB>;
     constexpr int SPT = S::SPT;
     const int g = lane >> 4, n = lane & 15;
@@ -389,6 +485,29 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
     // high-limb columns only), then add codes . (q s) with q s split exactly
     // into fp16 high and low parts (LP: the part of the lane's column).
     f4 C[2];
+    if constexpr (RP) {
+        // pre-RoPE: dequantize, rotate, split, contract with the plain query
+        rope_unit_base(R, wave, lane, t0);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const lds_u8* km = buf + S::META + (S::NR == 2 ? rt : 0) * S::MREC;
+            uint32_t kc[KB];
+            if (KB == 4) {
+                const u32x4 x = lds_read<u32x4>(buf + S::KC + rt * 1024 + 16 * lane);
+                kc[0] = x[0]; kc[1] = x[1]; kc[2] = x[2]; kc[3] = x[3];
+            } else {
+                const u32x2 x = lds_read<u32x2>(buf + S::KC + rt * 512 + 16 * ((g >> 1) * 16 + n) + 8 * (g & 1));
+                kc[0] = x[0]; kc[1] = x[1];
+            }
+            C[rt] = rope_key_tile(R, wave, rt, lane, Q, [&](int j, float* x) {
+                const h8 a = codes8<KB>(kc, j);
+                const h8 sj = __builtin_bit_cast(h8, lds_read<u32x4>(km + 16 * (4 * g + j)));
+                const h8 zj = __builtin_bit_cast(h8, lds_read<u32x4>(km + 256 + 16 * (4 * g + j)));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = fmaf((float)a[e], (float)sj[e], (float)zj[e]);
+            });
+        }
+    } else {
 #pragma unroll
     for (int i = 0; i < S::NR; ++i) {
         const lds_u8* km = buf + S::META + i * S::MREC;
@@ -437,6 +556,7 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
             C[rt] = acc;
         }
     }
+    }
 
     // value codes of this lane (per record)
     uint32_t vc[S::NR][S::VW];
@@ -471,7 +591,8 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
         for (int i = 0; i < 4; ++i) {
             const int k = 4 * rt + i;
             const int slot = S::NR == 2 ? i : k;
-            x[k] = LP ? add_limb_partner(C[rt][i]) : C[rt][i];
+            // (pre-RoPE: both limb columns hold the same head's full logit)
+            x[k] = LP && !RP ? add_limb_partner(C[rt][i]) : C[rt][i];
             vs[k] = h2f(lds_read<uint16_t>(vm + 2 * slot));
             vz[k] = h2f(lds_read<uint16_t>(vm + 2 * (SPT + slot)));
             valid[k] = S::NR == 1 || ((has >> rec) & 1);
@@ -617,10 +738,10 @@ __device__ __forceinline__ int ring_slot(int slot0, int r, int ring) {
 // high-limb columns carry it, the low-limb columns add zero).  The value rows
 // go straight to LDS (rows 0-15 to sva, 16-31 to svb, 256 bytes each; rows at
 // or past n read as zeros), from where each lane gathers its operand columns.
-template <bool LP>
+template <bool LP, bool RP>
 __device__ __forceinline__ void process_residual(WaveAcc& A, const Layout& L, const kvq_cache& c, long sh, int t0,
                                                  int n, const QOps& Q, float sl2, int lane, lds_u8* sva,
-                                                 lds_u8* svb) {
+                                                 lds_u8* svb, RopeLds* R, int wave) {
     const int g = lane >> 4, n16 = lane & 15;
     const int slot0 = t0 % L.ring;
     {
@@ -636,25 +757,36 @@ __device__ __forceinline__ void process_residual(WaveAcc& A, const Layout& L, co
     }
     const half_t* kr = (const half_t*)c.k_res + sh * L.ring * kD;
     f4 C[2];
+    if constexpr (RP) rope_unit_base(R, wave, lane, t0);
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
         const int r = 16 * rt + n16;
         f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
         const uint32_t keep = t0 + r < n ? 0xffffffffu : 0u;
         const uint4* row = (const uint4*)(kr + (long)(t0 + r < n ? ring_slot(slot0, r, L.ring) : slot0) * kD + 32 * g);
+        if constexpr (RP) {
+            C[rt] = rope_key_tile(R, wave, rt, lane, Q, [&](int j, float* x) {
+                uint4 w = row[j];
+                w.x &= keep; w.y &= keep; w.z &= keep; w.w &= keep;
+                const h8 k8 = words_h8(w);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint4 w = row[j];
-            w.x &= keep; w.y &= keep; w.z &= keep; w.w &= keep;
-            acc = mfma(words_h8(w), Q.q[j], acc);
+                for (int e = 0; e < 8; ++e) x[e] = (float)k8[e];
+            });
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint4 w = row[j];
+                w.x &= keep; w.y &= keep; w.z &= keep; w.w &= keep;
+                acc = mfma(words_h8(w), Q.q[j], acc);
+            }
+            C[rt] = LP && (lane & 8) ? f4{0.0f, 0.0f, 0.0f, 0.0f} : acc;
         }
-        C[rt] = LP && (lane & 8) ? f4{0.0f, 0.0f, 0.0f, 0.0f} : acc;
     }
     float x[8], vs[8], vz[8];
     bool valid[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        x[k] = LP ? add_limb_partner(C[k >> 2][k & 3]) : C[k >> 2][k & 3];
+        x[k] = LP && !RP ? add_limb_partner(C[k >> 2][k & 3]) : C[k >> 2][k & 3];
         vs[k] = 1.0f;
         vz[k] = 0.0f;
         valid[k] = t0 + (k >> 2) * 16 + 4 * g + (k & 3) < n;
@@ -720,19 +852,20 @@ __device__ __forceinline__ int unit_at(const SeqUnits& u, int x) {
 
 // Stage layout, unit issue and unit processing of a format.
 template <int G, int KB, int VB, int F>
-using StageT = typename std::conditional<F == kFmtKivi, Stage<G, KB, VB>, Stage8<G, F>>::type;
+using StageT = typename std::conditional<F == kFmtKivi || F == kFmtRope, Stage<G, KB, VB>, Stage8<G, F>>::type;
 
 template <int G, int KB, int VB, int F, bool PG>
 __device__ __forceinline__ uint32_t issue_any(lds_u8* buf, const Layout& L, const kvq_cache& c, int b, int h,
                                               int unit, int ngroups, int lane) {
-    if constexpr (F == kFmtKivi) return issue_unit<G, KB, VB, PG>(buf, L, c, b, h, unit, ngroups, lane);
+    if constexpr (F == kFmtKivi || F == kFmtRope) return issue_unit<G, KB, VB, PG>(buf, L, c, b, h, unit, ngroups, lane);
     else return issue_unit8<G, F, PG>(buf, L, c, b, h, unit, ngroups, lane);
 }
 
 template <int G, int KB, int VB, int F, bool LP>
 __device__ __forceinline__ void process_any(const lds_u8* buf, uint32_t has, WaveAcc& A, const QOps& Q, float sl2,
-                                            float qsum, float vscl, int lane) {
-    if constexpr (F == kFmtKivi) process_unit<G, KB, VB, LP>(buf, has, A, Q, sl2, lane);
+                                            float qsum, float vscl, int lane, RopeLds* R, int wave, int t0) {
+    if constexpr (F == kFmtKivi || F == kFmtRope)
+        process_unit<G, KB, VB, LP, F == kFmtRope>(buf, has, A, Q, sl2, lane, R, wave, t0);
     else process_unit8<G, F, LP>(buf, has, A, Q, sl2, qsum, vscl, lane);
 }
 
@@ -745,7 +878,7 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
                                                float (*wpz)[16], const Layout& L, const kvq_cache& c,
                                                const half_t* __restrict__ q, float sl2, int gq, int b, int h,
                                                const SeqUnits& su, int lo, int hi, float* __restrict__ part,
-                                               int lane, int wave) {
+                                               int lane, int wave, RopeLds* R) {
     using S = StageT<G, KB, VB, F>;
     // The lane index, produced afresh: per-lane addresses derived from it are
     // formed here, once per segment, instead of being hoisted out of the
@@ -806,7 +939,7 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
                 }
                 wave_sync();
                 set_progress_prio((q1 - u + kWaves - 1) / kWaves, ntot);
-                process_any<G, KB, VB, F, LP>(sa, ha, A, Q, sl2q, qsum, vscl, lane);
+                process_any<G, KB, VB, F, LP>(sa, ha, A, Q, sl2q, qsum, vscl, lane, R, wave, 32 * u);
                 u += kWaves;
                 if (u >= q1) break;
                 if (u + kWaves < q1) {
@@ -818,7 +951,7 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
                 }
                 wave_sync();
                 set_progress_prio((q1 - u + kWaves - 1) / kWaves, ntot);
-                process_any<G, KB, VB, F, LP>(sb, hb, A, Q, sl2q, qsum, vscl, lane);
+                process_any<G, KB, VB, F, LP>(sb, hb, A, Q, sl2q, qsum, vscl, lane, R, wave, 32 * u);
                 u += kWaves;
                 if (u >= q1) break;
             }
@@ -826,8 +959,9 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
     }
     for (int u = lo + wave; u < hi; u += kWaves)
         if (u >= su.uq)
-            process_residual<LP>(A, L, c, sh, su.nq + 32 * (u - su.uq), su.n, Q, sl2, lane,
-                                 (lds_u8*)(stage_a + wave * S::PITCH), (lds_u8*)(stage_b + wave * S::PITCH));
+            process_residual<LP, F == kFmtRope>(A, L, c, sh, su.nq + 32 * (u - su.uq), su.n, Q, sl2, lane,
+                                                (lds_u8*)(stage_a + wave * S::PITCH),
+                                                (lds_u8*)(stage_b + wave * S::PITCH), R, wave);
     __builtin_amdgcn_s_setprio(0);
 
     // Wave results -> LDS: totals over the lane groups, accumulators by head.
@@ -895,6 +1029,7 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
 // than INT2 ones.  (Three waves lose little where the kernel waits on HBM.)
 // The 8-bit formats stage twice the bytes per unit: their LDS allows two
 // workgroups per CU, two waves per SIMD.
+// Pre-RoPE keys take registers for the rotation: two waves as well.
 constexpr int attn_waves(int G, int KB, int VB, int F, bool LP, bool PG) {
     return F != kFmtKivi ? 2 : LP && VB == 2 && !(G == 16 && KB == 2) ? 4 : 3;
 }
@@ -916,6 +1051,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
+    RopeLds* R = nullptr;
+    if constexpr (F == kFmtRope) {
+        __shared__ __attribute__((aligned(16))) RopeLds rope_lds;
+        rope_setup(rope_lds, L.rope_theta, tid);
+        R = &rope_lds;
+    }
 
     // Units per sequence, prefix over the batch (each thread a run of
     // consecutive sequences, then a scan over the threads).  Flattened
@@ -979,7 +1120,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves(
         }
         attend_segment<G, KB, VB, F, LP, PG>(stage_a, stage_b, wm, wl, wpz, L, c, q, sl2, gq, b, h, su,
                                           unit_at(su, lo), unit_at(su, hi), ws + ((long)w + s) * gq * kPart,
-                                          lane, wave);
+                                          lane, wave, R);
         if (ps + hi >= end) break;
         // next stream that has work (x < end <= T guarantees one)
         ps += su.cost;
@@ -1162,9 +1303,15 @@ static int attn_slots_for() {
 // fp16 parts of q*s and p*s share one 16-column product.
 static inline bool limb_packed(int gq) { return gq <= 8; }
 
+// Instantiation key of the attention kernels: as layout_key, with the low-bit
+// format's pre-RoPE variant as format kFmtRope.
+static inline int attn_key(const Layout& L) {
+    return layout_key(L) + (L.rope_theta > 0.0f ? (kFmtRope - L.fmt) * 10000 : 0);
+}
+
 template <bool LP, bool PG>
 static int attn_slots_lp(const Layout& L) {
-    switch (layout_key(L)) {
+    switch (attn_key(L)) {
         case 1622: return attn_slots_for<16, 2, 2, kFmtKivi, LP, PG>();
         case 1624: return attn_slots_for<16, 2, 4, kFmtKivi, LP, PG>();
         case 1642: return attn_slots_for<16, 4, 2, kFmtKivi, LP, PG>();
@@ -1176,6 +1323,14 @@ static int attn_slots_lp(const Layout& L) {
         case 13288: return attn_slots_for<32, 8, 8, kFmtInt8, LP, PG>();
         case 21688: return attn_slots_for<16, 8, 8, kFmtFp8, LP, PG>();
         case 23288: return attn_slots_for<32, 8, 8, kFmtFp8, LP, PG>();
+        case 31622: return attn_slots_for<16, 2, 2, kFmtRope, LP, PG>();
+        case 31624: return attn_slots_for<16, 2, 4, kFmtRope, LP, PG>();
+        case 31642: return attn_slots_for<16, 4, 2, kFmtRope, LP, PG>();
+        case 31644: return attn_slots_for<16, 4, 4, kFmtRope, LP, PG>();
+        case 33222: return attn_slots_for<32, 2, 2, kFmtRope, LP, PG>();
+        case 33224: return attn_slots_for<32, 2, 4, kFmtRope, LP, PG>();
+        case 33242: return attn_slots_for<32, 4, 2, kFmtRope, LP, PG>();
+        case 33244: return attn_slots_for<32, 4, 4, kFmtRope, LP, PG>();
         default: return attn_slots_for<32, 4, 4, kFmtKivi, LP, PG>();
     }
 }
@@ -1228,7 +1383,7 @@ hipError_t launch_attention_partials(const Layout& L, const AttnPlan& P, const k
     } else {                                  \
         KVQ_ATT2(GG, KB, VB, FF, false);      \
     }
-    switch (layout_key(L)) {
+    switch (attn_key(L)) {
         case 1622: KVQ_ATT(16, 2, 2, kFmtKivi); break;
         case 1624: KVQ_ATT(16, 2, 4, kFmtKivi); break;
         case 1642: KVQ_ATT(16, 4, 2, kFmtKivi); break;
@@ -1241,6 +1396,14 @@ hipError_t launch_attention_partials(const Layout& L, const AttnPlan& P, const k
         case 13288: KVQ_ATT(32, 8, 8, kFmtInt8); break;
         case 21688: KVQ_ATT(16, 8, 8, kFmtFp8); break;
         case 23288: KVQ_ATT(32, 8, 8, kFmtFp8); break;
+        case 31622: KVQ_ATT(16, 2, 2, kFmtRope); break;
+        case 31624: KVQ_ATT(16, 2, 4, kFmtRope); break;
+        case 31642: KVQ_ATT(16, 4, 2, kFmtRope); break;
+        case 31644: KVQ_ATT(16, 4, 4, kFmtRope); break;
+        case 33222: KVQ_ATT(32, 2, 2, kFmtRope); break;
+        case 33224: KVQ_ATT(32, 2, 4, kFmtRope); break;
+        case 33242: KVQ_ATT(32, 4, 2, kFmtRope); break;
+        case 33244: KVQ_ATT(32, 4, 4, kFmtRope); break;
         default: return hipErrorInvalidValue;
     }
 #undef KVQ_ATT

@@ -57,6 +57,7 @@ constexpr int kFmtFp8 = KVQ_FORMAT_FP8_E4M3;
 
 struct Layout {
     int fmt;
+    float rope_theta;                             // > 0: keys are pre-RoPE, rotated on read
     int B, H, kbits, vbits, G, R, ring;
     int paged, num_blocks, max_blocks, groups;   // groups: record slots per sequence
     int capacity;                                 // max tokens a sequence may hold

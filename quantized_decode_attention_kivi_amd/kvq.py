@@ -32,7 +32,8 @@ FORMAT_KIVI, FORMAT_INT8, FORMAT_FP8_E4M3 = 0, 1, 2
 class kvq_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_seqs", "num_kv_heads", "head_dim", "k_bits", "v_bits", "group_size", "residual",
-        "max_tokens", "block_size", "num_blocks", "max_blocks_per_seq", "kv_format")]
+        "max_tokens", "block_size", "num_blocks", "max_blocks_per_seq", "kv_format")] + \
+        [("rope_theta", ctypes.c_float)]
 
 
 class kvq_cache(ctypes.Structure):
@@ -190,12 +191,13 @@ class CacheShape:
     num_blocks: int = 0
     max_blocks_per_seq: int = 0
     kv_format: int = FORMAT_KIVI
+    rope_theta: float = 0.0      # > 0: keys are pre-RoPE, rotated on read with this base
 
     def config(self) -> kvq_config:
         return kvq_config(self.num_seqs, self.num_kv_heads, HEAD_DIM, self.k_bits, self.v_bits,
                           self.group_size, self.residual, self.max_tokens if not self.paged else 0,
                           self.group_size if self.paged else 0, self.num_blocks, self.max_blocks_per_seq,
-                          self.kv_format)
+                          self.kv_format, self.rope_theta)
 
 
 class QuantizedKVCache:

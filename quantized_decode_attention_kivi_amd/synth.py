@@ -42,6 +42,7 @@ class Workload:
     layers: int = 1              # layers folded into the sequence axis
     tag: int = 0                 # distinguishes seeds between workloads
     kv_format: int = 0           # 0 low-bit KIVI, 1 INT8 per token, 2 FP8 E4M3 static
+    rope_theta: float = 0.0      # > 0: the keys are pre-RoPE (rotated on read with this base)
 
     @property
     def gq(self) -> int:
@@ -82,13 +83,26 @@ WORKLOADS_8BIT = {
 }
 
 
+# Pre-RoPE keys rotated on read ("KV cache compression: ...", section 3.3) on
+# the 8B-layer and 70B-layer shapes and data (same seeds); base 500000 (the
+# Llama-3 family's).  The generated keys are taken as the pre-RoPE keys.
+WORKLOADS_ROPE = {
+    "llama3_8b_layer_b8_32k_int4_prerope": Workload(
+        "llama3_8b_layer_b8_32k_int4_prerope", num_seqs=8, num_q_heads=32, num_kv_heads=8, k_bits=4,
+        v_bits=4, group_size=32, residual=128, context=32768, tag=2, rope_theta=500000.0),
+    "llama3_70b_layer_b1_128k_int2_prerope": Workload(
+        "llama3_70b_layer_b1_128k_int2_prerope", num_seqs=1, num_q_heads=64, num_kv_heads=8, k_bits=2,
+        v_bits=2, group_size=32, residual=128, context=131072, tag=3, rope_theta=500000.0),
+}
+
+
 def workload(name: str) -> Workload:
-    """A named workload of either table."""
-    if name in WORKLOADS:
-        return WORKLOADS[name]
-    if name in WORKLOADS_8BIT:
-        return WORKLOADS_8BIT[name]
-    raise KeyError("unknown workload %r (known: %s)" % (name, ", ".join(list(WORKLOADS) + list(WORKLOADS_8BIT))))
+    """A named workload of any table."""
+    for table in (WORKLOADS, WORKLOADS_8BIT, WORKLOADS_ROPE):
+        if name in table:
+            return table[name]
+    raise KeyError("unknown workload %r (known: %s)" % (
+        name, ", ".join(list(WORKLOADS) + list(WORKLOADS_8BIT) + list(WORKLOADS_ROPE))))
 
 
 def seed_for(tag: int, *parts: int) -> int:

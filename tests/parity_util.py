@@ -20,18 +20,20 @@ THREADS = min(16, os.cpu_count() or 1)
 
 
 def make_cache(w: synth.Workload, lens, max_tokens=None, num_blocks=None, shuffle_seed=None, scales=None):
-    """scales: FP8 format, the (k_scale, v_scale) pair of per-head tensors."""
+    """scales: FP8 format, the (k_scale, v_scale) pair of per-head tensors.
+    w.rope_theta > 0: the keys are pre-RoPE and attention rotates them."""
     G, R = w.group_size, w.residual
     if w.paged:
         mb = max(1, (int(np.max(lens)) + 64 - R) // G + 1)
         nb = num_blocks if num_blocks is not None else int(sum(kvq.num_quantized(int(n) + 64, G, R) // G
                                                                for n in lens)) + 4
         shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, G, R, paged=True,
-                               num_blocks=nb, max_blocks_per_seq=mb, kv_format=w.kv_format)
+                               num_blocks=nb, max_blocks_per_seq=mb, kv_format=w.kv_format,
+                               rope_theta=w.rope_theta)
     else:
         shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, G, R,
                                max_tokens=max_tokens if max_tokens is not None else int(np.max(lens)) + 64,
-                               kv_format=w.kv_format)
+                               kv_format=w.kv_format, rope_theta=w.rope_theta)
     ks, vs = scales if scales is not None else (None, None)
     c = kvq.QuantizedKVCache(shape, k_scale=ks, v_scale=vs)
     if w.paged and shuffle_seed is not None:
@@ -90,16 +92,17 @@ def compare_codes(cache: kvq.QuantizedKVCache, states, streams=None):
             assert np.all(kd[h, n:] == 0) and np.all(vd[h, n:] == 0)
 
 
-def oracle_attention(q16: np.ndarray, states, scale, rows=None):
+def oracle_attention(q16: np.ndarray, states, scale, rows=None, rope_base=0.0):
     """q16: uint16 fp16 bits [B][Hq][d] -> fp64 [B][Hq][d] (rows: list of
-    (b, hq) to compute, others NaN)."""
+    (b, hq) to compute, others NaN).  rope_base > 0: pre-RoPE keys rotated on
+    read."""
     qf = oracle.h2f(q16)
     B, Hq, d = qf.shape
     H = len(states[0])
     gq = Hq // H
     out = np.full((B, Hq, d), np.nan)
     if rows is None:
-        return oracle.decode_attention_batch(qf, states, scale, threads=THREADS)
+        return oracle.decode_attention_batch(qf, states, scale, threads=THREADS, rope_base=rope_base)
     from concurrent.futures import ThreadPoolExecutor
     by_stream = {}
     for b, hq in rows:
@@ -108,7 +111,8 @@ def oracle_attention(q16: np.ndarray, states, scale, rows=None):
     def one(item):
         (b, h), hqs = item
         kh, vh = states[b][h].dequantize()
-        o = oracle.attention(qf[b, hqs], kh, vh, scale)
+        o = oracle.attention_rope(qf[b, hqs], kh, vh, scale, rope_base) if rope_base > 0 \
+            else oracle.attention(qf[b, hqs], kh, vh, scale)
         for i, hq in enumerate(hqs):
             out[b, hq] = o[i]
 
