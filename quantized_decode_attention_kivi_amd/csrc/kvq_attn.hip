@@ -433,41 +433,50 @@ __device__ __forceinline__ void rope_unit_base(RopeLds* R, int wave, int lane, i
     wave_sync();
 }
 
-// Key logits of row tile rt (token t0 + 16rt + n of lane (g, n)) against the
-// lane's column head: getx(j, x) gives the pre-RoPE key values x[0..7] of
-// channels 32g + 8j .. + 7 (pairs i = 16g + 4j + p).
+// Key logits of both row tiles (token t0 + 16rt + n of lane (g, n), rt = 0, 1)
+// against the lane's column head: getx(rt, j, x) gives the pre-RoPE key
+// values x[0..7] of channels 32g + 8j .. + 7 (pairs i = 16g + 4j + p).  The
+// lane's table entries (row n) are read once for both tiles.
 template <typename GetX>
-__device__ __forceinline__ f4 rope_key_tile(const RopeLds* R, int wave, int rt, int lane, const QOps& Q, GetX getx) {
+__device__ __forceinline__ void rope_key_tiles(const RopeLds* R, int wave, int lane, const QOps& Q, f4 (&C)[2],
+                                               GetX getx) {
     const int g = lane >> 4, n = lane & 15;
-    f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    C[0] = C[1] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    // -1, opaque: keeps lo = fma(hi, -1, k) one mixed-precision fma with an
+    // fp16 result instead of being rewritten as a conversion and a subtraction
+    float m1 = -1.0f;
+    asm volatile("" : "+v"(m1));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        float x[8];
-        getx(j, x);
         const int i0 = 16 * g + 4 * j;
-        const f4 bs[2] = {*(const __attribute__((address_space(3))) f4*)&R->base[wave][rt][i0],
-                          *(const __attribute__((address_space(3))) f4*)&R->base[wave][rt][i0 + 2]};
         const f4 ts[2] = {*(const __attribute__((address_space(3))) f4*)&R->tab[n][i0],
                           *(const __attribute__((address_space(3))) f4*)&R->tab[n][i0 + 2]};
-        h8 hi, lo;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const f4 b = bs[p >> 1], t = ts[p >> 1];
-            const int o = 2 * (p & 1);
-            const float C = b[o] * t[o] - b[o + 1] * t[o + 1];
-            const float S = b[o + 1] * t[o] + b[o] * t[o + 1];
-            const float k0 = C * x[2 * p] - S * x[2 * p + 1];
-            const float k1 = S * x[2 * p] + C * x[2 * p + 1];
-            const _Float16 h0 = (_Float16)k0, h1 = (_Float16)k1;
-            hi[2 * p] = h0;
-            hi[2 * p + 1] = h1;
-            lo[2 * p] = (_Float16)(k0 - (float)h0);
-            lo[2 * p + 1] = (_Float16)(k1 - (float)h1);
+        for (int rt = 0; rt < 2; ++rt) {
+            float x[8];
+            getx(rt, j, x);
+            const f4 bs[2] = {*(const __attribute__((address_space(3))) f4*)&R->base[wave][rt][i0],
+                              *(const __attribute__((address_space(3))) f4*)&R->base[wave][rt][i0 + 2]};
+            h8 hi, lo;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const f4 b = bs[p >> 1], t = ts[p >> 1];
+                const int o = 2 * (p & 1);
+                const float Cs = b[o] * t[o] - b[o + 1] * t[o + 1];
+                const float Sn = b[o + 1] * t[o] + b[o] * t[o + 1];
+                const float k0 = Cs * x[2 * p] - Sn * x[2 * p + 1];
+                const float k1 = Sn * x[2 * p] + Cs * x[2 * p + 1];
+                const _Float16 h0 = (_Float16)k0, h1 = (_Float16)k1;
+                hi[2 * p] = h0;
+                hi[2 * p + 1] = h1;
+                // k - hi is exact in fp32: one mixed-precision fma per element
+                lo[2 * p] = (_Float16)__builtin_fmaf((float)h0, m1, k0);
+                lo[2 * p + 1] = (_Float16)__builtin_fmaf((float)h1, m1, k1);
+            }
+            C[rt] = mfma(hi, Q.q[j], C[rt]);
+            C[rt] = mfma(lo, Q.q[j], C[rt]);
         }
-        acc = mfma(hi, Q.q[j], acc);
-        acc = mfma(lo, Q.q[j], acc);
     }
-    return acc;
 }
 
 // One staged unit (see Stage): key logits on the matrix cores, then the
@@ -488,25 +497,27 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
     if constexpr (RP) {
         // pre-RoPE: dequantize, rotate, split, contract with the plain query
         rope_unit_base(R, wave, lane, t0);
+        uint32_t kc[2][KB];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            const lds_u8* km = buf + S::META + (S::NR == 2 ? rt : 0) * S::MREC;
-            uint32_t kc[KB];
             if (KB == 4) {
                 const u32x4 x = lds_read<u32x4>(buf + S::KC + rt * 1024 + 16 * lane);
-                kc[0] = x[0]; kc[1] = x[1]; kc[2] = x[2]; kc[3] = x[3];
+                kc[rt][0] = x[0]; kc[rt][1] = x[1]; kc[rt][2] = x[2]; kc[rt][3] = x[3];
             } else {
                 const u32x2 x = lds_read<u32x2>(buf + S::KC + rt * 512 + 16 * ((g >> 1) * 16 + n) + 8 * (g & 1));
-                kc[0] = x[0]; kc[1] = x[1];
+                kc[rt][0] = x[0]; kc[rt][1] = x[1];
             }
-            C[rt] = rope_key_tile(R, wave, rt, lane, Q, [&](int j, float* x) {
-                const h8 a = codes8<KB>(kc, j);
-                const h8 sj = __builtin_bit_cast(h8, lds_read<u32x4>(km + 16 * (4 * g + j)));
-                const h8 zj = __builtin_bit_cast(h8, lds_read<u32x4>(km + 256 + 16 * (4 * g + j)));
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = fmaf((float)a[e], (float)sj[e], (float)zj[e]);
-            });
         }
+        rope_key_tiles(R, wave, lane, Q, C, [&](int rt, int j, float* x) {
+            // the record's channel scales and zeros (one record for both
+            // tiles when G = 32, record rt when G = 16)
+            const lds_u8* km = buf + S::META + (S::NR == 2 ? rt : 0) * S::MREC;
+            const h8 a = codes8<KB>(kc[rt], j);
+            const h8 sj = __builtin_bit_cast(h8, lds_read<u32x4>(km + 16 * (4 * g + j)));
+            const h8 zj = __builtin_bit_cast(h8, lds_read<u32x4>(km + 256 + 16 * (4 * g + j)));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = fmaf((float)a[e], (float)sj[e], (float)zj[e]);
+        });
     } else {
 #pragma unroll
     for (int i = 0; i < S::NR; ++i) {
@@ -757,7 +768,20 @@ __device__ __forceinline__ void process_residual(WaveAcc& A, const Layout& L, co
     }
     const half_t* kr = (const half_t*)c.k_res + sh * L.ring * kD;
     f4 C[2];
-    if constexpr (RP) rope_unit_base(R, wave, lane, t0);
+    if constexpr (RP) {
+        rope_unit_base(R, wave, lane, t0);
+        rope_key_tiles(R, wave, lane, Q, C, [&](int rt, int j, float* x) {
+            const int r = 16 * rt + n16;
+            const uint32_t keep = t0 + r < n ? 0xffffffffu : 0u;
+            const uint4* row =
+                (const uint4*)(kr + (long)(t0 + r < n ? ring_slot(slot0, r, L.ring) : slot0) * kD + 32 * g);
+            uint4 w = row[j];
+            w.x &= keep; w.y &= keep; w.z &= keep; w.w &= keep;
+            const h8 k8 = words_h8(w);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = (float)k8[e];
+        });
+    }
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
         const int r = 16 * rt + n16;
@@ -765,13 +789,6 @@ __device__ __forceinline__ void process_residual(WaveAcc& A, const Layout& L, co
         const uint32_t keep = t0 + r < n ? 0xffffffffu : 0u;
         const uint4* row = (const uint4*)(kr + (long)(t0 + r < n ? ring_slot(slot0, r, L.ring) : slot0) * kD + 32 * g);
         if constexpr (RP) {
-            C[rt] = rope_key_tile(R, wave, rt, lane, Q, [&](int j, float* x) {
-                uint4 w = row[j];
-                w.x &= keep; w.y &= keep; w.z &= keep; w.w &= keep;
-                const h8 k8 = words_h8(w);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = (float)k8[e];
-            });
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -1029,9 +1046,9 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
 // than INT2 ones.  (Three waves lose little where the kernel waits on HBM.)
 // The 8-bit formats stage twice the bytes per unit: their LDS allows two
 // workgroups per CU, two waves per SIMD.
-// Pre-RoPE keys take registers for the rotation: two waves as well.
+// Pre-RoPE keys take registers for the rotation: three waves.
 constexpr int attn_waves(int G, int KB, int VB, int F, bool LP, bool PG) {
-    return F != kFmtKivi ? 2 : LP && VB == 2 && !(G == 16 && KB == 2) ? 4 : 3;
+    return F == kFmtRope ? 3 : F != kFmtKivi ? 2 : LP && VB == 2 && !(G == 16 && KB == 2) ? 4 : 3;
 }
 
 template <int G, int KB, int VB, int F, bool LP, bool PG>
