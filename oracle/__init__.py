@@ -100,6 +100,19 @@ def lib():
                                           _f64p]
             L.orc_attention_d.argtypes = [_f32p, ctypes.c_int, _f64p, _f32p, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_float, _f64p]
+            L.orc_codebook_scale.restype = ctypes.c_int
+            L.orc_codebook_scale.argtypes = [ctypes.c_int]
+            L.orc_codebook_levels.argtypes = [ctypes.c_int, _f64p]
+            L.orc_quantize_key_group_cb.argtypes = [_u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p,
+                                                    _u8p, _u16p, _u16p]
+            L.orc_quantize_value_token_cb.argtypes = [_u16p, ctypes.c_int, ctypes.c_int, _f64p,
+                                                      _u8p, _u16p, _u16p]
+            L.orc_prefill_stream_cb.restype = ctypes.c_int
+            L.orc_prefill_stream_cb.argtypes = L.orc_prefill_stream.argtypes
+            L.orc_append_stream_cb.restype = ctypes.c_int
+            L.orc_append_stream_cb.argtypes = L.orc_append_stream.argtypes
+            L.orc_dequantize_stream_cb.argtypes = [_u16p, _u16p] + [ctypes.c_int] * 6 + \
+                [_u8p, _u16p, _u16p, _u8p, _u16p, _u16p, _f32p, _f32p]
             L.orc_stream_bytes.restype = ctypes.c_double
             L.orc_stream_bytes.argtypes = [ctypes.c_long] + [ctypes.c_int] * 5
             L.orc_kv_bytes_closed_form.restype = ctypes.c_double
@@ -150,6 +163,38 @@ def fp8_encode(x: np.ndarray) -> np.ndarray:
 
 # cache formats: the low-bit KIVI format, and the two 8-bit formats
 FMT_KIVI, FMT_INT8, FMT_FP8 = 0, 1, 2
+# level grids of the low-bit format: uniform, normal-quantile codebook
+GRID_UNIFORM, GRID_CODEBOOK = 0, 1
+
+
+def codebook_levels(bits: int) -> np.ndarray:
+    """Levels L_0..L_Q of the b-bit normal-quantile codebook, in grid steps."""
+    out = np.empty(1 << bits, np.float64)
+    lib().orc_codebook_levels(int(bits), _p(out, _f64p))
+    return out
+
+
+def quantize_key_group_cb(x_bits: np.ndarray, bits: int, levels=None):
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    G, d = x.shape
+    lev = np.ascontiguousarray(codebook_levels(bits) if levels is None else levels, np.float64)
+    codes = np.empty((G, d), np.uint8)
+    s = np.empty(d, np.uint16)
+    z = np.empty(d, np.uint16)
+    lib().orc_quantize_key_group_cb(_p(x, _u16p), G, d, bits, _p(lev, _f64p), _p(codes, _u8p), _p(s, _u16p),
+                                    _p(z, _u16p))
+    return codes, s, z
+
+
+def quantize_value_token_cb(x_bits: np.ndarray, bits: int, levels=None):
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    lev = np.ascontiguousarray(codebook_levels(bits) if levels is None else levels, np.float64)
+    codes = np.empty(x.shape[0], np.uint8)
+    s = np.empty(1, np.uint16)
+    z = np.empty(1, np.uint16)
+    lib().orc_quantize_value_token_cb(_p(x, _u16p), x.shape[0], bits, _p(lev, _f64p), _p(codes, _u8p),
+                                      _p(s, _u16p), _p(z, _u16p))
+    return codes, int(s[0]), int(z[0])
 
 def num_quantized(n: int, G: int, R: int) -> int:
     return int(lib().orc_num_quantized(int(n), int(G), int(R)))
@@ -195,9 +240,10 @@ class StreamState:
     scale/zero per token.  FMT_FP8: E4M3 codes under the static scales
     kscale / vscale of the stream's kv head, no per-token metadata."""
 
-    def __init__(self, d, kbits, vbits, G, R, cap, fmt=FMT_KIVI, kscale=0.0, vscale=0.0):
+    def __init__(self, d, kbits, vbits, G, R, cap, fmt=FMT_KIVI, kscale=0.0, vscale=0.0, grid=GRID_UNIFORM):
         self.d, self.kbits, self.vbits, self.G, self.R, self.cap = d, kbits, vbits, G, R, cap
         self.fmt, self.kscale, self.vscale = fmt, float(kscale), float(vscale)
+        self.grid = grid
         self.n = 0
         self.nq = 0
         self.hist_k = np.zeros((cap, d), np.uint16)
@@ -219,14 +265,18 @@ class StreamState:
                 _p(self.vcodes, _u8p), _p(self.vs, _u16p), _p(self.vz, _u16p))
 
     @classmethod
-    def prefill(cls, k_bits, v_bits, kbits, vbits, G, R, cap=None, fmt=FMT_KIVI, kscale=0.0, vscale=0.0):
+    def prefill(cls, k_bits, v_bits, kbits, vbits, G, R, cap=None, fmt=FMT_KIVI, kscale=0.0, vscale=0.0,
+                grid=GRID_UNIFORM):
         k = np.ascontiguousarray(k_bits, np.uint16)
         v = np.ascontiguousarray(v_bits, np.uint16)
         n, d = k.shape
-        st = cls(d, kbits, vbits, G, R, cap if cap is not None else max(n, 1), fmt, kscale, vscale)
+        st = cls(d, kbits, vbits, G, R, cap if cap is not None else max(n, 1), fmt, kscale, vscale, grid)
         st.hist_k[:n] = k
         st.hist_v[:n] = v
-        if fmt == FMT_KIVI:
+        if fmt == FMT_KIVI and grid == GRID_CODEBOOK:
+            st.nq = int(lib().orc_prefill_stream_cb(
+                _p(k, _u16p), _p(v, _u16p), n, d, kbits, vbits, G, R, *st._arrays()))
+        elif fmt == FMT_KIVI:
             st.nq = int(lib().orc_prefill_stream(
                 _p(k, _u16p), _p(v, _u16p), n, d, kbits, vbits, G, R, *st._arrays()))
         else:
@@ -242,7 +292,8 @@ class StreamState:
         n = ctypes.c_int(self.n)
         nq = ctypes.c_int(self.nq)
         if self.fmt == FMT_KIVI:
-            r = lib().orc_append_stream(
+            fn = lib().orc_append_stream_cb if self.grid == GRID_CODEBOOK else lib().orc_append_stream
+            r = fn(
                 _p(self.hist_k, _u16p), _p(self.hist_v, _u16p), self.cap,
                 ctypes.byref(n), ctypes.byref(nq), _p(kn, _u16p), _p(vn, _u16p),
                 self.d, self.kbits, self.vbits, self.G, self.R, *self._arrays())
@@ -262,7 +313,11 @@ class StreamState:
         n, d = self.n, self.d
         ok = np.empty((max(n, 1), d), np.float32)
         ov = np.empty((max(n, 1), d), np.float32)
-        if self.fmt == FMT_KIVI:
+        if self.fmt == FMT_KIVI and self.grid == GRID_CODEBOOK:
+            lib().orc_dequantize_stream_cb(
+                _p(self.hist_k, _u16p), _p(self.hist_v, _u16p), n, self.nq, d, self.G, self.kbits, self.vbits,
+                *self._arrays(), _p(ok, _f32p), _p(ov, _f32p))
+        elif self.fmt == FMT_KIVI:
             lib().orc_dequantize_stream(
                 _p(self.hist_k, _u16p), _p(self.hist_v, _u16p), n, self.nq, d, self.G,
                 *self._arrays(), _p(ok, _f32p), _p(ov, _f32p))
@@ -358,7 +413,7 @@ def kv_bytes_closed_form(L, Hkv, n, d, bytes_per_elem) -> float:
 # --------------------------------------------------------------------------
 
 def prefill_batch(k_bits, v_bits, seq_lens, kbits, vbits, G, R, cap=None, threads=1,
-                  fmt=FMT_KIVI, kscales=None, vscales=None):
+                  fmt=FMT_KIVI, kscales=None, vscales=None, grid=GRID_UNIFORM):
     """k_bits, v_bits: uint16 [B][H][L][d]; seq_lens: [B]; kscales, vscales:
     FP8 static scales per kv head [H].
     -> list (per sequence) of lists (per kv-head) of StreamState."""
@@ -371,7 +426,7 @@ def prefill_batch(k_bits, v_bits, seq_lens, kbits, vbits, G, R, cap=None, thread
         vs = float(vscales[h]) if vscales is not None else 0.0
         return StreamState.prefill(k_bits[b, h, :n], v_bits[b, h, :n], kbits, vbits, G, R,
                                    cap=cap if cap is not None else max(n, 1), fmt=fmt,
-                                   kscale=ks, vscale=vs)
+                                   kscale=ks, vscale=vs, grid=grid)
 
     jobs = [(b, h) for b in range(B) for h in range(H)]
     if threads > 1:

@@ -22,8 +22,9 @@
  *  [P1] section 3.1: 8-bit KV (FP8 E4M3 with a static per-tensor or per-head
  *       scale, or INT8 with a dynamic per-token scale) as the first 2x.
  *  [P1] section 3.3 (KVQuant: quantize keys before RoPE, apply RoPE when
- *       reading) and section 2 (RoPE rotates pairs of dimensions, keeping
- *       each pair's norm).
+ *       reading; non-uniform grids with levels at quantiles of the
+ *       distribution, like NF4) and section 2 (RoPE rotates pairs of
+ *       dimensions, keeping each pair's norm).
  *  [P3] experiment 03: RoPE treats two adjacent dimensions as one plane.
  *  [P2] "KV compression and quantization", part B.1 (FP8 E4M3/E5M2 and INT8
  *       at 0.5x the fp16 bytes).
@@ -271,6 +272,169 @@ void orc_attention(const float *q, int gq, const float *kh, const float *vh, int
         }
     }
     free(logit);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Non-uniform grid ("codebook" mode; [P1] section 3.3: KVQuant places the   */
+/* levels at quantiles of the distribution, like NF4).  The 2^b levels sit   */
+/* at the standard-normal quantiles of the centres of 2^b equal-probability  */
+/* bins, c_k = Phi^-1((k + 1/2) / 2^b), mapped affinely onto each set's      */
+/* [min, max] like the uniform grid's levels (so min and max stay exact): in */
+/* grid steps of the uniform grid, L_k = Q (c_k - c_0) / (c_Q - c_0), rounded */
+/* to the nearest multiple of 1/F_b (ties to even), F_b the largest power of */
+/* two with F_b Q <= 255.  Scale, zero and 1/s are the uniform grid's; a      */
+/* value goes to the nearest level (ties to the even code) and dequantizes   */
+/* to L_code * s + z.  With L_k = k this is exactly the uniform rule.        */
+/* ------------------------------------------------------------------------ */
+
+/* Standard normal quantile: bisection on the cdf 0.5 erfc(-x / sqrt 2). */
+static double normal_quantile(double p)
+{
+    double lo = -40.0, hi = 40.0;
+    for (int it = 0; it < 200; ++it) {
+        double mid = 0.5 * (lo + hi);
+        if (0.5 * erfc(-mid / sqrt(2.0)) < p)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    return 0.5 * (lo + hi);
+}
+
+int orc_codebook_scale(int bits)
+{
+    int Q = (1 << bits) - 1, F = 1;
+    while (2 * F * Q <= 255) F *= 2;
+    return F;
+}
+
+/* Levels L_0 .. L_Q of the b-bit codebook, in uniform grid steps. */
+void orc_codebook_levels(int bits, double *levels)
+{
+    int n = 1 << bits, Q = n - 1;
+    double F = (double)orc_codebook_scale(bits);
+    double c[256];
+    for (int k = 0; k < n; ++k) c[k] = normal_quantile((k + 0.5) / n);
+    for (int k = 0; k < n; ++k)
+        levels[k] = nearbyint(F * Q * (c[k] - c[0]) / (c[Q] - c[0])) / F; /* round half to even */
+}
+
+/* Set quantizer on the codebook lev[] (see quantize_set for s, z, inv). */
+static void quantize_set_cb(const uint16_t *x, int count, long stride, int bits, const double *lev,
+                            uint8_t *codes, long code_stride, uint16_t *s_out, uint16_t *z_out)
+{
+    const int qmax = (1 << bits) - 1;
+    float mn = orc_h2f(x[0]);
+    float mx = mn;
+    for (int i = 1; i < count; ++i) {
+        float v = orc_h2f(x[(long)i * stride]);
+        if (v < mn) mn = v;
+        if (v > mx) mx = v;
+    }
+    mn = mn + 0.0f;
+    mx = mx + 0.0f;
+    float s32 = (mx - mn) / (float)qmax;
+    uint16_t s16 = orc_f2h(s32);
+    uint16_t z16 = orc_f2h(mn);
+    float s = orc_h2f(s16);
+    float z = orc_h2f(z16);
+    float inv = (s > 0.0f) ? 1.0f / s : 0.0f;
+    for (int i = 0; i < count; ++i) {
+        float v = orc_h2f(x[(long)i * stride]);
+        float t = (v - z) * inv;
+        /* nearest level: count the midpoints below t; a tie at the midpoint
+         * between levels k and k+1 goes to whichever of the two is even */
+        int code = 0;
+        for (int k = 0; k < qmax; ++k) {
+            float m = (float)(0.5 * (lev[k] + lev[k + 1])); /* exact */
+            if ((k % 2 == 0) ? (t > m) : (t >= m)) code += 1;
+        }
+        codes[(long)i * code_stride] = (uint8_t)code;
+    }
+    *s_out = s16;
+    *z_out = z16;
+}
+
+void orc_quantize_key_group_cb(const uint16_t *x, int G, int d, int bits, const double *lev,
+                               uint8_t *codes, uint16_t *s, uint16_t *z)
+{
+    for (int c = 0; c < d; ++c)
+        quantize_set_cb(x + c, G, d, bits, lev, codes + c, d, &s[c], &z[c]);
+}
+
+void orc_quantize_value_token_cb(const uint16_t *x, int d, int bits, const double *lev,
+                                 uint8_t *codes, uint16_t *s, uint16_t *z)
+{
+    quantize_set_cb(x, d, 1, bits, lev, codes, 1, s, z);
+}
+
+/* orc_prefill_stream / orc_append_stream / orc_dequantize_stream on the
+ * codebooks of kbits and vbits. */
+int orc_prefill_stream_cb(const uint16_t *k, const uint16_t *v, int n, int d,
+                          int kbits, int vbits, int G, int R,
+                          uint8_t *kcodes, uint16_t *ks, uint16_t *kz,
+                          uint8_t *vcodes, uint16_t *vs, uint16_t *vz)
+{
+    double klev[256], vlev[256];
+    orc_codebook_levels(kbits, klev);
+    orc_codebook_levels(vbits, vlev);
+    int nq = orc_num_quantized(n, G, R);
+    for (int g = 0; g < nq / G; ++g)
+        orc_quantize_key_group_cb(k + (long)g * G * d, G, d, kbits, klev,
+                                  kcodes + (long)g * G * d, ks + (long)g * d, kz + (long)g * d);
+    for (int t = 0; t < nq; ++t)
+        orc_quantize_value_token_cb(v + (long)t * d, d, vbits, vlev, vcodes + (long)t * d, vs + t, vz + t);
+    return nq;
+}
+
+int orc_append_stream_cb(uint16_t *hist_k, uint16_t *hist_v, int cap, int *n, int *nq,
+                         const uint16_t *k_new, const uint16_t *v_new, int d,
+                         int kbits, int vbits, int G, int R,
+                         uint8_t *kcodes, uint16_t *ks, uint16_t *kz,
+                         uint8_t *vcodes, uint16_t *vs, uint16_t *vz)
+{
+    if (*n >= cap) return -1;
+    memcpy(hist_k + (long)(*n) * d, k_new, sizeof(uint16_t) * d);
+    memcpy(hist_v + (long)(*n) * d, v_new, sizeof(uint16_t) * d);
+    *n += 1;
+    if (*n - *nq == R + G) {
+        double klev[256], vlev[256];
+        orc_codebook_levels(kbits, klev);
+        orc_codebook_levels(vbits, vlev);
+        int g = *nq / G;
+        orc_quantize_key_group_cb(hist_k + (long)(*nq) * d, G, d, kbits, klev,
+                                  kcodes + (long)(*nq) * d, ks + (long)g * d, kz + (long)g * d);
+        for (int t = *nq; t < *nq + G; ++t)
+            orc_quantize_value_token_cb(hist_v + (long)t * d, d, vbits, vlev,
+                                        vcodes + (long)t * d, vs + t, vz + t);
+        *nq += G;
+        return 1;
+    }
+    return 0;
+}
+
+void orc_dequantize_stream_cb(const uint16_t *k, const uint16_t *v, int n, int nq, int d, int G,
+                              int kbits, int vbits,
+                              const uint8_t *kcodes, const uint16_t *ks, const uint16_t *kz,
+                              const uint8_t *vcodes, const uint16_t *vs, const uint16_t *vz,
+                              float *out_k, float *out_v)
+{
+    double klev[256], vlev[256];
+    orc_codebook_levels(kbits, klev);
+    orc_codebook_levels(vbits, vlev);
+    for (int t = 0; t < n; ++t) {
+        for (int c = 0; c < d; ++c) {
+            long i = (long)t * d + c;
+            if (t < nq) {
+                long gi = (long)(t / G) * d + c;
+                out_k[i] = fmaf((float)klev[kcodes[i]], orc_h2f(ks[gi]), orc_h2f(kz[gi]));
+                out_v[i] = fmaf((float)vlev[vcodes[i]], orc_h2f(vs[t]), orc_h2f(vz[t]));
+            } else {
+                out_k[i] = orc_h2f(k[i]);
+                out_v[i] = orc_h2f(v[i]);
+            }
+        }
+    }
 }
 
 /* ------------------------------------------------------------------------ */

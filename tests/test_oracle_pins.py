@@ -731,6 +731,120 @@ def test_pre_rope_quantization_narrows_key_ranges(orc):
 
 
 # --------------------------------------------------------------------------
+# Non-uniform grid ("KV cache compression: ...", section 3.3: KVQuant's
+# levels at quantiles of the distribution, like NF4).  The levels are checked
+# against scipy's normal quantile function (an implementation of its own),
+# the quantizer against the uniform rule it reduces to with levels 0..Q, and
+# the grid's purpose: lower 2-bit error than the uniform grid on normal data.
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_codebook_levels_are_normal_quantiles(orc, bits):
+    from scipy.special import ndtri
+    n, Q = 1 << bits, (1 << bits) - 1
+    F = orc.lib().orc_codebook_scale(bits)
+    assert F * Q <= 255 < 2 * F * Q and F & (F - 1) == 0
+    c = ndtri((np.arange(n) + 0.5) / n)
+    want = np.rint(F * Q * (c - c[0]) / (c[-1] - c[0])) / F
+    lev = orc.codebook_levels(bits)
+    assert np.array_equal(lev, want)
+    assert lev[0] == 0 and lev[-1] == Q and np.all(np.diff(lev) > 0)
+    assert np.array_equal(lev + lev[::-1], np.full(n, float(Q)))      # symmetric, like the normal
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_codebook_with_identity_levels_is_the_uniform_rule(orc, bits):
+    rng = np.random.default_rng(100 + bits)
+    x = rng.standard_normal((32, 128)).astype(np.float16).view(np.uint16)
+    ident = np.arange(1 << bits, dtype=np.float64)
+    a = orc.quantize_key_group(x, bits)
+    b = orc.quantize_key_group_cb(x, bits, levels=ident)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+    g = _golden("tie_to_even_int2.json")           # ties included
+    vals = np.tile(np.array(g["values"])[:, None], (1, 128))
+    codes, _, _ = orc.quantize_key_group_cb(f16bits(vals), 2, levels=np.arange(4.0))
+    assert codes[:, 0].tolist() == g["expected_codes"]
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_codebook_grid_aligned_and_ties(orc, bits):
+    """Values on the codebook's levels (power-of-two step, exact in fp16)
+    come back with their codes and exactly; values on a midpoint between two
+    levels go to the even code."""
+    rng = np.random.default_rng(110 + bits)
+    lev = orc.codebook_levels(bits)
+    Q = (1 << bits) - 1
+    s, z = 2.0 ** -3, -1.5
+    codes = rng.integers(0, Q + 1, size=(32, 128))
+    codes[0], codes[1] = 0, Q
+    x = z + s * lev[codes]
+    got, gs, gz = orc.quantize_key_group_cb(f16bits(x), bits)
+    assert np.array_equal(got, codes)
+    assert np.all(orc.h2f(gs) == s) and np.all(orc.h2f(gz) == z)
+    mids = (lev[:-1] + lev[1:]) / 2
+    tok = np.concatenate([[z, z + s * Q], z + s * mids, np.full(128 - 2 - Q, z)])
+    c2, _, _ = orc.quantize_value_token_cb(f16bits(tok), bits)
+    k = np.arange(Q)
+    assert c2[2:2 + Q].tolist() == np.where(k % 2 == 0, k, k + 1).tolist()
+
+
+def test_codebook_beats_uniform_at_2_bits(orc):
+    """The quantile grid's purpose: lower 2-bit error than the uniform grid
+    on normally distributed key groups (32 tokens per channel) and value
+    tokens (128 channels)."""
+    rng = np.random.default_rng(120)
+    k = rng.standard_normal((32 * 64, 128)).astype(np.float16)
+    v = rng.standard_normal((256, 128)).astype(np.float16)
+
+    def rel(x16, xh):
+        x = x16.astype(np.float64)
+        return np.mean((x - xh) ** 2) / np.mean(x ** 2)
+
+    for cb in (False, True):
+        st = orc.StreamState.prefill(k.view(np.uint16), np.resize(v, k.shape).view(np.uint16), 2, 2, 32, 0,
+                                     grid=orc.GRID_CODEBOOK if cb else orc.GRID_UNIFORM)
+        kh, vh = st.dequantize()
+        if cb:
+            ek_cb, ev_cb = rel(k, kh), rel(np.resize(v, k.shape), vh)
+        else:
+            ek_u, ev_u = rel(k, kh), rel(np.resize(v, k.shape), vh)
+    assert ek_cb < 0.97 * ek_u and ev_cb < 0.93 * ev_u, (ek_cb, ek_u, ev_cb, ev_u)
+
+
+@pytest.mark.parametrize("kbits,vbits,G,R", [(2, 2, 32, 32), (4, 2, 16, 128), (4, 4, 32, 0)])
+def test_codebook_roundtrip_and_prefill_equals_appends(orc, kbits, vbits, G, R):
+    n_total, m = 400, 111
+    rng = np.random.default_rng(130 + G + R)
+    kb = (rng.standard_normal((n_total, 128)) * 3).astype(np.float16).view(np.uint16)
+    vb = rng.standard_normal((n_total, 128)).astype(np.float16).view(np.uint16)
+    cb = orc.GRID_CODEBOOK
+    full = orc.StreamState.prefill(kb, vb, kbits, vbits, G, R, cap=n_total, grid=cb)
+    inc = orc.StreamState.prefill(kb[:m], vb[:m], kbits, vbits, G, R, cap=n_total, grid=cb)
+    for t in range(m, n_total):
+        inc.append(kb[t], vb[t])
+    assert inc.nq == full.nq == orc.num_quantized(n_total, G, R)
+    for a, b in zip((inc.key_codes(), inc.value_codes()) + inc.key_meta() + inc.value_meta(),
+                    (full.key_codes(), full.value_codes()) + full.key_meta() + full.value_meta()):
+        assert np.array_equal(a, b)
+    kh, vh = full.dequantize()
+    nq = full.nq
+    for xb, xh, bits, (s16, z16), per_tok, codes in (
+            (kb, kh, kbits, full.key_meta(), False, full.key_codes()),
+            (vb, vh, vbits, full.value_meta(), True, full.value_codes())):
+        lev = orc.codebook_levels(bits)
+        gap = np.max(np.diff(lev))
+        x = orc.h2f(xb[:nq]).astype(np.float64)
+        sf = orc.h2f(s16)[:, None] if per_tok else np.repeat(orc.h2f(s16), G, axis=0)
+        zf = orc.h2f(z16)[:, None] if per_tok else np.repeat(orc.h2f(z16), G, axis=0)
+        bound = sf * gap / 2 + (1 << bits) * sf * 2.0 ** -11 + 4 * 2.0 ** -24 * (np.abs(x) + np.abs(zf) + 16 * sf)
+        assert np.all(np.abs(x - xh[:nq]) <= bound)
+        c = codes.reshape(-1, G, 128) if not per_tok else codes
+        ax = 1 if not per_tok else 1
+        assert np.all(c.min(axis=ax) == 0) and np.all(c.max(axis=ax) == (1 << bits) - 1)
+
+
+# --------------------------------------------------------------------------
 # Mutation check: planted mistakes in a copy of the oracle must be caught
 # --------------------------------------------------------------------------
 
@@ -757,6 +871,11 @@ MUTATIONS = [
     ("double theta = pow(base, -2.0 * (double)i / (double)d);",
      "double theta = pow(base, -1.0 * (double)i / (double)d);", "rope"),  # wrong frequencies
     ("double a = (double)(pos0 + t) * theta;", "double a = (double)(pos0 + t + 1) * theta;", "rope"),  # positions from 1
+    ("if ((k % 2 == 0) ? (t > m) : (t >= m)) code += 1;", "if (t > m) code += 1;", "cbtie"),  # ties always down
+    ("for (int k = 0; k < n; ++k) c[k] = normal_quantile((k + 0.5) / n);",
+     "for (int k = 0; k < n; ++k) c[k] = normal_quantile((k + 1.0) / (n + 1));", "cblev"),  # other quantiles
+    ("out_k[i] = fmaf((float)klev[kcodes[i]], orc_h2f(ks[gi]), orc_h2f(kz[gi]));",
+     "out_k[i] = fmaf((float)kcodes[i], orc_h2f(ks[gi]), orc_h2f(kz[gi]));", "cbdeq"),  # LUT skipped
 ]
 
 
@@ -776,6 +895,9 @@ def test_pin_catches_planted_mistakes(tmp_path):
         "fp8grid": "test_fp8_grid_aligned_exact",
         "int8grid": "test_int8_per_token_grid_aligned",
         "rope": "test_rope_unit_pairs_closed_form",
+        "cbtie": "test_codebook_grid_aligned_and_ties",
+        "cblev": "test_codebook_levels_are_normal_quantiles",
+        "cbdeq": "test_codebook_roundtrip_and_prefill_equals_appends",
     }
     for i, (old, new, which) in enumerate(MUTATIONS):
         assert old in src, old
