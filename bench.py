@@ -40,6 +40,11 @@ HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 MALL_BYTES = 256 << 20         # last-level (Infinity) cache
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 ATTN_KERNEL_SOURCES = ["quantized_decode_attention_kivi_amd/csrc/kvq_attn.hip",
+                       "quantized_decode_attention_kivi_amd/csrc/kvq_attn_impl.h",
+                       "quantized_decode_attention_kivi_amd/csrc/kvq_attn_kivi.hip",
+                       "quantized_decode_attention_kivi_amd/csrc/kvq_attn_rope.hip",
+                       "quantized_decode_attention_kivi_amd/csrc/kvq_attn_cb.hip",
+                       "quantized_decode_attention_kivi_amd/csrc/kvq_attn_8bit.hip",
                        "quantized_decode_attention_kivi_amd/csrc/kvq_device.h",
                        "quantized_decode_attention_kivi_amd/csrc/kvq_internal.h",
                        "quantized_decode_attention_kivi_amd/build.py"]
@@ -209,6 +214,7 @@ def cpu_baseline(w, K, V, q, lens, budget_s, scales=None):
         vx = V[b, h, :n].cpu().numpy().view(np.uint16)
         t0 = time.perf_counter()
         st = oracle.StreamState.prefill(kx, vx, w.k_bits, w.v_bits, w.group_size, w.residual, fmt=w.kv_format,
+                                        grid=w.grid,
                                         kscale=float(ksc[h]) if ksc is not None else 0.0,
                                         vscale=float(vsc[h]) if vsc is not None else 0.0)
         t1 = time.perf_counter()
@@ -312,10 +318,11 @@ def main():
         nb = int(sum(n_quant(int(n) + grow, G, R) // G for n in lens)) + 8
         shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, G, R, paged=True,
                                num_blocks=nb, max_blocks_per_seq=mb, kv_format=w.kv_format,
-                               rope_theta=w.rope_theta)
+                               rope_theta=w.rope_theta, grid=w.grid)
     else:
         shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, w.group_size, w.residual,
-                               max_tokens=L + total_steps + 8, kv_format=w.kv_format, rope_theta=w.rope_theta)
+                               max_tokens=L + total_steps + 8, kv_format=w.kv_format, rope_theta=w.rope_theta,
+                               grid=w.grid)
     ks, vs = scales if scales is not None else (None, None)
     caches = [kvq.QuantizedKVCache(shape, device=dev, k_scale=ks, v_scale=vs) for _ in range(copies)]
     if w.paged:
@@ -423,6 +430,7 @@ def main():
             "group_size": w.group_size, "residual": w.residual, "cache_copies_rotated": copies,
             "kv_format": ["kivi", "int8", "fp8_e4m3"][w.kv_format],
             "rope_on_read_theta": w.rope_theta,
+            "grid": ["uniform", "normal_quantile_codebook"][w.grid],
             "paged": w.paged, "layers": w.layers, "min_context": int(lens.min()),
             "tokens": int(lens.sum()),
         },

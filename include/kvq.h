@@ -18,7 +18,9 @@
  *    softmax(q k^T / sqrt(d_h)).
  *  - "KV cache compression: ...", section 3.3 (KVQuant): keys quantized
  *    before the rotary position embedding, which is applied by the attention
- *    kernel when it reads them; section 2: RoPE rotates pairs of dimensions.
+ *    kernel when it reads them; levels placed at quantiles of the
+ *    distribution (like NF4) instead of evenly; section 2: RoPE rotates
+ *    pairs of dimensions.
  *  - "KV cache compression: ...", section 3.1, and "KV compression and
  *    quantization", part B.1: 8-bit caches at half the fp16 bytes, either
  *    FP8 E4M3 under a static per-head scale or INT8 under a dynamic
@@ -40,6 +42,13 @@
  *   Attention: out[b][h] = sum_t softmax_t(scale * q[b][h] . k_t) v_t over all
  *   n tokens (dequantized part and fp16 residual), query head h reading kv
  *   head h / (Hq / H).  n = 0 gives out = 0.
+ *   Codebook grid (grid = KVQ_GRID_NORMAL_QUANTILE, low-bit format): the 2^b
+ *   levels are L_k = Q (c_k - c_0) / (c_Q - c_0), c_k = Phi^-1((k + 1/2) / 2^b)
+ *   the standard normal quantiles, rounded to the nearest multiple of 1/F
+ *   (F = 64 for 2 bits, 16 for 4; ties to even); s, z and inv as above;
+ *   code = the nearest level to (x - z) * inv, a tie at a midpoint going to
+ *   the even code; dequantized value fmaf(L_code, s, z).  kvq_codebook_levels
+ *   returns the levels.
  *   Pre-RoPE keys (rope_theta > 0): the cache holds keys before the rotary
  *   embedding and attention uses RoPE_t(k_t) in place of k_t, pair
  *   (2i, 2i+1) of token t (0-based position in its sequence) rotated by the
@@ -77,6 +86,10 @@ extern "C" {
                                  token; k_bits, v_bits in {2, 4}                 */
 #define KVQ_FORMAT_INT8 1     /* keys and values per token, 8-bit min/max grid
                                  computed at write time; k_bits = v_bits = 8     */
+/* Level grids of the low-bit format (kvq_config.grid). */
+#define KVQ_GRID_UNIFORM 0         /* 2^b evenly spaced levels (KIVI)              */
+#define KVQ_GRID_NORMAL_QUANTILE 1 /* levels at normal quantiles, table dequant    */
+
 #define KVQ_FORMAT_FP8_E4M3 2 /* keys and values FP8 E4M3 under static per-kv-head
                                  scales (kvq_cache.k_scale / v_scale);
                                  k_bits = v_bits = 8                             */
@@ -107,6 +120,8 @@ typedef struct kvq_config {
     float rope_theta;           /* 0: keys used as given.  > 0: keys are stored
                                    before RoPE and rotated on read with this base
                                    (10000, 500000, ...); low-bit format only     */
+    int32_t grid;               /* KVQ_GRID_*; the codebook grid needs the
+                                   low-bit format                                */
 } kvq_config;
 
 /* Device buffers of one cache.  Sizes come from kvq_buffer_sizes(). */
@@ -240,6 +255,11 @@ kvq_status kv_export_codes(const kvq_config *cfg, const kvq_cache *cache,
                            uint8_t *k_codes, uint8_t *v_codes,
                            uint16_t *k_s, uint16_t *k_z, uint16_t *v_s, uint16_t *v_z,
                            int32_t out_tokens, void *stream);
+
+/* Host only: the 2^bits levels L_0..L_Q (in steps of the uniform grid, so
+ * the uniform grid's are 0..Q) of the normal-quantile codebook for bits 2
+ * or 4, written to levels_host[0 .. 2^bits - 1]. */
+kvq_status kvq_codebook_levels(int32_t bits, float *levels_host);
 
 /* Static description of a status code. */
 const char *kvq_status_string(kvq_status status);

@@ -18,7 +18,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkvq.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["kvq_api.hip", "kvq_quant.hip", "kvq_attn.hip"]
+SOURCES = ["kvq_api.hip", "kvq_quant.hip", "kvq_attn.hip", "kvq_attn_kivi.hip", "kvq_attn_rope.hip",
+           "kvq_attn_cb.hip", "kvq_attn_8bit.hip"]
+ATTN_KERNEL_SOURCES = ["kvq_attn_kivi.hip", "kvq_attn_rope.hip", "kvq_attn_cb.hip", "kvq_attn_8bit.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
@@ -36,8 +38,9 @@ HIPCC_FLAGS = [
 # (masked slots are removed by selects, not arithmetic), so their max/min need
 # no NaN-quieting operand canonicalization; their resource usage is reported
 # so that the build can reject any that spills to scratch.
-SOURCE_FLAGS = {"kvq_attn.hip": ["-fno-honor-nans", "-Rpass-analysis=kernel-resource-usage"]}
-NO_SCRATCH = {"kvq_attn.hip": "attn_kernel"}
+SOURCE_FLAGS = {src: ["-fno-honor-nans", "-Rpass-analysis=kernel-resource-usage"]
+                for src in ["kvq_attn.hip"] + ATTN_KERNEL_SOURCES}
+NO_SCRATCH = {src: "attn_kernel" for src in ATTN_KERNEL_SOURCES}
 
 
 def scratch_users(remarks: str, name_part: str):

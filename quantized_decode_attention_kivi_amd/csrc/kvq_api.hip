@@ -1,6 +1,7 @@
 // kvq_api.hip -- C ABI of libkvq: host-side validation, sizes and dispatch.
 // Every entry point validates its arguments before anything is enqueued and
 // never allocates device memory.
+#include <cmath>
 #include <stdio.h>
 #include <string.h>
 
@@ -14,6 +15,38 @@ static kvq_status hip_status(hipError_t e) {
     if (e == hipSuccess) return KVQ_OK;
     snprintf(g_last_error, sizeof(g_last_error), "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
     return KVQ_EHIP;
+}
+
+// Standard normal quantile: Newton's method on Phi(x) - p from x = 0
+// (Phi(x) = erfc(-x / sqrt 2) / 2, Phi'(x) = exp(-x^2 / 2) / sqrt(2 pi)); the
+// codebook needs p in [1/32, 31/32], where it converges in a few steps.
+static double normal_quantile(double p) {
+    double x = 0.0;
+    for (int it = 0; it < 60; ++it) {
+        const double f = 0.5 * std::erfc(-x * M_SQRT1_2) - p;
+        const double d = std::exp(-0.5 * x * x) * 0.3989422804014326779;
+        x -= f / d;
+    }
+    return x;
+}
+
+int codebook_levels16(int bits, int* levels16) {
+    if (bits != 2 && bits != 4) return 0;
+    const int n = 1 << bits, Q = n - 1;
+    const int F = bits == 2 ? 64 : 16;   // largest power of two with F * Q <= 255
+    double c[16];
+    for (int k = 0; k < n; ++k) c[k] = normal_quantile((k + 0.5) / n);
+    for (int k = 0; k < n; ++k) levels16[k] = (int)std::nearbyint(F * Q * (c[k] - c[0]) / (c[Q] - c[0]));
+    return F;
+}
+
+static void fill_codebook(int bits, uint32_t* lut, float* mid) {
+    int lev[16] = {0};
+    const int F = codebook_levels16(bits, lev);
+    const int n = 1 << bits;
+    for (int w = 0; w < 4; ++w) lut[w] = 0;
+    for (int k = 0; k < n; ++k) lut[k >> 2] |= (uint32_t)lev[k] << (8 * (k & 3));
+    for (int k = 0; k < 15; ++k) mid[k] = k + 1 < n ? (float)(lev[k] + lev[k + 1]) / (float)(2 * F) : 0.0f;
 }
 
 kvq_status make_layout(const kvq_config* cfg, Layout* L) {
@@ -35,6 +68,15 @@ kvq_status make_layout(const kvq_config* cfg, Layout* L) {
     if (!(cfg->rope_theta >= 0.0f) || cfg->rope_theta > 1e30f) return KVQ_EINVAL;   // also rejects NaN
     if (cfg->rope_theta > 0.0f && (cfg->kv_format != kFmtKivi || cfg->rope_theta <= 1.0f)) return KVQ_EUNSUPPORTED;
     L->rope_theta = cfg->rope_theta;
+    if (cfg->grid != KVQ_GRID_UNIFORM && cfg->grid != KVQ_GRID_NORMAL_QUANTILE) return KVQ_EINVAL;
+    if (cfg->grid == KVQ_GRID_NORMAL_QUANTILE && cfg->kv_format != kFmtKivi) return KVQ_EUNSUPPORTED;
+    L->grid = cfg->grid;
+    for (int i = 0; i < 4; ++i) L->klut[i] = L->vlut[i] = 0;
+    for (int i = 0; i < 15; ++i) L->kmid[i] = L->vmid[i] = 0.0f;
+    if (L->grid == KVQ_GRID_NORMAL_QUANTILE) {
+        fill_codebook(cfg->k_bits, L->klut, L->kmid);
+        fill_codebook(cfg->v_bits, L->vlut, L->vmid);
+    }
     L->fmt = cfg->kv_format;
     L->B = cfg->num_seqs;
     L->H = cfg->num_kv_heads;
@@ -216,6 +258,15 @@ kvq_status kv_export_codes(const kvq_config* cfg, const kvq_cache* cache, uint8_
     if (out_tokens < 0 || out_tokens % L.G) return KVQ_EINVAL;
     return hip_status(launch_export(L, *cache, k_codes, v_codes, k_s, k_z, v_s, v_z, out_tokens,
                                     (hipStream_t)stream));
+}
+
+kvq_status kvq_codebook_levels(int32_t bits, float* levels_host) {
+    if (!levels_host) return KVQ_EINVAL;
+    int lev[16];
+    const int F = codebook_levels16(bits, lev);
+    if (!F) return KVQ_EUNSUPPORTED;
+    for (int k = 0; k < (1 << bits); ++k) levels_host[k] = (float)lev[k] / (float)F;
+    return KVQ_OK;
 }
 
 const char* kvq_status_string(kvq_status s) {

@@ -1,1153 +1,11 @@
-// kvq_attn.hip -- split-K decode attention over the packed KIVI cache (gfx950).
-//
-// What it computes ("KV cache compression" (jaedaily), formula paragraph;
-// "KV cache compression: quantization, eviction and sparse attention",
-// sections 3.1, 3.2, 3.4 and 8.2): for every query head h of sequence b,
-//   out = sum_t softmax_t(scale * q . k_t) v_t
-// over the dequantized keys/values of the quantized groups and the fp16
-// residual tokens.  The kernel dequantizes while it reads; the quantized part
-// and the residual are processed by different workgroups and merged.
-//
-// Dequantization is folded into the contractions instead of materialised:
-//   q . k_t      = sum_c (q_c s_c) code_tc + sum_c q_c z_c        (key group)
-//   sum_t p_t v_t = sum_t (p_t s_t) code_t + sum_t p_t z_t        (value tokens)
-// For one kv head and 32 tokens both are small dense products between the
-// query heads of the GQA group (up to 16, padded to 16) and the codes, so they
-// run on the matrix cores (v_mfma_f32_16x16x32_f16, fp32 accumulation):
-//   keys:   C[token][head]  = codes[token][c] . (q s)[c][head]
-//   values: acc[head][c]   += (p s)[head][token] . codes[token][c]
-// Codes are exact small integers in fp16.  q s is the exact product of two
-// fp16 numbers (22 significant bits), so it is split exactly into an fp16
-// high and low part and contracted twice; p s is split the same way (to 22
-// bits).  The key zero points enter as one more product, z[c] . q[c][head],
-// whose result seeds the key accumulator.  The vector ALU only unpacks codes
-// and runs the online softmax.
-//
-// Work split: each stream (b, kv head) is cut into `splits` ranges of 32-token
-// units plus one workgroup for the fp16 residual ring.  Waves walk their units
-// independently (two units in flight per wave), combine in LDS, and every
-// workgroup writes a partial (max, sum, output) to the workspace.  A second,
-// small kernel merges the partials of each (stream, head) by log-sum-exp.
-// The kernel boundary makes the partials visible to it; a per-workgroup
-// device-scope release would write back the XCD's L2 once per workgroup.
-#include <algorithm>
-#include <type_traits>
-
-#include "kvq_device.h"
+// kvq_attn.hip -- decode attention: split planning, dispatch to the kernel
+// families (instantiated in kvq_attn_*.hip) and the log-sum-exp merge
+// kernels (gfx950).
+#include "kvq_attn_impl.h"
 
 namespace kvq {
 
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-
-constexpr int kWaves = 4;
-constexpr int kPart = kD + 4;          // floats per head in a partial: out[128], m, l, pad
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNegInf = -__builtin_huge_valf();
-
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ __forceinline__ h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
-__device__ __forceinline__ uint32_t as_u32(h2 x) { return __builtin_bit_cast(uint32_t, x); }
-__device__ __forceinline__ h8 make_h8(h2 a, h2 b, h2 c, h2 d) {
-    return h8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-__device__ __forceinline__ h8 words_h8(uint4 w) {
-    return make_h8(as_h2(w.x), as_h2(w.y), as_h2(w.z), as_h2(w.w));
-}
-
-// Max over the four lane groups (lanes l, l^16, l^32, l^48).
-__device__ __forceinline__ float group_max(float x) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, x);
-    auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    x = fmaxf(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
-    const uint32_t v = __builtin_bit_cast(uint32_t, x);
-    auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    return fmaxf(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
-}
-__device__ __forceinline__ float group_sum(float x) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, x);
-    auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    x = __builtin_bit_cast(float, (uint32_t)a[0]) + __builtin_bit_cast(float, (uint32_t)a[1]);
-    const uint32_t v = __builtin_bit_cast(uint32_t, x);
-    auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    return __builtin_bit_cast(float, (uint32_t)b[0]) + __builtin_bit_cast(float, (uint32_t)b[1]);
-}
-
-// Code unpacking (word layout: code_bit()).  INT4: byte-spread nibbles read as
-// fp8 e4m3 are c * 2^-9 (exact, subnormals included), scaled by 512.  INT2:
-// codes 0..3 in the low bits of a nibble read as fp4 e2m1 are c / 2, scaled by 2.
-__device__ __forceinline__ h8 unpack4(uint32_t w) {
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-    return make_h8(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false),
-                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true),
-                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, false),
-                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, true));
-}
-__device__ __forceinline__ h8 unpack2_half(uint32_t w, bool upper) {
-    const uint32_t x = (upper ? (w >> 2) : w) & 0x33333333u;
-    return make_h8(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 0),
-                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 1),
-                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 2),
-                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 3));
-}
-// Codes 8j..8j+7 of a lane's code sequence held in words w[].
-template <int BITS>
-__device__ __forceinline__ h8 codes8(const uint32_t* w, int j) {
-    if (BITS == 4) return unpack4(w[j]);
-    return unpack2_half(w[j >> 1], j & 1);
-}
-
-__device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void* lds_ptr;
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-
-// One 32-token unit (NR = 32/G records) staged in LDS by the buffer unit's
-// direct-to-LDS loads: each load instruction moves 16 bytes per lane from any
-// record offset to LDS slot (base + 16*lane), so the next unit's codes are in
-// flight without occupying registers.  Byte offsets inside one stage buffer:
-//   KC   key codes.  16-bit keys (INT4): the 16 bytes lane (g, n) feeds the
-//        key product of row tile rt sit at KC + rt*1024 + 16*lane.  INT2: the 8
-//        bytes of (g, n, rt) sit at KC + rt*512 + 16*((g/2)*16 + n) + 8*(g%2).
-//   VC   value codes.  G = 32: lane l's words 0-3 at VC + 16l, words 4-7 (INT4)
-//        at VC + 1024 + 16l.  G = 16: record i's words of lane l at
-//        VC + i*64*VW*4 + VW*4*l (VW words per lane and record).
-//   META record i's key scale/zero table (512 B) then its value scale/zero
-//        table (4G B) at META + i*MREC.
-template <int G, int KB, int VB>
-struct Stage {
-    static constexpr int NR = 32 / G;
-    static constexpr int SPT = G == 16 ? 4 : 8;
-    static constexpr int VW = SPT * VB / 4;          // value words per lane and record
-    static constexpr int KC = 0;
-    static constexpr int VC = 512 * KB;
-    static constexpr int META = VC + 512 * VB;
-    static constexpr int MREC = 512 + 4 * G;
-    static constexpr int BYTES = META + NR * MREC;
-    // 16-byte aligned and large enough to hold a wave's [16][128] fp32
-    // accumulators at the end (two waves per stage array)
-    static constexpr int PITCH = BYTES < 4096 ? 4096 : (BYTES + 15) / 16 * 16;
-    // direct-to-LDS load instructions per unit (the wait counts below)
-    static constexpr int LOADS = G == 32 ? KB / 2 + VB / 2 + 1 : 6;
-};
-
-// s_waitcnt immediate that waits for all LDS operations of the wave.
-constexpr int kLgkmZero = 15 | (3 << 14) | (7 << 4);
-
-// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
-// memory operations of this wave are outstanding; other counters untouched.
-__device__ __forceinline__ constexpr int vmcnt_imm(int n) {
-    return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
-}
-
-// Buffer descriptor of one record, wave uniform (hardware range check: an
-// absent record gets num_records = 0 and every load from it returns zeros).
-__device__ __forceinline__ u32x4 record_desc(const uint8_t* rec, int bytes) {
-    const uint64_t a = (uint64_t)rec;
-    u32x4 d;
-    d[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
-    d[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
-    d[2] = __builtin_amdgcn_readfirstlane(rec ? (uint32_t)bytes : 0u);
-    d[3] = 0x00020000u;
-    return d;
-}
-
-// 16 bytes per lane from record offset `off` to LDS address lds + 16*lane.
-// Issued from inline assembly so that the compiler inserts no waits of its
-// own for the LDS write (it cannot tell the two stage buffers apart and would
-// drain the prefetch); the kernel waits explicitly before reading a buffer.
-__device__ __forceinline__ void lds_load16(u32x4 desc, lds_u8* dst, int off) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(desc), "{m0}"(m0) : "memory");
-}
-
-// Issues the direct-to-LDS loads of one unit into stage buffer `buf` (wave
-// uniform address) and returns which of its records exist.  Every call issues
-// exactly Stage::LOADS load instructions, so the wait counts stay exact.
-template <int G, int KB, int VB, bool PG>
-__device__ __forceinline__ uint32_t issue_unit(lds_u8* buf, const Layout& L, const kvq_cache& c, int b, int h,
-                                               int unit, int ngroups, int lane) {
-    using S = Stage<G, KB, VB>;
-    const int g = lane >> 4, n = lane & 15;
-    // The buffer's LDS address, made opaque here so that the per-load M0
-    // values are formed next to each load rather than hoisted out of the unit
-    // loop into scalar registers of their own.
-    uint32_t base = (uint32_t)(uintptr_t)buf;
-    asm volatile("" : "+s"(base));
-    buf = (lds_u8*)(uintptr_t)base;
-    uint32_t has = 0;
-#pragma unroll
-    for (int i = 0; i < S::NR; ++i) {
-        const int grp = unit * S::NR + i;
-        const uint8_t* rec = grp < ngroups ? record_at_t<PG>(L, c.packed, c.block_table, b, h, grp) : nullptr;
-        has |= (rec != nullptr) << i;
-        const u32x4 rs = record_desc(rec, L.record);
-        if (G == 32) {
-            if (KB == 4) {
-                lds_load16(rs, buf + S::KC, n * 64 + 16 * g);
-                lds_load16(rs, buf + S::KC + 1024, (16 + n) * 64 + 16 * g);
-            } else {
-                // slot l = rt*32 + gh*16 + n  <-  token 16rt + n, lane groups 2gh, 2gh+1
-                const int rt = lane >> 5, gh = (lane >> 4) & 1;
-                lds_load16(rs, buf + S::KC, (16 * rt + n) * 32 + 16 * gh);
-            }
-            lds_load16(rs, buf + S::VC, L.vcode_off + S::VW * 4 * lane);
-            if (VB == 4) lds_load16(rs, buf + S::VC + 1024, L.vcode_off + S::VW * 4 * lane + 16);
-        } else {
-            if (KB == 4) {
-                lds_load16(rs, buf + S::KC + i * 1024, n * 64 + 16 * g);
-            } else if (lane < 32) {
-                const int gh = lane >> 4;
-                lds_load16(rs, buf + S::KC + i * 512, n * 32 + 16 * gh);
-            }
-            if (VB == 4) {
-                lds_load16(rs, buf + S::VC + i * 1024, L.vcode_off + 16 * lane);
-            } else if (lane < 32) {
-                lds_load16(rs, buf + S::VC + i * 512, L.vcode_off + 16 * lane);
-            }
-        }
-        if (lane < 32 + G / 4)
-            lds_load16(rs, buf + S::META + i * S::MREC,
-                       lane < 32 ? L.kmeta_off + 16 * lane : L.vmeta_off + 16 * (lane - 32));
-    }
-    return has;
-}
-
-// 8-bit formats (INT8, FP8 E4M3): one 32-token unit (NR = 32/G records)
-// staged the same way, byte offsets inside one stage buffer:
-//   KC   key bytes: load i = 2rt + half puts the 16 bytes lane (g, n) feeds
-//        the key product of row tile rt (token 16rt + n, channels
-//        32g + 16half .. +15) at KC + 1024 i + 16 lane.
-//   VC   value bytes.  G = 32: bytes 16i .. 16i+15 of lane l's 64 at
-//        VC + 1024 i + 16 l.  G = 16: record r's lane-l bytes 16half .. at
-//        VC + 1024 (2r + half) + 16 l.
-//   META INT8 only: record r's per-token key table (4G bytes) then its value
-//        table (4G bytes) at META + 8G r.
-template <int G, int F>
-struct Stage8 {
-    static constexpr int NR = 32 / G;
-    static constexpr int SPT = G == 16 ? 4 : 8;
-    static constexpr int KC = 0;
-    static constexpr int VC = 4096;
-    static constexpr int META = 8192;
-    static constexpr int MREC = F == kFmtInt8 ? 8 * G : 0;
-    static constexpr int BYTES = META + NR * MREC;
-    static constexpr int PITCH = (BYTES + 15) / 16 * 16;
-    static constexpr int LOADS = 8 + (F == kFmtInt8 ? NR : 0);
-};
-
-template <int G, int F, bool PG>
-__device__ __forceinline__ uint32_t issue_unit8(lds_u8* buf, const Layout& L, const kvq_cache& c, int b, int h,
-                                                int unit, int ngroups, int lane) {
-    using S = Stage8<G, F>;
-    const int g = lane >> 4, n = lane & 15;
-    uint32_t base = (uint32_t)(uintptr_t)buf;
-    asm volatile("" : "+s"(base));
-    buf = (lds_u8*)(uintptr_t)base;
-    uint32_t has = 0;
-#pragma unroll
-    for (int i = 0; i < S::NR; ++i) {
-        const int grp = unit * S::NR + i;
-        const uint8_t* rec = grp < ngroups ? record_at_t<PG>(L, c.packed, c.block_table, b, h, grp) : nullptr;
-        has |= (rec != nullptr) << i;
-        const u32x4 rs = record_desc(rec, L.record);
-        if (G == 32) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k)   // k = 2rt + half
-                lds_load16(rs, buf + S::KC + 1024 * k, kD * (16 * (k >> 1) + n) + 32 * g + 16 * (k & 1));
-#pragma unroll
-            for (int k = 0; k < 4; ++k) lds_load16(rs, buf + S::VC + 1024 * k, L.vcode_off + 64 * lane + 16 * k);
-        } else {
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                lds_load16(rs, buf + S::KC + 1024 * (2 * i + hf), kD * n + 32 * g + 16 * hf);
-                lds_load16(rs, buf + S::VC + 1024 * (2 * i + hf), L.vcode_off + 32 * lane + 16 * hf);
-            }
-        }
-        if (F == kFmtInt8 && lane < G / 2) lds_load16(rs, buf + S::META + i * S::MREC, L.kmeta_off + 16 * lane);
-    }
-    return has;
-}
-
-// Per-wave online-softmax state and value accumulators.
-struct WaveAcc {
-    f4 acc[8];        // acc[ct][i]: head 4g+i, channel 16ct+n
-    float m;          // running max of head n (log2 units), same in all lane groups
-    float l, pz;      // this lane's share of sum p and sum p*z for head n
-};
-
-__device__ __forceinline__ void acc_init(WaveAcc& A) {
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) A.acc[ct] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    A.m = kNegInf;
-    A.l = 0.0f;
-    A.pz = 0.0f;
-}
-
-// Online-softmax step over the 8 logits x[] (raw q.k, slot order) of this
-// lane's column, then the value contraction with operands vop(ct).  vs/vz:
-// value scale/zero of each slot; valid: slot holds a token.  The weights p*s
-// are split into fp16 high and low parts (22 bits).  LP (limb-packed): rows
-// 0-7 of the value product take the high parts and rows 8-15 the low parts of
-// heads 0-7, one product per column tile; otherwise each part is a product of
-// its own over rows = heads.
-template <bool LP, typename VOp>
-__device__ __forceinline__ void softmax_and_values(WaveAcc& A, const float (&x)[8], const float (&vs)[8],
-                                                   const float (&vz)[8], const bool (&valid)[8], float sl2,
-                                                   int lane, VOp vop) {
-    float cm = kNegInf;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) cm = valid[k] ? fmaxf(cm, x[k]) : cm;
-    cm = group_max(cm);
-    const float mnew = fmaxf(A.m, cm * sl2);
-    // nothing accumulated yet (running max still -inf): no rescale needed
-    const float alpha = A.m == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(A.m - mnew);
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-        // rows of acc are columns 4g+i; column j's alpha lives in lanes with n == j
-        const int base = (lane & 48) | ((lane >> 4) << 2);
-        float ai[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, base + i);
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) A.acc[ct][i] *= ai[i];
-        A.l *= alpha;
-        A.pz *= alpha;
-    }
-    A.m = mnew;
-    float w[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        // invalid slots (masked tokens, missing records) contribute nothing,
-        // whatever their (possibly non-finite) scale and zero bits
-        const float p = valid[k] ? __builtin_amdgcn_exp2f(fmaf(x[k], sl2, -mnew)) : 0.0f;
-        A.l += p;
-        A.pz = valid[k] ? fmaf(p, vz[k], A.pz) : A.pz;
-        w[k] = valid[k] ? p * vs[k] : 0.0f;
-    }
-    h8 whi, wlo;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const _Float16 hi = (_Float16)w[k];
-        whi[k] = hi;
-        wlo[k] = (_Float16)(w[k] - (float)hi);
-    }
-    if (LP) {
-        const h8 wop = (lane & 8) ? wlo : whi;
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) A.acc[ct] = mfma(wop, vop(ct), A.acc[ct]);
-    } else {
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-            const h8 bop = vop(ct);
-            A.acc[ct] = mfma(whi, bop, A.acc[ct]);
-            A.acc[ct] = mfma(wlo, bop, A.acc[ct]);
-        }
-    }
-}
-
-// LP: the two limb partials of a logit sit in columns n and n^8 of the same
-// 16-lane row; one DPP rotation by 8 brings them together.
-__device__ __forceinline__ float add_limb_partner(float x) {
-    // bound_ctrl with a zero "old" lets the compiler fold the move into the add
-    const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128 /* row_ror:8 */, 0xf, 0xf, true);
-    return x + __builtin_bit_cast(float, y);
-}
-
-// Query operand of lane (g, n): q[head n][32g + 8j + e], zero for heads >= gq.
-struct QOps {
-    h8 q[4];
-};
-
-template <typename T>
-__device__ __forceinline__ T lds_read(const lds_u8* p) {
-    return *(const __attribute__((address_space(3))) T*)p;
-}
-
-// ---------------------------------------------------------------------------
-// Pre-RoPE keys rotated on read ("KV cache compression: ...", section 3.3:
-// KVQuant quantizes keys before the rotary embedding and applies it when
-// reading; section 2: RoPE rotates pairs of dimensions).  Pair i = (2i, 2i+1)
-// of token t turns by t * theta_i, theta_i = base^(-i/64).  The rotation
-// depends on the token, so it cannot be folded into the query operand: each
-// dequantized key element is rotated in fp32, split exactly into fp16 high
-// and low parts, and both parts go through the key product with the plain
-// fp16 query (its dequantization included: k = code * s + z per channel).
-//
-// Angles: phi_i = theta_i / 2pi turns per token as a 0.64 fixed-point
-// fraction, so t * phi_i mod 1 is an exact integer product at any position;
-// the (cos, sin) of a unit's first token comes from sincospi of that, those
-// of its tokens t0 + r from a per-workgroup table of (cos, sin)(r theta_i),
-// r <= 16, by the angle-addition formula.
-// ---------------------------------------------------------------------------
-constexpr int kFmtRope = 3;       // low-bit format with pre-RoPE keys (attention instantiations only)
-constexpr int kTabPitch = 66;     // float2 per table row: rows of lanes n = 0..15 hit distinct banks
-typedef float f2 __attribute__((ext_vector_type(2)));
-
-struct RopeLds {
-    uint64_t phi[64];                 // turns per token of pair i, 0.64 fixed point
-    f2 tab[17][kTabPitch];            // (cos, sin)(r theta_i), r = 0..16
-    f2 base[kWaves][2][64];           // per wave: (cos, sin) at the unit's tokens t0 and t0 + 16
-};
-
-// (sin, cos) of the angle a / 2^64 turns (the top 32 bits, signed: |turns| <= 1/2).
-__device__ __forceinline__ void turns_sincos(uint64_t a, float* s, float* c) {
-    const int hi = (int)(uint32_t)(a >> 32);
-    sincospif((float)hi * 0x1p-31f, s, c);
-}
-
-// Workgroup prologue: phi and the table.  All threads.
-__device__ void rope_setup(RopeLds& R, float theta, int tid) {
-    if (tid < 64) {
-        const double th = pow((double)theta, -(double)tid / 64.0);
-        R.phi[tid] = (uint64_t)(th * (18446744073709551616.0 / 6.283185307179586476925));
-    }
-    __syncthreads();
-    for (int e = tid; e < 17 * 64; e += 256) {
-        const int r = e >> 6, i = e & 63;
-        float sn, cs;
-        turns_sincos((uint64_t)r * R.phi[i], &sn, &cs);
-        R.tab[r][i] = f2{cs, sn};
-    }
-    __syncthreads();
-}
-
-// The wave's (cos, sin) at tokens t0 and t0 + 16 for every pair (lane = pair).
-__device__ __forceinline__ void rope_unit_base(RopeLds* R, int wave, int lane, int t0) {
-    float sn, cs;
-    turns_sincos((uint64_t)(uint32_t)t0 * R->phi[lane], &sn, &cs);
-    const f2 t16 = R->tab[16][lane];
-    R->base[wave][0][lane] = f2{cs, sn};
-    R->base[wave][1][lane] = f2{cs * t16[0] - sn * t16[1], sn * t16[0] + cs * t16[1]};
-    wave_sync();
-}
-
-// Key logits of both row tiles (token t0 + 16rt + n of lane (g, n), rt = 0, 1)
-// against the lane's column head: getx(rt, j, x) gives the pre-RoPE key
-// values x[0..7] of channels 32g + 8j .. + 7 (pairs i = 16g + 4j + p).  The
-// lane's table entries (row n) are read once for both tiles.
-template <typename GetX>
-__device__ __forceinline__ void rope_key_tiles(const RopeLds* R, int wave, int lane, const QOps& Q, f4 (&C)[2],
-                                               GetX getx) {
-    const int g = lane >> 4, n = lane & 15;
-    C[0] = C[1] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    // -1, opaque: keeps lo = fma(hi, -1, k) one mixed-precision fma with an
-    // fp16 result instead of being rewritten as a conversion and a subtraction
-    float m1 = -1.0f;
-    asm volatile("" : "+v"(m1));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int i0 = 16 * g + 4 * j;
-        const f4 ts[2] = {*(const __attribute__((address_space(3))) f4*)&R->tab[n][i0],
-                          *(const __attribute__((address_space(3))) f4*)&R->tab[n][i0 + 2]};
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            float x[8];
-            getx(rt, j, x);
-            const f4 bs[2] = {*(const __attribute__((address_space(3))) f4*)&R->base[wave][rt][i0],
-                              *(const __attribute__((address_space(3))) f4*)&R->base[wave][rt][i0 + 2]};
-            h8 hi, lo;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const f4 b = bs[p >> 1], t = ts[p >> 1];
-                const int o = 2 * (p & 1);
-                const float Cs = b[o] * t[o] - b[o + 1] * t[o + 1];
-                const float Sn = b[o + 1] * t[o] + b[o] * t[o + 1];
-                const float k0 = Cs * x[2 * p] - Sn * x[2 * p + 1];
-                const float k1 = Sn * x[2 * p] + Cs * x[2 * p + 1];
-                const _Float16 h0 = (_Float16)k0, h1 = (_Float16)k1;
-                hi[2 * p] = h0;
-                hi[2 * p + 1] = h1;
-                // k - hi is exact in fp32: one mixed-precision fma per element
-                lo[2 * p] = (_Float16)__builtin_fmaf((float)h0, m1, k0);
-                lo[2 * p + 1] = (_Float16)__builtin_fmaf((float)h1, m1, k1);
-            }
-            C[rt] = mfma(hi, Q.q[j], C[rt]);
-            C[rt] = mfma(lo, Q.q[j], C[rt]);
-        }
-    }
-}
-
-// One staged unit (see Stage): key logits on the matrix cores, then the
-// online-softmax step and the value product.  RP: pre-RoPE keys (R, wave:
-// the rotation tables; t0: the unit's first token).
-template <int G, int KB, int VB, bool LP, bool RP>
-__device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, WaveAcc& A, const QOps& Q, float sl2,
-                                             int lane, RopeLds* R, int wave, int t0) {
-    using S = Stage<G, KB, VB>;
-    constexpr int SPT = S::SPT;
-    const int g = lane >> 4, n = lane & 15;
-    const bool lo_limb = LP && (lane & 8);
-
-    // Key side: accumulators start from sum_c z[c] q[c][head] (every row; LP:
-    // high-limb columns only), then add codes . (q s) with q s split exactly
-    // into fp16 high and low parts (LP: the part of the lane's column).
-    f4 C[2];
-    if constexpr (RP) {
-        // pre-RoPE: dequantize, rotate, split, contract with the plain query
-        rope_unit_base(R, wave, lane, t0);
-        uint32_t kc[2][KB];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            if (KB == 4) {
-                const u32x4 x = lds_read<u32x4>(buf + S::KC + rt * 1024 + 16 * lane);
-                kc[rt][0] = x[0]; kc[rt][1] = x[1]; kc[rt][2] = x[2]; kc[rt][3] = x[3];
-            } else {
-                const u32x2 x = lds_read<u32x2>(buf + S::KC + rt * 512 + 16 * ((g >> 1) * 16 + n) + 8 * (g & 1));
-                kc[rt][0] = x[0]; kc[rt][1] = x[1];
-            }
-        }
-        rope_key_tiles(R, wave, lane, Q, C, [&](int rt, int j, float* x) {
-            // the record's channel scales and zeros (one record for both
-            // tiles when G = 32, record rt when G = 16)
-            const lds_u8* km = buf + S::META + (S::NR == 2 ? rt : 0) * S::MREC;
-            const h8 a = codes8<KB>(kc[rt], j);
-            const h8 sj = __builtin_bit_cast(h8, lds_read<u32x4>(km + 16 * (4 * g + j)));
-            const h8 zj = __builtin_bit_cast(h8, lds_read<u32x4>(km + 256 + 16 * (4 * g + j)));
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = fmaf((float)a[e], (float)sj[e], (float)zj[e]);
-        });
-    } else {
-#pragma unroll
-    for (int i = 0; i < S::NR; ++i) {
-        const lds_u8* km = buf + S::META + i * S::MREC;
-        f4 cz = f4{0.0f, 0.0f, 0.0f, 0.0f};
-        h8 qhi[4], qlo[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const h8 s = __builtin_bit_cast(h8, lds_read<u32x4>(km + 16 * (4 * g + j)));
-            const h8 z = __builtin_bit_cast(h8, lds_read<u32x4>(km + 256 + 16 * (4 * g + j)));
-            cz = mfma(z, Q.q[j], cz);
-            {
-#pragma clang fp contract(off)
-                const h8 hi = Q.q[j] * s;
-                qhi[j] = hi;
-                if (!LP) qlo[j] = __builtin_elementwise_fma(Q.q[j], s, -hi);
-            }
-        }
-        if (LP && lo_limb) {
-            // low-limb columns (a divergent branch: only these lanes pay for
-            // it): the exact low parts q s - hi(q s), and no bias
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const h8 s = __builtin_bit_cast(h8, lds_read<u32x4>(km + 16 * (4 * g + j)));
-                qhi[j] = __builtin_elementwise_fma(Q.q[j], s, -qhi[j]);
-            }
-            cz = f4{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            if (S::NR == 2 && rt != i) continue;
-            uint32_t kc[KB];
-            if (KB == 4) {
-                const u32x4 x = lds_read<u32x4>(buf + S::KC + rt * 1024 + 16 * lane);
-                kc[0] = x[0]; kc[1] = x[1]; kc[2] = x[2]; kc[3] = x[3];
-            } else {
-                const u32x2 x = lds_read<u32x2>(buf + S::KC + rt * 512 + 16 * ((g >> 1) * 16 + n) + 8 * (g & 1));
-                kc[0] = x[0]; kc[1] = x[1];
-            }
-            f4 acc = cz;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const h8 a = codes8<KB>(kc, j);
-                acc = mfma(a, qhi[j], acc);
-                if (!LP) acc = mfma(a, qlo[j], acc);
-            }
-            C[rt] = acc;
-        }
-    }
-    }
-
-    // value codes of this lane (per record)
-    uint32_t vc[S::NR][S::VW];
-    if (G == 32) {
-        const u32x4 x = lds_read<u32x4>(buf + S::VC + 16 * lane);
-        vc[0][0] = x[0]; vc[0][1] = x[1]; vc[0][2] = x[2]; vc[0][3] = x[3];
-        if (VB == 4) {
-            const u32x4 y = lds_read<u32x4>(buf + S::VC + 1024 + 16 * lane);
-            vc[0][4] = y[0]; vc[0][5] = y[1]; vc[0][6] = y[2]; vc[0][7] = y[3];
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < S::NR; ++i) {
-            if (VB == 4) {
-                const u32x4 x = lds_read<u32x4>(buf + S::VC + i * 1024 + 16 * lane);
-                vc[i][0] = x[0]; vc[i][1] = x[1]; vc[i][2] = x[2]; vc[i][3] = x[3];
-            } else {
-                const u32x2 x = lds_read<u32x2>(buf + S::VC + i * 512 + 8 * lane);
-                vc[i][0] = x[0]; vc[i][1] = x[1];
-            }
-        }
-    }
-
-    // value scale/zero of the lane's 8 slots: slot k = 4*rt + i <-> token 16rt + 4g + i
-    float x[8], vs[8], vz[8];
-    bool valid[8];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        const int rec = S::NR == 2 ? rt : 0;
-        const lds_u8* vm = buf + S::META + rec * S::MREC + 512 + g * 4 * SPT;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int k = 4 * rt + i;
-            const int slot = S::NR == 2 ? i : k;
-            // (pre-RoPE: both limb columns hold the same head's full logit)
-            x[k] = LP && !RP ? add_limb_partner(C[rt][i]) : C[rt][i];
-            vs[k] = h2f(lds_read<uint16_t>(vm + 2 * slot));
-            vz[k] = h2f(lds_read<uint16_t>(vm + 2 * (SPT + slot)));
-            valid[k] = S::NR == 1 || ((has >> rec) & 1);
-        }
-    }
-    softmax_and_values<LP>(A, x, vs, vz, valid, sl2, lane, [&](int ct) -> h8 {
-        if (S::NR == 1) return codes8<VB>(vc[0], ct);
-        // G = 16: 4 slots of each record; code q = 4ct + slot
-        const h8 a = codes8<VB>(vc[0], ct >> 1);
-        const h8 b = codes8<VB>(vc[1], ct >> 1);
-        const int o = 4 * (ct & 1);
-        return h8{a[o], a[o + 1], a[o + 2], a[o + 3], b[o], b[o + 1], b[o + 2], b[o + 3]};
-    });
-}
-
-// Eight 8-bit codes (words w0, w1, byte order) as an fp16 operand.  INT8:
-// code - 128, exact: v_perm_b32 pairs each byte with 0x64 into the fp16
-// number 1024 + code, and one packed subtraction recentres it.  FP8: the
-// E4M3 values themselves (exact in fp16).
-template <int F>
-__device__ __forceinline__ h8 conv8(uint32_t w0, uint32_t w1) {
-    if (F == kFmtInt8) {
-        const h2 off = h2{(_Float16)-1152.0f, (_Float16)-1152.0f};
-        const h2 a = as_h2(__builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u)) + off;
-        const h2 b = as_h2(__builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u)) + off;
-        const h2 c = as_h2(__builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u)) + off;
-        const h2 d = as_h2(__builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u)) + off;
-        return make_h8(a, b, c, d);
-    }
-    return make_h8(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false),
-                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true),
-                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false),
-                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true));
-}
-
-// One staged unit of an 8-bit format.  The query is an exact fp16 operand
-// and so are the codes, so each key product is one MFMA per 32 channels with
-// no high/low split; the per-token dequantization acts on the finished dot
-// products:
-//   INT8  q . k_t = s_t (q . (code_t - 128)) + (z_t + 128 s_t) sum_c q_c
-//   FP8   q . k_t = s_k (q . e_t)       (s_k folded into sl2 by the caller)
-// and on the value side p s_t multiplies the code operand as in the low-bit
-// format, with z_t + 128 s_t (INT8) or 0 (FP8) as the zero term.  LP: the
-// columns n and n + 8 hold the same head, so both lane halves compute the
-// same logits and need no limb partner.  qsum: sum_c q_c of the lane's head;
-// vscl: the static value scale (FP8).
-template <int G, int F, bool LP>
-__device__ __forceinline__ void process_unit8(const lds_u8* buf, uint32_t has, WaveAcc& A, const QOps& Q,
-                                              float sl2, float qsum, float vscl, int lane) {
-    using S = Stage8<G, F>;
-    constexpr int SPT = S::SPT;
-    const int g = lane >> 4;
-
-    f4 C[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        const u32x4 x0 = lds_read<u32x4>(buf + S::KC + 1024 * (2 * rt) + 16 * lane);
-        const u32x4 x1 = lds_read<u32x4>(buf + S::KC + 1024 * (2 * rt + 1) + 16 * lane);
-        f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
-        acc = mfma(conv8<F>(x0[0], x0[1]), Q.q[0], acc);
-        acc = mfma(conv8<F>(x0[2], x0[3]), Q.q[1], acc);
-        acc = mfma(conv8<F>(x1[0], x1[1]), Q.q[2], acc);
-        acc = mfma(conv8<F>(x1[2], x1[3]), Q.q[3], acc);
-        C[rt] = acc;
-    }
-
-    // value words of this lane: w[2][8]; column tile ct uses w[0][ct] and
-    // w[1][ct] (G = 32: the slot halves 0-3 and 4-7 of the same record;
-    // G = 16: slots 0-3 of records 0 and 1)
-    uint32_t w[2][8];
-    if (G == 32) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const u32x4 v = lds_read<u32x4>(buf + S::VC + 1024 * k + 16 * lane);
-            w[0][2 * k] = v[0];
-            w[1][2 * k] = v[1];
-            w[0][2 * k + 1] = v[2];
-            w[1][2 * k + 1] = v[3];
-        }
-    } else {
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const u32x4 v = lds_read<u32x4>(buf + S::VC + 1024 * (2 * r + hf) + 16 * lane);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) w[r][4 * hf + e] = v[e];
-            }
-    }
-
-    // slot k = 4rt + i <-> token 16rt + 4g + i
-    float x[8], vs[8], vz[8];
-    bool valid[8];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        const int rec = S::NR == 2 ? rt : 0;
-        float ks4[4], kz4[4], vs4[4], vz4[4];
-        if (F == kFmtInt8) {
-            // the record's tables: per lane group g, SPT scales then SPT zeros
-            const lds_u8* km = buf + S::META + rec * S::MREC + g * 4 * SPT;
-            const lds_u8* vm = km + 4 * G;
-            const int s0 = S::NR == 2 ? 0 : 4 * rt;   // first slot of this row tile
-            const u32x2 a = lds_read<u32x2>(km + 2 * s0);
-            const u32x2 bz = lds_read<u32x2>(km + 2 * SPT + 2 * s0);
-            const u32x2 cv = lds_read<u32x2>(vm + 2 * s0);
-            const u32x2 dz = lds_read<u32x2>(vm + 2 * SPT + 2 * s0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ks4[i] = h2f((a[i >> 1] >> (16 * (i & 1))) & 0xffffu);
-                kz4[i] = h2f((bz[i >> 1] >> (16 * (i & 1))) & 0xffffu);
-                vs4[i] = h2f((cv[i >> 1] >> (16 * (i & 1))) & 0xffffu);
-                vz4[i] = h2f((dz[i >> 1] >> (16 * (i & 1))) & 0xffffu);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int k = 4 * rt + i;
-            if (F == kFmtInt8) {
-                x[k] = fmaf(ks4[i], C[rt][i], fmaf(128.0f, ks4[i], kz4[i]) * qsum);
-                vs[k] = vs4[i];
-                vz[k] = fmaf(128.0f, vs4[i], vz4[i]);
-            } else {
-                x[k] = C[rt][i];
-                vs[k] = vscl;
-                vz[k] = 0.0f;
-            }
-            valid[k] = S::NR == 1 || ((has >> rec) & 1);
-        }
-    }
-    softmax_and_values<LP>(A, x, vs, vz, valid, sl2, lane, [&](int ct) -> h8 { return conv8<F>(w[0][ct], w[1][ct]); });
-}
-
-// Ring slot of token t0 + r (0 <= r < 32) given slot0 = t0 % ring; ring >= 16.
-__device__ __forceinline__ int ring_slot(int slot0, int r, int ring) {
-    int s = slot0 + r;
-    s -= s >= ring ? ring : 0;
-    s -= s >= ring ? ring : 0;
-    return s;
-}
-
-// One 32-token unit of the fp16 residual ring: tokens t0 .. t0+31 (< n).
-// Keys and query are exact fp16, so the key product needs one part (LP: the
-// high-limb columns carry it, the low-limb columns add zero).  The value rows
-// go straight to LDS (rows 0-15 to sva, 16-31 to svb, 256 bytes each; rows at
-// or past n read as zeros), from where each lane gathers its operand columns.
-template <bool LP, bool RP>
-__device__ __forceinline__ void process_residual(WaveAcc& A, const Layout& L, const kvq_cache& c, long sh, int t0,
-                                                 int n, const QOps& Q, float sl2, int lane, lds_u8* sva,
-                                                 lds_u8* svb, RopeLds* R, int wave) {
-    const int g = lane >> 4, n16 = lane & 15;
-    const int slot0 = t0 % L.ring;
-    {
-        const uint8_t* vbase = (const uint8_t*)c.v_res + sh * L.ring * kD * 2;
-        const u32x4 vd = record_desc(vbase, L.ring * kD * 2);
-        __builtin_amdgcn_s_waitcnt(kLgkmZero);   // earlier reads of these buffers returned
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = 4 * i + (lane >> 4);
-            const int off = t0 + r < n ? ring_slot(slot0, r, L.ring) * (kD * 2) + 16 * n16 : 0x40000000;
-            lds_load16(vd, i < 4 ? sva + 1024 * i : svb + 1024 * (i - 4), off);
-        }
-    }
-    const half_t* kr = (const half_t*)c.k_res + sh * L.ring * kD;
-    f4 C[2];
-    if constexpr (RP) {
-        rope_unit_base(R, wave, lane, t0);
-        rope_key_tiles(R, wave, lane, Q, C, [&](int rt, int j, float* x) {
-            const int r = 16 * rt + n16;
-            const uint32_t keep = t0 + r < n ? 0xffffffffu : 0u;
-            const uint4* row =
-                (const uint4*)(kr + (long)(t0 + r < n ? ring_slot(slot0, r, L.ring) : slot0) * kD + 32 * g);
-            uint4 w = row[j];
-            w.x &= keep; w.y &= keep; w.z &= keep; w.w &= keep;
-            const h8 k8 = words_h8(w);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = (float)k8[e];
-        });
-    }
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        const int r = 16 * rt + n16;
-        f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
-        const uint32_t keep = t0 + r < n ? 0xffffffffu : 0u;
-        const uint4* row = (const uint4*)(kr + (long)(t0 + r < n ? ring_slot(slot0, r, L.ring) : slot0) * kD + 32 * g);
-        if constexpr (RP) {
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint4 w = row[j];
-                w.x &= keep; w.y &= keep; w.z &= keep; w.w &= keep;
-                acc = mfma(words_h8(w), Q.q[j], acc);
-            }
-            C[rt] = LP && (lane & 8) ? f4{0.0f, 0.0f, 0.0f, 0.0f} : acc;
-        }
-    }
-    float x[8], vs[8], vz[8];
-    bool valid[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        x[k] = LP && !RP ? add_limb_partner(C[k >> 2][k & 3]) : C[k >> 2][k & 3];
-        vs[k] = 1.0f;
-        vz[k] = 0.0f;
-        valid[k] = t0 + (k >> 2) * 16 + 4 * g + (k & 3) < n;
-    }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the value rows are in LDS
-    wave_sync();
-    softmax_and_values<LP>(A, x, vs, vz, valid, sl2, lane, [&](int ct) -> h8 {
-        h8 b;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const lds_u8* rows = (k >> 2) ? svb : sva;
-            b[k] = __builtin_bit_cast(_Float16, lds_read<uint16_t>(rows + (4 * g + (k & 3)) * (kD * 2) +
-                                                                   (16 * ct + n16) * 2));
-        }
-        return b;
-    });
-}
-
-// A wave's [16][128] fp32 accumulator image after the unit loop.
-__device__ __forceinline__ float* wave_acc(uint8_t* stage_a, uint8_t* stage_b, int w, int pitch) {
-    return (float*)((w < 2 ? stage_a : stage_b) + (w & 1) * 16 * kD * 4);
-}
-
-// Wave priority from the share of this wave's units still to do (3: more
-// than 3/4 left ... 0: under 1/4).  Waves issue oldest-first, so without
-// this the first workgroup placed on a CU runs ahead and the CU spends the
-// end of the kernel with few waves; lagging waves now win arbitration and
-// the workgroups of a CU finish close together.
-__device__ __forceinline__ void set_progress_prio(int left, int total) {
-    const int lvl = (4 * left - 1) / total;   // 0..3 for 1 <= left <= total
-    if (lvl >= 3) __builtin_amdgcn_s_setprio(3);
-    else if (lvl == 2) __builtin_amdgcn_s_setprio(2);
-    else if (lvl == 1) __builtin_amdgcn_s_setprio(1);
-    else __builtin_amdgcn_s_setprio(0);
-}
-
-// 32-token units of sequence b: its quantized groups first (G = 16: two
-// records per unit), then its fp16 residual tokens.  Counters written by this
-// library satisfy 0 <= nq <= n <= nq + ring; the clamps keep any other value
-// inside the records and the ring.
-// In the flattened work split a residual unit counts kResCost times a
-// quantized one (its fp16 rows are gathered with plain loads, without the
-// staged prefetch): `cost` is the stream's length in those terms.
-constexpr int kResCost = 3;
-struct SeqUnits {
-    int nq, n, ngroups, uq, units, cost;
-};
-__device__ __forceinline__ SeqUnits seq_units(const Layout& L, const kvq_cache& c, int b) {
-    SeqUnits u;
-    u.nq = max(c.n_quant[b], 0);
-    u.n = min(max(c.n_tokens[b], u.nq), u.nq + L.ring);
-    u.ngroups = u.nq / L.G;
-    u.uq = (u.ngroups * L.G + 31) / 32;
-    u.units = u.uq + (u.n - u.nq + 31) / 32;
-    u.cost = u.uq + kResCost * (u.units - u.uq);
-    return u;
-}
-// First unit whose cost position is >= x (a unit belongs to the workgroup
-// that holds its first cost position).
-__device__ __forceinline__ int unit_at(const SeqUnits& u, int x) {
-    return x <= u.uq ? x : u.uq + (x - u.uq + kResCost - 1) / kResCost;
-}
-
-// Stage layout, unit issue and unit processing of a format.
-template <int G, int KB, int VB, int F>
-using StageT = typename std::conditional<F == kFmtKivi || F == kFmtRope, Stage<G, KB, VB>, Stage8<G, F>>::type;
-
-template <int G, int KB, int VB, int F, bool PG>
-__device__ __forceinline__ uint32_t issue_any(lds_u8* buf, const Layout& L, const kvq_cache& c, int b, int h,
-                                              int unit, int ngroups, int lane) {
-    if constexpr (F == kFmtKivi || F == kFmtRope) return issue_unit<G, KB, VB, PG>(buf, L, c, b, h, unit, ngroups, lane);
-    else return issue_unit8<G, F, PG>(buf, L, c, b, h, unit, ngroups, lane);
-}
-
-template <int G, int KB, int VB, int F, bool LP>
-__device__ __forceinline__ void process_any(const lds_u8* buf, uint32_t has, WaveAcc& A, const QOps& Q, float sl2,
-                                            float qsum, float vscl, int lane, RopeLds* R, int wave, int t0) {
-    if constexpr (F == kFmtKivi || F == kFmtRope)
-        process_unit<G, KB, VB, LP, F == kFmtRope>(buf, has, A, Q, sl2, lane, R, wave, t0);
-    else process_unit8<G, F, LP>(buf, has, A, Q, sl2, qsum, vscl, lane);
-}
-
-// Units [lo, hi) of stream (b, h) by the four waves of the workgroup (wave w
-// takes lo + w, lo + w + 4, ...), combined into one partial result (heads
-// < gq: output[128] unnormalised, running max in log2 units, weight sum) at
-// `part`.  Called by every thread of the workgroup.
-template <int G, int KB, int VB, int F, bool LP, bool PG>
-__device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_b, float (*wm)[16], float (*wl)[16],
-                                               float (*wpz)[16], const Layout& L, const kvq_cache& c,
-                                               const half_t* __restrict__ q, float sl2, int gq, int b, int h,
-                                               const SeqUnits& su, int lo, int hi, float* __restrict__ part,
-                                               int lane, int wave, RopeLds* R) {
-    using S = StageT<G, KB, VB, F>;
-    // The lane index, produced afresh: per-lane addresses derived from it are
-    // formed here, once per segment, instead of being hoisted out of the
-    // segment loop and held (or spilled) across every unit loop.
-    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
-    const int g = lane >> 4, n16 = lane & 15;
-    const int tid = wave * 64 + lane;
-    const int Hq = L.H * gq;
-    const long sh = (long)b * L.H + h;
-
-    QOps Q;
-    {
-        // column n: head n (LP: head n%8, high limb for n < 8, low limb above)
-        const int hd = LP ? (n16 & 7) : n16;
-        const bool hv = hd < gq;
-        const uint4* qp = (const uint4*)(q + ((long)b * Hq + h * gq + (hv ? hd : 0)) * kD + 32 * g);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Q.q[j] = words_h8(hv ? qp[j] : make_uint4(0, 0, 0, 0));
-        // The unit loop's loads are invisible to the compiler's wait counting:
-        // retire these here so that it places no wait on them inside the loop.
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    }
-    // 8-bit formats: sum_c q_c of the lane's head (INT8), the kv head's
-    // static scales (FP8; the key scale joins the logit scale)
-    float qsum = 0.0f, vscl = 0.0f, sl2q = sl2;
-    if (F == kFmtInt8) {
-        float t = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) t += (float)Q.q[j][e];
-        qsum = group_sum(t);
-    } else if (F == kFmtFp8) {
-        sl2q = sl2 * c.k_scale[h];
-        vscl = c.v_scale[h];
-    }
-    WaveAcc A;
-    acc_init(A);
-
-    {
-        const int q1 = min(hi, su.uq);
-        const int ntot = max(1, (q1 - (lo + wave) + kWaves - 1) / kWaves);   // this wave's units
-        int u = lo + wave;
-        if (u < q1) {
-            // Direct-to-LDS loads: unit u is staged in one buffer while the
-            // previous one is processed from the other.  The waits are explicit
-            // (vmcnt counts this wave's outstanding loads, in issue order).
-            lds_u8* const sa = (lds_u8*)(stage_a + wave * S::PITCH);
-            lds_u8* const sb = (lds_u8*)(stage_b + wave * S::PITCH);
-            uint32_t ha = issue_any<G, KB, VB, F, PG>(sa, L, c, b, h, u, su.ngroups, lane), hb = 0;
-            for (;;) {
-                if (u + kWaves < q1) {
-                    __builtin_amdgcn_s_waitcnt(kLgkmZero);   // last reads of sb returned
-                    hb = issue_any<G, KB, VB, F, PG>(sb, L, c, b, h, u + kWaves, su.ngroups, lane);
-                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::LOADS));
-                } else {
-                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-                }
-                wave_sync();
-                set_progress_prio((q1 - u + kWaves - 1) / kWaves, ntot);
-                process_any<G, KB, VB, F, LP>(sa, ha, A, Q, sl2q, qsum, vscl, lane, R, wave, 32 * u);
-                u += kWaves;
-                if (u >= q1) break;
-                if (u + kWaves < q1) {
-                    __builtin_amdgcn_s_waitcnt(kLgkmZero);
-                    ha = issue_any<G, KB, VB, F, PG>(sa, L, c, b, h, u + kWaves, su.ngroups, lane);
-                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::LOADS));
-                } else {
-                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-                }
-                wave_sync();
-                set_progress_prio((q1 - u + kWaves - 1) / kWaves, ntot);
-                process_any<G, KB, VB, F, LP>(sb, hb, A, Q, sl2q, qsum, vscl, lane, R, wave, 32 * u);
-                u += kWaves;
-                if (u >= q1) break;
-            }
-        }
-    }
-    for (int u = lo + wave; u < hi; u += kWaves)
-        if (u >= su.uq)
-            process_residual<LP, F == kFmtRope>(A, L, c, sh, su.nq + 32 * (u - su.uq), su.n, Q, sl2, lane,
-                                                (lds_u8*)(stage_a + wave * S::PITCH),
-                                                (lds_u8*)(stage_b + wave * S::PITCH), R, wave);
-    __builtin_amdgcn_s_setprio(0);
-
-    // Wave results -> LDS: totals over the lane groups, accumulators by head.
-    // The accumulators reuse the stage buffers: every wave has consumed its
-    // staged units and has no load in flight once all have passed the barrier.
-    const float lt = group_sum(A.l);
-    const float pzt = group_sum(A.pz);
-    __syncthreads();
-    if (lane < 16) {
-        wm[wave][lane] = A.m;
-        wl[wave][lane] = lt;
-        wpz[wave][lane] = pzt;
-    }
-    {
-        float* wacc = wave_acc(stage_a, stage_b, wave, S::PITCH);
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) wacc[(4 * g + i) * kD + 16 * ct + n16] = A.acc[ct][i];
-    }
-    __syncthreads();
-
-    // Workgroup partial (heads < gq) -> workspace.
-    for (int idx = tid; idx < gq * kD; idx += 256) {
-        const int hh = idx >> 7, ch = idx & (kD - 1);
-        float M = kNegInf;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w][hh]);
-        float o = 0.0f, Ls = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float mw = wm[w][hh];
-            const float f = mw == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-            // LP: rows hh and hh+8 hold the high- and low-limb sums of head hh
-            const float* wacc = wave_acc(stage_a, stage_b, w, S::PITCH);
-            const float a = LP ? wacc[hh * kD + ch] + wacc[(hh + 8) * kD + ch] : wacc[hh * kD + ch];
-            o += (a + wpz[w][hh]) * f;
-            Ls += wl[w][hh] * f;
-        }
-        part[hh * kPart + ch] = o;
-        if (ch == 0) {
-            part[hh * kPart + kD] = M;
-            part[hh * kPart + kD + 1] = Ls;
-        }
-    }
-    __syncthreads();   // the stage buffers are staged into again by the next segment
-}
-
-// Decode attention over the whole batch as one flattened sequence of work:
-// sequence b contributes H streams (b, h) of cost_b each (its units, residual
-// ones weighted kResCost), in (b, h) order, T in all, and workgroup w takes
-// positions [w T / nwg, (w+1) T / nwg), a unit going to the workgroup holding
-// its first position, whatever the sequence lengths (ragged batches and long
-// single streams are balanced alike).  It writes one partial per stream segment it covers, at
-// slot w + s for stream s (unique: along the workgroup order the covered
-// streams never decrease).  The first workgroup of each stream records the
-// stream's flattened start, and workgroup 0 records T; from these the merge
-// finds the stream's workgroups.
-// Waves per SIMD each instantiation is compiled for: four (at most 128
-// registers) where that fits without spilling, else three.  A kernel that
-// spills runs with scratch memory and far slower; the build rejects any
-// attention kernel that uses scratch, so this table is checked.  Four waves
-// fit the limb-packed kernels with INT2 values; without limb packing the
-// separate high/low query operands take 16 more registers, INT4 values more
-// than INT2 ones.  (Three waves lose little where the kernel waits on HBM.)
-// The 8-bit formats stage twice the bytes per unit: their LDS allows two
-// workgroups per CU, two waves per SIMD.
-// Pre-RoPE keys take registers for the rotation: three waves.
-constexpr int attn_waves(int G, int KB, int VB, int F, bool LP, bool PG) {
-    return F == kFmtRope ? 3 : F != kFmtKivi ? 2 : LP && VB == 2 && !(G == 16 && KB == 2) ? 4 : 3;
-}
-
-template <int G, int KB, int VB, int F, bool LP, bool PG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves(G, KB, VB, F, LP, PG)))) void attn_kernel(
-    Layout L, kvq_cache c, const half_t* __restrict__ q, float sl2, float* __restrict__ ws, int gq, int nwg,
-    long meta_off) {
-    using S = StageT<G, KB, VB, F>;
-    // Two stage buffers per wave (ping-pong), in two arrays: the compiler
-    // treats them as separate objects.  After the unit loop the same memory
-    // holds the waves' accumulators (waves 0-1 in stage_a, 2-3 in stage_b).
-    __shared__ __attribute__((aligned(16))) uint8_t stage_a[kWaves * S::PITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t stage_b[kWaves * S::PITCH];
-    __shared__ float wm[kWaves][16], wl[kWaves][16], wpz[kWaves][16];
-    __shared__ int wsum[kWaves];
-    __shared__ int first[2];   // sequence holding unit w T / nwg, flattened start of that sequence
-    const int w = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
-    RopeLds* R = nullptr;
-    if constexpr (F == kFmtRope) {
-        __shared__ __attribute__((aligned(16))) RopeLds rope_lds;
-        rope_setup(rope_lds, L.rope_theta, tid);
-        R = &rope_lds;
-    }
-
-    // Units per sequence, prefix over the batch (each thread a run of
-    // consecutive sequences, then a scan over the threads).  Flattened
-    // positions fit in 32 bits (the host rejects larger batches).
-    const int per = (L.B + 255) / 256;
-    const int b0 = min(tid * per, L.B), b1 = min(b0 + per, L.B);
-    int mine = 0;
-    for (int b = b0; b < b1; ++b) mine += L.H * seq_units(L, c, b).cost;
-    int incl = mine;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-    }
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    int T = 0, below = 0;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-        const int v = wsum[i];
-        below += i < wave ? v : 0;
-        T += v;
-    }
-    T = __builtin_amdgcn_readfirstlane(T);
-    const int excl = below + incl - mine;
-    const int start = __builtin_amdgcn_readfirstlane((int)((long)w * T / nwg));
-    const int end = __builtin_amdgcn_readfirstlane((int)((long)(w + 1) * T / nwg));
-    if (start < end && excl <= start && start < excl + mine) {
-        int p = excl;
-        for (int b = b0; b < b1; ++b) {
-            const int f = L.H * seq_units(L, c, b).cost;
-            if (start < p + f) {
-                first[0] = b;
-                first[1] = p;
-                break;
-            }
-            p += f;
-        }
-    }
-    __syncthreads();
-    int* meta = (int*)((uint8_t*)ws + meta_off);
-    if (w == 0 && tid == 0) meta[0] = T;
-    if (start >= end) return;   // fewer units than workgroups
-
-    int b = __builtin_amdgcn_readfirstlane(first[0]);
-    const int pb = __builtin_amdgcn_readfirstlane(first[1]);
-    SeqUnits su = seq_units(L, c, b);
-    // (the division runs on the vector ALU: bring the result back to a scalar
-    // register, or everything derived from it becomes per-lane)
-    int h = __builtin_amdgcn_readfirstlane((start - pb) / su.cost);
-    int ps = pb + h * su.cost;   // flattened start of stream (b, h)
-    for (;;) {
-        const int lo = __builtin_amdgcn_readfirstlane(max(start - ps, 0));
-        const int hi = __builtin_amdgcn_readfirstlane(min(end - ps, su.cost));
-        const int s = b * L.H + h;
-        if (lo == 0 && wave == 0) {
-            // the merge finds the stream's workgroups from its flattened start
-            int l0;
-            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l0));
-            if (l0 == 0) meta[1 + s] = ps;
-        }
-        attend_segment<G, KB, VB, F, LP, PG>(stage_a, stage_b, wm, wl, wpz, L, c, q, sl2, gq, b, h, su,
-                                          unit_at(su, lo), unit_at(su, hi), ws + ((long)w + s) * gq * kPart,
-                                          lane, wave, R);
-        if (ps + hi >= end) break;
-        // next stream that has work (x < end <= T guarantees one)
-        ps += su.cost;
-        if (++h == L.H) {
-            h = 0;
-            do su = seq_units(L, c, ++b);
-            while (su.units == 0);
-        }
-    }
-}
+KVQ_ALL_FAMILIES(KVQ_DECLARE_FAMILY)
 
 // Workgroup w of nwg covers units [w T / nwg, (w + 1) T / nwg): empty when
 // there are fewer units than workgroups; an empty one writes no partial.
@@ -1296,64 +154,23 @@ __global__ __launch_bounds__(256) void attn_merge_rows_kernel(Layout L, kvq_cach
     orow[lane] = Ls > 0.0f ? make_float2(acc.x / Ls, acc.y / Ls) : make_float2(0.0f, 0.0f);
 }
 
-// Resident attention workgroups on the current device: CUs x workgroups per
-// CU for this instantiation (from its register and LDS footprint).  Falls
-// back to 256 CUs x 3 when no device is visible (host-only size queries).
-template <int G, int KB, int VB, int F, bool LP, bool PG>
-static int attn_slots_for() {
-    static int cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256 * 3;
-    if (cached[dev]) return cached[dev];
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)attn_kernel<G, KB, VB, F, LP, PG>, 256, 0) !=
-            hipSuccess || per_cu <= 0)
-        per_cu = 3;
-    (void)hipGetLastError();
-    cached[dev] = cus * per_cu;
-    return cached[dev];
-}
-
-// Limb packing: with at most 8 query heads per kv head, the high and low
-// fp16 parts of q*s and p*s share one 16-column product.
-static inline bool limb_packed(int gq) { return gq <= 8; }
-
 // Instantiation key of the attention kernels: as layout_key, with the low-bit
 // format's pre-RoPE variant as format kFmtRope.
 static inline int attn_key(const Layout& L) {
-    return layout_key(L) + (L.rope_theta > 0.0f ? (kFmtRope - L.fmt) * 10000 : 0);
+    if (L.fmt != kFmtKivi) return layout_key(L);
+    const bool rp = L.rope_theta > 0.0f, cb = L.grid == KVQ_GRID_NORMAL_QUANTILE;
+    const int f = rp ? (cb ? kFmtRopeCb : kFmtRope) : (cb ? kFmtKiviCb : kFmtKivi);
+    return layout_key(L) + f * 10000;
 }
 
-template <bool LP, bool PG>
-static int attn_slots_lp(const Layout& L) {
-    switch (attn_key(L)) {
-        case 1622: return attn_slots_for<16, 2, 2, kFmtKivi, LP, PG>();
-        case 1624: return attn_slots_for<16, 2, 4, kFmtKivi, LP, PG>();
-        case 1642: return attn_slots_for<16, 4, 2, kFmtKivi, LP, PG>();
-        case 1644: return attn_slots_for<16, 4, 4, kFmtKivi, LP, PG>();
-        case 3222: return attn_slots_for<32, 2, 2, kFmtKivi, LP, PG>();
-        case 3224: return attn_slots_for<32, 2, 4, kFmtKivi, LP, PG>();
-        case 3242: return attn_slots_for<32, 4, 2, kFmtKivi, LP, PG>();
-        case 11688: return attn_slots_for<16, 8, 8, kFmtInt8, LP, PG>();
-        case 13288: return attn_slots_for<32, 8, 8, kFmtInt8, LP, PG>();
-        case 21688: return attn_slots_for<16, 8, 8, kFmtFp8, LP, PG>();
-        case 23288: return attn_slots_for<32, 8, 8, kFmtFp8, LP, PG>();
-        case 31622: return attn_slots_for<16, 2, 2, kFmtRope, LP, PG>();
-        case 31624: return attn_slots_for<16, 2, 4, kFmtRope, LP, PG>();
-        case 31642: return attn_slots_for<16, 4, 2, kFmtRope, LP, PG>();
-        case 31644: return attn_slots_for<16, 4, 4, kFmtRope, LP, PG>();
-        case 33222: return attn_slots_for<32, 2, 2, kFmtRope, LP, PG>();
-        case 33224: return attn_slots_for<32, 2, 4, kFmtRope, LP, PG>();
-        case 33242: return attn_slots_for<32, 4, 2, kFmtRope, LP, PG>();
-        case 33244: return attn_slots_for<32, 4, 4, kFmtRope, LP, PG>();
-        default: return attn_slots_for<32, 4, 4, kFmtKivi, LP, PG>();
-    }
-}
 static int attn_slots(const Layout& L, int gq) {
-    if (L.paged) return limb_packed(gq) ? attn_slots_lp<true, true>(L) : attn_slots_lp<false, true>(L);
-    return limb_packed(gq) ? attn_slots_lp<true, false>(L) : attn_slots_lp<false, false>(L);
+    switch (attn_key(L)) {
+#define KVQ_SLOTS_CASE(GG, KB, VB, FF) \
+    case FF * 10000 + GG * 100 + KB * 10 + VB: return attn_family_slots<GG, KB, VB, FF>(L, gq);
+        KVQ_ALL_FAMILIES(KVQ_SLOTS_CASE)
+#undef KVQ_SLOTS_CASE
+        default: return 256 * 3;
+    }
 }
 
 AttnPlan plan_attention(const Layout& L, int num_q_heads) {
@@ -1386,47 +203,13 @@ hipError_t launch_attention_partials(const Layout& L, const AttnPlan& P, const k
                                      int num_q_heads, float scale, void* ws, hipStream_t s) {
     const int gq = num_q_heads / L.H;
     const float sl2 = scale * kLog2e;
-#define KVQ_ATT3(GG, KB, VB, FF, LP, PG)                                                                   \
-    hipLaunchKernelGGL((attn_kernel<GG, KB, VB, FF, LP, PG>), dim3(P.nwg), dim3(256), 0, s, L, c, q, sl2,    \
-                       (float*)ws, gq, P.nwg, (long)P.meta_off)
-#define KVQ_ATT2(GG, KB, VB, FF, LP)         \
-    if (L.paged)                              \
-        KVQ_ATT3(GG, KB, VB, FF, LP, true);   \
-    else                                      \
-        KVQ_ATT3(GG, KB, VB, FF, LP, false)
-#define KVQ_ATT(GG, KB, VB, FF)              \
-    if (limb_packed(gq)) {                    \
-        KVQ_ATT2(GG, KB, VB, FF, true);       \
-    } else {                                  \
-        KVQ_ATT2(GG, KB, VB, FF, false);      \
-    }
     switch (attn_key(L)) {
-        case 1622: KVQ_ATT(16, 2, 2, kFmtKivi); break;
-        case 1624: KVQ_ATT(16, 2, 4, kFmtKivi); break;
-        case 1642: KVQ_ATT(16, 4, 2, kFmtKivi); break;
-        case 1644: KVQ_ATT(16, 4, 4, kFmtKivi); break;
-        case 3222: KVQ_ATT(32, 2, 2, kFmtKivi); break;
-        case 3224: KVQ_ATT(32, 2, 4, kFmtKivi); break;
-        case 3242: KVQ_ATT(32, 4, 2, kFmtKivi); break;
-        case 3244: KVQ_ATT(32, 4, 4, kFmtKivi); break;
-        case 11688: KVQ_ATT(16, 8, 8, kFmtInt8); break;
-        case 13288: KVQ_ATT(32, 8, 8, kFmtInt8); break;
-        case 21688: KVQ_ATT(16, 8, 8, kFmtFp8); break;
-        case 23288: KVQ_ATT(32, 8, 8, kFmtFp8); break;
-        case 31622: KVQ_ATT(16, 2, 2, kFmtRope); break;
-        case 31624: KVQ_ATT(16, 2, 4, kFmtRope); break;
-        case 31642: KVQ_ATT(16, 4, 2, kFmtRope); break;
-        case 31644: KVQ_ATT(16, 4, 4, kFmtRope); break;
-        case 33222: KVQ_ATT(32, 2, 2, kFmtRope); break;
-        case 33224: KVQ_ATT(32, 2, 4, kFmtRope); break;
-        case 33242: KVQ_ATT(32, 4, 2, kFmtRope); break;
-        case 33244: KVQ_ATT(32, 4, 4, kFmtRope); break;
+#define KVQ_LAUNCH_CASE(GG, KB, VB, FF) \
+    case FF * 10000 + GG * 100 + KB * 10 + VB: return launch_attn_family<GG, KB, VB, FF>(L, P, c, q, gq, sl2, ws, s);
+        KVQ_ALL_FAMILIES(KVQ_LAUNCH_CASE)
+#undef KVQ_LAUNCH_CASE
         default: return hipErrorInvalidValue;
     }
-#undef KVQ_ATT
-#undef KVQ_ATT2
-#undef KVQ_ATT3
-    return hipGetLastError();
 }
 
 hipError_t launch_attention_merge(const Layout& L, const AttnPlan& P, const kvq_cache& c, int num_q_heads,

@@ -88,6 +88,24 @@ __device__ __forceinline__ uint32_t fp8_code2(float x0, float x1, float inv) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;   // bytes: a, b
 }
 
+// Normal-quantile codebook: code of t = (x - z) * inv (grid steps) as the
+// nearest level, counting the midpoints below t; a tie at the midpoint of
+// levels k and k + 1 goes to the even one of the two (k even: '>', odd: '>=').
+template <int Q>
+__device__ __forceinline__ uint32_t cb_code(float t, const float (&mid)[15]) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < Q; ++k) c += (k & 1) ? (t >= mid[k] ? 1u : 0u) : (t > mid[k] ? 1u : 0u);
+    return c;
+}
+
+// Level of code c (grid steps) from a codebook byte table (byte c = F * L_c).
+__device__ __forceinline__ float cb_level(const uint32_t (&lut)[4], uint32_t c, int bits) {
+    const uint32_t w = c < 4 ? lut[0] : c < 8 ? lut[1] : c < 12 ? lut[2] : lut[3];
+    const float invF = bits == 2 ? 1.0f / 64.0f : 1.0f / 16.0f;
+    return (float)((w >> (8 * (c & 3))) & 0xffu) * invF;
+}
+
 // ---------------------------------------------------------------------------
 // Positions inside a record (see kvq_internal.h for the layout).
 // ---------------------------------------------------------------------------

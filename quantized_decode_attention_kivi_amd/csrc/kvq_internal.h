@@ -58,6 +58,9 @@ constexpr int kFmtFp8 = KVQ_FORMAT_FP8_E4M3;
 struct Layout {
     int fmt;
     float rope_theta;                             // > 0: keys are pre-RoPE, rotated on read
+    int grid;                                     // KVQ_GRID_*
+    uint32_t klut[4], vlut[4];                    // codebook: byte k = F_b * L_k (key / value bits)
+    float kmid[15], vmid[15];                     // codebook: midpoints of consecutive levels, grid steps
     int B, H, kbits, vbits, G, R, ring;
     int paged, num_blocks, max_blocks, groups;   // groups: record slots per sequence
     int capacity;                                 // max tokens a sequence may hold
@@ -73,6 +76,10 @@ __host__ __device__ inline int num_quantized(int n, int G, int R) {
     int over = n - R;
     return over <= 0 ? 0 : G * (over / G);
 }
+
+// Codebook levels of b bits (2 or 4) in 1/F_b grid steps, F_b = 64 or 16:
+// levels16[k] = F_b * L_k; returns F_b (0 for other widths).
+int codebook_levels16(int bits, int* levels16);
 
 // Instantiation key of a layout: format * 10000 + G * 100 + kbits * 10 + vbits.
 inline int layout_key(const Layout& L) { return L.fmt * 10000 + L.G * 100 + L.kbits * 10 + L.vbits; }

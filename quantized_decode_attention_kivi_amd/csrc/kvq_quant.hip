@@ -18,10 +18,23 @@ struct QuantSmem {
     uint8_t vcode[G][kD];             // value codes before packing
 };
 
+// Code of x on the set's grid: uniform (rint), or the normal-quantile
+// codebook's nearest level (CB; mid: its midpoints).
+template <bool CB, int BITS>
+__device__ __forceinline__ uint32_t code_of(float x, float z, float inv, const float (&mid)[15]) {
+    if constexpr (CB) {
+#pragma clang fp contract(off)
+        return cb_code<(1 << BITS) - 1>((x - z) * inv, mid);
+    } else {
+        return quant_code(x, z, inv, (float)((1 << BITS) - 1));
+    }
+}
+
 // Quantize G consecutive fp16 rows of keys (ksrc) and values (vsrc) into one
 // record.  Called by all 256 threads of a workgroup.  Thread (ts = tid/16,
-// cg = tid%16) holds channels 8cg..8cg+7 of tokens ts, ts+16, ...
-template <int G, int KB, int VB>
+// cg = tid%16) holds channels 8cg..8cg+7 of tokens ts, ts+16, ...  CB: the
+// normal-quantile codebook grid instead of the uniform one.
+template <int G, int KB, int VB, bool CB>
 __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* __restrict__ ksrc,
                                const half_t* __restrict__ vsrc, uint8_t* __restrict__ rec) {
     constexpr int NT = G / 16;
@@ -112,7 +125,7 @@ __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* 
         uint32_t w = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const uint32_t q = quant_code(kx[j][e], kzr[e], kir[e], kq);
+            const uint32_t q = code_of<CB, KB>(kx[j][e], kzr[e], kir[e], L.kmid);
             w |= q << (KB == 4 ? code_bit(4, e) : code_bit(2, e + 8 * (cg & 1)));
         }
         if (KB == 4) {
@@ -125,8 +138,8 @@ __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* 
         uint32_t v0 = 0, v1 = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            v0 |= quant_code(vx[j][e], pv[j].z, pv[j].inv, vq) << (8 * e);
-            v1 |= quant_code(vx[j][e + 4], pv[j].z, pv[j].inv, vq) << (8 * e);
+            v0 |= code_of<CB, VB>(vx[j][e], pv[j].z, pv[j].inv, L.vmid) << (8 * e);
+            v1 |= code_of<CB, VB>(vx[j][e + 4], pv[j].z, pv[j].inv, L.vmid) << (8 * e);
         }
         *(uint2*)&sm.vcode[t][8 * cg] = make_uint2(v0, v1);
     }
@@ -253,7 +266,8 @@ template <int G, int KB, int VB, int F>
 __device__ __forceinline__ void quantize_any(QuantSmem<G>& sm, const Layout& L, const kvq_cache& c, int h,
                                              const half_t* ksrc, const half_t* vsrc, uint8_t* rec) {
     if (F == kFmtKivi) {
-        quantize_group<G, KB, VB>(sm, L, ksrc, vsrc, rec);
+        if (L.grid == KVQ_GRID_NORMAL_QUANTILE) quantize_group<G, KB, VB, true>(sm, L, ksrc, vsrc, rec);
+        else quantize_group<G, KB, VB, false>(sm, L, ksrc, vsrc, rec);
     } else {
         const float kinv = F == kFmtFp8 ? fp8_inv_scale(c.k_scale[h]) : 0.0f;
         const float vinv = F == kFmtFp8 ? fp8_inv_scale(c.v_scale[h]) : 0.0f;
@@ -387,10 +401,13 @@ __global__ __launch_bounds__(256) void dequantize_kernel(Layout L, kvq_cache c, 
                 vv = fp8_value(vcode_at(L, rec, tg, ch)) * c.v_scale[h];
             } else if (rec) {
                 const bool tok = L.fmt == kFmtInt8;   // per-token key scale and zero
-                kv = fmaf((float)kcode_at(L, rec, tg, ch),
+                const bool cb = L.grid == KVQ_GRID_NORMAL_QUANTILE;
+                const uint32_t kcd = kcode_at(L, rec, tg, ch), vcd = vcode_at(L, rec, tg, ch);
+                kv = fmaf(cb ? cb_level(L.klut, kcd, L.kbits) : (float)kcd,
                           h2f(tok ? ktok_scale_bits(L, rec, tg) : kscale_bits(L, rec, ch)),
                           h2f(tok ? ktok_zero_bits(L, rec, tg) : kzero_bits(L, rec, ch)));
-                vv = fmaf((float)vcode_at(L, rec, tg, ch), h2f(vscale_bits(L, rec, tg)), h2f(vzero_bits(L, rec, tg)));
+                vv = fmaf(cb ? cb_level(L.vlut, vcd, L.vbits) : (float)vcd, h2f(vscale_bits(L, rec, tg)),
+                          h2f(vzero_bits(L, rec, tg)));
             }
         } else if (t < n) {
             const long row = ((long)sh * L.ring + (t % L.ring)) * kD + ch;

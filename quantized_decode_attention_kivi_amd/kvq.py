@@ -25,15 +25,16 @@ _lib = None
 
 KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ECAPACITY, KVQ_EHIP = range(5)
 HEAD_DIM = 128
-# cache formats (KVQ_FORMAT_*)
+# cache formats (KVQ_FORMAT_*) and level grids (KVQ_GRID_*)
 FORMAT_KIVI, FORMAT_INT8, FORMAT_FP8_E4M3 = 0, 1, 2
+GRID_UNIFORM, GRID_NORMAL_QUANTILE = 0, 1
 
 
 class kvq_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_seqs", "num_kv_heads", "head_dim", "k_bits", "v_bits", "group_size", "residual",
         "max_tokens", "block_size", "num_blocks", "max_blocks_per_seq", "kv_format")] + \
-        [("rope_theta", ctypes.c_float)]
+        [("rope_theta", ctypes.c_float), ("grid", ctypes.c_int32)]
 
 
 class kvq_cache(ctypes.Structure):
@@ -51,7 +52,8 @@ class kvq_sizes(ctypes.Structure):
 
 EXPORTED = ["kvq_buffer_sizes", "kv_quantize_prefill", "kv_append_token", "kv_dequantize",
             "kv_decode_attention_workspace_bytes", "kv_decode_attention", "kv_decode_attention_partials",
-            "kv_decode_attention_merge", "kv_export_codes", "kvq_status_string", "kvq_last_error"]
+            "kv_decode_attention_merge", "kv_export_codes", "kvq_codebook_levels", "kvq_status_string",
+            "kvq_last_error"]
 
 
 class KVQError(RuntimeError):
@@ -92,6 +94,8 @@ def lib():
         L.kv_decode_attention_merge.restype = ctypes.c_int
         L.kv_export_codes.argtypes = [P(kvq_config), P(kvq_cache)] + [vp] * 6 + [ctypes.c_int32, vp]
         L.kv_export_codes.restype = ctypes.c_int
+        L.kvq_codebook_levels.argtypes = [ctypes.c_int32, P(ctypes.c_float)]
+        L.kvq_codebook_levels.restype = ctypes.c_int
         L.kvq_status_string.argtypes = [ctypes.c_int]
         L.kvq_status_string.restype = ctypes.c_char_p
         L.kvq_last_error.argtypes = []
@@ -170,6 +174,12 @@ def kv_export_codes(cfg, cache, k_codes, v_codes, k_s, k_z, v_s, v_z, out_tokens
                                  _stream(stream)), "kv_export_codes")
 
 
+def kvq_codebook_levels(bits) -> np.ndarray:
+    out = (ctypes.c_float * (1 << int(bits)))()
+    _check(lib().kvq_codebook_levels(int(bits), out), "kvq_codebook_levels")
+    return np.array(out[:], np.float32)
+
+
 # ---------------------------------------------------------------------------
 # Buffer owner
 # ---------------------------------------------------------------------------
@@ -192,12 +202,13 @@ class CacheShape:
     max_blocks_per_seq: int = 0
     kv_format: int = FORMAT_KIVI
     rope_theta: float = 0.0      # > 0: keys are pre-RoPE, rotated on read with this base
+    grid: int = 0                # GRID_UNIFORM or GRID_NORMAL_QUANTILE (low-bit format)
 
     def config(self) -> kvq_config:
         return kvq_config(self.num_seqs, self.num_kv_heads, HEAD_DIM, self.k_bits, self.v_bits,
                           self.group_size, self.residual, self.max_tokens if not self.paged else 0,
                           self.group_size if self.paged else 0, self.num_blocks, self.max_blocks_per_seq,
-                          self.kv_format, self.rope_theta)
+                          self.kv_format, self.rope_theta, self.grid)
 
 
 class QuantizedKVCache:

@@ -43,6 +43,7 @@ class Workload:
     tag: int = 0                 # distinguishes seeds between workloads
     kv_format: int = 0           # 0 low-bit KIVI, 1 INT8 per token, 2 FP8 E4M3 static
     rope_theta: float = 0.0      # > 0: the keys are pre-RoPE (rotated on read with this base)
+    grid: int = 0                # 0 uniform levels, 1 normal-quantile codebook (low-bit format)
 
     @property
     def gq(self) -> int:
@@ -96,13 +97,26 @@ WORKLOADS_ROPE = {
 }
 
 
+# The normal-quantile codebook grid ("KV cache compression: ...", section
+# 3.3) on the same two shapes and data.
+WORKLOADS_CODEBOOK = {
+    "llama3_8b_layer_b8_32k_int4_codebook": Workload(
+        "llama3_8b_layer_b8_32k_int4_codebook", num_seqs=8, num_q_heads=32, num_kv_heads=8, k_bits=4,
+        v_bits=4, group_size=32, residual=128, context=32768, tag=2, grid=1),
+    "llama3_70b_layer_b1_128k_int2_codebook": Workload(
+        "llama3_70b_layer_b1_128k_int2_codebook", num_seqs=1, num_q_heads=64, num_kv_heads=8, k_bits=2,
+        v_bits=2, group_size=32, residual=128, context=131072, tag=3, grid=1),
+}
+
+_TABLES = (WORKLOADS, WORKLOADS_8BIT, WORKLOADS_ROPE, WORKLOADS_CODEBOOK)
+
+
 def workload(name: str) -> Workload:
     """A named workload of any table."""
-    for table in (WORKLOADS, WORKLOADS_8BIT, WORKLOADS_ROPE):
+    for table in _TABLES:
         if name in table:
             return table[name]
-    raise KeyError("unknown workload %r (known: %s)" % (
-        name, ", ".join(list(WORKLOADS) + list(WORKLOADS_8BIT) + list(WORKLOADS_ROPE))))
+    raise KeyError("unknown workload %r (known: %s)" % (name, ", ".join(k for t in _TABLES for k in t)))
 
 
 def seed_for(tag: int, *parts: int) -> int:

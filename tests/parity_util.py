@@ -29,11 +29,11 @@ def make_cache(w: synth.Workload, lens, max_tokens=None, num_blocks=None, shuffl
                                                                for n in lens)) + 4
         shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, G, R, paged=True,
                                num_blocks=nb, max_blocks_per_seq=mb, kv_format=w.kv_format,
-                               rope_theta=w.rope_theta)
+                               rope_theta=w.rope_theta, grid=w.grid)
     else:
         shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, G, R,
                                max_tokens=max_tokens if max_tokens is not None else int(np.max(lens)) + 64,
-                               kv_format=w.kv_format, rope_theta=w.rope_theta)
+                               kv_format=w.kv_format, rope_theta=w.rope_theta, grid=w.grid)
     ks, vs = scales if scales is not None else (None, None)
     c = kvq.QuantizedKVCache(shape, k_scale=ks, v_scale=vs)
     if w.paged and shuffle_seed is not None:
@@ -48,7 +48,7 @@ def oracle_states(kb: np.ndarray, vb: np.ndarray, lens, w: synth.Workload, cap=N
     if scales is not None:
         ks, vs = (t.detach().cpu().numpy().astype(np.float32) for t in scales)
     return oracle.prefill_batch(kb, vb, lens, w.k_bits, w.v_bits, w.group_size, w.residual,
-                                cap=cap, threads=THREADS, fmt=w.kv_format, kscales=ks, vscales=vs)
+                                cap=cap, threads=THREADS, fmt=w.kv_format, kscales=ks, vscales=vs, grid=w.grid)
 
 
 def compare_codes(cache: kvq.QuantizedKVCache, states, streams=None):

@@ -46,7 +46,8 @@ def test_library_exports_every_declared_symbol():
 
 def _cfg(kvq, **kw):
     d = dict(num_seqs=2, num_kv_heads=3, head_dim=128, k_bits=4, v_bits=2, group_size=32, residual=64,
-             max_tokens=1000, block_size=0, num_blocks=0, max_blocks_per_seq=0, kv_format=0)
+             max_tokens=1000, block_size=0, num_blocks=0, max_blocks_per_seq=0, kv_format=0, rope_theta=0.0,
+             grid=0)
     d.update(kw)
     return kvq.kvq_config(**d)
 
@@ -133,6 +134,29 @@ def test_fp8_cache_needs_scales_on_host():
     c = kvq.QuantizedKVCache(shape, device="cpu", k_scale=[0.1, 0.2, 0.3], v_scale=[1.0, 2.0, 3.0])
     assert c.cache.k_scale == c.k_scale.data_ptr() and c.cache.v_scale == c.v_scale.data_ptr()
     assert c.sequence_view(1).cache.k_scale == c.cache.k_scale
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_codebook_levels_equal_oracle(orc, bits):
+    """The library's normal-quantile codebook (computed on the host by its
+    own quantile routine) is the oracle's, level for level."""
+    kvq = _kvq()
+    import numpy as np
+    assert np.array_equal(kvq.kvq_codebook_levels(bits).astype(np.float64), orc.codebook_levels(bits))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(grid=2), "KVQ_EINVAL"),
+    (dict(grid=-1), "KVQ_EINVAL"),
+    (dict(grid=1, kv_format=1, k_bits=8, v_bits=8), "KVQ_EUNSUPPORTED"),   # low-bit format only
+])
+def test_grid_validation(kw, status):
+    kvq = _kvq()
+    cfg = _cfg(kvq, **kw)
+    out = kvq.kvq_sizes()
+    assert kvq.lib().kvq_buffer_sizes(ctypes.byref(cfg), ctypes.byref(out)) == getattr(kvq, status)
+    bad = (ctypes.c_float * 16)()
+    assert kvq.lib().kvq_codebook_levels(3, bad) == kvq.KVQ_EUNSUPPORTED
 
 
 def test_paged_sizes():
