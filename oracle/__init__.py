@@ -113,6 +113,16 @@ def lib():
             L.orc_append_stream_cb.argtypes = L.orc_append_stream.argtypes
             L.orc_dequantize_stream_cb.argtypes = [_u16p, _u16p] + [ctypes.c_int] * 6 + \
                 [_u8p, _u16p, _u16p, _u8p, _u16p, _u16p, _f32p, _f32p]
+            L.orc_quantize_key_group_ds.argtypes = [_u16p] + [ctypes.c_int] * 4 + [_u8p, _u16p, _u16p, _u16p,
+                                                                                 _u16p]
+            L.orc_prefill_stream_ds.restype = ctypes.c_int
+            L.orc_prefill_stream_ds.argtypes = [_u16p, _u16p] + [ctypes.c_int] * 7 + \
+                [_u8p, _u16p, _u16p, _u8p, _u16p, _u16p, _u16p, _u16p]
+            L.orc_append_stream_ds.restype = ctypes.c_int
+            L.orc_append_stream_ds.argtypes = [_u16p, _u16p, ctypes.c_int, _i32p, _i32p, _u16p, _u16p] + \
+                [ctypes.c_int] * 6 + [_u8p, _u16p, _u16p, _u8p, _u16p, _u16p, _u16p, _u16p]
+            L.orc_dequantize_stream_ds.argtypes = [_u16p, _u16p] + [ctypes.c_int] * 5 + \
+                [_u8p, _u16p, _u16p, _u8p, _u16p, _u16p, _u16p, _u16p, _f32p, _f32p]
             L.orc_stream_bytes.restype = ctypes.c_double
             L.orc_stream_bytes.argtypes = [ctypes.c_long] + [ctypes.c_int] * 5
             L.orc_kv_bytes_closed_form.restype = ctypes.c_double
@@ -186,6 +196,21 @@ def quantize_key_group_cb(x_bits: np.ndarray, bits: int, levels=None):
     return codes, s, z
 
 
+def quantize_key_group_ds(x_bits: np.ndarray, bits: int, n_out: int):
+    """Dense-and-sparse key group: -> (codes [G][d], s [d], z [d],
+    kept positions [n_out] ascending, kept fp16 bits [n_out])."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    G, d = x.shape
+    codes = np.empty((G, d), np.uint8)
+    s = np.empty(d, np.uint16)
+    z = np.empty(d, np.uint16)
+    pos = np.empty(n_out, np.uint16)
+    val = np.empty(n_out, np.uint16)
+    lib().orc_quantize_key_group_ds(_p(x, _u16p), G, d, bits, n_out, _p(codes, _u8p), _p(s, _u16p), _p(z, _u16p),
+                                    _p(pos, _u16p), _p(val, _u16p))
+    return codes, s, z, pos, val
+
+
 def quantize_value_token_cb(x_bits: np.ndarray, bits: int, levels=None):
     x = np.ascontiguousarray(x_bits, dtype=np.uint16)
     lev = np.ascontiguousarray(codebook_levels(bits) if levels is None else levels, np.float64)
@@ -240,10 +265,14 @@ class StreamState:
     scale/zero per token.  FMT_FP8: E4M3 codes under the static scales
     kscale / vscale of the stream's kv head, no per-token metadata."""
 
-    def __init__(self, d, kbits, vbits, G, R, cap, fmt=FMT_KIVI, kscale=0.0, vscale=0.0, grid=GRID_UNIFORM):
+    def __init__(self, d, kbits, vbits, G, R, cap, fmt=FMT_KIVI, kscale=0.0, vscale=0.0, grid=GRID_UNIFORM,
+                 sparse=False):
         self.d, self.kbits, self.vbits, self.G, self.R, self.cap = d, kbits, vbits, G, R, cap
         self.fmt, self.kscale, self.vscale = fmt, float(kscale), float(vscale)
         self.grid = grid
+        self.sparse = sparse          # dense-and-sparse keys: G kept entries per key group
+        self.opos = np.zeros((cap // G + 1, G), np.uint16)
+        self.oval = np.zeros((cap // G + 1, G), np.uint16)
         self.n = 0
         self.nq = 0
         self.hist_k = np.zeros((cap, d), np.uint16)
@@ -266,14 +295,18 @@ class StreamState:
 
     @classmethod
     def prefill(cls, k_bits, v_bits, kbits, vbits, G, R, cap=None, fmt=FMT_KIVI, kscale=0.0, vscale=0.0,
-                grid=GRID_UNIFORM):
+                grid=GRID_UNIFORM, sparse=False):
         k = np.ascontiguousarray(k_bits, np.uint16)
         v = np.ascontiguousarray(v_bits, np.uint16)
         n, d = k.shape
-        st = cls(d, kbits, vbits, G, R, cap if cap is not None else max(n, 1), fmt, kscale, vscale, grid)
+        st = cls(d, kbits, vbits, G, R, cap if cap is not None else max(n, 1), fmt, kscale, vscale, grid, sparse)
         st.hist_k[:n] = k
         st.hist_v[:n] = v
-        if fmt == FMT_KIVI and grid == GRID_CODEBOOK:
+        if sparse:
+            st.nq = int(lib().orc_prefill_stream_ds(
+                _p(k, _u16p), _p(v, _u16p), n, d, kbits, vbits, G, R, G, *st._arrays(),
+                _p(st.opos, _u16p), _p(st.oval, _u16p)))
+        elif fmt == FMT_KIVI and grid == GRID_CODEBOOK:
             st.nq = int(lib().orc_prefill_stream_cb(
                 _p(k, _u16p), _p(v, _u16p), n, d, kbits, vbits, G, R, *st._arrays()))
         elif fmt == FMT_KIVI:
@@ -291,7 +324,13 @@ class StreamState:
         vn = np.ascontiguousarray(v_new_bits, np.uint16)
         n = ctypes.c_int(self.n)
         nq = ctypes.c_int(self.nq)
-        if self.fmt == FMT_KIVI:
+        if self.sparse:
+            r = lib().orc_append_stream_ds(
+                _p(self.hist_k, _u16p), _p(self.hist_v, _u16p), self.cap,
+                ctypes.byref(n), ctypes.byref(nq), _p(kn, _u16p), _p(vn, _u16p),
+                self.d, self.kbits, self.vbits, self.G, self.R, self.G, *self._arrays(),
+                _p(self.opos, _u16p), _p(self.oval, _u16p))
+        elif self.fmt == FMT_KIVI:
             fn = lib().orc_append_stream_cb if self.grid == GRID_CODEBOOK else lib().orc_append_stream
             r = fn(
                 _p(self.hist_k, _u16p), _p(self.hist_v, _u16p), self.cap,
@@ -313,7 +352,11 @@ class StreamState:
         n, d = self.n, self.d
         ok = np.empty((max(n, 1), d), np.float32)
         ov = np.empty((max(n, 1), d), np.float32)
-        if self.fmt == FMT_KIVI and self.grid == GRID_CODEBOOK:
+        if self.sparse:
+            lib().orc_dequantize_stream_ds(
+                _p(self.hist_k, _u16p), _p(self.hist_v, _u16p), n, self.nq, d, self.G, self.G,
+                *self._arrays(), _p(self.opos, _u16p), _p(self.oval, _u16p), _p(ok, _f32p), _p(ov, _f32p))
+        elif self.fmt == FMT_KIVI and self.grid == GRID_CODEBOOK:
             lib().orc_dequantize_stream_cb(
                 _p(self.hist_k, _u16p), _p(self.hist_v, _u16p), n, self.nq, d, self.G, self.kbits, self.vbits,
                 *self._arrays(), _p(ok, _f32p), _p(ov, _f32p))
@@ -344,6 +387,12 @@ class StreamState:
 
     def value_meta(self):
         return self.vs[: self.nq], self.vz[: self.nq]
+
+    def outliers(self):
+        """Dense-and-sparse keys: kept positions (t*d + c within the group,
+        ascending) and fp16 values, [nq/G][G]."""
+        g = self.nq // self.G
+        return self.opos[:g], self.oval[:g]
 
     def residual(self):
         return self.hist_k[self.nq: self.n], self.hist_v[self.nq: self.n]
@@ -413,7 +462,7 @@ def kv_bytes_closed_form(L, Hkv, n, d, bytes_per_elem) -> float:
 # --------------------------------------------------------------------------
 
 def prefill_batch(k_bits, v_bits, seq_lens, kbits, vbits, G, R, cap=None, threads=1,
-                  fmt=FMT_KIVI, kscales=None, vscales=None, grid=GRID_UNIFORM):
+                  fmt=FMT_KIVI, kscales=None, vscales=None, grid=GRID_UNIFORM, sparse=False):
     """k_bits, v_bits: uint16 [B][H][L][d]; seq_lens: [B]; kscales, vscales:
     FP8 static scales per kv head [H].
     -> list (per sequence) of lists (per kv-head) of StreamState."""
@@ -426,7 +475,7 @@ def prefill_batch(k_bits, v_bits, seq_lens, kbits, vbits, G, R, cap=None, thread
         vs = float(vscales[h]) if vscales is not None else 0.0
         return StreamState.prefill(k_bits[b, h, :n], v_bits[b, h, :n], kbits, vbits, G, R,
                                    cap=cap if cap is not None else max(n, 1), fmt=fmt,
-                                   kscale=ks, vscale=vs, grid=grid)
+                                   kscale=ks, vscale=vs, grid=grid, sparse=sparse)
 
     jobs = [(b, h) for b in range(B) for h in range(H)]
     if threads > 1:

@@ -25,7 +25,9 @@
  *       reading; non-uniform grids with levels at quantiles of the
  *       distribution, like NF4) and section 2 (RoPE rotates pairs of
  *       dimensions, keeping each pair's norm).
- *  [P3] experiment 03: RoPE treats two adjacent dimensions as one plane.
+ *  [P3] experiment 03: RoPE treats two adjacent dimensions as one plane;
+ *       KVQuant keeps the few extreme key values in fp16 as a sparse matrix
+ *       and quantizes the rest.
  *  [P2] "KV compression and quantization", part B.1 (FP8 E4M3/E5M2 and INT8
  *       at 0.5x the fp16 bytes).
  *  [P4] "KV cache compression" (jaedaily), formula paragraph: per-channel key
@@ -435,6 +437,150 @@ void orc_dequantize_stream_cb(const uint16_t *k, const uint16_t *v, int n, int n
             }
         }
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dense-and-sparse keys ([P3] exp. 03, closing paragraph: KVQuant keeps the  */
+/* few extreme values in fp16 as a sparse matrix and quantizes the rest).    */
+/* Per key group of G tokens (one kv head): the n_out entries of largest     */
+/* magnitude |x| (ties: the lower position t*d + c first) are kept exactly;  */
+/* each channel's min, max, scale and zero are taken over its other values  */
+/* (none left: s = z = 0) and those values are quantized with the group     */
+/* quantizer above; a kept position's code is 0 and it dequantizes to the    */
+/* kept value.                                                               */
+/* ------------------------------------------------------------------------ */
+
+struct mag_pos {
+    float mag;
+    int pos;
+};
+
+/* larger magnitude first, then the lower position */
+static int cmp_magnitude_desc(const void *a, const void *b)
+{
+    const struct mag_pos *p = (const struct mag_pos *)a, *q = (const struct mag_pos *)b;
+    if (p->mag != q->mag) return p->mag > q->mag ? -1 : 1;
+    return p->pos < q->pos ? -1 : (p->pos > q->pos ? 1 : 0);
+}
+
+static int cmp_int_asc(const void *a, const void *b)
+{
+    int i = *(const int *)a, j = *(const int *)b;
+    return i < j ? -1 : (i > j ? 1 : 0);
+}
+
+/* x, codes: [G][d]; s, z: [d]; out_pos (t*d + c, ascending), out_val (fp16
+ * bits): [n_out]. */
+void orc_quantize_key_group_ds(const uint16_t *x, int G, int d, int bits, int n_out,
+                               uint8_t *codes, uint16_t *s, uint16_t *z,
+                               uint16_t *out_pos, uint16_t *out_val)
+{
+    const int n = G * d, qmax = (1 << bits) - 1;
+    struct mag_pos *e = (struct mag_pos *)malloc(sizeof(struct mag_pos) * n);
+    int *idx = (int *)malloc(sizeof(int) * n_out);
+    char *kept = (char *)calloc(n, 1);
+    for (int i = 0; i < n; ++i) {
+        e[i].mag = fabsf(orc_h2f(x[i]));
+        e[i].pos = i;
+    }
+    qsort(e, n, sizeof(struct mag_pos), cmp_magnitude_desc);
+    for (int k = 0; k < n_out; ++k) idx[k] = e[k].pos;
+    qsort(idx, n_out, sizeof(int), cmp_int_asc);
+    for (int k = 0; k < n_out; ++k) {
+        kept[idx[k]] = 1;
+        out_pos[k] = (uint16_t)idx[k];
+        out_val[k] = x[idx[k]];
+    }
+    free(e);
+    for (int c = 0; c < d; ++c) {
+        int any = 0;
+        float mn = 0.0f, mx = 0.0f;
+        for (int t = 0; t < G; ++t) {
+            if (kept[t * d + c]) continue;
+            float v = orc_h2f(x[t * d + c]);
+            if (!any || v < mn) mn = v;
+            if (!any || v > mx) mx = v;
+            any = 1;
+        }
+        mn = mn + 0.0f;
+        mx = mx + 0.0f;
+        float s32 = (mx - mn) / (float)qmax;
+        uint16_t s16 = orc_f2h(s32);
+        uint16_t z16 = orc_f2h(mn);
+        float sf = orc_h2f(s16);
+        float zf = orc_h2f(z16);
+        float inv = (sf > 0.0f) ? 1.0f / sf : 0.0f;
+        for (int t = 0; t < G; ++t) {
+            if (kept[t * d + c]) {
+                codes[t * d + c] = 0;
+                continue;
+            }
+            float v = orc_h2f(x[t * d + c]);
+            float r = rintf((v - zf) * inv);
+            if (r < 0.0f) r = 0.0f;
+            if (r > (float)qmax) r = (float)qmax;
+            codes[t * d + c] = (uint8_t)r;
+        }
+        s[c] = s16;
+        z[c] = z16;
+    }
+    free(idx);
+    free(kept);
+}
+
+/* Whole stream with dense-and-sparse keys (n_out kept entries per key
+ * group); values as in orc_prefill_stream.  opos, oval: [n_q/G][n_out]. */
+int orc_prefill_stream_ds(const uint16_t *k, const uint16_t *v, int n, int d,
+                          int kbits, int vbits, int G, int R, int n_out,
+                          uint8_t *kcodes, uint16_t *ks, uint16_t *kz,
+                          uint8_t *vcodes, uint16_t *vs, uint16_t *vz,
+                          uint16_t *opos, uint16_t *oval)
+{
+    int nq = orc_num_quantized(n, G, R);
+    for (int g = 0; g < nq / G; ++g)
+        orc_quantize_key_group_ds(k + (long)g * G * d, G, d, kbits, n_out, kcodes + (long)g * G * d,
+                                  ks + (long)g * d, kz + (long)g * d, opos + (long)g * n_out, oval + (long)g * n_out);
+    for (int t = 0; t < nq; ++t)
+        orc_quantize_value_token(v + (long)t * d, d, vbits, vcodes + (long)t * d, vs + t, vz + t);
+    return nq;
+}
+
+int orc_append_stream_ds(uint16_t *hist_k, uint16_t *hist_v, int cap, int *n, int *nq,
+                         const uint16_t *k_new, const uint16_t *v_new, int d,
+                         int kbits, int vbits, int G, int R, int n_out,
+                         uint8_t *kcodes, uint16_t *ks, uint16_t *kz,
+                         uint8_t *vcodes, uint16_t *vs, uint16_t *vz,
+                         uint16_t *opos, uint16_t *oval)
+{
+    if (*n >= cap) return -1;
+    memcpy(hist_k + (long)(*n) * d, k_new, sizeof(uint16_t) * d);
+    memcpy(hist_v + (long)(*n) * d, v_new, sizeof(uint16_t) * d);
+    *n += 1;
+    if (*n - *nq == R + G) {
+        int g = *nq / G;
+        orc_quantize_key_group_ds(hist_k + (long)(*nq) * d, G, d, kbits, n_out, kcodes + (long)(*nq) * d,
+                                  ks + (long)g * d, kz + (long)g * d, opos + (long)g * n_out,
+                                  oval + (long)g * n_out);
+        for (int t = *nq; t < *nq + G; ++t)
+            orc_quantize_value_token(hist_v + (long)t * d, d, vbits, vcodes + (long)t * d, vs + t, vz + t);
+        *nq += G;
+        return 1;
+    }
+    return 0;
+}
+
+void orc_dequantize_stream_ds(const uint16_t *k, const uint16_t *v, int n, int nq, int d, int G, int n_out,
+                              const uint8_t *kcodes, const uint16_t *ks, const uint16_t *kz,
+                              const uint8_t *vcodes, const uint16_t *vs, const uint16_t *vz,
+                              const uint16_t *opos, const uint16_t *oval,
+                              float *out_k, float *out_v)
+{
+    orc_dequantize_stream(k, v, n, nq, d, G, kcodes, ks, kz, vcodes, vs, vz, out_k, out_v);
+    for (int g = 0; g < nq / G; ++g)
+        for (int e = 0; e < n_out; ++e) {
+            int p = opos[(long)g * n_out + e];
+            out_k[(long)g * G * d + p] = orc_h2f(oval[(long)g * n_out + e]);
+        }
 }
 
 /* ------------------------------------------------------------------------ */

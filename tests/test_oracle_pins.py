@@ -845,6 +845,127 @@ def test_codebook_roundtrip_and_prefill_equals_appends(orc, kbits, vbits, G, R):
 
 
 # --------------------------------------------------------------------------
+# Dense-and-sparse keys ("KV Cache compression lab", experiment 03, closing
+# paragraph: KVQuant keeps the few extreme values in fp16 as a sparse matrix
+# and quantizes the rest).  Selection checked by brute force (numpy's own
+# sort), the dense part against the plain set quantizer on what is left.
+# --------------------------------------------------------------------------
+
+def _ds_group(rng, G, outlier_channels=(3, 70), gain=20.0):
+    x = rng.standard_normal((G, 128))
+    for c in outlier_channels:
+        x[:, c] *= gain
+    x[0, 5] = x[1, 5] = 7.0          # equal magnitudes: ties broken by position
+    x[2, 6] = -7.0
+    return x.astype(np.float16)
+
+
+@pytest.mark.parametrize("G", [16, 32])
+def test_ds_selection_is_the_largest_magnitudes(orc, G):
+    rng = np.random.default_rng(140 + G)
+    for trial in range(5):
+        x = _ds_group(rng, G, gain=[1.0, 20.0, 3.0, 20.0, 50.0][trial])
+        codes, s16, z16, pos, val = orc.quantize_key_group_ds(x.view(np.uint16), 2, G)
+        mag = np.abs(x.astype(np.float64)).ravel()
+        order = np.lexsort((np.arange(mag.size), -mag))        # by |x| descending, then position
+        want = np.sort(order[:G])
+        assert np.array_equal(pos.astype(np.int64), want)
+        assert np.array_equal(val, x.view(np.uint16).ravel()[want])
+        assert np.all(codes.ravel()[want] == 0)
+
+
+def test_ds_ties_at_the_boundary_go_to_the_lower_position(orc):
+    """G - 1 clearly largest entries, then three of equal magnitude (+-50)
+    competing for the last place: the lowest position wins."""
+    G = 32
+    x = np.random.default_rng(152).standard_normal((G, 128))
+    big = [(t, (7 * t) % 128) for t in range(G - 1)]
+    for i, (t, c) in enumerate(big):
+        x[t, c] = 100.0 + i
+    x[20, 100], x[5, 64], x[9, 1] = 50.0, -50.0, 50.0
+    codes, s16, z16, pos, val = orc.quantize_key_group_ds(x.astype(np.float16).view(np.uint16), 2, G)
+    want = sorted([t * 128 + c for t, c in big] + [5 * 128 + 64])
+    assert pos.tolist() == want
+
+
+def test_ds_dense_part_is_the_set_quantizer_on_the_rest(orc):
+    rng = np.random.default_rng(150)
+    G = 32
+    x = _ds_group(rng, G)
+    xb = x.view(np.uint16)
+    codes, s16, z16, pos, val = orc.quantize_key_group_ds(xb, 2, G)
+    kept = np.zeros(G * 128, bool)
+    kept[pos] = True
+    kept = kept.reshape(G, 128)
+    for c in range(128):
+        rest = xb[~kept[:, c], c]
+        if rest.size == 0:
+            assert s16[c] == 0 and z16[c] == 0
+            continue
+        cc, s, z = orc.quantize_value_token(rest, 2)       # the plain min/max set quantizer
+        assert np.array_equal(codes[~kept[:, c], c], cc) and s16[c] == s and z16[c] == z
+
+
+def test_ds_channel_with_no_dense_values(orc):
+    """A channel whose every value is among the group's largest keeps them
+    all; its scale and zero are 0."""
+    G = 16
+    x = np.random.default_rng(151).standard_normal((G, 128)).astype(np.float16)
+    x[:, 9] = (100 + np.arange(G)).astype(np.float16)
+    codes, s16, z16, pos, val = orc.quantize_key_group_ds(x.view(np.uint16), 4, G)
+    assert np.array_equal(pos, np.arange(G) * 128 + 9)
+    assert s16[9] == 0 and z16[9] == 0
+
+
+@pytest.mark.parametrize("G,R", [(32, 0), (16, 128), (32, 64)])
+def test_ds_stream_roundtrip_and_appends(orc, G, R):
+    n_total, m = 420, 97
+    rng = np.random.default_rng(160 + G + R)
+    k = rng.standard_normal((n_total, 128))
+    k[:, [3, 77]] *= 20
+    kb = k.astype(np.float16).view(np.uint16)
+    vb = rng.standard_normal((n_total, 128)).astype(np.float16).view(np.uint16)
+    full = orc.StreamState.prefill(kb, vb, 2, 2, G, R, cap=n_total, sparse=True)
+    inc = orc.StreamState.prefill(kb[:m], vb[:m], 2, 2, G, R, cap=n_total, sparse=True)
+    for t in range(m, n_total):
+        inc.append(kb[t], vb[t])
+    assert inc.nq == full.nq
+    for a, b in zip((inc.key_codes(), inc.value_codes()) + inc.key_meta() + inc.value_meta() + inc.outliers(),
+                    (full.key_codes(), full.value_codes()) + full.key_meta() + full.value_meta() + full.outliers()):
+        assert np.array_equal(a, b)
+    kh, _ = full.dequantize()
+    nq = full.nq
+    opos, oval = full.outliers()
+    xk = orc.h2f(kb[:nq]).astype(np.float64)
+    kept = np.zeros((nq // G, G * 128), bool)
+    for g in range(nq // G):
+        kept[g, opos[g]] = True
+    kept = kept.reshape(nq, 128)
+    assert np.array_equal(kh[:nq][kept], xk[kept].astype(np.float32))      # kept entries exact
+    s = np.repeat(orc.h2f(full.key_meta()[0]), G, axis=0)
+    z = np.repeat(orc.h2f(full.key_meta()[1]), G, axis=0)
+    err = np.abs(xk - kh[:nq])
+    assert np.all(err[~kept] <= _roundtrip_bound(xk, s, z, 2)[~kept])
+
+
+def test_ds_lowers_key_error(orc):
+    """The purpose: at 2 bits, keeping the few extreme keys exact lowers the
+    key error of the synthetic keys (outlier channels) against per-channel
+    quantization of everything."""
+    from quantized_decode_attention_kivi_amd import synth
+    w = synth.Workload("t", 1, 4, 1, 2, 2, 32, 0, context=2048, tag=79)
+    K, _ = synth.make_kv(w)
+    kb = K.numpy().view(np.uint16)[0, 0]
+    x = orc.h2f(kb).astype(np.float64)
+    errs = []
+    for sparse in (False, True):
+        st = orc.StreamState.prefill(kb, kb, 2, 2, 32, 0, sparse=sparse)
+        kh, _ = st.dequantize()
+        errs.append(np.mean((x - kh) ** 2))
+    assert errs[1] < 0.8 * errs[0], errs
+
+
+# --------------------------------------------------------------------------
 # Mutation check: planted mistakes in a copy of the oracle must be caught
 # --------------------------------------------------------------------------
 
@@ -876,6 +997,12 @@ MUTATIONS = [
      "for (int k = 0; k < n; ++k) c[k] = normal_quantile((k + 1.0) / (n + 1));", "cblev"),  # other quantiles
     ("out_k[i] = fmaf((float)klev[kcodes[i]], orc_h2f(ks[gi]), orc_h2f(kz[gi]));",
      "out_k[i] = fmaf((float)kcodes[i], orc_h2f(ks[gi]), orc_h2f(kz[gi]));", "cbdeq"),  # LUT skipped
+    ("return p->pos < q->pos ? -1 : (p->pos > q->pos ? 1 : 0);",
+     "return p->pos > q->pos ? -1 : (p->pos < q->pos ? 1 : 0);", "dssel"),   # ties to the higher position
+    ("            if (kept[t * d + c]) continue;\n            float v = orc_h2f(x[t * d + c]);",
+     "            float v = orc_h2f(x[t * d + c]);", "dsdense"),                 # kept values in the range
+    ("out_k[(long)g * G * d + p] = orc_h2f(oval[(long)g * n_out + e]);",
+     "(void)p;", "dsdeq"),                                                    # kept values not restored
 ]
 
 
@@ -898,6 +1025,9 @@ def test_pin_catches_planted_mistakes(tmp_path):
         "cbtie": "test_codebook_grid_aligned_and_ties",
         "cblev": "test_codebook_levels_are_normal_quantiles",
         "cbdeq": "test_codebook_roundtrip_and_prefill_equals_appends",
+        "dssel": "test_ds_ties_at_the_boundary_go_to_the_lower_position",
+        "dsdense": "test_ds_dense_part_is_the_set_quantizer_on_the_rest",
+        "dsdeq": "test_ds_stream_roundtrip_and_appends",
     }
     for i, (old, new, which) in enumerate(MUTATIONS):
         assert old in src, old
