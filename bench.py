@@ -44,6 +44,7 @@ ATTN_KERNEL_SOURCES = ["quantized_decode_attention_kivi_amd/csrc/kvq_attn.hip",
                        "quantized_decode_attention_kivi_amd/csrc/kvq_attn_kivi.hip",
                        "quantized_decode_attention_kivi_amd/csrc/kvq_attn_rope.hip",
                        "quantized_decode_attention_kivi_amd/csrc/kvq_attn_cb.hip",
+                       "quantized_decode_attention_kivi_amd/csrc/kvq_attn_sparse.hip",
                        "quantized_decode_attention_kivi_amd/csrc/kvq_attn_8bit.hip",
                        "quantized_decode_attention_kivi_amd/csrc/kvq_device.h",
                        "quantized_decode_attention_kivi_amd/csrc/kvq_internal.h",
@@ -86,7 +87,8 @@ def meta_bytes(nq, w, d=128):
         return 0
     if w.kv_format == 1:
         return nq * 8
-    return (nq // w.group_size) * d * 4 + nq * 4
+    # dense-and-sparse keys: G (position, fp16) pairs of 4 bytes per key group
+    return (nq // w.group_size) * d * 4 + nq * 4 + (nq * 4 if w.sparse_keys else 0)
 
 
 def attention_bytes(lens, w, d=128):
@@ -214,7 +216,7 @@ def cpu_baseline(w, K, V, q, lens, budget_s, scales=None):
         vx = V[b, h, :n].cpu().numpy().view(np.uint16)
         t0 = time.perf_counter()
         st = oracle.StreamState.prefill(kx, vx, w.k_bits, w.v_bits, w.group_size, w.residual, fmt=w.kv_format,
-                                        grid=w.grid,
+                                        grid=w.grid, sparse=bool(w.sparse_keys),
                                         kscale=float(ksc[h]) if ksc is not None else 0.0,
                                         vscale=float(vsc[h]) if vsc is not None else 0.0)
         t1 = time.perf_counter()
@@ -318,11 +320,12 @@ def main():
         nb = int(sum(n_quant(int(n) + grow, G, R) // G for n in lens)) + 8
         shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, G, R, paged=True,
                                num_blocks=nb, max_blocks_per_seq=mb, kv_format=w.kv_format,
-                               rope_theta=w.rope_theta, grid=w.grid)
+                               rope_theta=w.rope_theta, grid=w.grid,
+                               sparse_keys=w.sparse_keys)
     else:
         shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, w.group_size, w.residual,
                                max_tokens=L + total_steps + 8, kv_format=w.kv_format, rope_theta=w.rope_theta,
-                               grid=w.grid)
+                               grid=w.grid, sparse_keys=w.sparse_keys)
     ks, vs = scales if scales is not None else (None, None)
     caches = [kvq.QuantizedKVCache(shape, device=dev, k_scale=ks, v_scale=vs) for _ in range(copies)]
     if w.paged:
@@ -431,6 +434,7 @@ def main():
             "kv_format": ["kivi", "int8", "fp8_e4m3"][w.kv_format],
             "rope_on_read_theta": w.rope_theta,
             "grid": ["uniform", "normal_quantile_codebook"][w.grid],
+            "sparse_keys": bool(w.sparse_keys),
             "paged": w.paged, "layers": w.layers, "min_context": int(lens.min()),
             "tokens": int(lens.sum()),
         },

@@ -21,6 +21,8 @@
  *    kernel when it reads them; levels placed at quantiles of the
  *    distribution (like NF4) instead of evenly; section 2: RoPE rotates
  *    pairs of dimensions.
+ *  - "KV Cache compression lab", experiment 03: KVQuant keeps the few
+ *    extreme key values in fp16 as a sparse matrix and quantizes the rest.
  *  - "KV cache compression: ...", section 3.1, and "KV compression and
  *    quantization", part B.1: 8-bit caches at half the fp16 bytes, either
  *    FP8 E4M3 under a static per-head scale or INT8 under a dynamic
@@ -49,6 +51,11 @@
  *   code = the nearest level to (x - z) * inv, a tie at a midpoint going to
  *   the even code; dequantized value fmaf(L_code, s, z).  kvq_codebook_levels
  *   returns the levels.
+ *   Dense-and-sparse keys (sparse_keys = 1, low-bit format): in each key
+ *   group the G entries of largest |x| (ties: lower position t*128 + c) are
+ *   kept exactly in fp16; each channel's mn, mx (hence s, z) are taken over
+ *   its other values (none left: s = z = 0); kept positions carry code 0 and
+ *   dequantize to the kept value.
  *   Pre-RoPE keys (rope_theta > 0): the cache holds keys before the rotary
  *   embedding and attention uses RoPE_t(k_t) in place of k_t, pair
  *   (2i, 2i+1) of token t (0-based position in its sequence) rotated by the
@@ -122,6 +129,8 @@ typedef struct kvq_config {
                                    (10000, 500000, ...); low-bit format only     */
     int32_t grid;               /* KVQ_GRID_*; the codebook grid needs the
                                    low-bit format                                */
+    int32_t sparse_keys;        /* 1: dense-and-sparse keys (low-bit format, not
+                                   with pre-RoPE keys); 0: off                   */
 } kvq_config;
 
 /* Device buffers of one cache.  Sizes come from kvq_buffer_sizes(). */
@@ -144,7 +153,8 @@ typedef struct kvq_cache {
  * Record = one (key group, kv head): G*d*k_bits/8 key-code bytes,
  * G*d*v_bits/8 value-code bytes, d fp16 key scales and d fp16 key zeros,
  * G fp16 value scales and G fp16 value zeros (INT8: G fp16 key scales and
- * zeros instead of d; FP8: no scales or zeros), arranged inside the record in
+ * zeros instead of d; FP8: no scales or zeros; dense-and-sparse keys: plus G
+ * (position, fp16 value) pairs of 4 bytes), arranged inside the record in
  * the order the decode kernel consumes them (an internal format: use
  * kv_export_codes / kv_dequantize for a logical view).  Contiguous mode holds B*H*floor(max(0,max_tokens-R)/G)
  * records; paged mode holds num_blocks*H records. */
@@ -255,6 +265,14 @@ kvq_status kv_export_codes(const kvq_config *cfg, const kvq_cache *cache,
                            uint8_t *k_codes, uint8_t *v_codes,
                            uint16_t *k_s, uint16_t *k_z, uint16_t *v_s, uint16_t *v_z,
                            int32_t out_tokens, void *stream);
+
+/* Dense-and-sparse keys (test hook): the kept entries of every quantized key
+ * group.  pos, val: uint16 [B][H][out_tokens/G][G], ascending positions
+ * t*128 + c within the group and their fp16 values for groups < n_q[b]/G, 0
+ * elsewhere.  out_tokens must be a multiple of G; KVQ_EINVAL unless the
+ * cache has sparse_keys. */
+kvq_status kv_export_outliers(const kvq_config *cfg, const kvq_cache *cache, uint16_t *pos, uint16_t *val,
+                              int32_t out_tokens, void *stream);
 
 /* Host only: the 2^bits levels L_0..L_Q (in steps of the uniform grid, so
  * the uniform grid's are 0..Q) of the normal-quantile codebook for bits 2

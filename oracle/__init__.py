@@ -48,12 +48,12 @@ def build(force: bool = True) -> str:
 
 
 def lib():
-    """Load the oracle library, compiling it first only if no build exists."""
+    """Load the oracle library, compiling it first if no build exists or the
+    source is newer than the build."""
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB_PATH):
-                build(force=True)
+            build(force=False)
             L = ctypes.CDLL(_LIB_PATH)
             L.orc_h2f.restype = ctypes.c_float
             L.orc_h2f.argtypes = [ctypes.c_uint16]
@@ -113,15 +113,15 @@ def lib():
             L.orc_append_stream_cb.argtypes = L.orc_append_stream.argtypes
             L.orc_dequantize_stream_cb.argtypes = [_u16p, _u16p] + [ctypes.c_int] * 6 + \
                 [_u8p, _u16p, _u16p, _u8p, _u16p, _u16p, _f32p, _f32p]
-            L.orc_quantize_key_group_ds.argtypes = [_u16p] + [ctypes.c_int] * 4 + [_u8p, _u16p, _u16p, _u16p,
-                                                                                 _u16p]
+            L.orc_quantize_key_group_ds.argtypes = [_u16p] + [ctypes.c_int] * 4 + [_f64p, _u8p, _u16p, _u16p,
+                                                                                 _u16p, _u16p]
             L.orc_prefill_stream_ds.restype = ctypes.c_int
-            L.orc_prefill_stream_ds.argtypes = [_u16p, _u16p] + [ctypes.c_int] * 7 + \
+            L.orc_prefill_stream_ds.argtypes = [_u16p, _u16p] + [ctypes.c_int] * 8 + \
                 [_u8p, _u16p, _u16p, _u8p, _u16p, _u16p, _u16p, _u16p]
             L.orc_append_stream_ds.restype = ctypes.c_int
             L.orc_append_stream_ds.argtypes = [_u16p, _u16p, ctypes.c_int, _i32p, _i32p, _u16p, _u16p] + \
-                [ctypes.c_int] * 6 + [_u8p, _u16p, _u16p, _u8p, _u16p, _u16p, _u16p, _u16p]
-            L.orc_dequantize_stream_ds.argtypes = [_u16p, _u16p] + [ctypes.c_int] * 5 + \
+                [ctypes.c_int] * 7 + [_u8p, _u16p, _u16p, _u8p, _u16p, _u16p, _u16p, _u16p]
+            L.orc_dequantize_stream_ds.argtypes = [_u16p, _u16p] + [ctypes.c_int] * 8 + \
                 [_u8p, _u16p, _u16p, _u8p, _u16p, _u16p, _u16p, _u16p, _f32p, _f32p]
             L.orc_stream_bytes.restype = ctypes.c_double
             L.orc_stream_bytes.argtypes = [ctypes.c_long] + [ctypes.c_int] * 5
@@ -206,8 +206,8 @@ def quantize_key_group_ds(x_bits: np.ndarray, bits: int, n_out: int):
     z = np.empty(d, np.uint16)
     pos = np.empty(n_out, np.uint16)
     val = np.empty(n_out, np.uint16)
-    lib().orc_quantize_key_group_ds(_p(x, _u16p), G, d, bits, n_out, _p(codes, _u8p), _p(s, _u16p), _p(z, _u16p),
-                                    _p(pos, _u16p), _p(val, _u16p))
+    lib().orc_quantize_key_group_ds(_p(x, _u16p), G, d, bits, n_out, None, _p(codes, _u8p), _p(s, _u16p),
+                                    _p(z, _u16p), _p(pos, _u16p), _p(val, _u16p))
     return codes, s, z, pos, val
 
 
@@ -304,7 +304,7 @@ class StreamState:
         st.hist_v[:n] = v
         if sparse:
             st.nq = int(lib().orc_prefill_stream_ds(
-                _p(k, _u16p), _p(v, _u16p), n, d, kbits, vbits, G, R, G, *st._arrays(),
+                _p(k, _u16p), _p(v, _u16p), n, d, kbits, vbits, G, R, G, int(grid), *st._arrays(),
                 _p(st.opos, _u16p), _p(st.oval, _u16p)))
         elif fmt == FMT_KIVI and grid == GRID_CODEBOOK:
             st.nq = int(lib().orc_prefill_stream_cb(
@@ -328,7 +328,7 @@ class StreamState:
             r = lib().orc_append_stream_ds(
                 _p(self.hist_k, _u16p), _p(self.hist_v, _u16p), self.cap,
                 ctypes.byref(n), ctypes.byref(nq), _p(kn, _u16p), _p(vn, _u16p),
-                self.d, self.kbits, self.vbits, self.G, self.R, self.G, *self._arrays(),
+                self.d, self.kbits, self.vbits, self.G, self.R, self.G, int(self.grid), *self._arrays(),
                 _p(self.opos, _u16p), _p(self.oval, _u16p))
         elif self.fmt == FMT_KIVI:
             fn = lib().orc_append_stream_cb if self.grid == GRID_CODEBOOK else lib().orc_append_stream
@@ -354,8 +354,9 @@ class StreamState:
         ov = np.empty((max(n, 1), d), np.float32)
         if self.sparse:
             lib().orc_dequantize_stream_ds(
-                _p(self.hist_k, _u16p), _p(self.hist_v, _u16p), n, self.nq, d, self.G, self.G,
-                *self._arrays(), _p(self.opos, _u16p), _p(self.oval, _u16p), _p(ok, _f32p), _p(ov, _f32p))
+                _p(self.hist_k, _u16p), _p(self.hist_v, _u16p), n, self.nq, d, self.G, self.G, self.kbits,
+                self.vbits, int(self.grid), *self._arrays(), _p(self.opos, _u16p), _p(self.oval, _u16p),
+                _p(ok, _f32p), _p(ov, _f32p))
         elif self.fmt == FMT_KIVI and self.grid == GRID_CODEBOOK:
             lib().orc_dequantize_stream_cb(
                 _p(self.hist_k, _u16p), _p(self.hist_v, _u16p), n, self.nq, d, self.G, self.kbits, self.vbits,

@@ -470,8 +470,8 @@ static int cmp_int_asc(const void *a, const void *b)
 }
 
 /* x, codes: [G][d]; s, z: [d]; out_pos (t*d + c, ascending), out_val (fp16
- * bits): [n_out]. */
-void orc_quantize_key_group_ds(const uint16_t *x, int G, int d, int bits, int n_out,
+ * bits): [n_out].  lev: the codebook's levels, or NULL for the uniform grid. */
+void orc_quantize_key_group_ds(const uint16_t *x, int G, int d, int bits, int n_out, const double *lev,
                                uint8_t *codes, uint16_t *s, uint16_t *z,
                                uint16_t *out_pos, uint16_t *out_val)
 {
@@ -516,7 +516,17 @@ void orc_quantize_key_group_ds(const uint16_t *x, int G, int d, int bits, int n_
                 continue;
             }
             float v = orc_h2f(x[t * d + c]);
-            float r = rintf((v - zf) * inv);
+            float tt = (v - zf) * inv;
+            if (lev) { /* nearest codebook level, ties to the even code (quantize_set_cb) */
+                int code = 0;
+                for (int k = 0; k < qmax; ++k) {
+                    float m = (float)(0.5 * (lev[k] + lev[k + 1]));
+                    if ((k % 2 == 0) ? (tt > m) : (tt >= m)) code += 1;
+                }
+                codes[t * d + c] = (uint8_t)code;
+                continue;
+            }
+            float r = rintf(tt);
             if (r < 0.0f) r = 0.0f;
             if (r > (float)qmax) r = (float)qmax;
             codes[t * d + c] = (uint8_t)r;
@@ -528,26 +538,43 @@ void orc_quantize_key_group_ds(const uint16_t *x, int G, int d, int bits, int n_
     free(kept);
 }
 
+/* One value token on the uniform grid (grid 0) or the codebook (grid 1). */
+static void quantize_value_token_grid(const uint16_t *x, int d, int bits, int grid, uint8_t *codes,
+                                      uint16_t *s, uint16_t *z)
+{
+    if (grid) {
+        double lev[256];
+        orc_codebook_levels(bits, lev);
+        orc_quantize_value_token_cb(x, d, bits, lev, codes, s, z);
+    } else {
+        orc_quantize_value_token(x, d, bits, codes, s, z);
+    }
+}
+
 /* Whole stream with dense-and-sparse keys (n_out kept entries per key
- * group); values as in orc_prefill_stream.  opos, oval: [n_q/G][n_out]. */
+ * group) on the uniform grid (grid 0) or the codebook (grid 1); values as in
+ * orc_prefill_stream(_cb).  opos, oval: [n_q/G][n_out]. */
 int orc_prefill_stream_ds(const uint16_t *k, const uint16_t *v, int n, int d,
-                          int kbits, int vbits, int G, int R, int n_out,
+                          int kbits, int vbits, int G, int R, int n_out, int grid,
                           uint8_t *kcodes, uint16_t *ks, uint16_t *kz,
                           uint8_t *vcodes, uint16_t *vs, uint16_t *vz,
                           uint16_t *opos, uint16_t *oval)
 {
+    double klev[256];
+    if (grid) orc_codebook_levels(kbits, klev);
     int nq = orc_num_quantized(n, G, R);
     for (int g = 0; g < nq / G; ++g)
-        orc_quantize_key_group_ds(k + (long)g * G * d, G, d, kbits, n_out, kcodes + (long)g * G * d,
-                                  ks + (long)g * d, kz + (long)g * d, opos + (long)g * n_out, oval + (long)g * n_out);
+        orc_quantize_key_group_ds(k + (long)g * G * d, G, d, kbits, n_out, grid ? klev : NULL,
+                                  kcodes + (long)g * G * d, ks + (long)g * d, kz + (long)g * d,
+                                  opos + (long)g * n_out, oval + (long)g * n_out);
     for (int t = 0; t < nq; ++t)
-        orc_quantize_value_token(v + (long)t * d, d, vbits, vcodes + (long)t * d, vs + t, vz + t);
+        quantize_value_token_grid(v + (long)t * d, d, vbits, grid, vcodes + (long)t * d, vs + t, vz + t);
     return nq;
 }
 
 int orc_append_stream_ds(uint16_t *hist_k, uint16_t *hist_v, int cap, int *n, int *nq,
                          const uint16_t *k_new, const uint16_t *v_new, int d,
-                         int kbits, int vbits, int G, int R, int n_out,
+                         int kbits, int vbits, int G, int R, int n_out, int grid,
                          uint8_t *kcodes, uint16_t *ks, uint16_t *kz,
                          uint8_t *vcodes, uint16_t *vs, uint16_t *vz,
                          uint16_t *opos, uint16_t *oval)
@@ -558,11 +585,13 @@ int orc_append_stream_ds(uint16_t *hist_k, uint16_t *hist_v, int cap, int *n, in
     *n += 1;
     if (*n - *nq == R + G) {
         int g = *nq / G;
-        orc_quantize_key_group_ds(hist_k + (long)(*nq) * d, G, d, kbits, n_out, kcodes + (long)(*nq) * d,
-                                  ks + (long)g * d, kz + (long)g * d, opos + (long)g * n_out,
-                                  oval + (long)g * n_out);
+        double klev[256];
+        if (grid) orc_codebook_levels(kbits, klev);
+        orc_quantize_key_group_ds(hist_k + (long)(*nq) * d, G, d, kbits, n_out, grid ? klev : NULL,
+                                  kcodes + (long)(*nq) * d, ks + (long)g * d, kz + (long)g * d,
+                                  opos + (long)g * n_out, oval + (long)g * n_out);
         for (int t = *nq; t < *nq + G; ++t)
-            orc_quantize_value_token(hist_v + (long)t * d, d, vbits, vcodes + (long)t * d, vs + t, vz + t);
+            quantize_value_token_grid(hist_v + (long)t * d, d, vbits, grid, vcodes + (long)t * d, vs + t, vz + t);
         *nq += G;
         return 1;
     }
@@ -570,12 +599,16 @@ int orc_append_stream_ds(uint16_t *hist_k, uint16_t *hist_v, int cap, int *n, in
 }
 
 void orc_dequantize_stream_ds(const uint16_t *k, const uint16_t *v, int n, int nq, int d, int G, int n_out,
+                              int kbits, int vbits, int grid,
                               const uint8_t *kcodes, const uint16_t *ks, const uint16_t *kz,
                               const uint8_t *vcodes, const uint16_t *vs, const uint16_t *vz,
                               const uint16_t *opos, const uint16_t *oval,
                               float *out_k, float *out_v)
 {
-    orc_dequantize_stream(k, v, n, nq, d, G, kcodes, ks, kz, vcodes, vs, vz, out_k, out_v);
+    if (grid)
+        orc_dequantize_stream_cb(k, v, n, nq, d, G, kbits, vbits, kcodes, ks, kz, vcodes, vs, vz, out_k, out_v);
+    else
+        orc_dequantize_stream(k, v, n, nq, d, G, kcodes, ks, kz, vcodes, vs, vz, out_k, out_v);
     for (int g = 0; g < nq / G; ++g)
         for (int e = 0; e < n_out; ++e) {
             int p = opos[(long)g * n_out + e];

@@ -19,8 +19,9 @@ LIB = os.path.join(HERE, "libkvq.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["kvq_api.hip", "kvq_quant.hip", "kvq_attn.hip", "kvq_attn_kivi.hip", "kvq_attn_rope.hip",
-           "kvq_attn_cb.hip", "kvq_attn_8bit.hip"]
-ATTN_KERNEL_SOURCES = ["kvq_attn_kivi.hip", "kvq_attn_rope.hip", "kvq_attn_cb.hip", "kvq_attn_8bit.hip"]
+           "kvq_attn_cb.hip", "kvq_attn_sparse.hip", "kvq_attn_8bit.hip"]
+ATTN_KERNEL_SOURCES = ["kvq_attn_kivi.hip", "kvq_attn_rope.hip", "kvq_attn_cb.hip", "kvq_attn_sparse.hip",
+                       "kvq_attn_8bit.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

@@ -77,6 +77,9 @@ kvq_status make_layout(const kvq_config* cfg, Layout* L) {
         fill_codebook(cfg->k_bits, L->klut, L->kmid);
         fill_codebook(cfg->v_bits, L->vlut, L->vmid);
     }
+    if (cfg->sparse_keys != 0 && cfg->sparse_keys != 1) return KVQ_EINVAL;
+    if (cfg->sparse_keys && (cfg->kv_format != kFmtKivi || cfg->rope_theta > 0.0f)) return KVQ_EUNSUPPORTED;
+    L->sparse = cfg->sparse_keys;
     L->fmt = cfg->kv_format;
     L->B = cfg->num_seqs;
     L->H = cfg->num_kv_heads;
@@ -109,7 +112,8 @@ kvq_status make_layout(const kvq_config* cfg, Layout* L) {
     // key table: per (group, channel) for KIVI, per token for INT8, none for FP8
     const int kmeta = L->fmt == kFmtKivi ? kD * 4 : L->fmt == kFmtInt8 ? G * 4 : 0;
     L->vmeta_off = L->kmeta_off + kmeta;
-    L->record = L->vmeta_off + (L->fmt == kFmtFp8 ? 0 : G * 4);
+    L->sparse_off = L->vmeta_off + (L->fmt == kFmtFp8 ? 0 : G * 4);
+    L->record = L->sparse_off + (L->sparse ? G * 4 : 0);
     return KVQ_OK;
 }
 
@@ -258,6 +262,16 @@ kvq_status kv_export_codes(const kvq_config* cfg, const kvq_cache* cache, uint8_
     if (out_tokens < 0 || out_tokens % L.G) return KVQ_EINVAL;
     return hip_status(launch_export(L, *cache, k_codes, v_codes, k_s, k_z, v_s, v_z, out_tokens,
                                     (hipStream_t)stream));
+}
+
+kvq_status kv_export_outliers(const kvq_config* cfg, const kvq_cache* cache, uint16_t* pos, uint16_t* val,
+                              int32_t out_tokens, void* stream) {
+    Layout L;
+    kvq_status st = make_layout(cfg, &L);
+    if (st != KVQ_OK) return st;
+    if ((st = check_cache(L, cache)) != KVQ_OK) return st;
+    if (!L.sparse || !pos || !val || out_tokens < 0 || out_tokens % L.G) return KVQ_EINVAL;
+    return hip_status(launch_export_outliers(L, *cache, pos, val, out_tokens, (hipStream_t)stream));
 }
 
 kvq_status kvq_codebook_levels(int32_t bits, float* levels_host) {

@@ -159,7 +159,8 @@ __global__ __launch_bounds__(256) void attn_merge_rows_kernel(Layout L, kvq_cach
 static inline int attn_key(const Layout& L) {
     if (L.fmt != kFmtKivi) return layout_key(L);
     const bool rp = L.rope_theta > 0.0f, cb = L.grid == KVQ_GRID_NORMAL_QUANTILE;
-    const int f = rp ? (cb ? kFmtRopeCb : kFmtRope) : (cb ? kFmtKiviCb : kFmtKivi);
+    const int f = L.sparse ? (cb ? kFmtKiviCbSp : kFmtKiviSp)
+                           : rp ? (cb ? kFmtRopeCb : kFmtRope) : (cb ? kFmtKiviCb : kFmtKivi);
     return layout_key(L) + f * 10000;
 }
 

@@ -168,8 +168,9 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 //        at VC + 1024 + 16l.  G = 16: record i's words of lane l at
 //        VC + i*64*VW*4 + VW*4*l (VW words per lane and record).
 //   META record i's key scale/zero table (512 B) then its value scale/zero
-//        table (4G B) at META + i*MREC.
-template <int G, int KB, int VB>
+//        table (4G B) at META + i*MREC; SP (dense-and-sparse keys): then its
+//        G kept-key entries (4G B).
+template <int G, int KB, int VB, bool SP = false>
 struct Stage {
     static constexpr int NR = 32 / G;
     static constexpr int SPT = G == 16 ? 4 : 8;
@@ -177,7 +178,7 @@ struct Stage {
     static constexpr int KC = 0;
     static constexpr int VC = 512 * KB;
     static constexpr int META = VC + 512 * VB;
-    static constexpr int MREC = 512 + 4 * G;
+    static constexpr int MREC = 512 + 4 * G + (SP ? 4 * G : 0);
     static constexpr int BYTES = META + NR * MREC;
     // 16-byte aligned and large enough to hold a wave's [16][128] fp32
     // accumulators at the end (two waves per stage array)
@@ -219,10 +220,10 @@ __device__ __forceinline__ void lds_load16(u32x4 desc, lds_u8* dst, int off) {
 // Issues the direct-to-LDS loads of one unit into stage buffer `buf` (wave
 // uniform address) and returns which of its records exist.  Every call issues
 // exactly Stage::LOADS load instructions, so the wait counts stay exact.
-template <int G, int KB, int VB, bool PG>
+template <int G, int KB, int VB, bool PG, bool SP = false>
 __device__ __forceinline__ uint32_t issue_unit(lds_u8* buf, const Layout& L, const kvq_cache& c, int b, int h,
                                                int unit, int ngroups, int lane) {
-    using S = Stage<G, KB, VB>;
+    using S = Stage<G, KB, VB, SP>;
     const int g = lane >> 4, n = lane & 15;
     // The buffer's LDS address, made opaque here so that the per-load M0
     // values are formed next to each load rather than hoisted out of the unit
@@ -261,7 +262,8 @@ __device__ __forceinline__ uint32_t issue_unit(lds_u8* buf, const Layout& L, con
                 lds_load16(rs, buf + S::VC + i * 512, L.vcode_off + 16 * lane);
             }
         }
-        if (lane < 32 + G / 4)
+        // key table, value table (and kept keys): contiguous in the record
+        if (lane < 32 + (SP ? G / 2 : G / 4))
             lds_load16(rs, buf + S::META + i * S::MREC,
                        lane < 32 ? L.kmeta_off + 16 * lane : L.vmeta_off + 16 * (lane - 32));
     }
@@ -441,9 +443,12 @@ __device__ __forceinline__ T lds_read(const lds_u8* p) {
 constexpr int kFmtRope = 3;
 constexpr int kFmtKiviCb = 4;
 constexpr int kFmtRopeCb = 5;
+constexpr int kFmtKiviSp = 6;     // dense-and-sparse keys, uniform grid
+constexpr int kFmtKiviCbSp = 7;   // dense-and-sparse keys, codebook grid
 constexpr bool low_bit(int F) { return F == kFmtKivi || F >= kFmtRope; }
 constexpr bool rope_fmt(int F) { return F == kFmtRope || F == kFmtRopeCb; }
-constexpr bool cb_fmt(int F) { return F == kFmtKiviCb || F == kFmtRopeCb; }
+constexpr bool cb_fmt(int F) { return F == kFmtKiviCb || F == kFmtRopeCb || F == kFmtKiviCbSp; }
+constexpr bool sp_fmt(int F) { return F == kFmtKiviSp || F == kFmtKiviCbSp; }
 constexpr int kTabPitch = 66;     // float2 per table row: rows of lanes n = 0..15 hit distinct banks
 typedef float f2 __attribute__((ext_vector_type(2)));
 
@@ -531,13 +536,52 @@ __device__ __forceinline__ void rope_key_tiles(const RopeLds* R, int wave, int l
     }
 }
 
+// ---------------------------------------------------------------------------
+// Dense-and-sparse keys ("KV Cache compression lab", experiment 03: KVQuant
+// keeps the few extreme keys in fp16 as a sparse matrix and quantizes the
+// rest).  A kept entry's code is 0, so the dense product gave it the
+// channel's zero z; its logit correction is q[head][c] * (x - z) for every
+// query head.  One lane per entry: the corrections are added into a per-wave
+// (head, token) tile in LDS (entries of one record in one instruction, so the
+// order of equal-address adds is fixed) and each lane adds its slots'.
+// ---------------------------------------------------------------------------
+struct SparseLds {
+    _Float16 q[kD][16];               // the segment's query, [channel][head]
+    float corr[kWaves][16][32];       // per wave: logit corrections [head][token of the unit]
+};
+
+template <int G, int MREC>
+__device__ __forceinline__ void sparse_corrections(const lds_u8* meta, SparseLds* SPL, int wave, int lane, int gq) {
+    f4* tile = (f4*)&SPL->corr[wave][0][0];
+    tile[2 * lane] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    tile[2 * lane + 1] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    wave_sync();
+#pragma unroll
+    for (int i = 0; i < 32 / G; ++i) {
+        const lds_u8* m = meta + i * MREC;
+        const uint32_t e = lane < G ? lds_read<uint32_t>(m + 512 + 4 * G + 4 * lane) : 0u;
+        // (a position outside the group, possible only in a record this
+        // library did not write, is ignored)
+        if (lane < G && (e & 0xffffu) < (uint32_t)(G * kD)) {
+            const int pos = (int)(e & 0xffffu), ch = pos & (kD - 1), tu = i * G + (pos >> 7);
+            const float d = h2f(e >> 16) - h2f(lds_read<uint16_t>(m + 256 + 2 * ch));
+            const h8 qa = __builtin_bit_cast(h8, *(const __attribute__((address_space(3))) u32x4*)&SPL->q[ch][0]);
+            const h8 qb = __builtin_bit_cast(h8, *(const __attribute__((address_space(3))) u32x4*)&SPL->q[ch][8]);
+            for (int h = 0; h < gq; ++h)
+                atomicAdd(&SPL->corr[wave][h][tu], (float)(h < 8 ? qa[h & 7] : qb[h & 7]) * d);
+        }
+    }
+    wave_sync();
+}
+
 // One staged unit (see Stage): key logits on the matrix cores, then the
 // online-softmax step and the value product.  RP: pre-RoPE keys (R, wave:
 // the rotation tables; t0: the unit's first token).
-template <int G, int KB, int VB, bool LP, bool RP, bool CB>
+template <int G, int KB, int VB, bool LP, bool RP, bool CB, bool SP>
 __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, WaveAcc& A, const QOps& Q, float sl2,
-                                             int lane, RopeLds* R, int wave, int t0, const Layout& L) {
-    using S = Stage<G, KB, VB>;
+                                             int lane, RopeLds* R, int wave, int t0, const Layout& L,
+                                             SparseLds* SPL, int gq) {
+    using S = Stage<G, KB, VB, SP>;
     constexpr int SPT = S::SPT;
     const int g = lane >> 4, n = lane & 15;
     const bool lo_limb = LP && (lane & 8);
@@ -643,6 +687,10 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
         }
     }
 
+    // dense-and-sparse keys: the kept entries' corrections q . (x - z) to
+    // their tokens' logits, gathered per (head, token) in the wave's tile
+    if constexpr (SP) sparse_corrections<G, S::MREC>(buf + S::META, SPL, wave, lane, gq);
+
     // value scale/zero of the lane's 8 slots: slot k = 4*rt + i <-> token 16rt + 4g + i
     float x[8], vs[8], vz[8];
     bool valid[8];
@@ -656,6 +704,7 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
             const int slot = S::NR == 2 ? i : k;
             // (pre-RoPE: both limb columns hold the same head's full logit)
             x[k] = LP && !RP ? add_limb_partner(C[rt][i]) : C[rt][i];
+            if constexpr (SP) x[k] += SPL->corr[wave][LP ? (n & 7) : n][16 * rt + 4 * g + i];
             vs[k] = h2f(lds_read<uint16_t>(vm + 2 * slot));
             vz[k] = h2f(lds_read<uint16_t>(vm + 2 * (SPT + slot)));
             valid[k] = S::NR == 1 || ((has >> rec) & 1);
@@ -921,21 +970,22 @@ __device__ __forceinline__ int unit_at(const SeqUnits& u, int x) {
 
 // Stage layout, unit issue and unit processing of a format.
 template <int G, int KB, int VB, int F>
-using StageT = typename std::conditional<low_bit(F), Stage<G, KB, VB>, Stage8<G, F>>::type;
+using StageT = typename std::conditional<low_bit(F), Stage<G, KB, VB, sp_fmt(F)>, Stage8<G, F>>::type;
 
 template <int G, int KB, int VB, int F, bool PG>
 __device__ __forceinline__ uint32_t issue_any(lds_u8* buf, const Layout& L, const kvq_cache& c, int b, int h,
                                               int unit, int ngroups, int lane) {
-    if constexpr (low_bit(F)) return issue_unit<G, KB, VB, PG>(buf, L, c, b, h, unit, ngroups, lane);
+    if constexpr (low_bit(F)) return issue_unit<G, KB, VB, PG, sp_fmt(F)>(buf, L, c, b, h, unit, ngroups, lane);
     else return issue_unit8<G, F, PG>(buf, L, c, b, h, unit, ngroups, lane);
 }
 
 template <int G, int KB, int VB, int F, bool LP>
 __device__ __forceinline__ void process_any(const lds_u8* buf, uint32_t has, WaveAcc& A, const QOps& Q, float sl2,
                                             float qsum, float vscl, int lane, RopeLds* R, int wave, int t0,
-                                            const Layout& L) {
+                                            const Layout& L, SparseLds* SPL, int gq) {
     if constexpr (low_bit(F))
-        process_unit<G, KB, VB, LP, rope_fmt(F), cb_fmt(F)>(buf, has, A, Q, sl2, lane, R, wave, t0, L);
+        process_unit<G, KB, VB, LP, rope_fmt(F), cb_fmt(F), sp_fmt(F)>(buf, has, A, Q, sl2, lane, R, wave, t0, L,
+                                                                       SPL, gq);
     else process_unit8<G, F, LP>(buf, has, A, Q, sl2, qsum, vscl, lane);
 }
 
@@ -948,7 +998,7 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
                                                float (*wpz)[16], const Layout& L, const kvq_cache& c,
                                                const half_t* __restrict__ q, float sl2, int gq, int b, int h,
                                                const SeqUnits& su, int lo, int hi, float* __restrict__ part,
-                                               int lane, int wave, RopeLds* R) {
+                                               int lane, int wave, RopeLds* R, SparseLds* SPL) {
     using S = StageT<G, KB, VB, F>;
     // The lane index, produced afresh: per-lane addresses derived from it are
     // formed here, once per segment, instead of being hoisted out of the
@@ -970,6 +1020,14 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
         // The unit loop's loads are invisible to the compiler's wait counting:
         // retire these here so that it places no wait on them inside the loop.
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    if constexpr (sp_fmt(F)) {
+        // the segment's query for the kept-key corrections, [channel][head]
+        for (int idx = tid; idx < kD * 16; idx += 256) {
+            const int ch = idx >> 4, hh = idx & 15;
+            SPL->q[ch][hh] = hh < gq ? q[((long)b * Hq + h * gq + hh) * kD + ch] : (_Float16)0.0f;
+        }
+        __syncthreads();
     }
     // 8-bit formats: sum_c q_c of the lane's head (INT8), the kv head's
     // static scales (FP8; the key scale joins the logit scale)
@@ -1009,7 +1067,7 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
                 }
                 wave_sync();
                 set_progress_prio((q1 - u + kWaves - 1) / kWaves, ntot);
-                process_any<G, KB, VB, F, LP>(sa, ha, A, Q, sl2q, qsum, vscl, lane, R, wave, 32 * u, L);
+                process_any<G, KB, VB, F, LP>(sa, ha, A, Q, sl2q, qsum, vscl, lane, R, wave, 32 * u, L, SPL, gq);
                 u += kWaves;
                 if (u >= q1) break;
                 if (u + kWaves < q1) {
@@ -1021,7 +1079,7 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
                 }
                 wave_sync();
                 set_progress_prio((q1 - u + kWaves - 1) / kWaves, ntot);
-                process_any<G, KB, VB, F, LP>(sb, hb, A, Q, sl2q, qsum, vscl, lane, R, wave, 32 * u, L);
+                process_any<G, KB, VB, F, LP>(sb, hb, A, Q, sl2q, qsum, vscl, lane, R, wave, 32 * u, L, SPL, gq);
                 u += kWaves;
                 if (u >= q1) break;
             }
@@ -1101,7 +1159,7 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
 // workgroups per CU, two waves per SIMD.
 // Pre-RoPE keys take registers for the rotation: three waves.
 constexpr int attn_waves(int G, int KB, int VB, int F, bool LP, bool PG) {
-    return rope_fmt(F) ? 3 : !low_bit(F) ? 2 : F == kFmtKiviCb ? 3 : LP && VB == 2 && !(G == 16 && KB == 2) ? 4 : 3;
+    return rope_fmt(F) ? 3 : !low_bit(F) ? 2 : F != kFmtKivi ? 3 : LP && VB == 2 && !(G == 16 && KB == 2) ? 4 : 3;
 }
 
 template <int G, int KB, int VB, int F, bool LP, bool PG>
@@ -1121,6 +1179,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
+    SparseLds* SPL = nullptr;
+    if constexpr (sp_fmt(F)) {
+        __shared__ __attribute__((aligned(16))) SparseLds sparse_lds;
+        SPL = &sparse_lds;
+    }
     RopeLds* R = nullptr;
     if constexpr (rope_fmt(F)) {
         __shared__ __attribute__((aligned(16))) RopeLds rope_lds;
@@ -1190,7 +1253,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves(
         }
         attend_segment<G, KB, VB, F, LP, PG>(stage_a, stage_b, wm, wl, wpz, L, c, q, sl2, gq, b, h, su,
                                           unit_at(su, lo), unit_at(su, hi), ws + ((long)w + s) * gq * kPart,
-                                          lane, wave, R);
+                                          lane, wave, R, SPL);
         if (ps + hi >= end) break;
         // next stream that has work (x < end <= T guarantees one)
         ps += su.cost;
@@ -1259,7 +1322,8 @@ int attn_family_slots(const Layout& L, int gq) {
 #define KVQ_8BIT_FAMILIES(X) X(16, 8, 8, kFmtInt8) X(32, 8, 8, kFmtInt8) X(16, 8, 8, kFmtFp8) X(32, 8, 8, kFmtFp8)
 #define KVQ_ALL_FAMILIES(X)                                                                             \
     KVQ_LOW_BIT_FAMILIES(X, kFmtKivi) KVQ_LOW_BIT_FAMILIES(X, kFmtRope) KVQ_LOW_BIT_FAMILIES(X, kFmtKiviCb) \
-    KVQ_LOW_BIT_FAMILIES(X, kFmtRopeCb) KVQ_8BIT_FAMILIES(X)
+    KVQ_LOW_BIT_FAMILIES(X, kFmtRopeCb) KVQ_LOW_BIT_FAMILIES(X, kFmtKiviSp)                                 \
+    KVQ_LOW_BIT_FAMILIES(X, kFmtKiviCbSp) KVQ_8BIT_FAMILIES(X)
 
 #define KVQ_INSTANTIATE_FAMILY(GG, KB, VB, FF)                                                                     \
     template hipError_t launch_attn_family<GG, KB, VB, FF>(const Layout&, const AttnPlan&, const kvq_cache&,        \

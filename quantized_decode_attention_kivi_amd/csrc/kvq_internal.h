@@ -35,6 +35,10 @@
 // out like the value table (kmeta_off, 4G bytes, INT8 only), and FP8 records
 // carry no tables at all (its scales are per kv head, outside the records).
 //
+// Dense-and-sparse keys add, after the value table, G 4-byte entries
+// (position t*128 + c in the low half, the fp16 key in the high half), in
+// ascending position order: the group's kept extreme keys.
+//
 // Contiguous caches address record (b, h, g) at ((b*H + h)*groups + g); paged
 // caches at (block_table[b][g]*H + h).  The fp16 residual ring of (b, h) holds
 // token i at slot i % (R + G), token-major, 128 channels per slot.
@@ -61,6 +65,8 @@ struct Layout {
     int grid;                                     // KVQ_GRID_*
     uint32_t klut[4], vlut[4];                    // codebook: byte k = F_b * L_k (key / value bits)
     float kmid[15], vmid[15];                     // codebook: midpoints of consecutive levels, grid steps
+    int sparse;                                   // dense-and-sparse keys: G kept (pos, fp16) pairs per record
+    int sparse_off;                               // their offset in the record (after the value table)
     int B, H, kbits, vbits, G, R, ring;
     int paged, num_blocks, max_blocks, groups;   // groups: record slots per sequence
     int capacity;                                 // max tokens a sequence may hold
@@ -110,6 +116,8 @@ hipError_t launch_dequantize(const Layout& L, const kvq_cache& c, float* ko, flo
                              hipStream_t s);
 hipError_t launch_export(const Layout& L, const kvq_cache& c, uint8_t* kc, uint8_t* vc, uint16_t* ks,
                          uint16_t* kz, uint16_t* vs, uint16_t* vz, int out_tokens, hipStream_t s);
+hipError_t launch_export_outliers(const Layout& L, const kvq_cache& c, uint16_t* pos, uint16_t* val, int out_tokens,
+                                  hipStream_t s);
 
 struct AttnPlan {
     int nwg;             // attention workgroups (each an equal share of the batch's units)

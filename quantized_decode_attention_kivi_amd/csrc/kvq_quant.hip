@@ -16,7 +16,87 @@ struct QuantSmem {
     float kmn[16][kD], kmx[16][kD];   // per token slice, per channel
     float kz[kD], kinv[kD];
     uint8_t vcode[G][kD];             // value codes before packing
+    int red[2][4];                    // dense-and-sparse: per-wave counts (double-buffered)
+    uint32_t kept[G * kD / 32];       // dense-and-sparse: kept positions, one bit each
+    int wtot[2];                      // dense-and-sparse: kept count of the first two words' waves
 };
+
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// Dense-and-sparse keys ("KV Cache compression lab", experiment 03: KVQuant
+// keeps the few extreme keys in fp16 as a sparse matrix).  Marks in kbit[]
+// the group's G entries of largest |x| (ties: lower position) and writes
+// them, in ascending position order, as (position, fp16) pairs at `sparse`.
+// Each entry's key ((|x| bits) << 12 | (4095 - position)) is unique, so the
+// G-th largest key, found bit by bit from the top by counting keys at or
+// above each candidate, selects exactly G entries.  All 256 threads.
+template <int G>
+__device__ __forceinline__ void select_extremes(QuantSmem<G>& sm, const uint32_t (&kb)[G / 16][8],
+                                                uint32_t (&kbit)[G / 16], const half_t* __restrict__ ksrc,
+                                                uint32_t* __restrict__ sparse) {
+    constexpr int NT = G / 16;
+    const int tid = threadIdx.x, cg = tid & 15, ts = tid >> 4, lane = tid & 63, wave = tid >> 6;
+    uint32_t key[NT][8];
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            key[j][e] = ((kb[j][e] & 0x7fffu) << 12) | (4095u - (uint32_t)((ts + 16 * j) * kD + 8 * cg + e));
+    uint32_t T = 0;
+    for (int bit = 26; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) cnt += key[j][e] >= cand ? 1 : 0;
+        cnt = wave_sum_i(cnt);
+        if (lane == 0) sm.red[bit & 1][wave] = cnt;
+        __syncthreads();
+        cnt = sm.red[bit & 1][0] + sm.red[bit & 1][1] + sm.red[bit & 1][2] + sm.red[bit & 1][3];
+        if (cnt >= G) T = cand;
+    }
+    for (int i = tid; i < G * kD / 32; i += 256) sm.kept[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        kbit[j] = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (key[j][e] >= T) {
+                kbit[j] |= 1u << e;
+                const int pos = (ts + 16 * j) * kD + 8 * cg + e;
+                atomicOr(&sm.kept[pos >> 5], 1u << (pos & 31));
+            }
+    }
+    __syncthreads();
+    // ordered compaction: word i covers positions 32i .. 32i + 31
+    constexpr int W = G * kD / 32;   // 64 or 128 words: the first one or two waves
+    const int mine = tid < W ? __builtin_popcount(sm.kept[tid]) : 0;
+    int incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63 && wave < 2) sm.wtot[wave] = incl;
+    __syncthreads();
+    if (tid < W) {
+        int idx = incl - mine + (wave == 1 ? sm.wtot[0] : 0);
+        uint32_t w = sm.kept[tid];
+        while (w) {
+            const int b = __builtin_ctz(w);
+            w &= w - 1;
+            const int pos = 32 * tid + b;
+            const uint32_t val = __builtin_bit_cast(uint16_t, ksrc[pos]);
+            sparse[idx++] = (val << 16) | (uint32_t)pos;
+        }
+    }
+}
 
 // Code of x on the set's grid: uniform (rint), or the normal-quantile
 // codebook's nearest level (CB; mid: its midpoints).
@@ -34,17 +114,16 @@ __device__ __forceinline__ uint32_t code_of(float x, float z, float inv, const f
 // record.  Called by all 256 threads of a workgroup.  Thread (ts = tid/16,
 // cg = tid%16) holds channels 8cg..8cg+7 of tokens ts, ts+16, ...  CB: the
 // normal-quantile codebook grid instead of the uniform one.
-template <int G, int KB, int VB, bool CB>
+template <int G, int KB, int VB, bool CB, bool SP>
 __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* __restrict__ ksrc,
                                const half_t* __restrict__ vsrc, uint8_t* __restrict__ rec) {
     constexpr int NT = G / 16;
-    constexpr float kq = (float)((1 << KB) - 1);
-    constexpr float vq = (float)((1 << VB) - 1);
     const int tid = threadIdx.x;
     const int cg = tid & 15;
     const int ts = tid >> 4;
 
     float kx[NT][8], vx[NT][8];
+    uint32_t kraw[NT][8];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
         const int t = ts + 16 * j;
@@ -54,21 +133,28 @@ __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* 
         const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
+            kraw[j][2 * e] = aw[e] & 0xffffu;
+            kraw[j][2 * e + 1] = aw[e] >> 16;
             kx[j][2 * e] = h2f(aw[e] & 0xffffu);
             kx[j][2 * e + 1] = h2f(aw[e] >> 16);
             vx[j][2 * e] = h2f(bw[e] & 0xffffu);
             vx[j][2 * e + 1] = h2f(bw[e] >> 16);
         }
     }
+    // dense-and-sparse: the kept extremes leave the channels' ranges
+    uint32_t kbit[NT] = {};
+    if constexpr (SP) select_extremes<G>(sm, kraw, kbit, ksrc, (uint32_t*)(rec + L.sparse_off));
 
-    // Key statistics: per channel over the G tokens.
+    // Key statistics: per channel over the G tokens (without kept extremes).
+    constexpr float kInf = __builtin_huge_valf();
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        float mn = kx[0][e], mx = kx[0][e];
+        float mn = kInf, mx = -kInf;
 #pragma unroll
-        for (int j = 1; j < NT; ++j) {
-            mn = fminf(mn, kx[j][e]);
-            mx = fmaxf(mx, kx[j][e]);
+        for (int j = 0; j < NT; ++j) {
+            const bool k = SP && ((kbit[j] >> e) & 1);
+            mn = fminf(mn, k ? kInf : kx[j][e]);
+            mx = fmaxf(mx, k ? -kInf : kx[j][e]);
         }
         sm.kmn[ts][8 * cg + e] = mn;
         sm.kmx[ts][8 * cg + e] = mx;
@@ -104,6 +190,7 @@ __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* 
             mn = fminf(mn, sm.kmn[j][tid]);
             mx = fmaxf(mx, sm.kmx[j][tid]);
         }
+        if (mn > mx) mn = mx = 0.0f;   // every value of the channel kept: s = z = 0
         const QParams p = make_qparams(mn, mx, KB);
         sm.kz[tid] = p.z;
         sm.kinv[tid] = p.inv;
@@ -125,7 +212,7 @@ __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* 
         uint32_t w = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const uint32_t q = code_of<CB, KB>(kx[j][e], kzr[e], kir[e], L.kmid);
+            const uint32_t q = SP && ((kbit[j] >> e) & 1) ? 0u : code_of<CB, KB>(kx[j][e], kzr[e], kir[e], L.kmid);
             w |= q << (KB == 4 ? code_bit(4, e) : code_bit(2, e + 8 * (cg & 1)));
         }
         if (KB == 4) {
@@ -261,13 +348,26 @@ __device__ void quantize_group8(QuantSmem<G>& sm, const Layout& L, const half_t*
     __syncthreads();  // LDS may be reused by the caller
 }
 
-// Quantizes one group of the format F (kFmtKivi: key bits KB, value bits VB).
+// Quantizer variants (compile-time): the 8-bit formats kFmtInt8 and kFmtFp8,
+// and the low-bit format on the uniform grid (kQUniform), the codebook
+// grid (kQCodebook), each with dense-and-sparse keys (kQSparse, kQCodebookSparse).
+constexpr int kQUniform = 0, kQCodebook = 4, kQSparse = 6, kQCodebookSparse = 7;
+__host__ __device__ constexpr bool q_low_bit(int F) { return F == kQUniform || F >= kQCodebook; }
+
+// Variant of a layout (host).
+inline int quant_variant(const Layout& L) {
+    if (L.fmt != kFmtKivi) return L.fmt;
+    const bool cb = L.grid == KVQ_GRID_NORMAL_QUANTILE;
+    return L.sparse ? (cb ? kQCodebookSparse : kQSparse) : (cb ? kQCodebook : kQUniform);
+}
+
+// Quantizes one group in variant F (low-bit: key bits KB, value bits VB).
 template <int G, int KB, int VB, int F>
 __device__ __forceinline__ void quantize_any(QuantSmem<G>& sm, const Layout& L, const kvq_cache& c, int h,
                                              const half_t* ksrc, const half_t* vsrc, uint8_t* rec) {
-    if (F == kFmtKivi) {
-        if (L.grid == KVQ_GRID_NORMAL_QUANTILE) quantize_group<G, KB, VB, true>(sm, L, ksrc, vsrc, rec);
-        else quantize_group<G, KB, VB, false>(sm, L, ksrc, vsrc, rec);
+    if constexpr (q_low_bit(F)) {
+        quantize_group<G, KB, VB, F == kQCodebook || F == kQCodebookSparse, F == kQSparse || F == kQCodebookSparse>(
+            sm, L, ksrc, vsrc, rec);
     } else {
         const float kinv = F == kFmtFp8 ? fp8_inv_scale(c.k_scale[h]) : 0.0f;
         const float vinv = F == kFmtFp8 ? fp8_inv_scale(c.v_scale[h]) : 0.0f;
@@ -454,27 +554,60 @@ __global__ __launch_bounds__(256) void export_kernel(Layout L, kvq_cache c, uint
     }
 }
 
+// Dense-and-sparse keys: kept entries of group g of stream sh (grid
+// (groups, B*H), G threads).  restore: write them over the dequantized keys;
+// export: the logical (position, value) lists.
+__global__ void restore_outliers_kernel(Layout L, kvq_cache c, float* ko, int out_tokens) {
+    const int g = blockIdx.x, sh = blockIdx.y, e = threadIdx.x;
+    const int b = sh / L.H, h = sh % L.H;
+    const int nq = max(c.n_quant[b], 0);
+    if ((g + 1) * L.G > nq || e >= L.G) return;
+    const uint8_t* rec = record_at(L, c.packed, c.block_table, b, h, g);
+    if (!rec) return;
+    const uint32_t w = ((const uint32_t*)(rec + L.sparse_off))[e];
+    const int pos = (int)(w & 0xffffu);
+    const int t = g * L.G + (pos >> 7);
+    if (pos < L.G * kD && t < out_tokens) ko[((long)sh * out_tokens + t) * kD + (pos & (kD - 1))] = h2f(w >> 16);
+}
+
+__global__ void export_outliers_kernel(Layout L, kvq_cache c, uint16_t* pos, uint16_t* val, int out_tokens) {
+    const int g = blockIdx.x, sh = blockIdx.y, e = threadIdx.x;
+    const int b = sh / L.H, h = sh % L.H;
+    if (e >= L.G) return;
+    const long o = ((long)sh * (out_tokens / L.G) + g) * L.G + e;
+    const int nq = max(c.n_quant[b], 0);
+    const uint8_t* rec = (g + 1) * L.G <= nq ? record_at(L, c.packed, c.block_table, b, h, g) : nullptr;
+    const uint32_t w = rec ? ((const uint32_t*)(rec + L.sparse_off))[e] : 0u;
+    pos[o] = (uint16_t)(w & 0xffffu);
+    val[o] = (uint16_t)(w >> 16);
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 
-#define KVQ_DISPATCH(L_, F)                                                    \
-    do {                                                                       \
-        switch (layout_key(L_)) {                                              \
-            case 1622: F(16, 2, 2, kFmtKivi); break;                           \
-            case 1624: F(16, 2, 4, kFmtKivi); break;                           \
-            case 1642: F(16, 4, 2, kFmtKivi); break;                           \
-            case 1644: F(16, 4, 4, kFmtKivi); break;                           \
-            case 3222: F(32, 2, 2, kFmtKivi); break;                           \
-            case 3224: F(32, 2, 4, kFmtKivi); break;                           \
-            case 3242: F(32, 4, 2, kFmtKivi); break;                           \
-            case 3244: F(32, 4, 4, kFmtKivi); break;                           \
-            case 11688: F(16, 8, 8, kFmtInt8); break;                          \
-            case 13288: F(32, 8, 8, kFmtInt8); break;                          \
-            case 21688: F(16, 8, 8, kFmtFp8); break;                           \
-            case 23288: F(32, 8, 8, kFmtFp8); break;                           \
-            default: return hipErrorInvalidValue;                              \
-        }                                                                      \
+#define KVQ_LOW_BIT_Q(F, Q)                                                                                   \
+    case Q * 10000 + 1622: F(16, 2, 2, Q); break;                                                           \
+    case Q * 10000 + 1624: F(16, 2, 4, Q); break;                                                           \
+    case Q * 10000 + 1642: F(16, 4, 2, Q); break;                                                           \
+    case Q * 10000 + 1644: F(16, 4, 4, Q); break;                                                           \
+    case Q * 10000 + 3222: F(32, 2, 2, Q); break;                                                           \
+    case Q * 10000 + 3224: F(32, 2, 4, Q); break;                                                           \
+    case Q * 10000 + 3242: F(32, 4, 2, Q); break;                                                           \
+    case Q * 10000 + 3244: F(32, 4, 4, Q); break;
+#define KVQ_DISPATCH(L_, F)                                                                                    \
+    do {                                                                                                       \
+        switch (quant_variant(L_) * 10000 + (L_).G * 100 + (L_).kbits * 10 + (L_).vbits) {                    \
+            KVQ_LOW_BIT_Q(F, kQUniform)                                                                        \
+            KVQ_LOW_BIT_Q(F, kQCodebook)                                                                       \
+            KVQ_LOW_BIT_Q(F, kQSparse)                                                                         \
+            KVQ_LOW_BIT_Q(F, kQCodebookSparse)                                                                 \
+            case 11688: F(16, 8, 8, kFmtInt8); break;                                                          \
+            case 13288: F(32, 8, 8, kFmtInt8); break;                                                          \
+            case 21688: F(16, 8, 8, kFmtFp8); break;                                                           \
+            case 23288: F(32, 8, 8, kFmtFp8); break;                                                           \
+            default: return hipErrorInvalidValue;                                                              \
+        }                                                                                                      \
     } while (0)
 
 hipError_t launch_prefill(const Layout& L, const kvq_cache& c, const half_t* k, const half_t* v,
@@ -508,6 +641,20 @@ hipError_t launch_dequantize(const Layout& L, const kvq_cache& c, float* ko, flo
     if (out_tokens <= 0) return hipSuccess;
     dim3 grid((out_tokens + 15) / 16, L.B * L.H);
     hipLaunchKernelGGL(dequantize_kernel, grid, dim3(256), 0, s, L, c, ko, vo, out_tokens);
+    if (L.sparse) {
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(restore_outliers_kernel, dim3((out_tokens + L.G - 1) / L.G, L.B * L.H), dim3(L.G), 0, s, L,
+                           c, ko, out_tokens);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_export_outliers(const Layout& L, const kvq_cache& c, uint16_t* pos, uint16_t* val, int out_tokens,
+                                  hipStream_t s) {
+    if (out_tokens <= 0) return hipSuccess;
+    hipLaunchKernelGGL(export_outliers_kernel, dim3(out_tokens / L.G, L.B * L.H), dim3(L.G), 0, s, L, c, pos, val,
+                       out_tokens);
     return hipGetLastError();
 }
 

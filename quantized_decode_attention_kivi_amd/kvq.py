@@ -34,7 +34,7 @@ class kvq_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_seqs", "num_kv_heads", "head_dim", "k_bits", "v_bits", "group_size", "residual",
         "max_tokens", "block_size", "num_blocks", "max_blocks_per_seq", "kv_format")] + \
-        [("rope_theta", ctypes.c_float), ("grid", ctypes.c_int32)]
+        [("rope_theta", ctypes.c_float), ("grid", ctypes.c_int32), ("sparse_keys", ctypes.c_int32)]
 
 
 class kvq_cache(ctypes.Structure):
@@ -52,7 +52,8 @@ class kvq_sizes(ctypes.Structure):
 
 EXPORTED = ["kvq_buffer_sizes", "kv_quantize_prefill", "kv_append_token", "kv_dequantize",
             "kv_decode_attention_workspace_bytes", "kv_decode_attention", "kv_decode_attention_partials",
-            "kv_decode_attention_merge", "kv_export_codes", "kvq_codebook_levels", "kvq_status_string",
+            "kv_decode_attention_merge", "kv_export_codes", "kv_export_outliers", "kvq_codebook_levels",
+            "kvq_status_string",
             "kvq_last_error"]
 
 
@@ -94,6 +95,8 @@ def lib():
         L.kv_decode_attention_merge.restype = ctypes.c_int
         L.kv_export_codes.argtypes = [P(kvq_config), P(kvq_cache)] + [vp] * 6 + [ctypes.c_int32, vp]
         L.kv_export_codes.restype = ctypes.c_int
+        L.kv_export_outliers.argtypes = [P(kvq_config), P(kvq_cache), vp, vp, ctypes.c_int32, vp]
+        L.kv_export_outliers.restype = ctypes.c_int
         L.kvq_codebook_levels.argtypes = [ctypes.c_int32, P(ctypes.c_float)]
         L.kvq_codebook_levels.restype = ctypes.c_int
         L.kvq_status_string.argtypes = [ctypes.c_int]
@@ -174,6 +177,11 @@ def kv_export_codes(cfg, cache, k_codes, v_codes, k_s, k_z, v_s, v_z, out_tokens
                                  _stream(stream)), "kv_export_codes")
 
 
+def kv_export_outliers(cfg, cache, pos, val, out_tokens, stream=None):
+    _check(lib().kv_export_outliers(ctypes.byref(cfg), ctypes.byref(cache), _ptr(pos), _ptr(val), int(out_tokens),
+                                    _stream(stream)), "kv_export_outliers")
+
+
 def kvq_codebook_levels(bits) -> np.ndarray:
     out = (ctypes.c_float * (1 << int(bits)))()
     _check(lib().kvq_codebook_levels(int(bits), out), "kvq_codebook_levels")
@@ -203,12 +211,13 @@ class CacheShape:
     kv_format: int = FORMAT_KIVI
     rope_theta: float = 0.0      # > 0: keys are pre-RoPE, rotated on read with this base
     grid: int = 0                # GRID_UNIFORM or GRID_NORMAL_QUANTILE (low-bit format)
+    sparse_keys: int = 0         # 1: dense-and-sparse keys (G kept fp16 keys per group)
 
     def config(self) -> kvq_config:
         return kvq_config(self.num_seqs, self.num_kv_heads, HEAD_DIM, self.k_bits, self.v_bits,
                           self.group_size, self.residual, self.max_tokens if not self.paged else 0,
                           self.group_size if self.paged else 0, self.num_blocks, self.max_blocks_per_seq,
-                          self.kv_format, self.rope_theta, self.grid)
+                          self.kv_format, self.rope_theta, self.grid, self.sparse_keys)
 
 
 class QuantizedKVCache:
@@ -392,6 +401,17 @@ class QuantizedKVCache:
             vz = torch.empty_like(vs)
         kv_export_codes(self.cfg, self.cache, kc, vc, ks, kz, vs, vz, T, stream)
         return kc, vc, ks, kz, vs, vz
+
+    def export_outliers(self, out_tokens=None, stream=None):
+        """Dense-and-sparse keys: (positions, fp16 values) [B][H][T/G][G]."""
+        G = self.G
+        T = int(out_tokens if out_tokens is not None else max(int(self.lens.max()), 1))
+        T = (T + G - 1) // G * G
+        B, H = self.shape.num_seqs, self.shape.num_kv_heads
+        pos = torch.empty((B, H, T // G, G), dtype=torch.int16, device=self.device)
+        val = torch.empty_like(pos)
+        kv_export_outliers(self.cfg, self.cache, pos, val, T, stream)
+        return pos, val
 
     def workspace(self, num_q_heads):
         nb = kv_decode_attention_workspace_bytes(self.cfg, num_q_heads)

@@ -44,6 +44,7 @@ class Workload:
     kv_format: int = 0           # 0 low-bit KIVI, 1 INT8 per token, 2 FP8 E4M3 static
     rope_theta: float = 0.0      # > 0: the keys are pre-RoPE (rotated on read with this base)
     grid: int = 0                # 0 uniform levels, 1 normal-quantile codebook (low-bit format)
+    sparse_keys: int = 0         # 1: dense-and-sparse keys (G kept fp16 keys per group)
 
     @property
     def gq(self) -> int:
@@ -108,7 +109,18 @@ WORKLOADS_CODEBOOK = {
         v_bits=2, group_size=32, residual=128, context=131072, tag=3, grid=1),
 }
 
-_TABLES = (WORKLOADS, WORKLOADS_8BIT, WORKLOADS_ROPE, WORKLOADS_CODEBOOK)
+# Dense-and-sparse keys ("KV Cache compression lab", experiment 03) on the
+# same two shapes and data.
+WORKLOADS_SPARSE = {
+    "llama3_8b_layer_b8_32k_int4_sparse": Workload(
+        "llama3_8b_layer_b8_32k_int4_sparse", num_seqs=8, num_q_heads=32, num_kv_heads=8, k_bits=4,
+        v_bits=4, group_size=32, residual=128, context=32768, tag=2, sparse_keys=1),
+    "llama3_70b_layer_b1_128k_int2_sparse": Workload(
+        "llama3_70b_layer_b1_128k_int2_sparse", num_seqs=1, num_q_heads=64, num_kv_heads=8, k_bits=2,
+        v_bits=2, group_size=32, residual=128, context=131072, tag=3, sparse_keys=1),
+}
+
+_TABLES = (WORKLOADS, WORKLOADS_8BIT, WORKLOADS_ROPE, WORKLOADS_CODEBOOK, WORKLOADS_SPARSE)
 
 
 def workload(name: str) -> Workload:

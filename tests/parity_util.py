@@ -29,11 +29,13 @@ def make_cache(w: synth.Workload, lens, max_tokens=None, num_blocks=None, shuffl
                                                                for n in lens)) + 4
         shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, G, R, paged=True,
                                num_blocks=nb, max_blocks_per_seq=mb, kv_format=w.kv_format,
-                               rope_theta=w.rope_theta, grid=w.grid)
+                               rope_theta=w.rope_theta, grid=w.grid,
+                               sparse_keys=w.sparse_keys)
     else:
         shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, G, R,
                                max_tokens=max_tokens if max_tokens is not None else int(np.max(lens)) + 64,
-                               kv_format=w.kv_format, rope_theta=w.rope_theta, grid=w.grid)
+                               kv_format=w.kv_format, rope_theta=w.rope_theta, grid=w.grid,
+                               sparse_keys=w.sparse_keys)
     ks, vs = scales if scales is not None else (None, None)
     c = kvq.QuantizedKVCache(shape, k_scale=ks, v_scale=vs)
     if w.paged and shuffle_seed is not None:
@@ -48,7 +50,8 @@ def oracle_states(kb: np.ndarray, vb: np.ndarray, lens, w: synth.Workload, cap=N
     if scales is not None:
         ks, vs = (t.detach().cpu().numpy().astype(np.float32) for t in scales)
     return oracle.prefill_batch(kb, vb, lens, w.k_bits, w.v_bits, w.group_size, w.residual,
-                                cap=cap, threads=THREADS, fmt=w.kv_format, kscales=ks, vscales=vs, grid=w.grid)
+                                cap=cap, threads=THREADS, fmt=w.kv_format, kscales=ks, vscales=vs, grid=w.grid,
+                                sparse=bool(w.sparse_keys))
 
 
 def compare_codes(cache: kvq.QuantizedKVCache, states, streams=None):
@@ -72,6 +75,8 @@ def compare_codes(cache: kvq.QuantizedKVCache, states, streams=None):
         kd, vd = [t[0].cpu().numpy() for t in view.dequantize(T)]
         nt = int(view.n_tokens.cpu()[0])
         nqs = int(view.n_quant.cpu()[0])
+        if cache.shape.sparse_keys:
+            opos, oval = [t[0].cpu().numpy().view(np.uint16) for t in view.export_outliers(T)]
         for h in heads:
             st = states[b][h]
             assert nt == st.n and nqs == st.nq, (b, nt, st.n, nqs, st.nq)
@@ -86,6 +91,11 @@ def compare_codes(cache: kvq.QuantizedKVCache, states, streams=None):
                 ovs, ovz = st.value_meta()
                 assert np.array_equal(vs[h, :nq], ovs), ("value scales", b, h)
                 assert np.array_equal(vz[h, :nq], ovz), ("value zeros", b, h)
+            if cache.shape.sparse_keys:
+                sp, sv = st.outliers()
+                assert np.array_equal(opos[h, :nq // G], sp), ("kept key positions", b, h)
+                assert np.array_equal(oval[h, :nq // G], sv), ("kept key values", b, h)
+                assert not opos[h, nq // G:].any() and not oval[h, nq // G:].any()
             okd, ovd = st.dequantize()
             assert np.array_equal(kd[h, :n], okd), ("dequantized keys", b, h)
             assert np.array_equal(vd[h, :n], ovd), ("dequantized values", b, h)

@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 def _cfg(kvq, **kw):
     d = dict(num_seqs=2, num_kv_heads=3, head_dim=128, k_bits=4, v_bits=2, group_size=32, residual=64,
              max_tokens=1000, block_size=0, num_blocks=0, max_blocks_per_seq=0, kv_format=0, rope_theta=0.0,
-             grid=0)
+             grid=0, sparse_keys=0)
     d.update(kw)
     return kvq.kvq_config(**d)
 
@@ -157,6 +157,28 @@ def test_grid_validation(kw, status):
     assert kvq.lib().kvq_buffer_sizes(ctypes.byref(cfg), ctypes.byref(out)) == getattr(kvq, status)
     bad = (ctypes.c_float * 16)()
     assert kvq.lib().kvq_codebook_levels(3, bad) == kvq.KVQ_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sparse_keys=2), "KVQ_EINVAL"),
+    (dict(sparse_keys=1, kv_format=2, k_bits=8, v_bits=8), "KVQ_EUNSUPPORTED"),
+    (dict(sparse_keys=1, rope_theta=10000.0), "KVQ_EUNSUPPORTED"),
+])
+def test_sparse_validation(kw, status):
+    kvq = _kvq()
+    cfg = _cfg(kvq, **kw)
+    out = kvq.kvq_sizes()
+    assert kvq.lib().kvq_buffer_sizes(ctypes.byref(cfg), ctypes.byref(out)) == getattr(kvq, status)
+
+
+@pytest.mark.parametrize("G", [16, 32])
+def test_sparse_record_size(G):
+    """Dense-and-sparse keys add G (position, fp16) pairs of 4 bytes to every
+    record."""
+    kvq = _kvq()
+    a = kvq.kvq_buffer_sizes(_cfg(kvq, group_size=G, residual=2 * G))
+    b = kvq.kvq_buffer_sizes(_cfg(kvq, group_size=G, residual=2 * G, sparse_keys=1))
+    assert b.record_bytes == a.record_bytes + 4 * G and b.packed_bytes == a.packed_bytes // a.record_bytes * b.record_bytes
 
 
 def test_paged_sizes():

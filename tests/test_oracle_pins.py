@@ -948,6 +948,29 @@ def test_ds_stream_roundtrip_and_appends(orc, G, R):
     assert np.all(err[~kept] <= _roundtrip_bound(xk, s, z, 2)[~kept])
 
 
+def test_ds_codebook_dense_part_is_the_codebook_on_the_rest(orc):
+    """Dense-and-sparse on the codebook grid: the kept extremes as on the
+    uniform grid, the rest of each channel on the codebook quantizer."""
+    rng = np.random.default_rng(153)
+    G = 32
+    x = _ds_group(rng, G)
+    xb = x.view(np.uint16)
+    st = orc.StreamState.prefill(xb, xb, 2, 2, G, 0, sparse=True, grid=orc.GRID_CODEBOOK)
+    pos, val = st.outliers()
+    u = orc.quantize_key_group_ds(xb, 2, G)
+    assert np.array_equal(pos[0], u[3]) and np.array_equal(val[0], u[4])
+    kept = np.zeros(G * 128, bool)
+    kept[pos[0]] = True
+    kept = kept.reshape(G, 128)
+    codes = st.key_codes()
+    s16, z16 = st.key_meta()
+    for c in range(128):
+        rest = xb[~kept[:, c], c]
+        if rest.size:
+            cc, s, z = orc.quantize_value_token_cb(rest, 2)
+            assert np.array_equal(codes[~kept[:, c], c], cc) and s16[0, c] == s and z16[0, c] == z
+
+
 def test_ds_lowers_key_error(orc):
     """The purpose: at 2 bits, keeping the few extreme keys exact lowers the
     key error of the synthetic keys (outlier channels) against per-channel
