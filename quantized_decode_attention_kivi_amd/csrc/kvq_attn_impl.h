@@ -541,35 +541,58 @@ __device__ __forceinline__ void rope_key_tiles(const RopeLds* R, int wave, int l
 // keeps the few extreme keys in fp16 as a sparse matrix and quantizes the
 // rest).  A kept entry's code is 0, so the dense product gave it the
 // channel's zero z; its logit correction is q[head][c] * (x - z) for every
-// query head.  One lane per entry: the corrections are added into a per-wave
-// (head, token) tile in LDS (entries of one record in one instruction, so the
-// order of equal-address adds is fixed) and each lane adds its slots'.
+// query head.  The unit's entries are sorted by token, so each entry lane
+// marks where its token's run starts and ends; then lane t (one per token)
+// sums its run's corrections for all heads in registers and writes them to a
+// per-wave [token][head] tile, from which each lane adds its logit slots'.
+// No atomics: LDS atomics serialise across lanes.
 // ---------------------------------------------------------------------------
 struct SparseLds {
     _Float16 q[kD][16];               // the segment's query, [channel][head]
-    float corr[kWaves][16][32];       // per wave: logit corrections [head][token of the unit]
+    float corr[kWaves][32][16];       // per wave: logit corrections [token of the unit][head]
+    uint8_t run[kWaves][2][32];       // per wave: first and one-past-last entry of each token
 };
 
 template <int G, int MREC>
-__device__ __forceinline__ void sparse_corrections(const lds_u8* meta, SparseLds* SPL, int wave, int lane, int gq) {
-    f4* tile = (f4*)&SPL->corr[wave][0][0];
-    tile[2 * lane] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    tile[2 * lane + 1] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    wave_sync();
-#pragma unroll
-    for (int i = 0; i < 32 / G; ++i) {
-        const lds_u8* m = meta + i * MREC;
-        const uint32_t e = lane < G ? lds_read<uint32_t>(m + 512 + 4 * G + 4 * lane) : 0u;
+__device__ __forceinline__ void sparse_corrections(const lds_u8* meta, SparseLds* SPL, int wave, int lane) {
+    // entry o = i*G + l of the unit (record i, entry l; ascending tokens)
+    uint8_t(&run)[2][32] = SPL->run[wave];
+    if (lane < 16) ((uint32_t*)&run[0][0])[lane] = 0u;   // empty runs
+    int tok = 255;
+    if (lane < 32) {
+        const int i = lane / G, l = lane % G;
+        const uint32_t e = lds_read<uint32_t>(meta + i * MREC + 512 + 4 * G + 4 * l);
         // (a position outside the group, possible only in a record this
         // library did not write, is ignored)
-        if (lane < G && (e & 0xffffu) < (uint32_t)(G * kD)) {
-            const int pos = (int)(e & 0xffffu), ch = pos & (kD - 1), tu = i * G + (pos >> 7);
+        if ((e & 0xffffu) < (uint32_t)(G * kD)) tok = i * G + (int)((e & 0xffffu) >> 7);
+    }
+    const int prev = __shfl_up(tok, 1), next = __shfl_down(tok, 1);
+    if (lane < 32 && tok < 32) {
+        if (lane == 0 || prev != tok) run[0][tok] = (uint8_t)lane;
+        if (lane == 31 || next != tok) run[1][tok] = (uint8_t)(lane + 1);
+    }
+    wave_sync();
+    if (lane < 32) {
+        float acc[16];
+#pragma unroll
+        for (int h = 0; h < 16; ++h) acc[h] = 0.0f;
+        const int o1 = run[1][lane];
+        for (int o = run[0][lane]; o < o1; ++o) {
+            const lds_u8* m = meta + (o / G) * MREC;
+            const uint32_t e = lds_read<uint32_t>(m + 512 + 4 * G + 4 * (o % G));
+            const int ch = (int)(e & (kD - 1));
             const float d = h2f(e >> 16) - h2f(lds_read<uint16_t>(m + 256 + 2 * ch));
             const h8 qa = __builtin_bit_cast(h8, *(const __attribute__((address_space(3))) u32x4*)&SPL->q[ch][0]);
             const h8 qb = __builtin_bit_cast(h8, *(const __attribute__((address_space(3))) u32x4*)&SPL->q[ch][8]);
-            for (int h = 0; h < gq; ++h)
-                atomicAdd(&SPL->corr[wave][h][tu], (float)(h < 8 ? qa[h & 7] : qb[h & 7]) * d);
+#pragma unroll
+            for (int h = 0; h < 8; ++h) {
+                acc[h] = fmaf((float)qa[h], d, acc[h]);
+                acc[h + 8] = fmaf((float)qb[h], d, acc[h + 8]);
+            }
         }
+        f4* row = (f4*)&SPL->corr[wave][lane][0];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) row[k] = f4{acc[4 * k], acc[4 * k + 1], acc[4 * k + 2], acc[4 * k + 3]};
     }
     wave_sync();
 }
@@ -689,7 +712,7 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
 
     // dense-and-sparse keys: the kept entries' corrections q . (x - z) to
     // their tokens' logits, gathered per (head, token) in the wave's tile
-    if constexpr (SP) sparse_corrections<G, S::MREC>(buf + S::META, SPL, wave, lane, gq);
+    if constexpr (SP) sparse_corrections<G, S::MREC>(buf + S::META, SPL, wave, lane);
 
     // value scale/zero of the lane's 8 slots: slot k = 4*rt + i <-> token 16rt + 4g + i
     float x[8], vs[8], vz[8];
@@ -704,7 +727,7 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
             const int slot = S::NR == 2 ? i : k;
             // (pre-RoPE: both limb columns hold the same head's full logit)
             x[k] = LP && !RP ? add_limb_partner(C[rt][i]) : C[rt][i];
-            if constexpr (SP) x[k] += SPL->corr[wave][LP ? (n & 7) : n][16 * rt + 4 * g + i];
+            if constexpr (SP) x[k] += SPL->corr[wave][16 * rt + 4 * g + i][LP ? (n & 7) : n];
             vs[k] = h2f(lds_read<uint16_t>(vm + 2 * slot));
             vz[k] = h2f(lds_read<uint16_t>(vm + 2 * (SPT + slot)));
             valid[k] = S::NR == 1 || ((has >> rec) & 1);
