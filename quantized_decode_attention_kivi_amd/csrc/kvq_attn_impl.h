@@ -1016,8 +1016,9 @@ __device__ __forceinline__ void process_any(const lds_u8* buf, uint32_t has, Wav
 // takes lo + w, lo + w + 4, ...), combined into one partial result (heads
 // < gq: output[128] unnormalised, running max in log2 units, weight sum) at
 // `part`.  Called by every thread of the workgroup.
-template <int G, int KB, int VB, int F, bool LP, bool PG>
-__device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_b, float (*wm)[16], float (*wl)[16],
+template <int G, int KB, int VB, int F, bool LP, bool PG, int NS>
+__device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_b, uint8_t* stage_c, float (*wm)[16],
+                                               float (*wl)[16],
                                                float (*wpz)[16], const Layout& L, const kvq_cache& c,
                                                const half_t* __restrict__ q, float sl2, int gq, int b, int h,
                                                const SeqUnits& su, int lo, int hi, float* __restrict__ part,
@@ -1074,37 +1075,46 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
         const int ntot = max(1, (q1 - (lo + wave) + kWaves - 1) / kWaves);   // this wave's units
         int u = lo + wave;
         if (u < q1) {
-            // Direct-to-LDS loads: unit u is staged in one buffer while the
-            // previous one is processed from the other.  The waits are explicit
-            // (vmcnt counts this wave's outstanding loads, in issue order).
-            lds_u8* const sa = (lds_u8*)(stage_a + wave * S::PITCH);
-            lds_u8* const sb = (lds_u8*)(stage_b + wave * S::PITCH);
-            uint32_t ha = issue_any<G, KB, VB, F, PG>(sa, L, c, b, h, u, su.ngroups, lane), hb = 0;
+            // Direct-to-LDS loads: the next NS - 1 units of the wave are in
+            // flight, each in a stage buffer of its own, while unit u is
+            // processed from its buffer; the buffers rotate.  The waits are
+            // explicit (vmcnt counts this wave's outstanding loads, in issue
+            // order).
+            lds_u8* s0 = (lds_u8*)(stage_a + wave * S::PITCH);
+            lds_u8* s1 = (lds_u8*)(stage_b + wave * S::PITCH);
+            lds_u8* s2 = (lds_u8*)(stage_c + wave * S::PITCH);   // (NS == 3 only)
+            uint32_t h0 = issue_any<G, KB, VB, F, PG>(s0, L, c, b, h, u, su.ngroups, lane), h1 = 0, h2 = 0;
+            if (NS == 3 && u + kWaves < q1) h1 = issue_any<G, KB, VB, F, PG>(s1, L, c, b, h, u + kWaves, su.ngroups, lane);
             for (;;) {
-                if (u + kWaves < q1) {
-                    __builtin_amdgcn_s_waitcnt(kLgkmZero);   // last reads of sb returned
-                    hb = issue_any<G, KB, VB, F, PG>(sb, L, c, b, h, u + kWaves, su.ngroups, lane);
+                // issue the unit NS - 1 ahead into the buffer freed last
+                lds_u8* const nxt = NS == 3 ? s2 : s1;
+                const int ahead = u + (NS - 1) * kWaves;
+                if (ahead < q1) {
+                    __builtin_amdgcn_s_waitcnt(kLgkmZero);   // last reads of that buffer returned
+                    const uint32_t hn = issue_any<G, KB, VB, F, PG>(nxt, L, c, b, h, ahead, su.ngroups, lane);
+                    if (NS == 3) h2 = hn; else h1 = hn;
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * S::LOADS));
+                } else if (NS == 3 && u + kWaves < q1) {
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::LOADS));
                 } else {
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
                 }
                 wave_sync();
                 set_progress_prio((q1 - u + kWaves - 1) / kWaves, ntot);
-                process_any<G, KB, VB, F, LP>(sa, ha, A, Q, sl2q, qsum, vscl, lane, R, wave, 32 * u, L, SPL, gq);
+                process_any<G, KB, VB, F, LP>(s0, h0, A, Q, sl2q, qsum, vscl, lane, R, wave, 32 * u, L, SPL, gq);
                 u += kWaves;
                 if (u >= q1) break;
-                if (u + kWaves < q1) {
-                    __builtin_amdgcn_s_waitcnt(kLgkmZero);
-                    ha = issue_any<G, KB, VB, F, PG>(sa, L, c, b, h, u + kWaves, su.ngroups, lane);
-                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::LOADS));
+                // rotate: the buffer just processed is the next to be refilled
+                lds_u8* const t = s0;
+                s0 = s1;
+                h0 = h1;
+                if (NS == 3) {
+                    s1 = s2;
+                    h1 = h2;
+                    s2 = t;
                 } else {
-                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                    s1 = t;
                 }
-                wave_sync();
-                set_progress_prio((q1 - u + kWaves - 1) / kWaves, ntot);
-                process_any<G, KB, VB, F, LP>(sb, hb, A, Q, sl2q, qsum, vscl, lane, R, wave, 32 * u, L, SPL, gq);
-                u += kWaves;
-                if (u >= q1) break;
             }
         }
     }
@@ -1180,6 +1190,11 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
 // than INT2 ones.  (Three waves lose little where the kernel waits on HBM.)
 // The 8-bit formats stage twice the bytes per unit: their LDS allows two
 // workgroups per CU, two waves per SIMD.
+// Stage buffers per wave.  Two everywhere: three (two units in flight while
+// one is processed) measured no faster on the INT4 8 x 32K layer (66.8 us
+// either way), its LDS leaving two workgroups per CU instead of three.
+constexpr int attn_stages(int G, int KB, int VB, int F) { return 2; }
+
 // Pre-RoPE keys take registers for the rotation: three waves.
 constexpr int attn_waves(int G, int KB, int VB, int F, bool LP, bool PG) {
     return rope_fmt(F) ? 3 : !low_bit(F) ? 2 : F != kFmtKivi ? 3 : LP && VB == 2 && !(G == 16 && KB == 2) ? 4 : 3;
@@ -1195,6 +1210,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves(
     // holds the waves' accumulators (waves 0-1 in stage_a, 2-3 in stage_b).
     __shared__ __attribute__((aligned(16))) uint8_t stage_a[kWaves * S::PITCH];
     __shared__ __attribute__((aligned(16))) uint8_t stage_b[kWaves * S::PITCH];
+    constexpr int NS = attn_stages(G, KB, VB, F);
+    uint8_t* stage_c = nullptr;
+    if constexpr (NS == 3) {
+        __shared__ __attribute__((aligned(16))) uint8_t stage_c_lds[kWaves * S::PITCH];
+        stage_c = stage_c_lds;
+    }
     __shared__ float wm[kWaves][16], wl[kWaves][16], wpz[kWaves][16];
     __shared__ int wsum[kWaves];
     __shared__ int first[2];   // sequence holding unit w T / nwg, flattened start of that sequence
@@ -1274,7 +1295,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves(
             asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l0));
             if (l0 == 0) meta[1 + s] = ps;
         }
-        attend_segment<G, KB, VB, F, LP, PG>(stage_a, stage_b, wm, wl, wpz, L, c, q, sl2, gq, b, h, su,
+        attend_segment<G, KB, VB, F, LP, PG, NS>(stage_a, stage_b, stage_c, wm, wl, wpz, L, c, q, sl2, gq, b, h, su,
                                           unit_at(su, lo), unit_at(su, hi), ws + ((long)w + s) * gq * kPart,
                                           lane, wave, R, SPL);
         if (ps + hi >= end) break;
