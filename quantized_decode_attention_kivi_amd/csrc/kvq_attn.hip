@@ -10,7 +10,9 @@ KVQ_ALL_FAMILIES(KVQ_DECLARE_FAMILY)
 // Workgroup w of nwg covers units [w T / nwg, (w + 1) T / nwg): empty when
 // there are fewer units than workgroups; an empty one writes no partial.
 __device__ __forceinline__ bool covers_units(long w, long T, long nwg) {
-    return w * T / nwg != (w + 1) * T / nwg;
+    // (with at least as many units as workgroups every share is non-empty:
+    // no divisions in the common case)
+    return T >= nwg || w * T / nwg != (w + 1) * T / nwg;
 }
 
 // Split merge: grid (B*H, gq), 1024 threads.  Log-sum-exp over the partials
@@ -50,6 +52,14 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(Layout L, kvq
     const long stride = (long)gq * kPart;
     const float* p = ws + ((long)(w0 + s) * gq + hh) * kPart;
 
+    // The first batch of outputs is read together with the maxima and sums
+    // (the partials of workgroups with an empty share are not read).
+    float o0[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+        const int i = slice + j * kMergeSlices;
+        o0[j] = i < parts && covers_units(w0 + i, T, nwg) ? p[i * stride + ch] : 0.0f;
+    }
     float m = kNegInf, l = 0.0f;
     if (tid < parts && covers_units(w0 + tid, T, nwg)) {
         m = p[tid * stride + kD];
@@ -70,7 +80,12 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(Layout L, kvq
     Ls = 0.0f;
     for (int w = 0; w < kMergeThreads / 64; ++w) Ls += red[w][1];
     float sum = 0.0f;
-    for (int i0 = slice; i0 < parts; i0 += kMergeSlices * kMergeBatch) {
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+        const int i = slice + j * kMergeSlices;
+        if (i < parts) sum = fmaf(o0[j], fac[i], sum);
+    }
+    for (int i0 = slice + kMergeSlices * kMergeBatch; i0 < parts; i0 += kMergeSlices * kMergeBatch) {
         float o[kMergeBatch];
 #pragma unroll
         for (int j = 0; j < kMergeBatch; ++j) {
@@ -99,7 +114,6 @@ constexpr int kRowsPerMerge = 4;
 __global__ __launch_bounds__(256) void attn_merge_rows_kernel(Layout L, kvq_cache c, const float* __restrict__ ws,
                                                               float* __restrict__ out, int gq, int nwg,
                                                               long meta_off) {
-    __shared__ float fac[kRowsPerMerge][kMaxParts];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const long row = (long)blockIdx.x * kRowsPerMerge + wave;
     if (row >= (long)L.B * L.H * gq) return;   // (no workgroup barrier below)
@@ -119,37 +133,42 @@ __global__ __launch_bounds__(256) void attn_merge_rows_kernel(Layout L, kvq_cach
     const long stride = (long)gq * kPart;
     const float* p = ws + ((long)(w0 + s) * gq + hh) * kPart;
 
-    float M = kNegInf;
-    for (int i = lane; i < parts; i += 64)
-        if (covers_units(w0 + i, T, nwg)) M = fmaxf(M, p[i * stride + kD]);
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float Ls = 0.0f;
-    for (int i = lane; i < parts; i += 64) {
-        float f = 0.0f;
-        if (covers_units(w0 + i, T, nwg)) {
-            const float m = p[i * stride + kD];
-            f = m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-            Ls += p[i * stride + kD + 1] * f;
-        }
-        fac[wave][i] = f;
-    }
-    for (int off = 32; off >= 1; off >>= 1) Ls += __shfl_xor(Ls, off);
-    wave_sync();   // fac written by other lanes of this wave
+    // Chunks of 16 partials, each read in one go (partial i0 + j's max and
+    // weight sum by lanes j, j + 16, ..., its outputs by all lanes) and merged
+    // into running sums rescaled to the running max: one round trip per chunk.
+    float M = kNegInf, Ls = 0.0f;
     float2 acc = make_float2(0.0f, 0.0f);
-    for (int i0 = 0; i0 < parts; i0 += 8) {
-        float2 v[8];
+    for (int i0 = 0; i0 < parts; i0 += 16) {
+        const int i = i0 + (lane & 15);
+        const bool mine = i < parts && covers_units(w0 + i, T, nwg);
+        float2 v[16];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            v[j] = i0 + j < parts && fac[wave][i0 + j] != 0.0f ? *(const float2*)(p + (i0 + j) * stride + 2 * lane)
-                                                              : make_float2(0.0f, 0.0f);
+        for (int j = 0; j < 16; ++j)
+            v[j] = i0 + j < parts && covers_units(w0 + i0 + j, T, nwg)
+                       ? *(const float2*)(p + (long)(i0 + j) * stride + 2 * lane)
+                       : make_float2(0.0f, 0.0f);
+        const float mi = mine ? p[(long)i * stride + kD] : kNegInf;
+        const float li = mine ? p[(long)i * stride + kD + 1] : 0.0f;
+        float cm = mi;
+        for (int off = 8; off >= 1; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off));
+        const float Mn = fmaxf(M, cm);
+        if (Mn == kNegInf) continue;   // nothing in this chunk or before it
+        const float r = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+        const float f = mi == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mi - Mn);
+        // (every 16-lane group holds the chunk's 16 partials: sums within a
+        // group give every lane the chunk's total)
+        float lf = li * f;
+        for (int off = 8; off >= 1; off >>= 1) lf += __shfl_xor(lf, off);
+        Ls = Ls * r + lf;
+        acc.x *= r;
+        acc.y *= r;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (i0 + j < parts) {
-                const float f = fac[wave][i0 + j];
-                acc.x = fmaf(v[j].x, f, acc.x);
-                acc.y = fmaf(v[j].y, f, acc.y);
-            }
+        for (int j = 0; j < 16; ++j) {
+            const float fj = __shfl(f, j);
+            acc.x = fmaf(v[j].x, fj, acc.x);
+            acc.y = fmaf(v[j].y, fj, acc.y);
         }
+        M = Mn;
     }
     orow[lane] = Ls > 0.0f ? make_float2(acc.x / Ls, acc.y / Ls) : make_float2(0.0f, 0.0f);
 }
