@@ -412,6 +412,70 @@ __device__ __forceinline__ float add_limb_partner(float x) {
     return x + __builtin_bit_cast(float, y);
 }
 
+// Token packing (limb-packed, at most 4 query heads per kv head): columns
+// 4-7 and 12-15 of the products carry no head, so the second 16-token tile's
+// logits move there, column c then holding head c & 3, tile (c >> 2) & 1 and
+// limb c >> 3.  One DPP shift by 4 columns, written only to those columns
+// (bank mask), does the move; every lane then has 4 logits instead of 8.
+__device__ __forceinline__ float pack_second_tile(float first, float second) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, first),
+                                                                 __builtin_bit_cast(int, second),
+                                                                 0x114 /* row_shr:4 */, 0xf, 0xa, false));
+}
+
+// Online-softmax step and value contraction of a token-packed lane: 4 logits
+// x[] (raw q.k) of its tile, value scale/zero vs/vz of those tokens.  The
+// running max is shared by the head's four columns (one rotation by 4 pairs
+// the tiles; the limb columns hold copies).  The value operand holds the
+// lane's weights in its tile's half of the 8 token slots and zeros in the
+// other half, so accumulator rows c, c + 4, c + 8, c + 12 add up to head c.
+template <typename VOp>
+__device__ __forceinline__ void softmax_and_values_tp(WaveAcc& A, const float (&x)[4], const float (&vs)[4],
+                                                      const float (&vz)[4], const bool (&valid)[4], float sl2,
+                                                      int lane, VOp vop) {
+    float cm = kNegInf;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cm = valid[k] ? fmaxf(cm, x[k]) : cm;
+    cm = fmaxf(cm, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, cm),
+                                                                          0x124 /* row_ror:4 */, 0xf, 0xf, true)));
+    cm = group_max(cm);
+    const float mnew = fmaxf(A.m, cm * sl2);
+    const float alpha = A.m == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(A.m - mnew);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+        const int base = (lane & 48) | ((lane >> 4) << 2);
+        float ai[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, base + i);
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) A.acc[ct][i] *= ai[i];
+        A.l *= alpha;
+        A.pz *= alpha;
+    }
+    A.m = mnew;
+    float w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float p = valid[k] ? __builtin_amdgcn_exp2f(fmaf(x[k], sl2, -mnew)) : 0.0f;
+        A.l += p;
+        A.pz = valid[k] ? fmaf(p, vz[k], A.pz) : A.pz;
+        w[k] = valid[k] ? p * vs[k] : 0.0f;
+    }
+    // the lane's limb of each weight: high part, or the exact low part
+    const bool lo = lane & 8;
+    _Float16 part[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const _Float16 hi = (_Float16)w[k];
+        part[k] = lo ? (_Float16)(w[k] - (float)hi) : hi;
+    }
+    const h2 a = h2{part[0], part[1]}, b = h2{part[2], part[3]}, z = h2{(_Float16)0.0f, (_Float16)0.0f};
+    const h8 wop = (lane & 4) ? make_h8(z, z, a, b) : make_h8(a, b, z, z);
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) A.acc[ct] = mfma(wop, vop(ct), A.acc[ct]);
+}
+
 // Query operand of lane (g, n): q[head n][32g + 8j + e], zero for heads >= gq.
 struct QOps {
     h8 q[4];
@@ -600,7 +664,7 @@ __device__ __forceinline__ void sparse_corrections(const lds_u8* meta, SparseLds
 // One staged unit (see Stage): key logits on the matrix cores, then the
 // online-softmax step and the value product.  RP: pre-RoPE keys (R, wave:
 // the rotation tables; t0: the unit's first token).
-template <int G, int KB, int VB, bool LP, bool RP, bool CB, bool SP>
+template <int G, int KB, int VB, bool LP, bool RP, bool CB, bool SP, bool TP>
 __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, WaveAcc& A, const QOps& Q, float sl2,
                                              int lane, RopeLds* R, int wave, int t0, const Layout& L,
                                              SparseLds* SPL, int gq) {
@@ -714,6 +778,35 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
     // their tokens' logits, gathered per (head, token) in the wave's tile
     if constexpr (SP) sparse_corrections<G, S::MREC>(buf + S::META, SPL, wave, lane);
 
+    auto vop = [&](int ct) -> h8 {
+        if (S::NR == 1) return levels8<VB, CB>(vc[0], ct, L.vlut);
+        // G = 16: 4 slots of each record; code q = 4ct + slot
+        const h8 a = levels8<VB, CB>(vc[0], ct >> 1, L.vlut);
+        const h8 b = levels8<VB, CB>(vc[1], ct >> 1, L.vlut);
+        const int o = 4 * (ct & 1);
+        return h8{a[o], a[o + 1], a[o + 2], a[o + 3], b[o], b[o + 1], b[o + 2], b[o + 3]};
+    };
+    if constexpr (TP) {
+        static_assert(LP && !RP && !SP, "token packing: limb-packed, post-RoPE keys, no kept keys");
+        // the lane's tile (columns with bit 2 set: the second 16 tokens) and
+        // its 4 logits, value scales and zeros
+        const int rt = (lane >> 2) & 1;
+        const int rec = S::NR == 2 ? rt : 0;
+        const lds_u8* vm = buf + S::META + rec * S::MREC + 512 + g * 4 * SPT;
+        float x[4], vs[4], vz[4];
+        bool valid[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int slot = S::NR == 2 ? i : 4 * rt + i;
+            x[i] = pack_second_tile(add_limb_partner(C[0][i]), add_limb_partner(C[1][i]));
+            vs[i] = h2f(lds_read<uint16_t>(vm + 2 * slot));
+            vz[i] = h2f(lds_read<uint16_t>(vm + 2 * (SPT + slot)));
+            valid[i] = S::NR == 1 || ((has >> rec) & 1);
+        }
+        softmax_and_values_tp(A, x, vs, vz, valid, sl2, lane, vop);
+        return;
+    }
+
     // value scale/zero of the lane's 8 slots: slot k = 4*rt + i <-> token 16rt + 4g + i
     float x[8], vs[8], vz[8];
     bool valid[8];
@@ -733,14 +826,7 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
             valid[k] = S::NR == 1 || ((has >> rec) & 1);
         }
     }
-    softmax_and_values<LP>(A, x, vs, vz, valid, sl2, lane, [&](int ct) -> h8 {
-        if (S::NR == 1) return levels8<VB, CB>(vc[0], ct, L.vlut);
-        // G = 16: 4 slots of each record; code q = 4ct + slot
-        const h8 a = levels8<VB, CB>(vc[0], ct >> 1, L.vlut);
-        const h8 b = levels8<VB, CB>(vc[1], ct >> 1, L.vlut);
-        const int o = 4 * (ct & 1);
-        return h8{a[o], a[o + 1], a[o + 2], a[o + 3], b[o], b[o + 1], b[o + 2], b[o + 3]};
-    });
+    softmax_and_values<LP>(A, x, vs, vz, valid, sl2, lane, vop);
 }
 
 // Eight 8-bit codes (words w0, w1, byte order) as an fp16 operand.  INT8:
@@ -873,7 +959,7 @@ __device__ __forceinline__ int ring_slot(int slot0, int r, int ring) {
 // high-limb columns carry it, the low-limb columns add zero).  The value rows
 // go straight to LDS (rows 0-15 to sva, 16-31 to svb, 256 bytes each; rows at
 // or past n read as zeros), from where each lane gathers its operand columns.
-template <bool LP, bool RP>
+template <bool LP, bool RP, bool TP>
 __device__ __forceinline__ void process_residual(WaveAcc& A, const Layout& L, const kvq_cache& c, long sh, int t0,
                                                  int n, const QOps& Q, float sl2, int lane, lds_u8* sva,
                                                  lds_u8* svb, RopeLds* R, int wave) {
@@ -923,6 +1009,33 @@ __device__ __forceinline__ void process_residual(WaveAcc& A, const Layout& L, co
             C[rt] = LP && (lane & 8) ? f4{0.0f, 0.0f, 0.0f, 0.0f} : acc;
         }
     }
+    auto vop = [&](int ct) -> h8 {
+        h8 b;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const lds_u8* rows = (k >> 2) ? svb : sva;
+            b[k] = __builtin_bit_cast(_Float16, lds_read<uint16_t>(rows + (4 * g + (k & 3)) * (kD * 2) +
+                                                                   (16 * ct + n16) * 2));
+        }
+        return b;
+    };
+    if constexpr (TP) {
+        // token-packed columns, as in the quantized units
+        const int rt = (lane >> 2) & 1;
+        float x[4], vs[4], vz[4];
+        bool valid[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = pack_second_tile(add_limb_partner(C[0][i]), add_limb_partner(C[1][i]));
+            vs[i] = 1.0f;
+            vz[i] = 0.0f;
+            valid[i] = t0 + rt * 16 + 4 * g + i < n;
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the value rows are in LDS
+        wave_sync();
+        softmax_and_values_tp(A, x, vs, vz, valid, sl2, lane, vop);
+        return;
+    }
     float x[8], vs[8], vz[8];
     bool valid[8];
 #pragma unroll
@@ -934,16 +1047,7 @@ __device__ __forceinline__ void process_residual(WaveAcc& A, const Layout& L, co
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the value rows are in LDS
     wave_sync();
-    softmax_and_values<LP>(A, x, vs, vz, valid, sl2, lane, [&](int ct) -> h8 {
-        h8 b;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const lds_u8* rows = (k >> 2) ? svb : sva;
-            b[k] = __builtin_bit_cast(_Float16, lds_read<uint16_t>(rows + (4 * g + (k & 3)) * (kD * 2) +
-                                                                   (16 * ct + n16) * 2));
-        }
-        return b;
-    });
+    softmax_and_values<LP>(A, x, vs, vz, valid, sl2, lane, vop);
 }
 
 // A wave's [16][128] fp32 accumulator image after the unit loop.
@@ -1002,13 +1106,13 @@ __device__ __forceinline__ uint32_t issue_any(lds_u8* buf, const Layout& L, cons
     else return issue_unit8<G, F, PG>(buf, L, c, b, h, unit, ngroups, lane);
 }
 
-template <int G, int KB, int VB, int F, bool LP>
+template <int G, int KB, int VB, int F, bool LP, bool TP>
 __device__ __forceinline__ void process_any(const lds_u8* buf, uint32_t has, WaveAcc& A, const QOps& Q, float sl2,
                                             float qsum, float vscl, int lane, RopeLds* R, int wave, int t0,
                                             const Layout& L, SparseLds* SPL, int gq) {
     if constexpr (low_bit(F))
-        process_unit<G, KB, VB, LP, rope_fmt(F), cb_fmt(F), sp_fmt(F)>(buf, has, A, Q, sl2, lane, R, wave, t0, L,
-                                                                       SPL, gq);
+        process_unit<G, KB, VB, LP, rope_fmt(F), cb_fmt(F), sp_fmt(F), TP>(buf, has, A, Q, sl2, lane, R, wave, t0,
+                                                                           L, SPL, gq);
     else process_unit8<G, F, LP>(buf, has, A, Q, sl2, qsum, vscl, lane);
 }
 
@@ -1016,7 +1120,7 @@ __device__ __forceinline__ void process_any(const lds_u8* buf, uint32_t has, Wav
 // takes lo + w, lo + w + 4, ...), combined into one partial result (heads
 // < gq: output[128] unnormalised, running max in log2 units, weight sum) at
 // `part`.  Called by every thread of the workgroup.
-template <int G, int KB, int VB, int F, bool LP, bool PG, int NS>
+template <int G, int KB, int VB, int F, bool LP, bool TP, bool PG, int NS>
 __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_b, uint8_t* stage_c, float (*wm)[16],
                                                float (*wl)[16],
                                                float (*wpz)[16], const Layout& L, const kvq_cache& c,
@@ -1101,7 +1205,7 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
                 }
                 wave_sync();
                 set_progress_prio((q1 - u + kWaves - 1) / kWaves, ntot);
-                process_any<G, KB, VB, F, LP>(s0, h0, A, Q, sl2q, qsum, vscl, lane, R, wave, 32 * u, L, SPL, gq);
+                process_any<G, KB, VB, F, LP, TP>(s0, h0, A, Q, sl2q, qsum, vscl, lane, R, wave, 32 * u, L, SPL, gq);
                 u += kWaves;
                 if (u >= q1) break;
                 // rotate: the buffer just processed is the next to be refilled
@@ -1120,7 +1224,7 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
     }
     for (int u = lo + wave; u < hi; u += kWaves)
         if (u >= su.uq)
-            process_residual<LP, rope_fmt(F)>(A, L, c, sh, su.nq + 32 * (u - su.uq), su.n, Q, sl2, lane,
+            process_residual<LP, rope_fmt(F), TP>(A, L, c, sh, su.nq + 32 * (u - su.uq), su.n, Q, sl2, lane,
                                                 (lds_u8*)(stage_a + wave * S::PITCH),
                                                 (lds_u8*)(stage_b + wave * S::PITCH), R, wave);
     __builtin_amdgcn_s_setprio(0);
@@ -1131,10 +1235,13 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
     const float lt = group_sum(A.l);
     const float pzt = group_sum(A.pz);
     __syncthreads();
+    // TP: columns hh and hh + 4 hold the two token tiles of head hh
+    const float lh = TP ? lt + __shfl(lt, (lane + 4) & 15) : lt;
+    const float pzh = TP ? pzt + __shfl(pzt, (lane + 4) & 15) : pzt;
     if (lane < 16) {
         wm[wave][lane] = A.m;
-        wl[wave][lane] = lt;
-        wpz[wave][lane] = pzt;
+        wl[wave][lane] = lh;
+        wpz[wave][lane] = pzh;
     }
     {
         float* wacc = wave_acc(stage_a, stage_b, wave, S::PITCH);
@@ -1157,8 +1264,10 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
             const float mw = wm[w][hh];
             const float f = mw == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
             // LP: rows hh and hh+8 hold the high- and low-limb sums of head hh
+            // (TP: rows hh + 4 and hh + 12 its second token tile)
             const float* wacc = wave_acc(stage_a, stage_b, w, S::PITCH);
-            const float a = LP ? wacc[hh * kD + ch] + wacc[(hh + 8) * kD + ch] : wacc[hh * kD + ch];
+            float a = LP ? wacc[hh * kD + ch] + wacc[(hh + 8) * kD + ch] : wacc[hh * kD + ch];
+            if (TP) a += wacc[(hh + 4) * kD + ch] + wacc[(hh + 12) * kD + ch];
             o += (a + wpz[w][hh]) * f;
             Ls += wl[w][hh] * f;
         }
@@ -1200,7 +1309,7 @@ constexpr int attn_waves(int G, int KB, int VB, int F, bool LP, bool PG) {
     return rope_fmt(F) ? 3 : !low_bit(F) ? 2 : F != kFmtKivi ? 3 : LP && VB == 2 && !(G == 16 && KB == 2) ? 4 : 3;
 }
 
-template <int G, int KB, int VB, int F, bool LP, bool PG>
+template <int G, int KB, int VB, int F, bool LP, bool TP, bool PG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves(G, KB, VB, F, LP, PG)))) void attn_kernel(
     Layout L, kvq_cache c, const half_t* __restrict__ q, float sl2, float* __restrict__ ws, int gq, int nwg,
     long meta_off) {
@@ -1295,7 +1404,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves(
             asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l0));
             if (l0 == 0) meta[1 + s] = ps;
         }
-        attend_segment<G, KB, VB, F, LP, PG, NS>(stage_a, stage_b, stage_c, wm, wl, wpz, L, c, q, sl2, gq, b, h, su,
+        attend_segment<G, KB, VB, F, LP, TP, PG, NS>(stage_a, stage_b, stage_c, wm, wl, wpz, L, c, q, sl2, gq, b, h, su,
                                           unit_at(su, lo), unit_at(su, hi), ws + ((long)w + s) * gq * kPart,
                                           lane, wave, R, SPL);
         if (ps + hi >= end) break;
@@ -1312,7 +1421,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves(
 // Resident attention workgroups on the current device: CUs x workgroups per
 // CU for this instantiation (from its register and LDS footprint).  Falls
 // back to 256 CUs x 3 when no device is visible (host-only size queries).
-template <int G, int KB, int VB, int F, bool LP, bool PG>
+template <int G, int KB, int VB, int F, bool LP, bool TP, bool PG>
 int attn_slots_for() {
     static int cached[64];
     int dev = 0;
@@ -1321,7 +1430,7 @@ int attn_slots_for() {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)attn_kernel<G, KB, VB, F, LP, PG>, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)attn_kernel<G, KB, VB, F, LP, TP, PG>, 256, 0) !=
             hipSuccess || per_cu <= 0)
         per_cu = 3;
     (void)hipGetLastError();
@@ -1335,18 +1444,30 @@ static inline bool limb_packed(int gq) { return gq <= 8; }
 
 // Launch of one (G, KB, VB, format) family: limb packing from the query
 // heads per kv head, paged addressing from the layout.
+// Token packing (see pack_second_tile): the uniform low-bit format with at
+// most 4 query heads per kv head.
+template <int F>
+static inline bool token_packed(int gq) {
+    return F == kFmtKivi && gq <= 4;
+}
+
 template <int G, int KB, int VB, int F>
 hipError_t launch_attn_family(const Layout& L, const AttnPlan& P, const kvq_cache& c, const half_t* q, int gq,
                               float sl2, void* ws, hipStream_t s) {
-#define KVQ_ATT3(LP, PG)                                                                                 \
-    hipLaunchKernelGGL((attn_kernel<G, KB, VB, F, LP, PG>), dim3(P.nwg), dim3(256), 0, s, L, c, q, sl2, \
+#define KVQ_ATT3(LP, TP, PG)                                                                                 \
+    hipLaunchKernelGGL((attn_kernel<G, KB, VB, F, LP, TP, PG>), dim3(P.nwg), dim3(256), 0, s, L, c, q, sl2, \
                        (float*)ws, gq, P.nwg, (long)P.meta_off)
-    if (limb_packed(gq)) {
-        if (L.paged) KVQ_ATT3(true, true);
-        else KVQ_ATT3(true, false);
+    if (limb_packed(gq) && token_packed<F>(gq)) {
+        if constexpr (F == kFmtKivi) {
+            if (L.paged) KVQ_ATT3(true, true, true);
+            else KVQ_ATT3(true, true, false);
+        }
+    } else if (limb_packed(gq)) {
+        if (L.paged) KVQ_ATT3(true, false, true);
+        else KVQ_ATT3(true, false, false);
     } else {
-        if (L.paged) KVQ_ATT3(false, true);
-        else KVQ_ATT3(false, false);
+        if (L.paged) KVQ_ATT3(false, false, true);
+        else KVQ_ATT3(false, false, false);
     }
 #undef KVQ_ATT3
     return hipGetLastError();
@@ -1355,8 +1476,16 @@ hipError_t launch_attn_family(const Layout& L, const AttnPlan& P, const kvq_cach
 // Resident workgroups of the family's instantiation for this launch.
 template <int G, int KB, int VB, int F>
 int attn_family_slots(const Layout& L, int gq) {
-    if (limb_packed(gq)) return L.paged ? attn_slots_for<G, KB, VB, F, true, true>() : attn_slots_for<G, KB, VB, F, true, false>();
-    return L.paged ? attn_slots_for<G, KB, VB, F, false, true>() : attn_slots_for<G, KB, VB, F, false, false>();
+    if (limb_packed(gq) && token_packed<F>(gq)) {
+        if constexpr (F == kFmtKivi)
+            return L.paged ? attn_slots_for<G, KB, VB, F, true, true, true>()
+                           : attn_slots_for<G, KB, VB, F, true, true, false>();
+    }
+    if (limb_packed(gq))
+        return L.paged ? attn_slots_for<G, KB, VB, F, true, false, true>()
+                       : attn_slots_for<G, KB, VB, F, true, false, false>();
+    return L.paged ? attn_slots_for<G, KB, VB, F, false, false, true>()
+                   : attn_slots_for<G, KB, VB, F, false, false, false>();
 }
 
 // Families and where they are instantiated: X(G, KB, VB, F).
