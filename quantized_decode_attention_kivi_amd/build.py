@@ -41,6 +41,9 @@ HIPCC_FLAGS = [
 # so that the build can reject any that spills to scratch.
 SOURCE_FLAGS = {src: ["-fno-honor-nans", "-Rpass-analysis=kernel-resource-usage"]
                 for src in ["kvq_attn.hip"] + ATTN_KERNEL_SOURCES}
+# The quantizer's inputs are finite (a documented precondition), so its
+# min/max need no NaN quieting either.
+SOURCE_FLAGS["kvq_quant.hip"] = ["-fno-honor-nans"]
 NO_SCRATCH = {src: "attn_kernel" for src in ATTN_KERNEL_SOURCES}
 
 

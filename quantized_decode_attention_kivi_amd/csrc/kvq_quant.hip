@@ -252,6 +252,191 @@ __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* 
     __syncthreads();  // LDS may be reused by the caller
 }
 
+// The uniform grid without kept keys (the plain method), written for the
+// vector ALU's issue budget: the same codes, scales and zeros as
+// quantize_group, with fewer instructions per element.
+//  - x - z is one mixed-precision fma, x * 1 + (-z), reading x straight from
+//    its fp16 half: one rounding, exactly (float)x - z.
+//  - rint and the clamp leave an integer in [0, Q] that v_cvt_pk_u8_f32
+//    converts and drops into its byte of a word; code words are assembled
+//    from those byte words (code_bit: INT4 codes 0-3 are bytes 0-3 and codes
+//    4-7 the same bytes' high nibbles; INT2 codes 0-7 are nibbles 0-7, even
+//    codes in low nibbles, and codes 8-15 the same nibbles shifted by 2).
+//  - value extremes: packed fp16 min/max over the thread's 8 channels, then
+//    the 16 lanes of a row by DPP (quad swaps, half-row and row mirrors).
+template <int HI>
+__device__ __forceinline__ float minus_z(uint32_t w, float nz) {
+    float r;
+    if (HI) asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(nz));
+    else asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(nz));
+    return r;
+}
+
+// Code of the fp16 half HI of w as a byte of `acc` (byte `pos`).
+template <int HI>
+__device__ __forceinline__ uint32_t code_byte(uint32_t w, float nz, float inv, float qmax, int pos, uint32_t acc) {
+#pragma clang fp contract(off)
+    const float t = minus_z<HI>(w, nz) * inv;
+    const float r = fminf(fmaxf(__builtin_rintf(t), 0.0f), qmax);
+    return __builtin_amdgcn_cvt_pk_u8_f32(r, pos, acc);
+}
+
+typedef _Float16 hh2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_min(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(hh2, a), __builtin_bit_cast(hh2, b)));
+}
+__device__ __forceinline__ uint32_t pk_max(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(hh2, a), __builtin_bit_cast(hh2, b)));
+}
+
+// Min (MAX = false) or max over the 16 lanes of each row.
+template <bool MAX, int CTRL>
+__device__ __forceinline__ float row_step(float x) {
+    const float y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf,
+                                                                        0xf, false));
+    return MAX ? fmaxf(x, y) : fminf(x, y);
+}
+template <bool MAX>
+__device__ __forceinline__ float row16(float x) {
+    x = row_step<MAX, 0xB1>(x);    // quad_perm [1,0,3,2]
+    x = row_step<MAX, 0x4E>(x);    // quad_perm [2,3,0,1]
+    x = row_step<MAX, 0x141>(x);   // row_half_mirror
+    return row_step<MAX, 0x140>(x);   // row_mirror
+}
+
+template <int G, int KB, int VB>
+__device__ void quantize_group_uniform(QuantSmem<G>& sm, const Layout& L, const half_t* __restrict__ ksrc,
+                                       const half_t* __restrict__ vsrc, uint8_t* __restrict__ rec) {
+    constexpr int NT = G / 16;
+    const int tid = threadIdx.x;
+    const int cg = tid & 15;
+    const int ts = tid >> 4;
+
+    uint32_t kw[NT][4], vw[NT][4];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int t = ts + 16 * j;
+        const uint4 a = *(const uint4*)(ksrc + t * kD + 8 * cg);
+        const uint4 b = *(const uint4*)(vsrc + t * kD + 8 * cg);
+        kw[j][0] = a.x; kw[j][1] = a.y; kw[j][2] = a.z; kw[j][3] = a.w;
+        vw[j][0] = b.x; vw[j][1] = b.y; vw[j][2] = b.z; vw[j][3] = b.w;
+    }
+
+    // Key statistics: per channel over the thread's tokens (packed fp16),
+    // then over the 16 token slices.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t mn = kw[0][i], mx = kw[0][i];
+#pragma unroll
+        for (int j = 1; j < NT; ++j) {
+            mn = pk_min(mn, kw[j][i]);
+            mx = pk_max(mx, kw[j][i]);
+        }
+        sm.kmn[ts][8 * cg + 2 * i] = h2f(mn & 0xffffu);
+        sm.kmn[ts][8 * cg + 2 * i + 1] = h2f(mn >> 16);
+        sm.kmx[ts][8 * cg + 2 * i] = h2f(mx & 0xffffu);
+        sm.kmx[ts][8 * cg + 2 * i + 1] = h2f(mx >> 16);
+    }
+
+    // Value statistics and codes: per token over its 128 channels.
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const uint32_t m2 = pk_min(pk_min(vw[j][0], vw[j][1]), pk_min(vw[j][2], vw[j][3]));
+        const uint32_t x2 = pk_max(pk_max(vw[j][0], vw[j][1]), pk_max(vw[j][2], vw[j][3]));
+        const float mn = row16<false>(fminf(h2f(m2 & 0xffffu), h2f(m2 >> 16)));
+        const float mx = row16<true>(fmaxf(h2f(x2 & 0xffffu), h2f(x2 >> 16)));
+        const QParams p = make_qparams(mn, mx, VB);
+        const int t = ts + 16 * j;
+        if (cg == 0) {
+            const int pos = vmeta_pos(L, t);
+            *(uint16_t*)(rec + pos) = p.s_bits;
+            *(uint16_t*)(rec + pos + 2 * L.spt) = p.z_bits;
+        }
+        const float nz = -p.z, qv = (float)((1 << VB) - 1);
+        uint32_t v0 = 0, v1 = 0;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            v0 = code_byte<0>(vw[j][i], nz, p.inv, qv, 2 * i, v0);
+            v0 = code_byte<1>(vw[j][i], nz, p.inv, qv, 2 * i + 1, v0);
+            v1 = code_byte<0>(vw[j][i + 2], nz, p.inv, qv, 2 * i, v1);
+            v1 = code_byte<1>(vw[j][i + 2], nz, p.inv, qv, 2 * i + 1, v1);
+        }
+        *(uint2*)&sm.vcode[t][8 * cg] = make_uint2(v0, v1);
+    }
+    __syncthreads();
+    if (tid < kD) {
+        float mn = sm.kmn[0][tid], mx = sm.kmx[0][tid];
+        for (int j = 1; j < 16; ++j) {
+            mn = fminf(mn, sm.kmn[j][tid]);
+            mx = fmaxf(mx, sm.kmx[j][tid]);
+        }
+        const QParams p = make_qparams(mn, mx, KB);
+        sm.kz[tid] = -p.z;   // (negated: the fma's addend)
+        sm.kinv[tid] = p.inv;
+        *(uint16_t*)(rec + L.kmeta_off + 2 * tid) = p.s_bits;
+        *(uint16_t*)(rec + L.kmeta_off + 2 * kD + 2 * tid) = p.z_bits;
+    }
+    __syncthreads();
+
+    // Key codes: channels 8cg .. 8cg+7 of the thread's tokens.
+    float nzr[8], kir[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        nzr[e] = sm.kz[8 * cg + e];
+        kir[e] = sm.kinv[8 * cg + e];
+    }
+    const float qk = (float)((1 << KB) - 1);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int t = ts + 16 * j;
+        if (KB == 4) {
+            // bytes of codes 0-3 (channel pairs of words 0, 1) and 4-7 (words 2, 3)
+            uint32_t a = 0, b = 0;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                a = code_byte<0>(kw[j][i], nzr[2 * i], kir[2 * i], qk, 2 * i, a);
+                a = code_byte<1>(kw[j][i], nzr[2 * i + 1], kir[2 * i + 1], qk, 2 * i + 1, a);
+                b = code_byte<0>(kw[j][i + 2], nzr[2 * i + 4], kir[2 * i + 4], qk, 2 * i, b);
+                b = code_byte<1>(kw[j][i + 2], nzr[2 * i + 5], kir[2 * i + 5], qk, 2 * i + 1, b);
+            }
+            *(uint32_t*)(rec + t * 64 + 4 * cg) = a | (b << 4);
+        } else {
+            // even codes (channel 2i: low halves) and odd codes (high halves),
+            // nibble e of the half word; this thread's 8 codes are codes
+            // 8 (cg & 1) .. of the word shared with its neighbour
+            uint32_t ev = 0, od = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ev = code_byte<0>(kw[j][i], nzr[2 * i], kir[2 * i], qk, i, ev);
+                od = code_byte<1>(kw[j][i], nzr[2 * i + 1], kir[2 * i + 1], qk, i, od);
+            }
+            uint32_t w = (ev | (od << 4)) << (2 * (cg & 1));
+            w |= __shfl_xor(w, 1);
+            if ((cg & 1) == 0) *(uint32_t*)(rec + t * 32 + 2 * cg) = w;
+        }
+    }
+    __syncthreads();
+
+    // Value code words, lane-major in decode-operand order.
+    constexpr int SPT = G == 16 ? 4 : 8;
+    constexpr int WPL = SPT * VB / 4;        // words per lane
+    constexpr int CPW = 32 / VB;             // codes per word
+    for (int D = tid; D < 64 * WPL; D += 256) {
+        const int lane = D / WPL, wi = D % WPL;
+        const int g = lane >> 4, n = lane & 15;
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < CPW; ++e) {
+            const int q = wi * CPW + e;
+            const int ct = q / SPT, slot = q % SPT;
+            const int t = (slot >> 2) * 16 + 4 * g + (slot & 3);
+            w |= (uint32_t)sm.vcode[t][16 * ct + n] << code_bit(VB, e);
+        }
+        *(uint32_t*)(rec + L.vcode_off + lane * SPT * VB + 4 * wi) = w;
+    }
+    __syncthreads();  // LDS may be reused by the caller
+}
+
 // The same for the 8-bit formats ("KV cache compression: ...", section 3.1):
 // every key and value token on its own.  F = kFmtInt8: the min/max grid with
 // 8 bits over the token's 128 channels (the 16 threads of a row reduce it);
@@ -365,7 +550,9 @@ inline int quant_variant(const Layout& L) {
 template <int G, int KB, int VB, int F>
 __device__ __forceinline__ void quantize_any(QuantSmem<G>& sm, const Layout& L, const kvq_cache& c, int h,
                                              const half_t* ksrc, const half_t* vsrc, uint8_t* rec) {
-    if constexpr (q_low_bit(F)) {
+    if constexpr (F == kQUniform) {
+        quantize_group_uniform<G, KB, VB>(sm, L, ksrc, vsrc, rec);
+    } else if constexpr (q_low_bit(F)) {
         quantize_group<G, KB, VB, F == kQCodebook || F == kQCodebookSparse, F == kQSparse || F == kQCodebookSparse>(
             sm, L, ksrc, vsrc, rec);
     } else {

@@ -333,6 +333,27 @@ class QuantizedKVCache:
         if changed:
             self.block_table.copy_(torch.from_numpy(self._bt_host))
 
+    def _prefill_blocks(self, lens):
+        """Block table after a prefill: the whole pool is free again and each
+        sequence in turn takes a block per key group from the pool, in the
+        order the pool hands them out.  The device table is rewritten only if
+        it changes (a rewrite waits for the device: in-flight calls may read
+        the table)."""
+        need = np.array([num_quantized(int(n), self.G, self.R) // self.G for n in lens], np.int64)
+        total = int(need.sum())
+        if total > len(self._block_order) or (len(need) and int(need.max()) > self._bt_host.shape[1]):
+            raise KVQError(KVQ_ECAPACITY, "paged cache out of blocks")
+        order = np.asarray(self._block_order[::-1][:total], np.int32)   # pop() order
+        table = np.full_like(self._bt_host, -1)
+        start = 0
+        for b, k in enumerate(need):
+            table[b, :k] = order[start:start + k]
+            start += int(k)
+        self._free = self._block_order[:len(self._block_order) - total]
+        if not np.array_equal(table, self._bt_host):
+            self._bt_host[:] = table
+            self.block_table.copy_(torch.from_numpy(self._bt_host))
+
     def shuffle_free_blocks(self, seed):
         """Hand blocks out in a seeded random order (so paged parity tests do
         not see an accidentally contiguous pool)."""
@@ -355,9 +376,7 @@ class QuantizedKVCache:
         if np.any(lens < 0) or np.any(lens > max_len) or np.any(lens > self.capacity()):
             raise ValueError("sequence length outside [0, min(max_len, capacity)]")
         if self.shape.paged:
-            self._bt_host[:] = -1
-            self._free = list(self._block_order)
-            self._ensure_blocks(lens)
+            self._prefill_blocks(lens)
         sl = seq_lens_device
         if sl is None:
             sl = torch.as_tensor(lens.astype(np.int32), device=self.device)

@@ -9,7 +9,9 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvq.h")
@@ -286,3 +288,41 @@ def test_sequence_view_offsets(paged):
         c.sequence_view(1).append(None, None)
     with pytest.raises(IndexError):
         c.sequence_view(5)
+
+
+def test_prefill_block_assignment():
+    """Paged prefill hands the whole pool out again, sequence by sequence, in
+    the pool's order: the same table as taking blocks one at a time from a
+    fresh free list; the table is rewritten only when it changes; appends
+    continue from what is left (host bookkeeping only, no kernel)."""
+    kvq = _kvq()
+    G, R = 16, 32
+    shape = kvq.CacheShape(4, 2, 4, 2, G, R, paged=True, num_blocks=60, max_blocks_per_seq=20)
+    c = kvq.QuantizedKVCache(shape, device="cpu")
+    c.shuffle_free_blocks(7)
+    for lens in ([300, 47, 0, 200], [40, 300, 200, 17], [0, 0, 0, 0]):
+        lens = np.array(lens)
+        c._prefill_blocks(lens)
+        free = list(c._block_order)
+        want = np.full((4, 20), -1, np.int32)
+        for b, n in enumerate(lens):
+            for i in range(kvq.num_quantized(int(n), G, R) // G):
+                want[b, i] = free.pop()
+        assert np.array_equal(c._bt_host, want)
+        assert np.array_equal(c.block_table.numpy(), want)
+        assert c._free == free
+    # unchanged table: no rewrite (the device copy is left alone)
+    lens = np.array([300, 47, 0, 200])
+    c._prefill_blocks(lens)
+    c.block_table.fill_(-5)
+    c._prefill_blocks(lens)
+    assert int(c.block_table.min()) == -5
+    # an append that crosses a group boundary takes the next free block
+    c.block_table.copy_(torch.from_numpy(c._bt_host))
+    nxt = c._free[-1]
+    grow = lens.copy()
+    grow[2] = R + G   # sequence 2's first group becomes full
+    c._ensure_blocks(grow)
+    assert c._bt_host[2, 0] == nxt and c.block_table[2, 0] == nxt
+    with pytest.raises(kvq.KVQError):
+        c._prefill_blocks(np.array([340, 340, 340, 340]))   # 19 blocks each > 60 in the pool
