@@ -341,6 +341,7 @@ def main():
     # untimed calls first, about 0.2 s of device time, so that the timed ones
     # run at steady clocks (a short leg measured 8-12 % slower)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    caches[0].prefill(K, V, lens, seq_lens_device=lens_dev)   # (the first call also loads the module)
     e0.record(stream)
     caches[0].prefill(K, V, lens, seq_lens_device=lens_dev)
     e1.record(stream)
