@@ -257,8 +257,12 @@ __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* 
 // quantize_group, with fewer instructions per element.
 //  - x - z is one mixed-precision fma, x * 1 + (-z), reading x straight from
 //    its fp16 half: one rounding, exactly (float)x - z.
-//  - rint and the clamp leave an integer in [0, Q] that v_cvt_pk_u8_f32
-//    converts and drops into its byte of a word; code words are assembled
+//  - t = (x - z) * inv clamped to [0, Q], then v_cvt_pk_u8_f32 rounds it to
+//    the nearest integer, ties to even (the conversion rounds in the default
+//    round-to-nearest-even mode; checked on the device at every half-integer
+//    up to 255), and drops it into its byte of a word: clamping before
+//    rounding gives the same integer as clamp(rint(t), 0, Q), since 0 and Q
+//    are integers and rounding is monotonic.  Code words are assembled
 //    from those byte words (code_bit: INT4 codes 0-3 are bytes 0-3 and codes
 //    4-7 the same bytes' high nibbles; INT2 codes 0-7 are nibbles 0-7, even
 //    codes in low nibbles, and codes 8-15 the same nibbles shifted by 2).
@@ -277,8 +281,7 @@ template <int HI>
 __device__ __forceinline__ uint32_t code_byte(uint32_t w, float nz, float inv, float qmax, int pos, uint32_t acc) {
 #pragma clang fp contract(off)
     const float t = minus_z<HI>(w, nz) * inv;
-    const float r = fminf(fmaxf(__builtin_rintf(t), 0.0f), qmax);
-    return __builtin_amdgcn_cvt_pk_u8_f32(r, pos, acc);
+    return __builtin_amdgcn_cvt_pk_u8_f32(fminf(fmaxf(t, 0.0f), qmax), pos, acc);
 }
 
 typedef _Float16 hh2 __attribute__((ext_vector_type(2)));
