@@ -1137,6 +1137,14 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
     const int Hq = L.H * gq;
     const long sh = (long)b * L.H + h;
 
+    // The first unit's loads go out before the query's, so that the two
+    // latencies overlap (the wait below covers both).
+    const int q1 = min(hi, su.uq);
+    int u = lo + wave;
+    lds_u8* s0 = (lds_u8*)(stage_a + wave * S::PITCH);
+    uint32_t h0 = 0;
+    if (u < q1) h0 = issue_any<G, KB, VB, F, PG>(s0, L, c, b, h, u, su.ngroups, lane);
+
     QOps Q;
     {
         // column n: head n (LP: head n%8, high limb for n < 8, low limb above)
@@ -1146,7 +1154,8 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
 #pragma unroll
         for (int j = 0; j < 4; ++j) Q.q[j] = words_h8(hv ? qp[j] : make_uint4(0, 0, 0, 0));
         // The unit loop's loads are invisible to the compiler's wait counting:
-        // retire these here so that it places no wait on them inside the loop.
+        // retire these here (with the first unit's) so that it places no wait
+        // on them inside the loop.
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
     if constexpr (sp_fmt(F)) {
@@ -1175,19 +1184,16 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
     acc_init(A);
 
     {
-        const int q1 = min(hi, su.uq);
         const int ntot = max(1, (q1 - (lo + wave) + kWaves - 1) / kWaves);   // this wave's units
-        int u = lo + wave;
         if (u < q1) {
             // Direct-to-LDS loads: the next NS - 1 units of the wave are in
             // flight, each in a stage buffer of its own, while unit u is
             // processed from its buffer; the buffers rotate.  The waits are
             // explicit (vmcnt counts this wave's outstanding loads, in issue
-            // order).
-            lds_u8* s0 = (lds_u8*)(stage_a + wave * S::PITCH);
+            // order).  Unit u's loads were issued above.
             lds_u8* s1 = (lds_u8*)(stage_b + wave * S::PITCH);
             lds_u8* s2 = (lds_u8*)(stage_c + wave * S::PITCH);   // (NS == 3 only)
-            uint32_t h0 = issue_any<G, KB, VB, F, PG>(s0, L, c, b, h, u, su.ngroups, lane), h1 = 0, h2 = 0;
+            uint32_t h1 = 0, h2 = 0;
             if (NS == 3 && u + kWaves < q1) h1 = issue_any<G, KB, VB, F, PG>(s1, L, c, b, h, u + kWaves, su.ngroups, lane);
             for (;;) {
                 // issue the unit NS - 1 ahead into the buffer freed last
