@@ -284,6 +284,14 @@ __device__ __forceinline__ uint32_t code_byte(uint32_t w, float nz, float inv, f
     return __builtin_amdgcn_cvt_pk_u8_f32(fminf(fmaxf(t, 0.0f), qmax), pos, acc);
 }
 
+// The same with the byte conversion's saturation to [0, 255] as the clamp
+// (8-bit codes).
+template <int HI>
+__device__ __forceinline__ uint32_t code_byte_sat(uint32_t w, float nz, float inv, int pos, uint32_t acc) {
+#pragma clang fp contract(off)
+    return __builtin_amdgcn_cvt_pk_u8_f32(minus_z<HI>(w, nz) * inv, pos, acc);
+}
+
 typedef _Float16 hh2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pk_min(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(hh2, a), __builtin_bit_cast(hh2, b)));
@@ -462,40 +470,32 @@ __device__ void quantize_group8(QuantSmem<G>& sm, const Layout& L, const half_t*
         const uint4 b = *(const uint4*)(vsrc + t * kD + 8 * cg);
         const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
         const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
-        float kx[8], vx[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            kx[2 * e] = h2f(aw[e] & 0xffffu);
-            kx[2 * e + 1] = h2f(aw[e] >> 16);
-            vx[2 * e] = h2f(bw[e] & 0xffffu);
-            vx[2 * e + 1] = h2f(bw[e] >> 16);
-        }
         uint32_t kw[2], vw[2];
         if (F == kFmtInt8) {
-            float kmn = kx[0], kmx = kx[0], vmn = vx[0], vmx = vx[0];
-#pragma unroll
-            for (int e = 1; e < 8; ++e) {
-                kmn = fminf(kmn, kx[e]);
-                kmx = fmaxf(kmx, kx[e]);
-                vmn = fminf(vmn, vx[e]);
-                vmx = fmaxf(vmx, vx[e]);
-            }
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) {
-                kmn = fminf(kmn, __shfl_xor(kmn, off));
-                kmx = fmaxf(kmx, __shfl_xor(kmx, off));
-                vmn = fminf(vmn, __shfl_xor(vmn, off));
-                vmx = fmaxf(vmx, __shfl_xor(vmx, off));
-            }
+            // extremes of the token's 8 channels (packed fp16), then of its
+            // row of 16 lanes
+            const uint32_t km = pk_min(pk_min(aw[0], aw[1]), pk_min(aw[2], aw[3]));
+            const uint32_t kM = pk_max(pk_max(aw[0], aw[1]), pk_max(aw[2], aw[3]));
+            const uint32_t vm = pk_min(pk_min(bw[0], bw[1]), pk_min(bw[2], bw[3]));
+            const uint32_t vM = pk_max(pk_max(bw[0], bw[1]), pk_max(bw[2], bw[3]));
+            const float kmn = row16<false>(fminf(h2f(km & 0xffffu), h2f(km >> 16)));
+            const float kmx = row16<true>(fmaxf(h2f(kM & 0xffffu), h2f(kM >> 16)));
+            const float vmn = row16<false>(fminf(h2f(vm & 0xffffu), h2f(vm >> 16)));
+            const float vmx = row16<true>(fmaxf(h2f(vM & 0xffffu), h2f(vM >> 16)));
             const QParams pk = make_qparams(kmn, kmx, 8);
             const QParams pv = make_qparams(vmn, vmx, 8);
+            // codes: the byte conversion rounds to nearest even and saturates
+            // to [0, 255], which is the clamp itself
+            const float nk = -pk.z, nv = -pv.z;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 kw[h] = vw[h] = 0;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    kw[h] |= quant_code(kx[4 * h + e], pk.z, pk.inv, 255.0f) << (8 * e);
-                    vw[h] |= quant_code(vx[4 * h + e], pv.z, pv.inv, 255.0f) << (8 * e);
+                for (int i = 0; i < 2; ++i) {
+                    kw[h] = code_byte_sat<0>(aw[2 * h + i], nk, pk.inv, 2 * i, kw[h]);
+                    kw[h] = code_byte_sat<1>(aw[2 * h + i], nk, pk.inv, 2 * i + 1, kw[h]);
+                    vw[h] = code_byte_sat<0>(bw[2 * h + i], nv, pv.inv, 2 * i, vw[h]);
+                    vw[h] = code_byte_sat<1>(bw[2 * h + i], nv, pv.inv, 2 * i + 1, vw[h]);
                 }
             }
             if (cg == 0) {
@@ -506,6 +506,14 @@ __device__ void quantize_group8(QuantSmem<G>& sm, const Layout& L, const half_t*
                 *(uint16_t*)(rec + vp + 2 * SPT) = pv.z_bits;
             }
         } else {
+            float kx[8], vx[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kx[2 * e] = h2f(aw[e] & 0xffffu);
+                kx[2 * e + 1] = h2f(aw[e] >> 16);
+                vx[2 * e] = h2f(bw[e] & 0xffffu);
+                vx[2 * e + 1] = h2f(bw[e] >> 16);
+            }
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 kw[h] = fp8_code2(kx[4 * h], kx[4 * h + 1], kinv) | fp8_code2(kx[4 * h + 2], kx[4 * h + 3], kinv) << 16;

@@ -255,32 +255,39 @@ def test_split_entry_points_equal_combined_call():
     compare_attention(b.cpu().numpy(), oracle_attention(to_bits(q), states, SCALE))
 
 
-@pytest.mark.parametrize("kb,vb,G", [(4, 4, 32), (2, 2, 32), (4, 2, 16), (2, 4, 16)])
+@pytest.mark.parametrize("kb,vb,G", [(4, 4, 32), (2, 2, 32), (4, 2, 16), (2, 4, 16), (8, 8, 32), (8, 8, 16)])
 def test_prefill_ties_on_power_of_two_grids(kb, vb, G):
-    """Keys on a per-channel grid and values on a per-token grid, both with a
-    power-of-two step and both extremes present, at half steps: t = (x - z)/s
-    is exact and every odd multiple of 1/2 is a tie, which rounds to even.
-    Codes, scales and zeros bit-exact against the oracle."""
+    """Keys on a per-channel grid (INT8: per-token, like the values) and
+    values on a per-token grid, both with a power-of-two step and both
+    extremes present, at half steps: t = (x - z)/s is exact and every odd
+    multiple of 1/2 is a tie, which rounds to even.  Codes, scales and zeros
+    bit-exact against the oracle."""
     Q = (1 << kb) - 1
     R = G
     B, H, L = 2, 2, 5 * G + R + 3
     w = _w("llama3_8b_layer_b8_32k_int4", name="ties", num_seqs=B, num_q_heads=2 * H, num_kv_heads=H, k_bits=kb,
-           v_bits=vb, group_size=G, residual=R, context=L, tag=43)
+           v_bits=vb, group_size=G, residual=R, context=L, tag=43, kv_format=1 if kb == 8 else 0)
     rng = np.random.Generator(np.random.PCG64(17))
-    # keys: channel c of every group holds base_c + (k/2) s_c, k in [0, 2Q],
-    # the group's first two tokens at k = 0 and k = 2Q
-    k = rng.integers(0, 2 * Q + 1, (B, H, L, 128))
-    g0 = np.arange(L) % G
-    k[:, :, g0 == 0, :] = 0
-    k[:, :, g0 == 1, :] = 2 * Q
-    sk = 2.0 ** -rng.integers(2, 6, (B, H, 1, 128))
-    K = rng.integers(-8, 8, (B, H, 1, 128)) * 0.125 + k * 0.5 * sk
-    # values: token t holds base_t + (k/2) s_t over its channels, channels 0/1 at the extremes
-    Qv = (1 << vb) - 1
-    kv = rng.integers(0, 2 * Qv + 1, (B, H, L, 128))
-    kv[..., 0], kv[..., 1] = 0, 2 * Qv
-    sv = 2.0 ** -rng.integers(2, 6, (B, H, L, 1))
-    V = rng.integers(-8, 8, (B, H, L, 1)) * 0.125 + kv * 0.5 * sv
+
+    def per_token(Qb):
+        # token t holds base_t + (k/2) s_t over its channels, channels 0/1 at the extremes
+        kk = rng.integers(0, 2 * Qb + 1, (B, H, L, 128))
+        kk[..., 0], kk[..., 1] = 0, 2 * Qb
+        st = 2.0 ** -rng.integers(2, 6, (B, H, L, 1))
+        return kk, rng.integers(-8, 8, (B, H, L, 1)) * 0.125 + kk * 0.5 * st
+
+    if kb == 8:
+        k, K = per_token(Q)
+    else:
+        # channel c of every group holds base_c + (k/2) s_c, k in [0, 2Q],
+        # the group's first two tokens at k = 0 and k = 2Q
+        k = rng.integers(0, 2 * Q + 1, (B, H, L, 128))
+        g0 = np.arange(L) % G
+        k[:, :, g0 == 0, :] = 0
+        k[:, :, g0 == 1, :] = 2 * Q
+        sk = 2.0 ** -rng.integers(2, 6, (B, H, 1, 128))
+        K = rng.integers(-8, 8, (B, H, 1, 128)) * 0.125 + k * 0.5 * sk
+    kv, V = per_token((1 << vb) - 1)
     Kt = torch.from_numpy(K.astype(np.float16)).cuda()
     Vt = torch.from_numpy(V.astype(np.float16)).cuda()
     assert np.array_equal(Kt.cpu().numpy().astype(np.float64), K)   # every value exact in fp16
