@@ -627,48 +627,67 @@ __global__ __launch_bounds__(256) void prefill_tail_kernel(Layout L, kvq_cache c
 }
 
 // ---------------------------------------------------------------------------
-// Append one token per (sequence, head) and flush a full group: grid (B).
+// Append one token per (sequence, head) and flush a full group: grid (B, H),
+// then the counters: grid (ceil(B / 256)).
 // ---------------------------------------------------------------------------
 
+// State of sequence b before an append.  Counters written by this library
+// satisfy 0 <= nq <= n, nq % G == 0; anything else is treated as a full cache
+// (nothing is written).  A flush happens when the new token brings the ring
+// to R + G tokens: its oldest G leave the residual window.
+struct AppendState {
+    int n, nq;
+    bool room, flush;
+};
+__device__ __forceinline__ AppendState append_state(const Layout& L, const kvq_cache& c, int b) {
+    AppendState a;
+    a.n = c.n_tokens[b];
+    a.nq = c.n_quant[b];
+    const bool sane = a.nq >= 0 && a.n >= a.nq && (a.nq % L.G) == 0;
+    a.room = sane && (a.n - a.nq) < L.ring && a.n < L.capacity;
+    a.flush = a.room && (a.n + 1 - a.nq == L.R + L.G);
+    return a;
+}
+
+// Append: grid (B, H), one workgroup per (sequence, kv head), so the heads'
+// flushes run side by side.  The new token goes into the ring; on a flush
+// the oldest G ring tokens (the new one among them when R = 0) are quantized
+// into the group's record.  The counters are read here by every head and
+// advanced afterwards by append_counters_kernel.
 template <int G, int KB, int VB, int F>
 __global__ __launch_bounds__(256) void append_kernel(Layout L, kvq_cache c, const half_t* knew,
                                                      const half_t* vnew) {
     __shared__ QuantSmem<G> sm;
-    const int b = blockIdx.x;
-    const int n = c.n_tokens[b];
-    const int nq = c.n_quant[b];
-    // counters written by this library satisfy 0 <= nq <= n, nq % G == 0;
-    // anything else is treated as a full cache (nothing is written)
-    const bool sane = nq >= 0 && n >= nq && (nq % G) == 0;
-    const bool room = sane && (n - nq) < L.ring && n < L.capacity;
-    const bool flush = room && (n + 1 - nq == L.R + G);
-    bool flushed = flush;
-    for (int h = 0; h < L.H; ++h) {
-        const long sh = (long)b * L.H + h;
-        if (room && threadIdx.x < 64) {
-            const int slot = n % L.ring;
-            ((uint32_t*)c.k_res)[(sh * L.ring + slot) * (kD / 2) + threadIdx.x] =
-                ((const uint32_t*)knew)[sh * (kD / 2) + threadIdx.x];
-            ((uint32_t*)c.v_res)[(sh * L.ring + slot) * (kD / 2) + threadIdx.x] =
-                ((const uint32_t*)vnew)[sh * (kD / 2) + threadIdx.x];
-        }
-        __syncthreads();
-        if (flush) {
-            uint8_t* rec = record_at(L, c.packed, c.block_table, b, h, nq / G);
-            if (rec) {
-                const long row = (sh * L.ring + (nq % L.ring)) * kD;
-                quantize_any<G, KB, VB, F>(sm, L, c, h, (const half_t*)c.k_res + row,
-                                           (const half_t*)c.v_res + row, rec);
-            } else {
-                flushed = false;
-            }
-        }
-        __syncthreads();
+    const int b = blockIdx.x, h = blockIdx.y;
+    const AppendState a = append_state(L, c, b);
+    if (!a.room) return;
+    const long sh = (long)b * L.H + h;
+    if (threadIdx.x < 64) {
+        const int slot = a.n % L.ring;
+        ((uint32_t*)c.k_res)[(sh * L.ring + slot) * (kD / 2) + threadIdx.x] =
+            ((const uint32_t*)knew)[sh * (kD / 2) + threadIdx.x];
+        ((uint32_t*)c.v_res)[(sh * L.ring + slot) * (kD / 2) + threadIdx.x] =
+            ((const uint32_t*)vnew)[sh * (kD / 2) + threadIdx.x];
     }
-    if (threadIdx.x == 0 && room) {
-        c.n_tokens[b] = n + 1;
-        c.n_quant[b] = nq + (flushed ? G : 0);
-    }
+    if (!a.flush) return;
+    uint8_t* rec = record_at(L, c.packed, c.block_table, b, h, a.nq / G);
+    if (!rec) return;   // (no block for the group: the counters do not advance it either)
+    __syncthreads();    // the new token's row is visible to the whole workgroup
+    const long row = (sh * L.ring + (a.nq % L.ring)) * kD;
+    quantize_any<G, KB, VB, F>(sm, L, c, h, (const half_t*)c.k_res + row, (const half_t*)c.v_res + row, rec);
+}
+
+// Counters after an append (one thread per sequence, after append_kernel):
+// n + 1, and n_q + G when the group was flushed (it has a record; the record
+// exists for every head or for none).
+__global__ __launch_bounds__(256) void append_counters_kernel(Layout L, kvq_cache c) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= L.B) return;
+    const AppendState a = append_state(L, c, b);
+    if (!a.room) return;
+    const bool flushed = a.flush && record_at(L, c.packed, c.block_table, b, 0, a.nq / L.G) != nullptr;
+    c.n_tokens[b] = a.n + 1;
+    c.n_quant[b] = a.nq + (flushed ? L.G : 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -828,9 +847,12 @@ hipError_t launch_prefill(const Layout& L, const kvq_cache& c, const half_t* k, 
 hipError_t launch_append(const Layout& L, const kvq_cache& c, const half_t* k, const half_t* v,
                          hipStream_t s) {
 #define KVQ_AP(GG, KB, VB, FF) \
-    hipLaunchKernelGGL((append_kernel<GG, KB, VB, FF>), dim3(L.B), dim3(256), 0, s, L, c, k, v)
+    hipLaunchKernelGGL((append_kernel<GG, KB, VB, FF>), dim3(L.B, L.H), dim3(256), 0, s, L, c, k, v)
     KVQ_DISPATCH(L, KVQ_AP);
 #undef KVQ_AP
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(append_counters_kernel, dim3((L.B + 255) / 256), dim3(256), 0, s, L, c);
     return hipGetLastError();
 }
 
