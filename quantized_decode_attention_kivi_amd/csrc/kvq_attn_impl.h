@@ -148,6 +148,19 @@ __device__ __forceinline__ h8 levels8(const uint32_t* w, int j, const uint32_t (
     }
 }
 
+// a * b - c elementwise with one fp16 rounding (the exact low part of a * b
+// when c is its rounded value): the subtrahend's sign by the instruction's
+// negate modifiers, which the compiler does not always choose on its own.
+__device__ __forceinline__ h8 fma_sub_h8(h8 a, h8 b, h8 c) {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    const u4 x = __builtin_bit_cast(u4, a), y = __builtin_bit_cast(u4, b), z = __builtin_bit_cast(u4, c);
+    u4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        asm("v_pk_fma_f16 %0, %1, %2, %3 neg_lo:[0,0,1] neg_hi:[0,0,1]" : "=v"(r[i]) : "v"(x[i]), "v"(y[i]), "v"(z[i]));
+    return __builtin_bit_cast(h8, r);
+}
+
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -716,7 +729,7 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
 #pragma clang fp contract(off)
                 const h8 hi = Q.q[j] * s;
                 qhi[j] = hi;
-                if (!LP) qlo[j] = __builtin_elementwise_fma(Q.q[j], s, -hi);
+                if (!LP) qlo[j] = fma_sub_h8(Q.q[j], s, hi);
             }
         }
         if (LP && lo_limb) {
@@ -725,7 +738,7 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const h8 s = __builtin_bit_cast(h8, lds_read<u32x4>(km + 16 * (4 * g + j)));
-                qhi[j] = __builtin_elementwise_fma(Q.q[j], s, -qhi[j]);
+                qhi[j] = fma_sub_h8(Q.q[j], s, qhi[j]);
             }
             cz = f4{0.0f, 0.0f, 0.0f, 0.0f};
         }
