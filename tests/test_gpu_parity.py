@@ -301,3 +301,46 @@ def test_prefill_ties_on_power_of_two_grids(kb, vb, G):
     odd = (k % 2 == 1).mean()
     assert odd > 0.3
     compare_codes(cache, states)
+
+
+@pytest.mark.parametrize("kb,vb,G", [(4, 4, 32), (2, 2, 16), (4, 2, 32), (8, 8, 32)])
+def test_prefill_degenerate_sets(kb, vb, G):
+    """Sets whose scale is 0 or an fp16 subnormal, and signed zeros: key
+    channels constant over a group (0 and -0 among them) or spanning a few
+    subnormal steps; value rows (and INT8 key rows) constant, of mixed +-0,
+    or of subnormals.  Codes, scales, zeros and dequantized values bit-exact
+    against the oracle."""
+    B, H, R = 2, 2, G
+    L = 6 * G + R + 5
+    w = _w("llama3_8b_layer_b8_32k_int4", name="degenerate", num_seqs=B, num_q_heads=2 * H, num_kv_heads=H,
+           k_bits=kb, v_bits=vb, group_size=G, residual=R, context=L, tag=44, kv_format=1 if kb == 8 else 0)
+    rng = np.random.Generator(np.random.PCG64(23))
+    K = rng.standard_normal((B, H, L, 128)).astype(np.float16)
+    V = rng.standard_normal((B, H, L, 128)).astype(np.float16)
+    # fp16 subnormals: a span of 5 steps (the scale rounds to 0 or one step)
+    # or of up to 399 (a subnormal scale)
+    tiny = lambda shape, top=400: (rng.integers(0, top, shape) * 2.0 ** -24).astype(np.float16)
+    signed_zero = lambda shape: np.where(rng.integers(0, 2, shape) == 1, np.float16(-0.0), np.float16(0.0))
+    g0 = (np.arange(L) // G) * G
+    K[..., 0:6] = K[:, :, g0, 0:6]              # constant over each group
+    K[..., 6:10] = signed_zero((B, H, L, 4))    # +-0 only
+    K[..., 10:12] = tiny((B, H, L, 2), 6)       # a few subnormal steps
+    K[..., 12:14] = tiny((B, H, L, 2))
+    K[..., 14:18] = (1.0 + rng.integers(0, 3, (B, H, L, 4)) * 2.0 ** -10).astype(np.float16)
+    for rows, fill in ((np.arange(L) % 7 == 0, "const"), (np.arange(L) % 11 == 0, "zero"),
+                       (np.arange(L) % 13 == 0, "tiny")):
+        for T in ((K, V) if kb == 8 else (V,)):
+            if fill == "const":
+                T[:, :, rows, :] = T[:, :, rows, :1]
+            elif fill == "zero":
+                T[:, :, rows, :] = signed_zero((B, H, int(rows.sum()), 128))
+            else:
+                T[:, :, rows, :] = tiny((B, H, int(rows.sum()), 128))
+    Kt = torch.from_numpy(K).cuda()
+    Vt = torch.from_numpy(V).cuda()
+    lens = np.array([L, L - G - 3])
+    cache = make_cache(w, lens)
+    print("degenerate kb=%d vb=%d G=%d" % (kb, vb, G), flush=True)
+    cache.prefill(Kt, Vt, lens)
+    states = oracle_states(to_bits(Kt), to_bits(Vt), lens, w, cap=L + 256)
+    compare_codes(cache, states)
