@@ -1134,7 +1134,8 @@ __device__ __forceinline__ void process_any(const lds_u8* buf, uint32_t has, Wav
 // < gq: output[128] unnormalised, running max in log2 units, weight sum) at
 // `part`.  Called by every thread of the workgroup.
 template <int G, int KB, int VB, int F, bool LP, bool TP, bool PG, int NS>
-__device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_b, uint8_t* stage_c, float (*wm)[16],
+__device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_b, uint8_t* stage_c, uint8_t* stage_d,
+                                               float (*wm)[16],
                                                float (*wl)[16],
                                                float (*wpz)[16], const Layout& L, const kvq_cache& c,
                                                const half_t* __restrict__ q, float sl2, int gq, int b, int h,
@@ -1204,40 +1205,45 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
             // processed from its buffer; the buffers rotate.  The waits are
             // explicit (vmcnt counts this wave's outstanding loads, in issue
             // order).  Unit u's loads were issued above.
-            lds_u8* s1 = (lds_u8*)(stage_b + wave * S::PITCH);
-            lds_u8* s2 = (lds_u8*)(stage_c + wave * S::PITCH);   // (NS == 3 only)
-            uint32_t h1 = 0, h2 = 0;
-            if (NS == 3 && u + kWaves < q1) h1 = issue_any<G, KB, VB, F, PG>(s1, L, c, b, h, u + kWaves, su.ngroups, lane);
+            lds_u8* sb[NS];
+            uint32_t hb[NS] = {};
+            sb[0] = s0;
+            hb[0] = h0;
+            uint8_t* const arrays[4] = {stage_a, stage_b, stage_c, stage_d};
+#pragma unroll
+            for (int i = 1; i < NS; ++i) sb[i] = (lds_u8*)(arrays[i] + wave * S::PITCH);
+            // units u + kWaves .. u + (NS - 2) kWaves go out now, the one
+            // NS - 1 ahead at the top of each iteration
+#pragma unroll
+            for (int i = 1; i + 1 < NS; ++i)
+                if (u + i * kWaves < q1) hb[i] = issue_any<G, KB, VB, F, PG>(sb[i], L, c, b, h, u + i * kWaves, su.ngroups, lane);
             for (;;) {
                 // issue the unit NS - 1 ahead into the buffer freed last
-                lds_u8* const nxt = NS == 3 ? s2 : s1;
                 const int ahead = u + (NS - 1) * kWaves;
                 if (ahead < q1) {
                     __builtin_amdgcn_s_waitcnt(kLgkmZero);   // last reads of that buffer returned
-                    const uint32_t hn = issue_any<G, KB, VB, F, PG>(nxt, L, c, b, h, ahead, su.ngroups, lane);
-                    if (NS == 3) h2 = hn; else h1 = hn;
+                    hb[NS - 1] = issue_any<G, KB, VB, F, PG>(sb[NS - 1], L, c, b, h, ahead, su.ngroups, lane);
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * S::LOADS));
-                } else if (NS == 3 && u + kWaves < q1) {
-                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::LOADS));
                 } else {
-                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                    // the wave's later units still in flight: min(NS - 2, those left)
+                    const int left = min((q1 - 1 - u) / kWaves, NS - 2);
+                    if (NS >= 4 && left >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * S::LOADS));
+                    else if (NS >= 3 && left >= 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::LOADS));
+                    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
                 }
                 wave_sync();
                 set_progress_prio((q1 - u + kWaves - 1) / kWaves, ntot);
-                process_any<G, KB, VB, F, LP, TP>(s0, h0, A, Q, sl2q, qsum, vscl, lane, R, wave, 32 * u, L, SPL, gq);
+                process_any<G, KB, VB, F, LP, TP>(sb[0], hb[0], A, Q, sl2q, qsum, vscl, lane, R, wave, 32 * u, L, SPL, gq);
                 u += kWaves;
                 if (u >= q1) break;
                 // rotate: the buffer just processed is the next to be refilled
-                lds_u8* const t = s0;
-                s0 = s1;
-                h0 = h1;
-                if (NS == 3) {
-                    s1 = s2;
-                    h1 = h2;
-                    s2 = t;
-                } else {
-                    s1 = t;
+                lds_u8* const t = sb[0];
+#pragma unroll
+                for (int i = 0; i + 1 < NS; ++i) {
+                    sb[i] = sb[i + 1];
+                    hb[i] = hb[i + 1];
                 }
+                sb[NS - 1] = t;
             }
         }
     }
@@ -1318,9 +1324,10 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
 // than INT2 ones.  (Three waves lose little where the kernel waits on HBM.)
 // The 8-bit formats stage twice the bytes per unit: their LDS allows two
 // workgroups per CU, two waves per SIMD.
-// Stage buffers per wave.  Two everywhere: three (two units in flight while
-// one is processed) measured no faster on the INT4 8 x 32K layer (66.8 us
-// either way), its LDS leaving two workgroups per CU instead of three.
+// Stage buffers per wave (the unit loop takes 2 to 4).  Two everywhere: more
+// units in flight per wave cost workgroups per CU through LDS, and measured
+// no faster (INT4 8 x 32K layer: 65.4 us with two, 65.7 with three, 66.2
+// with four; INT2 1 x 128K: 30.0, 30.3, 31.8; paged batch: 152, 152, 163).
 constexpr int attn_stages(int G, int KB, int VB, int F) { return 2; }
 
 // Pre-RoPE keys take registers for the rotation: three waves.
@@ -1340,9 +1347,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves(
     __shared__ __attribute__((aligned(16))) uint8_t stage_b[kWaves * S::PITCH];
     constexpr int NS = attn_stages(G, KB, VB, F);
     uint8_t* stage_c = nullptr;
-    if constexpr (NS == 3) {
+    uint8_t* stage_d = nullptr;
+    if constexpr (NS >= 3) {
         __shared__ __attribute__((aligned(16))) uint8_t stage_c_lds[kWaves * S::PITCH];
         stage_c = stage_c_lds;
+    }
+    if constexpr (NS >= 4) {
+        __shared__ __attribute__((aligned(16))) uint8_t stage_d_lds[kWaves * S::PITCH];
+        stage_d = stage_d_lds;
     }
     __shared__ float wm[kWaves][16], wl[kWaves][16], wpz[kWaves][16];
     __shared__ int wsum[kWaves];
@@ -1423,7 +1435,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves(
             asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l0));
             if (l0 == 0) meta[1 + s] = ps;
         }
-        attend_segment<G, KB, VB, F, LP, TP, PG, NS>(stage_a, stage_b, stage_c, wm, wl, wpz, L, c, q, sl2, gq, b, h, su,
+        attend_segment<G, KB, VB, F, LP, TP, PG, NS>(stage_a, stage_b, stage_c, stage_d, wm, wl, wpz, L, c, q, sl2, gq, b, h, su,
                                           unit_at(su, lo), unit_at(su, hi), ws + ((long)w + s) * gq * kPart,
                                           lane, wave, R, SPL);
         if (ps + hi >= end) break;
