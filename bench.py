@@ -186,6 +186,26 @@ def write_traffic(args):
     print(json.dumps(rec[w.name]))
 
 
+def stream_copy_gbs(torch, dev, nbytes=1 << 30, reps=10):
+    """Reference point measured in the same run: a device-to-device copy of
+    nbytes (4x the last-level cache), (read + written bytes) / time, median of
+    reps event-timed copies after three untimed ones."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    stream = torch.cuda.current_stream()
+    for a, b in evs:
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    del src, dst
+    return round(2.0 * nbytes / (ms / 1e3) / 1e9, 1)
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the same workload
 # ---------------------------------------------------------------------------
@@ -419,6 +439,8 @@ def main():
     kern_achieved = float(np.mean(step_bytes2)) / kern_avg_s / 1e9
     ms_per_step = wall / args.steps * 1e3
 
+    copy_gbs = stream_copy_gbs(torch, dev)
+
     digest = source_digest(ATTN_KERNEL_SOURCES)
     traffic = recorded_traffic(w.name, digest)
     res = {
@@ -454,6 +476,7 @@ def main():
         "attention_kernel_us": round(kern_avg_s * 1e6, 3),
         "merge_kernel_us": round(float(merge_ms.mean()) * 1e3, 3),
         "attention_bytes_per_launch": int(bytes_avg),
+        "stream_copy_gbs": copy_gbs,
         "quantize_tokens_per_s": round(float(lens.sum()) / (pre_t / 1e3), 1),
         "quantize_gbs": round(pbytes / (pre_t / 1e3) / 1e9, 2),
         "quantize_us": round(pre_t * 1e3, 3),
