@@ -40,13 +40,31 @@ int codebook_levels16(int bits, int* levels16) {
     return F;
 }
 
-static void fill_codebook(int bits, uint32_t* lut, float* mid) {
+// The kernels' tables of a codebook grid: byte levels (lut) and the
+// midpoints between neighbouring levels (mid).  They depend on the bit width
+// alone, so they are computed once per width (the quantiles cost tens of
+// microseconds, far more than a decode call's launch).
+struct CodebookTables {
+    uint32_t lut[4];
+    float mid[15];
+};
+
+static CodebookTables make_codebook_tables(int bits) {
+    CodebookTables t;
     int lev[16] = {0};
     const int F = codebook_levels16(bits, lev);
     const int n = 1 << bits;
-    for (int w = 0; w < 4; ++w) lut[w] = 0;
-    for (int k = 0; k < n; ++k) lut[k >> 2] |= (uint32_t)lev[k] << (8 * (k & 3));
-    for (int k = 0; k < 15; ++k) mid[k] = k + 1 < n ? (float)(lev[k] + lev[k + 1]) / (float)(2 * F) : 0.0f;
+    for (int w = 0; w < 4; ++w) t.lut[w] = 0;
+    for (int k = 0; k < n; ++k) t.lut[k >> 2] |= (uint32_t)lev[k] << (8 * (k & 3));
+    for (int k = 0; k < 15; ++k) t.mid[k] = k + 1 < n ? (float)(lev[k] + lev[k + 1]) / (float)(2 * F) : 0.0f;
+    return t;
+}
+
+static void fill_codebook(int bits, uint32_t* lut, float* mid) {
+    static const CodebookTables t2 = make_codebook_tables(2), t4 = make_codebook_tables(4);   // (thread-safe init)
+    const CodebookTables& t = bits == 2 ? t2 : t4;
+    for (int w = 0; w < 4; ++w) lut[w] = t.lut[w];
+    for (int k = 0; k < 15; ++k) mid[k] = t.mid[k];
 }
 
 kvq_status make_layout(const kvq_config* cfg, Layout* L) {
