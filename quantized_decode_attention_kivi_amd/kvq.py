@@ -245,6 +245,7 @@ class QuantizedKVCache:
             self._bt_host = np.full((shape.num_seqs, shape.max_blocks_per_seq), -1, np.int32)
             self._block_order = list(range(shape.num_blocks - 1, -1, -1))  # pop() hands out 0, 1, 2, ...
             self._free = list(self._block_order)
+            self._nblk = np.zeros(shape.num_seqs, np.int64)   # blocks held per sequence (table prefix)
         self.lens = np.zeros(shape.num_seqs, np.int64)
         self.k_scale = self.v_scale = None
         if shape.kv_format == FORMAT_FP8_E4M3:
@@ -317,21 +318,33 @@ class QuantizedKVCache:
 
     # -- paged block bookkeeping (host) ------------------------------------
     def _ensure_blocks(self, lens_after):
-        """Give every sequence a block for each key group it will hold."""
+        """Give every sequence a block for each key group it will hold.  Only
+        the new entries go to the device table: a copy from pinned memory and
+        an indexed store, both ordered on the current stream before the call
+        that reads them, so the host does not wait for the device."""
         if not self.shape.paged:
             return
-        changed = False
-        for b, n in enumerate(lens_after):
-            need = num_quantized(int(n), self.G, self.R) // self.G
-            have = int(np.count_nonzero(self._bt_host[b] >= 0))
-            while have < need:
+        need = np.maximum(np.asarray(lens_after, np.int64) - self.R, 0) // self.G
+        short = np.nonzero(need > self._nblk)[0]
+        if len(short) == 0:
+            return
+        if int(need.max()) > self._bt_host.shape[1]:
+            raise KVQError(KVQ_ECAPACITY, "paged cache: a sequence needs more than max_blocks_per_seq blocks")
+        rows, cols, vals = [], [], []
+        for b in short:
+            for g in range(int(self._nblk[b]), int(need[b])):
                 if not self._free:
                     raise KVQError(KVQ_ECAPACITY, "paged cache out of blocks")
-                self._bt_host[b, have] = self._free.pop()
-                have += 1
-                changed = True
-        if changed:
-            self.block_table.copy_(torch.from_numpy(self._bt_host))
+                blk = self._free.pop()
+                self._bt_host[b, g] = blk
+                rows.append(int(b))
+                cols.append(g)
+                vals.append(blk)
+            self._nblk[b] = need[b]
+        upd = torch.tensor([rows, cols, vals], dtype=torch.int64)
+        if self.device.type == "cuda":
+            upd = upd.pin_memory().to(self.device, non_blocking=True)
+        self.block_table[upd[0], upd[1]] = upd[2].to(torch.int32)
 
     def _prefill_blocks(self, lens):
         """Block table after a prefill: the whole pool is free again and each
@@ -350,6 +363,7 @@ class QuantizedKVCache:
             table[b, :k] = order[start:start + k]
             start += int(k)
         self._free = self._block_order[:len(self._block_order) - total]
+        self._nblk = need.copy()
         if not np.array_equal(table, self._bt_host):
             self._bt_host[:] = table
             self.block_table.copy_(torch.from_numpy(self._bt_host))

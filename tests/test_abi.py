@@ -324,5 +324,25 @@ def test_prefill_block_assignment():
     grow[2] = R + G   # sequence 2's first group becomes full
     c._ensure_blocks(grow)
     assert c._bt_host[2, 0] == nxt and c.block_table[2, 0] == nxt
+    assert np.array_equal(c.block_table.numpy(), c._bt_host)
+    # several sequences, several groups at once: the next blocks in pool
+    # order, in sequence order, and only those entries are written
+    free = list(c._free)
+    c.block_table[c.block_table < 0] = -7          # marks the entries that must stay unwritten
+    before = c.block_table.clone()
+    grow2 = grow + np.array([16, 0, 3 * G, 2 * G])
+    c._ensure_blocks(grow2)
+    want = {}
+    for b, n in enumerate(grow2):
+        for g in range(int(np.count_nonzero(before[b].numpy() >= 0)), kvq.num_quantized(int(n), G, R) // G):
+            want[(b, g)] = free.pop()
+    assert c._free == free and len(want) == 6   # 1 + 3 + 2 new groups
+    tab = c.block_table.numpy()
+    for (b, g), blk in want.items():
+        assert tab[b, g] == blk and c._bt_host[b, g] == blk
+    untouched = np.ones(tab.shape, bool)
+    for (b, g) in want:
+        untouched[b, g] = False
+    assert np.array_equal(tab[untouched], before.numpy()[untouched])
     with pytest.raises(kvq.KVQError):
         c._prefill_blocks(np.array([340, 340, 340, 340]))   # 19 blocks each > 60 in the pool
