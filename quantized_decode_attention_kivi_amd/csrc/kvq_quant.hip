@@ -258,9 +258,10 @@ __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* 
 //  - x - z is one mixed-precision fma, x * 1 + (-z), reading x straight from
 //    its fp16 half: one rounding, exactly (float)x - z.
 //  - t = (x - z) * inv clamped to [0, Q], then v_cvt_pk_u8_f32 rounds it to
-//    the nearest integer, ties to even (the conversion rounds in the default
-//    round-to-nearest-even mode; checked on the device at every half-integer
-//    up to 255), and drops it into its byte of a word: clamping before
+//    the nearest integer, ties to even (the conversion follows the default
+//    round-to-nearest-even mode and saturates to [0, 255]; the GPU parity
+//    tests put keys and values on exact ties at every bit width), and drops
+//    it into its byte of a word: clamping before
 //    rounding gives the same integer as clamp(rint(t), 0, Q), since 0 and Q
 //    are integers and rounding is monotonic.  Code words are assembled
 //    from those byte words (code_bit: INT4 codes 0-3 are bytes 0-3 and codes
