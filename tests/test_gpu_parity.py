@@ -39,6 +39,7 @@ SMALL = {
                          num_kv_heads=2, k_bits=4, v_bits=2, group_size=16, residual=32, context=777, tag=22),
     "mha_g32_r0": _w("llama3_8b_layer_b8_32k_int4", name="mha", num_seqs=2, num_q_heads=4, num_kv_heads=4,
                      k_bits=4, v_bits=2, group_size=32, residual=0, context=1000, tag=23),
+    "paged_k4v2_g16": _w("paged_64seq_1k_16k_k4v2", name="pga", num_seqs=3, context=700, min_context=200, tag=25),
 }
 
 
@@ -84,17 +85,19 @@ def test_edge_lengths_in_one_batch():
     compare_attention(out, ref)
 
 
-@pytest.mark.parametrize("case", ["gqa4_int4_ragged", "gqa16_k4v2_g16", "mha_g32_r0"])
+@pytest.mark.parametrize("case", ["gqa4_int4_ragged", "gqa16_k4v2_g16", "mha_g32_r0", "paged_k4v2_g16"])
 def test_append_sequence_matches_prefill(case):
     """prefill(m) followed by appends that cross several flushes must equal
-    the oracle's incremental state, step by step."""
+    the oracle's incremental state, step by step (paged: each flush's block
+    is handed out from a shuffled pool and written into the device table
+    between calls)."""
     w = SMALL[case]
     m = 300 if w.residual < 300 else w.residual + 5
     steps = 3 * w.group_size + 7
     lens0 = np.full(w.num_seqs, m, np.int64)
     lens0[-1] = max(0, m - 17)  # ragged
     K, V = synth.make_kv(w, max_len=m + steps, device="cuda")
-    cache = make_cache(w, lens0 + steps + 1, max_tokens=m + steps + 8)
+    cache = make_cache(w, lens0 + steps + 1, max_tokens=m + steps + 8, shuffle_seed=5)
     cache.prefill(K[:, :, :m].contiguous(), V[:, :, :m].contiguous(), lens0)
     kb, vb = to_bits(K), to_bits(V)
     states = oracle_states(kb[:, :, :m], vb[:, :, :m], lens0, w, cap=m + steps + 8)
