@@ -193,6 +193,21 @@ static int attn_slots(const Layout& L, int gq) {
     }
 }
 
+// Compute units of the current device (256 when none is visible).
+static int device_cus() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        (void)hipGetLastError();
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
 AttnPlan plan_attention(const Layout& L, int num_q_heads) {
     AttnPlan P;
     const int gq = num_q_heads / L.H;
@@ -204,6 +219,15 @@ AttnPlan plan_attention(const Layout& L, int num_q_heads) {
     // mix of lengths), no more than 1 per 8 units of the batch at capacity,
     // and never more partials per stream than the merge holds.
     long nwg = attn_slots(L, gq);
+    // Uniform low-bit grid in a contiguous cache: two workgroups per CU keep
+    // the split-K kernel as fast as a full round and halve the partials, so
+    // the merge reads one chunk per row; so no more than about 8 partials
+    // per stream, and no fewer than two workgroups per CU (70B layer, 8
+    // streams: whole call 39.0-39.9 -> 37.3-37.5 us; 8B layer, 64 streams:
+    // within run-to-run spread; the 80-layer cache, paged batches and the
+    // heavier formats keep a full round, which they need).
+    if (attn_key(L) / 10000 == kFmtKivi && !L.paged)
+        nwg = std::min(nwg, std::max(2L * device_cus(), 8 * streams));
     nwg = std::min(nwg, std::max(1L, (streams * maxu + 7) / 8));
     if (const char* e = getenv("KVQ_WORKGROUPS")) {
         const int v = atoi(e);
