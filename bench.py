@@ -248,11 +248,19 @@ def cpu_baseline(w, K, V, q, lens, budget_s, scales=None):
         t2 = time.perf_counter()
         return t1 - t0, t2 - t1
 
+    def stream_bytes(b):
+        n = int(lens[b])
+        nq = n_quant(n, w.group_size, w.residual)
+        return nq * 128 * (w.k_bits + w.v_bits) // 8 + meta_bytes(nq, w) + (n - nq) * 128 * 4 + gq * 128 * 6
+
     wall0 = time.perf_counter()
     attn_wall = 0.0
     quant_wall = 0.0
+    # the first stream alone on one thread: the single-threaded rate
+    q1, a1 = one(jobs[0])
+    single = stream_bytes(jobs[0][0]) / a1 / 1e9
     with ThreadPoolExecutor(threads) as ex:
-        i = 0
+        i = 1
         while i < len(jobs) and time.perf_counter() - wall0 < budget_s:
             batch = jobs[i:i + threads]
             tb = time.perf_counter()
@@ -266,23 +274,24 @@ def cpu_baseline(w, K, V, q, lens, budget_s, scales=None):
             attn_wall += (te - tb) * sa / max(sq + sa, 1e-12)
             done.extend(batch)
             i += len(batch)
+    pooled = bool(done)
+    if not pooled:   # a single stream: the pool had nothing left
+        done, quant_wall, attn_wall, threads = [jobs[0]], q1, a1, 1
     # algorithmic bytes of the sampled streams (query/output shares included)
-    sb = 0
-    stok = 0
-    for b, h in done:
-        n = int(lens[b])
-        nq = n_quant(n, w.group_size, w.residual)
-        sb += (nq * 128 * (w.k_bits + w.v_bits) // 8 + meta_bytes(nq, w) + (n - nq) * 128 * 4 + gq * 128 * 6)
-        stok += n
+    sb = sum(stream_bytes(b) for b, _ in done)
+    stok = sum(int(lens[b]) for b, _ in done)
     return {
         "value": round(sb / attn_wall / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
         "sample": "%d of %d (sequence, kv head) streams of %s, each quantized then dequantized and "
-                  "attended by its %d query heads in fp64 (%.1f s wall)" % (
-                      len(done), len(jobs), w.name, gq, time.perf_counter() - wall0),
+                  "attended by its %d query heads in fp64 %s (%.1f s wall)" % (
+                      len(done), len(jobs), w.name, gq,
+                      "on the thread pool; the first stream also alone on one thread for single_thread_value"
+                      if pooled else "on one thread", time.perf_counter() - wall0),
         "quantize_tokens_per_s": round(stok / w.num_kv_heads / quant_wall, 1),
+        "single_thread_value": round(single, 4),
         "host_cpus": os.cpu_count(),
     }
 
