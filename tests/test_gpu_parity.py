@@ -171,6 +171,39 @@ def test_full_size_workload(name):
     compare_attention(out.cpu().numpy(), oracle_attention(to_bits(q), states, SCALE))
 
 
+def test_full_size_decode_steps():
+    """The 8B layer at full size through the decode steps the benchmark times:
+    prefill, then 40 appends (every stream flushes one group at the 32nd),
+    then attention; sampled streams bit-exact and every attention row against
+    the oracle's incremental state."""
+    w = synth.WORKLOADS["llama3_8b_layer_b8_32k_int4"]
+    lens = synth.seq_lengths(w)
+    L = int(lens.max())
+    steps = 40
+    K, V = synth.make_kv(w, max_len=L, device="cuda")
+    cache = make_cache(w, lens, max_tokens=L + steps + 8)
+    print("prefill %s, then %d appends" % (w.name, steps), flush=True)
+    cache.prefill(K, V, lens)
+    kb, vb = to_bits(K), to_bits(V)
+    del K, V
+    states = oracle_states(kb, vb, lens, w, cap=L + steps + 8)
+    del kb, vb
+    for s in range(steps):
+        kn, vn = synth.make_tokens(w, s, device="cuda")
+        cache.append(kn.contiguous(), vn.contiguous())
+        knb, vnb = to_bits(kn), to_bits(vn)
+        for b in range(w.num_seqs):
+            for h in range(w.num_kv_heads):
+                states[b][h].append(knb[b, h], vnb[b, h])
+    assert all(states[b][h].nq == lens[b] - w.residual + w.group_size
+               for b in range(w.num_seqs) for h in range(w.num_kv_heads))
+    compare_codes(cache, states, streams=[(0, 0), (w.num_seqs - 1, w.num_kv_heads - 1)])
+    q = synth.make_query(w, device="cuda", step=7)
+    out = cache.decode_attention(q, SCALE)
+    torch.cuda.synchronize()
+    compare_attention(out.cpu().numpy(), oracle_attention(to_bits(q), states, SCALE))
+
+
 def test_full_size_paged_workload():
     """The paged workload at full size (64 sequences of 1K-16K tokens, G = 16
     blocks handed out from a shuffled pool): sampled sequences bit-exact,
