@@ -14,6 +14,7 @@ import torch
 
 import oracle
 from quantized_decode_attention_kivi_amd import synth
+from quantized_decode_attention_kivi_amd.kvq import num_quantized as kvq_num_quantized
 from parity_util import (compare_attention, compare_codes, make_cache, oracle_attention, oracle_states,
                          to_bits)
 
@@ -212,6 +213,40 @@ def test_full_size_paged_workload():
     cache, states, _, _ = _run_prefill(w)
     compare_codes(cache, states, streams=[(0, 0), (17, 3), (w.num_seqs - 1, w.num_kv_heads - 1)])
     q = synth.make_query(w, device="cuda")
+    out = cache.decode_attention(q, SCALE)
+    torch.cuda.synchronize()
+    compare_attention(out.cpu().numpy(), oracle_attention(to_bits(q), states, SCALE))
+
+
+def test_full_size_paged_decode_steps():
+    """The paged workload at full size through decode steps: prefill from a
+    shuffled pool, then 20 appends (every sequence crosses at least one
+    16-token flush, its block written into the device table between calls),
+    then attention; sampled sequences bit-exact, every attention row."""
+    w = synth.WORKLOADS["paged_64seq_1k_16k_k4v2"]
+    lens = synth.seq_lengths(w).astype(np.int64)
+    L = int(lens.max())
+    steps = 20
+    K, V = synth.make_kv(w, max_len=L, device="cuda")
+    cache = make_cache(w, lens + steps + 1, shuffle_seed=9)
+    print("prefill %s, then %d appends" % (w.name, steps), flush=True)
+    cache.prefill(K, V, lens)
+    kb, vb = to_bits(K), to_bits(V)
+    del K, V
+    states = oracle_states(kb, vb, lens, w, cap=L + steps + 8)
+    del kb, vb
+    for s in range(steps):
+        kn, vn = synth.make_tokens(w, s, device="cuda")
+        cache.append(kn.contiguous(), vn.contiguous())
+        knb, vnb = to_bits(kn), to_bits(vn)
+        for b in range(w.num_seqs):
+            for h in range(w.num_kv_heads):
+                states[b][h].append(knb[b, h], vnb[b, h])
+    flushed = [states[b][0].nq > kvq_num_quantized(int(lens[b]), w.group_size, w.residual)
+               for b in range(w.num_seqs)]
+    assert all(flushed)
+    compare_codes(cache, states, streams=[(0, 0), (17, 3), (w.num_seqs - 1, w.num_kv_heads - 1)])
+    q = synth.make_query(w, device="cuda", step=5)
     out = cache.decode_attention(q, SCALE)
     torch.cuda.synchronize()
     compare_attention(out.cpu().numpy(), oracle_attention(to_bits(q), states, SCALE))
