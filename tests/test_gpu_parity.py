@@ -172,12 +172,13 @@ def test_full_size_workload(name):
     compare_attention(out.cpu().numpy(), oracle_attention(to_bits(q), states, SCALE))
 
 
-def test_full_size_decode_steps():
-    """The 8B layer at full size through the decode steps the benchmark times:
-    prefill, then 40 appends (every stream flushes one group at the 32nd),
-    then attention; sampled streams bit-exact and every attention row against
-    the oracle's incremental state."""
-    w = synth.WORKLOADS["llama3_8b_layer_b8_32k_int4"]
+@pytest.mark.parametrize("name", ["llama3_8b_layer_b8_32k_int4", "llama3_70b_layer_b1_128k_int2"])
+def test_full_size_decode_steps(name):
+    """The single-layer workloads at full size through the decode steps the
+    benchmark times: prefill, then 40 appends (every stream flushes one group
+    at the 32nd), then attention; sampled streams bit-exact and every
+    attention row against the oracle's incremental state."""
+    w = synth.WORKLOADS[name]
     lens = synth.seq_lengths(w)
     L = int(lens.max())
     steps = 40
