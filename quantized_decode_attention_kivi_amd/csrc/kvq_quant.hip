@@ -449,6 +449,145 @@ __device__ void quantize_group_uniform(QuantSmem<G>& sm, const Layout& L, const 
     __syncthreads();  // LDS may be reused by the caller
 }
 
+// Two consecutive 16-token records of one stream on the uniform grid in one
+// workgroup (bulk quantization of G = 16 layouts): the same arithmetic as
+// quantize_group_uniform, record by record, with the per-record work (the
+// 128 channel extremes and scales) spread over all four waves.  Thread
+// (ts, cg) holds channels 8cg .. 8cg+7 of token ts of each record.  A null
+// record pointer: that record is skipped (its rows are not read).
+struct QuantSmemPair {
+    uint16_t kmn[2][16][kD], kmx[2][16][kD];   // fp16 extremes per record, token, channel
+    float kz[2][kD], kinv[2][kD];
+    uint8_t vcode[32][kD];
+};
+
+template <int KB, int VB>
+__device__ void quantize_pair16(QuantSmemPair& sm, const Layout& L, const half_t* __restrict__ ksrc,
+                                const half_t* __restrict__ vsrc, uint8_t* __restrict__ rec0,
+                                uint8_t* __restrict__ rec1) {
+    const int tid = threadIdx.x;
+    const int cg = tid & 15;
+    const int ts = tid >> 4;
+    uint8_t* const recs[2] = {rec0, rec1};
+
+    uint32_t kw[2][4], vw[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int t = ts + 16 * j;
+        uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+        if (recs[j]) {
+            a = *(const uint4*)(ksrc + t * kD + 8 * cg);
+            b = *(const uint4*)(vsrc + t * kD + 8 * cg);
+        }
+        kw[j][0] = a.x; kw[j][1] = a.y; kw[j][2] = a.z; kw[j][3] = a.w;
+        vw[j][0] = b.x; vw[j][1] = b.y; vw[j][2] = b.z; vw[j][3] = b.w;
+        // key extremes: this token's values, reduced over the record's 16 tokens below
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            *(uint32_t*)&sm.kmn[j][ts][8 * cg + 2 * i] = kw[j][i];
+            *(uint32_t*)&sm.kmx[j][ts][8 * cg + 2 * i] = kw[j][i];
+        }
+    }
+
+    // Value statistics and codes: per token over its 128 channels.
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t m2 = pk_min(pk_min(vw[j][0], vw[j][1]), pk_min(vw[j][2], vw[j][3]));
+        const uint32_t x2 = pk_max(pk_max(vw[j][0], vw[j][1]), pk_max(vw[j][2], vw[j][3]));
+        const float mn = row16<false>(fminf(h2f(m2 & 0xffffu), h2f(m2 >> 16)));
+        const float mx = row16<true>(fmaxf(h2f(x2 & 0xffffu), h2f(x2 >> 16)));
+        const QParams p = make_qparams(mn, mx, VB);
+        if (cg == 0 && recs[j]) {
+            const int pos = vmeta_pos(L, ts);
+            *(uint16_t*)(recs[j] + pos) = p.s_bits;
+            *(uint16_t*)(recs[j] + pos + 2 * L.spt) = p.z_bits;
+        }
+        const float nz = -p.z, qv = (float)((1 << VB) - 1);
+        uint32_t v0 = 0, v1 = 0;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            v0 = code_byte<0>(vw[j][i], nz, p.inv, qv, 2 * i, v0);
+            v0 = code_byte<1>(vw[j][i], nz, p.inv, qv, 2 * i + 1, v0);
+            v1 = code_byte<0>(vw[j][i + 2], nz, p.inv, qv, 2 * i, v1);
+            v1 = code_byte<1>(vw[j][i + 2], nz, p.inv, qv, 2 * i + 1, v1);
+        }
+        *(uint2*)&sm.vcode[ts + 16 * j][8 * cg] = make_uint2(v0, v1);
+    }
+    __syncthreads();
+    {
+        // channel ch of record j: all four waves, one (record, channel) each
+        const int j = tid >> 7, ch = tid & (kD - 1);
+        // (reduced in fp32 in the single-record order: the same extremes)
+        float mn = h2f(sm.kmn[j][0][ch]), mx = h2f(sm.kmx[j][0][ch]);
+        for (int r = 1; r < 16; ++r) {
+            mn = fminf(mn, h2f(sm.kmn[j][r][ch]));
+            mx = fmaxf(mx, h2f(sm.kmx[j][r][ch]));
+        }
+        const QParams p = make_qparams(mn, mx, KB);
+        sm.kz[j][ch] = -p.z;   // (negated: the fma's addend)
+        sm.kinv[j][ch] = p.inv;
+        if (recs[j]) {
+            *(uint16_t*)(recs[j] + L.kmeta_off + 2 * ch) = p.s_bits;
+            *(uint16_t*)(recs[j] + L.kmeta_off + 2 * kD + 2 * ch) = p.z_bits;
+        }
+    }
+    __syncthreads();
+
+    // Key codes: channels 8cg .. 8cg+7 of token ts of each record.
+    const float qk = (float)((1 << KB) - 1);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        float nzr[8], kir[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            nzr[e] = sm.kz[j][8 * cg + e];
+            kir[e] = sm.kinv[j][8 * cg + e];
+        }
+        if (KB == 4) {
+            uint32_t a = 0, b = 0;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                a = code_byte<0>(kw[j][i], nzr[2 * i], kir[2 * i], qk, 2 * i, a);
+                a = code_byte<1>(kw[j][i], nzr[2 * i + 1], kir[2 * i + 1], qk, 2 * i + 1, a);
+                b = code_byte<0>(kw[j][i + 2], nzr[2 * i + 4], kir[2 * i + 4], qk, 2 * i, b);
+                b = code_byte<1>(kw[j][i + 2], nzr[2 * i + 5], kir[2 * i + 5], qk, 2 * i + 1, b);
+            }
+            if (recs[j]) *(uint32_t*)(recs[j] + ts * 64 + 4 * cg) = a | (b << 4);
+        } else {
+            uint32_t ev = 0, od = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ev = code_byte<0>(kw[j][i], nzr[2 * i], kir[2 * i], qk, i, ev);
+                od = code_byte<1>(kw[j][i], nzr[2 * i + 1], kir[2 * i + 1], qk, i, od);
+            }
+            uint32_t w = (ev | (od << 4)) << (2 * (cg & 1));
+            w |= __shfl_xor(w, 1);
+            if ((cg & 1) == 0 && recs[j]) *(uint32_t*)(recs[j] + ts * 32 + 2 * cg) = w;
+        }
+    }
+
+    // Value code words of each record, lane-major in decode-operand order
+    // (the codes of LDS rows 16j .. 16j+15).
+    constexpr int SPT = 4;
+    constexpr int WPL = SPT * VB / 4;        // words per lane
+    constexpr int CPW = 32 / VB;             // codes per word
+    for (int D = tid; D < 2 * 64 * WPL; D += 256) {
+        const int j = D / (64 * WPL), Dj = D % (64 * WPL);
+        const int lane = Dj / WPL, wi = Dj % WPL;
+        const int g = lane >> 4, n = lane & 15;
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < CPW; ++e) {
+            const int q = wi * CPW + e;
+            const int ct = q / SPT, slot = q % SPT;
+            const int t = 4 * g + slot;
+            w |= (uint32_t)sm.vcode[16 * j + t][16 * ct + n] << code_bit(VB, e);
+        }
+        if (recs[j]) *(uint32_t*)(recs[j] + L.vcode_off + lane * SPT * VB + 4 * wi) = w;
+    }
+    __syncthreads();  // LDS may be reused by the caller
+}
+
 // The same for the 8-bit formats ("KV cache compression: ...", section 3.1):
 // every key and value token on its own.  F = kFmtInt8: the min/max grid with
 // 8 bits over the token's 128 channels (the 16 threads of a row reduce it);
@@ -601,6 +740,26 @@ __global__ __launch_bounds__(256) void prefill_groups_kernel(Layout L, kvq_cache
     if (!rec) return;
     const long base = ((long)sh * max_len + (long)g * G) * kD;
     quantize_any<G, KB, VB, F>(sm, L, c, h, k + base, v + base, rec);
+}
+
+// Uniform grid, G = 16: grid (ceil(max_len / 32), B*H); one workgroup per two
+// consecutive groups of a stream.
+template <int KB, int VB>
+__global__ __launch_bounds__(256) void prefill_pairs16_kernel(Layout L, kvq_cache c, const half_t* k,
+                                                              const half_t* v, int max_len,
+                                                              const int32_t* seq_lens) {
+    __shared__ QuantSmemPair sm;
+    const int g = 2 * blockIdx.x;
+    const int sh = blockIdx.y;
+    const int b = sh / L.H, h = sh % L.H;
+    const int n = clamped_len(L, seq_lens, b, max_len);
+    const int nq = num_quantized(n, 16, L.R);
+    if (g * 16 >= nq) return;
+    uint8_t* rec0 = record_at(L, c.packed, c.block_table, b, h, g);
+    uint8_t* rec1 = (g + 1) * 16 < nq ? record_at(L, c.packed, c.block_table, b, h, g + 1) : nullptr;
+    if (!rec0 && !rec1) return;
+    const long base = ((long)sh * max_len + (long)g * 16) * kD;
+    quantize_pair16<KB, VB>(sm, L, k + base, v + base, rec0, rec1);
 }
 
 // Residual copy and counters: grid (B*H), 256 threads.
@@ -831,7 +990,21 @@ __global__ void export_outliers_kernel(Layout L, kvq_cache c, uint16_t* pos, uin
 hipError_t launch_prefill(const Layout& L, const kvq_cache& c, const half_t* k, const half_t* v,
                           int max_len, const int32_t* seq_lens, hipStream_t s) {
     const int ngroups = (max_len + L.G - 1) / L.G;
-    if (ngroups > 0) {
+    if (ngroups > 0 && L.G == 16 && quant_variant(L) == kQUniform) {
+        dim3 grid((ngroups + 1) / 2, L.B * L.H);
+#define KVQ_PP(KB, VB)                                                                                      \
+    hipLaunchKernelGGL((prefill_pairs16_kernel<KB, VB>), grid, dim3(256), 0, s, L, c, k, v, max_len, seq_lens)
+        switch (L.kbits * 10 + L.vbits) {
+            case 22: KVQ_PP(2, 2); break;
+            case 24: KVQ_PP(2, 4); break;
+            case 42: KVQ_PP(4, 2); break;
+            case 44: KVQ_PP(4, 4); break;
+            default: return hipErrorInvalidValue;
+        }
+#undef KVQ_PP
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    } else if (ngroups > 0) {
         dim3 grid(ngroups, L.B * L.H);
 #define KVQ_PF(GG, KB, VB, FF)                                                                               \
     hipLaunchKernelGGL((prefill_groups_kernel<GG, KB, VB, FF>), grid, dim3(256), 0, s, L, c, k, v, max_len, \
