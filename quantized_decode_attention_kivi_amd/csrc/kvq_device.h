@@ -125,7 +125,7 @@ __device__ __forceinline__ void vcode_pos(const Layout& L, int t, int c, int* by
     const int cpw = 32 / L.vbits;
     const int lane = 16 * g + (c & 15);
     const int q = (c >> 4) * L.spt + slot;
-    *byte = L.vcode_off + lane * L.spt * L.vbits + 4 * (q / cpw);
+    *byte = L.vcode_off + vlane_byte(L.spt * L.vbits, lane, 4 * (q / cpw));
     *bit = code_bit(L.vbits, q % cpw);
 }
 

@@ -13,11 +13,16 @@
 //                         a token the 32 channels 32g..32g+31 of lane group g
 //                         occupy 4*kb bytes at offset 4*kb*g, in code order
 //                         q = channel - 32g packed by code_bit().
-//   [vcode_off, +vcode)   value codes, lane-major: lane l = 16g + n owns SPT*vb
-//                         bytes at offset l*SPT*vb holding, in code order
-//                         q = ct*SPT + slot (ct = 0..7, slot = 0..SPT-1), the
-//                         code of channel 16*ct + n for the token of that slot
-//                         (vslot()).  SPT = 8 for G = 32, 4 for G = 16.
+//   [vcode_off, +vcode)   value codes: lane l = 16g + n owns SPT*vb bytes
+//                         holding, in code order q = ct*SPT + slot (ct = 0..7,
+//                         slot = 0..SPT-1), the code of channel 16*ct + n for
+//                         the token of that slot (vslot()).  SPT = 8 for
+//                         G = 32, 4 for G = 16.  Lanes of at most 32 bytes are
+//                         contiguous (offset l*SPT*vb); the 64-byte lanes of
+//                         the 8-bit formats at G = 32 are cut into 16-byte
+//                         chunks, chunk k of lane l at 1024*k + 16*l
+//                         (vlane_byte()), so that each 16-byte load per lane
+//                         reads 1 KiB of whole cache lines.
 //   [kmeta_off, +512)     key scales s[128] then key zeros z[128], fp16,
 //                         channel order.
 //   [vmeta_off, +4G)      per lane group g: SPT value scales then SPT value
@@ -78,6 +83,11 @@ struct Layout {
 kvq_status make_layout(const kvq_config* cfg, Layout* L);
 
 // Largest n_q a sequence may reach.
+// Offset inside the value codes of byte b of lane `lane`'s lane_bytes bytes.
+__host__ __device__ inline int vlane_byte(int lane_bytes, int lane, int b) {
+    return lane_bytes <= 32 ? lane * lane_bytes + b : 1024 * (b >> 4) + 16 * lane + (b & 15);
+}
+
 __host__ __device__ inline int num_quantized(int n, int G, int R) {
     int over = n - R;
     return over <= 0 ? 0 : G * (over / G);

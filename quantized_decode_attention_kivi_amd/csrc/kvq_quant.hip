@@ -237,7 +237,9 @@ __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* 
     constexpr int WPL = SPT * VB / 4;        // words per lane
     constexpr int CPW = 32 / VB;             // codes per word
     for (int D = tid; D < 64 * WPL; D += 256) {
-        const int lane = D / WPL, wi = D % WPL;
+        // (lanes over 32 bytes: D runs chunk-major, so writes follow the layout)
+        const int lane = WPL > 8 ? (D >> 2) & 63 : D / WPL;
+        const int wi = WPL > 8 ? 4 * (D >> 8) + (D & 3) : D % WPL;
         const int g = lane >> 4, n = lane & 15;
         uint32_t w = 0;
 #pragma unroll
@@ -247,7 +249,7 @@ __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* 
             const int t = (slot >> 2) * 16 + 4 * g + (slot & 3);
             w |= (uint32_t)sm.vcode[t][16 * ct + n] << code_bit(VB, e);
         }
-        *(uint32_t*)(rec + L.vcode_off + lane * SPT * VB + 4 * wi) = w;
+        *(uint32_t*)(rec + L.vcode_off + vlane_byte(SPT * VB, lane, 4 * wi)) = w;
     }
     __syncthreads();  // LDS may be reused by the caller
 }
@@ -434,7 +436,9 @@ __device__ void quantize_group_uniform(QuantSmem<G>& sm, const Layout& L, const 
     constexpr int WPL = SPT * VB / 4;        // words per lane
     constexpr int CPW = 32 / VB;             // codes per word
     for (int D = tid; D < 64 * WPL; D += 256) {
-        const int lane = D / WPL, wi = D % WPL;
+        // (lanes over 32 bytes: D runs chunk-major, so writes follow the layout)
+        const int lane = WPL > 8 ? (D >> 2) & 63 : D / WPL;
+        const int wi = WPL > 8 ? 4 * (D >> 8) + (D & 3) : D % WPL;
         const int g = lane >> 4, n = lane & 15;
         uint32_t w = 0;
 #pragma unroll
@@ -444,7 +448,7 @@ __device__ void quantize_group_uniform(QuantSmem<G>& sm, const Layout& L, const 
             const int t = (slot >> 2) * 16 + 4 * g + (slot & 3);
             w |= (uint32_t)sm.vcode[t][16 * ct + n] << code_bit(VB, e);
         }
-        *(uint32_t*)(rec + L.vcode_off + lane * SPT * VB + 4 * wi) = w;
+        *(uint32_t*)(rec + L.vcode_off + vlane_byte(SPT * VB, lane, 4 * wi)) = w;
     }
     __syncthreads();  // LDS may be reused by the caller
 }
@@ -583,7 +587,7 @@ __device__ void quantize_pair16(QuantSmemPair& sm, const Layout& L, const half_t
             const int t = 4 * g + slot;
             w |= (uint32_t)sm.vcode[16 * j + t][16 * ct + n] << code_bit(VB, e);
         }
-        if (recs[j]) *(uint32_t*)(recs[j] + L.vcode_off + lane * SPT * VB + 4 * wi) = w;
+        if (recs[j]) *(uint32_t*)(recs[j] + L.vcode_off + vlane_byte(SPT * VB, lane, 4 * wi)) = w;
     }
     __syncthreads();  // LDS may be reused by the caller
 }
@@ -669,7 +673,9 @@ __device__ void quantize_group8(QuantSmem<G>& sm, const Layout& L, const half_t*
     // of its SPT*8 bytes, the code of channel 16ct + n for the slot's token.
     constexpr int WPL = SPT * 2;   // words per lane
     for (int D = tid; D < 64 * WPL; D += 256) {
-        const int lane = D / WPL, wi = D % WPL;
+        // (lanes over 32 bytes: D runs chunk-major, so writes follow the layout)
+        const int lane = WPL > 8 ? (D >> 2) & 63 : D / WPL;
+        const int wi = WPL > 8 ? 4 * (D >> 8) + (D & 3) : D % WPL;
         const int g = lane >> 4, n = lane & 15;
         uint32_t w = 0;
 #pragma unroll
@@ -679,7 +685,7 @@ __device__ void quantize_group8(QuantSmem<G>& sm, const Layout& L, const half_t*
             const int t = (slot >> 2) * 16 + 4 * g + (slot & 3);
             w |= (uint32_t)sm.vcode[t][16 * ct + n] << (8 * e);
         }
-        *(uint32_t*)(rec + L.vcode_off + lane * SPT * 8 + 4 * wi) = w;
+        *(uint32_t*)(rec + L.vcode_off + vlane_byte(SPT * 8, lane, 4 * wi)) = w;
     }
     __syncthreads();  // LDS may be reused by the caller
 }
