@@ -225,19 +225,15 @@ __device__ __forceinline__ u32x4 record_desc(const uint8_t* rec, int bytes) {
 // Issued from inline assembly so that the compiler inserts no waits of its
 // own for the LDS write (it cannot tell the two stage buffers apart and would
 // drain the prefetch); the kernel waits explicitly before reading a buffer.
-// NT: the load carries the non-temporal policy (nt), for data read once per
-// call (the codes, tables and residual rows: 7-12 % faster on the INT4 and
-// paged layers).  The 8-bit key loads read each 128-byte token row as 16-byte
-// pieces at a 32-byte lane stride, and keep the default policy: with it on
-// them, and on 8-bit values read at a 64-byte lane stride, the INT8 layer ran
-// 106 -> 145 us.
-template <bool NT>
+// The load carries the non-temporal policy (nt): the cache is read once per
+// call (7-12 % faster on the INT4 and paged layers).  Loads that read a line
+// in pieces spread over several instructions lose with it (8-bit codes read
+// at a 32- or 64-byte lane stride: INT8 layer 106 -> 145 us), which is why
+// the 8-bit records store their codes in 16-byte pieces, so that every load
+// here reads whole lines.
 __device__ __forceinline__ void lds_load16(u32x4 desc, lds_u8* dst, int off) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
-    if constexpr (NT)
-        asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(off), "s"(desc), "{m0}"(m0) : "memory");
-    else
-        asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(desc), "{m0}"(m0) : "memory");
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(off), "s"(desc), "{m0}"(m0) : "memory");
 }
 
 // Issues the direct-to-LDS loads of one unit into stage buffer `buf` (wave
@@ -263,31 +259,31 @@ __device__ __forceinline__ uint32_t issue_unit(lds_u8* buf, const Layout& L, con
         const u32x4 rs = record_desc(rec, L.record);
         if (G == 32) {
             if (KB == 4) {
-                lds_load16<true>(rs, buf + S::KC, n * 64 + 16 * g);
-                lds_load16<true>(rs, buf + S::KC + 1024, (16 + n) * 64 + 16 * g);
+                lds_load16(rs, buf + S::KC, n * 64 + 16 * g);
+                lds_load16(rs, buf + S::KC + 1024, (16 + n) * 64 + 16 * g);
             } else {
                 // slot l = rt*32 + gh*16 + n  <-  token 16rt + n, lane groups 2gh, 2gh+1
                 const int rt = lane >> 5, gh = (lane >> 4) & 1;
-                lds_load16<true>(rs, buf + S::KC, (16 * rt + n) * 32 + 16 * gh);
+                lds_load16(rs, buf + S::KC, (16 * rt + n) * 32 + 16 * gh);
             }
-            lds_load16<true>(rs, buf + S::VC, L.vcode_off + S::VW * 4 * lane);
-            if (VB == 4) lds_load16<true>(rs, buf + S::VC + 1024, L.vcode_off + S::VW * 4 * lane + 16);
+            lds_load16(rs, buf + S::VC, L.vcode_off + S::VW * 4 * lane);
+            if (VB == 4) lds_load16(rs, buf + S::VC + 1024, L.vcode_off + S::VW * 4 * lane + 16);
         } else {
             if (KB == 4) {
-                lds_load16<true>(rs, buf + S::KC + i * 1024, n * 64 + 16 * g);
+                lds_load16(rs, buf + S::KC + i * 1024, n * 64 + 16 * g);
             } else if (lane < 32) {
                 const int gh = lane >> 4;
-                lds_load16<true>(rs, buf + S::KC + i * 512, n * 32 + 16 * gh);
+                lds_load16(rs, buf + S::KC + i * 512, n * 32 + 16 * gh);
             }
             if (VB == 4) {
-                lds_load16<true>(rs, buf + S::VC + i * 1024, L.vcode_off + 16 * lane);
+                lds_load16(rs, buf + S::VC + i * 1024, L.vcode_off + 16 * lane);
             } else if (lane < 32) {
-                lds_load16<true>(rs, buf + S::VC + i * 512, L.vcode_off + 16 * lane);
+                lds_load16(rs, buf + S::VC + i * 512, L.vcode_off + 16 * lane);
             }
         }
         // key table, value table (and kept keys): contiguous in the record
         if (lane < 32 + (SP ? G / 2 : G / 4))
-            lds_load16<true>(rs, buf + S::META + i * S::MREC,
+            lds_load16(rs, buf + S::META + i * S::MREC,
                        lane < 32 ? L.kmeta_off + 16 * lane : L.vmeta_off + 16 * (lane - 32));
     }
     return has;
@@ -320,7 +316,6 @@ template <int G, int F, bool PG>
 __device__ __forceinline__ uint32_t issue_unit8(lds_u8* buf, const Layout& L, const kvq_cache& c, int b, int h,
                                                 int unit, int ngroups, int lane) {
     using S = Stage8<G, F>;
-    const int g = lane >> 4, n = lane & 15;
     uint32_t base = (uint32_t)(uintptr_t)buf;
     asm volatile("" : "+s"(base));
     buf = (lds_u8*)(uintptr_t)base;
@@ -334,17 +329,17 @@ __device__ __forceinline__ uint32_t issue_unit8(lds_u8* buf, const Layout& L, co
         if (G == 32) {
 #pragma unroll
             for (int k = 0; k < 4; ++k)   // k = 2rt + half
-                lds_load16<false>(rs, buf + S::KC + 1024 * k, kD * (16 * (k >> 1) + n) + 32 * g + 16 * (k & 1));
+                lds_load16(rs, buf + S::KC + 1024 * k, 1024 * k + 16 * lane);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) lds_load16<true>(rs, buf + S::VC + 1024 * k, L.vcode_off + 1024 * k + 16 * lane);
+            for (int k = 0; k < 4; ++k) lds_load16(rs, buf + S::VC + 1024 * k, L.vcode_off + 1024 * k + 16 * lane);
         } else {
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                lds_load16<false>(rs, buf + S::KC + 1024 * (2 * i + hf), kD * n + 32 * g + 16 * hf);
-                lds_load16<true>(rs, buf + S::VC + 1024 * (2 * i + hf), L.vcode_off + 32 * lane + 16 * hf);
+                lds_load16(rs, buf + S::KC + 1024 * (2 * i + hf), 1024 * hf + 16 * lane);
+                lds_load16(rs, buf + S::VC + 1024 * (2 * i + hf), L.vcode_off + 32 * lane + 16 * hf);
             }
         }
-        if (F == kFmtInt8 && lane < G / 2) lds_load16<false>(rs, buf + S::META + i * S::MREC, L.kmeta_off + 16 * lane);
+        if (F == kFmtInt8 && lane < G / 2) lds_load16(rs, buf + S::META + i * S::MREC, L.kmeta_off + 16 * lane);
     }
     return has;
 }
@@ -996,7 +991,7 @@ __device__ __forceinline__ void process_residual(WaveAcc& A, const Layout& L, co
         for (int i = 0; i < 8; ++i) {
             const int r = 4 * i + (lane >> 4);
             const int off = t0 + r < n ? ring_slot(slot0, r, L.ring) * (kD * 2) + 16 * n16 : 0x40000000;
-            lds_load16<true>(vd, i < 4 ? sva + 1024 * i : svb + 1024 * (i - 4), off);
+            lds_load16(vd, i < 4 ? sva + 1024 * i : svb + 1024 * (i - 4), off);
         }
     }
     const half_t* kr = (const half_t*)c.k_res + sh * L.ring * kD;

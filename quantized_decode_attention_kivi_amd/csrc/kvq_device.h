@@ -112,6 +112,11 @@ __device__ __forceinline__ float cb_level(const uint32_t (&lut)[4], uint32_t c, 
 
 // Byte offset and bit of key code (token t, channel c).
 __device__ __forceinline__ void kcode_pos(const Layout& L, int t, int c, int* byte, int* bit) {
+    if (L.kbits == 8) {   // (channels 4j .. 4j+3 of a token are one word)
+        *byte = k8_byte(t, c & ~3);
+        *bit = 8 * (c & 3);
+        return;
+    }
     const int cpw = 32 / L.kbits;           // codes per word
     const int q = c & 31;
     *byte = t * 16 * L.kbits + 4 * L.kbits * (c >> 5) + 4 * (q / cpw);

@@ -35,8 +35,12 @@
 // nibbles, so the decode kernel unpacks a word straight into operand order.
 //
 // 8-bit formats (INT8, FP8 E4M3) keep the same sections with one byte per
-// code (code_bit(8, q) = 8q, so key bytes are in channel order and a lane's
-// value bytes in code order); their key scale/zero table is per token, laid
+// code (code_bit(8, q) = 8q, so a lane's value bytes are in code order).
+// Their key bytes are stored in 16-byte pieces, the piece of token t holding
+// channels 16h .. 16h+15 (h = c/16) at 1024*(2*(t/16) + h%2) + 16*(16*(h/2) +
+// t%16) (k8_byte()): piece k of lane l = 16g + n at 1024*k + 16*l is the
+// lane's 16-byte key operand for token 16*(k/2) + n, channels 32g + 16*(k%2),
+// so that each 16-byte load per lane reads 1 KiB of whole cache lines; their key scale/zero table is per token, laid
 // out like the value table (kmeta_off, 4G bytes, INT8 only), and FP8 records
 // carry no tables at all (its scales are per kv head, outside the records).
 //
@@ -83,6 +87,12 @@ struct Layout {
 kvq_status make_layout(const kvq_config* cfg, Layout* L);
 
 // Largest n_q a sequence may reach.
+// Offset inside the key codes of the 8-bit formats of the byte of token t,
+// channel c.
+__host__ __device__ inline int k8_byte(int t, int c) {
+    return 1024 * (2 * (t >> 4) + ((c >> 4) & 1)) + 16 * (16 * (c >> 5) + (t & 15)) + (c & 15);
+}
+
 // Offset inside the value codes of byte b of lane `lane`'s lane_bytes bytes.
 __host__ __device__ inline int vlane_byte(int lane_bytes, int lane, int b) {
     return lane_bytes <= 32 ? lane * lane_bytes + b : 1024 * (b >> 4) + 16 * lane + (b & 15);

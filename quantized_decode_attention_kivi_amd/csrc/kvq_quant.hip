@@ -664,7 +664,7 @@ __device__ void quantize_group8(QuantSmem<G>& sm, const Layout& L, const half_t*
                 vw[h] = fp8_code2(vx[4 * h], vx[4 * h + 1], vinv) | fp8_code2(vx[4 * h + 2], vx[4 * h + 3], vinv) << 16;
             }
         }
-        *(uint2*)(rec + t * kD + 8 * cg) = make_uint2(kw[0], kw[1]);
+        *(uint2*)(rec + k8_byte(t, 8 * cg)) = make_uint2(kw[0], kw[1]);
         *(uint2*)&sm.vcode[t][8 * cg] = make_uint2(vw[0], vw[1]);
     }
     __syncthreads();
