@@ -244,10 +244,12 @@ void orc_dequantize_stream(const uint16_t *k, const uint16_t *v, int n, int nq, 
 /* Scaled dot-product attention of gq query rows against n key/value rows,
  * accumulated in fp64 ([P4]: softmax(q k^T / sqrt(d_h)) weighting v; the
  * softmax subtracts the row maximum before exponentiating, which leaves its
- * value unchanged).  q: [gq][d]; kh, vh: [n][d]; out: [gq][d];
- * weights (optional, may be NULL): [gq][n].  n == 0 gives out = 0. */
-void orc_attention(const float *q, int gq, const float *kh, const float *vh, int n, int d,
-                   float scale, double *out, double *weights)
+ * value unchanged).  One function serves fp32 keys (kf) and fp64 keys (kd,
+ * e.g. keys rotated by orc_rope_rotate): exactly one of the two is non-NULL.
+ * q: [gq][d]; keys, vh: [n][d]; out: [gq][d]; weights (optional, may be
+ * NULL): [gq][n].  n == 0 gives out = 0. */
+static void attention_core(const float *q, int gq, const float *kf, const double *kd, const float *vh,
+                           int n, int d, float scale, double *out, double *weights)
 {
     double *logit = (double *)malloc(sizeof(double) * (n > 0 ? n : 1));
     for (int h = 0; h < gq; ++h) {
@@ -257,8 +259,10 @@ void orc_attention(const float *q, int gq, const float *kh, const float *vh, int
         double m = -INFINITY;
         for (int t = 0; t < n; ++t) {
             double acc = 0.0;
-            for (int c = 0; c < d; ++c)
-                acc += (double)q[(long)h * d + c] * (double)kh[(long)t * d + c];
+            for (int c = 0; c < d; ++c) {
+                long i = (long)t * d + c;
+                acc += (double)q[(long)h * d + c] * (kf ? (double)kf[i] : kd[i]);
+            }
             logit[t] = (double)scale * acc;
             if (logit[t] > m) m = logit[t];
         }
@@ -274,6 +278,13 @@ void orc_attention(const float *q, int gq, const float *kh, const float *vh, int
         }
     }
     free(logit);
+}
+
+/* Attention over fp32 keys (the dequantized cache). */
+void orc_attention(const float *q, int gq, const float *kh, const float *vh, int n, int d,
+                   float scale, double *out, double *weights)
+{
+    attention_core(q, gq, kh, NULL, vh, n, d, scale, out, weights);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -822,34 +833,12 @@ void orc_rope_rotate(const float *k, int n, int d, long pos0, double base, doubl
     }
 }
 
-/* orc_attention with fp64 keys (e.g. keys rotated by orc_rope_rotate). */
+/* Attention over fp64 keys (e.g. keys rotated by orc_rope_rotate): the same
+ * function as orc_attention, reading the keys in fp64. */
 void orc_attention_d(const float *q, int gq, const double *kh, const float *vh, int n, int d,
                      float scale, double *out)
 {
-    double *logit = (double *)malloc(sizeof(double) * (n > 0 ? n : 1));
-    for (int h = 0; h < gq; ++h) {
-        double *o = out + (long)h * d;
-        for (int c = 0; c < d; ++c) o[c] = 0.0;
-        if (n == 0) continue;
-        double m = -INFINITY;
-        for (int t = 0; t < n; ++t) {
-            double acc = 0.0;
-            for (int c = 0; c < d; ++c)
-                acc += (double)q[(long)h * d + c] * kh[(long)t * d + c];
-            logit[t] = (double)scale * acc;
-            if (logit[t] > m) m = logit[t];
-        }
-        double l = 0.0;
-        for (int t = 0; t < n; ++t) {
-            logit[t] = exp(logit[t] - m);
-            l += logit[t];
-        }
-        for (int t = 0; t < n; ++t) {
-            double p = logit[t] / l;
-            for (int c = 0; c < d; ++c) o[c] += p * (double)vh[(long)t * d + c];
-        }
-    }
-    free(logit);
+    attention_core(q, gq, NULL, kh, vh, n, d, scale, out, NULL);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -701,6 +701,69 @@ def test_attention_rope_matches_rotated_keys(orc):
     assert np.allclose(got, p @ v.astype(np.float64), rtol=0, atol=1e-12)
 
 
+def test_attention_rope_single_token_constant_values_and_empty(orc):
+    """Pre-RoPE attention, cases fixed whatever the rotation does: one token
+    gives its value row; equal value rows give that row; no tokens give 0."""
+    rng = np.random.default_rng(94)
+    q = rng.standard_normal((3, 128)).astype(np.float32)
+    k = (rng.standard_normal((1, 128)) * 5).astype(np.float32)
+    v = rng.standard_normal((1, 128)).astype(np.float32)
+    assert np.array_equal(orc.attention_rope(q, k, v, 0.3, 10000.0), np.repeat(v.astype(np.float64), 3, axis=0))
+    k = (rng.standard_normal((90, 128)) * 5).astype(np.float32)
+    c = rng.standard_normal((1, 128)).astype(np.float32)
+    out = orc.attention_rope(q, k, np.repeat(c, 90, axis=0), 128 ** -0.5, 500000.0)
+    assert np.allclose(out, np.repeat(c.astype(np.float64), 3, axis=0), atol=1e-6, rtol=0)
+    e = np.zeros((0, 128), np.float32)
+    assert np.all(orc.attention_rope(q, e, e, 0.3, 10000.0) == 0)
+
+
+def test_attention_rope_zero_and_counter_rotated_keys_give_the_mean(orc):
+    """All rotated keys equal -> equal logits -> the mean value row.  Zero
+    keys stay zero under any rotation; keys built as one vector turned back
+    by their own position's angles (complex multiplication by
+    exp(-i t theta_j)) come out of the rotation as that vector again."""
+    rng = np.random.default_rng(95)
+    n, base = 200, 10000.0
+    q = (rng.standard_normal((2, 128)) * 3).astype(np.float32)
+    v = rng.standard_normal((n, 128)).astype(np.float32)
+    mean = np.repeat(v.astype(np.float64).mean(axis=0, keepdims=True), 2, axis=0)
+    out = orc.attention_rope(q, np.zeros((n, 128), np.float32), v, 128 ** -0.5, base)
+    assert np.allclose(out, mean, atol=1e-12, rtol=0)
+    c = rng.standard_normal(128)
+    z = c[0::2] + 1j * c[1::2]
+    freq = np.power(base, -np.arange(64) / 64.0)
+    back = z[None, :] * np.exp(-1j * np.arange(n)[:, None] * freq[None, :])
+    k = np.empty((n, 128))
+    k[:, 0::2], k[:, 1::2] = back.real, back.imag
+    out = orc.attention_rope(q, k.astype(np.float32), v, 128 ** -0.5, base)
+    assert np.allclose(out, mean, atol=1e-5, rtol=0)
+    # the plain attention over the same (unrotated) keys is not the mean
+    assert np.abs(orc.attention(q, k.astype(np.float32), v, 128 ** -0.5) - mean).max() > 1e-2
+
+
+def test_attention_rope_two_tokens_logistic(orc):
+    """Two tokens at positions 0 and 1, keys on one channel pair: token 0 is
+    not rotated, token 1's pair i turns by theta_i = base^(-i/64) radians.
+    The weight of token 0 is the logistic function of the logit difference
+    worked out by hand for each pair and channel."""
+    scale = 0.5
+    for base in (10000.0, 500000.0):
+        for i in (0, 5, 63):
+            th = base ** (-i / 64.0)
+            for ch, a, b in ((2 * i, 3.0, 2.0), (2 * i + 1, -1.0, 4.0)):
+                q = np.zeros((1, 128), np.float32)
+                q[0, ch] = 1.0
+                k = np.zeros((2, 128), np.float32)
+                k[0, 2 * i], k[1, 2 * i] = a, b          # both keys on the pair's first channel
+                v = _rand((2, 128), 96 + i)
+                # rotated token 1: (b cos th, b sin th) on channels (2i, 2i+1)
+                l0 = a if ch == 2 * i else 0.0
+                l1 = b * np.cos(th) if ch == 2 * i else b * np.sin(th)
+                w0 = 1.0 / (1.0 + np.exp(-scale * (l0 - l1)))
+                out = orc.attention_rope(q, k, v, scale, base)
+                assert np.allclose(out[0], w0 * v[0] + (1 - w0) * v[1], atol=1e-12, rtol=0), (base, i, ch)
+
+
 def test_pre_rope_quantization_narrows_key_ranges(orc):
     """Section 3.3's reason for quantizing before RoPE: on keys whose outlier
     channels are consistently large (the "bright vertical lines" of
@@ -1002,6 +1065,10 @@ MUTATIONS = [
     ("if (*n - *nq == R + G)", "if (*n - *nq == R)", "append"),         # wrong flush condition
     ("logit[t] = exp(logit[t] - m);", "logit[t] = exp(logit[t]);", None),  # still exact (no overflow here)
     ("p = logit[t] / l;", "p = logit[t];", "attn"),                     # dropped normalisation
+    ("p = logit[t] / l;", "p = logit[t];", "attnrope"),                 # the same, seen by the pre-RoPE pins
+    ("(kf ? (double)kf[i] : kd[i])", "(kf ? (double)kf[i] : 0.5 * kd[i])", "attnrope"),  # fp64 keys misread
+    ("logit[t] = (double)scale * acc;", "logit[t] = acc;", "attnrope"),   # softmax scale dropped
+    ("logit[t] = (double)scale * acc;", "logit[t] = acc;", "attn2"),      # the same, plain attention
     ("mn = mn + 0.0f;", "mn = mn;", "negzero"),                        # -0 not canonicalised
     ("double m = rint(ldexp(a, 3 - e));", "double m = floor(ldexp(a, 3 - e) + 0.5);", "fp8enc"),  # ties away
     ("v = ldexp((double)(frac + 8), expo - 10);", "v = ldexp((double)(frac + 8), expo - 9);", "fp8dec"),
@@ -1039,6 +1106,8 @@ def test_pin_catches_planted_mistakes(tmp_path):
         "dequant": "test_dequantize_grid_aligned_multi_group_exact",
         "append": "test_prefill_equals_prefill_plus_appends",
         "attn": "test_attention_weights_sum_to_one",
+        "attn2": "test_attention_two_tokens_logistic",
+        "attnrope": "attention_rope",
         "negzero": "test_negative_zero_extremes_canonicalised",
         "fp8enc": "test_fp8_encode_matches_torch",
         "fp8dec": "test_fp8_decode_every_code",
