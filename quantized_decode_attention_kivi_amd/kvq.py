@@ -298,6 +298,39 @@ class QuantizedKVCache:
         v._ws = None
         return v
 
+    def stream_view(self, b: int, h: int) -> "QuantizedKVCache":
+        """Read-only cache of stream (sequence b, kv head h) alone, sharing
+        this cache's memory (contiguous mode).  In a contiguous cache the
+        records of one (sequence, kv head) are consecutive and so is its
+        residual ring, so the stream is itself a valid cache of one sequence
+        and one kv head; its counters are the sequence's."""
+        if self.shape.paged:
+            raise ValueError("stream_view: contiguous caches only")
+        if not (0 <= b < self.shape.num_seqs and 0 <= h < self.shape.num_kv_heads):
+            raise IndexError((b, h))
+        v = object.__new__(QuantizedKVCache)
+        v.shape = replace(self.shape, num_seqs=1, num_kv_heads=1)
+        v.cfg = v.shape.config()
+        v.sizes = kvq_buffer_sizes(v.cfg)
+        v.device = self.device
+        v._parent = self
+        v._view = True
+        s = b * self.shape.num_kv_heads + h
+        per = v.sizes.packed_bytes
+        v.packed = self.packed[s * per:(s + 1) * per]
+        per_ring = v.sizes.residual_bytes // 2
+        v.k_res = self.k_res[s * per_ring:(s + 1) * per_ring]
+        v.v_res = self.v_res[s * per_ring:(s + 1) * per_ring]
+        v.n_tokens = self.n_tokens[b:b + 1]
+        v.n_quant = self.n_quant[b:b + 1]
+        v.block_table = None
+        v.lens = self.lens[b:b + 1].copy()
+        v.k_scale = self.k_scale[h:h + 1] if self.k_scale is not None else None
+        v.v_scale = self.v_scale[h:h + 1] if self.v_scale is not None else None
+        v.cache = v._make_cache()
+        v._ws = None
+        return v
+
     def _writable(self, what):
         if getattr(self, "_view", False):
             raise KVQError(KVQ_EINVAL, "%s on a read-only sequence view" % what)

@@ -54,6 +54,44 @@ def oracle_states(kb: np.ndarray, vb: np.ndarray, lens, w: synth.Workload, cap=N
                                 sparse=bool(w.sparse_keys))
 
 
+def _compare_exported(view, hix, states_of_heads, b):
+    """Exports view (a one-sequence cache) and compares its heads hix[i]
+    with states_of_heads[i]."""
+    G = view.G
+    T = int(view.lens.max()) + G     # a group past the end: must read back as zeros
+    fmt = view.shape.kv_format
+    kc, vc, ks, kz, vs, vz = [None if t is None else t[0].cpu().numpy() for t in view.export_codes(T)]
+    if fmt != kvq.FORMAT_FP8_E4M3:
+        ks, kz, vs, vz = (a.view(np.uint16) for a in (ks, kz, vs, vz))
+    kd, vd = [t[0].cpu().numpy() for t in view.dequantize(T)]
+    nt = int(view.n_tokens.cpu()[0])
+    nqs = int(view.n_quant.cpu()[0])
+    if view.shape.sparse_keys:
+        opos, oval = [t[0].cpu().numpy().view(np.uint16) for t in view.export_outliers(T)]
+    for h, st in zip(hix, states_of_heads):
+        assert nt == st.n and nqs == st.nq, (b, nt, st.n, nqs, st.nq)
+        nq, n = st.nq, st.n
+        assert np.array_equal(kc[h, :nq], st.key_codes()), ("key codes", b, h)
+        assert np.array_equal(vc[h, :nq], st.value_codes()), ("value codes", b, h)
+        if fmt != kvq.FORMAT_FP8_E4M3:
+            nk = nq // G if fmt == kvq.FORMAT_KIVI else nq   # per group or per token
+            oks, okz = st.key_meta()
+            assert np.array_equal(ks[h, :nk], oks), ("key scales", b, h)
+            assert np.array_equal(kz[h, :nk], okz), ("key zeros", b, h)
+            ovs, ovz = st.value_meta()
+            assert np.array_equal(vs[h, :nq], ovs), ("value scales", b, h)
+            assert np.array_equal(vz[h, :nq], ovz), ("value zeros", b, h)
+        if view.shape.sparse_keys:
+            sp, sv = st.outliers()
+            assert np.array_equal(opos[h, :nq // G], sp), ("kept key positions", b, h)
+            assert np.array_equal(oval[h, :nq // G], sv), ("kept key values", b, h)
+            assert not opos[h, nq // G:].any() and not oval[h, nq // G:].any()
+        okd, ovd = st.dequantize()
+        assert np.array_equal(kd[h, :n], okd), ("dequantized keys", b, h)
+        assert np.array_equal(vd[h, :n], ovd), ("dequantized values", b, h)
+        assert np.all(kd[h, n:] == 0) and np.all(vd[h, n:] == 0)
+
+
 def compare_codes(cache: kvq.QuantizedKVCache, states, streams=None):
     """Bit-exact comparison of codes, scales, zeros and dequantized values of
     the (b, h) streams (default: all), exported one sequence at a time through
@@ -64,42 +102,15 @@ def compare_codes(cache: kvq.QuantizedKVCache, states, streams=None):
     by_seq = {}
     for b, h in streams:
         by_seq.setdefault(b, []).append(h)
-    G = cache.G
     for b, heads in sorted(by_seq.items()):
-        view = cache.sequence_view(b)
-        T = int(view.lens.max()) + G     # a group past the end: must read back as zeros
-        fmt = cache.shape.kv_format
-        kc, vc, ks, kz, vs, vz = [None if t is None else t[0].cpu().numpy() for t in view.export_codes(T)]
-        if fmt != kvq.FORMAT_FP8_E4M3:
-            ks, kz, vs, vz = (a.view(np.uint16) for a in (ks, kz, vs, vz))
-        kd, vd = [t[0].cpu().numpy() for t in view.dequantize(T)]
-        nt = int(view.n_tokens.cpu()[0])
-        nqs = int(view.n_quant.cpu()[0])
-        if cache.shape.sparse_keys:
-            opos, oval = [t[0].cpu().numpy().view(np.uint16) for t in view.export_outliers(T)]
-        for h in heads:
-            st = states[b][h]
-            assert nt == st.n and nqs == st.nq, (b, nt, st.n, nqs, st.nq)
-            nq, n = st.nq, st.n
-            assert np.array_equal(kc[h, :nq], st.key_codes()), ("key codes", b, h)
-            assert np.array_equal(vc[h, :nq], st.value_codes()), ("value codes", b, h)
-            if fmt != kvq.FORMAT_FP8_E4M3:
-                nk = nq // G if fmt == kvq.FORMAT_KIVI else nq   # per group or per token
-                oks, okz = st.key_meta()
-                assert np.array_equal(ks[h, :nk], oks), ("key scales", b, h)
-                assert np.array_equal(kz[h, :nk], okz), ("key zeros", b, h)
-                ovs, ovz = st.value_meta()
-                assert np.array_equal(vs[h, :nq], ovs), ("value scales", b, h)
-                assert np.array_equal(vz[h, :nq], ovz), ("value zeros", b, h)
-            if cache.shape.sparse_keys:
-                sp, sv = st.outliers()
-                assert np.array_equal(opos[h, :nq // G], sp), ("kept key positions", b, h)
-                assert np.array_equal(oval[h, :nq // G], sv), ("kept key values", b, h)
-                assert not opos[h, nq // G:].any() and not oval[h, nq // G:].any()
-            okd, ovd = st.dequantize()
-            assert np.array_equal(kd[h, :n], okd), ("dequantized keys", b, h)
-            assert np.array_equal(vd[h, :n], ovd), ("dequantized values", b, h)
-            assert np.all(kd[h, n:] == 0) and np.all(vd[h, n:] == 0)
+        _compare_exported(cache.sequence_view(b), heads, [states[b][h] for h in heads], b)
+
+
+def compare_stream_codes(cache: kvq.QuantizedKVCache, b: int, h: int, st):
+    """compare_codes for one stream of a contiguous cache, exported through a
+    one-stream view (only that stream's bytes leave the device)."""
+    torch.cuda.synchronize()
+    _compare_exported(cache.stream_view(b, h), [0], [st], b)
 
 
 def oracle_attention(q16: np.ndarray, states, scale, rows=None, rope_base=0.0):

@@ -253,39 +253,53 @@ def test_full_size_paged_decode_steps():
     compare_attention(out.cpu().numpy(), oracle_attention(to_bits(q), states, SCALE))
 
 
+@pytest.mark.timeout(600)
 def test_full_size_80_layer_cache():
     """The 80-layer, 128K-token INT2 cache with the layers folded into the
-    batch (43 GB of fp16 input, 7 GB packed): sampled (layer, kv head) streams
-    are quantized by the oracle from the same input bits and must match bit
-    for bit; their query rows of one decode call must match the oracle."""
+    batch (43 GB of fp16 input, 7 GB packed), every stream: each layer's
+    input is pulled back and the oracle quantizes all of its 8 (layer, kv
+    head) streams from the same bits on the host thread pool; the 64 query
+    rows of every layer (5120 in all) must match the oracle's attention, and
+    kv head (layer mod 8) of every layer -- 80 streams, kv heads 0-7 ten times
+    each -- must match bit for bit in codes, scales, zeros and dequantized
+    values."""
+    from concurrent.futures import ThreadPoolExecutor
+    from parity_util import THREADS, compare_stream_codes
     w = synth.WORKLOADS["llama3_70b_cache_80l_128k_int2"]
     lens = synth.seq_lengths(w)
     L = int(lens.max())
-    print("generating %s (%d x %d x %d x 128 fp16, K and V)" % (w.name, w.num_seqs, w.num_kv_heads, L), flush=True)
+    B, H, gq = w.num_seqs, w.num_kv_heads, w.gq
+    print("generating %s (%d x %d x %d x 128 fp16, K and V)" % (w.name, B, H, L), flush=True)
     K, V = synth.make_kv(w, max_len=L, device="cuda")
     cache = make_cache(w, lens)
     cache.prefill(K, V, lens)
-    torch.cuda.synchronize()
-    samples = [(0, 0), (37, 5), (w.num_seqs - 1, w.num_kv_heads - 1)]
-    states = {}
-    for b, h in samples:
-        print("oracle prefill of stream", (b, h), flush=True)
-        states.setdefault(b, {})[h] = oracle.StreamState.prefill(to_bits(K[b, h]), to_bits(V[b, h]), w.k_bits,
-                                                                 w.v_bits, w.group_size, w.residual)
+    q = synth.make_query(w, device="cuda")
+    out = cache.decode_attention(q, SCALE).cpu().numpy()
+    qf = oracle.h2f(to_bits(q))
+    ref = np.empty(out.shape, np.float64)
+
+    def one(job):
+        b, h, kb, vb = job
+        st = oracle.StreamState.prefill(kb, vb, w.k_bits, w.v_bits, w.group_size, w.residual)
+        kh, vh = st.dequantize()
+        ref[b, h * gq:(h + 1) * gq] = oracle.attention(qf[b, h * gq:(h + 1) * gq], kh, vh, SCALE)
+        return st if h == b % H else None
+
+    per = max(1, THREADS // H)   # layers per round: one stream per pool thread
+    with ThreadPoolExecutor(THREADS) as ex:
+        for b0 in range(0, B, per):
+            bs = range(b0, min(b0 + per, B))
+            kb = to_bits(K[b0:bs[-1] + 1])
+            vb = to_bits(V[b0:bs[-1] + 1])
+            jobs = [(b, h, kb[b - b0, h, :lens[b]], vb[b - b0, h, :lens[b]]) for b in bs for h in range(H)]
+            for st, (b, h, _, _) in zip(ex.map(one, jobs), jobs):
+                if st is not None:
+                    compare_stream_codes(cache, b, h, st)
+            if b0 % 16 == 0:
+                print("layers %d-%d checked" % (b0, bs[-1]), flush=True)
     del K, V
     torch.cuda.empty_cache()
-    compare_codes(cache, states, streams=samples)
-    q = synth.make_query(w, device="cuda")
-    out = cache.decode_attention(q, SCALE)
-    torch.cuda.synchronize()
-    got, ref = [], []
-    qf = oracle.h2f(to_bits(q))
-    for b, h in samples:
-        kh, vh = states[b][h].dequantize()
-        hqs = list(range(h * w.gq, (h + 1) * w.gq))
-        ref.append(oracle.attention(qf[b, hqs], kh, vh, SCALE))
-        got.append(out[b, hqs].cpu().numpy())
-    compare_attention(np.concatenate(got), np.concatenate(ref))
+    compare_attention(out, ref)
     del cache
     torch.cuda.empty_cache()
 
