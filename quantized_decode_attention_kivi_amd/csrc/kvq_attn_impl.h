@@ -430,6 +430,99 @@ __device__ __forceinline__ float add_limb_partner(float x) {
     return x + __builtin_bit_cast(float, y);
 }
 
+// DPP rotation of a 32-bit value by 8 lanes within each 16-lane row: lane n
+// receives lane n ^ 8's value.  Every source lane exists, so the zero "old"
+// value with bound control is never used; it lets the compiler fold the move
+// into the instruction that consumes it.
+__device__ __forceinline__ uint32_t ror8(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128 /* row_ror:8 */, 0xf, 0xf, true);
+}
+__device__ __forceinline__ float ror8f(float x) { return __builtin_bit_cast(float, ror8(__builtin_bit_cast(uint32_t, x))); }
+
+// Limb-packed rows split the unit's 8 slots between the two lanes of a head:
+// lane n (< 8, the high limb) owns slots 0-3 (row tile 0), lane n + 8 (the
+// low limb) slots 4-7 (row tile 1).  own_logit() forms the lane's full logit
+// of slot (4 rt + i) for its own rt from the two row tiles' results: with
+// `partnered`, the two lanes hold the high and low limb parts of the same
+// logit (one DPP rotation adds the partner's); otherwise both hold it whole.
+__device__ __forceinline__ bool high_limb_lane(int lane) { return (lane & 8) == 0; }
+__device__ __forceinline__ float own_logit(float c0, float c1, int lane, bool partnered) {
+    const bool hi = high_limb_lane(lane);
+    const float own = hi ? c0 : c1;
+    return partnered ? own + ror8f(hi ? c1 : c0) : own;
+}
+
+// Online-softmax step and value contraction of a limb-packed lane over its 4
+// own slots (x[]: raw q.k, vs/vz: value scale/zero, valid: holds a token).
+// Each lane evaluates the weights p s of its own slots only and forms both
+// fp16 limbs of them (high part and exact low part: 22 bits); the lanes of a
+// head then trade the limbs the other needs by DPP, so that row n of the
+// value product gets the high parts of all 8 slots and row n + 8 the low
+// parts, as before, with each weight evaluated once.  A.l and A.pz hold the
+// lane's share (its own slots): the two lanes of a head are added at the end.
+// TS, TZ: _Float16 where the scales and zeros are stored fp16 values (read
+// by the mixed-precision fmas directly), float otherwise.
+template <typename TS, typename TZ, typename VOp>
+__device__ __forceinline__ void softmax_and_values_lp(WaveAcc& A, const float (&x)[4], const TS (&vs)[4],
+                                                      const TZ (&vz)[4], const bool (&valid)[4], float sl2,
+                                                      int lane, VOp vop) {
+    float cm = kNegInf;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cm = valid[k] ? fmaxf(cm, x[k]) : cm;
+    cm = fmaxf(cm, ror8f(cm));   // the partner's 4 slots
+    cm = group_max(cm);
+    const float mnew = fmaxf(A.m, cm * sl2);
+    const float alpha = A.m == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(A.m - mnew);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+        const int base = (lane & 48) | ((lane >> 4) << 2);
+        float ai[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, base + i);
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) A.acc[ct][i] *= ai[i];
+        A.l *= alpha;
+        A.pz *= alpha;
+    }
+    A.m = mnew;
+    _Float16 hp[4], lp[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        // invalid slots (masked tokens, missing records) contribute nothing,
+        // whatever their (possibly non-finite) scale and zero bits
+        const float p = valid[k] ? __builtin_amdgcn_exp2f(fmaf(x[k], sl2, -mnew)) : 0.0f;
+        A.l += p;
+        A.pz = valid[k] ? fmaf(p, (float)vz[k], A.pz) : A.pz;
+        // the weight p s as an fp16 high part (p s rounded once) and the
+        // exact residual p s - hi rounded once: two mixed-precision fmas
+        // reading s in fp16
+        const float s = valid[k] ? (float)vs[k] : 0.0f;
+        hp[k] = (_Float16)__builtin_fmaf(p, s, 0.0f);
+        lp[k] = (_Float16)__builtin_fmaf(p, s, -(float)hp[k]);
+    }
+    const bool hi = high_limb_lane(lane);
+    uint32_t d[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t H = as_u32(h2{hp[2 * j], hp[2 * j + 1]});
+        const uint32_t Lw = as_u32(h2{lp[2 * j], lp[2 * j + 1]});
+        // what the partner needs from this lane: the high lane's low limbs
+        // (for the partner's slots 0-3), the low lane's high limbs (for the
+        // partner's slots 4-7)
+        const uint32_t X = hi ? Lw : H;
+        // slots 0-3: the high lane keeps its own; the low lane (lanes 8-15
+        // of the row, banks 2-3) takes the partner's
+        d[j] = (uint32_t)__builtin_amdgcn_update_dpp((int)H, (int)X, 0x128 /* row_ror:8 */, 0xf, 0xc, false);
+        // slots 4-7: the low lane keeps its own; the high lane (banks 0-1)
+        // takes the partner's
+        d[2 + j] = (uint32_t)__builtin_amdgcn_update_dpp((int)Lw, (int)X, 0x128, 0xf, 0x3, false);
+    }
+    const h8 wop = make_h8(as_h2(d[0]), as_h2(d[1]), as_h2(d[2]), as_h2(d[3]));
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) A.acc[ct] = mfma(wop, vop(ct), A.acc[ct]);
+}
+
 // Token packing (limb-packed, at most 4 query heads per kv head): columns
 // 4-7 and 12-15 of the products carry no head, so the second 16-token tile's
 // logits move there, column c then holding head c & 3, tile (c >> 2) & 1 and
@@ -825,6 +918,28 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
         return;
     }
 
+    if constexpr (LP) {
+        // the lane's own 4 slots: row tile rt = 0 (high limb lane) or 1 (low);
+        // slot 4rt + i <-> token 16rt + 4g + i (pre-RoPE: both limb columns
+        // already hold the head's full logit)
+        const int rt = high_limb_lane(lane) ? 0 : 1;
+        const int rec = S::NR == 2 ? rt : 0;
+        const lds_u8* vm = buf + S::META + rec * S::MREC + 512 + g * 4 * SPT;
+        float x[4];
+        _Float16 vs[4], vz[4];
+        bool valid[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int slot = S::NR == 2 ? i : 4 * rt + i;
+            x[i] = own_logit(C[0][i], C[1][i], lane, !RP);
+            if constexpr (SP) x[i] += SPL->corr[wave][16 * rt + 4 * g + i][n & 7];
+            vs[i] = lds_read<_Float16>(vm + 2 * slot);
+            vz[i] = lds_read<_Float16>(vm + 2 * (SPT + slot));
+            valid[i] = S::NR == 1 || ((has >> rec) & 1);
+        }
+        softmax_and_values_lp(A, x, vs, vz, valid, sl2, lane, vop);
+        return;
+    }
     // value scale/zero of the lane's 8 slots: slot k = 4*rt + i <-> token 16rt + 4g + i
     float x[8], vs[8], vz[8];
     bool valid[8];
@@ -836,15 +951,14 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
         for (int i = 0; i < 4; ++i) {
             const int k = 4 * rt + i;
             const int slot = S::NR == 2 ? i : k;
-            // (pre-RoPE: both limb columns hold the same head's full logit)
-            x[k] = LP && !RP ? add_limb_partner(C[rt][i]) : C[rt][i];
-            if constexpr (SP) x[k] += SPL->corr[wave][16 * rt + 4 * g + i][LP ? (n & 7) : n];
+            x[k] = C[rt][i];
+            if constexpr (SP) x[k] += SPL->corr[wave][16 * rt + 4 * g + i][n];
             vs[k] = h2f(lds_read<uint16_t>(vm + 2 * slot));
             vz[k] = h2f(lds_read<uint16_t>(vm + 2 * (SPT + slot)));
             valid[k] = S::NR == 1 || ((has >> rec) & 1);
         }
     }
-    softmax_and_values<LP>(A, x, vs, vz, valid, sl2, lane, vop);
+    softmax_and_values<false>(A, x, vs, vz, valid, sl2, lane, vop);
 }
 
 // Eight 8-bit codes (words w0, w1, byte order) as an fp16 operand.  INT8:
@@ -922,11 +1036,10 @@ __device__ __forceinline__ void process_unit8(const lds_u8* buf, uint32_t has, W
             }
     }
 
-    // slot k = 4rt + i <-> token 16rt + 4g + i
-    float x[8], vs[8], vz[8];
-    bool valid[8];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    auto vop = [&](int ct) -> h8 { return conv8<F>(w[0][ct], w[1][ct]); };
+    // Per-token dequantization of row tile rt's 4 logits c[] of this lane
+    // (slot 4rt + i <-> token 16rt + 4g + i), with their value scales and zeros.
+    auto tile = [&](int rt, f4 c, float (&x)[4], float (&vs)[4], float (&vz)[4], bool (&valid)[4]) {
         const int rec = S::NR == 2 ? rt : 0;
         float ks4[4], kz4[4], vs4[4], vz4[4];
         if (F == kFmtInt8) {
@@ -948,20 +1061,48 @@ __device__ __forceinline__ void process_unit8(const lds_u8* buf, uint32_t has, W
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int k = 4 * rt + i;
             if (F == kFmtInt8) {
-                x[k] = fmaf(ks4[i], C[rt][i], fmaf(128.0f, ks4[i], kz4[i]) * qsum);
-                vs[k] = vs4[i];
-                vz[k] = fmaf(128.0f, vs4[i], vz4[i]);
+                x[i] = fmaf(ks4[i], c[i], fmaf(128.0f, ks4[i], kz4[i]) * qsum);
+                vs[i] = vs4[i];
+                vz[i] = fmaf(128.0f, vs4[i], vz4[i]);
             } else {
-                x[k] = C[rt][i];
-                vs[k] = vscl;
-                vz[k] = 0.0f;
+                x[i] = c[i];
+                vs[i] = vscl;
+                vz[i] = 0.0f;
             }
-            valid[k] = S::NR == 1 || ((has >> rec) & 1);
+            valid[i] = S::NR == 1 || ((has >> rec) & 1);
+        }
+    };
+    if constexpr (LP) {
+        // both limb columns hold the head's full logits: each lane takes its
+        // own row tile (0 for the high limb lane, 1 for the low), reading
+        // that tile's tables at a per-lane address
+        const bool hi = high_limb_lane(lane);
+        f4 co;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) co[i] = hi ? C[0][i] : C[1][i];
+        float x[4], vs[4], vz[4];
+        bool valid[4];
+        tile(hi ? 0 : 1, co, x, vs, vz, valid);
+        softmax_and_values_lp(A, x, vs, vz, valid, sl2, lane, vop);
+        return;
+    }
+    float x[8], vs[8], vz[8];
+    bool valid[8];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        float xt[4], vst[4], vzt[4];
+        bool vt[4];
+        tile(rt, C[rt], xt, vst, vzt, vt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[4 * rt + i] = xt[i];
+            vs[4 * rt + i] = vst[i];
+            vz[4 * rt + i] = vzt[i];
+            valid[4 * rt + i] = vt[i];
         }
     }
-    softmax_and_values<LP>(A, x, vs, vz, valid, sl2, lane, [&](int ct) -> h8 { return conv8<F>(w[0][ct], w[1][ct]); });
+    softmax_and_values<false>(A, x, vs, vz, valid, sl2, lane, vop);
 }
 
 // Ring slot of token t0 + r (0 <= r < 32) given slot0 = t0 % ring; ring >= 16.
@@ -1054,18 +1195,36 @@ __device__ __forceinline__ void process_residual(WaveAcc& A, const Layout& L, co
         softmax_and_values_tp(A, x, vs, vz, valid, sl2, lane, vop);
         return;
     }
+    if constexpr (LP) {
+        // own slots, as in the quantized units (the low limb lanes' key
+        // products are zero unless pre-RoPE keys made both limbs whole)
+        const int rt = high_limb_lane(lane) ? 0 : 1;
+        float x[4], vs[4], vz[4];
+        bool valid[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = own_logit(C[0][i], C[1][i], lane, !RP);
+            vs[i] = 1.0f;
+            vz[i] = 0.0f;
+            valid[i] = t0 + rt * 16 + 4 * g + i < n;
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the value rows are in LDS
+        wave_sync();
+        softmax_and_values_lp(A, x, vs, vz, valid, sl2, lane, vop);
+        return;
+    }
     float x[8], vs[8], vz[8];
     bool valid[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        x[k] = LP && !RP ? add_limb_partner(C[k >> 2][k & 3]) : C[k >> 2][k & 3];
+        x[k] = C[k >> 2][k & 3];
         vs[k] = 1.0f;
         vz[k] = 0.0f;
         valid[k] = t0 + (k >> 2) * 16 + 4 * g + (k & 3) < n;
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the value rows are in LDS
     wave_sync();
-    softmax_and_values<LP>(A, x, vs, vz, valid, sl2, lane, vop);
+    softmax_and_values<false>(A, x, vs, vz, valid, sl2, lane, vop);
 }
 
 // A wave's [16][128] fp32 accumulator image after the unit loop.
@@ -1077,12 +1236,19 @@ __device__ __forceinline__ float* wave_acc(uint8_t* stage_a, uint8_t* stage_b, i
 // than 3/4 left ... 0: under 1/4).  Waves issue oldest-first, so without
 // this the first workgroup placed on a CU runs ahead and the CU spends the
 // end of the kernel with few waves; lagging waves now win arbitration and
-// the workgroups of a CU finish close together.
-__device__ __forceinline__ void set_progress_prio(int left, int total) {
-    const int lvl = (4 * left - 1) / total;   // 0..3 for 1 <= left <= total
-    if (lvl >= 3) __builtin_amdgcn_s_setprio(3);
-    else if (lvl == 2) __builtin_amdgcn_s_setprio(2);
-    else if (lvl == 1) __builtin_amdgcn_s_setprio(1);
+// the workgroups of a CU finish close together.  Level k is reached while
+// (4 left - 1) / total >= k, i.e. left >= ceil((k total + 1) / 4): the three
+// thresholds are formed once per segment, so the unit loop only compares.
+struct ProgressPrio {
+    int t1, t2, t3;
+};
+__device__ __forceinline__ ProgressPrio progress_prio(int total) {
+    return ProgressPrio{(total + 4) / 4, (2 * total + 4) / 4, (3 * total + 4) / 4};
+}
+__device__ __forceinline__ void set_progress_prio(int left, const ProgressPrio& p) {
+    if (left >= p.t3) __builtin_amdgcn_s_setprio(3);
+    else if (left >= p.t2) __builtin_amdgcn_s_setprio(2);
+    else if (left >= p.t1) __builtin_amdgcn_s_setprio(1);
     else __builtin_amdgcn_s_setprio(0);
 }
 
@@ -1204,6 +1370,8 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
 
     {
         const int ntot = max(1, (q1 - (lo + wave) + kWaves - 1) / kWaves);   // this wave's units
+        const ProgressPrio prio = progress_prio(ntot);
+        int left = ntot;   // units of this wave from u on
         if (u < q1) {
             // Direct-to-LDS loads: the next NS - 1 units of the wave are in
             // flight, each in a stage buffer of its own, while unit u is
@@ -1237,7 +1405,7 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
                     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
                 }
                 wave_sync();
-                set_progress_prio((q1 - u + kWaves - 1) / kWaves, ntot);
+                set_progress_prio(left--, prio);
                 process_any<G, KB, VB, F, LP, TP>(sb[0], hb[0], A, Q, sl2q, qsum, vscl, lane, R, wave, 32 * u, L, SPL, gq);
                 u += kWaves;
                 if (u >= q1) break;
@@ -1262,8 +1430,14 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
     // Wave results -> LDS: totals over the lane groups, accumulators by head.
     // The accumulators reuse the stage buffers: every wave has consumed its
     // staged units and has no load in flight once all have passed the barrier.
-    const float lt = group_sum(A.l);
-    const float pzt = group_sum(A.pz);
+    // (limb-packed without token packing: the two lanes of a head each hold
+    // the sums over their own slots)
+    float lt = group_sum(A.l);
+    float pzt = group_sum(A.pz);
+    if (LP && !TP) {
+        lt += ror8f(lt);
+        pzt += ror8f(pzt);
+    }
     __syncthreads();
     // TP: columns hh and hh + 4 hold the two token tiles of head hh
     const float lh = TP ? lt + __shfl(lt, (lane + 4) & 15) : lt;
