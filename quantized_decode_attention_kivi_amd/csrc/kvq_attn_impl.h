@@ -501,22 +501,17 @@ __device__ __forceinline__ void softmax_and_values_lp(WaveAcc& A, const float (&
         hp[k] = (_Float16)__builtin_fmaf(p, s, 0.0f);
         lp[k] = (_Float16)__builtin_fmaf(p, s, -(float)hp[k]);
     }
-    const bool hi = high_limb_lane(lane);
     uint32_t d[4];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const uint32_t H = as_u32(h2{hp[2 * j], hp[2 * j + 1]});
         const uint32_t Lw = as_u32(h2{lp[2 * j], lp[2 * j + 1]});
-        // what the partner needs from this lane: the high lane's low limbs
-        // (for the partner's slots 0-3), the low lane's high limbs (for the
-        // partner's slots 4-7)
-        const uint32_t X = hi ? Lw : H;
-        // slots 0-3: the high lane keeps its own; the low lane (lanes 8-15
-        // of the row, banks 2-3) takes the partner's
-        d[j] = (uint32_t)__builtin_amdgcn_update_dpp((int)H, (int)X, 0x128 /* row_ror:8 */, 0xf, 0xc, false);
-        // slots 4-7: the low lane keeps its own; the high lane (banks 0-1)
-        // takes the partner's
-        d[2 + j] = (uint32_t)__builtin_amdgcn_update_dpp((int)Lw, (int)X, 0x128, 0xf, 0x3, false);
+        // slots 0-3: the high lane keeps its own high limbs; the low lane
+        // (lanes 8-15 of the row, banks 2-3) takes its partner's low limbs
+        d[j] = (uint32_t)__builtin_amdgcn_update_dpp((int)H, (int)Lw, 0x128 /* row_ror:8 */, 0xf, 0xc, false);
+        // slots 4-7: the low lane keeps its own low limbs; the high lane
+        // (banks 0-1) takes its partner's high limbs
+        d[2 + j] = (uint32_t)__builtin_amdgcn_update_dpp((int)Lw, (int)H, 0x128, 0xf, 0x3, false);
     }
     const h8 wop = make_h8(as_h2(d[0]), as_h2(d[1]), as_h2(d[2]), as_h2(d[3]));
 #pragma unroll
@@ -813,6 +808,19 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
             for (int e = 0; e < 8; ++e) x[e] = fmaf((float)a[e], (float)sj[e], (float)zj[e]);
         });
     } else {
+    // the unit's key codes are read first, so that their LDS latency overlaps
+    // the scale/zero tables' reads and the q s products
+    uint32_t kc[2][KB];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        if (KB == 4) {
+            const u32x4 x = lds_read<u32x4>(buf + S::KC + rt * 1024 + 16 * lane);
+            kc[rt][0] = x[0]; kc[rt][1] = x[1]; kc[rt][2] = x[2]; kc[rt][3] = x[3];
+        } else {
+            const u32x2 x = lds_read<u32x2>(buf + S::KC + rt * 512 + 16 * ((g >> 1) * 16 + n) + 8 * (g & 1));
+            kc[rt][0] = x[0]; kc[rt][1] = x[1];
+        }
+    }
 #pragma unroll
     for (int i = 0; i < S::NR; ++i) {
         const lds_u8* km = buf + S::META + i * S::MREC;
@@ -843,18 +851,10 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             if (S::NR == 2 && rt != i) continue;
-            uint32_t kc[KB];
-            if (KB == 4) {
-                const u32x4 x = lds_read<u32x4>(buf + S::KC + rt * 1024 + 16 * lane);
-                kc[0] = x[0]; kc[1] = x[1]; kc[2] = x[2]; kc[3] = x[3];
-            } else {
-                const u32x2 x = lds_read<u32x2>(buf + S::KC + rt * 512 + 16 * ((g >> 1) * 16 + n) + 8 * (g & 1));
-                kc[0] = x[0]; kc[1] = x[1];
-            }
             f4 acc = cz;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const h8 a = levels8<KB, CB>(kc, j, L.klut);
+                const h8 a = levels8<KB, CB>(kc[rt], j, L.klut);
                 acc = mfma(a, qhi[j], acc);
                 if (!LP) acc = mfma(a, qlo[j], acc);
             }
@@ -1251,6 +1251,11 @@ __device__ __forceinline__ void set_progress_prio(int left, const ProgressPrio& 
     else if (left >= p.t1) __builtin_amdgcn_s_setprio(1);
     else __builtin_amdgcn_s_setprio(0);
 }
+// The same levels, set only where the level changes (left is one of the
+// thresholds, or the first unit): one scalar compare in the other units.
+__device__ __forceinline__ void update_progress_prio(int left, bool first, const ProgressPrio& p) {
+    if (first || left == p.t3 - 1 || left == p.t2 - 1 || left == p.t1 - 1) set_progress_prio(left, p);
+}
 
 // 32-token units of sequence b: its quantized groups first (G = 16: two
 // records per unit), then its fp16 residual tokens.  Counters written by this
@@ -1405,7 +1410,8 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
                     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
                 }
                 wave_sync();
-                set_progress_prio(left--, prio);
+                update_progress_prio(left, left == ntot, prio);
+                --left;
                 process_any<G, KB, VB, F, LP, TP>(sb[0], hb[0], A, Q, sl2q, qsum, vscl, lane, R, wave, 32 * u, L, SPL, gq);
                 u += kWaves;
                 if (u >= q1) break;
