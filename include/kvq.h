@@ -65,7 +65,7 @@
  * Conventions for every call below:
  *   - Pointers named *_host are host memory; every other data pointer is a
  *     device pointer owned by the caller.  The library allocates and frees
- *     nothing and keeps no pointer after a call returns.
+ *     nothing and keeps no pointer to caller memory after a call returns.
  *   - `stream` is a hipStream_t passed as void* (NULL = default stream).  All
  *     device work is enqueued asynchronously on it; the call returns once the
  *     work is enqueued.
@@ -253,6 +253,26 @@ kvq_status kv_decode_attention_partials(const kvq_config *cfg, const kvq_cache *
 kvq_status kv_decode_attention_merge(const kvq_config *cfg, const kvq_cache *cache,
                                      int32_t num_q_heads, const void *workspace,
                                      size_t workspace_bytes, float *out, void *stream);
+
+/* kv_decode_attention without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments (minus the
+ * workspace), checks and result as kv_decode_attention; the partial results
+ * go to a fixed device array of KVQ_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends.  The call allocates
+ * nothing: on its first use on a device it looks up that device's array
+ * (the device of `stream`, or the current device for the null stream).
+ * A call whose partials need more than the array holds
+ * (kv_decode_attention_workspace_bytes(cfg, num_q_heads) above the limit)
+ * returns KVQ_ECAPACITY with the sizes in kvq_last_error(), enqueueing
+ * nothing.  Nothing in the array needs clearing between calls (every slot
+ * the merge reads is written first in the same call), but every call on a
+ * GPU uses that GPU's one array: calls that overlap on one GPU (different
+ * streams, or threads without ordering) race and give wrong results. */
+#define KVQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+kvq_status kv_decode_attention_noalloc(const kvq_config *cfg, const kvq_cache *cache,
+                                       const void *q, int32_t num_q_heads, float softmax_scale,
+                                       float *out, void *stream);
 
 /* Logical view of the quantized part (test hook).  k_codes, v_codes: uint8
  * [B][H][out_tokens][d], one code per element for t < n_q[b], 0 elsewhere;

@@ -2,6 +2,7 @@
 // Every entry point validates its arguments before anything is enqueued and
 // never allocates device memory.
 #include <cmath>
+#include <mutex>
 #include <stdio.h>
 #include <string.h>
 
@@ -10,6 +11,18 @@
 namespace kvq {
 
 static thread_local char g_last_error[256] = "";
+
+// Fixed device scratch of kv_decode_attention_noalloc: one copy per GPU the
+// library runs on, held until the process ends.  In host code the array's
+// name is only a stand-in for the symbol, never a device address: the
+// address of each GPU's copy comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address is handed to
+// kernels.
+constexpr size_t kScratchBytes = (size_t)KVQ_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mutex;
+static void* g_scratch_ptr[kMaxDevices];
 
 static kvq_status hip_status(hipError_t e) {
     if (e == hipSuccess) return KVQ_OK;
@@ -146,6 +159,34 @@ static kvq_status check_cache(const Layout& L, const kvq_cache* c) {
     return KVQ_OK;
 }
 
+// Device address of the scratch array on the device that `stream` belongs to
+// (the current device for the null stream), looked up on the first call for
+// that device with the device made current for the lookup.
+static kvq_status scratch_address(hipStream_t stream, void** out) {
+    int cur = 0, dev = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_status(e);
+    dev = cur;
+    if (stream && (e = hipStreamGetDevice(stream, &dev)) != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices) return KVQ_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e);
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t restore = dev != cur ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess) return hip_status(e);
+        if (restore != hipSuccess) return hip_status(restore);
+        if (!p || ((uintptr_t)p & 255)) {
+            snprintf(g_last_error, sizeof(g_last_error), "scratch array of device %d at a bad address %p", dev, p);
+            return KVQ_EHIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KVQ_OK;
+}
+
 }  // namespace kvq
 
 using namespace kvq;
@@ -266,6 +307,30 @@ kvq_status kv_decode_attention(const kvq_config* cfg, const kvq_cache* cache, co
                                               workspace, (hipStream_t)stream));
     if (st != KVQ_OK) return st;
     return hip_status(launch_attention_merge(L, P, *cache, num_q_heads, workspace, out, (hipStream_t)stream));
+}
+
+kvq_status kv_decode_attention_noalloc(const kvq_config* cfg, const kvq_cache* cache, const void* q,
+                                       int32_t num_q_heads, float softmax_scale, float* out, void* stream) {
+    Layout L;
+    AttnPlan P;
+    // validation first, with a stand-in workspace address: the size and
+    // argument checks need no device and enqueue nothing
+    kvq_status st = check_attention(cfg, cache, q, num_q_heads, softmax_scale, (const void*)(uintptr_t)256,
+                                    kScratchBytes, &L, &P);
+    if (st == KVQ_ECAPACITY || (st == KVQ_OK && P.workspace > kScratchBytes)) {
+        snprintf(g_last_error, sizeof(g_last_error),
+                 "kv_decode_attention_noalloc: this call needs %zu bytes of scratch, the fixed array holds %zu",
+                 (size_t)P.workspace, kScratchBytes);
+        return KVQ_ECAPACITY;
+    }
+    if (st != KVQ_OK) return st;
+    if (!out) return KVQ_EINVAL;
+    void* ws = nullptr;
+    if ((st = scratch_address((hipStream_t)stream, &ws)) != KVQ_OK) return st;
+    st = hip_status(launch_attention_partials(L, P, *cache, (const _Float16*)q, num_q_heads, softmax_scale, ws,
+                                              (hipStream_t)stream));
+    if (st != KVQ_OK) return st;
+    return hip_status(launch_attention_merge(L, P, *cache, num_q_heads, ws, out, (hipStream_t)stream));
 }
 
 kvq_status kv_export_codes(const kvq_config* cfg, const kvq_cache* cache, uint8_t* k_codes, uint8_t* v_codes,

@@ -52,7 +52,7 @@ class kvq_sizes(ctypes.Structure):
 
 EXPORTED = ["kvq_buffer_sizes", "kv_quantize_prefill", "kv_append_token", "kv_dequantize",
             "kv_decode_attention_workspace_bytes", "kv_decode_attention", "kv_decode_attention_partials",
-            "kv_decode_attention_merge", "kv_export_codes", "kv_export_outliers", "kvq_codebook_levels",
+            "kv_decode_attention_merge", "kv_decode_attention_noalloc", "kv_export_codes", "kv_export_outliers", "kvq_codebook_levels",
             "kvq_status_string",
             "kvq_last_error"]
 
@@ -93,6 +93,9 @@ def lib():
         L.kv_decode_attention_merge.argtypes = [P(kvq_config), P(kvq_cache), ctypes.c_int32, vp, ctypes.c_size_t,
                                                 vp, vp]
         L.kv_decode_attention_merge.restype = ctypes.c_int
+        L.kv_decode_attention_noalloc.argtypes = [P(kvq_config), P(kvq_cache), vp, ctypes.c_int32, ctypes.c_float,
+                                                  vp, vp]
+        L.kv_decode_attention_noalloc.restype = ctypes.c_int
         L.kv_export_codes.argtypes = [P(kvq_config), P(kvq_cache)] + [vp] * 6 + [ctypes.c_int32, vp]
         L.kv_export_codes.restype = ctypes.c_int
         L.kv_export_outliers.argtypes = [P(kvq_config), P(kvq_cache), vp, vp, ctypes.c_int32, vp]
@@ -169,6 +172,12 @@ def kv_decode_attention_merge(cfg, cache, num_q_heads, workspace, out, stream=No
     _check(lib().kv_decode_attention_merge(ctypes.byref(cfg), ctypes.byref(cache), int(num_q_heads), _ptr(workspace),
                                            workspace.numel() * workspace.element_size(), _ptr(out),
                                            _stream(stream)), "kv_decode_attention_merge")
+
+
+def kv_decode_attention_noalloc(cfg, cache, q, num_q_heads, softmax_scale, out, stream=None):
+    _check(lib().kv_decode_attention_noalloc(ctypes.byref(cfg), ctypes.byref(cache), _ptr(q), int(num_q_heads),
+                                             ctypes.c_float(softmax_scale), _ptr(out), _stream(stream)),
+           "kv_decode_attention_noalloc")
 
 
 def kv_export_codes(cfg, cache, k_codes, v_codes, k_s, k_z, v_s, v_z, out_tokens, stream=None):

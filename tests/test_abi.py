@@ -261,6 +261,31 @@ def test_calls_reject_bad_arguments_before_launch():
     assert L.kvq_status_string(kvq.KVQ_ECAPACITY).decode() == "buffer or workspace too small"
 
 
+def test_noalloc_rejects_oversized_calls_before_any_device_work():
+    """The no-allocation entry point checks the scratch its partials need
+    against its fixed array on the host: an oversized batch is refused with
+    KVQ_ECAPACITY and both sizes in the error text (no device is touched:
+    this runs on a machine without a GPU); a malformed call is refused as by
+    kv_decode_attention."""
+    kvq = _kvq()
+    L = kvq.lib()
+    good = 0x10000
+    cache = kvq.kvq_cache(good, good, good, good, good, None)
+    vp, by = ctypes.c_void_p, ctypes.byref
+    cfg = _cfg(kvq, num_seqs=4096, num_kv_heads=8, max_tokens=4096)
+    need = kvq.kv_decode_attention_workspace_bytes(cfg, 128)
+    assert need > 16 << 20
+    st = L.kv_decode_attention_noalloc(by(cfg), by(cache), vp(good), 128, ctypes.c_float(0.088), vp(good), None)
+    assert st == kvq.KVQ_ECAPACITY
+    msg = L.kvq_last_error().decode()
+    assert str(need) in msg and str(16 << 20) in msg
+    small = _cfg(kvq)
+    assert L.kv_decode_attention_noalloc(by(small), by(cache), vp(good), 7, ctypes.c_float(0.088), vp(good),
+                                         None) == kvq.KVQ_EINVAL
+    assert L.kv_decode_attention_noalloc(by(small), by(cache), vp(good), 6, ctypes.c_float(0.088), None,
+                                         None) == kvq.KVQ_EINVAL
+
+
 @pytest.mark.parametrize("paged", [False, True])
 def test_sequence_view_offsets(paged):
     """A sequence view is the one-sequence cache at fixed offsets of the
