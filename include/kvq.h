@@ -216,10 +216,13 @@ size_t kv_decode_attention_workspace_bytes(const kvq_config *cfg, int32_t num_q_
  * dequantizes while it reads, the quantized part and the full-precision
  * residual are computed separately and merged).  q: fp16 [B][Hq][d];
  * out: fp32 [B][Hq][d]; Hq a multiple of H with Hq/H <= 16; softmax_scale is
- * normally 1/sqrt(d).  q must be 16-byte aligned.  KIVI format: the products
- * |q[c]| * s[c] of a query element and its key group's channel scale must
- * stay below 65504 (they are formed in fp16; true for any query of O(1..100)
- * against keys whose per-group range is below ~1000).
+ * normally 1/sqrt(d).  q must be 16-byte aligned.  Any finite fp16 query
+ * and cache give a finite result: the kernel scales the query by a power of
+ * two before it forms q * s in fp16 (and pre-RoPE keys before their fp16
+ * split), and moves the factor into the softmax scale.  Accuracy is that of
+ * fp32 accumulation: logits carrying terms far above 65504 (key groups
+ * spanning most of the fp16 range against large query elements) keep the
+ * fp32 rounding of those terms.
  * workspace: 256-byte aligned device memory of at least
  * kv_decode_attention_workspace_bytes(cfg, Hq) bytes that receives the
  * partial results (no initialisation needed, content not preserved between

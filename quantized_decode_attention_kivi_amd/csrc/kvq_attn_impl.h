@@ -651,9 +651,14 @@ __device__ void rope_setup(RopeLds& R, float theta, int tid) {
 }
 
 // The wave's (cos, sin) at tokens t0 and t0 + 16 for every pair (lane = pair).
+// The (cos, sin) pairs are stored halved, so the keys come out of the
+// rotation at half their value (exactly: a power of two), which keeps their
+// fp16 parts finite; the caller's logit scale is doubled to match.
 __device__ __forceinline__ void rope_unit_base(RopeLds* R, int wave, int lane, int t0) {
     float sn, cs;
     turns_sincos((uint64_t)(uint32_t)t0 * R->phi[lane], &sn, &cs);
+    sn *= 0.5f;
+    cs *= 0.5f;
     const f2 t16 = R->tab[16][lane];
     R->base[wave][0][lane] = f2{cs, sn};
     R->base[wave][1][lane] = f2{cs * t16[0] - sn * t16[1], sn * t16[0] + cs * t16[1]};
@@ -813,7 +818,7 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
     uint32_t kc[2][KB];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-        if (KB == 4) {
+        if constexpr (KB == 4) {
             const u32x4 x = lds_read<u32x4>(buf + S::KC + rt * 1024 + 16 * lane);
             kc[rt][0] = x[0]; kc[rt][1] = x[1]; kc[rt][2] = x[2]; kc[rt][3] = x[3];
         } else {
@@ -1348,17 +1353,54 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
         // on them inside the loop.
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
+    // Logit scale of the units' products (log2 units).  The low-bit keys are
+    // contracted with q s formed in fp16: the query is first scaled by an
+    // exact power of two 2^-k (k >= 0, one for the whole segment) that brings
+    // every |q| below 1, so |q s| < s stays inside the fp16 range for any
+    // finite scale s; 2^k moves into the logit scale.  Pre-RoPE keys are
+    // rotated in fp32 and split into fp16 parts at half their value (a
+    // rotated pair can reach sqrt(2) times the largest fp16), so their scale
+    // doubles.
+    float sl2s = sl2;
+    _Float16 qscale = (_Float16)1.0f;
+    if constexpr (rope_fmt(F)) {
+        sl2s = 2.0f * sl2;
+    } else if constexpr (low_bit(F)) {
+        h2 m2 = h2{(_Float16)0.0f, (_Float16)0.0f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                m2 = __builtin_elementwise_max(m2, __builtin_elementwise_abs(h2{Q.q[j][2 * e], Q.q[j][2 * e + 1]}));
+        float m = group_max(fmaxf((float)m2[0], (float)m2[1]));
+        // over the 16 columns of a row: lane ^ 8, ^ 4, ^ 2, ^ 1 (swizzle in
+        // bit mode: and-mask 0x1f, xor-mask in bits 10-14)
+        m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, m), 0x201f)));
+        m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, m), 0x101f)));
+        m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, m), 0x081f)));
+        m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, m), 0x041f)));
+        // m = f 2^e with f in [1/2, 1): k = max(e, 0) leaves max |q| 2^-k < 1
+        const int k = __builtin_amdgcn_readfirstlane(max(__builtin_amdgcn_frexp_expf(m), 0));
+        if (k > 0) {
+            qscale = (_Float16)__builtin_ldexpf(1.0f, -k);
+            const h8 f = h8{qscale, qscale, qscale, qscale, qscale, qscale, qscale, qscale};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Q.q[j] = Q.q[j] * f;
+            sl2s = __builtin_ldexpf(sl2, k);
+        }
+    }
     if constexpr (sp_fmt(F)) {
-        // the segment's query for the kept-key corrections, [channel][head]
+        // the segment's query for the kept-key corrections, [channel][head],
+        // scaled like the query operands
         for (int idx = tid; idx < kD * 16; idx += 256) {
             const int ch = idx >> 4, hh = idx & 15;
-            SPL->q[ch][hh] = hh < gq ? q[((long)b * Hq + h * gq + hh) * kD + ch] : (_Float16)0.0f;
+            SPL->q[ch][hh] = hh < gq ? q[((long)b * Hq + h * gq + hh) * kD + ch] * qscale : (_Float16)0.0f;
         }
         __syncthreads();
     }
     // 8-bit formats: sum_c q_c of the lane's head (INT8), the kv head's
     // static scales (FP8; the key scale joins the logit scale)
-    float qsum = 0.0f, vscl = 0.0f, sl2q = sl2;
+    float qsum = 0.0f, vscl = 0.0f, sl2q = sl2s;
     if (F == kFmtInt8) {
         float t = 0.0f;
 #pragma unroll
@@ -1428,7 +1470,7 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
     }
     for (int u = lo + wave; u < hi; u += kWaves)
         if (u >= su.uq)
-            process_residual<LP, rope_fmt(F), TP>(A, L, c, sh, su.nq + 32 * (u - su.uq), su.n, Q, sl2, lane,
+            process_residual<LP, rope_fmt(F), TP>(A, L, c, sh, su.nq + 32 * (u - su.uq), su.n, Q, sl2s, lane,
                                                 (lds_u8*)(stage_a + wave * S::PITCH),
                                                 (lds_u8*)(stage_b + wave * S::PITCH), R, wave);
     __builtin_amdgcn_s_setprio(0);

@@ -430,3 +430,81 @@ def test_prefill_degenerate_sets(kb, vb, G):
     cache.prefill(Kt, Vt, lens)
     states = oracle_states(to_bits(Kt), to_bits(Vt), lens, w, cap=L + 256)
     compare_codes(cache, states)
+
+
+def _fp32_attention(q32, kh, vh, scale):
+    """Attention with the logits summed in fp32 over the channels (products
+    of the fp32 query and dequantized keys, rounded to fp32 one by one), the
+    rest in fp64: what plain fp32 arithmetic gives on these logits."""
+    lg = np.zeros((q32.shape[0], kh.shape[0]), np.float32)
+    for c in range(kh.shape[1]):
+        lg = lg + (q32[:, c:c + 1].astype(np.float64) * kh[None, :, c]).astype(np.float32)
+    lg = lg.astype(np.float64) * np.float32(scale)
+    p = np.exp(lg - lg.max(axis=1, keepdims=True))
+    return (p @ vh.astype(np.float64)) / p.sum(axis=1, keepdims=True)
+
+
+@pytest.mark.parametrize("kb,vb,gq,rope", [(2, 2, 8, 0.0), (4, 4, 4, 0.0), (4, 2, 16, 0.0), (2, 2, 8, 10000.0)])
+def test_wide_range_keys_and_large_queries(kb, vb, gq, rope):
+    """Key groups spanning most of the fp16 range: channel 5 holds -60000 on
+    two tokens of every 32 and +60000 on the rest, so its scale is 40000
+    (INT2) or 8000 (INT4), and the query's element on it (2 or 10) makes
+    |q s| = 80000, beyond the largest fp16 (the fp16 products overflowed
+    before the query was scaled).  Pre-RoPE keys: channels 4 and 5 both at
+    +-60000, whose rotation reaches 84852; the query is 0 there, so the keys'
+    fp16 parts must stay finite for the logits to.  Attention must be finite
+    and match the oracle.
+
+    Bar: max-abs 2e-3 and row cosine 0.9999 for INT2 and pre-RoPE keys.  For
+    INT4 the inputs that overflowed carry a logit term of at least
+    65504 * 15 / 2 = 5 10^5, whose fp32 rounding alone puts plain fp32
+    attention over the same dequantized cache (logits summed in fp32)
+    outside that bar on this data; these rows are held to twice the error
+    of that plain fp32 attention instead (and to the bar where it is looser)."""
+    B, H, G, R = 2, 2, 32, 32
+    lens = np.array([600, 417])
+    L = int(lens.max())
+    w = _w("llama3_8b_layer_b8_32k_int4", name="wide", num_seqs=B, num_q_heads=H * gq, num_kv_heads=H, k_bits=kb,
+           v_bits=vb, group_size=G, residual=R, context=L, tag=47, rope_theta=rope)
+    rng = np.random.Generator(np.random.PCG64(48))
+    K = rng.standard_normal((B, H, L, 128)).astype(np.float16)
+    V = (rng.standard_normal((B, H, L, 128)) * 0.25).astype(np.float16)
+    wide = np.where(np.arange(L) % G < 2, np.float16(-60000.0), np.float16(60000.0))
+    K[:, :, :, 5] = wide
+    if rope:
+        K[:, :, :, 4] = wide
+    q = (rng.standard_normal((B, H * gq, 128)) * (3.0 if kb == 2 else 1.0)).astype(np.float16)
+    if rope:
+        q[:, :, 4:6] = 0
+    else:
+        q[:, :, 5] = 2.0 if kb == 2 else 10.0
+    Kt, Vt, qt = (torch.from_numpy(a).cuda() for a in (K, V, q))
+    cache = make_cache(w, lens)
+    print("wide-range keys kb=%d vb=%d gq=%d rope=%g" % (kb, vb, gq, rope), flush=True)
+    cache.prefill(Kt, Vt, lens)
+    out = cache.decode_attention(qt, SCALE)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    assert np.isfinite(out).all()
+    states = oracle_states(to_bits(Kt), to_bits(Vt), lens, w, cap=L + 64)
+    if not rope:
+        st = states[0][0]
+        assert np.array_equal(st.key_meta()[0][:, 5], np.full(st.nq // G, np.float16(120000.0 / ((1 << kb) - 1))
+                                                               .view(np.uint16)))
+    ref = oracle_attention(to_bits(qt), states, SCALE, rope_base=rope)
+    if kb == 2:
+        compare_attention(out, ref)
+        return
+    qf = oracle.h2f(to_bits(qt))
+    for b in range(B):
+        for h in range(H):
+            kh, vh = states[b][h].dequantize()
+            rows = slice(h * gq, (h + 1) * gq)
+            plain = _fp32_attention(qf[b, rows], kh, vh, SCALE)
+            r, o = ref[b, rows], out[b, rows].astype(np.float64)
+            cos = lambda x: (x * r).sum(-1) / (np.linalg.norm(x, axis=-1) * np.linalg.norm(r, axis=-1))
+            tol = max(2e-3, 2 * np.abs(plain - r).max())
+            assert np.abs(o - r).max() <= tol, (b, h, np.abs(o - r).max(), tol)
+            assert cos(o).min() >= min(0.9999, 1 - 2 * (1 - cos(plain).min())), (b, h, cos(o).min(), cos(plain).min())
+
+
