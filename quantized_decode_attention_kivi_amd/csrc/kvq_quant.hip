@@ -7,6 +7,8 @@
 // group of G tokens, values per token over their 128 channels, each set with
 // its own min/max scale and zero; the newest R tokens stay fp16 and a group
 // is quantized once it is full and outside them.
+#include <type_traits>
+
 #include "kvq_device.h"
 
 namespace kvq {
@@ -20,6 +22,26 @@ struct QuantSmem {
     uint32_t kept[G * kD / 32];       // dense-and-sparse: kept positions, one bit each
     int wtot[2];                      // dense-and-sparse: kept count of the first two words' waves
 };
+
+// Shared memory of the uniform-grid and 8-bit quantizers: the channel
+// extremes of each token slice are kept as the fp16 values they are (min and
+// max are exact in any precision), so a workgroup needs about 14 KB instead
+// of 22 and eight of them fit a compute unit.
+template <int G>
+struct QuantSmemU {
+    uint16_t kmn[16][kD], kmx[16][kD];   // per token slice, per channel (fp16 bits)
+    float kz[kD], kinv[kD];
+    uint8_t vcode[G][kD];                 // value codes before packing
+};
+
+// Quantizer variants (compile-time): the 8-bit formats kFmtInt8 and kFmtFp8,
+// and the low-bit format on the uniform grid (kQUniform), the codebook
+// grid (kQCodebook), each with dense-and-sparse keys (kQSparse, kQCodebookSparse).
+constexpr int kQUniform = 0, kQCodebook = 4, kQSparse = 6, kQCodebookSparse = 7;
+__host__ __device__ constexpr bool q_low_bit(int F) { return F == kQUniform || F >= kQCodebook; }
+// Shared memory of variant F.
+template <int G, int F>
+using QSmem = typename std::conditional<F == kQUniform || !q_low_bit(F), QuantSmemU<G>, QuantSmem<G>>::type;
 
 __device__ __forceinline__ int wave_sum_i(int x) {
 #pragma unroll
@@ -319,7 +341,7 @@ __device__ __forceinline__ float row16(float x) {
 }
 
 template <int G, int KB, int VB>
-__device__ void quantize_group_uniform(QuantSmem<G>& sm, const Layout& L, const half_t* __restrict__ ksrc,
+__device__ void quantize_group_uniform(QuantSmemU<G>& sm, const Layout& L, const half_t* __restrict__ ksrc,
                                        const half_t* __restrict__ vsrc, uint8_t* __restrict__ rec) {
     constexpr int NT = G / 16;
     const int tid = threadIdx.x;
@@ -346,10 +368,8 @@ __device__ void quantize_group_uniform(QuantSmem<G>& sm, const Layout& L, const 
             mn = pk_min(mn, kw[j][i]);
             mx = pk_max(mx, kw[j][i]);
         }
-        sm.kmn[ts][8 * cg + 2 * i] = h2f(mn & 0xffffu);
-        sm.kmn[ts][8 * cg + 2 * i + 1] = h2f(mn >> 16);
-        sm.kmx[ts][8 * cg + 2 * i] = h2f(mx & 0xffffu);
-        sm.kmx[ts][8 * cg + 2 * i + 1] = h2f(mx >> 16);
+        *(uint32_t*)&sm.kmn[ts][8 * cg + 2 * i] = mn;
+        *(uint32_t*)&sm.kmx[ts][8 * cg + 2 * i] = mx;
     }
 
     // Value statistics and codes: per token over its 128 channels.
@@ -379,10 +399,10 @@ __device__ void quantize_group_uniform(QuantSmem<G>& sm, const Layout& L, const 
     }
     __syncthreads();
     if (tid < kD) {
-        float mn = sm.kmn[0][tid], mx = sm.kmx[0][tid];
+        float mn = h2f(sm.kmn[0][tid]), mx = h2f(sm.kmx[0][tid]);
         for (int j = 1; j < 16; ++j) {
-            mn = fminf(mn, sm.kmn[j][tid]);
-            mx = fmaxf(mx, sm.kmx[j][tid]);
+            mn = fminf(mn, h2f(sm.kmn[j][tid]));
+            mx = fmaxf(mx, h2f(sm.kmx[j][tid]));
         }
         const QParams p = make_qparams(mn, mx, KB);
         sm.kz[tid] = -p.z;   // (negated: the fma's addend)
@@ -599,7 +619,7 @@ __device__ void quantize_pair16(QuantSmemPair& sm, const Layout& L, const half_t
 // vinv).  Key bytes go straight to the record in channel order; value bytes
 // through LDS into the lane-major operand order.
 template <int G, int F>
-__device__ void quantize_group8(QuantSmem<G>& sm, const Layout& L, const half_t* __restrict__ ksrc,
+__device__ void quantize_group8(QuantSmemU<G>& sm, const Layout& L, const half_t* __restrict__ ksrc,
                                 const half_t* __restrict__ vsrc, uint8_t* __restrict__ rec, float kinv,
                                 float vinv) {
     constexpr int NT = G / 16;
@@ -690,12 +710,6 @@ __device__ void quantize_group8(QuantSmem<G>& sm, const Layout& L, const half_t*
     __syncthreads();  // LDS may be reused by the caller
 }
 
-// Quantizer variants (compile-time): the 8-bit formats kFmtInt8 and kFmtFp8,
-// and the low-bit format on the uniform grid (kQUniform), the codebook
-// grid (kQCodebook), each with dense-and-sparse keys (kQSparse, kQCodebookSparse).
-constexpr int kQUniform = 0, kQCodebook = 4, kQSparse = 6, kQCodebookSparse = 7;
-__host__ __device__ constexpr bool q_low_bit(int F) { return F == kQUniform || F >= kQCodebook; }
-
 // Variant of a layout (host).
 inline int quant_variant(const Layout& L) {
     if (L.fmt != kFmtKivi) return L.fmt;
@@ -705,7 +719,7 @@ inline int quant_variant(const Layout& L) {
 
 // Quantizes one group in variant F (low-bit: key bits KB, value bits VB).
 template <int G, int KB, int VB, int F>
-__device__ __forceinline__ void quantize_any(QuantSmem<G>& sm, const Layout& L, const kvq_cache& c, int h,
+__device__ __forceinline__ void quantize_any(QSmem<G, F>& sm, const Layout& L, const kvq_cache& c, int h,
                                              const half_t* ksrc, const half_t* vsrc, uint8_t* rec) {
     if constexpr (F == kQUniform) {
         quantize_group_uniform<G, KB, VB>(sm, L, ksrc, vsrc, rec);
@@ -735,7 +749,7 @@ template <int G, int KB, int VB, int F>
 __global__ __launch_bounds__(256) void prefill_groups_kernel(Layout L, kvq_cache c, const half_t* k,
                                                              const half_t* v, int max_len,
                                                              const int32_t* seq_lens) {
-    __shared__ QuantSmem<G> sm;
+    __shared__ QSmem<G, F> sm;
     const int g = blockIdx.x;
     const int sh = blockIdx.y;
     const int b = sh / L.H, h = sh % L.H;
@@ -823,7 +837,7 @@ __device__ __forceinline__ AppendState append_state(const Layout& L, const kvq_c
 template <int G, int KB, int VB, int F>
 __global__ __launch_bounds__(256) void append_kernel(Layout L, kvq_cache c, const half_t* knew,
                                                      const half_t* vnew) {
-    __shared__ QuantSmem<G> sm;
+    __shared__ QSmem<G, F> sm;
     const int b = blockIdx.x, h = blockIdx.y;
     const AppendState a = append_state(L, c, b);
     if (!a.room) return;

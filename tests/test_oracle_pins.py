@@ -16,6 +16,8 @@ import subprocess
 import numpy as np
 import pytest
 
+from midpoint_extremes import MIDPOINT_EXTREMES
+
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
@@ -131,6 +133,39 @@ def test_ties_to_even_golden(orc):
     tok = np.concatenate([vals, np.full(123, 3.0)])
     c2, s2, z2 = orc.quantize_value_token(f16bits(tok), g["bits"])
     assert c2[:5].tolist() == g["expected_codes"]
+
+
+def _even_neighbour_of_midpoint(mn, mx, bits):
+    from fractions import Fraction
+    q = (Fraction(mx) - Fraction(mn)) / ((1 << bits) - 1)
+    lo = np.float16(float(q))
+    lo = lo if Fraction(float(lo)) < q else np.nextafter(lo, np.float16(-np.inf))
+    hi = np.nextafter(lo, np.float16(np.inf))
+    assert Fraction(float(lo)) < q < Fraction(float(hi)) and 2 * q == Fraction(float(lo)) + Fraction(float(hi))
+    return lo if int(lo.view(np.uint16)) % 2 == 0 else hi
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_scale_on_fp16_midpoint_goes_to_even(orc, bits):
+    """The scale is the fp16 rounding of (max - min) / (2^b - 1); for the
+    sets whose quotient lies exactly halfway between two fp16 numbers it is
+    the even one of the two (checked here in exact rational arithmetic)."""
+    for mn, mx in MIDPOINT_EXTREMES[bits]:
+        want = _even_neighbour_of_midpoint(mn, mx, bits)
+        x = np.linspace(mn, mx, 32)
+        x[0], x[-1] = mn, mx
+        if bits == 4:
+            _, s, z = orc.quantize_key_group(f16bits(np.tile(x[:, None], (1, 128))), bits)
+            assert np.all(s == want.view(np.uint16)) and np.all(orc.h2f(z) == np.float32(np.float16(mn)))
+            tok = np.concatenate([x, np.full(96, mn)])
+            _, sv, _ = orc.quantize_value_token(f16bits(tok), bits)
+            assert sv == want.view(np.uint16)
+        else:
+            tok = np.concatenate([x, np.full(96, mx)])
+            st = orc.StreamState.prefill(np.tile(f16bits(tok), (32, 1)), np.tile(f16bits(tok), (32, 1)),
+                                         8, 8, 32, 0, fmt=orc.FMT_INT8)
+            assert np.all(st.key_meta()[0] == want.view(np.uint16))
+            assert np.all(st.value_meta()[0] == want.view(np.uint16))
 
 
 def test_outlier_crowds_levels_golden(orc):
