@@ -32,6 +32,7 @@ struct QuantSmemU {
     uint16_t kmn[16][kD], kmx[16][kD];   // per token slice, per channel (fp16 bits)
     float kz[kD], kinv[kD];
     uint8_t vcode[G][kD];                 // value codes before packing
+    uint32_t vmeta[G];                    // image of the record's value scale/zero table
 };
 
 // Quantizer variants (compile-time): the 8-bit formats kFmtInt8 and kFmtFp8,
@@ -42,6 +43,20 @@ __host__ __device__ constexpr bool q_low_bit(int F) { return F == kQUniform || F
 // Shared memory of variant F.
 template <int G, int F>
 using QSmem = typename std::conditional<F == kQUniform || !q_low_bit(F), QuantSmemU<G>, QuantSmem<G>>::type;
+
+// 16 bytes of a source row, read once: a non-temporal load.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_once16(const half_t* p) {
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// A record word written once (non-temporal store).
+__device__ __forceinline__ void store_once(uint8_t* p, uint32_t w) { __builtin_nontemporal_store(w, (uint32_t*)p); }
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_once8(uint8_t* p, uint32_t a, uint32_t b) {
+    __builtin_nontemporal_store(u32x2{a, b}, (u32x2*)p);
+}
 
 __device__ __forceinline__ int wave_sum_i(int x) {
 #pragma unroll
@@ -149,8 +164,8 @@ __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* 
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
         const int t = ts + 16 * j;
-        const uint4 a = *(const uint4*)(ksrc + t * kD + 8 * cg);
-        const uint4 b = *(const uint4*)(vsrc + t * kD + 8 * cg);
+        const uint4 a = load_once16(ksrc + t * kD + 8 * cg);
+        const uint4 b = load_once16(vsrc + t * kD + 8 * cg);
         const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
         const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -238,10 +253,10 @@ __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* 
             w |= q << (KB == 4 ? code_bit(4, e) : code_bit(2, e + 8 * (cg & 1)));
         }
         if (KB == 4) {
-            *(uint32_t*)(rec + t * 64 + 4 * cg) = w;
+            store_once(rec + t * 64 + 4 * cg, w);
         } else {
             w |= __shfl_xor(w, 1);
-            if ((cg & 1) == 0) *(uint32_t*)(rec + t * 32 + 2 * cg) = w;
+            if ((cg & 1) == 0) store_once(rec + t * 32 + 2 * cg, w);
         }
         // value codes of the same token into LDS, channel order
         uint32_t v0 = 0, v1 = 0;
@@ -271,7 +286,7 @@ __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* 
             const int t = (slot >> 2) * 16 + 4 * g + (slot & 3);
             w |= (uint32_t)sm.vcode[t][16 * ct + n] << code_bit(VB, e);
         }
-        *(uint32_t*)(rec + L.vcode_off + vlane_byte(SPT * VB, lane, 4 * wi)) = w;
+        store_once(rec + L.vcode_off + vlane_byte(SPT * VB, lane, 4 * wi), w);
     }
     __syncthreads();  // LDS may be reused by the caller
 }
@@ -344,6 +359,11 @@ template <int G, int KB, int VB>
 __device__ void quantize_group_uniform(QuantSmemU<G>& sm, const Layout& L, const half_t* __restrict__ ksrc,
                                        const half_t* __restrict__ vsrc, uint8_t* __restrict__ rec) {
     constexpr int NT = G / 16;
+    // Metadata stores: with INT2 keys, non-temporal, the value table written
+    // as whole words from an LDS image; with INT4 keys, plain stores from the
+    // lanes that compute them (each the faster choice in same-box timing of
+    // the two layouts).
+    constexpr bool kMetaOnce = KB == 2;
     const int tid = threadIdx.x;
     const int cg = tid & 15;
     const int ts = tid >> 4;
@@ -352,8 +372,8 @@ __device__ void quantize_group_uniform(QuantSmemU<G>& sm, const Layout& L, const
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
         const int t = ts + 16 * j;
-        const uint4 a = *(const uint4*)(ksrc + t * kD + 8 * cg);
-        const uint4 b = *(const uint4*)(vsrc + t * kD + 8 * cg);
+        const uint4 a = load_once16(ksrc + t * kD + 8 * cg);
+        const uint4 b = load_once16(vsrc + t * kD + 8 * cg);
         kw[j][0] = a.x; kw[j][1] = a.y; kw[j][2] = a.z; kw[j][3] = a.w;
         vw[j][0] = b.x; vw[j][1] = b.y; vw[j][2] = b.z; vw[j][3] = b.w;
     }
@@ -383,8 +403,14 @@ __device__ void quantize_group_uniform(QuantSmemU<G>& sm, const Layout& L, const
         const int t = ts + 16 * j;
         if (cg == 0) {
             const int pos = vmeta_pos(L, t);
-            *(uint16_t*)(rec + pos) = p.s_bits;
-            *(uint16_t*)(rec + pos + 2 * L.spt) = p.z_bits;
+            if constexpr (kMetaOnce) {   // into the table's image; written out whole below
+                uint16_t* img = (uint16_t*)sm.vmeta;
+                img[(pos - L.vmeta_off) / 2] = p.s_bits;
+                img[(pos - L.vmeta_off) / 2 + L.spt] = p.z_bits;
+            } else {
+                *(uint16_t*)(rec + pos) = p.s_bits;
+                *(uint16_t*)(rec + pos + 2 * L.spt) = p.z_bits;
+            }
         }
         const float nz = -p.z, qv = (float)((1 << VB) - 1);
         uint32_t v0 = 0, v1 = 0;
@@ -407,8 +433,15 @@ __device__ void quantize_group_uniform(QuantSmemU<G>& sm, const Layout& L, const
         const QParams p = make_qparams(mn, mx, KB);
         sm.kz[tid] = -p.z;   // (negated: the fma's addend)
         sm.kinv[tid] = p.inv;
-        *(uint16_t*)(rec + L.kmeta_off + 2 * tid) = p.s_bits;
-        *(uint16_t*)(rec + L.kmeta_off + 2 * kD + 2 * tid) = p.z_bits;
+        if constexpr (kMetaOnce) {
+            __builtin_nontemporal_store(p.s_bits, (uint16_t*)(rec + L.kmeta_off + 2 * tid));
+            __builtin_nontemporal_store(p.z_bits, (uint16_t*)(rec + L.kmeta_off + 2 * kD + 2 * tid));
+        } else {
+            *(uint16_t*)(rec + L.kmeta_off + 2 * tid) = p.s_bits;
+            *(uint16_t*)(rec + L.kmeta_off + 2 * kD + 2 * tid) = p.z_bits;
+        }
+    } else if (kMetaOnce && tid < kD + G) {
+        __builtin_nontemporal_store(sm.vmeta[tid - kD], (uint32_t*)(rec + L.vmeta_off) + (tid - kD));
     }
     __syncthreads();
 
@@ -433,7 +466,7 @@ __device__ void quantize_group_uniform(QuantSmemU<G>& sm, const Layout& L, const
                 b = code_byte<0>(kw[j][i + 2], nzr[2 * i + 4], kir[2 * i + 4], qk, 2 * i, b);
                 b = code_byte<1>(kw[j][i + 2], nzr[2 * i + 5], kir[2 * i + 5], qk, 2 * i + 1, b);
             }
-            *(uint32_t*)(rec + t * 64 + 4 * cg) = a | (b << 4);
+            store_once(rec + t * 64 + 4 * cg, a | (b << 4));
         } else {
             // even codes (channel 2i: low halves) and odd codes (high halves),
             // nibble e of the half word; this thread's 8 codes are codes
@@ -446,7 +479,7 @@ __device__ void quantize_group_uniform(QuantSmemU<G>& sm, const Layout& L, const
             }
             uint32_t w = (ev | (od << 4)) << (2 * (cg & 1));
             w |= __shfl_xor(w, 1);
-            if ((cg & 1) == 0) *(uint32_t*)(rec + t * 32 + 2 * cg) = w;
+            if ((cg & 1) == 0) store_once(rec + t * 32 + 2 * cg, w);
         }
     }
     __syncthreads();
@@ -468,7 +501,7 @@ __device__ void quantize_group_uniform(QuantSmemU<G>& sm, const Layout& L, const
             const int t = (slot >> 2) * 16 + 4 * g + (slot & 3);
             w |= (uint32_t)sm.vcode[t][16 * ct + n] << code_bit(VB, e);
         }
-        *(uint32_t*)(rec + L.vcode_off + vlane_byte(SPT * VB, lane, 4 * wi)) = w;
+        store_once(rec + L.vcode_off + vlane_byte(SPT * VB, lane, 4 * wi), w);
     }
     __syncthreads();  // LDS may be reused by the caller
 }
@@ -500,8 +533,8 @@ __device__ void quantize_pair16(QuantSmemPair& sm, const Layout& L, const half_t
         const int t = ts + 16 * j;
         uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
         if (recs[j]) {
-            a = *(const uint4*)(ksrc + t * kD + 8 * cg);
-            b = *(const uint4*)(vsrc + t * kD + 8 * cg);
+            a = load_once16(ksrc + t * kD + 8 * cg);
+            b = load_once16(vsrc + t * kD + 8 * cg);
         }
         kw[j][0] = a.x; kw[j][1] = a.y; kw[j][2] = a.z; kw[j][3] = a.w;
         vw[j][0] = b.x; vw[j][1] = b.y; vw[j][2] = b.z; vw[j][3] = b.w;
@@ -576,7 +609,7 @@ __device__ void quantize_pair16(QuantSmemPair& sm, const Layout& L, const half_t
                 b = code_byte<0>(kw[j][i + 2], nzr[2 * i + 4], kir[2 * i + 4], qk, 2 * i, b);
                 b = code_byte<1>(kw[j][i + 2], nzr[2 * i + 5], kir[2 * i + 5], qk, 2 * i + 1, b);
             }
-            if (recs[j]) *(uint32_t*)(recs[j] + ts * 64 + 4 * cg) = a | (b << 4);
+            if (recs[j]) store_once(recs[j] + ts * 64 + 4 * cg, a | (b << 4));
         } else {
             uint32_t ev = 0, od = 0;
 #pragma unroll
@@ -586,7 +619,7 @@ __device__ void quantize_pair16(QuantSmemPair& sm, const Layout& L, const half_t
             }
             uint32_t w = (ev | (od << 4)) << (2 * (cg & 1));
             w |= __shfl_xor(w, 1);
-            if ((cg & 1) == 0 && recs[j]) *(uint32_t*)(recs[j] + ts * 32 + 2 * cg) = w;
+            if ((cg & 1) == 0 && recs[j]) store_once(recs[j] + ts * 32 + 2 * cg, w);
         }
     }
 
@@ -607,7 +640,7 @@ __device__ void quantize_pair16(QuantSmemPair& sm, const Layout& L, const half_t
             const int t = 4 * g + slot;
             w |= (uint32_t)sm.vcode[16 * j + t][16 * ct + n] << code_bit(VB, e);
         }
-        if (recs[j]) *(uint32_t*)(recs[j] + L.vcode_off + vlane_byte(SPT * VB, lane, 4 * wi)) = w;
+        if (recs[j]) store_once(recs[j] + L.vcode_off + vlane_byte(SPT * VB, lane, 4 * wi), w);
     }
     __syncthreads();  // LDS may be reused by the caller
 }
@@ -630,8 +663,8 @@ __device__ void quantize_group8(QuantSmemU<G>& sm, const Layout& L, const half_t
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
         const int t = ts + 16 * j;
-        const uint4 a = *(const uint4*)(ksrc + t * kD + 8 * cg);
-        const uint4 b = *(const uint4*)(vsrc + t * kD + 8 * cg);
+        const uint4 a = load_once16(ksrc + t * kD + 8 * cg);
+        const uint4 b = load_once16(vsrc + t * kD + 8 * cg);
         const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
         const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
         uint32_t kw[2], vw[2];
@@ -684,7 +717,7 @@ __device__ void quantize_group8(QuantSmemU<G>& sm, const Layout& L, const half_t
                 vw[h] = fp8_code2(vx[4 * h], vx[4 * h + 1], vinv) | fp8_code2(vx[4 * h + 2], vx[4 * h + 3], vinv) << 16;
             }
         }
-        *(uint2*)(rec + k8_byte(t, 8 * cg)) = make_uint2(kw[0], kw[1]);
+        store_once8(rec + k8_byte(t, 8 * cg), kw[0], kw[1]);
         *(uint2*)&sm.vcode[t][8 * cg] = make_uint2(vw[0], vw[1]);
     }
     __syncthreads();
@@ -705,7 +738,7 @@ __device__ void quantize_group8(QuantSmemU<G>& sm, const Layout& L, const half_t
             const int t = (slot >> 2) * 16 + 4 * g + (slot & 3);
             w |= (uint32_t)sm.vcode[t][16 * ct + n] << (8 * e);
         }
-        *(uint32_t*)(rec + L.vcode_off + vlane_byte(SPT * 8, lane, 4 * wi)) = w;
+        store_once(rec + L.vcode_off + vlane_byte(SPT * 8, lane, 4 * wi), w);
     }
     __syncthreads();  // LDS may be reused by the caller
 }
