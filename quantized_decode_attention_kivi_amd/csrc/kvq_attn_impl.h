@@ -75,6 +75,12 @@ __device__ __forceinline__ float group_max(float x) {
     auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
     return fmaxf(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
 }
+// x(l) + x(l ^ 32): the first step of group_sum.
+__device__ __forceinline__ float add_group_pairs(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (uint32_t)a[0]) + __builtin_bit_cast(float, (uint32_t)a[1]);
+}
 __device__ __forceinline__ float group_sum(float x) {
     const uint32_t u = __builtin_bit_cast(uint32_t, x);
     auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
@@ -1233,9 +1239,26 @@ __device__ __forceinline__ void process_residual(WaveAcc& A, const Layout& L, co
 }
 
 // A wave's [16][128] fp32 accumulator image after the unit loop.
+// Rows of a wave's accumulator image: limb-packed waves add the low-limb
+// rows (head hh + 8) to the high ones in registers before writing it, token
+// packing also the second token tile (hh + 4), so that the image holds one
+// row per head.
+template <bool LP, bool TP>
+constexpr int acc_rows() { return TP ? 4 : LP ? 8 : 16; }
+// Images per stage array (kWaves * pitch bytes): 4 (all in stage_a) or 2.
+template <int ROWS>
+constexpr int acc_per_array(int pitch) { return kWaves * pitch / (ROWS * kD * 4) >= kWaves ? kWaves : 2; }
+template <int ROWS>
 __device__ __forceinline__ float* wave_acc(uint8_t* stage_a, uint8_t* stage_b, int w, int pitch) {
-    return (float*)((w < 2 ? stage_a : stage_b) + (w & 1) * 16 * kD * 4);
+    const int per = acc_per_array<ROWS>(pitch);
+    return (float*)((w < per ? stage_a : stage_b) + (w % per) * ROWS * kD * 4);
 }
+
+// The workgroup reduction's per-wave totals (running max, weight sum, sum of
+// p z per head); the kernel's prologue uses the same memory for its scan.
+struct WaveRed {
+    float m[kWaves][16], l[kWaves][16], pz[kWaves][16];
+};
 
 // Wave priority from the share of this wave's units still to do (3: more
 // than 3/4 left ... 0: under 1/4).  Waves issue oldest-first, so without
@@ -1316,9 +1339,7 @@ __device__ __forceinline__ void process_any(const lds_u8* buf, uint32_t has, Wav
 // `part`.  Called by every thread of the workgroup.
 template <int G, int KB, int VB, int F, bool LP, bool TP, bool PG, int NS>
 __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_b, uint8_t* stage_c, uint8_t* stage_d,
-                                               float (*wm)[16],
-                                               float (*wl)[16],
-                                               float (*wpz)[16], const Layout& L, const kvq_cache& c,
+                                               WaveRed* red, const Layout& L, const kvq_cache& c,
                                                const half_t* __restrict__ q, float sl2, int gq, int b, int h,
                                                const SeqUnits& su, int lo, int hi, float* __restrict__ part,
                                                int lane, int wave, RopeLds* R, SparseLds* SPL) {
@@ -1491,16 +1512,27 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
     const float lh = TP ? lt + __shfl(lt, (lane + 4) & 15) : lt;
     const float pzh = TP ? pzt + __shfl(pzt, (lane + 4) & 15) : pzt;
     if (lane < 16) {
-        wm[wave][lane] = A.m;
-        wl[wave][lane] = lh;
-        wpz[wave][lane] = pzh;
+        red->m[wave][lane] = A.m;
+        red->l[wave][lane] = lh;
+        red->pz[wave][lane] = pzh;
     }
     {
-        float* wacc = wave_acc(stage_a, stage_b, wave, S::PITCH);
+        // LP: row 4g + i + 8 (lane group g + 2) onto row 4g + i; TP: all
+        // four lane groups onto group 0
+        constexpr int ROWS = acc_rows<LP, TP>();
+        if constexpr (LP) {
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
+            for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wacc[(4 * g + i) * kD + 16 * ct + n16] = A.acc[ct][i];
+                for (int i = 0; i < 4; ++i) A.acc[ct][i] = TP ? group_sum(A.acc[ct][i]) : add_group_pairs(A.acc[ct][i]);
+        }
+        float* wacc = wave_acc<ROWS>(stage_a, stage_b, wave, S::PITCH);
+        if (4 * g < ROWS) {
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) wacc[(4 * g + i) * kD + 16 * ct + n16] = A.acc[ct][i];
+        }
     }
     __syncthreads();
 
@@ -1509,19 +1541,15 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
         const int hh = idx >> 7, ch = idx & (kD - 1);
         float M = kNegInf;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w][hh]);
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red->m[w][hh]);
         float o = 0.0f, Ls = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float mw = wm[w][hh];
+            const float mw = red->m[w][hh];
             const float f = mw == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-            // LP: rows hh and hh+8 hold the high- and low-limb sums of head hh
-            // (TP: rows hh + 4 and hh + 12 its second token tile)
-            const float* wacc = wave_acc(stage_a, stage_b, w, S::PITCH);
-            float a = LP ? wacc[hh * kD + ch] + wacc[(hh + 8) * kD + ch] : wacc[hh * kD + ch];
-            if (TP) a += wacc[(hh + 4) * kD + ch] + wacc[(hh + 12) * kD + ch];
-            o += (a + wpz[w][hh]) * f;
-            Ls += wl[w][hh] * f;
+            const float a = wave_acc<acc_rows<LP, TP>()>(stage_a, stage_b, w, S::PITCH)[hh * kD + ch];
+            o += (a + red->pz[w][hh]) * f;
+            Ls += red->l[w][hh] * f;
         }
         part[hh * kPart + ch] = o;
         if (ch == 0) {
@@ -1569,7 +1597,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves(
     using S = StageT<G, KB, VB, F>;
     // Two stage buffers per wave (ping-pong), in two arrays: the compiler
     // treats them as separate objects.  After the unit loop the same memory
-    // holds the waves' accumulators (waves 0-1 in stage_a, 2-3 in stage_b).
+    // holds the waves' accumulator images (all four in stage_a when they are
+    // 4 KB, as with limb packing; else waves 0-1 in stage_a, 2-3 in stage_b).
     __shared__ __attribute__((aligned(16))) uint8_t stage_a[kWaves * S::PITCH];
     __shared__ __attribute__((aligned(16))) uint8_t stage_b[kWaves * S::PITCH];
     constexpr int NS = attn_stages(G, KB, VB, F);
@@ -1583,9 +1612,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves(
         __shared__ __attribute__((aligned(16))) uint8_t stage_d_lds[kWaves * S::PITCH];
         stage_d = stage_d_lds;
     }
-    __shared__ float wm[kWaves][16], wl[kWaves][16], wpz[kWaves][16];
-    __shared__ int wsum[kWaves];
-    __shared__ int first[2];   // sequence holding unit w T / nwg, flattened start of that sequence
+    // The reduction totals: in stage_b where all four accumulator images fit
+    // in stage_a (limb-packed kernels; their workgroups then take
+    // 2 * kWaves * PITCH bytes of LDS), else an array of their own.
+    WaveRed* red;
+    if constexpr (acc_per_array<acc_rows<LP, TP>()>(S::PITCH) == kWaves) {
+        static_assert(sizeof(WaveRed) <= kWaves * S::PITCH, "reduction totals fit a stage array");
+        red = (WaveRed*)stage_b;
+    } else {
+        __shared__ WaveRed red_lds;
+        red = &red_lds;
+    }
+    int* const wsum = (int*)red;            // [kWaves]
+    int* const first = wsum + kWaves;       // sequence holding unit w T / nwg, flattened start of that sequence
     const int w = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1647,6 +1686,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves(
 
     int b = __builtin_amdgcn_readfirstlane(first[0]);
     const int pb = __builtin_amdgcn_readfirstlane(first[1]);
+    __syncthreads();   // first[] read by every wave before stage buffers (which may hold it) are written
     SeqUnits su = seq_units(L, c, b);
     // (the division runs on the vector ALU: bring the result back to a scalar
     // register, or everything derived from it becomes per-lane)
@@ -1662,7 +1702,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves(
             asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l0));
             if (l0 == 0) meta[1 + s] = ps;
         }
-        attend_segment<G, KB, VB, F, LP, TP, PG, NS>(stage_a, stage_b, stage_c, stage_d, wm, wl, wpz, L, c, q, sl2, gq, b, h, su,
+        attend_segment<G, KB, VB, F, LP, TP, PG, NS>(stage_a, stage_b, stage_c, stage_d, red, L, c, q, sl2, gq, b, h, su,
                                           unit_at(su, lo), unit_at(su, hi), ws + ((long)w + s) * gq * kPart,
                                           lane, wave, R, SPL);
         if (ps + hi >= end) break;
