@@ -147,6 +147,13 @@ typedef struct kvq_cache {
                                    positive and finite (caller-calibrated, e.g.
                                    max |k| / 448); ignored by other formats      */
     const float *v_scale;       /* FP8 format: [H] static value scale, likewise  */
+    int32_t *arrivals;          /* optional [B] int32 (counter_bytes), 4-byte
+                                   aligned: zero before the first
+                                   kv_append_token (kv_quantize_prefill zeroes
+                                   it) and left zero by the library.  With it an
+                                   append is one kernel, whose last workgroup of
+                                   each sequence advances that sequence's
+                                   counters; NULL: a second kernel does that     */
 } kvq_cache;
 
 /* Byte sizes of the buffers of kvq_cache and of one group record.
@@ -162,7 +169,7 @@ typedef struct kvq_sizes {
     size_t packed_bytes;
     size_t record_bytes;
     size_t residual_bytes;     /* each of k_res and v_res                        */
-    size_t counter_bytes;      /* each of n_tokens and n_quant                   */
+    size_t counter_bytes;      /* each of n_tokens, n_quant and arrivals         */
     size_t block_table_bytes;  /* paged mode only, else 0                        */
     int32_t groups_per_seq;    /* key groups one sequence can hold               */
     int32_t residual_slots;    /* R + G                                          */
@@ -191,7 +198,11 @@ kvq_status kv_quantize_prefill(const kvq_config *cfg, const kvq_cache *cache,
  * tail holds R + G tokens its oldest G tokens form a full group outside the
  * most recent R, which is quantized into a record and leaves the ring).
  * k_new, v_new: fp16 [B][H][d].  n_tokens and n_quant are updated on the
- * device, so a sequence of appends needs no host synchronisation.
+ * device, so a sequence of appends needs no host synchronisation: by the
+ * append kernel itself when cache->arrivals is given (the last of a
+ * sequence's kv-head workgroups to finish, counted by an agent-scope atomic
+ * on arrivals[b], advances the counters once every head has read them, and
+ * resets the count), else by a second one-thread-per-sequence kernel.
  * Preconditions (caller): n + 1 within capacity; in paged mode
  * block_table[b][n_q/G] holds a free block before the append that flushes.
  * A flush that would leave the buffers is skipped (no write) and the token is

@@ -150,6 +150,7 @@ kvq_status make_layout(const kvq_config* cfg, Layout* L) {
 
 static kvq_status check_cache(const Layout& L, const kvq_cache* c) {
     if (!c || !c->packed || !c->k_res || !c->v_res || !c->n_tokens || !c->n_quant) return KVQ_EINVAL;
+    if ((uintptr_t)c->arrivals & 3) return KVQ_EINVAL;
     if (L.paged && !c->block_table) return KVQ_EINVAL;
     if (((uintptr_t)c->packed & 15) || ((uintptr_t)c->k_res & 15) || ((uintptr_t)c->v_res & 15))
         return KVQ_EINVAL;

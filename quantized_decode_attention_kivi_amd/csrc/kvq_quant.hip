@@ -836,6 +836,7 @@ __global__ __launch_bounds__(256) void prefill_tail_kernel(Layout L, kvq_cache c
     if (h == 0 && threadIdx.x == 0) {
         c.n_tokens[b] = n;
         c.n_quant[b] = nq;
+        if (c.arrivals) c.arrivals[b] = 0;
     }
 }
 
@@ -865,15 +866,19 @@ __device__ __forceinline__ AppendState append_state(const Layout& L, const kvq_c
 // Append: grid (B, H), one workgroup per (sequence, kv head), so the heads'
 // flushes run side by side.  The new token goes into the ring; on a flush
 // the oldest G ring tokens (the new one among them when R = 0) are quantized
-// into the group's record.  The counters are read here by every head and
-// advanced afterwards by append_counters_kernel.
+// into the group's record.  Every head reads the counters first; they then
+// advance (n + 1, and n_q + G when the group was flushed: it has a record,
+// which exists for every head or for none) once all heads of the sequence
+// have read them: with c.arrivals, by the last of the sequence's workgroups
+// to arrive (an agent-scope atomic counter that it resets), else by
+// append_counters_kernel after this kernel.
 template <int G, int KB, int VB, int F>
 __global__ __launch_bounds__(256) void append_kernel(Layout L, kvq_cache c, const half_t* knew,
                                                      const half_t* vnew) {
     __shared__ QSmem<G, F> sm;
     const int b = blockIdx.x, h = blockIdx.y;
     const AppendState a = append_state(L, c, b);
-    if (!a.room) return;
+    if (!a.room) return;   // (the same for every head of b: none arrives)
     const long sh = (long)b * L.H + h;
     if (threadIdx.x < 64) {
         const int slot = a.n % L.ring;
@@ -882,17 +887,29 @@ __global__ __launch_bounds__(256) void append_kernel(Layout L, kvq_cache c, cons
         ((uint32_t*)c.v_res)[(sh * L.ring + slot) * (kD / 2) + threadIdx.x] =
             ((const uint32_t*)vnew)[sh * (kD / 2) + threadIdx.x];
     }
-    if (!a.flush) return;
-    uint8_t* rec = record_at(L, c.packed, c.block_table, b, h, a.nq / G);
-    if (!rec) return;   // (no block for the group: the counters do not advance it either)
-    __syncthreads();    // the new token's row is visible to the whole workgroup
-    const long row = (sh * L.ring + (a.nq % L.ring)) * kD;
-    quantize_any<G, KB, VB, F>(sm, L, c, h, (const half_t*)c.k_res + row, (const half_t*)c.v_res + row, rec);
+    uint8_t* rec = a.flush ? record_at(L, c.packed, c.block_table, b, h, a.nq / G) : nullptr;
+    if (rec) {   // (no block for the group: the counters do not advance it either)
+        __syncthreads();   // the new token's row is visible to the whole workgroup
+        const long row = (sh * L.ring + (a.nq % L.ring)) * kD;
+        quantize_any<G, KB, VB, F>(sm, L, c, h, (const half_t*)c.k_res + row, (const half_t*)c.v_res + row, rec);
+    }
+    if (!c.arrivals) return;
+    __syncthreads();   // every thread of this workgroup has read the counters
+    if (threadIdx.x == 0) {
+        // (relaxed: the other heads' counter reads completed before their
+        // arrivals, and no data of theirs is read here)
+        const int before = __hip_atomic_fetch_add(&c.arrivals[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (before == L.H - 1) {   // every head of b has read the counters
+            __hip_atomic_store(&c.arrivals[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const bool flushed = a.flush && record_at(L, c.packed, c.block_table, b, 0, a.nq / L.G) != nullptr;
+            c.n_tokens[b] = a.n + 1;
+            c.n_quant[b] = a.nq + (flushed ? L.G : 0);
+        }
+    }
 }
 
-// Counters after an append (one thread per sequence, after append_kernel):
-// n + 1, and n_q + G when the group was flushed (it has a record; the record
-// exists for every head or for none).
+// Counters after an append without c.arrivals (one thread per sequence,
+// after append_kernel): as above.
 __global__ __launch_bounds__(256) void append_counters_kernel(Layout L, kvq_cache c) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= L.B) return;
@@ -1079,7 +1096,7 @@ hipError_t launch_append(const Layout& L, const kvq_cache& c, const half_t* k, c
 #undef KVQ_AP
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(append_counters_kernel, dim3((L.B + 255) / 256), dim3(256), 0, s, L, c);
+    if (!c.arrivals) hipLaunchKernelGGL(append_counters_kernel, dim3((L.B + 255) / 256), dim3(256), 0, s, L, c);
     return hipGetLastError();
 }
 

@@ -40,7 +40,8 @@ class kvq_config(ctypes.Structure):
 class kvq_cache(ctypes.Structure):
     _fields_ = [("packed", ctypes.c_void_p), ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
                 ("n_tokens", ctypes.c_void_p), ("n_quant", ctypes.c_void_p),
-                ("block_table", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+                ("block_table", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("arrivals", ctypes.c_void_p)]
 
 
 class kvq_sizes(ctypes.Structure):
@@ -247,6 +248,8 @@ class QuantizedKVCache:
         self.v_res = torch.zeros(sz.residual_bytes // 2, dtype=torch.float16, device=self.device)
         self.n_tokens = torch.zeros(shape.num_seqs, dtype=torch.int32, device=self.device)
         self.n_quant = torch.zeros(shape.num_seqs, dtype=torch.int32, device=self.device)
+        # per-sequence arrival counters of the append kernel (kept zero by the library)
+        self.arrivals = torch.zeros(shape.num_seqs, dtype=torch.int32, device=self.device)
         self.block_table = None
         if shape.paged:
             self.block_table = torch.full((shape.num_seqs, shape.max_blocks_per_seq), -1, dtype=torch.int32,
@@ -271,7 +274,8 @@ class QuantizedKVCache:
                          self.n_tokens.data_ptr(), self.n_quant.data_ptr(),
                          self.block_table.data_ptr() if self.block_table is not None else None,
                          self.k_scale.data_ptr() if self.k_scale is not None else None,
-                         self.v_scale.data_ptr() if self.v_scale is not None else None)
+                         self.v_scale.data_ptr() if self.v_scale is not None else None,
+                         self.arrivals.data_ptr())
 
     def sequence_view(self, b: int) -> "QuantizedKVCache":
         """Read-only cache of sequence b alone, sharing this cache's memory.
@@ -300,6 +304,7 @@ class QuantizedKVCache:
         v.v_res = self.v_res[b * per_ring:(b + 1) * per_ring]
         v.n_tokens = self.n_tokens[b:b + 1]
         v.n_quant = self.n_quant[b:b + 1]
+        v.arrivals = self.arrivals[b:b + 1]
         v.block_table = self.block_table[b:b + 1] if self.block_table is not None else None
         v.lens = self.lens[b:b + 1].copy()
         v.k_scale, v.v_scale = self.k_scale, self.v_scale
@@ -332,6 +337,7 @@ class QuantizedKVCache:
         v.v_res = self.v_res[s * per_ring:(s + 1) * per_ring]
         v.n_tokens = self.n_tokens[b:b + 1]
         v.n_quant = self.n_quant[b:b + 1]
+        v.arrivals = self.arrivals[b:b + 1]
         v.block_table = None
         v.lens = self.lens[b:b + 1].copy()
         v.k_scale = self.k_scale[h:h + 1] if self.k_scale is not None else None

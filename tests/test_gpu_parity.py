@@ -86,12 +86,15 @@ def test_edge_lengths_in_one_batch():
     compare_attention(out, ref)
 
 
-@pytest.mark.parametrize("case", ["gqa4_int4_ragged", "gqa16_k4v2_g16", "mha_g32_r0", "paged_k4v2_g16"])
-def test_append_sequence_matches_prefill(case):
+@pytest.mark.parametrize("case,arrivals", [("gqa4_int4_ragged", True), ("gqa16_k4v2_g16", True),
+                                           ("mha_g32_r0", True), ("paged_k4v2_g16", True),
+                                           ("gqa4_int4_ragged", False), ("paged_k4v2_g16", False)])
+def test_append_sequence_matches_prefill(case, arrivals):
     """prefill(m) followed by appends that cross several flushes must equal
     the oracle's incremental state, step by step (paged: each flush's block
     is handed out from a shuffled pool and written into the device table
-    between calls)."""
+    between calls).  arrivals: the counters advance inside the append kernel
+    (per-sequence arrival counts, left zero), else in a second kernel."""
     w = SMALL[case]
     m = 300 if w.residual < 300 else w.residual + 5
     steps = 3 * w.group_size + 7
@@ -99,6 +102,8 @@ def test_append_sequence_matches_prefill(case):
     lens0[-1] = max(0, m - 17)  # ragged
     K, V = synth.make_kv(w, max_len=m + steps, device="cuda")
     cache = make_cache(w, lens0 + steps + 1, max_tokens=m + steps + 8, shuffle_seed=5)
+    if not arrivals:
+        cache.cache.arrivals = None
     cache.prefill(K[:, :, :m].contiguous(), V[:, :, :m].contiguous(), lens0)
     kb, vb = to_bits(K), to_bits(V)
     states = oracle_states(kb[:, :, :m], vb[:, :, :m], lens0, w, cap=m + steps + 8)
@@ -112,6 +117,7 @@ def test_append_sequence_matches_prefill(case):
         lens0 += 1
         if s % 16 == 15 or s == steps - 1:
             compare_codes(cache, states)
+    assert not cache.arrivals.any()
     q = synth.make_query(w, device="cuda", step=3)
     out = cache.decode_attention(q, SCALE)
     torch.cuda.synchronize()
