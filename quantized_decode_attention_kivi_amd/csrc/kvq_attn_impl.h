@@ -232,11 +232,13 @@ __device__ __forceinline__ u32x4 record_desc(const uint8_t* rec, int bytes) {
 // own for the LDS write (it cannot tell the two stage buffers apart and would
 // drain the prefetch); the kernel waits explicitly before reading a buffer.
 // The load carries the non-temporal policy (nt): the cache is read once per
-// call (7-12 % faster on the INT4 and paged layers).  Loads that read a line
-// in pieces spread over several instructions lose with it (8-bit codes read
-// at a 32- or 64-byte lane stride: INT8 layer 106 -> 145 us), which is why
-// the 8-bit records store their codes in 16-byte pieces, so that every load
-// here reads whole lines.
+// call (7-12 % faster on the INT4 and paged layers).  With it, lanes of 64
+// bytes read 16 bytes at a time (each load touching a quarter of every line
+// it reaches) were much slower (8-bit G = 32 layout before its codes were
+// stored in 16-byte chunks: INT8 layer 106 -> 145 us); lanes of 32 bytes read
+// in two halves are not (INT4 values at G = 32; 8-bit values at G = 16:
+// INT8 and FP8 8 x 32K layers at G = 16, 89.5 and 84.1 us with nt, 89.4 and
+// 84.7 us without, same box).
 __device__ __forceinline__ void lds_load16(u32x4 desc, lds_u8* dst, int off) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
     asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(off), "s"(desc), "{m0}"(m0) : "memory");

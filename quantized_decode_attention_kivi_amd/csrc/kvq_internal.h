@@ -86,7 +86,6 @@ struct Layout {
 // Fills *L from cfg; returns KVQ_OK or the validation error.
 kvq_status make_layout(const kvq_config* cfg, Layout* L);
 
-// Largest n_q a sequence may reach.
 // Offset inside the key codes of the 8-bit formats of the byte of token t,
 // channel c.
 __host__ __device__ inline int k8_byte(int t, int c) {
@@ -98,6 +97,8 @@ __host__ __device__ inline int vlane_byte(int lane_bytes, int lane, int b) {
     return lane_bytes <= 32 ? lane * lane_bytes + b : 1024 * (b >> 4) + 16 * lane + (b & 15);
 }
 
+// Quantized tokens of a sequence holding n: whole groups outside the
+// newest R tokens.
 __host__ __device__ inline int num_quantized(int n, int G, int R) {
     int over = n - R;
     return over <= 0 ? 0 : G * (over / G);
