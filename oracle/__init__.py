@@ -63,6 +63,8 @@ def lib():
             L.orc_f2h_array.argtypes = [_f32p, _u16p, ctypes.c_long]
             L.orc_num_quantized.restype = ctypes.c_int
             L.orc_num_quantized.argtypes = [ctypes.c_int] * 3
+            L.orc_num_quantized8.restype = ctypes.c_int
+            L.orc_num_quantized8.argtypes = [ctypes.c_int] * 3
             L.orc_quantize_key_group.argtypes = [_u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                  _u8p, _u16p, _u16p]
             L.orc_quantize_value_token.argtypes = [_u16p, ctypes.c_int, ctypes.c_int,
@@ -221,7 +223,11 @@ def quantize_value_token_cb(x_bits: np.ndarray, bits: int, levels=None):
                                       _p(s, _u16p), _p(z, _u16p))
     return codes, int(s[0]), int(z[0])
 
-def num_quantized(n: int, G: int, R: int) -> int:
+def num_quantized(n: int, G: int, R: int, fmt: int = 0) -> int:
+    """Quantized tokens of a stream holding n (fmt: FMT_KIVI, or an 8-bit
+    format, whose streams with R = 0 quantize every token on write)."""
+    if fmt:
+        return int(lib().orc_num_quantized8(int(n), int(G), int(R)))
     return int(lib().orc_num_quantized(int(n), int(G), int(R)))
 
 

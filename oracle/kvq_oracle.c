@@ -631,9 +631,12 @@ void orc_dequantize_stream_ds(const uint16_t *k, const uint16_t *v, int n, int n
 /* 8-bit KV formats ([P1] section 3.1: FP8 E4M3 with a static per-tensor or  */
 /* per-head scale, or INT8 with a dynamic per-token scale, dequantized by    */
 /* the attention kernel as it reads; [P2] part B.1: FP8 and INT8 hold the    */
-/* cache at half the fp16 bytes).  Both keep the residual window and group   */
-/* bookkeeping of the low-bit format: tokens [0, n_q) are quantized, every   */
-/* token on its own (no per-channel key groups).                             */
+/* cache at half the fp16 bytes).  Tokens [0, n_q) are quantized, every      */
+/* token on its own (no per-channel key groups).  With no residual window    */
+/* (R = 0) every token is quantized as it is written, n_q = n: a per-token   */
+/* quantizer needs no group to be complete, and the pages' 8-bit cache      */
+/* stores each token in 8 bits.  With R > 0 the low-bit format's residual    */
+/* window and group flushes apply.                                           */
 /* ------------------------------------------------------------------------ */
 
 #define ORC_FMT_INT8 1
@@ -715,6 +718,13 @@ static void quantize_token8(int fmt, const uint16_t *x, int d, float scale,
     }
 }
 
+/* Quantized tokens of an 8-bit stream holding n tokens (see above). */
+int orc_num_quantized8(int n, int G, int R)
+{
+    if (R == 0) return n > 0 ? n : 0;
+    return orc_num_quantized(n, G, R);
+}
+
 /* Whole-stream quantization in an 8-bit format (fmt 1 = INT8 per token,
  * 2 = FP8 E4M3 with static scales kscale / vscale of this kv head).
  * k, v: [n][d]; kcodes, vcodes: [n_q][d]; ks, kz, vs, vz: [n_q] (INT8 only,
@@ -724,7 +734,7 @@ int orc_prefill_stream8(int fmt, const uint16_t *k, const uint16_t *v, int n, in
                         uint8_t *kcodes, uint16_t *ks, uint16_t *kz,
                         uint8_t *vcodes, uint16_t *vs, uint16_t *vz)
 {
-    int nq = orc_num_quantized(n, G, R);
+    int nq = orc_num_quantized8(n, G, R);
     for (int t = 0; t < nq; ++t) {
         quantize_token8(fmt, k + (long)t * d, d, kscale, kcodes + (long)t * d, ks + t, kz + t);
         quantize_token8(fmt, v + (long)t * d, d, vscale, vcodes + (long)t * d, vs + t, vz + t);
@@ -732,8 +742,10 @@ int orc_prefill_stream8(int fmt, const uint16_t *k, const uint16_t *v, int n, in
     return nq;
 }
 
-/* Incremental form of orc_prefill_stream8, with the same flush rule as
- * orc_append_stream (the oldest G tail tokens once the tail holds R + G). */
+/* Incremental form of orc_prefill_stream8: with R = 0 the new token is
+ * quantized at once; otherwise the same flush rule as orc_append_stream (the
+ * oldest G tail tokens once the tail holds R + G).  Returns 1 when tokens
+ * were quantized. */
 int orc_append_stream8(int fmt, uint16_t *hist_k, uint16_t *hist_v, int cap, int *n, int *nq,
                        const uint16_t *k_new, const uint16_t *v_new, int d, int G, int R,
                        float kscale, float vscale,
@@ -744,6 +756,13 @@ int orc_append_stream8(int fmt, uint16_t *hist_k, uint16_t *hist_v, int cap, int
     memcpy(hist_k + (long)(*n) * d, k_new, sizeof(uint16_t) * d);
     memcpy(hist_v + (long)(*n) * d, v_new, sizeof(uint16_t) * d);
     *n += 1;
+    if (R == 0) {
+        int t = *n - 1;
+        quantize_token8(fmt, hist_k + (long)t * d, d, kscale, kcodes + (long)t * d, ks + t, kz + t);
+        quantize_token8(fmt, hist_v + (long)t * d, d, vscale, vcodes + (long)t * d, vs + t, vz + t);
+        *nq = *n;
+        return 1;
+    }
     if (*n - *nq == R + G) {
         for (int t = *nq; t < *nq + G; ++t) {
             quantize_token8(fmt, hist_k + (long)t * d, d, kscale, kcodes + (long)t * d, ks + t, kz + t);
@@ -786,7 +805,7 @@ void orc_dequantize_stream8(int fmt, const uint16_t *k, const uint16_t *v, int n
  * stream, and are not counted. */
 double orc_stream_bytes8(int fmt, long n, int d, int G, int R)
 {
-    long nq = orc_num_quantized((int)n, G, R);
+    long nq = orc_num_quantized8((int)n, G, R);
     double codes = (double)nq * d * 2.0;
     double meta = fmt == ORC_FMT_INT8 ? (double)nq * 8.0 : 0.0;
     double resid = (double)(n - nq) * d * 2.0 * 2.0;

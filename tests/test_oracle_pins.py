@@ -529,7 +529,7 @@ def test_fp8_roundtrip_bound_and_saturation(orc, G, R):
     st = orc.StreamState.prefill(k.view(np.uint16), v.view(np.uint16), 8, 8, G, R,
                                  fmt=orc.FMT_FP8, kscale=ks, vscale=vs)
     nq = st.nq
-    assert nq == orc.num_quantized(n, G, R)
+    assert nq == orc.num_quantized(n, G, R, orc.FMT_FP8) == (n if R == 0 else orc.num_quantized(n, G, R))
     kh, vh = st.dequantize()
     for x16, xh, sc in ((k, kh, ks), (v, vh, vs)):
         x = x16[:nq].astype(np.float64)
@@ -633,7 +633,8 @@ def test_8bit_prefill_equals_prefill_plus_appends(orc, fmt, G, R):
     inc = orc.StreamState.prefill(kb[:m], vb[:m], 8, 8, G, R, cap=n_total, **kw)
     for t in range(m, n_total):
         inc.append(kb[t], vb[t])
-        assert inc.nq == orc.num_quantized(inc.n, G, R)
+        assert inc.nq == orc.num_quantized(inc.n, G, R, fmt)
+        assert inc.nq == (inc.n if R == 0 else orc.num_quantized(inc.n, G, R))
     assert inc.n == full.n and inc.nq == full.nq
     assert np.array_equal(inc.key_codes(), full.key_codes())
     assert np.array_equal(inc.value_codes(), full.value_codes())
@@ -642,6 +643,39 @@ def test_8bit_prefill_equals_prefill_plus_appends(orc, fmt, G, R):
     ka, va = inc.dequantize()
     kf, vf = full.dequantize()
     assert np.array_equal(ka, kf) and np.array_equal(va, vf)
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("G", [16, 32])
+def test_8bit_quantized_on_write_without_residual(orc, fmt, G):
+    """8-bit formats with R = 0 ("KV cache compression: quantization,
+    eviction and sparse attention", section 3.1: the FP8 / INT8 cache holds
+    every token in 8 bits): every token is quantized when it is written,
+    whatever the group size, by the per-token quantizer alone (INT8: the
+    8-bit min/max set quantizer over the token's channels; FP8: E4M3 under
+    the static scale), and the stream keeps no fp16 token."""
+    n, m = 2 * G + 5, G - 3        # ragged: neither count is a multiple of G
+    rng = np.random.default_rng(90 + G + fmt)
+    kb = (rng.standard_normal((n, 128)) * 3).astype(np.float16).view(np.uint16)
+    vb = rng.standard_normal((n, 128)).astype(np.float16).view(np.uint16)
+    kw = dict(fmt=fmt, kscale=0.02, vscale=0.01)
+    st = orc.StreamState.prefill(kb[:m], vb[:m], 8, 8, G, 0, cap=n, **kw)
+    assert (st.n, st.nq) == (m, m)
+    for t in range(m, n):
+        st.append(kb[t], vb[t])
+        assert st.nq == st.n == t + 1
+    for t in range(n):
+        for x, codes, meta, sc in ((kb[t], st.key_codes()[t], st.key_meta(), kw["kscale"]),
+                                   (vb[t], st.value_codes()[t], st.value_meta(), kw["vscale"])):
+            if fmt == orc.FMT_INT8:
+                c, s16, z16 = orc.quantize_value_token(x, 8)
+                assert np.array_equal(codes, c) and meta[0][t] == s16 and meta[1][t] == z16
+            else:
+                assert np.array_equal(codes, orc.quantize_token_fp8(x, sc))
+    kh, vh = st.dequantize()
+    assert st.residual()[0].shape[0] == 0
+    # no token is returned exactly as stored: every one went through its codes
+    assert not np.array_equal(kh, orc.h2f(kb)) and not np.array_equal(vh, orc.h2f(vb))
 
 
 def test_8bit_bytes_golden(orc):
@@ -1092,6 +1126,7 @@ def test_ds_lowers_key_error(orc):
 
 MUTATIONS = [
     ("rintf(t)", "floorf(t + 0.5f)", "ties"),                           # wrong rounding rule
+    ("if (R == 0) return n > 0 ? n : 0;", "if (0) return n;", "onwrite"),  # 8-bit waits for whole groups
     ("codes[(long)i * code_stride] = (uint8_t)r;",
      "codes[(long)i * code_stride] = (uint8_t)r; if (0) {}", None),     # no-op (control)
     ("(long)(t / G) * d + c", "(long)(t / G) * d", "dequant"),          # dropped channel index
@@ -1155,6 +1190,7 @@ def test_pin_catches_planted_mistakes(tmp_path):
         "dssel": "test_ds_ties_at_the_boundary_go_to_the_lower_position",
         "dsdense": "test_ds_dense_part_is_the_set_quantizer_on_the_rest",
         "dsdeq": "test_ds_stream_roundtrip_and_appends",
+        "onwrite": "test_8bit_quantized_on_write_without_residual",
     }
     for i, (old, new, which) in enumerate(MUTATIONS):
         assert old in src, old
