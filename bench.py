@@ -78,7 +78,11 @@ def parse_args():
 # Algorithmic byte counts (what the method must move at minimum)
 # ---------------------------------------------------------------------------
 
-def n_quant(n, G, R):
+def n_quant(n, G, R, fmt=0):
+    """Quantized tokens of a stream holding n (8-bit formats with R = 0
+    quantize every token on write)."""
+    if fmt and R == 0:
+        return max(n, 0)
     return 0 if n <= R else G * ((n - R) // G)
 
 
@@ -101,7 +105,7 @@ def attention_bytes(lens, w, d=128):
     sequence the fp16 query and fp32 output."""
     tot = 0
     for n in lens:
-        nq = n_quant(int(n), w.group_size, w.residual)
+        nq = n_quant(int(n), w.group_size, w.residual, w.kv_format)
         per_head = nq * d * (w.k_bits + w.v_bits) // 8 + meta_bytes(nq, w, d) + (int(n) - nq) * d * 2 * 2
         tot += w.num_kv_heads * per_head + w.num_q_heads * d * (2 + 4)
     return tot
@@ -111,7 +115,7 @@ def prefill_bytes(lens, w, d=128):
     """fp16 K and V read, packed records and fp16 residual written."""
     tot = 0
     for n in lens:
-        nq = n_quant(int(n), w.group_size, w.residual)
+        nq = n_quant(int(n), w.group_size, w.residual, w.kv_format)
         tot += w.num_kv_heads * (int(n) * d * 2 * 2 + nq * d * (w.k_bits + w.v_bits) // 8
                                  + meta_bytes(nq, w, d) + (int(n) - nq) * d * 2 * 2)
     return tot
@@ -253,7 +257,7 @@ def cpu_baseline(w, K, V, q, lens, budget_s, scales=None):
 
     def stream_bytes(b):
         n = int(lens[b])
-        nq = n_quant(n, w.group_size, w.residual)
+        nq = n_quant(n, w.group_size, w.residual, w.kv_format)
         return nq * 128 * (w.k_bits + w.v_bits) // 8 + meta_bytes(nq, w) + (n - nq) * 128 * 4 + gq * 128 * 6
 
     wall0 = time.perf_counter()
@@ -349,7 +353,7 @@ def main():
         G, R = w.group_size, w.residual
         grow = total_steps + 8
         mb = (L + grow - R) // G + 1
-        nb = int(sum(n_quant(int(n) + grow, G, R) // G for n in lens)) + 8
+        nb = int(sum(-(-n_quant(int(n) + grow, G, R, w.kv_format) // G) for n in lens)) + 8
         shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, G, R, paged=True,
                                num_blocks=nb, max_blocks_per_seq=mb, kv_format=w.kv_format,
                                rope_theta=w.rope_theta, grid=w.grid,

@@ -119,6 +119,10 @@ kvq_status make_layout(const kvq_config* cfg, Layout* L) {
     L->G = G;
     L->R = cfg->residual;
     L->ring = cfg->residual + G;
+    // 8-bit formats quantize each token on its own: without a residual
+    // window a token is quantized when written (the group's record fills up
+    // token by token)
+    L->onwrite = cfg->kv_format != kFmtKivi && cfg->residual == 0;
     L->paged = cfg->block_size != 0;
     if (L->paged) {
         if (cfg->block_size != G) return KVQ_EINVAL;
@@ -126,13 +130,13 @@ kvq_status make_layout(const kvq_config* cfg, Layout* L) {
         L->num_blocks = cfg->num_blocks;
         L->max_blocks = cfg->max_blocks_per_seq;
         L->groups = cfg->max_blocks_per_seq;
-        const long cap = (long)L->R + (long)(L->max_blocks + 1) * G - 1;
+        const long cap = L->onwrite ? (long)L->max_blocks * G : (long)L->R + (long)(L->max_blocks + 1) * G - 1;
         L->capacity = cap > 0x7fffffffL ? 0x7fffffff : (int)cap;
     } else {
         if (cfg->max_tokens < 0) return KVQ_EINVAL;
         L->num_blocks = 0;
         L->max_blocks = 0;
-        L->groups = num_quantized(cfg->max_tokens, G, L->R) / G;
+        L->groups = L->onwrite ? (cfg->max_tokens + G - 1) / G : num_quantized(cfg->max_tokens, G, L->R) / G;
         L->capacity = cfg->max_tokens;
     }
     L->spt = G == 16 ? 4 : 8;

@@ -1007,7 +1007,7 @@ __device__ __forceinline__ h8 conv8(uint32_t w0, uint32_t w1) {
 // vscl: the static value scale (FP8).
 template <int G, int F, bool LP>
 __device__ __forceinline__ void process_unit8(const lds_u8* buf, uint32_t has, WaveAcc& A, const QOps& Q,
-                                              float sl2, float qsum, float vscl, int lane) {
+                                              float sl2, float qsum, float vscl, int lane, int nvalid) {
     using S = Stage8<G, F>;
     constexpr int SPT = S::SPT;
     const int g = lane >> 4;
@@ -1083,7 +1083,9 @@ __device__ __forceinline__ void process_unit8(const lds_u8* buf, uint32_t has, W
                 vs[i] = vscl;
                 vz[i] = 0.0f;
             }
-            valid[i] = S::NR == 1 || ((has >> rec) & 1);
+            // (quantize-on-write: the unit may end inside its last record;
+            // its later slots hold zero tokens, masked here)
+            valid[i] = (S::NR == 1 || ((has >> rec) & 1)) && 16 * rt + 4 * g + i < nvalid;
         }
     };
     if constexpr (LP) {
@@ -1302,7 +1304,7 @@ __device__ __forceinline__ SeqUnits seq_units(const Layout& L, const kvq_cache& 
     SeqUnits u;
     u.nq = max(c.n_quant[b], 0);
     u.n = min(max(c.n_tokens[b], u.nq), u.nq + L.ring);
-    u.ngroups = u.nq / L.G;
+    u.ngroups = (u.nq + L.G - 1) / L.G;   // (the last one partial only when quantized on write)
     u.uq = (u.ngroups * L.G + 31) / 32;
     u.units = u.uq + (u.n - u.nq + 31) / 32;
     u.cost = u.uq + kResCost * (u.units - u.uq);
@@ -1328,11 +1330,11 @@ __device__ __forceinline__ uint32_t issue_any(lds_u8* buf, const Layout& L, cons
 template <int G, int KB, int VB, int F, bool LP, bool TP>
 __device__ __forceinline__ void process_any(const lds_u8* buf, uint32_t has, WaveAcc& A, const QOps& Q, float sl2,
                                             float qsum, float vscl, int lane, RopeLds* R, int wave, int t0,
-                                            const Layout& L, SparseLds* SPL, int gq) {
+                                            const Layout& L, SparseLds* SPL, int gq, int nq) {
     if constexpr (low_bit(F))
         process_unit<G, KB, VB, LP, rope_fmt(F), cb_fmt(F), sp_fmt(F), TP>(buf, has, A, Q, sl2, lane, R, wave, t0,
                                                                            L, SPL, gq);
-    else process_unit8<G, F, LP>(buf, has, A, Q, sl2, qsum, vscl, lane);
+    else process_unit8<G, F, LP>(buf, has, A, Q, sl2, qsum, vscl, lane, nq - t0);
 }
 
 // Units [lo, hi) of stream (b, h) by the four waves of the workgroup (wave w
@@ -1477,7 +1479,8 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
                 wave_sync();
                 update_progress_prio(left, left == ntot, prio);
                 --left;
-                process_any<G, KB, VB, F, LP, TP>(sb[0], hb[0], A, Q, sl2q, qsum, vscl, lane, R, wave, 32 * u, L, SPL, gq);
+                process_any<G, KB, VB, F, LP, TP>(sb[0], hb[0], A, Q, sl2q, qsum, vscl, lane, R, wave, 32 * u, L, SPL, gq,
+                                                  su.nq);
                 u += kWaves;
                 if (u >= q1) break;
                 // rotate: the buffer just processed is the next to be refilled

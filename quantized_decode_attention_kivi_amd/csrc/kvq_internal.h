@@ -77,6 +77,8 @@ struct Layout {
     int sparse;                                   // dense-and-sparse keys: G kept (pos, fp16) pairs per record
     int sparse_off;                               // their offset in the record (after the value table)
     int B, H, kbits, vbits, G, R, ring;
+    int onwrite;                                  // 8-bit format without a residual window:
+                                                  // every token quantized as it is written
     int paged, num_blocks, max_blocks, groups;   // groups: record slots per sequence
     int capacity;                                 // max tokens a sequence may hold
     int spt;                                      // value-code slots per lane and column tile
@@ -102,6 +104,12 @@ __host__ __device__ inline int vlane_byte(int lane_bytes, int lane, int b) {
 __host__ __device__ inline int num_quantized(int n, int G, int R) {
     int over = n - R;
     return over <= 0 ? 0 : G * (over / G);
+}
+
+// The same for layout L: with quantize-on-write (L.onwrite) all n tokens,
+// the last group possibly partial.
+__host__ __device__ inline int quantized_count(const Layout& L, int n) {
+    return L.onwrite ? (n > 0 ? n : 0) : num_quantized(n, L.G, L.R);
 }
 
 // Codebook levels of b bits (2 or 4) in 1/F_b grid steps, F_b = 64 or 16:

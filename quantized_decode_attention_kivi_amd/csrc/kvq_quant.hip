@@ -650,11 +650,13 @@ __device__ void quantize_pair16(QuantSmemPair& sm, const Layout& L, const half_t
 // 8 bits over the token's 128 channels (the 16 threads of a row reduce it);
 // F = kFmtFp8: E4M3 codes under the kv head's static scales (inverses kinv,
 // vinv).  Key bytes go straight to the record in channel order; value bytes
-// through LDS into the lane-major operand order.
+// through LDS into the lane-major operand order.  rows: tokens present (a
+// partial group when quantized on write); the others are not read and are
+// stored as zero tokens (codes 0, INT8 scale and zero 0).
 template <int G, int F>
 __device__ void quantize_group8(QuantSmemU<G>& sm, const Layout& L, const half_t* __restrict__ ksrc,
                                 const half_t* __restrict__ vsrc, uint8_t* __restrict__ rec, float kinv,
-                                float vinv) {
+                                float vinv, int rows) {
     constexpr int NT = G / 16;
     constexpr int SPT = G == 16 ? 4 : 8;
     const int tid = threadIdx.x;
@@ -663,8 +665,9 @@ __device__ void quantize_group8(QuantSmemU<G>& sm, const Layout& L, const half_t
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
         const int t = ts + 16 * j;
-        const uint4 a = load_once16(ksrc + t * kD + 8 * cg);
-        const uint4 b = load_once16(vsrc + t * kD + 8 * cg);
+        const uint4 z4 = make_uint4(0, 0, 0, 0);
+        const uint4 a = t < rows ? load_once16(ksrc + t * kD + 8 * cg) : z4;
+        const uint4 b = t < rows ? load_once16(vsrc + t * kD + 8 * cg) : z4;
         const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
         const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
         uint32_t kw[2], vw[2];
@@ -751,9 +754,11 @@ inline int quant_variant(const Layout& L) {
 }
 
 // Quantizes one group in variant F (low-bit: key bits KB, value bits VB).
+// rows: tokens of the group present (8-bit formats quantized on write; the
+// low-bit formats always quantize whole groups).
 template <int G, int KB, int VB, int F>
 __device__ __forceinline__ void quantize_any(QSmem<G, F>& sm, const Layout& L, const kvq_cache& c, int h,
-                                             const half_t* ksrc, const half_t* vsrc, uint8_t* rec) {
+                                             const half_t* ksrc, const half_t* vsrc, uint8_t* rec, int rows = G) {
     if constexpr (F == kQUniform) {
         quantize_group_uniform<G, KB, VB>(sm, L, ksrc, vsrc, rec);
     } else if constexpr (q_low_bit(F)) {
@@ -762,7 +767,7 @@ __device__ __forceinline__ void quantize_any(QSmem<G, F>& sm, const Layout& L, c
     } else {
         const float kinv = F == kFmtFp8 ? fp8_inv_scale(c.k_scale[h]) : 0.0f;
         const float vinv = F == kFmtFp8 ? fp8_inv_scale(c.v_scale[h]) : 0.0f;
-        quantize_group8<G, F>(sm, L, ksrc, vsrc, rec, kinv, vinv);
+        quantize_group8<G, F>(sm, L, ksrc, vsrc, rec, kinv, vinv, rows);
     }
 }
 
@@ -787,12 +792,12 @@ __global__ __launch_bounds__(256) void prefill_groups_kernel(Layout L, kvq_cache
     const int sh = blockIdx.y;
     const int b = sh / L.H, h = sh % L.H;
     const int n = clamped_len(L, seq_lens, b, max_len);
-    const int nq = num_quantized(n, G, L.R);
+    const int nq = quantized_count(L, n);
     if (g * G >= nq) return;
     uint8_t* rec = record_at(L, c.packed, c.block_table, b, h, g);
     if (!rec) return;
     const long base = ((long)sh * max_len + (long)g * G) * kD;
-    quantize_any<G, KB, VB, F>(sm, L, c, h, k + base, v + base, rec);
+    quantize_any<G, KB, VB, F>(sm, L, c, h, k + base, v + base, rec, min(G, nq - g * G));
 }
 
 // Uniform grid, G = 16: grid (ceil(max_len / 32), B*H); one workgroup per two
@@ -822,7 +827,7 @@ __global__ __launch_bounds__(256) void prefill_tail_kernel(Layout L, kvq_cache c
     const int sh = blockIdx.x;
     const int b = sh / L.H, h = sh % L.H;
     const int n = clamped_len(L, seq_lens, b, max_len);
-    const int nq = num_quantized(n, L.G, L.R);
+    const int nq = quantized_count(L, n);
     const uint4* k16 = (const uint4*)(k + (long)sh * max_len * kD);
     const uint4* v16 = (const uint4*)(v + (long)sh * max_len * kD);
     uint4* kr = (uint4*)c.k_res + (long)sh * L.ring * (kD / 8);
@@ -846,21 +851,110 @@ __global__ __launch_bounds__(256) void prefill_tail_kernel(Layout L, kvq_cache c
 // ---------------------------------------------------------------------------
 
 // State of sequence b before an append.  Counters written by this library
-// satisfy 0 <= nq <= n, nq % G == 0; anything else is treated as a full cache
-// (nothing is written).  A flush happens when the new token brings the ring
-// to R + G tokens: its oldest G leave the residual window.
+// satisfy 0 <= nq <= n, nq % G == 0 (quantize-on-write layouts: nq = n);
+// anything else is treated as a full cache (nothing is written).  A flush
+// happens when the new token brings the ring to R + G tokens: its oldest G
+// leave the residual window.  On write, the new token goes straight into
+// the record of group n / G, which must exist (write).
 struct AppendState {
     int n, nq;
-    bool room, flush;
+    bool room, flush, write;
 };
 __device__ __forceinline__ AppendState append_state(const Layout& L, const kvq_cache& c, int b) {
     AppendState a;
     a.n = c.n_tokens[b];
     a.nq = c.n_quant[b];
+    if (L.onwrite) {
+        a.room = a.n >= 0 && a.nq == a.n && a.n < L.capacity;
+        a.flush = false;
+        a.write = a.room && record_at(L, c.packed, c.block_table, b, 0, a.n / L.G) != nullptr;
+        return a;
+    }
     const bool sane = a.nq >= 0 && a.n >= a.nq && (a.nq % L.G) == 0;
     a.room = sane && (a.n - a.nq) < L.ring && a.n < L.capacity;
     a.flush = a.room && (a.n + 1 - a.nq == L.R + L.G);
+    a.write = false;
     return a;
+}
+
+// Counters after an append in state a (the record of a flushed or written
+// group exists for every head or for none).
+__device__ __forceinline__ void advance_counters(const Layout& L, const kvq_cache& c, int b, const AppendState& a) {
+    if (L.onwrite) {
+        if (!a.write) return;   // no block for the token's group: nothing was appended
+        c.n_tokens[b] = a.n + 1;
+        c.n_quant[b] = a.n + 1;
+        return;
+    }
+    const bool flushed = a.flush && record_at(L, c.packed, c.block_table, b, 0, a.nq / L.G) != nullptr;
+    c.n_tokens[b] = a.n + 1;
+    c.n_quant[b] = a.nq + (flushed ? L.G : 0);
+}
+
+// One token of an 8-bit format quantized into slot t of its group's record
+// (quantize-on-write), by the 16 threads of one DPP row, thread cg holding
+// channels 8cg .. 8cg+7: the same per-token arithmetic as quantize_group8.
+template <int F>
+__device__ void quantize_token8(const Layout& L, const half_t* __restrict__ krow, const half_t* __restrict__ vrow,
+                                uint8_t* __restrict__ rec, int t, int cg, float kinv, float vinv) {
+    const uint4 a = *(const uint4*)(krow + 8 * cg);
+    const uint4 bb = *(const uint4*)(vrow + 8 * cg);
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+    const uint32_t bw[4] = {bb.x, bb.y, bb.z, bb.w};
+    uint32_t kw[2], vw[2];
+    if (F == kFmtInt8) {
+        const uint32_t km = pk_min(pk_min(aw[0], aw[1]), pk_min(aw[2], aw[3]));
+        const uint32_t kM = pk_max(pk_max(aw[0], aw[1]), pk_max(aw[2], aw[3]));
+        const uint32_t vm = pk_min(pk_min(bw[0], bw[1]), pk_min(bw[2], bw[3]));
+        const uint32_t vM = pk_max(pk_max(bw[0], bw[1]), pk_max(bw[2], bw[3]));
+        const float kmn = row16<false>(fminf(h2f(km & 0xffffu), h2f(km >> 16)));
+        const float kmx = row16<true>(fmaxf(h2f(kM & 0xffffu), h2f(kM >> 16)));
+        const float vmn = row16<false>(fminf(h2f(vm & 0xffffu), h2f(vm >> 16)));
+        const float vmx = row16<true>(fmaxf(h2f(vM & 0xffffu), h2f(vM >> 16)));
+        const QParams pk = make_qparams(kmn, kmx, 8);
+        const QParams pv = make_qparams(vmn, vmx, 8);
+        const float nk = -pk.z, nv = -pv.z;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            kw[h] = vw[h] = 0;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                kw[h] = code_byte_sat<0>(aw[2 * h + i], nk, pk.inv, 2 * i, kw[h]);
+                kw[h] = code_byte_sat<1>(aw[2 * h + i], nk, pk.inv, 2 * i + 1, kw[h]);
+                vw[h] = code_byte_sat<0>(bw[2 * h + i], nv, pv.inv, 2 * i, vw[h]);
+                vw[h] = code_byte_sat<1>(bw[2 * h + i], nv, pv.inv, 2 * i + 1, vw[h]);
+            }
+        }
+        if (cg == 0) {
+            const int kp = tmeta_pos(L, L.kmeta_off, t), vp = tmeta_pos(L, L.vmeta_off, t);
+            *(uint16_t*)(rec + kp) = pk.s_bits;
+            *(uint16_t*)(rec + kp + 2 * L.spt) = pk.z_bits;
+            *(uint16_t*)(rec + vp) = pv.s_bits;
+            *(uint16_t*)(rec + vp + 2 * L.spt) = pv.z_bits;
+        }
+    } else {
+        float kx[8], vx[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kx[2 * e] = h2f(aw[e] & 0xffffu);
+            kx[2 * e + 1] = h2f(aw[e] >> 16);
+            vx[2 * e] = h2f(bw[e] & 0xffffu);
+            vx[2 * e + 1] = h2f(bw[e] >> 16);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            kw[h] = fp8_code2(kx[4 * h], kx[4 * h + 1], kinv) | fp8_code2(kx[4 * h + 2], kx[4 * h + 3], kinv) << 16;
+            vw[h] = fp8_code2(vx[4 * h], vx[4 * h + 1], vinv) | fp8_code2(vx[4 * h + 2], vx[4 * h + 3], vinv) << 16;
+        }
+    }
+    *(uint2*)(rec + k8_byte(t, 8 * cg)) = make_uint2(kw[0], kw[1]);
+    // value bytes: each to its place in the lane-major operand layout
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        int by, bi;
+        vcode_pos(L, t, 8 * cg + e, &by, &bi);
+        rec[by + bi / 8] = (uint8_t)(vw[e >> 2] >> (8 * (e & 3)));
+    }
 }
 
 // Append: grid (B, H), one workgroup per (sequence, kv head), so the heads'
@@ -880,18 +974,40 @@ __global__ __launch_bounds__(256) void append_kernel(Layout L, kvq_cache c, cons
     const AppendState a = append_state(L, c, b);
     if (!a.room) return;   // (the same for every head of b: none arrives)
     const long sh = (long)b * L.H + h;
-    if (threadIdx.x < 64) {
-        const int slot = a.n % L.ring;
-        ((uint32_t*)c.k_res)[(sh * L.ring + slot) * (kD / 2) + threadIdx.x] =
-            ((const uint32_t*)knew)[sh * (kD / 2) + threadIdx.x];
-        ((uint32_t*)c.v_res)[(sh * L.ring + slot) * (kD / 2) + threadIdx.x] =
-            ((const uint32_t*)vnew)[sh * (kD / 2) + threadIdx.x];
+    if constexpr (!q_low_bit(F)) {
+        if (L.onwrite) {
+            // quantize-on-write: the token goes straight into its group's
+            // record; a group's first token finds the record cleared to zero
+            // tokens first, so its unwritten slots read as zero codes
+            uint8_t* rec = a.write ? record_at(L, c.packed, c.block_table, b, h, a.n / G) : nullptr;
+            if (rec) {
+                if (a.n % G == 0) {
+                    for (int i = threadIdx.x; i < L.record / 16; i += 256)
+                        ((uint4*)rec)[i] = make_uint4(0, 0, 0, 0);
+                    __syncthreads();
+                }
+                if (threadIdx.x < 16) {
+                    const float kinv = F == kFmtFp8 ? fp8_inv_scale(c.k_scale[h]) : 0.0f;
+                    const float vinv = F == kFmtFp8 ? fp8_inv_scale(c.v_scale[h]) : 0.0f;
+                    quantize_token8<F>(L, knew + sh * kD, vnew + sh * kD, rec, a.n % G, threadIdx.x, kinv, vinv);
+                }
+            }
+        }
     }
-    uint8_t* rec = a.flush ? record_at(L, c.packed, c.block_table, b, h, a.nq / G) : nullptr;
-    if (rec) {   // (no block for the group: the counters do not advance it either)
-        __syncthreads();   // the new token's row is visible to the whole workgroup
-        const long row = (sh * L.ring + (a.nq % L.ring)) * kD;
-        quantize_any<G, KB, VB, F>(sm, L, c, h, (const half_t*)c.k_res + row, (const half_t*)c.v_res + row, rec);
+    if (!L.onwrite) {
+        if (threadIdx.x < 64) {
+            const int slot = a.n % L.ring;
+            ((uint32_t*)c.k_res)[(sh * L.ring + slot) * (kD / 2) + threadIdx.x] =
+                ((const uint32_t*)knew)[sh * (kD / 2) + threadIdx.x];
+            ((uint32_t*)c.v_res)[(sh * L.ring + slot) * (kD / 2) + threadIdx.x] =
+                ((const uint32_t*)vnew)[sh * (kD / 2) + threadIdx.x];
+        }
+        uint8_t* rec = a.flush ? record_at(L, c.packed, c.block_table, b, h, a.nq / G) : nullptr;
+        if (rec) {   // (no block for the group: the counters do not advance it either)
+            __syncthreads();   // the new token's row is visible to the whole workgroup
+            const long row = (sh * L.ring + (a.nq % L.ring)) * kD;
+            quantize_any<G, KB, VB, F>(sm, L, c, h, (const half_t*)c.k_res + row, (const half_t*)c.v_res + row, rec);
+        }
     }
     if (!c.arrivals) return;
     __syncthreads();   // every thread of this workgroup has read the counters
@@ -901,9 +1017,7 @@ __global__ __launch_bounds__(256) void append_kernel(Layout L, kvq_cache c, cons
         const int before = __hip_atomic_fetch_add(&c.arrivals[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (before == L.H - 1) {   // every head of b has read the counters
             __hip_atomic_store(&c.arrivals[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const bool flushed = a.flush && record_at(L, c.packed, c.block_table, b, 0, a.nq / L.G) != nullptr;
-            c.n_tokens[b] = a.n + 1;
-            c.n_quant[b] = a.nq + (flushed ? L.G : 0);
+            advance_counters(L, c, b, a);
         }
     }
 }
@@ -915,9 +1029,7 @@ __global__ __launch_bounds__(256) void append_counters_kernel(Layout L, kvq_cach
     if (b >= L.B) return;
     const AppendState a = append_state(L, c, b);
     if (!a.room) return;
-    const bool flushed = a.flush && record_at(L, c.packed, c.block_table, b, 0, a.nq / L.G) != nullptr;
-    c.n_tokens[b] = a.n + 1;
-    c.n_quant[b] = a.nq + (flushed ? L.G : 0);
+    advance_counters(L, c, b, a);
 }
 
 // ---------------------------------------------------------------------------

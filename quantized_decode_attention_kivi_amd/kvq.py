@@ -202,8 +202,18 @@ def kvq_codebook_levels(bits) -> np.ndarray:
 # Buffer owner
 # ---------------------------------------------------------------------------
 
-def num_quantized(n, G, R):
+def num_quantized(n, G, R, onwrite=False):
+    """Quantized tokens of a sequence holding n: whole groups outside the
+    newest R tokens; every token when quantized on write (8-bit formats with
+    R = 0)."""
+    if onwrite:
+        return max(int(n), 0)
     return 0 if n <= R else G * ((n - R) // G)
+
+
+def groups_held(n, G, R, onwrite=False):
+    """Key groups (records, paged blocks) a sequence holding n uses."""
+    return -(-num_quantized(n, G, R, onwrite) // G)
 
 
 @dataclass
@@ -358,9 +368,16 @@ class QuantizedKVCache:
     def R(self):
         return self.shape.residual
 
+    @property
+    def onwrite(self):
+        """8-bit format without a residual window: tokens quantized as written."""
+        return self.shape.kv_format != FORMAT_KIVI and self.shape.residual == 0
+
     def capacity(self):
         s = self.shape
         if s.paged:
+            if self.onwrite:
+                return s.max_blocks_per_seq * s.group_size
             return s.residual + (s.max_blocks_per_seq + 1) * s.group_size - 1
         return s.max_tokens
 
@@ -372,7 +389,8 @@ class QuantizedKVCache:
         that reads them, so the host does not wait for the device."""
         if not self.shape.paged:
             return
-        need = np.maximum(np.asarray(lens_after, np.int64) - self.R, 0) // self.G
+        need = np.array([groups_held(int(n), self.G, self.R, self.onwrite) for n in np.atleast_1d(lens_after)],
+                        np.int64)
         short = np.nonzero(need > self._nblk)[0]
         if len(short) == 0:
             return
@@ -400,7 +418,7 @@ class QuantizedKVCache:
         order the pool hands them out.  The device table is rewritten only if
         it changes (a rewrite waits for the device: in-flight calls may read
         the table)."""
-        need = np.array([num_quantized(int(n), self.G, self.R) // self.G for n in lens], np.int64)
+        need = np.array([groups_held(int(n), self.G, self.R, self.onwrite) for n in lens], np.int64)
         total = int(need.sum())
         if total > len(self._block_order) or (len(need) and int(need.max()) > self._bt_host.shape[1]):
             raise KVQError(KVQ_ECAPACITY, "paged cache out of blocks")

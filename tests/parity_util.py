@@ -25,7 +25,8 @@ def make_cache(w: synth.Workload, lens, max_tokens=None, num_blocks=None, shuffl
     G, R = w.group_size, w.residual
     if w.paged:
         mb = max(1, (int(np.max(lens)) + 64 - R) // G + 1)
-        nb = num_blocks if num_blocks is not None else int(sum(kvq.num_quantized(int(n) + 64, G, R) // G
+        onwrite = w.kv_format != kvq.FORMAT_KIVI and R == 0
+        nb = num_blocks if num_blocks is not None else int(sum(kvq.groups_held(int(n) + 64, G, R, onwrite)
                                                                for n in lens)) + 4
         shape = kvq.CacheShape(w.num_seqs, w.num_kv_heads, w.k_bits, w.v_bits, G, R, paged=True,
                                num_blocks=nb, max_blocks_per_seq=mb, kv_format=w.kv_format,

@@ -115,6 +115,48 @@ def test_append_sequence_8bit(fmt):
     compare_attention(out.cpu().numpy(), oracle_attention(to_bits(q), states, SCALE))
 
 
+@pytest.mark.parametrize("fmt", list(FORMATS))
+@pytest.mark.parametrize("G,paged", [(16, False), (32, False), (16, True), (32, True)])
+def test_quantized_on_write_8bit(fmt, G, paged):
+    """Without a residual window the 8-bit formats quantize every token as it
+    is written ("KV cache compression: quantization, eviction and sparse
+    attention", section 3.1): after a prefill of ragged lengths and after
+    every append n_q = n, the partial last group included; codes, scales,
+    zeros and dequantized values bit-exact against the oracle, attention
+    within the bar (paged: each group's block is handed out when its first
+    token is written)."""
+    w = _w(fmt, name="e8ow", num_seqs=3, num_q_heads=8, num_kv_heads=2, group_size=G, residual=0,
+           context=300, tag=59 + G, paged=paged)
+    m, steps = 200, G + 7
+    lens0 = np.array([m, m - 5, m - G - 3], np.int64)
+    K, V = synth.make_kv(w, max_len=m + steps, device="cuda")
+    scales = synth.calibrate_fp8_scales(K, V) if w.kv_format == kvq.FORMAT_FP8_E4M3 else None
+    cache = make_cache(w, lens0 + steps + 1, max_tokens=m + steps + 8, shuffle_seed=13, scales=scales)
+    print("on-write %s G=%d paged=%d" % (fmt, G, paged), flush=True)
+    cache.prefill(K[:, :, :m].contiguous(), V[:, :, :m].contiguous(), lens0)
+    kb, vb = to_bits(K), to_bits(V)
+    states = oracle_states(kb[:, :, :m], vb[:, :, :m], lens0, w, cap=m + steps + 8, scales=scales)
+    torch.cuda.synchronize()
+    assert np.array_equal(cache.n_quant.cpu().numpy(), lens0) and np.array_equal(cache.n_tokens.cpu().numpy(), lens0)
+    compare_codes(cache, states)
+    for s in range(steps):
+        kn = torch.stack([K[b, :, int(lens0[b])] for b in range(w.num_seqs)]).contiguous()
+        vn = torch.stack([V[b, :, int(lens0[b])] for b in range(w.num_seqs)]).contiguous()
+        cache.append(kn, vn)
+        for b in range(w.num_seqs):
+            for h in range(w.num_kv_heads):
+                states[b][h].append(kb[b, h, int(lens0[b])], vb[b, h, int(lens0[b])])
+        lens0 += 1
+        if s in (0, 2, G - 3, steps - 1):
+            torch.cuda.synchronize()
+            assert np.array_equal(cache.n_quant.cpu().numpy(), lens0)
+            compare_codes(cache, states)
+    q = synth.make_query(w, device="cuda", step=5)
+    out = cache.decode_attention(q, SCALE)
+    torch.cuda.synchronize()
+    compare_attention(out.cpu().numpy(), oracle_attention(to_bits(q), states, SCALE))
+
+
 def test_fp8_codes_are_the_e4m3_encoding_of_every_value():
     """Every E4M3 code (both signs, subnormals, 448) and the midpoints between
     neighbouring codes go through the device quantizer: inputs x = v * s with
