@@ -118,7 +118,9 @@ typedef struct kvq_config {
     int32_t k_bits;             /* key code width: 2 or 4 (8 in 8-bit formats)   */
     int32_t v_bits;             /* value code width: 2 or 4 (8 in 8-bit formats) */
     int32_t group_size;         /* G: 16 or 32 tokens per key group              */
-    int32_t residual;           /* R >= 0, a multiple of G                       */
+    int32_t residual;           /* R >= 0, a multiple of G.  8-bit formats with
+                                   R = 0 quantize every token as it is written
+                                   (n_q = n, the last group filling up)         */
     int32_t max_tokens;         /* contiguous mode: per-sequence capacity        */
     int32_t block_size;         /* 0 = contiguous; otherwise paged, == G         */
     int32_t num_blocks;         /* paged: blocks in the pool                     */
@@ -183,7 +185,9 @@ kvq_status kvq_buffer_sizes(const kvq_config *cfg, kvq_sizes *out);
  * k, v: fp16 [B][H][max_len][d]; seq_lens: device int32 [B], the number of
  * valid tokens of each sequence.  Overwrites the cache state: for every
  * sequence, groups [0, n_q) are quantized into records and tokens [n_q, n)
- * are copied into the residual ring; n_tokens = n and n_quant = n_q.
+ * are copied into the residual ring; n_tokens = n and n_quant = n_q (8-bit
+ * formats with R = 0: n_q = n, the last group's record holding its tokens
+ * and zero tokens after them).
  * Preconditions (caller): 0 <= seq_lens[b] <= max_len, seq_lens[b] within the
  * capacity (max_tokens, or max_blocks_per_seq*G with block_table rows filled
  * for every quantized group).  The kernels clamp a violating length to the
@@ -203,8 +207,13 @@ kvq_status kv_quantize_prefill(const kvq_config *cfg, const kvq_cache *cache,
  * sequence's kv-head workgroups to finish, counted by an agent-scope atomic
  * on arrivals[b], advances the counters once every head has read them, and
  * resets the count), else by a second one-thread-per-sequence kernel.
+ * 8-bit formats with R = 0 quantize the new token at once into slot n % G
+ * of its group's record (the group's first token clears the record first)
+ * and advance n_q with n.
  * Preconditions (caller): n + 1 within capacity; in paged mode
- * block_table[b][n_q/G] holds a free block before the append that flushes.
+ * block_table[b][n_q/G] holds a free block before the append that flushes
+ * (8-bit formats with R = 0: block_table[b][n/G] before the append of each
+ * group's first token; without it nothing is appended).
  * A flush that would leave the buffers is skipped (no write) and the token is
  * still appended to the ring only if the ring has room. */
 kvq_status kv_append_token(const kvq_config *cfg, const kvq_cache *cache,
