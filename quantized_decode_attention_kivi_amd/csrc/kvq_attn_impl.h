@@ -45,6 +45,7 @@ namespace kvq {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kPart = kD + 4;          // floats per head in a partial: out[128], m, l, pad
@@ -66,14 +67,20 @@ __device__ __forceinline__ h8 words_h8(uint4 w) {
     return make_h8(as_h2(w.x), as_h2(w.y), as_h2(w.z), as_h2(w.w));
 }
 
+// Maximum of two logits (finite, or -inf for nothing seen).  The
+// NaN-propagating form is one instruction (v_maximum3_f32); fmaxf would first
+// quiet each operand the compiler cannot prove canonical, such as a value
+// received from another lane, at one extra instruction per operand.
+__device__ __forceinline__ float max_logit(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Max over the four lane groups (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float group_max(float x) {
     const uint32_t u = __builtin_bit_cast(uint32_t, x);
     auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    x = fmaxf(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
+    x = max_logit(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
     const uint32_t v = __builtin_bit_cast(uint32_t, x);
     auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    return fmaxf(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
+    return max_logit(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
 }
 // x(l) + x(l ^ 32): the first step of group_sum.
 __device__ __forceinline__ float add_group_pairs(float x) {
@@ -367,25 +374,13 @@ __device__ __forceinline__ void acc_init(WaveAcc& A) {
     A.pz = 0.0f;
 }
 
-// Online-softmax step over the 8 logits x[] (raw q.k, slot order) of this
-// lane's column, then the value contraction with operands vop(ct).  vs/vz:
-// value scale/zero of each slot; valid: slot holds a token.  The weights p*s
-// are split into fp16 high and low parts (22 bits).  LP (limb-packed): rows
-// 0-7 of the value product take the high parts and rows 8-15 the low parts of
-// heads 0-7, one product per column tile; otherwise each part is a product of
-// its own over rows = heads.
-template <bool LP, typename VOp>
-__device__ __forceinline__ void softmax_and_values(WaveAcc& A, const float (&x)[8], const float (&vs)[8],
-                                                   const float (&vz)[8], const bool (&valid)[8], float sl2,
-                                                   int lane, VOp vop) {
-    float cm = kNegInf;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) cm = valid[k] ? fmaxf(cm, x[k]) : cm;
-    cm = group_max(cm);
-    const float mnew = fmaxf(A.m, cm * sl2);
-    // nothing accumulated yet (running max still -inf): no rescale needed
-    const float alpha = A.m == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(A.m - mnew);
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+// Moves the running max of every lane to mnew (>= A.m).  Only when it rose
+// in some lane are the accumulators scaled, each row by its head's
+// exp2(m - mnew): 1 where the max did not move, 0 where nothing was seen
+// yet (m = -inf, the accumulators still zero).
+__device__ __forceinline__ void raise_max(WaveAcc& A, float mnew, int lane) {
+    if (__builtin_amdgcn_ballot_w64(mnew > A.m)) {
+        const float alpha = mnew > A.m ? __builtin_amdgcn_exp2f(A.m - mnew) : 1.0f;
         // rows of acc are columns 4g+i; column j's alpha lives in lanes with n == j
         const int base = (lane & 48) | ((lane >> 4) << 2);
         float ai[4];
@@ -399,6 +394,26 @@ __device__ __forceinline__ void softmax_and_values(WaveAcc& A, const float (&x)[
         A.pz *= alpha;
     }
     A.m = mnew;
+}
+
+// Online-softmax step over the 8 logits x[] (raw q.k, slot order) of this
+// lane's column, then the value contraction with operands vop(ct).  vs/vz:
+// value scale/zero of each slot; valid: slot holds a token.  The weights p*s
+// are split into fp16 high and low parts (22 bits).  LP (limb-packed): rows
+// 0-7 of the value product take the high parts and rows 8-15 the low parts of
+// heads 0-7, one product per column tile; otherwise each part is a product of
+// its own over rows = heads.
+template <bool LP, typename VOp>
+__device__ __forceinline__ void softmax_and_values(WaveAcc& A, const float (&x)[8], const float (&vs)[8],
+                                                   const float (&vz)[8], const bool (&valid)[8], float sl2,
+                                                   int lane, VOp vop) {
+    float cm = kNegInf;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) cm = valid[k] ? max_logit(cm, x[k]) : cm;
+    cm = group_max(cm);
+    const float mnew = max_logit(A.m, cm * sl2);
+    // nothing accumulated yet (running max still -inf): no rescale needed
+    raise_max(A, mnew, lane);
     float w[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -463,38 +478,25 @@ __device__ __forceinline__ float own_logit(float c0, float c1, int lane, bool pa
 // Online-softmax step and value contraction of a limb-packed lane over its 4
 // own slots (x[]: raw q.k, vs/vz: value scale/zero, valid: holds a token).
 // Each lane evaluates the weights p s of its own slots only and forms both
-// fp16 limbs of them (high part and exact low part: 22 bits); the lanes of a
-// head then trade the limbs the other needs by DPP, so that row n of the
-// value product gets the high parts of all 8 slots and row n + 8 the low
-// parts, as before, with each weight evaluated once.  A.l and A.pz hold the
-// lane's share (its own slots): the two lanes of a head are added at the end.
-// TS, TZ: _Float16 where the scales and zeros are stored fp16 values (read
-// by the mixed-precision fmas directly), float otherwise.
+// fp16 limbs of them (high part and low part: 22 bits); the lanes of a head
+// then trade the limbs the other needs by DPP, so that row n of the value
+// product gets the high parts of all 8 slots and row n + 8 the low parts,
+// with each weight evaluated once.  A.l and A.pz hold the lane's share (its
+// own slots): the two lanes of a head are added at the end.  TS, TZ:
+// _Float16 where the scales and zeros are stored fp16 values, float
+// otherwise.
 template <typename TS, typename TZ, typename VOp>
 __device__ __forceinline__ void softmax_and_values_lp(WaveAcc& A, const float (&x)[4], const TS (&vs)[4],
                                                       const TZ (&vz)[4], const bool (&valid)[4], float sl2,
                                                       int lane, VOp vop) {
     float cm = kNegInf;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) cm = valid[k] ? fmaxf(cm, x[k]) : cm;
-    cm = fmaxf(cm, ror8f(cm));   // the partner's 4 slots
+    for (int k = 0; k < 4; ++k) cm = valid[k] ? max_logit(cm, x[k]) : cm;
+    cm = max_logit(cm, ror8f(cm));   // the partner's 4 slots
     cm = group_max(cm);
-    const float mnew = fmaxf(A.m, cm * sl2);
-    const float alpha = A.m == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(A.m - mnew);
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-        const int base = (lane & 48) | ((lane >> 4) << 2);
-        float ai[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, base + i);
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) A.acc[ct][i] *= ai[i];
-        A.l *= alpha;
-        A.pz *= alpha;
-    }
-    A.m = mnew;
-    _Float16 hp[4], lp[4];
+    const float mnew = max_logit(A.m, cm * sl2);
+    raise_max(A, mnew, lane);
+    float w[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         // invalid slots (masked tokens, missing records) contribute nothing,
@@ -502,18 +504,21 @@ __device__ __forceinline__ void softmax_and_values_lp(WaveAcc& A, const float (&
         const float p = valid[k] ? __builtin_amdgcn_exp2f(fmaf(x[k], sl2, -mnew)) : 0.0f;
         A.l += p;
         A.pz = valid[k] ? fmaf(p, (float)vz[k], A.pz) : A.pz;
-        // the weight p s as an fp16 high part (p s rounded once) and the
-        // exact residual p s - hi rounded once: two mixed-precision fmas
-        // reading s in fp16
-        const float s = valid[k] ? (float)vs[k] : 0.0f;
-        hp[k] = (_Float16)__builtin_fmaf(p, s, 0.0f);
-        lp[k] = (_Float16)__builtin_fmaf(p, s, -(float)hp[k]);
+        w[k] = valid[k] ? p * (float)vs[k] : 0.0f;
+    }
+    // the weights as fp16 high parts (w rounded) and low parts (w - hi, exact
+    // in fp32, rounded): 22 bits, two weights per packed conversion
+    h2 hp[2], lp[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        hp[j] = __builtin_convertvector((f2){w[2 * j], w[2 * j + 1]}, h2);
+        lp[j] = __builtin_convertvector((f2){w[2 * j] - (float)hp[j][0], w[2 * j + 1] - (float)hp[j][1]}, h2);
     }
     uint32_t d[4];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const uint32_t H = as_u32(h2{hp[2 * j], hp[2 * j + 1]});
-        const uint32_t Lw = as_u32(h2{lp[2 * j], lp[2 * j + 1]});
+        const uint32_t H = as_u32(hp[j]);
+        const uint32_t Lw = as_u32(lp[j]);
         // slots 0-3: the high lane keeps its own high limbs; the low lane
         // (lanes 8-15 of the row, banks 2-3) takes its partner's low limbs
         d[j] = (uint32_t)__builtin_amdgcn_update_dpp((int)H, (int)Lw, 0x128 /* row_ror:8 */, 0xf, 0xc, false);
@@ -549,25 +554,12 @@ __device__ __forceinline__ void softmax_and_values_tp(WaveAcc& A, const float (&
                                                       int lane, VOp vop) {
     float cm = kNegInf;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) cm = valid[k] ? fmaxf(cm, x[k]) : cm;
-    cm = fmaxf(cm, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, cm),
-                                                                          0x124 /* row_ror:4 */, 0xf, 0xf, true)));
+    for (int k = 0; k < 4; ++k) cm = valid[k] ? max_logit(cm, x[k]) : cm;
+    cm = max_logit(cm, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, cm),
+                                                                              0x124 /* row_ror:4 */, 0xf, 0xf, true)));
     cm = group_max(cm);
-    const float mnew = fmaxf(A.m, cm * sl2);
-    const float alpha = A.m == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(A.m - mnew);
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-        const int base = (lane & 48) | ((lane >> 4) << 2);
-        float ai[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, base + i);
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) A.acc[ct][i] *= ai[i];
-        A.l *= alpha;
-        A.pz *= alpha;
-    }
-    A.m = mnew;
+    const float mnew = max_logit(A.m, cm * sl2);
+    raise_max(A, mnew, lane);
     float w[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
