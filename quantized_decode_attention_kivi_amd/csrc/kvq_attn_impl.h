@@ -46,6 +46,8 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kPart = kD + 4;          // floats per head in a partial: out[128], m, l, pad
@@ -162,24 +164,23 @@ __device__ __forceinline__ h8 levels8(const uint32_t* w, int j, const uint32_t (
 }
 
 // a * b - c elementwise with one fp16 rounding (the exact low part of a * b
-// when c is its rounded value): the subtrahend's sign by the instruction's
-// negate modifiers, which the compiler does not always choose on its own.
+// when c is its rounded value), one packed fma per word with the
+// subtrahend's sign in the instruction's negate modifiers.  Written with the
+// compiler's fma (not inline assembly) so that its hazard tracking covers
+// these instructions next to the matrix products.
+__device__ __forceinline__ h2 fma_sub_h2(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_elementwise_fma(as_h2(a), as_h2(b), -as_h2(c));
+}
 __device__ __forceinline__ h8 fma_sub_h8(h8 a, h8 b, h8 c) {
-    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-    const u4 x = __builtin_bit_cast(u4, a), y = __builtin_bit_cast(u4, b), z = __builtin_bit_cast(u4, c);
-    u4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        asm("v_pk_fma_f16 %0, %1, %2, %3 neg_lo:[0,0,1] neg_hi:[0,0,1]" : "=v"(r[i]) : "v"(x[i]), "v"(y[i]), "v"(z[i]));
-    return __builtin_bit_cast(h8, r);
+    const u32x4 x = __builtin_bit_cast(u32x4, a), y = __builtin_bit_cast(u32x4, b), z = __builtin_bit_cast(u32x4, c);
+    return make_h8(fma_sub_h2(x[0], y[0], z[0]), fma_sub_h2(x[1], y[1], z[1]), fma_sub_h2(x[2], y[2], z[2]),
+                   fma_sub_h2(x[3], y[3], z[3]));
 }
 
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
@@ -620,7 +621,6 @@ constexpr bool rope_fmt(int F) { return F == kFmtRope || F == kFmtRopeCb; }
 constexpr bool cb_fmt(int F) { return F == kFmtKiviCb || F == kFmtRopeCb || F == kFmtKiviCbSp; }
 constexpr bool sp_fmt(int F) { return F == kFmtKiviSp || F == kFmtKiviCbSp; }
 constexpr int kTabPitch = 66;     // float2 per table row: rows of lanes n = 0..15 hit distinct banks
-typedef float f2 __attribute__((ext_vector_type(2)));
 
 struct RopeLds {
     uint64_t phi[64];                 // turns per token of pair i, 0.64 fixed point
