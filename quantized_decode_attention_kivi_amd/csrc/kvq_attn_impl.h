@@ -569,15 +569,17 @@ __device__ __forceinline__ void softmax_and_values_tp(WaveAcc& A, const float (&
         A.pz = valid[k] ? fmaf(p, vz[k], A.pz) : A.pz;
         w[k] = valid[k] ? p * vs[k] : 0.0f;
     }
-    // the lane's limb of each weight: high part, or the exact low part
+    // the lane's limb of each weight, two weights per packed conversion: the
+    // high part (w rounded), or the low part (w - hi, exact in fp32, rounded)
     const bool lo = lane & 8;
-    _Float16 part[4];
+    h2 part[2];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const _Float16 hi = (_Float16)w[k];
-        part[k] = lo ? (_Float16)(w[k] - (float)hi) : hi;
+    for (int j = 0; j < 2; ++j) {
+        const h2 hi = __builtin_convertvector((f2){w[2 * j], w[2 * j + 1]}, h2);
+        const h2 lw = __builtin_convertvector((f2){w[2 * j] - (float)hi[0], w[2 * j + 1] - (float)hi[1]}, h2);
+        part[j] = as_h2(lo ? as_u32(lw) : as_u32(hi));
     }
-    const h2 a = h2{part[0], part[1]}, b = h2{part[2], part[3]}, z = h2{(_Float16)0.0f, (_Float16)0.0f};
+    const h2 a = part[0], b = part[1], z = h2{(_Float16)0.0f, (_Float16)0.0f};
     const h8 wop = (lane & 4) ? make_h8(z, z, a, b) : make_h8(a, b, z, z);
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) A.acc[ct] = mfma(wop, vop(ct), A.acc[ct]);
