@@ -676,10 +676,6 @@ __device__ __forceinline__ void rope_key_tiles(const RopeLds* R, int wave, int l
                                                GetX getx) {
     const int g = lane >> 4, n = lane & 15;
     C[0] = C[1] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    // -1, opaque: keeps lo = fma(hi, -1, k) one mixed-precision fma with an
-    // fp16 result instead of being rewritten as a conversion and a subtraction
-    float m1 = -1.0f;
-    asm volatile("" : "+v"(m1));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int i0 = 16 * g + 4 * j;
@@ -691,7 +687,7 @@ __device__ __forceinline__ void rope_key_tiles(const RopeLds* R, int wave, int l
             getx(rt, j, x);
             const f4 bs[2] = {*(const __attribute__((address_space(3))) f4*)&R->base[wave][rt][i0],
                               *(const __attribute__((address_space(3))) f4*)&R->base[wave][rt][i0 + 2]};
-            h8 hi, lo;
+            h2 hi[4], lo[4];
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 const f4 b = bs[p >> 1], t = ts[p >> 1];
@@ -700,15 +696,13 @@ __device__ __forceinline__ void rope_key_tiles(const RopeLds* R, int wave, int l
                 const float Sn = b[o + 1] * t[o] + b[o] * t[o + 1];
                 const float k0 = Cs * x[2 * p] - Sn * x[2 * p + 1];
                 const float k1 = Sn * x[2 * p] + Cs * x[2 * p + 1];
-                const _Float16 h0 = (_Float16)k0, h1 = (_Float16)k1;
-                hi[2 * p] = h0;
-                hi[2 * p + 1] = h1;
-                // k - hi is exact in fp32: one mixed-precision fma per element
-                lo[2 * p] = (_Float16)__builtin_fmaf((float)h0, m1, k0);
-                lo[2 * p + 1] = (_Float16)__builtin_fmaf((float)h1, m1, k1);
+                // the pair's fp16 high parts (one packed conversion) and low
+                // parts k - hi (exact in fp32), rounded
+                hi[p] = __builtin_convertvector((f2){k0, k1}, h2);
+                lo[p] = __builtin_convertvector((f2){k0 - (float)hi[p][0], k1 - (float)hi[p][1]}, h2);
             }
-            C[rt] = mfma(hi, Q.q[j], C[rt]);
-            C[rt] = mfma(lo, Q.q[j], C[rt]);
+            C[rt] = mfma(make_h8(hi[0], hi[1], hi[2], hi[3]), Q.q[j], C[rt]);
+            C[rt] = mfma(make_h8(lo[0], lo[1], lo[2], lo[3]), Q.q[j], C[rt]);
         }
     }
 }
