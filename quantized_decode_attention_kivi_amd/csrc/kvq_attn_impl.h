@@ -425,13 +425,15 @@ __device__ __forceinline__ void softmax_and_values(WaveAcc& A, const float (&x)[
         A.pz = valid[k] ? fmaf(p, vz[k], A.pz) : A.pz;
         w[k] = valid[k] ? p * vs[k] : 0.0f;
     }
-    h8 whi, wlo;
+    // fp16 high parts (w rounded) and low parts (w - hi, exact in fp32,
+    // rounded), two weights per packed conversion
+    h2 hp[4], lp[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const _Float16 hi = (_Float16)w[k];
-        whi[k] = hi;
-        wlo[k] = (_Float16)(w[k] - (float)hi);
+    for (int j = 0; j < 4; ++j) {
+        hp[j] = __builtin_convertvector((f2){w[2 * j], w[2 * j + 1]}, h2);
+        lp[j] = __builtin_convertvector((f2){w[2 * j] - (float)hp[j][0], w[2 * j + 1] - (float)hp[j][1]}, h2);
     }
+    const h8 whi = make_h8(hp[0], hp[1], hp[2], hp[3]), wlo = make_h8(lp[0], lp[1], lp[2], lp[3]);
     if (LP) {
         const h8 wop = (lane & 8) ? wlo : whi;
 #pragma unroll
