@@ -246,10 +246,13 @@ __device__ __forceinline__ u32x4 record_desc(const uint8_t* rec, int bytes) {
 // stored in 16-byte chunks: INT8 layer 106 -> 145 us); lanes of 32 bytes read
 // in two halves are not (INT4 values at G = 32; 8-bit values at G = 16:
 // INT8 and FP8 8 x 32K layers at G = 16, 89.5 and 84.1 us with nt, 89.4 and
-// 84.7 us without, same box).
+// 84.7 us without, same box).  The compiler's hazard tracking does not see
+// inside the assembly, so the one wait state this chip family needs between a
+// scalar write of M0 and a direct-to-LDS load reading it is written here.
 __device__ __forceinline__ void lds_load16(u32x4 desc, lds_u8* dst, int off) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(off), "s"(desc), "{m0}"(m0) : "memory");
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(off), "s"(desc), "{m0}"(m0)
+                 : "memory");
 }
 
 // Issues the direct-to-LDS loads of one unit into stage buffer `buf` (wave
