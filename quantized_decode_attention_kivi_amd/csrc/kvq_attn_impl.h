@@ -254,6 +254,23 @@ __device__ __forceinline__ void lds_load16(u32x4 desc, lds_u8* dst, int off) {
     asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(off), "s"(desc), "{m0}"(m0)
                  : "memory");
 }
+// The same with the instruction's offset field K, which moves the LDS
+// destination (m0 + K + 16*lane) and the record offset alike: loads whose LDS
+// offsets inside the stage buffer equal their record offsets share one M0
+// value (one scalar write and one wait state per unit instead of one per
+// load).  off >= K in every lane; FIRST: the load right after M0 is written.
+template <int K, bool FIRST>
+__device__ __forceinline__ void lds_load16_at(u32x4 desc, uint32_t m0, int off) {
+    static_assert(K >= 0 && K < 4096, "the offset field holds 12 bits");
+    if constexpr (FIRST)
+        asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen offset:%3 nt lds" ::"v"(off - K), "s"(desc),
+                     "{m0}"(m0), "n"(K)
+                     : "memory");
+    else
+        asm volatile("buffer_load_dwordx4 %0, %1, 0 offen offset:%3 nt lds" ::"v"(off - K), "s"(desc), "{m0}"(m0),
+                     "n"(K)
+                     : "memory");
+}
 
 // Issues the direct-to-LDS loads of one unit into stage buffer `buf` (wave
 // uniform address) and returns which of its records exist.  Every call issues
@@ -276,6 +293,23 @@ __device__ __forceinline__ uint32_t issue_unit(lds_u8* buf, const Layout& L, con
         const uint8_t* rec = grp < ngroups ? record_at_t<PG>(L, c.packed, c.block_table, b, h, grp) : nullptr;
         has |= (rec != nullptr) << i;
         const u32x4 rs = record_desc(rec, L.record);
+        if constexpr (G == 32 && KB == 2 && VB == 2) {
+            // record sections at the same offsets as in the stage buffer
+            // (key codes 0, value codes 1024, tables 2048): one M0 value
+            const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)buf);
+            const int rt = lane >> 5, gh = (lane >> 4) & 1;
+            lds_load16_at<S::KC, true>(rs, m0, (16 * rt + n) * 32 + 16 * gh);
+            lds_load16_at<S::VC, false>(rs, m0, L.vcode_off + S::VW * 4 * lane);
+            // tables: lanes past them read out of range (zeros into the
+            // stage buffer's unused tail, below PITCH) rather than branch,
+            // so that the three loads stay in one block under one M0 write
+            static_assert(S::META + 16 * 64 <= S::PITCH, "the table load's idle lanes land in the stage");
+            const int nt = 32 + (SP ? G / 2 : G / 4);
+            lds_load16_at<S::META, false>(rs, m0, lane < 32   ? L.kmeta_off + 16 * lane
+                                                  : lane < nt ? L.vmeta_off + 16 * (lane - 32)
+                                                              : 0x40000000);
+            continue;
+        }
         if (G == 32) {
             if (KB == 4) {
                 lds_load16(rs, buf + S::KC, n * 64 + 16 * g);
@@ -416,7 +450,6 @@ __device__ __forceinline__ void softmax_and_values(WaveAcc& A, const float (&x)[
     for (int k = 0; k < 8; ++k) cm = valid[k] ? max_logit(cm, x[k]) : cm;
     cm = group_max(cm);
     const float mnew = max_logit(A.m, cm * sl2);
-    // nothing accumulated yet (running max still -inf): no rescale needed
     raise_max(A, mnew, lane);
     float w[8];
 #pragma unroll
