@@ -21,6 +21,7 @@ struct QuantSmem {
     int red[2][4];                    // dense-and-sparse: per-wave counts (double-buffered)
     uint32_t kept[G * kD / 32];       // dense-and-sparse: kept positions, one bit each
     int wtot[2];                      // dense-and-sparse: kept count of the first two words' waves
+    uint2 cb4[240];                   // 4-bit codebook: per 1/16 of a grid step (threshold bits, code)
 };
 
 // Shared memory of the uniform-grid and 8-bit quantizers: the channel
@@ -147,6 +148,33 @@ __device__ __forceinline__ uint32_t code_of(float x, float z, float inv, const f
     }
 }
 
+// The 4-bit codebook code by table: t = (x - z) * inv falls in bin
+// i = floor(16 t) (exact: a power-of-two scale), clamped to [0, 239]; the
+// code counts the midpoints passed, which is the count at the bin's start
+// plus at most one more (neighbouring midpoints are more than 1/16 of a
+// step apart), passed when t exceeds the bin's threshold: the next midpoint
+// m, or for a midpoint whose tie goes up (odd index, t >= m) the float just
+// below it.  Equal to cb_code for every fp32 t.  Built by threads 0..239.
+__device__ __forceinline__ void cb4_table(uint2 (&tab)[240], const float (&mid)[15], int tid) {
+    if (tid < 240) {
+        const float a = (float)tid * 0.0625f;
+        const uint32_t lo = cb_code<15>(a, mid);
+        uint32_t thr = 0x7f800000u;   // +inf: no midpoint left
+        if (lo < 15) {
+            const uint32_t mb = __builtin_bit_cast(uint32_t, mid[lo]);
+            thr = (lo & 1) ? mb - 1 : mb;   // (mid > 0: the next float below is bits - 1)
+        }
+        tab[tid] = make_uint2(thr, lo);
+    }
+}
+__device__ __forceinline__ uint32_t cb4_code(float x, float z, float inv, const uint2 (&tab)[240]) {
+#pragma clang fp contract(off)
+    const float t = (x - z) * inv;
+    const int i = min(max((int)(t * 16.0f), 0), 239);
+    const uint2 e = tab[i];
+    return e.y + (t > __builtin_bit_cast(float, e.x) ? 1u : 0u);
+}
+
 // Quantize G consecutive fp16 rows of keys (ksrc) and values (vsrc) into one
 // record.  Called by all 256 threads of a workgroup.  Thread (ts = tid/16,
 // cg = tid%16) holds channels 8cg..8cg+7 of tokens ts, ts+16, ...  CB: the
@@ -178,6 +206,8 @@ __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* 
             vx[j][2 * e + 1] = h2f(bw[e] >> 16);
         }
     }
+    // 4-bit codebook: its bin table (read after the barriers below)
+    if constexpr (CB && (KB == 4 || VB == 4)) cb4_table(sm.cb4, KB == 4 ? L.kmid : L.vmid, tid);
     // dense-and-sparse: the kept extremes leave the channels' ranges
     uint32_t kbit[NT] = {};
     if constexpr (SP) select_extremes<G>(sm, kraw, kbit, ksrc, (uint32_t*)(rec + L.sparse_off));
@@ -249,7 +279,9 @@ __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* 
         uint32_t w = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const uint32_t q = SP && ((kbit[j] >> e) & 1) ? 0u : code_of<CB, KB>(kx[j][e], kzr[e], kir[e], L.kmid);
+            const uint32_t q = SP && ((kbit[j] >> e) & 1) ? 0u
+                               : CB && KB == 4 ? cb4_code(kx[j][e], kzr[e], kir[e], sm.cb4)
+                                               : code_of<CB, KB>(kx[j][e], kzr[e], kir[e], L.kmid);
             w |= q << (KB == 4 ? code_bit(4, e) : code_bit(2, e + 8 * (cg & 1)));
         }
         if (KB == 4) {
@@ -262,8 +294,13 @@ __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* 
         uint32_t v0 = 0, v1 = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            v0 |= code_of<CB, VB>(vx[j][e], pv[j].z, pv[j].inv, L.vmid) << (8 * e);
-            v1 |= code_of<CB, VB>(vx[j][e + 4], pv[j].z, pv[j].inv, L.vmid) << (8 * e);
+            if constexpr (CB && VB == 4) {
+                v0 |= cb4_code(vx[j][e], pv[j].z, pv[j].inv, sm.cb4) << (8 * e);
+                v1 |= cb4_code(vx[j][e + 4], pv[j].z, pv[j].inv, sm.cb4) << (8 * e);
+            } else {
+                v0 |= code_of<CB, VB>(vx[j][e], pv[j].z, pv[j].inv, L.vmid) << (8 * e);
+                v1 |= code_of<CB, VB>(vx[j][e + 4], pv[j].z, pv[j].inv, L.vmid) << (8 * e);
+            }
         }
         *(uint2*)&sm.vcode[t][8 * cg] = make_uint2(v0, v1);
     }
