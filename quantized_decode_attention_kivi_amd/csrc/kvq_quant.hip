@@ -59,19 +59,13 @@ __device__ __forceinline__ void store_once8(uint8_t* p, uint32_t a, uint32_t b) 
     __builtin_nontemporal_store(u32x2{a, b}, (u32x2*)p);
 }
 
-__device__ __forceinline__ int wave_sum_i(int x) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o);
-    return x;
-}
-
 // Dense-and-sparse keys ("KV Cache compression lab", experiment 03: KVQuant
 // keeps the few extreme keys in fp16 as a sparse matrix).  Marks in kbit[]
 // the group's G entries of largest |x| (ties: lower position) and writes
 // them, in ascending position order, as (position, fp16) pairs at `sparse`.
-// Each entry's key ((|x| bits) << 12 | (4095 - position)) is unique, so the
-// G-th largest key, found bit by bit from the top by counting keys at or
-// above each candidate, selects exactly G entries.  All 256 threads.
+// Each entry's key ((|x| bits) << 12 | (4095 - position)) is unique, so a
+// threshold found bit by bit from the top, by counting keys at or above each
+// candidate, selects exactly G entries.  All 256 threads.
 template <int G>
 __device__ __forceinline__ void select_extremes(QuantSmem<G>& sm, const uint32_t (&kb)[G / 16][8],
                                                 uint32_t (&kbit)[G / 16], const half_t* __restrict__ ksrc,
@@ -84,20 +78,54 @@ __device__ __forceinline__ void select_extremes(QuantSmem<G>& sm, const uint32_t
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             key[j][e] = ((kb[j][e] & 0x7fffu) << 12) | (4095u - (uint32_t)((ts + 16 * j) * kD + 8 * cg + e));
-    uint32_t T = 0;
+    // The group's G largest keys are among the G largest of each wave's
+    // quarter.  Each wave finds a threshold with exactly G of its keys at or
+    // above it (counts by ballot: no barrier; the search stops at the first
+    // candidate with exactly G), writes those G keys to LDS, and the first
+    // wave finds the G-th largest of the 4G, which is the group's.
+    uint32_t Tw = 0;
     for (int bit = 26; bit >= 0; --bit) {
-        const uint32_t cand = T | (1u << bit);
+        const uint32_t cand = Tw | (1u << bit);
         int cnt = 0;
 #pragma unroll
         for (int j = 0; j < NT; ++j)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) cnt += key[j][e] >= cand ? 1 : 0;
-        cnt = wave_sum_i(cnt);
-        if (lane == 0) sm.red[bit & 1][wave] = cnt;
-        __syncthreads();
-        cnt = sm.red[bit & 1][0] + sm.red[bit & 1][1] + sm.red[bit & 1][2] + sm.red[bit & 1][3];
-        if (cnt >= G) T = cand;
+            for (int e = 0; e < 8; ++e) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[j][e] >= cand));
+        if (cnt >= G) {
+            Tw = cand;
+            if (cnt == G) break;   // exactly G at or above: the lower bits change nothing
+        }
     }
+    uint32_t* cands = sm.kept;   // 4G words, free until the marking below
+    int base = wave * G;
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const bool up = key[j][e] >= Tw;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(up);
+            const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+            if (up) cands[base + below] = key[j][e];
+            base += (int)__builtin_popcountll(m);
+        }
+    __syncthreads();
+    if (wave == 0) {
+        constexpr int PL = 4 * G / 64;   // candidates per lane: 2 (G = 32) or 1
+        uint32_t c[PL];
+#pragma unroll
+        for (int i = 0; i < PL; ++i) c[i] = cands[64 * i + lane];
+        uint32_t T = 0;
+        for (int bit = 26; bit >= 0; --bit) {
+            const uint32_t cand = T | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int i = 0; i < PL; ++i) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(c[i] >= cand));
+            if (cnt >= G) T = cand;   // the exact G-th largest: every key of the group is tested against it
+        }
+        if (lane == 0) sm.red[0][0] = (int)T;
+    }
+    __syncthreads();
+    const uint32_t T = (uint32_t)sm.red[0][0];
     for (int i = tid; i < G * kD / 32; i += 256) sm.kept[i] = 0;
     __syncthreads();
 #pragma unroll
