@@ -69,10 +69,9 @@ __device__ __forceinline__ h8 words_h8(uint4 w) {
     return make_h8(as_h2(w.x), as_h2(w.y), as_h2(w.z), as_h2(w.w));
 }
 
-// Maximum of two logits (finite, or -inf for nothing seen).  The
-// NaN-propagating form is one instruction (v_maximum3_f32); fmaxf would first
-// quiet each operand the compiler cannot prove canonical, such as a value
-// received from another lane, at one extra instruction per operand.
+// Maximum of two logits (finite, or -inf for nothing seen): one max
+// instruction (these sources are built without NaN semantics, so no operand
+// is quieted first, and a move from another lane folds into it as DPP).
 __device__ __forceinline__ float max_logit(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 // Max over the four lane groups (lanes l, l^16, l^32, l^48).
