@@ -309,7 +309,9 @@ class QuantizedKVCache:
             v.packed = self.packed
         else:
             per = v.sizes.packed_bytes
-            v.packed = self.packed[b * per:(b + 1) * per]
+            # no group records at this capacity: the parent's placeholder
+            # (a zero-size slice has no address to hand over)
+            v.packed = self.packed[b * per:(b + 1) * per] if per else self.packed
         v.k_res = self.k_res[b * per_ring:(b + 1) * per_ring]
         v.v_res = self.v_res[b * per_ring:(b + 1) * per_ring]
         v.n_tokens = self.n_tokens[b:b + 1]
@@ -341,7 +343,7 @@ class QuantizedKVCache:
         v._view = True
         s = b * self.shape.num_kv_heads + h
         per = v.sizes.packed_bytes
-        v.packed = self.packed[s * per:(s + 1) * per]
+        v.packed = self.packed[s * per:(s + 1) * per] if per else self.packed
         per_ring = v.sizes.residual_bytes // 2
         v.k_res = self.k_res[s * per_ring:(s + 1) * per_ring]
         v.v_res = self.v_res[s * per_ring:(s + 1) * per_ring]

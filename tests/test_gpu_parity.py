@@ -15,8 +15,8 @@ import torch
 import oracle
 from quantized_decode_attention_kivi_amd import synth
 from quantized_decode_attention_kivi_amd.kvq import num_quantized as kvq_num_quantized
-from parity_util import (compare_attention, compare_codes, make_cache, oracle_attention, oracle_states,
-                         to_bits)
+from parity_util import (compare_attention, compare_codes, compare_stream_codes, make_cache, oracle_attention,
+                         oracle_states, to_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,6 +84,40 @@ def test_edge_lengths_in_one_batch():
     assert np.all(out[0] == 0)  # n = 0 gives 0
     ref = oracle_attention(to_bits(q), states, SCALE)
     compare_attention(out, ref)
+
+
+def test_cache_without_group_capacity():
+    """A contiguous cache too short ever to flush a group (max_tokens below
+    R + G): it holds no group records, every token stays in the residual
+    window.  Prefill, appends, exports through sequence and stream views, and
+    attention all work on it; the views hand over the cache's placeholder
+    record buffer, since a zero-size slice has no address."""
+    G, R, cap = 32, 32, 43
+    w = _w("llama3_8b_layer_b8_32k_int4", name="nogroups", num_seqs=3, num_kv_heads=2, num_q_heads=8, k_bits=2,
+           v_bits=2, group_size=G, residual=R, context=cap, tag=34)
+    lens0, steps = np.array([0, 20, 7], np.int64), 20
+    K, V = synth.make_kv(w, max_len=cap, device="cuda")
+    cache = make_cache(w, lens0 + steps, max_tokens=cap)
+    assert cache.sizes.packed_bytes == 0
+    print("no-group cache: lens=%s steps=%d cap=%d" % (list(lens0), steps, cap), flush=True)
+    m = int(lens0.max())
+    cache.prefill(K[:, :, :m].contiguous(), V[:, :, :m].contiguous(), lens0)
+    kb, vb = to_bits(K), to_bits(V)
+    states = oracle_states(kb[:, :, :m], vb[:, :, :m], lens0, w, cap=cap)
+    lens = lens0.copy()
+    for _ in range(steps):
+        cache.append(torch.stack([K[b, :, int(lens[b])] for b in range(3)]).contiguous(),
+                     torch.stack([V[b, :, int(lens[b])] for b in range(3)]).contiguous())
+        for b in range(3):
+            for h in range(2):
+                states[b][h].append(kb[b, h, int(lens[b])], vb[b, h, int(lens[b])])
+        lens += 1
+    assert all(st.nq == 0 for row in states for st in row)
+    compare_codes(cache, states)
+    compare_stream_codes(cache, 1, 1, states[1][1])
+    q = synth.make_query(w, device="cuda")
+    out = cache.decode_attention(q, SCALE).cpu().numpy()
+    compare_attention(out, oracle_attention(to_bits(q), states, SCALE))
 
 
 @pytest.mark.parametrize("case,arrivals", [("gqa4_int4_ragged", True), ("gqa16_k4v2_g16", True),
@@ -270,7 +304,7 @@ def test_full_size_80_layer_cache():
     each -- must match bit for bit in codes, scales, zeros and dequantized
     values."""
     from concurrent.futures import ThreadPoolExecutor
-    from parity_util import THREADS, compare_stream_codes
+    from parity_util import THREADS
     w = synth.WORKLOADS["llama3_70b_cache_80l_128k_int2"]
     lens = synth.seq_lengths(w)
     L = int(lens.max())
