@@ -3,7 +3,9 @@ mixed with group sizes, residual windows, query heads per kv head, ragged
 lengths (empty sequences included) and contiguous or paged caches.  Each
 configuration is prefilled, then appended until every sequence has flushed
 at least one group, and compared with the oracle: codes, scales, zeros and dequantized values
-bit for bit, attention within max-abs 2e-3 and per-row cosine 0.9999.
+bit for bit, attention within max-abs 2e-3 and per-row cosine 0.9999; the
+split entry points (partials, then merge) and the no-allocation entry point
+must equal the combined call bit for bit.
 The configurations come from a fixed seed, so the set is the same on every
 run; each one prints its parameters before touching the GPU."""
 import dataclasses
@@ -78,3 +80,11 @@ def test_random_configuration(i):
     out = cache.decode_attention(q, SCALE)
     torch.cuda.synchronize()
     compare_attention(out.cpu().numpy(), oracle_attention(to_bits(q), states, SCALE, rope_base=w.rope_theta))
+    # the split entry points and the no-allocation entry point compute the
+    # same thing as the combined call, bit for bit
+    ev = tuple(torch.cuda.Event() for _ in range(3))
+    split = cache.decode_attention(q, SCALE, split_events=ev)
+    noalloc = torch.empty_like(out)
+    kvq.kv_decode_attention_noalloc(cache.cfg, cache.cache, q, w.num_q_heads, SCALE, noalloc)
+    torch.cuda.synchronize()
+    assert torch.equal(split, out) and torch.equal(noalloc, out)
