@@ -7,7 +7,8 @@ ring) followed by decode attention of one query token per sequence over the
 whole cache (kv_decode_attention: quantized part dequantized in-kernel,
 fp16 residual, split merge).  Bulk quantization of the prompt
 (kv_quantize_prefill) runs once per request, so it is timed as its own leg
-over the same batch and reported as the quantize rate.
+over the same batch and reported as the quantize rate; kv_dequantize, the
+verification path, is timed over single sequences of the same cache.
 
 Timing is taken with HIP events recorded on the stream the kernels run on.
 Every step reads a different copy of the packed cache (enough copies to
@@ -119,6 +120,49 @@ def prefill_bytes(lens, w, d=128):
         tot += w.num_kv_heads * (int(n) * d * 2 * 2 + nq * d * (w.k_bits + w.v_bits) // 8
                                  + meta_bytes(nq, w, d) + (int(n) - nq) * d * 2 * 2)
     return tot
+
+
+def dequantize_bytes(n, w, d=128):
+    """kv_dequantize of one sequence holding n tokens: its records and fp16
+    residual read, fp32 keys and values written (per kv head)."""
+    nq = n_quant(int(n), w.group_size, w.residual, w.kv_format)
+    per_head = nq * d * (w.k_bits + w.v_bits) // 8 + meta_bytes(nq, w, d) + (int(n) - nq) * d * 2 * 2
+    return w.num_kv_heads * (per_head + int(n) * d * 4 * 2)
+
+
+def dequantize_leg(torch, caches, lens, w, stream, calls=16):
+    """kv_dequantize (the verification path), timed one sequence per call
+    through read-only sequence views, rotating over the sequences and cache
+    copies; returns (microseconds per call, GB/s, description)."""
+    from quantized_decode_attention_kivi_amd import kvq
+    nv = min(calls, w.num_seqs * len(caches))
+    views = [caches[i % len(caches)].sequence_view((i * 7) % w.num_seqs) for i in range(nv)]
+    T = int(max(int(lens[(i * 7) % w.num_seqs]) for i in range(nv)))
+    ko = torch.empty((1, w.num_kv_heads, max(T, 1), 128), dtype=torch.float32, device=caches[0].device)
+    vo = torch.empty_like(ko)
+
+    def call(i):
+        v = views[i]
+        n = int(lens[(i * 7) % w.num_seqs])
+        kvq.kv_dequantize(v.cfg, v.cache, ko, vo, n, stream)
+        return n
+
+    for i in range(min(nv, 4)):
+        call(i)
+    evs, nbytes = [], 0
+    for r in range(2):
+        for i in range(nv):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            n = call(i)
+            e1.record(stream)
+            evs.append((e0, e1))
+            nbytes += dequantize_bytes(n, w)
+    torch.cuda.synchronize()
+    t = sum(a.elapsed_time(b) for a, b in evs) / 1e3
+    desc = ("%d calls, each one sequence (%d kv heads, up to %d tokens) of the cache: records and residual "
+            "read, fp32 keys and values written" % (len(evs), w.num_kv_heads, T))
+    return t / len(evs) * 1e6, nbytes / t / 1e9, desc
 
 
 def source_digest(paths):
@@ -396,6 +440,7 @@ def main():
     torch.cuda.synchronize()
     pre_t = float(np.mean([a.elapsed_time(b) for a, b in pre_ms]))
     pbytes = prefill_bytes(lens, w)
+    deq_us, deq_gbs, deq_desc = dequantize_leg(torch, caches, lens, w, stream)
     if args.no_cpu_baseline:
         del K, V
         K = V = None
@@ -527,6 +572,9 @@ def main():
         "quantize_tokens_per_s": round(float(lens.sum()) / (pre_t / 1e3), 1),
         "quantize_gbs": round(pbytes / (pre_t / 1e3) / 1e9, 2),
         "quantize_us": round(pre_t * 1e3, 3),
+        "dequantize_us": round(deq_us, 3),
+        "dequantize_gbs": round(deq_gbs, 2),
+        "dequantize_sample": deq_desc,
         "roofline": {
             "bound": "hbm",
             "achieved": round(kern_achieved, 2),

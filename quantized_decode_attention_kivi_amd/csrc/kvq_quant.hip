@@ -1102,44 +1102,103 @@ __global__ __launch_bounds__(256) void append_counters_kernel(Layout L, kvq_cach
 // per block; thread -> token t = tid/16, channels (tid%16)*8 .. +8.
 // ---------------------------------------------------------------------------
 
+// Largest record of any format (INT8 at G = 32; at G = 16 two records of a
+// 32-token block take the same bytes).
+constexpr int kMaxRecordBytes = 8448;
+
+// Value of key (token tg of the record, channel ch) from a record in LDS; the
+// arithmetic of the quantizer's dequantization (one fma, or code times the
+// static FP8 scale).
+__device__ __forceinline__ float deq_key(const Layout& L, const kvq_cache& c, const uint8_t* rec, int h, int tg,
+                                         int ch) {
+    const uint32_t kcd = kcode_at(L, rec, tg, ch);
+    if (L.fmt == kFmtFp8) {
+#pragma clang fp contract(off)
+        return fp8_value(kcd) * c.k_scale[h];
+    }
+    const bool tok = L.fmt == kFmtInt8;   // per-token key scale and zero
+    const bool cb = L.grid == KVQ_GRID_NORMAL_QUANTILE;
+    return fmaf(cb ? cb_level(L.klut, kcd, L.kbits) : (float)kcd,
+                h2f(tok ? ktok_scale_bits(L, rec, tg) : kscale_bits(L, rec, ch)),
+                h2f(tok ? ktok_zero_bits(L, rec, tg) : kzero_bits(L, rec, ch)));
+}
+__device__ __forceinline__ float deq_value(const Layout& L, const kvq_cache& c, const uint8_t* rec, int h, int tg,
+                                           int ch) {
+    const uint32_t vcd = vcode_at(L, rec, tg, ch);
+    if (L.fmt == kFmtFp8) {
+#pragma clang fp contract(off)
+        return fp8_value(vcd) * c.v_scale[h];
+    }
+    const bool cb = L.grid == KVQ_GRID_NORMAL_QUANTILE;
+    return fmaf(cb ? cb_level(L.vlut, vcd, L.vbits) : (float)vcd, h2f(vscale_bits(L, rec, tg)),
+                h2f(vzero_bits(L, rec, tg)));
+}
+
+// kv_dequantize: 32 tokens of one stream per workgroup (grid
+// (ceil(out_tokens / 32), B*H), 256 threads).  The records holding them
+// (32 / G) are copied to LDS with 16-byte loads; then each thread writes 4
+// consecutive channels of a token per 16-byte store, keys and values, 4 of
+// each: quantized tokens from the records, ring tokens converted from fp16,
+// zeros past the sequence's end.
+// KB, VB, G, F, CB: the layout's bit widths, group size, format and grid,
+// fixed at compile time (written into a copy of the layout, so that the
+// position helpers fold to shifts and masks).
+template <int KB, int VB, int G, int F, bool CB>
 __global__ __launch_bounds__(256) void dequantize_kernel(Layout L, kvq_cache c, float* ko, float* vo,
                                                          int out_tokens) {
+    L.kbits = KB;
+    L.vbits = VB;
+    L.G = G;
+    L.spt = G == 16 ? 4 : 8;
+    L.fmt = F;
+    L.grid = CB ? KVQ_GRID_NORMAL_QUANTILE : KVQ_GRID_UNIFORM;
+    __shared__ __align__(16) uint8_t srec[kMaxRecordBytes];
     const int sh = blockIdx.y;
     const int b = sh / L.H, h = sh % L.H;
-    const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int c0 = (threadIdx.x & 15) * 8;
-    if (t >= out_tokens) return;
+    const int t0 = blockIdx.x * 32;
+    const int tid = threadIdx.x;
     const int nq = max(c.n_quant[b], 0);
     const int n = min(max(c.n_tokens[b], nq), nq + L.ring);
-    float* kd = ko + ((long)sh * out_tokens + t) * kD + c0;
-    float* vd = vo + ((long)sh * out_tokens + t) * kD + c0;
-    const uint8_t* rec = t < nq ? record_at(L, c.packed, c.block_table, b, h, t / L.G) : nullptr;
-    const int tg = t % L.G;
-    for (int i = 0; i < 8; ++i) {
-        const int ch = c0 + i;
-        float kv = 0.0f, vv = 0.0f;
-        if (t < nq) {
-            if (rec && L.fmt == kFmtFp8) {
-#pragma clang fp contract(off)
-                kv = fp8_value(kcode_at(L, rec, tg, ch)) * c.k_scale[h];
-                vv = fp8_value(vcode_at(L, rec, tg, ch)) * c.v_scale[h];
-            } else if (rec) {
-                const bool tok = L.fmt == kFmtInt8;   // per-token key scale and zero
-                const bool cb = L.grid == KVQ_GRID_NORMAL_QUANTILE;
-                const uint32_t kcd = kcode_at(L, rec, tg, ch), vcd = vcode_at(L, rec, tg, ch);
-                kv = fmaf(cb ? cb_level(L.klut, kcd, L.kbits) : (float)kcd,
-                          h2f(tok ? ktok_scale_bits(L, rec, tg) : kscale_bits(L, rec, ch)),
-                          h2f(tok ? ktok_zero_bits(L, rec, tg) : kzero_bits(L, rec, ch)));
-                vv = fmaf(cb ? cb_level(L.vlut, vcd, L.vbits) : (float)vcd, h2f(vscale_bits(L, rec, tg)),
-                          h2f(vzero_bits(L, rec, tg)));
+    const int nr = 32 / L.G;
+    uint32_t has = 0;
+    for (int r = 0; r < nr; ++r) {
+        const int tr = t0 + r * L.G;
+        const uint8_t* rec = tr < nq ? record_at(L, c.packed, c.block_table, b, h, tr / L.G) : nullptr;
+        if (!rec) continue;
+        has |= 1u << r;
+        uint4* dst = (uint4*)(srec + r * L.record);
+        for (int i = tid; i < L.record / 16; i += 256) dst[i] = ((const uint4*)rec)[i];
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int side = 0; side < 2; ++side) {
+        float* out = side ? vo : ko;
+        const half_t* res = (const half_t*)(side ? c.v_res : c.k_res);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int idx = tid + 256 * k;   // (token, channel quad) of the block
+            const int t = t0 + (idx >> 5), c4 = (idx & 31) * 4;
+            if (t >= out_tokens) continue;
+            float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (t < nq) {
+                const int r = (t - t0) / L.G;
+                if ((has >> r) & 1) {
+                    const uint8_t* rec = srec + r * L.record;
+                    const int tg = t % L.G;
+                    float e[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        e[i] = side ? deq_value(L, c, rec, h, tg, c4 + i) : deq_key(L, c, rec, h, tg, c4 + i);
+                    o = make_float4(e[0], e[1], e[2], e[3]);
+                }
+            } else if (t < n) {
+                const half_t* row = res + ((long)sh * L.ring + (t % L.ring)) * kD + c4;
+                o = make_float4((float)row[0], (float)row[1], (float)row[2], (float)row[3]);
             }
-        } else if (t < n) {
-            const long row = ((long)sh * L.ring + (t % L.ring)) * kD + ch;
-            kv = (float)((const half_t*)c.k_res)[row];
-            vv = (float)((const half_t*)c.v_res)[row];
+            const u32x4 ob = u32x4{__float_as_uint(o.x), __float_as_uint(o.y), __float_as_uint(o.z),
+                                   __float_as_uint(o.w)};
+            __builtin_nontemporal_store(ob, (u32x4*)(out + ((long)sh * out_tokens + t) * kD + c4));
         }
-        kd[i] = kv;
-        vd[i] = vv;
     }
 }
 
@@ -1280,8 +1339,22 @@ hipError_t launch_append(const Layout& L, const kvq_cache& c, const half_t* k, c
 hipError_t launch_dequantize(const Layout& L, const kvq_cache& c, float* ko, float* vo, int out_tokens,
                              hipStream_t s) {
     if (out_tokens <= 0) return hipSuccess;
-    dim3 grid((out_tokens + 15) / 16, L.B * L.H);
-    hipLaunchKernelGGL(dequantize_kernel, grid, dim3(256), 0, s, L, c, ko, vo, out_tokens);
+    static_assert(kMaxRecordBytes % 16 == 0, "records are copied in 16-byte pieces");
+    if (L.record > kMaxRecordBytes * L.G / 32) return hipErrorInvalidValue;
+    dim3 grid((out_tokens + 31) / 32, L.B * L.H);
+    const bool cb = L.grid == KVQ_GRID_NORMAL_QUANTILE;
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, L, c, ko, vo, out_tokens); };
+#define KVQ_DEQ_G(KB, VB, F, CB) \
+    (L.G == 16 ? go(dequantize_kernel<KB, VB, 16, F, CB>) : go(dequantize_kernel<KB, VB, 32, F, CB>))
+#define KVQ_DEQ_LOWBIT(KB, VB) (cb ? KVQ_DEQ_G(KB, VB, kFmtKivi, true) : KVQ_DEQ_G(KB, VB, kFmtKivi, false))
+    if (L.fmt == kFmtInt8) KVQ_DEQ_G(8, 8, kFmtInt8, false);
+    else if (L.fmt == kFmtFp8) KVQ_DEQ_G(8, 8, kFmtFp8, false);
+    else if (L.kbits == 2 && L.vbits == 2) KVQ_DEQ_LOWBIT(2, 2);
+    else if (L.kbits == 2) KVQ_DEQ_LOWBIT(2, 4);
+    else if (L.vbits == 2) KVQ_DEQ_LOWBIT(4, 2);
+    else KVQ_DEQ_LOWBIT(4, 4);
+#undef KVQ_DEQ_LOWBIT
+#undef KVQ_DEQ_G
     if (L.sparse) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
