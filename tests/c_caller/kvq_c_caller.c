@@ -3,11 +3,16 @@
  * hipMalloc, no Python and no torch, so the boundary is exercised the way a
  * C or C++ serving loop would use it.
  *
- * It quantizes a small seeded batch (kv_quantize_prefill), appends tokens
- * across group flushes (kv_append_token), reads the cache back
- * (kv_dequantize) and runs decode attention (kv_decode_attention, and the
- * no-allocation form), then checks against the oracle (oracle/kvq_oracle.c,
- * test infrastructure, linked into this test program only):
+ * Two caches: contiguous (INT2 keys, INT4 values, G = 32, R = 64) and paged
+ * (INT4 keys, INT2 values, G = 16, R = 32), whose block table this program
+ * keeps as the header asks of a caller: a block id from a shuffled pool for
+ * every key group before the call that quantizes it (the prefill, or the
+ * append that flushes the group).  For each, it quantizes a small seeded
+ * batch (kv_quantize_prefill), appends tokens across group flushes
+ * (kv_append_token), reads the cache back (kv_dequantize) and runs decode
+ * attention (kv_decode_attention, and the no-allocation form), then checks
+ * against the oracle (oracle/kvq_oracle.c, test infrastructure, linked into
+ * this test program only):
  *   - dequantized keys and values bit for bit, zeros past each sequence;
  *   - attention within max-abs 2e-3 and per-row cosine 0.9999 of the
  *     oracle's fp64 attention over the same dequantized cache;
@@ -43,7 +48,7 @@ void orc_dequantize_stream(const uint16_t *k, const uint16_t *v, int n, int nq, 
 void orc_attention(const float *q, int gq, const float *kh, const float *vh, int n, int d, float scale,
                    double *out, double *weights);
 
-enum { B = 3, H = 2, GQ = 4, HQ = H * GQ, D = 128, KB = 2, VB = 4, G = 32, R = 64, STEPS = 2 * G + 5, CAP = 400 };
+enum { B = 3, H = 2, GQ = 4, HQ = H * GQ, D = 128, CAP = 400, MAXG = 64 };
 
 #define HIP_OK(x)                                                                   \
     do {                                                                            \
@@ -79,8 +84,16 @@ static float normalish(void)
     return (float)((s - 2.0) * 1.7320508075688772);
 }
 
-int main(void)
+static int num_quantized(int n, int G, int R)
 {
+    return n <= R ? 0 : G * ((n - R) / G);
+}
+
+/* One cache: prefill, STEPS appends, read back, attention, checks.  Returns
+ * 0 when every check passes. */
+static int run(int paged, int KB, int VB, int G, int R)
+{
+    const int STEPS = 2 * G + R / 2 + 5;
     const int lens0[B] = {150, 0, 77};
     int T = 0;
     for (int b = 0; b < B; ++b)
@@ -105,7 +118,12 @@ int main(void)
     cfg.v_bits = VB;
     cfg.group_size = G;
     cfg.residual = R;
-    cfg.max_tokens = CAP;
+    cfg.max_tokens = paged ? 0 : CAP;
+    if (paged) {
+        cfg.block_size = G;
+        cfg.max_blocks_per_seq = MAXG;
+        cfg.num_blocks = B * MAXG;
+    }
     cfg.kv_format = KVQ_FORMAT_KIVI;
     cfg.grid = KVQ_GRID_UNIFORM;
     kvq_sizes sz;
@@ -122,6 +140,35 @@ int main(void)
     HIP_OK(hipMemset(cache.arrivals, 0, sz.counter_bytes));
     HIP_OK(hipMemset(cache.n_tokens, 0, sz.counter_bytes));
     HIP_OK(hipMemset(cache.n_quant, 0, sz.counter_bytes));
+    /* paged: the block table and a pool handed out in a seeded shuffled order */
+    int32_t table[B * MAXG], assigned[B] = {0}, pool[B * MAXG], pool_next = 0;
+    int32_t *dtable = NULL;
+    if (paged) {
+        for (int i = 0; i < B * MAXG; ++i) {
+            table[i] = -1;
+            pool[i] = i;
+        }
+        for (int i = B * MAXG - 1; i > 0; --i) {
+            const int j = (int)(uniform01() * (i + 1));
+            const int32_t t = pool[i];
+            pool[i] = pool[j];
+            pool[j] = t;
+        }
+        HIP_OK(hipMalloc((void **)&dtable, sz.block_table_bytes));
+        cache.block_table = dtable;
+    }
+    /* every sequence gets a block for each key group it will hold after the
+     * next call, before that call */
+#define ASSIGN_BLOCKS(NEXT_LEN)                                                           \
+    do {                                                                                \
+        if (!paged) break;                                                              \
+        for (int b_ = 0; b_ < B; ++b_)                                                  \
+            for (int g_ = assigned[b_]; g_ < num_quantized((NEXT_LEN)[b_], G, R) / G; ++g_) \
+                table[b_ * MAXG + g_] = pool[pool_next++];                              \
+        for (int b_ = 0; b_ < B; ++b_)                                                  \
+            assigned[b_] = num_quantized((NEXT_LEN)[b_], G, R) / G;                    \
+        HIP_OK(hipMemcpy(dtable, table, sizeof table, hipMemcpyHostToDevice));          \
+    } while (0)
 
     /* prefill: the first lens0[b] tokens, as [B][H][L][D] with L = max lens0 */
     int L = 0;
@@ -140,6 +187,7 @@ int main(void)
     HIP_OK(hipMemcpy(dk, kp, sizeof(uint16_t) * B * H * L * D, hipMemcpyHostToDevice));
     HIP_OK(hipMemcpy(dv, vp, sizeof(uint16_t) * B * H * L * D, hipMemcpyHostToDevice));
     HIP_OK(hipMemcpy(dlens, lens0, sizeof(int32_t) * B, hipMemcpyHostToDevice));
+    ASSIGN_BLOCKS(lens0);
     KVQ_OK_(kv_quantize_prefill(&cfg, &cache, dk, dv, L, (const int32_t *)dlens, NULL));
 
     /* appends: token lens0[b] + s of every stream at step s */
@@ -155,6 +203,9 @@ int main(void)
             }
         HIP_OK(hipMemcpy(dkn, kn, sizeof kn, hipMemcpyHostToDevice));
         HIP_OK(hipMemcpy(dvn, vn, sizeof vn, hipMemcpyHostToDevice));
+        int next[B];
+        for (int b = 0; b < B; ++b) next[b] = lens0[b] + s + 1;
+        ASSIGN_BLOCKS(next);
         KVQ_OK_(kv_append_token(&cfg, &cache, dkn, dvn, NULL));
     }
 
@@ -245,9 +296,22 @@ int main(void)
         fprintf(stderr, "the no-allocation call differs from the workspace call\n");
         bad = 1;
     }
-    printf("c caller: B=%d H=%d gq=%d k%d/v%d G=%d R=%d, %d appends: dequantized %s, attention max-abs %.3g "
+    printf("c caller, %s: B=%d H=%d gq=%d k%d/v%d G=%d R=%d, %d appends: dequantized %s, attention max-abs %.3g "
            "min cosine %.8f, no-allocation call %s\n",
-           B, H, GQ, KB, VB, G, R, STEPS, bad ? "CHECK FAILED" : "bit-exact", max_err, min_cos,
-           memcmp(out, out2, sizeof out) ? "differs" : "identical");
+           paged ? "paged" : "contiguous", B, H, GQ, KB, VB, G, R, STEPS, bad ? "CHECK FAILED" : "bit-exact",
+           max_err, min_cos, memcmp(out, out2, sizeof out) ? "differs" : "identical");
+    void *bufs[] = {cache.packed, cache.k_res, cache.v_res, cache.n_tokens, cache.n_quant, cache.arrivals, dtable,
+                    dk, dv, dlens, dkn, dvn, dq, dout, dout2, dws, dko, dvo};
+    for (unsigned i = 0; i < sizeof bufs / sizeof bufs[0]; ++i)
+        if (bufs[i]) HIP_OK(hipFree(bufs[i]));
+    free(Kh); free(Vh); free(kp); free(vp); free(ko); free(vo); free(kc); free(vc); free(ks); free(kz);
+    free(hk); free(hv); free(ok); free(ov);
+    return bad;
+}
+
+int main(void)
+{
+    int bad = run(0, 2, 4, 32, 64);
+    bad |= run(1, 4, 2, 16, 32);
     return bad;
 }

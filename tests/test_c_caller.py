@@ -3,9 +3,10 @@ Python binding and no torch between the caller and the library.
 
 CPU: the program builds (include/kvq.h read by a C99 compiler with -Wall
 -Werror, linked against the in-tree library) and the binary depends on that
-library.  GPU: the program runs prefill, appends across group flushes,
-kv_dequantize and both attention entry points on device memory from
-hipMalloc, and checks them against the oracle compiled into it (dequantized
+library.  GPU: on a contiguous cache and on a paged one whose block table the
+program keeps itself (a block per key group before the call that quantizes
+it), the program runs prefill, appends across group flushes, kv_dequantize
+and both attention entry points on device memory from hipMalloc, and checks them against the oracle compiled into it (dequantized
 values bit for bit, attention within max-abs 2e-3 and per-row cosine 0.9999,
 the no-allocation call equal to the workspace call); it exits 0 only if all
 checks pass."""
@@ -38,4 +39,4 @@ def test_c_caller_against_oracle():
     r = subprocess.run([BIN], capture_output=True, text=True, timeout=120)
     print(r.stdout, r.stderr, flush=True)
     assert r.returncode == 0, r.stderr
-    assert "bit-exact" in r.stdout and "identical" in r.stdout
+    assert r.stdout.count("bit-exact") == 2 and r.stdout.count("call identical") == 2
