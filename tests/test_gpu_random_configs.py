@@ -21,11 +21,12 @@ from parity_util import (compare_attention, compare_codes, make_cache, oracle_at
 pytestmark = pytest.mark.gpu
 
 SCALE = 128 ** -0.5
-N_CONFIGS = 40
+N_CONFIGS = 96
+N_LONG_CONFIGS = 24
 
 
-def _config(i):
-    rng = np.random.Generator(np.random.PCG64(0x5EED + 7919 * i))
+def _config(i, long_context=False):
+    rng = np.random.Generator(np.random.PCG64((0x10C9 if long_context else 0x5EED) + 7919 * i))
     fmt = int(rng.choice([kvq.FORMAT_KIVI] * 4 + [kvq.FORMAT_INT8, kvq.FORMAT_FP8_E4M3]))
     G = int(rng.choice([16, 32]))
     H = int(rng.integers(1, 4))
@@ -41,19 +42,29 @@ def _config(i):
         grid = 1 if option == 1 or (option == 3 and rng.integers(0, 2)) else 0
         theta = 10000.0 if option == 2 else 0.0
         sparse = 1 if option == 3 else 0
-    lens = rng.integers(0, 900, size=B)
-    lens[int(rng.integers(0, B))] = int(rng.integers(0, 3))   # an empty or nearly empty sequence
+    lens = rng.integers(0, 6000 if long_context else 900, size=B)
+    if not long_context or B > 1:
+        lens[int(rng.integers(0, B))] = int(rng.integers(0, 3))   # an empty or nearly empty sequence
     base = synth.WORKLOADS["llama3_8b_layer_b8_32k_int4"]
-    w = dataclasses.replace(base, name="rnd%d" % i, num_seqs=B, num_q_heads=H * gq, num_kv_heads=H, k_bits=kb,
+    w = dataclasses.replace(base, name="rnd%s%d" % ("L" if long_context else "", i), num_seqs=B, num_q_heads=H * gq, num_kv_heads=H, k_bits=kb,
                             v_bits=vb, group_size=G, residual=R, context=int(lens.max()) + 1, paged=paged,
-                            min_context=0, tag=200 + i, kv_format=fmt, rope_theta=theta, grid=grid,
+                            min_context=0, tag=(300 if long_context else 200) + i, kv_format=fmt, rope_theta=theta, grid=grid,
                             sparse_keys=sparse)
     return w, lens.astype(np.int64), R + G + 1   # every sequence, the empty one too, flushes a group
 
 
 @pytest.mark.parametrize("i", range(N_CONFIGS))
 def test_random_configuration(i):
-    w, lens0, steps = _config(i)
+    _check_configuration(i, *_config(i))
+
+
+@pytest.mark.parametrize("i", range(N_LONG_CONFIGS))
+def test_random_long_configuration(i):
+    """Lengths up to 6000 tokens: streams split over several workgroups."""
+    _check_configuration(i, *_config(i, long_context=True))
+
+
+def _check_configuration(i, w, lens0, steps):
     print("config %d: fmt=%d k%d/v%d G=%d R=%d B=%d H=%d gq=%d paged=%s theta=%g grid=%d sparse=%d lens=%s"
           % (i, w.kv_format, w.k_bits, w.v_bits, w.group_size, w.residual, w.num_seqs, w.num_kv_heads, w.gq,
              w.paged, w.rope_theta, w.grid, w.sparse_keys, list(lens0)), flush=True)
