@@ -710,6 +710,166 @@ __device__ void quantize_pair16(QuantSmemPair& sm, const Layout& L, const half_t
     __syncthreads();  // LDS may be reused by the caller
 }
 
+// Codebook grid at G = 16: two consecutive groups of a stream per workgroup,
+// each thread holding channels 8cg..8cg+7 of token ts of both records (as
+// quantize_group does for the two halves of a G = 32 group), so every thread
+// quantizes 16 elements instead of 8 (8B-layer shape at G = 16: 416 -> 352
+// us).  Each record gets exactly the bytes quantize_group<16> writes: the
+// same reductions (min and max are exact in any order) and the same code
+// arithmetic.  rec1 may be null (the stream's last group); its rows are then
+// neither read nor written.  (With dense-and-sparse keys the two selections
+// run one after the other and the pairing gained nothing: those keep one
+// group per workgroup.)
+struct QuantSmemPairG {
+    uint16_t kmn[2][16][kD], kmx[2][16][kD];   // per record, token, channel: fp16 bits
+    float kz[2][kD], kinv[2][kD];
+    uint8_t vcode[32][kD];                     // value codes, rows 16j + ts
+    uint2 cb4[240];                            // 4-bit codebook bin table
+};
+
+template <int KB, int VB>
+__device__ void quantize_pair16cb(QuantSmemPairG& sm, const Layout& L, const half_t* __restrict__ ksrc,
+                                 const half_t* __restrict__ vsrc, uint8_t* __restrict__ rec0,
+                                 uint8_t* __restrict__ rec1) {
+    const int tid = threadIdx.x;
+    const int cg = tid & 15;
+    const int ts = tid >> 4;
+    uint8_t* const recs[2] = {rec0, rec1};
+
+    float kx[2][8], vx[2][8];
+    uint32_t kraw[2][8];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int t = ts + 16 * j;
+        uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+        if (recs[j]) {
+            a = load_once16(ksrc + t * kD + 8 * cg);
+            b = load_once16(vsrc + t * kD + 8 * cg);
+        }
+        const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+        const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kraw[j][2 * e] = aw[e] & 0xffffu;
+            kraw[j][2 * e + 1] = aw[e] >> 16;
+            kx[j][2 * e] = h2f(aw[e] & 0xffffu);
+            kx[j][2 * e + 1] = h2f(aw[e] >> 16);
+            vx[j][2 * e] = h2f(bw[e] & 0xffffu);
+            vx[j][2 * e + 1] = h2f(bw[e] >> 16);
+        }
+    }
+    if constexpr (KB == 4 || VB == 4) cb4_table(sm.cb4, KB == 4 ? L.kmid : L.vmid, tid);
+
+    // Key statistics: this token's values per record, reduced over the
+    // record's 16 tokens below.
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            sm.kmn[j][ts][8 * cg + e] = (uint16_t)kraw[j][e];
+            sm.kmx[j][ts][8 * cg + e] = (uint16_t)kraw[j][e];
+        }
+
+    // Value statistics: per token over its 128 channels (16 lanes of a row).
+    QParams pv[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        float mn = vx[j][0], mx = vx[j][0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) {
+            mn = fminf(mn, vx[j][e]);
+            mx = fmaxf(mx, vx[j][e]);
+        }
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            mn = fminf(mn, __shfl_xor(mn, off));
+            mx = fmaxf(mx, __shfl_xor(mx, off));
+        }
+        pv[j] = make_qparams(mn, mx, VB);
+        if (cg == 0 && recs[j]) {
+            const int pos = vmeta_pos(L, ts);
+            *(uint16_t*)(recs[j] + pos) = pv[j].s_bits;
+            *(uint16_t*)(recs[j] + pos + 2 * L.spt) = pv[j].z_bits;
+        }
+    }
+    __syncthreads();
+    {
+        // channel ch of record j: all four waves, one (record, channel) each
+        const int j = tid >> 7, ch = tid & (kD - 1);
+        float mn = h2f(sm.kmn[j][0][ch]), mx = h2f(sm.kmx[j][0][ch]);
+        for (int r = 1; r < 16; ++r) {
+            mn = fminf(mn, h2f(sm.kmn[j][r][ch]));
+            mx = fmaxf(mx, h2f(sm.kmx[j][r][ch]));
+        }
+        const QParams p = make_qparams(mn, mx, KB);
+        sm.kz[j][ch] = p.z;
+        sm.kinv[j][ch] = p.inv;
+        if (recs[j]) {
+            *(uint16_t*)(recs[j] + L.kmeta_off + 2 * ch) = p.s_bits;
+            *(uint16_t*)(recs[j] + L.kmeta_off + 2 * kD + 2 * ch) = p.z_bits;
+        }
+    }
+    __syncthreads();
+
+    // Key codes (token ts of each record) and the value codes into LDS.
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        float kzr[8], kir[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            kzr[e] = sm.kz[j][8 * cg + e];
+            kir[e] = sm.kinv[j][8 * cg + e];
+        }
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t q = KB == 4 ? cb4_code(kx[j][e], kzr[e], kir[e], sm.cb4)
+                                       : code_of<true, KB>(kx[j][e], kzr[e], kir[e], L.kmid);
+            w |= q << (KB == 4 ? code_bit(4, e) : code_bit(2, e + 8 * (cg & 1)));
+        }
+        if (KB == 4) {
+            if (recs[j]) store_once(recs[j] + ts * 64 + 4 * cg, w);
+        } else {
+            w |= __shfl_xor(w, 1);
+            if ((cg & 1) == 0 && recs[j]) store_once(recs[j] + ts * 32 + 2 * cg, w);
+        }
+        uint32_t v0 = 0, v1 = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (VB == 4) {
+                v0 |= cb4_code(vx[j][e], pv[j].z, pv[j].inv, sm.cb4) << (8 * e);
+                v1 |= cb4_code(vx[j][e + 4], pv[j].z, pv[j].inv, sm.cb4) << (8 * e);
+            } else {
+                v0 |= code_of<true, VB>(vx[j][e], pv[j].z, pv[j].inv, L.vmid) << (8 * e);
+                v1 |= code_of<true, VB>(vx[j][e + 4], pv[j].z, pv[j].inv, L.vmid) << (8 * e);
+            }
+        }
+        *(uint2*)&sm.vcode[16 * j + ts][8 * cg] = make_uint2(v0, v1);
+    }
+    __syncthreads();
+
+    // Value code words of each record, lane-major in decode-operand order
+    // (the codes of LDS rows 16j .. 16j+15).
+    constexpr int SPT = 4;
+    constexpr int WPL = SPT * VB / 4;        // words per lane
+    constexpr int CPW = 32 / VB;             // codes per word
+    for (int D = tid; D < 2 * 64 * WPL; D += 256) {
+        const int j = D / (64 * WPL), Dj = D % (64 * WPL);
+        const int lane = Dj / WPL, wi = Dj % WPL;
+        const int g = lane >> 4, n = lane & 15;
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < CPW; ++e) {
+            const int q = wi * CPW + e;
+            const int ct = q / SPT, slot = q % SPT;
+            const int t = 4 * g + slot;
+            w |= (uint32_t)sm.vcode[16 * j + t][16 * ct + n] << code_bit(VB, e);
+        }
+        if (recs[j]) store_once(recs[j] + L.vcode_off + vlane_byte(SPT * VB, lane, 4 * wi), w);
+    }
+    __syncthreads();  // LDS may be reused by the caller
+}
+
 // The same for the 8-bit formats ("KV cache compression: ...", section 3.1):
 // every key and value token on its own.  F = kFmtInt8: the min/max grid with
 // 8 bits over the token's 128 channels (the 16 threads of a row reduce it);
@@ -883,6 +1043,26 @@ __global__ __launch_bounds__(256) void prefill_pairs16_kernel(Layout L, kvq_cach
     if (!rec0 && !rec1) return;
     const long base = ((long)sh * max_len + (long)g * 16) * kD;
     quantize_pair16<KB, VB>(sm, L, k + base, v + base, rec0, rec1);
+}
+
+// Codebook grid, G = 16: grid (ceil(max_len / 32), B*H); one workgroup per
+// two consecutive groups of a stream.
+template <int KB, int VB>
+__global__ __launch_bounds__(256) void prefill_pairs16cb_kernel(Layout L, kvq_cache c, const half_t* k,
+                                                                const half_t* v, int max_len,
+                                                                const int32_t* seq_lens) {
+    __shared__ QuantSmemPairG sm;
+    const int g = 2 * blockIdx.x;
+    const int sh = blockIdx.y;
+    const int b = sh / L.H, h = sh % L.H;
+    const int n = clamped_len(L, seq_lens, b, max_len);
+    const int nq = num_quantized(n, 16, L.R);
+    if (g * 16 >= nq) return;
+    uint8_t* rec0 = record_at(L, c.packed, c.block_table, b, h, g);
+    uint8_t* rec1 = (g + 1) * 16 < nq ? record_at(L, c.packed, c.block_table, b, h, g + 1) : nullptr;
+    if (!rec0 && !rec1) return;
+    const long base = ((long)sh * max_len + (long)g * 16) * kD;
+    quantize_pair16cb<KB, VB>(sm, L, k + base, v + base, rec0, rec1);
 }
 
 // Residual copy and counters: grid (B*H), 256 threads.
@@ -1308,6 +1488,20 @@ hipError_t launch_prefill(const Layout& L, const kvq_cache& c, const half_t* k, 
             default: return hipErrorInvalidValue;
         }
 #undef KVQ_PP
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    } else if (ngroups > 0 && L.G == 16 && quant_variant(L) == kQCodebook) {
+        dim3 grid((ngroups + 1) / 2, L.B * L.H);
+#define KVQ_PC(KB, VB) \
+    hipLaunchKernelGGL((prefill_pairs16cb_kernel<KB, VB>), grid, dim3(256), 0, s, L, c, k, v, max_len, seq_lens)
+        switch (L.kbits * 10 + L.vbits) {
+            case 22: KVQ_PC(2, 2); break;
+            case 24: KVQ_PC(2, 4); break;
+            case 42: KVQ_PC(4, 2); break;
+            case 44: KVQ_PC(4, 4); break;
+            default: return hipErrorInvalidValue;
+        }
+#undef KVQ_PC
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     } else if (ngroups > 0) {
