@@ -971,6 +971,71 @@ __device__ void quantize_group8(QuantSmemU<G>& sm, const Layout& L, const half_t
     __syncthreads();  // LDS may be reused by the caller
 }
 
+// FP8 E4M3 at G = 16: two consecutive groups of a stream per workgroup, each
+// thread holding channels 8cg..8cg+7 of token ts of both records, with the
+// arithmetic of quantize_group8<16> (every token on its own, so each record
+// gets exactly the bytes that one writes; 8B-layer shape at G = 16: 320 ->
+// 272 us).  rows0, rows1: tokens present in each record (a partial last
+// record when quantized on write); rec1 may be null.  (INT8 measured no
+// faster this way and keeps one group per workgroup.)
+__device__ void quantize_pair16_fp8(QuantSmemU<32>& sm, const Layout& L, const half_t* __restrict__ ksrc,
+                                  const half_t* __restrict__ vsrc, uint8_t* __restrict__ rec0,
+                                  uint8_t* __restrict__ rec1, float kinv, float vinv, int rows0, int rows1) {
+    constexpr int SPT = 4;
+    const int tid = threadIdx.x;
+    const int cg = tid & 15;
+    const int ts = tid >> 4;
+    uint8_t* const recs[2] = {rec0, rec1};
+    const int rows[2] = {rows0, rows1};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        uint8_t* const rec = recs[j];
+        const int t = ts + 16 * j;   // row of the pair; token ts of record j
+        const uint4 z4 = make_uint4(0, 0, 0, 0);
+        const bool here = rec && ts < rows[j];
+        const uint4 a = here ? load_once16(ksrc + t * kD + 8 * cg) : z4;
+        const uint4 b = here ? load_once16(vsrc + t * kD + 8 * cg) : z4;
+        const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+        const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+        uint32_t kw[2], vw[2];
+        {
+            float kx[8], vx[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kx[2 * e] = h2f(aw[e] & 0xffffu);
+                kx[2 * e + 1] = h2f(aw[e] >> 16);
+                vx[2 * e] = h2f(bw[e] & 0xffffu);
+                vx[2 * e + 1] = h2f(bw[e] >> 16);
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                kw[h] = fp8_code2(kx[4 * h], kx[4 * h + 1], kinv) | fp8_code2(kx[4 * h + 2], kx[4 * h + 3], kinv) << 16;
+                vw[h] = fp8_code2(vx[4 * h], vx[4 * h + 1], vinv) | fp8_code2(vx[4 * h + 2], vx[4 * h + 3], vinv) << 16;
+            }
+        }
+        if (rec) store_once8(rec + k8_byte(ts, 8 * cg), kw[0], kw[1]);
+        *(uint2*)&sm.vcode[t][8 * cg] = make_uint2(vw[0], vw[1]);
+    }
+    __syncthreads();
+
+    // Value bytes of each record, lane-major (LDS rows 16j .. 16j+15).
+    constexpr int WPL = SPT * 2;   // words per lane
+    for (int D = tid; D < 2 * 64 * WPL; D += 256) {
+        const int j = D / (64 * WPL), Dj = D % (64 * WPL);
+        const int lane = Dj / WPL, wi = Dj % WPL;
+        const int g = lane >> 4, n = lane & 15;
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int q = wi * 4 + e;
+            const int ct = q / SPT, slot = q % SPT;
+            w |= (uint32_t)sm.vcode[16 * j + 4 * g + slot][16 * ct + n] << (8 * e);
+        }
+        if (recs[j]) store_once(recs[j] + L.vcode_off + vlane_byte(SPT * 8, lane, 4 * wi), w);
+    }
+    __syncthreads();  // LDS may be reused by the caller
+}
+
 // Variant of a layout (host).
 inline int quant_variant(const Layout& L) {
     if (L.fmt != kFmtKivi) return L.fmt;
@@ -1063,6 +1128,26 @@ __global__ __launch_bounds__(256) void prefill_pairs16cb_kernel(Layout L, kvq_ca
     if (!rec0 && !rec1) return;
     const long base = ((long)sh * max_len + (long)g * 16) * kD;
     quantize_pair16cb<KB, VB>(sm, L, k + base, v + base, rec0, rec1);
+}
+
+// FP8, G = 16: grid (ceil(max_len / 32), B*H); one workgroup per two
+// consecutive groups of a stream.
+__global__ __launch_bounds__(256) void prefill_pairs16_fp8_kernel(Layout L, kvq_cache c, const half_t* k,
+                                                                  const half_t* v, int max_len,
+                                                                  const int32_t* seq_lens) {
+    __shared__ QuantSmemU<32> sm;
+    const int g = 2 * blockIdx.x;
+    const int sh = blockIdx.y;
+    const int b = sh / L.H, h = sh % L.H;
+    const int n = clamped_len(L, seq_lens, b, max_len);
+    const int nq = quantized_count(L, n);
+    if (g * 16 >= nq) return;
+    uint8_t* rec0 = record_at(L, c.packed, c.block_table, b, h, g);
+    uint8_t* rec1 = (g + 1) * 16 < nq ? record_at(L, c.packed, c.block_table, b, h, g + 1) : nullptr;
+    if (!rec0 && !rec1) return;
+    const long base = ((long)sh * max_len + (long)g * 16) * kD;
+    quantize_pair16_fp8(sm, L, k + base, v + base, rec0, rec1, fp8_inv_scale(c.k_scale[h]),
+                        fp8_inv_scale(c.v_scale[h]), min(16, nq - g * 16), min(16, nq - (g + 1) * 16));
 }
 
 // Residual copy and counters: grid (B*H), 256 threads.
@@ -1488,6 +1573,11 @@ hipError_t launch_prefill(const Layout& L, const kvq_cache& c, const half_t* k, 
             default: return hipErrorInvalidValue;
         }
 #undef KVQ_PP
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    } else if (ngroups > 0 && L.G == 16 && L.fmt == kFmtFp8) {
+        dim3 grid((ngroups + 1) / 2, L.B * L.H);
+        hipLaunchKernelGGL(prefill_pairs16_fp8_kernel, grid, dim3(256), 0, s, L, c, k, v, max_len, seq_lens);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     } else if (ngroups > 0 && L.G == 16 && quant_variant(L) == kQCodebook) {
