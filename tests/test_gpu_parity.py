@@ -86,6 +86,47 @@ def test_edge_lengths_in_one_batch():
     compare_attention(out, ref)
 
 
+@pytest.mark.parametrize("paged", [False, True])
+def test_many_short_sequences(paged):
+    """3000 sequences of 0 to 400 tokens in one batch (6000 streams, more
+    than one workgroup round): the per-sequence prefix every workgroup
+    computes in its prologue, the flattened split across many streams, the
+    merge, and appends of 3000 sequences per launch across a group flush.
+    Attention of every row against the oracle after the prefill and after
+    the appends; codes of a sample of sequences bit for bit."""
+    B = 3000
+    w = _w("paged_64seq_1k_16k_k4v2" if paged else "llama3_8b_layer_b8_32k_int4", name="many%d" % paged,
+           num_seqs=B, num_q_heads=8, num_kv_heads=2, k_bits=2, v_bits=4, group_size=16 if paged else 32,
+           residual=32, context=400, min_context=0, tag=35 + paged)
+    lens = np.random.Generator(np.random.PCG64(35 + paged)).integers(0, 401, size=B).astype(np.int64)
+    steps = w.group_size + 1   # every sequence flushes a group at most once, most none
+    L = int(lens.max()) + steps
+    K, V = synth.make_kv(w, max_len=L, device="cuda")
+    cache = make_cache(w, lens + steps, shuffle_seed=7)
+    print("many sequences: B=%d paged=%s steps=%d" % (B, paged, steps), flush=True)
+    cache.prefill(K[:, :, :int(lens.max())].contiguous(), V[:, :, :int(lens.max())].contiguous(), lens)
+    kb, vb = to_bits(K), to_bits(V)
+    states = oracle_states(kb[:, :, :int(lens.max())], vb[:, :, :int(lens.max())], lens, w, cap=L + 64)
+    rng = np.random.Generator(np.random.PCG64(7))
+    sample = [(int(b), h) for b in rng.choice(B, 40, replace=False) for h in range(2)]
+    compare_codes(cache, states, sample)
+    q = synth.make_query(w, device="cuda")
+    compare_attention(cache.decode_attention(q, SCALE).cpu().numpy(), oracle_attention(to_bits(q), states, SCALE))
+    # appends: one kernel launch for all 3000 sequences per step
+    n = lens.copy()
+    for _ in range(steps):
+        idx = torch.as_tensor(n, device="cuda")
+        ar = torch.arange(B, device="cuda")
+        cache.append(K[ar, :, idx].contiguous(), V[ar, :, idx].contiguous())
+        for b in range(B):
+            for h in range(2):
+                states[b][h].append(kb[b, h, n[b]], vb[b, h, n[b]])
+        n += 1
+    compare_codes(cache, states, sample)
+    q = synth.make_query(w, device="cuda", step=1)
+    compare_attention(cache.decode_attention(q, SCALE).cpu().numpy(), oracle_attention(to_bits(q), states, SCALE))
+
+
 def test_cache_without_group_capacity():
     """A contiguous cache too short ever to flush a group (max_tokens below
     R + G): it holds no group records, every token stays in the residual
