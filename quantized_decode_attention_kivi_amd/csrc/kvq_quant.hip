@@ -15,11 +15,13 @@ namespace kvq {
 
 template <int G>
 struct QuantSmem {
-    float kmn[16][kD], kmx[16][kD];   // per token slice, per channel
+    uint16_t kmn[16][kD], kmx[16][kD];   // per token slice, per channel: fp16 bits (exact: fp16
+                                         // inputs, or infinities for kept extremes)
     float kz[kD], kinv[kD];
     uint8_t vcode[G][kD];             // value codes before packing
     int red[2][4];                    // dense-and-sparse: per-wave counts (double-buffered)
     uint32_t kept[G * kD / 32];       // dense-and-sparse: kept positions, one bit each
+    uint32_t cand[8 * G];             // dense-and-sparse: each wave's candidates (2G slots per wave)
     int wtot[2];                      // dense-and-sparse: kept count of the first two words' waves
     uint2 cb4[240];                   // 4-bit codebook: per 1/16 of a grid step (threshold bits, code)
 };
@@ -78,12 +80,16 @@ __device__ __forceinline__ void select_extremes(QuantSmem<G>& sm, const uint32_t
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             key[j][e] = ((kb[j][e] & 0x7fffu) << 12) | (4095u - (uint32_t)((ts + 16 * j) * kD + 8 * cg + e));
+    // the kept-position words start empty (first read after the barriers below)
+    for (int i = tid; i < G * kD / 32; i += 256) sm.kept[i] = 0;
     // The group's G largest keys are among the G largest of each wave's
-    // quarter.  Each wave finds a threshold with exactly G of its keys at or
-    // above it (counts by ballot: no barrier; the search stops at the first
-    // candidate with exactly G), writes those G keys to LDS, and the first
-    // wave finds the G-th largest of the 4G, which is the group's.
+    // quarter.  Each wave finds a threshold with between G and 2G of its keys
+    // at or above it (counts by ballot: no barrier; the search stops at the
+    // first candidate threshold in that range), writes those keys to its 2G
+    // slots in LDS (zeros, below every key, in the rest), and the first wave
+    // finds the G-th largest of the candidates, which is the group's.
     uint32_t Tw = 0;
+    int nw = 0;
     for (int bit = 26; bit >= 0; --bit) {
         const uint32_t cand = Tw | (1u << bit);
         int cnt = 0;
@@ -93,11 +99,15 @@ __device__ __forceinline__ void select_extremes(QuantSmem<G>& sm, const uint32_t
             for (int e = 0; e < 8; ++e) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[j][e] >= cand));
         if (cnt >= G) {
             Tw = cand;
-            if (cnt == G) break;   // exactly G at or above: the lower bits change nothing
+            nw = cnt;
+            if (cnt <= 2 * G) break;   // the wave's G largest, and at most G others
         }
     }
-    uint32_t* cands = sm.kept;   // 4G words, free until the marking below
-    int base = wave * G;
+    // (the search always stops in the range: its last step up leaves exactly
+    // G keys at or above, the keys being distinct; the slot bound below only
+    // keeps the writes inside the wave's 2G slots)
+    uint32_t* const cands = sm.cand + wave * 2 * G;
+    int base = 0;
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
@@ -105,29 +115,38 @@ __device__ __forceinline__ void select_extremes(QuantSmem<G>& sm, const uint32_t
             const bool up = key[j][e] >= Tw;
             const uint64_t m = __builtin_amdgcn_ballot_w64(up);
             const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-            if (up) cands[base + below] = key[j][e];
+            if (up && base + below < 2 * G) cands[base + below] = key[j][e];
             base += (int)__builtin_popcountll(m);
         }
+    for (int i = min(nw, 2 * G) + lane; i < 2 * G; i += 64) cands[i] = 0u;
     __syncthreads();
     if (wave == 0) {
-        constexpr int PL = 4 * G / 64;   // candidates per lane: 2 (G = 32) or 1
+        constexpr int PL = 8 * G / 64;   // candidate slots per lane: 4 (G = 32) or 2
         uint32_t c[PL];
 #pragma unroll
-        for (int i = 0; i < PL; ++i) c[i] = cands[64 * i + lane];
+        for (int i = 0; i < PL; ++i) c[i] = sm.cand[64 * i + lane];
         uint32_t T = 0;
         for (int bit = 26; bit >= 0; --bit) {
             const uint32_t cand = T | (1u << bit);
             int cnt = 0;
 #pragma unroll
             for (int i = 0; i < PL; ++i) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(c[i] >= cand));
-            if (cnt >= G) T = cand;   // the exact G-th largest: every key of the group is tested against it
+            if (cnt >= G) {
+                T = cand;
+                if (cnt == G) break;   // exactly G at or above
+            }
         }
-        if (lane == 0) sm.red[0][0] = (int)T;
+        // the G-th largest candidate itself (the smallest of the G at or above
+        // T), so that no key outside the candidates reaches the threshold
+        uint32_t mn = 0xffffffffu;
+#pragma unroll
+        for (int i = 0; i < PL; ++i) mn = c[i] >= T ? min(mn, c[i]) : mn;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+        if (lane == 0) sm.red[0][0] = (int)mn;
     }
     __syncthreads();
     const uint32_t T = (uint32_t)sm.red[0][0];
-    for (int i = tid; i < G * kD / 32; i += 256) sm.kept[i] = 0;
-    __syncthreads();
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
         kbit[j] = 0;
@@ -251,8 +270,8 @@ __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* 
             mn = fminf(mn, k ? kInf : kx[j][e]);
             mx = fmaxf(mx, k ? -kInf : kx[j][e]);
         }
-        sm.kmn[ts][8 * cg + e] = mn;
-        sm.kmx[ts][8 * cg + e] = mx;
+        sm.kmn[ts][8 * cg + e] = __builtin_bit_cast(uint16_t, (_Float16)mn);
+        sm.kmx[ts][8 * cg + e] = __builtin_bit_cast(uint16_t, (_Float16)mx);
     }
 
     // Value statistics: per token over its 128 channels (16 lanes of a row).
@@ -280,10 +299,10 @@ __device__ void quantize_group(QuantSmem<G>& sm, const Layout& L, const half_t* 
     }
     __syncthreads();
     if (tid < kD) {
-        float mn = sm.kmn[0][tid], mx = sm.kmx[0][tid];
+        float mn = h2f(sm.kmn[0][tid]), mx = h2f(sm.kmx[0][tid]);
         for (int j = 1; j < 16; ++j) {
-            mn = fminf(mn, sm.kmn[j][tid]);
-            mx = fmaxf(mx, sm.kmx[j][tid]);
+            mn = fminf(mn, h2f(sm.kmn[j][tid]));
+            mx = fmaxf(mx, h2f(sm.kmx[j][tid]));
         }
         if (mn > mx) mn = mx = 0.0f;   // every value of the channel kept: s = z = 0
         const QParams p = make_qparams(mn, mx, KB);
