@@ -13,6 +13,11 @@
 
 namespace kvq {
 
+// Shared memory of the codebook and dense-and-sparse quantizers (about 17 KB
+// at G = 32).  The channel extremes of each token slice are kept as the fp16
+// values they are: min and max are exact in any precision, and half the
+// bytes of fp32 let more workgroups share a compute unit (24 -> 17 KB:
+// dense-and-sparse 8B-layer prefill 490 -> 458 us).
 template <int G>
 struct QuantSmem {
     uint16_t kmn[16][kD], kmx[16][kD];   // per token slice, per channel: fp16 bits (exact: fp16
@@ -26,10 +31,9 @@ struct QuantSmem {
     uint2 cb4[240];                   // 4-bit codebook: per 1/16 of a grid step (threshold bits, code)
 };
 
-// Shared memory of the uniform-grid and 8-bit quantizers: the channel
-// extremes of each token slice are kept as the fp16 values they are (min and
-// max are exact in any precision), so a workgroup needs about 14 KB instead
-// of 22 and eight of them fit a compute unit.
+// Shared memory of the uniform-grid and 8-bit quantizers: the same fp16
+// extremes without the codebook table and the selection's arrays (about
+// 14 KB: eight workgroups fit a compute unit).
 template <int G>
 struct QuantSmemU {
     uint16_t kmn[16][kD], kmx[16][kD];   // per token slice, per channel (fp16 bits)
