@@ -859,16 +859,34 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
             kc[rt][0] = x[0]; kc[rt][1] = x[1];
         }
     }
+    // G = 16: both records' zero-point sums from one set of products, record
+    // 0's zeros in rows 0-7 (lanes n < 8) and record 1's in rows 8-15; lane
+    // groups 0-1 then hold record 0's sums and 2-3 record 1's, and one swap
+    // of the wave's halves gives every lane both (the same products and
+    // order as one record at a time: the same sums).
+    float czr[S::NR];
+    if constexpr (S::NR == 2) {
+        const lds_u8* kz = buf + S::META + (n >= 8 ? S::MREC : 0) + 256;
+        f4 c2 = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c2 = mfma(__builtin_bit_cast(h8, lds_read<u32x4>(kz + 16 * (4 * g + j))), Q.q[j], c2);
+        const uint32_t u = __builtin_bit_cast(uint32_t, c2[0]);
+        const auto hv = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        czr[0] = __builtin_bit_cast(float, (uint32_t)hv[0]);
+        czr[1] = __builtin_bit_cast(float, (uint32_t)hv[1]);
+    }
 #pragma unroll
     for (int i = 0; i < S::NR; ++i) {
         const lds_u8* km = buf + S::META + i * S::MREC;
-        f4 cz = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        f4 cz = S::NR == 2 ? f4{czr[i], czr[i], czr[i], czr[i]} : f4{0.0f, 0.0f, 0.0f, 0.0f};
         h8 qhi[4], qlo[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const h8 s = __builtin_bit_cast(h8, lds_read<u32x4>(km + 16 * (4 * g + j)));
-            const h8 z = __builtin_bit_cast(h8, lds_read<u32x4>(km + 256 + 16 * (4 * g + j)));
-            cz = mfma(z, Q.q[j], cz);
+            if constexpr (S::NR == 1) {
+                const h8 z = __builtin_bit_cast(h8, lds_read<u32x4>(km + 256 + 16 * (4 * g + j)));
+                cz = mfma(z, Q.q[j], cz);
+            }
             {
 #pragma clang fp contract(off)
                 const h8 hi = Q.q[j] * s;
