@@ -875,6 +875,39 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
         czr[0] = __builtin_bit_cast(float, (uint32_t)hv[0]);
         czr[1] = __builtin_bit_cast(float, (uint32_t)hv[1]);
     }
+    if constexpr (TP && S::NR == 2) {
+        // Token packing at G = 16: column n carries head n & 3 of row tile
+        // (n >> 2) & 1, whose tokens are that record's, so each lane forms
+        // the q s limbs of its own column's record only (one set of products
+        // instead of one per record) and both tiles' products use them: row
+        // tile rt's logits are right in the columns of tile rt.
+        const lds_u8* km = buf + S::META + ((n >> 2) & 1) * S::MREC;
+        h8 qop[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const h8 s = __builtin_bit_cast(h8, lds_read<u32x4>(km + 16 * (4 * g + j)));
+            {
+#pragma clang fp contract(off)
+                qop[j] = Q.q[j] * s;
+            }
+        }
+        if (lo_limb) {
+            // low-limb columns (a divergent branch): q s - hi(q s), no bias
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const h8 s = __builtin_bit_cast(h8, lds_read<u32x4>(km + 16 * (4 * g + j)));
+                qop[j] = fma_sub_h8(Q.q[j], s, qop[j]);
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const float z = lo_limb ? 0.0f : czr[rt];
+            f4 acc = f4{z, z, z, z};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc = mfma(levels8<KB, CB>(kc[rt], j, L.klut), qop[j], acc);
+            C[rt] = acc;
+        }
+    } else {
 #pragma unroll
     for (int i = 0; i < S::NR; ++i) {
         const lds_u8* km = buf + S::META + i * S::MREC;
@@ -916,6 +949,7 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
             }
             C[rt] = acc;
         }
+    }
     }
     }
 
@@ -965,7 +999,10 @@ __device__ __forceinline__ void process_unit(const lds_u8* buf, uint32_t has, Wa
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int slot = S::NR == 2 ? i : 4 * rt + i;
-            x[i] = pack_second_tile(add_limb_partner(C[0][i]), add_limb_partner(C[1][i]));
+            // G = 16: each tile's logits are already in its own columns (the
+            // limb partner n ^ 8 is in the same tile)
+            x[i] = S::NR == 2 ? add_limb_partner(rt ? C[1][i] : C[0][i])
+                              : pack_second_tile(add_limb_partner(C[0][i]), add_limb_partner(C[1][i]));
             vs[i] = h2f(lds_read<uint16_t>(vm + 2 * slot));
             vz[i] = h2f(lds_read<uint16_t>(vm + 2 * (SPT + slot)));
             valid[i] = S::NR == 1 || ((has >> rec) & 1);
@@ -1410,8 +1447,10 @@ __device__ __forceinline__ void attend_segment(uint8_t* stage_a, uint8_t* stage_
 
     QOps Q;
     {
-        // column n: head n (LP: head n%8, high limb for n < 8, low limb above)
-        const int hd = LP ? (n16 & 7) : n16;
+        // column n: head n (LP: head n%8, high limb for n < 8, low limb above;
+        // token packing at G = 16: head n%4, columns 4-7 and 12-15 for the
+        // second row tile's record)
+        const int hd = TP && G == 16 ? (n16 & 3) : LP ? (n16 & 7) : n16;
         const bool hv = hd < gq;
         const uint4* qp = (const uint4*)(q + ((long)b * Hq + h * gq + (hv ? hd : 0)) * kD + 32 * g);
 #pragma unroll
