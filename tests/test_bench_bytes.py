@@ -65,3 +65,24 @@ def test_80_layer_int2_cache_closed_form():
     want = 80 * (8 * (nq * (64 + 16 + 4) + 128 * 512) + 64 * 128 * 6)
     assert bench.attention_bytes(lens, w) == want
     assert abs(want / 1e9 - 7.09) < 0.01
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_dequantize_bytes_are_records_and_fp32_output(name):
+    """kv_dequantize of one sequence: its records and fp16 residual read (the
+    attention bytes without query and output), its fp32 keys and values
+    written (2 x 4 bytes per element)."""
+    w = synth.workload(name)
+    n = int(synth.seq_lengths(w)[0])
+    rec = _record_bytes(w)
+    nq = kvq.num_quantized(n, w.group_size, w.residual)
+    want = w.num_kv_heads * ((nq // w.group_size) * rec + (n - nq) * 128 * 2 * 2 + n * 128 * 4 * 2)
+    assert bench.dequantize_bytes(n, w) == want
+
+
+def test_dequantize_bytes_closed_form_80_layer_cache():
+    """One layer of one sequence of the 80-layer INT2 cache: 8 kv heads x
+    (131072 - 128 quantized tokens x 84 bytes + 128 fp16 residual tokens x
+    512 bytes + 131072 tokens x 1024 bytes of fp32 keys and values)."""
+    w = synth.workload("llama3_70b_cache_80l_128k_int2")
+    assert bench.dequantize_bytes(131072, w) == 8 * ((131072 - 128) * 84 + 128 * 512 + 131072 * 1024)
